@@ -1,0 +1,266 @@
+"""CPU oracle for padded variable-length attention.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may use this package; the GPU library never
+does.  It wraps ``oracle.c`` (plain C, compiled with gcc) through ctypes and
+drives it one (batch entry, head) slice at a time on a thread pool (ctypes
+releases the GIL during each call).
+
+All tensors are numpy ``uint16`` arrays of bf16 bit patterns laid out
+``[B, H, L, d]``; results are float64 (``precision="f64"``) or float32
+(``precision="f32"``).  Every function cites the passage it follows in
+``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+SIGMOID, SOFTMAX, SOFTMAX1 = 0, 1, 2
+BIAS_NONE, BIAS_LOG_SEQLEN, BIAS_LOG_PADLEN = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c twice (double and float) into liboracle.so with gcc."""
+    if not force and os.path.exists(_LIB_PATH) and \
+            os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    flags = ["-O2", "-std=c11", "-fPIC", "-fno-fast-math", "-Wall", "-Wextra"]
+    objs = []
+    for real, sfx, extra in (("double", "_f64", ["-DORACLE_WITH_BLOCKMASK"]),
+                             ("float", "_f32", [])):
+        obj = os.path.join(_HERE, f"oracle{sfx}.o")
+        subprocess.check_call(["gcc", *flags, f"-DREAL={real}", f"-DSFX={sfx}", *extra,
+                               "-c", _SRC, "-o", obj])
+        objs.append(obj)
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-shared", "-o", tmp, *objs, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+    for obj in objs:
+        os.remove(obj)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    for sfx, R in (("_f64", ctypes.c_double), ("_f32", ctypes.c_float)):
+        f = getattr(lib, "oracle_fwd_rows" + sfx)
+        f.argtypes = [I, I, I, P, P, P, P, I, I, R, I, I, P, P]
+        f.restype = None
+        f = getattr(lib, "oracle_fwd_tiled" + sfx)
+        f.argtypes = [I, I, I, P, P, P, P, P, I, I, I, I, R, P, P]
+        f.restype = None
+        f = getattr(lib, "oracle_bwd_dq_rows" + sfx)
+        f.argtypes = [I, I, I, P, P, P, P, P, I, I, R, I, I, P]
+        f.restype = None
+        f = getattr(lib, "oracle_bwd_dkv_rows" + sfx)
+        f.argtypes = [I, I, I, P, P, P, P, P, I, I, R, I, I, P, P]
+        f.restype = None
+    lib.oracle_blockmask.argtypes = [P, P, I, I, I, I, P]
+    lib.oracle_blockmask.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _dtype(precision):
+    return {"f64": np.float64, "f32": np.float32}[precision]
+
+
+def _threads(threads):
+    return threads or os.cpu_count() or 1
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d), d the head dimension (the scaled dot product of both pages)."""
+    return 1.0 / float(np.sqrt(d))
+
+
+def blockmask(seq_lens, mask, L: int, block_q: int, block_k: int) -> np.ndarray:
+    """Binary block matrix [B, Tq, Tk] (uint8, 0/1); see oracle_blockmask."""
+    lib = _load()
+    n = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B = n.shape[0]
+    m = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+    Tq, Tk = -(-L // block_q), -(-L // block_k)
+    out = np.zeros((B, Tq, Tk), dtype=np.uint8)
+    lib.oracle_blockmask(_ptr(n), _ptr(m), B, L, block_q, block_k, _ptr(out))
+    return out
+
+
+def _heads(q):
+    B, H, L, d = q.shape
+    return B, H, L, d
+
+
+def fwd(q, k, v, seq_lens, mask=None, bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None,
+        precision="f64", threads=None, heads=None):
+    """Forward by the plain definition (oracle_fwd_rows) for every row.
+
+    Returns (o [B, H, L, d], lse [B, H, L]).  ``heads``: optional list of
+    (b, h) pairs to compute; the others are left at zero / -inf.
+    """
+    lib = _load()
+    B, H, L, d = _heads(q)
+    dt = _dtype(precision)
+    fn = getattr(lib, "oracle_fwd_rows_" + precision)
+    scale = default_scale(d) if scale is None else scale
+    o = np.zeros((B, H, L, d), dtype=dt)
+    lse = np.full((B, H, L), -np.inf, dtype=dt)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+
+    def one(bh):
+        b, h = bh
+        qs, ks, vs = (np.ascontiguousarray(t[b, h]) for t in (q, k, v))
+        mb = None if mask is None else np.ascontiguousarray(mask[b])
+        ob = np.zeros((L, d), dtype=dt)
+        lb = np.zeros(L, dtype=dt)
+        fn(L, d, int(seq_lens[b]), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(mb), bias, variant,
+           scale, 0, L, _ptr(ob), _ptr(lb))
+        o[b, h] = ob
+        lse[b, h] = lb
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        list(ex.map(one, pairs))
+    return o, lse
+
+
+def fwd_rows(q, k, v, seq_lens, b: int, h: int, rows, mask=None, bias=BIAS_LOG_SEQLEN,
+             variant=SIGMOID, scale=None, precision="f64"):
+    """Selected output rows of one head: (o [len(rows), d], lse [len(rows)])."""
+    lib = _load()
+    B, H, L, d = _heads(q)
+    dt = _dtype(precision)
+    fn = getattr(lib, "oracle_fwd_rows_" + precision)
+    scale = default_scale(d) if scale is None else scale
+    qs, ks, vs = (np.ascontiguousarray(t[b, h]) for t in (q, k, v))
+    mb = None if mask is None else np.ascontiguousarray(mask[b])
+    rows = list(rows)
+    o = np.zeros((len(rows), d), dtype=dt)
+    lse = np.zeros(len(rows), dtype=dt)
+    one_o = np.zeros((1, d), dtype=dt)
+    one_l = np.zeros(1, dtype=dt)
+    for i, r in enumerate(rows):
+        fn(L, d, int(seq_lens[b]), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(mb), bias, variant,
+           scale, int(r), int(r) + 1, _ptr(one_o), _ptr(one_l))
+        o[i] = one_o[0]
+        lse[i] = one_l[0]
+    return o, lse
+
+
+def fwd_tiled(q, k, v, seq_lens, block_mask=None, block_q=64, block_k=64, mask=None,
+              bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None, precision="f64",
+              threads=None):
+    """Forward by the tiled online algorithm (oracle_fwd_tiled).
+
+    ``block_mask`` [B, Tq, Tk] selects the tiles visited; None visits all.
+    """
+    lib = _load()
+    B, H, L, d = _heads(q)
+    dt = _dtype(precision)
+    fn = getattr(lib, "oracle_fwd_tiled_" + precision)
+    scale = default_scale(d) if scale is None else scale
+    o = np.zeros((B, H, L, d), dtype=dt)
+    lse = np.zeros((B, H, L), dtype=dt)
+
+    def one(bh):
+        b, h = bh
+        qs, ks, vs = (np.ascontiguousarray(t[b, h]) for t in (q, k, v))
+        mb = None if mask is None else np.ascontiguousarray(mask[b])
+        bmb = None if block_mask is None else np.ascontiguousarray(block_mask[b], dtype=np.uint8)
+        ob = np.zeros((L, d), dtype=dt)
+        lb = np.zeros(L, dtype=dt)
+        fn(L, d, int(seq_lens[b]), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(mb), _ptr(bmb),
+           block_q, block_k, bias, variant, scale, _ptr(ob), _ptr(lb))
+        o[b, h] = ob
+        lse[b, h] = lb
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        list(ex.map(one, [(b, h) for b in range(B) for h in range(H)]))
+    return o, lse
+
+
+def bwd(q, k, v, do, seq_lens, mask=None, bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None,
+        precision="f64", threads=None, heads=None):
+    """dQ, dK, dV [B, H, L, d] by the plain definition (oracle_bwd_*_rows)."""
+    lib = _load()
+    B, H, L, d = _heads(q)
+    dt = _dtype(precision)
+    fq = getattr(lib, "oracle_bwd_dq_rows_" + precision)
+    fkv = getattr(lib, "oracle_bwd_dkv_rows_" + precision)
+    scale = default_scale(d) if scale is None else scale
+    dq = np.zeros((B, H, L, d), dtype=dt)
+    dk = np.zeros((B, H, L, d), dtype=dt)
+    dv = np.zeros((B, H, L, d), dtype=dt)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+
+    def one(bh):
+        b, h = bh
+        qs, ks, vs, ds = (np.ascontiguousarray(t[b, h]) for t in (q, k, v, do))
+        mb = None if mask is None else np.ascontiguousarray(mask[b])
+        gq = np.zeros((L, d), dtype=dt)
+        gk = np.zeros((L, d), dtype=dt)
+        gv = np.zeros((L, d), dtype=dt)
+        n = int(seq_lens[b])
+        fq(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(mb), bias, variant, scale,
+           0, L, _ptr(gq))
+        fkv(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(mb), bias, variant, scale,
+            0, L, _ptr(gk), _ptr(gv))
+        dq[b, h], dk[b, h], dv[b, h] = gq, gk, gv
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        list(ex.map(one, pairs))
+    return dq, dk, dv
+
+
+def bwd_rows(q, k, v, do, seq_lens, b: int, h: int, q_rows, k_rows, mask=None,
+             bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None, precision="f64"):
+    """Selected rows of one head: (dq [len(q_rows), d], dk, dv [len(k_rows), d])."""
+    lib = _load()
+    B, H, L, d = _heads(q)
+    dt = _dtype(precision)
+    fq = getattr(lib, "oracle_bwd_dq_rows_" + precision)
+    fkv = getattr(lib, "oracle_bwd_dkv_rows_" + precision)
+    scale = default_scale(d) if scale is None else scale
+    qs, ks, vs, ds = (np.ascontiguousarray(t[b, h]) for t in (q, k, v, do))
+    mb = None if mask is None else np.ascontiguousarray(mask[b])
+    n = int(seq_lens[b])
+    q_rows, k_rows = list(q_rows), list(k_rows)
+    dq = np.zeros((len(q_rows), d), dtype=dt)
+    for i, r in enumerate(q_rows):
+        row = np.zeros((1, d), dtype=dt)
+        fq(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(mb), bias, variant, scale,
+           int(r), int(r) + 1, _ptr(row))
+        dq[i] = row[0]
+    dk = np.zeros((len(k_rows), d), dtype=dt)
+    dv = np.zeros((len(k_rows), d), dtype=dt)
+    if k_rows:
+        # One call per contiguous run keeps the softmax row statistics shared.
+        lo, hi = min(k_rows), max(k_rows) + 1
+        gk = np.zeros((hi - lo, d), dtype=dt)
+        gv = np.zeros((hi - lo, d), dtype=dt)
+        fkv(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(mb), bias, variant, scale,
+            lo, hi, _ptr(gk), _ptr(gv))
+        for i, c in enumerate(k_rows):
+            dk[i] = gk[c - lo]
+            dv[i] = gv[c - lo]
+    return dq, dk, dv
