@@ -1,0 +1,226 @@
+"""Benchmark: valid-work TFLOP/s of padded varlen sigmoid attention, forward
+plus backward, on one MI355X.
+
+One step = the whole hot path over one synthetic single-cell-shaped batch
+(B32 H8 d64, log-normal lengths with median 800 clipped to [200, 2048], padded
+to the batch maximum, block 128, bias -ln n):
+  blockmask_build (from seq_lens) -> sigattn_fwd -> sigattn_bwd_dkdv -> sigattn_bwd_dq
+Inputs are resident in HBM before the timed region.  Valid FLOPs count only
+attended (query, key) pairs: 4 d per pair per head forward, 10 d backward.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "valid-work TFLOP/s + % bf16 MFMA peak, padded varlen sigmoid attn fwd/bwd"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "fwd": "varlen_attention_amd/csrc/fwd.hip",
+    "bwd_dkdv": "varlen_attention_amd/csrc/bwd.hip",
+    "bwd_dq": "varlen_attention_amd/csrc/bwd.hip",
+    "blockmask": "varlen_attention_amd/csrc/blockmask.hip",
+}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest(kernel: str) -> str:
+    paths = [KERNEL_SOURCES[kernel], "varlen_attention_amd/csrc/device_common.h"]
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if it still
+    describes the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != source_digest(kernel):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float = 15.0):
+    """The oracle (fp32 statement) timed on host cores over a sample of
+    (batch entry, head) pairs: forward + backward, valid TFLOP/s."""
+    import oracle
+
+    threads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16") or 16))
+    order = np.argsort(w.seq_lens)  # start small to size the sample
+    pairs_all = [(int(b), h) for b in order for h in range(w.H)]
+    # Calibrate on one pair.
+    b0, h0 = pairs_all[len(pairs_all) // 2]
+    t0 = time.perf_counter()
+    oracle.fwd(w.q, w.k, w.v, w.seq_lens, heads=[(b0, h0)], precision="f32", threads=1)
+    oracle.bwd(w.q, w.k, w.v, w.do, w.seq_lens, heads=[(b0, h0)], precision="f32", threads=1)
+    per_pair = max(time.perf_counter() - t0, 1e-3) / float(w.seq_lens[b0]) ** 2
+    # Pick pairs spread over the batch until the estimated CPU time fills the budget.
+    rng = np.random.default_rng(0)
+    pairs, est = [], 0.0
+    for idx in rng.permutation(len(pairs_all)):
+        b, h = pairs_all[idx]
+        cost = per_pair * float(w.seq_lens[b]) ** 2 / threads
+        if est + cost > budget_s and pairs:
+            break
+        pairs.append((b, h))
+        est += cost
+    t0 = time.perf_counter()
+    oracle.fwd(w.q, w.k, w.v, w.seq_lens, heads=pairs, precision="f32", threads=threads)
+    oracle.bwd(w.q, w.k, w.v, w.do, w.seq_lens, heads=pairs, precision="f32", threads=threads)
+    dt = time.perf_counter() - t0
+    flops = sum(14.0 * w.d * float(w.seq_lens[b]) ** 2 for b, _ in pairs)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(pairs)} of {w.B * w.H} (batch entry, head) pairs of the same "
+                      f"workload, forward + backward, fp32 oracle, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by batch entry and head without any exchange).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synthetic as syn
+    import varlen_attention_amd as va
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = syn.single_cell(args.seed, tensors=("q", "k", "v", "do"))
+    workload = "single_cell_b32h8d64_lognormal800"
+    B, H, L, d = w.B, w.H, w.L, w.d
+    pairs = w.valid_pairs  # summed over the batch, per head
+    log(f"workload {workload}: B={B} H={H} L={L} d={d} sum_n={int(w.seq_lens.sum())} "
+        f"valid pairs/head={pairs}")
+
+    def gpu(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (gpu(t) for t in (w.q, w.k, w.v, w.do))
+    n = torch.from_numpy(w.seq_lens).to(dev)
+    bq = bk = 128
+    bm = torch.empty((B, va.num_tiles(L, bq), va.num_tiles(L, bk)), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    names = ["blockmask", "fwd", "bwd_dkdv", "bwd_dq"]
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record(stream)
+        mark(0)
+        va.blockmask_build(n, L, bq, bk, out=bm)
+        mark(1)
+        va.sigattn_fwd(q, k, v, n, block_mask=bm, out=o, block_q=bq, block_k=bk)
+        mark(2)
+        va.sigattn_bwd_dkdv(q, k, v, do, n, block_mask=bm, dk=dk, dv=dv, block_q=bq, block_k=bk)
+        mark(3)
+        va.sigattn_bwd_dq(q, k, v, do, n, block_mask=bm, dq=dq, block_q=bq, block_k=bk)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    per_kernel = {nm: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1])
+                                     for s in range(args.steps)]))
+                  for i, nm in enumerate(names)}
+    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step; per kernel (ms): "
+        + ", ".join(f"{k_}={v_:.4f}" for k_, v_ in per_kernel.items()))
+
+    flops_fwd = 4.0 * d * H * pairs
+    flops_bwd = 10.0 * d * H * pairs
+    value = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
+    # Per-kernel algorithmic FLOPs per launch: the GEMMs each kernel's output needs.
+    algo = {"fwd": 4.0 * d * H * pairs, "bwd_dkdv": 8.0 * d * H * pairs,
+            "bwd_dq": 6.0 * d * H * pairs}
+    dominant = max(algo, key=lambda k_: per_kernel[k_])
+    achieved = algo[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
+    traffic = read_traffic(dominant, workload)
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    kernels = {}
+    for nm in names:
+        ent = {"ms": round(per_kernel[nm], 4)}
+        if nm in algo:
+            tf = algo[nm] / (per_kernel[nm] * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 2), frac_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        kernels[nm] = ent
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        cpu = cpu_baseline(w)
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "B": B, "H": H, "L": L, "d": d,
+                   "sum_n": int(w.seq_lens.sum()), "valid_pairs_per_head": int(pairs),
+                   "block": bq, "variant": "sigmoid", "bias": "-ln n", "seed": args.seed,
+                   "step": "blockmask_build + fwd + bwd_dkdv + bwd_dq",
+                   "parallelism": "single GPU"},
+        "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,170 @@
+/*
+ * sigattn.h - C ABI of libsigattn.so: fused, tiled attention over padded
+ * variable-length batches on AMD Instinct MI355X (gfx950).
+ *
+ * Operation (per batch entry b, head h; n = clamp(seq_lens[b], 0, L)):
+ *   valid(r, c) = r < n and c < n and (mask == NULL or mask[b, r, c] != 0)
+ *                 and (block_mask == NULL or its entry for the tile of (r, c) is 1)
+ *   s[r, c]     = scale * <q_r, k_c> + beta
+ *   beta        = 0 (NONE), -ln n (LOG_SEQLEN), -ln L (LOG_PADLEN)
+ *   SIGMOID     o_r = sum_c sigma(s[r, c]) v_c
+ *               ("Better Models, Faster Training: Sigmoid Attention for
+ *               single-cell Foundation Models", section 2.A, with the bias
+ *               b = -log(n) of the same section)
+ *   SOFTMAX     o_r = sum_c exp(s) v_c / sum_c exp(s)     (Flash Attention page,
+ *               "the mathematics"; computed with a running max and sum)
+ *   SOFTMAX1    o_r = sum_c exp(s) v_c / (1 + sum_c exp(s))  (softmax_1 /
+ *               QuietAttention page, "Proposition")
+ * Sums run over valid (r, c) only.  Padded query rows (r >= n) and rows with
+ * no valid key produce exactly zero output and zero gradients.  The content
+ * of padded rows of Q, K, V and dO is never read, so it may hold anything,
+ * NaN included.
+ *
+ * Tiles that the binary block mask marks 0 are skipped without loading
+ * anything ("Binary Block Masking", "Presentation" / "How it works"; padded
+ * blocks on the query and key sides, single-cell page section 2.C).
+ *
+ * Conventions shared by every entry point:
+ * - Device pointers are marked [device], host pointers [host].  The caller
+ *   owns every buffer.  The library allocates nothing and never
+ *   synchronises: each call enqueues its kernels on `stream` (a hipStream_t;
+ *   NULL is the default stream) and returns.  Inputs are never modified.
+ * - Return value: SIGATTN_OK or a negative sigattn_status.  Argument errors
+ *   are detected on the host before anything is enqueued; SIGATTN_ERR_LAUNCH
+ *   reports a failed kernel launch.  sigattn_last_error() gives a message for
+ *   the last failure on the calling thread.
+ * - seq_lens lives in device memory, so its values are not checked on the
+ *   host; kernels clamp each length into [0, L].
+ */
+#ifndef SIGATTN_H
+#define SIGATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SIGATTN_SIGMOID = 0,
+    SIGATTN_SOFTMAX = 1,
+    SIGATTN_SOFTMAX1 = 2
+} sigattn_variant;
+
+typedef enum {
+    SIGATTN_BIAS_NONE = 0,
+    SIGATTN_BIAS_LOG_SEQLEN = 1, /* beta = -ln(n), n the unpadded length of the sequence */
+    SIGATTN_BIAS_LOG_PADLEN = 2  /* beta = -ln(L), L the padded length */
+} sigattn_bias_mode;
+
+typedef enum {
+    SIGATTN_OK = 0,
+    SIGATTN_ERR_INVALID_ARG = -1, /* null required pointer, non-positive size, bad enum */
+    SIGATTN_ERR_UNSUPPORTED = -2, /* head dim or block size not built, strides not unit in d */
+    SIGATTN_ERR_ALIGNMENT = -3,   /* pointer or stride not 16-byte aligned */
+    SIGATTN_ERR_LAUNCH = -4       /* HIP reported an error while enqueuing */
+} sigattn_status;
+
+/*
+ * Problem shape.  Q, K, V and dO share one layout, O, dQ, dK and dV another;
+ * both are [B, H, L, d] with the head dimension contiguous (stride 1) and the
+ * other strides given in elements.  A zero o_stride_* triple means "same as
+ * the input strides".  Every base pointer and every stride must be a multiple
+ * of 16 bytes (8 bf16 elements).
+ */
+typedef struct {
+    int32_t B, H, L, d;       /* batch, heads, padded length, head dim (64 or 128) */
+    int64_t stride_b, stride_h, stride_l;       /* Q, K, V, dO */
+    int64_t o_stride_b, o_stride_h, o_stride_l; /* O, dQ, dK, dV (0,0,0: as inputs) */
+    float scale;              /* score scale; <= 0 selects 1/sqrt(d) */
+    int32_t block_q, block_k; /* block-mask tile: 32, 64 or 128 rows / columns */
+} sigattn_shape;
+
+/*
+ * blockmask_build - binary block matrix of one batch (Binary Block Masking,
+ * "Presentation": keep a block when it holds at least one active element;
+ * built once and shared by every head and layer).
+ *
+ *   seq_lens    [device] int32 [B]
+ *   mask        [device] uint8 [B, L, L] row-major, non-zero = may attend;
+ *               NULL for padding-only batches.  Must be 16-byte aligned.
+ *   block_mask  [device] uint8 [B, Tq, Tk] output, Tq = ceil(L / block_q),
+ *               Tk = ceil(L / block_k); every entry is written with 0 or 1.
+ * Entry (b, i, j) is 1 iff some r in [i*block_q, min((i+1)*block_q, L)) and c
+ * in [j*block_k, min((j+1)*block_k, L)) is valid (definition above without
+ * the block-mask term).  With mask == NULL this is i*block_q < n && j*block_k < n.
+ * Errors: INVALID_ARG (null seq_lens/block_mask, B or L <= 0), UNSUPPORTED
+ * (block size not 32/64/128), ALIGNMENT (mask not 16-byte aligned), LAUNCH.
+ */
+int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, int32_t B, int32_t L,
+                    int32_t block_q, int32_t block_k, uint8_t *block_mask, void *stream);
+
+/*
+ * sigattn_fwd - forward pass (single-cell page section 2.C: one fused kernel,
+ * block-sparse over padding; Flash Attention page: tiles staged on chip, K/V
+ * streamed, online softmax for the softmax variants).
+ *
+ *   shape       [host]   see sigattn_shape
+ *   q, k, v     [device] bf16 [B, H, L, d] (input layout)
+ *   seq_lens    [device] int32 [B]
+ *   block_mask  [device] uint8 [B, Tq, Tk] from blockmask_build with the same
+ *               block sizes, or NULL: tiles are then chosen from seq_lens
+ *               alone.  Required when mask != NULL.
+ *   mask        [device] uint8 [B, L, L] or NULL (element mask, all heads)
+ *   o           [device] bf16 [B, H, L, d] (output layout), fully written
+ *   lse         [device] float [B, H, L] contiguous, or NULL.  Softmax
+ *               variants write the natural log of each row's denominator
+ *               (-inf for padded rows and, for SOFTMAX, rows without a valid
+ *               key); SIGMOID does not write it.
+ * Accumulation is fp32; the weights are rounded to bf16 before the product
+ * with V and the output is rounded to bf16 (round to nearest even).
+ * Errors: INVALID_ARG, UNSUPPORTED (d not 64/128, block size), ALIGNMENT, LAUNCH.
+ */
+int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+                const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
+                int32_t bias_mode, int32_t variant, void *o, float *lse, void *stream);
+
+/*
+ * sigattn_bwd - gradients dQ, dK, dV of sum(dO * O) for the SIGMOID variant
+ * (single-cell page section 2.C: two kernels, one for dQ and one for dK/dV,
+ * no atomics, scores and weights recomputed on the fly; section 2.B: the
+ * Jacobian of sigmoid attention is diagonal, dS = dP * sigma * (1 - sigma)).
+ *
+ *   q, k, v, dout   [device] bf16 [B, H, L, d] (input layout)
+ *   seq_lens, block_mask, mask: as for sigattn_fwd
+ *   dq, dk, dv      [device] bf16 [B, H, L, d] (output layout), fully written;
+ *                   rows >= n are 0.
+ * The two kernels write disjoint outputs and use no atomics, so results are
+ * bit-for-bit reproducible.
+ * Errors: as sigattn_fwd; UNSUPPORTED for a variant other than SIGMOID.
+ */
+int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+                const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
+                const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dq, void *dk,
+                void *dv, void *stream);
+
+/*
+ * sigattn_bwd_dkdv / sigattn_bwd_dq - the two halves of sigattn_bwd, each one
+ * kernel launch (single-cell page section 2.C: the backward pass is split
+ * into a kernel for the K/V gradients and a kernel for the Q gradients).
+ * Arguments, layouts and errors as sigattn_bwd; sigattn_bwd_dkdv writes only
+ * dk and dv, sigattn_bwd_dq writes only dq.  Useful when only one side needs
+ * gradients, and to time the two kernels apart.
+ */
+int sigattn_bwd_dkdv(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+                     const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
+                     const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dk,
+                     void *dv, void *stream);
+int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+                   const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
+                   const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dq,
+                   void *stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char *sigattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIGATTN_H */

@@ -1,0 +1,104 @@
+"""The C-ABI library loads on the CPU, exports every function that
+include/sigattn.h declares, and rejects bad arguments on the host before
+anything reaches the GPU (none of these calls launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sigattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import varlen_attention_amd as va
+    if not os.path.exists(va.LIB_PATH):
+        pytest.fail("libsigattn.so is not built (python -m varlen_attention_amd.build)")
+    return va.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["blockmask_build", "sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq",
+         "sigattn_last_error"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _shape(va, **kw):
+    base = dict(B=2, H=2, L=100, d=64, stride_b=2 * 100 * 64, stride_h=100 * 64, stride_l=64,
+                o_stride_b=0, o_stride_h=0, o_stride_l=0, scale=0.0, block_q=128, block_k=128)
+    base.update(kw)
+    return va.Shape(**base)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails first
+
+
+def _fwd(lib, va, shape, q=FAKE, k=FAKE, v=FAKE, seq=FAKE, bm=None, mask=None, bias=1, var=0,
+         o=FAKE, lse=None):
+    return lib.sigattn_fwd(ctypes.byref(shape) if shape is not None else None, q, k, v, seq, bm,
+                           mask, bias, var, o, lse, None)
+
+
+def test_forward_argument_errors(lib):
+    import varlen_attention_amd as va
+    assert _fwd(lib, va, None) == va.ERR_INVALID_ARG
+    assert b"shape" in lib.sigattn_last_error()
+    assert _fwd(lib, va, _shape(va, d=96)) == va.ERR_UNSUPPORTED
+    assert _fwd(lib, va, _shape(va, B=0)) == va.ERR_INVALID_ARG
+    assert _fwd(lib, va, _shape(va, block_q=48)) == va.ERR_UNSUPPORTED
+    assert _fwd(lib, va, _shape(va), q=None) == va.ERR_INVALID_ARG
+    assert _fwd(lib, va, _shape(va), seq=None) == va.ERR_INVALID_ARG
+    assert _fwd(lib, va, _shape(va), o=None) == va.ERR_INVALID_ARG
+    assert _fwd(lib, va, _shape(va), bias=7) == va.ERR_INVALID_ARG
+    assert _fwd(lib, va, _shape(va), var=5) == va.ERR_INVALID_ARG
+    assert _fwd(lib, va, _shape(va), mask=FAKE) == va.ERR_INVALID_ARG  # mask needs block mask
+    assert _fwd(lib, va, _shape(va), k=ctypes.c_void_p(0x10008)) == va.ERR_ALIGNMENT
+    assert _fwd(lib, va, _shape(va, stride_l=68)) == va.ERR_ALIGNMENT
+    assert _fwd(lib, va, _shape(va, stride_l=32)) == va.ERR_INVALID_ARG
+    assert _fwd(lib, va, _shape(va), lse=ctypes.c_void_p(0x10002)) == va.ERR_ALIGNMENT
+
+
+def test_backward_argument_errors(lib):
+    import varlen_attention_amd as va
+    sh = _shape(va)
+    args = [FAKE] * 4
+    assert lib.sigattn_bwd(ctypes.byref(sh), *args, FAKE, None, None, 1, 1, FAKE, FAKE, FAKE,
+                           None) == va.ERR_UNSUPPORTED  # softmax backward not built
+    assert lib.sigattn_bwd(ctypes.byref(sh), *args, FAKE, None, None, 1, 0, FAKE, None, FAKE,
+                           None) == va.ERR_INVALID_ARG
+    sh128 = _shape(va, d=128, L=0)
+    assert lib.sigattn_bwd(ctypes.byref(sh128), *args, FAKE, None, None, 1, 0, FAKE, FAKE, FAKE,
+                           None) == va.ERR_INVALID_ARG
+
+
+def test_blockmask_argument_errors(lib):
+    import varlen_attention_amd as va
+    assert lib.blockmask_build(None, None, 2, 100, 32, 32, FAKE, None) == va.ERR_INVALID_ARG
+    assert lib.blockmask_build(FAKE, None, 2, 100, 32, 32, None, None) == va.ERR_INVALID_ARG
+    assert lib.blockmask_build(FAKE, None, 0, 100, 32, 32, FAKE, None) == va.ERR_INVALID_ARG
+    assert lib.blockmask_build(FAKE, None, 2, 100, 16, 32, FAKE, None) == va.ERR_UNSUPPORTED
+    assert lib.blockmask_build(FAKE, ctypes.c_void_p(0x10001), 2, 100, 32, 32, FAKE,
+                               None) == va.ERR_ALIGNMENT
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    import varlen_attention_amd as va
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        va.sigattn_fwd(q, q, q, torch.zeros(1, dtype=torch.int32))

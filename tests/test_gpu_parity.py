@@ -1,0 +1,380 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle on the same
+seeded bf16 inputs.  Block masks must match bit for bit; outputs and
+gradients within max abs 1e-2 and relative L2 5e-3 on valid rows, with padded
+rows exactly zero.  Small cases span several tiles and a ragged tail; the
+benchmark workloads are checked at full size on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+from _gpu import (assert_close, assert_rows, gpu_f64, row_valid, say, to_gpu, to_gpu_bf16)
+
+pytestmark = pytest.mark.gpu
+
+SIGMOID, SOFTMAX, SOFTMAX1 = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def va():
+    import varlen_attention_amd as va
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    va.load_library()
+    return va
+
+
+def _inputs(seed, B, H, L, d, seq_lens, names=("q", "k", "v")):
+    rng = np.random.default_rng(seed)
+    return [syn.random_tensor(rng, (B, H, L, d)) for _ in names]
+
+
+def _bm(va, n_gpu, L, bq, bk, mask_gpu=None):
+    out = va.blockmask_build(n_gpu, L, bq, bk, mask=mask_gpu)
+    torch.cuda.synchronize()
+    return out
+
+
+# --------------------------------------------------------------- block mask
+@pytest.mark.parametrize("L,bq,bk", [(128, 32, 32), (100, 64, 32), (1584, 128, 128),
+                                     (257, 32, 128), (1, 128, 64)])
+def test_blockmask_padding_bitexact(va, L, bq, bk):
+    rng = np.random.default_rng(L + bq)
+    n = rng.integers(-2, L + 3, size=7).astype(np.int32)
+    n[:3] = [0, L, 1]
+    say(f"blockmask padding L={L} bq={bq} bk={bk}")
+    got = _bm(va, to_gpu(n, torch.int32), L, bq, bk).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.blockmask(n, None, L, bq, bk))
+
+
+@pytest.mark.parametrize("L,bq,bk,density", [(96, 32, 32, 0.01), (300, 64, 128, 0.002),
+                                             (1031, 128, 32, 0.0003), (77, 32, 64, 0.5)])
+def test_blockmask_arbitrary_mask_bitexact(va, L, bq, bk, density):
+    rng = np.random.default_rng(L)
+    B = 4
+    n = np.array([L, L // 2, 0, L - 5], np.int32)
+    mask = (rng.random((B, L, L)) < density).astype(np.uint8)
+    mask[0, L - 1, L - 1] = 1  # corner of the clipped last tile
+    say(f"blockmask mask L={L} bq={bq} bk={bk}")
+    got = _bm(va, to_gpu(n, torch.int32), L, bq, bk, to_gpu(mask, torch.uint8)).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.blockmask(n, mask, L, bq, bk))
+
+
+def test_blockmask_long_documents_full_size(va):
+    w = syn.long_packed_docs(tensors=())
+    say(f"blockmask {w.name} L={w.L}")
+    got = _bm(va, to_gpu(w.seq_lens, torch.int32), w.L, 128, 128,
+              to_gpu(w.mask, torch.uint8)).cpu().numpy()
+    want = oracle.blockmask(w.seq_lens, w.mask, w.L, 128, 128)
+    np.testing.assert_array_equal(got, want)
+    assert int(want.sum()) == 885
+
+
+# --------------------------------------------------------------- forward, small
+FWD_CASES = [
+    # d, L, block_q, block_k, variant, bias, with_mask
+    (64, 300, 128, 128, SIGMOID, 1, False),
+    (64, 300, 64, 64, SIGMOID, 2, False),
+    (64, 211, 32, 32, SIGMOID, 0, True),
+    (128, 300, 128, 128, SIGMOID, 1, False),
+    (128, 257, 128, 64, SIGMOID, 1, True),
+    (64, 300, 128, 128, SOFTMAX, 0, False),
+    (64, 200, 64, 32, SOFTMAX, 1, True),
+    (128, 300, 128, 128, SOFTMAX, 0, True),
+    (64, 300, 128, 128, SOFTMAX1, 0, False),
+    (128, 190, 32, 64, SOFTMAX1, 2, True),
+]
+
+
+@pytest.mark.parametrize("d,L,bq,bk,variant,bias,with_mask", FWD_CASES)
+def test_forward_small(va, d, L, bq, bk, variant, bias, with_mask):
+    B, H = 4, 2
+    n = np.array([L, L - 37, 1, 0], np.int32)
+    q, k, v = _inputs(1000 + d + L + variant, B, H, L, d, n)
+    rng = np.random.default_rng(7)
+    mask = None
+    if with_mask:
+        mask = (rng.random((B, L, L)) < 0.3).astype(np.uint8)
+        mask[0, 5, :] = 0  # a valid query row with no valid key
+        mask[1, :, : L // 2] = 0  # whole tiles empty
+    say(f"fwd small d={d} L={L} bq={bq} bk={bk} variant={variant} bias={bias} mask={with_mask}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = None if mask is None else to_gpu(mask, torch.uint8)
+    bm = _bm(va, n_gpu, L, bq, bk, m_gpu) if with_mask else None
+    o, lse = va.sigattn_fwd(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v), n_gpu,
+                            block_mask=bm, mask=m_gpu, bias=bias, variant=variant,
+                            block_q=bq, block_k=bk, return_lse=True)
+    torch.cuda.synchronize()
+    want, want_lse = oracle.fwd(q, k, v, n, mask=mask, bias=bias, variant=variant)
+    assert_rows(gpu_f64(o), want, n, "O")
+    if variant != SIGMOID:
+        got_lse = lse.cpu().numpy().astype(np.float64)
+        valid = row_valid(n, B, L)
+        for b in range(B):
+            for h in range(H):
+                g, wl = got_lse[b, h], want_lse[b, h]
+                assert np.array_equal(np.isneginf(g), np.isneginf(wl))
+                fin = np.isfinite(wl)
+                assert np.all(np.abs(g[fin] - wl[fin]) <= 1e-3 * np.maximum(1, np.abs(wl[fin])))
+                assert np.all(np.isneginf(g[~valid[b]]))
+
+
+def test_forward_block_mask_optional_for_padding(va):
+    """Without a block mask the tiles come from seq_lens; results are identical."""
+    B, H, L, d = 3, 2, 400, 64
+    n = np.array([400, 129, 7], np.int32)
+    q, k, v = (to_gpu_bf16(t) for t in _inputs(5, B, H, L, d, n))
+    n_gpu = to_gpu(n, torch.int32)
+    bm = _bm(va, n_gpu, L, 128, 128)
+    o1 = va.sigattn_fwd(q, k, v, n_gpu, block_mask=bm)
+    o2 = va.sigattn_fwd(q, k, v, n_gpu)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_forward_poisoned_padding_and_determinism(va):
+    """NaN in every padded row of Q, K, V changes nothing, and two runs agree bitwise."""
+    B, H, L, d = 3, 2, 333, 128
+    n = np.array([333, 200, 64], np.int32)
+    q, k, v = _inputs(11, B, H, L, d, n)
+    qp, kp, vp = q.copy(), k.copy(), v.copy()
+    for t in (qp, kp, vp):
+        for b in range(B):
+            t[b, :, n[b]:] = np.uint16(0x7FC0)
+    n_gpu = to_gpu(n, torch.int32)
+    for variant in (SIGMOID, SOFTMAX, SOFTMAX1):
+        say(f"poison variant={variant}")
+        a = va.sigattn_fwd(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v), n_gpu, variant=variant)
+        bq, bk_, bv = to_gpu_bf16(qp), to_gpu_bf16(kp), to_gpu_bf16(vp)
+        b1 = va.sigattn_fwd(bq, bk_, bv, n_gpu, variant=variant)
+        b2 = va.sigattn_fwd(bq, bk_, bv, n_gpu, variant=variant)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b1.view(torch.int16))
+        assert torch.equal(b1.view(torch.int16), b2.view(torch.int16))
+
+
+def test_forward_strided_views(va):
+    """Q, K, V as views of a packed [B, L, 3, H, d] tensor; O written with its own strides."""
+    B, H, L, d = 2, 4, 260, 64
+    n = np.array([260, 100], np.int32)
+    rng = np.random.default_rng(21)
+    packed = syn.random_tensor(rng, (B, L, 3, H, d))
+    t = to_gpu_bf16(packed)
+    q, k, v = (t[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+    out_store = torch.zeros(B, L, H, d, dtype=torch.bfloat16, device="cuda")
+    o = out_store.permute(0, 2, 1, 3)
+    n_gpu = to_gpu(n, torch.int32)
+    va.sigattn_fwd(q, k, v, n_gpu, out=o)
+    torch.cuda.synchronize()
+    qn, kn, vn = (np.ascontiguousarray(packed[:, :, i].transpose(0, 2, 1, 3)) for i in range(3))
+    want, _ = oracle.fwd(qn, kn, vn, n)
+    assert_rows(gpu_f64(o), want, n, "O (strided)")
+
+
+def test_softmax1_equals_softmax_with_zero_key_on_gpu(va):
+    """softmax_1 page: a prepended zero key with a zero value adds 1 to each denominator."""
+    B, H, L, d = 2, 2, 190, 64
+    n = np.array([190, 77], np.int32)
+    q, k, v = _inputs(31, B, H, L, d, n)
+    z = np.zeros((B, H, 1, d), np.uint16)
+    q2, k2, v2 = (np.concatenate([z, t], axis=2) for t in (q, k, v))
+    n_gpu = to_gpu(n, torch.int32)
+    o1 = va.sigattn_fwd(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v), n_gpu, variant=SOFTMAX1,
+                        bias=0)
+    o2 = va.sigattn_fwd(to_gpu_bf16(q2), to_gpu_bf16(k2), to_gpu_bf16(v2),
+                        to_gpu(n + 1, torch.int32), variant=SOFTMAX, bias=0)
+    torch.cuda.synchronize()
+    a, b = gpu_f64(o1), gpu_f64(o2)
+    for bb in range(B):
+        assert_close(a[bb, :, : n[bb]], b[bb, :, 1 : n[bb] + 1], "softmax1 vs prepended zero")
+
+
+def test_unit_values_row_sums(va):
+    B, H, L, d = 2, 2, 300, 64
+    n = np.array([300, 150], np.int32)
+    q, k, _ = _inputs(41, B, H, L, d, n)
+    v = syn.f32_to_bf16_bits(np.ones((B, H, L, d), np.float32))
+    n_gpu = to_gpu(n, torch.int32)
+    o = gpu_f64(va.sigattn_fwd(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v), n_gpu,
+                               variant=SOFTMAX, bias=0))
+    o1 = gpu_f64(va.sigattn_fwd(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v), n_gpu,
+                                variant=SOFTMAX1, bias=0))
+    for b in range(B):
+        assert np.abs(o[b, :, : n[b]] - 1).max() <= 2 ** -7
+        assert np.all(o1[b, :, : n[b]] > 0) and np.all(o1[b, :, : n[b]] <= 1)
+
+
+# --------------------------------------------------------------- forward, full size
+def _sample_rows(rng, n, L, count=6):
+    rows = {0, max(n - 1, 0), min(n, L - 1)}
+    rows |= set(rng.integers(0, max(n, 1), size=count).tolist())
+    return sorted(r for r in rows if r < L)
+
+
+def _check_sampled_fwd(va, w, variant=SIGMOID, bias=1, heads=8):
+    n = w.seq_lens
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = None if w.mask is None else to_gpu(w.mask, torch.uint8)
+    bm = _bm(va, n_gpu, w.L, w.block_q, w.block_k, m_gpu)
+    o = va.sigattn_fwd(to_gpu_bf16(w.q), to_gpu_bf16(w.k), to_gpu_bf16(w.v), n_gpu,
+                       block_mask=bm, mask=m_gpu, bias=bias, variant=variant,
+                       block_q=w.block_q, block_k=w.block_k)
+    torch.cuda.synchronize()
+    og = gpu_f64(o)
+    valid = row_valid(n, w.B, w.L)
+    assert np.all(og[np.broadcast_to(~valid[:, None, :], og.shape[:3])] == 0)
+    rng = np.random.default_rng(0)
+    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(heads)]
+    pairs += [(int(np.argmax(n)), 0), (int(np.argmin(n)), w.H - 1)]
+    got, want = [], []
+    for b, h in pairs:
+        rows = _sample_rows(rng, int(n[b]), w.L)
+        ref, _ = oracle.fwd_rows(w.q, w.k, w.v, n, b, h, rows, mask=w.mask, bias=bias,
+                                 variant=variant)
+        got.append(og[b, h, rows])
+        want.append(ref)
+    return assert_close(np.concatenate(got), np.concatenate(want), f"O sampled {w.name}")
+
+
+@pytest.fixture(scope="module")
+def single_cell_inputs():
+    return syn.single_cell_backward(0)  # same lengths as the forward workload; carries dO
+
+
+def test_forward_single_cell_full_size(va, single_cell_inputs):
+    w = single_cell_inputs
+    say(f"fwd full {w.name} L={w.L}")
+    _check_sampled_fwd(va, w)
+
+
+def test_forward_single_cell_variants_full_size(va, single_cell_inputs):
+    w = single_cell_inputs
+    for variant in (SOFTMAX, SOFTMAX1):
+        say(f"fwd full variant={variant}")
+        _check_sampled_fwd(va, w, variant=variant, bias=0, heads=4)
+
+
+def test_forward_long_documents_full_size(va):
+    w = syn.long_packed_docs()
+    say(f"fwd full {w.name} L={w.L}")
+    _check_sampled_fwd(va, w)
+
+
+@pytest.mark.parametrize("variant", [SIGMOID, SOFTMAX, SOFTMAX1])
+def test_forward_tiny_workloads(va, variant):
+    w = syn.tiny_variants(0, variant)
+    say(f"fwd tiny variant={variant}")
+    n_gpu = to_gpu(w.seq_lens, torch.int32)
+    bm = _bm(va, n_gpu, w.L, w.block_q, w.block_k)
+    np.testing.assert_array_equal(bm.cpu().numpy(),
+                                  oracle.blockmask(w.seq_lens, None, w.L, 32, 32))
+    o = va.sigattn_fwd(to_gpu_bf16(w.q), to_gpu_bf16(w.k), to_gpu_bf16(w.v), n_gpu,
+                       block_mask=bm, bias=w.bias, variant=variant, block_q=32, block_k=32)
+    torch.cuda.synchronize()
+    want, _ = oracle.fwd_tiled(w.q, w.k, w.v, w.seq_lens,
+                               oracle.blockmask(w.seq_lens, None, w.L, 32, 32), 32, 32,
+                               bias=w.bias, variant=variant)
+    assert_rows(gpu_f64(o), want, w.seq_lens, f"O tiny variant {variant}")
+
+
+# --------------------------------------------------------------- backward
+BWD_CASES = [
+    # d, L, block_q, block_k, bias, with_mask
+    (64, 300, 128, 128, 1, False),
+    (64, 230, 64, 32, 2, True),
+    (64, 150, 32, 64, 0, False),
+    (128, 300, 128, 128, 1, False),
+    (128, 201, 64, 128, 1, True),
+]
+
+
+@pytest.mark.parametrize("d,L,bq,bk,bias,with_mask", BWD_CASES)
+def test_backward_small(va, d, L, bq, bk, bias, with_mask):
+    B, H = 4, 2
+    n = np.array([L, L - 41, 1, 0], np.int32)
+    q, k, v, do = _inputs(2000 + d + L, B, H, L, d, n, names="qkvd")
+    mask = None
+    if with_mask:
+        rng = np.random.default_rng(3)
+        mask = (rng.random((B, L, L)) < 0.4).astype(np.uint8)
+        mask[1, : L // 3, :] = 0
+    say(f"bwd small d={d} L={L} bq={bq} bk={bk} bias={bias} mask={with_mask}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = None if mask is None else to_gpu(mask, torch.uint8)
+    bm = _bm(va, n_gpu, L, bq, bk, m_gpu)
+    dq, dk, dv = va.sigattn_bwd(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v), to_gpu_bf16(do),
+                                n_gpu, block_mask=bm, mask=m_gpu, bias=bias, block_q=bq,
+                                block_k=bk)
+    torch.cuda.synchronize()
+    wq, wk, wv = oracle.bwd(q, k, v, do, n, mask=mask, bias=bias)
+    assert_rows(gpu_f64(dq), wq, n, "dQ")
+    assert_rows(gpu_f64(dk), wk, n, "dK")
+    assert_rows(gpu_f64(dv), wv, n, "dV")
+
+
+def test_backward_poison_determinism_and_identities(va):
+    B, H, L, d = 3, 2, 333, 64
+    n = np.array([333, 180, 40], np.int32)
+    q, k, v, do = _inputs(77, B, H, L, d, n, names="qkvd")
+    poisoned = [t.copy() for t in (q, k, v, do)]
+    for t in poisoned:
+        for b in range(B):
+            t[b, :, n[b]:] = np.uint16(0x7FC0)
+    n_gpu = to_gpu(n, torch.int32)
+    g1 = va.sigattn_bwd(*(to_gpu_bf16(t) for t in (q, k, v, do)), n_gpu)
+    g2 = va.sigattn_bwd(*(to_gpu_bf16(t) for t in poisoned), n_gpu)
+    g3 = va.sigattn_bwd(*(to_gpu_bf16(t) for t in poisoned), n_gpu)
+    o = va.sigattn_fwd(*(to_gpu_bf16(t) for t in (q, k, v)), n_gpu)
+    torch.cuda.synchronize()
+    for a, b, c in zip(g1, g2, g3):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        assert torch.equal(b.view(torch.int16), c.view(torch.int16))
+    # <dQ,Q> = <dK,K> and <dV,V> = <dO,O> from the GPU's own results (no oracle).
+    qf, kf, vf, dof = (syn.bf16_bits_to_f32(t).astype(np.float64) for t in (q, k, v, do))
+    dq, dk, dv = (gpu_f64(t) for t in g1)
+    of = gpu_f64(o)
+    for b in range(B):
+        nb = n[b]
+        for h in range(H):
+            a1 = (dq[b, h, :nb] * qf[b, h, :nb]).sum()
+            a2 = (dk[b, h, :nb] * kf[b, h, :nb]).sum()
+            scale = np.abs(dq[b, h, :nb] * qf[b, h, :nb]).sum()
+            assert abs(a1 - a2) <= 2e-2 * scale + 1e-6
+            e1 = (dv[b, h, :nb] * vf[b, h, :nb]).sum()
+            e2 = (dof[b, h, :nb] * of[b, h, :nb]).sum()
+            scale = np.abs(dv[b, h, :nb] * vf[b, h, :nb]).sum()
+            assert abs(e1 - e2) <= 2e-2 * scale + 1e-6
+
+
+def test_backward_single_cell_full_size(va, single_cell_inputs):
+    w = single_cell_inputs
+    say(f"bwd full {w.name} L={w.L}")
+    n = w.seq_lens
+    n_gpu = to_gpu(n, torch.int32)
+    bm = _bm(va, n_gpu, w.L, 128, 128)
+    dq, dk, dv = va.sigattn_bwd(*(to_gpu_bf16(t) for t in (w.q, w.k, w.v, w.do)), n_gpu,
+                                block_mask=bm)
+    torch.cuda.synchronize()
+    dq, dk, dv = (gpu_f64(t) for t in (dq, dk, dv))
+    valid = row_valid(n, w.B, w.L)
+    pad = np.broadcast_to(~valid[:, None, :], dq.shape[:3])
+    for g in (dq, dk, dv):
+        assert np.all(g[pad] == 0)
+    rng = np.random.default_rng(1)
+    got = {"dq": [], "dk": [], "dv": []}
+    want = {"dq": [], "dk": [], "dv": []}
+    for _ in range(4):
+        b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
+        nb = int(n[b])
+        q_rows = _sample_rows(rng, nb, w.L, 4)
+        k0 = int(rng.integers(0, max(nb - 8, 1)))
+        k_rows = list(range(k0, min(k0 + 8, nb)))
+        rq, rk, rv = oracle.bwd_rows(w.q, w.k, w.v, w.do, n, b, h, q_rows, k_rows)
+        got["dq"].append(dq[b, h, q_rows])
+        want["dq"].append(rq)
+        got["dk"].append(dk[b, h, k_rows])
+        want["dk"].append(rk)
+        got["dv"].append(dv[b, h, k_rows])
+        want["dv"].append(rv)
+    for key in got:
+        assert_close(np.concatenate(got[key]), np.concatenate(want[key]), f"{key} sampled")

@@ -1,0 +1,247 @@
+"""varlen_attention_amd: fused, tiled attention over padded variable-length
+batches on AMD MI355X (gfx950).
+
+Thin Python binding of ``libsigattn.so`` (C ABI in ``include/sigattn.h``).
+Every function here only marshals arguments: it takes torch tensors that
+already live on the GPU, checks their dtypes, devices and layouts, and calls
+the C entry point of the same name on torch's current stream.  All
+computation happens in the HIP kernels; there is no CPU or PyTorch fallback,
+and the import fails loudly if the library has not been built
+(``python -m varlen_attention_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+SIGMOID, SOFTMAX, SOFTMAX1 = 0, 1, 2
+BIAS_NONE, BIAS_LOG_SEQLEN, BIAS_LOG_PADLEN = 0, 1, 2
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_LAUNCH = 0, -1, -2, -3, -4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsigattn.so")
+EXPORTS = ("blockmask_build", "sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq",
+           "sigattn_last_error")
+
+
+class SigattnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+        ("stride_l", ctypes.c_int64),
+        ("o_stride_b", ctypes.c_int64), ("o_stride_h", ctypes.c_int64),
+        ("o_stride_l", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsigattn.so and declare its signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m varlen_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int32
+    lib.blockmask_build.argtypes = [P, P, I, I, I, I, P, P]
+    lib.blockmask_build.restype = ctypes.c_int
+    lib.sigattn_fwd.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, I, I, P, P, P]
+    lib.sigattn_fwd.restype = ctypes.c_int
+    lib.sigattn_bwd.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, I, I, P, P, P, P]
+    lib.sigattn_bwd.restype = ctypes.c_int
+    lib.sigattn_bwd_dkdv.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.sigattn_bwd_dkdv.restype = ctypes.c_int
+    lib.sigattn_bwd_dq.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, I, I, P, P]
+    lib.sigattn_bwd_dq.restype = ctypes.c_int
+    lib.sigattn_last_error.argtypes = []
+    lib.sigattn_last_error.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        msg = load_library().sigattn_last_error().decode()
+        raise SigattnError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+def _layout(ts, names):
+    """All tensors [B, H, L, d] with equal strides and unit stride in d."""
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError(f"{names[0]} must be [B, H, L, d]")
+    for t, nm in zip(ts, names):
+        if t.shape != ref.shape:
+            raise ValueError(f"{nm} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+        if t.stride() != ref.stride():
+            raise ValueError(f"{nm} strides {t.stride()} differ from {names[0]} {ref.stride()}")
+        if t.stride(3) != 1:
+            raise ValueError(f"{nm} must be contiguous along the head dimension")
+    return ref.stride()
+
+
+def _shape(q: torch.Tensor, out_strides, scale, block_q, block_k) -> Shape:
+    B, H, L, d = q.shape
+    s = q.stride()
+    return Shape(B, H, L, d, s[0], s[1], s[2], out_strides[0], out_strides[1], out_strides[2],
+                 float(scale) if scale is not None else 0.0, block_q, block_k)
+
+
+def num_tiles(L: int, block: int) -> int:
+    return -(-L // block)
+
+
+def blockmask_build(seq_lens: torch.Tensor, L: int, block_q: int = 128, block_k: int = 128,
+                    mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Binary block matrix uint8 [B, ceil(L/block_q), ceil(L/block_k)] on the GPU."""
+    _need(seq_lens, "seq_lens", torch.int32)
+    B = seq_lens.shape[0]
+    if mask is not None:
+        _need(mask, "mask", torch.uint8)
+        if tuple(mask.shape) != (B, L, L) or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous uint8 [B, L, L] tensor")
+    shape = (B, num_tiles(L, block_q), num_tiles(L, block_k))
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=seq_lens.device)
+    elif tuple(out.shape) != shape or out.dtype != torch.uint8 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous uint8 tensor of shape {shape}")
+    lib = load_library()
+    _check(lib.blockmask_build(_ptr(seq_lens.contiguous()), _ptr(mask), B, L, block_q, block_k,
+                               _ptr(out), _stream(stream)))
+    return out
+
+
+def sigattn_fwd(q, k, v, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
+                variant=SIGMOID, scale=None, block_q=128, block_k=128, out=None, lse=None,
+                return_lse=False, stream=None):
+    """Forward pass.  q, k, v: bf16 [B, H, L, d] on the GPU (equal strides).
+
+    Returns o (bf16, same shape) or (o, lse) with ``return_lse=True``.
+    """
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16)
+    _layout([q, k, v], ["q", "k", "v"])
+    _need(seq_lens, "seq_lens", torch.int32)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _need(out, "out", torch.bfloat16)
+    if tuple(out.shape) != tuple(q.shape) or out.stride(3) != 1:
+        raise ValueError("out must match q's shape with unit stride in d")
+    B, H, L, d = q.shape
+    if (return_lse or lse is not None) and lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [B, H, L] tensor")
+    if mask is not None:
+        _need(mask, "mask", torch.uint8)
+        if tuple(mask.shape) != (B, L, L) or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous uint8 [B, L, L] tensor")
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8)
+        want = (B, num_tiles(L, block_q), num_tiles(L, block_k))
+        if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
+            raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
+    shape = _shape(q, out.stride(), scale, block_q, block_k)
+    lib = load_library()
+    _check(lib.sigattn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), bias,
+                           variant, _ptr(out), _ptr(lse), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k):
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, nm, torch.bfloat16)
+    _layout([q, k, v, dout], ["q", "k", "v", "dout"])
+    _need(seq_lens, "seq_lens", torch.int32)
+    outs = [torch.empty_like(q, memory_format=torch.contiguous_format) if g is None else g
+            for g in grads]
+    for g in outs:
+        _need(g, "gradient output", torch.bfloat16)
+    _layout(outs, ["gradient output"] * len(outs))
+    B, H, L, d = q.shape
+    if mask is not None:
+        _need(mask, "mask", torch.uint8)
+        if tuple(mask.shape) != (B, L, L) or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous uint8 [B, L, L] tensor")
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8)
+        want = (B, num_tiles(L, block_q), num_tiles(L, block_k))
+        if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
+            raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
+    return outs
+
+
+def sigattn_bwd(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
+                variant=SIGMOID, scale=None, block_q=128, block_k=128, dq=None, dk=None,
+                dv=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * o); bf16 [B, H, L, d] on the GPU."""
+    dq, dk, dv = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dq, dk, dv), block_q,
+                           block_k)
+    shape = _shape(q, dq.stride(), scale, block_q, block_k)
+    _check(load_library().sigattn_bwd(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(seq_lens.contiguous()),
+        _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dq), _ptr(dk), _ptr(dv),
+        _stream(stream)))
+    return dq, dk, dv
+
+
+def sigattn_bwd_dkdv(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
+                     variant=SIGMOID, scale=None, block_q=128, block_k=128, dk=None, dv=None,
+                     stream=None):
+    """The dK/dV half of the backward pass (one kernel): returns (dk, dv)."""
+    dk, dv = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dk, dv), block_q, block_k)
+    shape = _shape(q, dk.stride(), scale, block_q, block_k)
+    _check(load_library().sigattn_bwd_dkdv(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(seq_lens.contiguous()),
+        _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dk), _ptr(dv), _stream(stream)))
+    return dk, dv
+
+
+def sigattn_bwd_dq(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
+                   variant=SIGMOID, scale=None, block_q=128, block_k=128, dq=None, stream=None):
+    """The dQ half of the backward pass (one kernel): returns dq."""
+    (dq,) = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dq,), block_q, block_k)
+    shape = _shape(q, dq.stride(), scale, block_q, block_k)
+    _check(load_library().sigattn_bwd_dq(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(seq_lens.contiguous()),
+        _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dq), _stream(stream)))
+    return dq

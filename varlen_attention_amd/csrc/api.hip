@@ -1,0 +1,218 @@
+// Host side of the C ABI declared in include/sigattn.h: argument validation,
+// shape normalisation and dispatch to the kernel launchers.  Nothing here
+// allocates memory or synchronises; every call only enqueues work on the
+// caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/sigattn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return SIGATTN_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool block_size_ok(int b) { return b == 32 || b == 64 || b == 128; }
+
+int launch_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(SIGATTN_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Shared checks of sigattn_fwd / sigattn_bwd; fills the common parameter block.
+int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inputs,
+                    void *const *outputs, int n_outputs, const int32_t *seq_lens,
+                    const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode,
+                    int32_t variant, sigattn::AttnParams *p) {
+    if (s == nullptr) return fail(SIGATTN_ERR_INVALID_ARG, "shape is NULL");
+    if (s->B <= 0 || s->H <= 0 || s->L <= 0)
+        return fail(SIGATTN_ERR_INVALID_ARG, "B, H and L must be positive (got %d, %d, %d)",
+                    s->B, s->H, s->L);
+    if (s->B > 65535 || s->H > 65535)
+        return fail(SIGATTN_ERR_UNSUPPORTED, "B and H must be at most 65535");
+    if (s->d != 64 && s->d != 128)
+        return fail(SIGATTN_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", s->d);
+    if (!block_size_ok(s->block_q) || !block_size_ok(s->block_k))
+        return fail(SIGATTN_ERR_UNSUPPORTED, "block sizes must be 32, 64 or 128 (got %d, %d)",
+                    s->block_q, s->block_k);
+    if (bias_mode < SIGATTN_BIAS_NONE || bias_mode > SIGATTN_BIAS_LOG_PADLEN)
+        return fail(SIGATTN_ERR_INVALID_ARG, "unknown bias mode %d", bias_mode);
+    if (variant < SIGATTN_SIGMOID || variant > SIGATTN_SOFTMAX1)
+        return fail(SIGATTN_ERR_INVALID_ARG, "unknown variant %d", variant);
+    if (seq_lens == nullptr) return fail(SIGATTN_ERR_INVALID_ARG, "seq_lens is NULL");
+    for (int i = 0; i < n_inputs; ++i)
+        if (inputs[i] == nullptr) return fail(SIGATTN_ERR_INVALID_ARG, "input %d is NULL", i);
+    for (int i = 0; i < n_outputs; ++i)
+        if (outputs[i] == nullptr) return fail(SIGATTN_ERR_INVALID_ARG, "output %d is NULL", i);
+    if (mask != nullptr && block_mask == nullptr)
+        return fail(SIGATTN_ERR_INVALID_ARG, "an element mask needs its block mask");
+    for (int i = 0; i < n_inputs; ++i)
+        if (!aligned16(inputs[i]))
+            return fail(SIGATTN_ERR_ALIGNMENT, "input %d is not 16-byte aligned", i);
+    for (int i = 0; i < n_outputs; ++i)
+        if (!aligned16(outputs[i]))
+            return fail(SIGATTN_ERR_ALIGNMENT, "output %d is not 16-byte aligned", i);
+    int64_t osb = s->o_stride_b, osh = s->o_stride_h, osl = s->o_stride_l;
+    if (osb == 0 && osh == 0 && osl == 0) {
+        osb = s->stride_b;
+        osh = s->stride_h;
+        osl = s->stride_l;
+    }
+    const int64_t strides[6] = {s->stride_b, s->stride_h, s->stride_l, osb, osh, osl};
+    for (int i = 0; i < 6; ++i) {
+        if (strides[i] < 0) return fail(SIGATTN_ERR_INVALID_ARG, "negative stride");
+        if (strides[i] % 8 != 0)
+            return fail(SIGATTN_ERR_ALIGNMENT, "stride %lld is not a multiple of 8 elements",
+                        (long long)strides[i]);
+    }
+    if (s->stride_l < s->d || osl < s->d)
+        return fail(SIGATTN_ERR_INVALID_ARG, "row stride smaller than the head dimension");
+    p->seq_lens = seq_lens;
+    p->block_mask = block_mask;
+    p->mask = mask;
+    p->sb = s->stride_b;
+    p->sh = s->stride_h;
+    p->sl = s->stride_l;
+    p->osb = osb;
+    p->osh = osh;
+    p->osl = osl;
+    p->B = s->B;
+    p->H = s->H;
+    p->L = s->L;
+    p->d = s->d;
+    p->block_q = s->block_q;
+    p->block_k = s->block_k;
+    p->Tq = (s->L + s->block_q - 1) / s->block_q;
+    p->Tk = (s->L + s->block_k - 1) / s->block_k;
+    p->scale = s->scale > 0.0f ? s->scale : 1.0f / sqrtf((float)s->d);
+    p->bias_mode = bias_mode;
+    p->variant = variant;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, int32_t B, int32_t L,
+                    int32_t block_q, int32_t block_k, uint8_t *block_mask, void *stream) {
+    if (seq_lens == nullptr || block_mask == nullptr)
+        return fail(SIGATTN_ERR_INVALID_ARG, "seq_lens and block_mask must not be NULL");
+    if (B <= 0 || L <= 0) return fail(SIGATTN_ERR_INVALID_ARG, "B and L must be positive");
+    if (B > 65535) return fail(SIGATTN_ERR_UNSUPPORTED, "B must be at most 65535");
+    if (!block_size_ok(block_q) || !block_size_ok(block_k))
+        return fail(SIGATTN_ERR_UNSUPPORTED, "block sizes must be 32, 64 or 128 (got %d, %d)",
+                    block_q, block_k);
+    if (mask != nullptr && !aligned16(mask))
+        return fail(SIGATTN_ERR_ALIGNMENT, "mask is not 16-byte aligned");
+    return launch_status(sigattn::launch_blockmask(seq_lens, mask, B, L, block_q, block_k,
+                                                   block_mask, (hipStream_t)stream),
+                         "blockmask_build");
+}
+
+int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+                const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
+                int32_t bias_mode, int32_t variant, void *o, float *lse, void *stream) {
+    sigattn::AttnParams p = {};
+    const void *inputs[3] = {q, k, v};
+    void *outputs[1] = {o};
+    int st = check_attention(shape, inputs, 3, outputs, 1, seq_lens, block_mask, mask,
+                             bias_mode, variant, &p);
+    if (st != SIGATTN_OK) return st;
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+        return fail(SIGATTN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    return launch_status(sigattn::launch_fwd(p, (hipStream_t)stream), "sigattn_fwd");
+}
+
+}  // extern "C"
+
+namespace {
+
+enum BwdParts { kPartDkdv = 1, kPartDq = 2 };
+
+int backward(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+             const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
+             const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dq, void *dk,
+             void *dv, void *stream, int parts, const char *name) {
+    sigattn::AttnParams p = {};
+    const void *inputs[4] = {q, k, v, dout};
+    void *outputs[3];
+    int n_out = 0;
+    if (parts & kPartDq) outputs[n_out++] = dq;
+    if (parts & kPartDkdv) {
+        outputs[n_out++] = dk;
+        outputs[n_out++] = dv;
+    }
+    int st = check_attention(shape, inputs, 4, outputs, n_out, seq_lens, block_mask, mask,
+                             bias_mode, variant, &p);
+    if (st != SIGATTN_OK) return st;
+    if (variant != SIGATTN_SIGMOID)
+        return fail(SIGATTN_ERR_UNSUPPORTED, "backward is built for the SIGMOID variant only");
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    hipStream_t s = (hipStream_t)stream;
+    if (parts & kPartDkdv) {
+        st = launch_status(sigattn::launch_bwd_dkdv(p, s), name);
+        if (st != SIGATTN_OK) return st;
+    }
+    if (parts & kPartDq) return launch_status(sigattn::launch_bwd_dq(p, s), name);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+                const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
+                const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dq, void *dk,
+                void *dv, void *stream) {
+    return backward(shape, q, k, v, dout, seq_lens, block_mask, mask, bias_mode, variant, dq, dk,
+                    dv, stream, kPartDkdv | kPartDq, "sigattn_bwd");
+}
+
+int sigattn_bwd_dkdv(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+                     const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
+                     const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dk,
+                     void *dv, void *stream) {
+    return backward(shape, q, k, v, dout, seq_lens, block_mask, mask, bias_mode, variant,
+                    nullptr, dk, dv, stream, kPartDkdv, "sigattn_bwd_dkdv");
+}
+
+int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+                   const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
+                   const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dq,
+                   void *stream) {
+    return backward(shape, q, k, v, dout, seq_lens, block_mask, mask, bias_mode, variant, dq,
+                    nullptr, nullptr, stream, kPartDq, "sigattn_bwd_dq");
+}
+
+const char *sigattn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Binary block mask builder (Binary Block Masking, "Presentation" and "How it
+// works"): entry (b, i, j) is 1 when query tile i x key tile j of batch entry b
+// holds at least one valid element.  One matrix per batch entry, shared by
+// every head and layer.
+//
+// Padding-only batches use the closed form (i*bq < n) && (j*bk < n), one thread
+// per entry.  With an element mask the builder is one HBM scan of the valid
+// rectangle [0, n) x [0, n) of each mask: a workgroup owns a band of bq rows
+// and a group of key tiles, so it writes its outputs alone (no atomics to
+// global memory), and each wave walks one row at a time with 16-byte loads.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace sigattn {
+
+__global__ void __launch_bounds__(256)
+blockmask_padding_kernel(const int32_t *__restrict__ seq_lens, int B, int L, int bq, int bk,
+                         int Tq, int Tk, uint8_t *__restrict__ out) {
+    int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t total = (int64_t)B * Tq * Tk;
+    if (idx >= total) return;
+    int j = (int)(idx % Tk);
+    int i = (int)((idx / Tk) % Tq);
+    int b = (int)(idx / ((int64_t)Tq * Tk));
+    int n = clamp_len(seq_lens[b], L);
+    out[idx] = (uint8_t)((i * bq < n) && (j * bk < n));
+}
+
+// Grid: (Tq * groups, B); 256 threads.  tiles_per_group * bk <= 1024 columns,
+// and tiles_per_group <= 32 so one 32-bit word holds the group's flags.
+__global__ void __launch_bounds__(256)
+blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict__ mask,
+                      int L, int bq, int bk_shift, int Tq, int Tk, int tiles_per_group,
+                      int groups, uint8_t *__restrict__ out) {
+    __shared__ uint32_t flags;
+    const int b = blockIdx.y;
+    const int i = blockIdx.x / groups;
+    const int g = blockIdx.x % groups;
+    const int j0 = g * tiles_per_group;
+    const int j1 = min(j0 + tiles_per_group, Tk);
+    const int n = clamp_len(seq_lens[b], L);
+    const int r_lo = i * bq, r_hi = min(min(r_lo + bq, L), n);
+    const int c_lo = j0 << bk_shift, c_hi = min(j1 << bk_shift, n);
+    if (threadIdx.x == 0) flags = 0u;
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t total = (uint64_t)gridDim.y * (uint64_t)L * (uint64_t)L;
+    uint32_t bits = 0;
+    if (r_lo < r_hi && c_lo < c_hi) {
+        for (int r = r_lo + wave; r < r_hi; r += 4) {
+            const uint64_t row = ((uint64_t)b * L + r) * (uint64_t)L;
+            const uint64_t lo = row + c_lo, hi = row + c_hi;
+            for (uint64_t a = (lo & ~(uint64_t)15) + 16u * lane; a < hi; a += 16u * 64) {
+                uint8_t bytes[16];
+                if (a + 16 <= total) {
+                    uint4 u = *reinterpret_cast<const uint4 *>(mask + a);
+                    if ((u.x | u.y | u.z | u.w) == 0u) continue;
+                    *reinterpret_cast<uint4 *>(bytes) = u;
+                } else {
+                    for (int t = 0; t < 16; ++t) bytes[t] = (a + t < total) ? mask[a + t] : 0;
+                }
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const uint64_t p = a + t;
+                    if (bytes[t] != 0 && p >= lo && p < hi) {
+                        const int c = (int)(p - row);
+                        bits |= 1u << ((c >> bk_shift) - j0);
+                    }
+                }
+            }
+        }
+    }
+    if (bits) atomicOr(&flags, bits);
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < j1 - j0) out[((int64_t)b * Tq + i) * Tk + j0 + t] = (uint8_t)((flags >> t) & 1u);
+}
+
+hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask, int B, int L,
+                            int block_q, int block_k, uint8_t *out, hipStream_t stream) {
+    const int Tq = (L + block_q - 1) / block_q;
+    const int Tk = (L + block_k - 1) / block_k;
+    if (mask == nullptr) {
+        const int64_t total = (int64_t)B * Tq * Tk;
+        const int threads = 256;
+        const int64_t blocks = (total + threads - 1) / threads;
+        hipLaunchKernelGGL(blockmask_padding_kernel, dim3((unsigned)blocks), dim3(threads), 0,
+                           stream, seq_lens, B, L, block_q, block_k, Tq, Tk, out);
+        return hipGetLastError();
+    }
+    int bk_shift = 0;
+    while ((1 << bk_shift) < block_k) ++bk_shift;
+    const int tiles_per_group = 1024 / block_k;  // 8, 16 or 32 tiles: 1 KiB of each row
+    const int groups = (Tk + tiles_per_group - 1) / tiles_per_group;
+    hipLaunchKernelGGL(blockmask_scan_kernel, dim3((unsigned)(Tq * groups), (unsigned)B),
+                       dim3(256), 0, stream, seq_lens, mask, L, block_q, bk_shift, Tq, Tk,
+                       tiles_per_group, groups, out);
+    return hipGetLastError();
+}
+
+}  // namespace sigattn

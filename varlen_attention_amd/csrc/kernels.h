@@ -1,0 +1,32 @@
+// Parameter blocks and launchers of the gfx950 kernels.  The host ABI layer
+// (api.hip) validates arguments and calls these; each launcher enqueues its
+// kernels on the given stream and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sigattn {
+
+struct AttnParams {
+    const void *q, *k, *v, *dout;   // bf16 [B, H, L, d] (input layout); dout: backward only
+    void *o, *dq, *dk, *dv;         // bf16 [B, H, L, d] (output layout)
+    float *lse;                     // float [B, H, L] or null
+    const int32_t *seq_lens;        // [B]
+    const uint8_t *block_mask;      // [B, Tq, Tk] or null
+    const uint8_t *mask;            // [B, L, L] or null
+    int64_t sb, sh, sl;             // input strides (elements)
+    int64_t osb, osh, osl;          // output strides (elements)
+    int B, H, L, d;
+    int block_q, block_k, Tq, Tk;   // block-mask geometry
+    float scale;
+    int bias_mode, variant;
+};
+
+hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask, int B, int L,
+                            int block_q, int block_k, uint8_t *out, hipStream_t stream);
+hipError_t launch_fwd(const AttnParams &p, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const AttnParams &p, hipStream_t stream);
+hipError_t launch_bwd_dq(const AttnParams &p, hipStream_t stream);
+
+}  // namespace sigattn
