@@ -9,14 +9,16 @@
 // head); each wave holds its 32 K and V rows in registers and walks the query
 // tiles whose block-mask entry is 1 (one column of the block matrix):
 //   S  = Q K^T,  dP = dO V^T            (Q, dO rows from LDS)
-//   dV^T += dO^T P,  dK^T += Q^T dS     (P, dS stay in registers; Q^T, dO^T
-//                                        from transposed, permuted LDS copies)
+//   dV^T += dO^T P,  dK^T += Q^T dS     (P, dS stay in registers; Q^T and dO^T
+//                                        come from transposing LDS reads)
 // dQ kernel: a workgroup owns 32*NW queries; each wave holds its Q and dO rows
 // and walks the key tiles of one block-mask row:
 //   S^T = K Q^T,  dP^T = V dO^T         (K, V rows from LDS)
-//   dQ^T += K^T dS^T                    (K^T from a transposed LDS copy)
-// The two kernels write disjoint outputs and are launched back to back on one
-// stream.
+//   dQ^T += K^T dS^T                    (K^T from transposing LDS reads)
+// Tiles are double-buffered in LDS (unpadded, XOR-swizzled rows): the next
+// tile is fetched into registers through bounds-checked buffer loads while
+// the current one computes, with one barrier per tile.  The two kernels write
+// disjoint outputs.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -24,51 +26,39 @@ namespace sigattn {
 
 namespace {
 
-// Stage a [BT x D] tile of one or two tensors: row-major copies [BT][D + 8]
-// and, where requested, transposed copies [D][BT + 8] with rows in perm16 order.
+// Moves a [BT x D] tile of two tensors (rows [r0, n) of each; rows >= n read
+// as zeros) into swizzled LDS tiles, CH 16-byte chunks per thread and tensor.
 template <int D, int BT, int NT>
-struct TileStage {
+struct PairStage {
     static constexpr int kChunksPerRow = D / 8;
     static constexpr int CH = BT * kChunksPerRow / NT;
     static_assert(CH * NT == BT * kChunksPerRow, "tile must split evenly over threads");
     uint4 a[CH], b[CH];
+    int goff[CH], loff[CH];
 
-    __device__ __forceinline__ void load(const bf16 *pa, const bf16 *pb, int64_t sl, int r0,
-                                         int n, int tid) {
+    __device__ __forceinline__ void init(int64_t sl, int tid) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int idx = tid + c * NT;
             const int row = idx / kChunksPerRow, col = (idx % kChunksPerRow) * 8;
-            const int r = r0 + row;
-            if (r < n) {
-                a[c] = load16(pa + (int64_t)r * sl + col);
-                b[c] = load16(pb + (int64_t)r * sl + col);
-            } else {
-                a[c] = make_uint4(0, 0, 0, 0);
-                b[c] = make_uint4(0, 0, 0, 0);
-            }
+            goff[c] = (int)(((int64_t)row * sl + col) * 2);
+            loff[c] = swz_off<D>(row, col);
         }
     }
 
-    __device__ __forceinline__ static void put(const uint4 &x, bf16 (*rows)[D + 8],
-                                               bf16 (*cols)[BT + 8], int idx) {
-        const int row = idx / kChunksPerRow, col = (idx % kChunksPerRow) * 8;
-        if (rows) *reinterpret_cast<uint4 *>(&rows[row][col]) = x;
-        if (cols) {
-            const bf16x8 xv = as_bf16x8(x);
-            const int pos = perm16(row);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cols[col + e][pos] = xv[e];
-        }
-    }
-
-    __device__ __forceinline__ void store(bf16 (*a_rows)[D + 8], bf16 (*a_cols)[BT + 8],
-                                          bf16 (*b_rows)[D + 8], bf16 (*b_cols)[BT + 8],
-                                          int tid) const {
+    __device__ __forceinline__ void load(rsrc_t ra, rsrc_t rb) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            put(a[c], a_rows, a_cols, tid + c * NT);
-            put(b[c], b_rows, b_cols, tid + c * NT);
+            a[c] = buffer_load16(ra, goff[c]);
+            b[c] = buffer_load16(rb, goff[c]);
+        }
+    }
+
+    __device__ __forceinline__ void store(bf16 *ta, bf16 *tb) const {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            *reinterpret_cast<uint4 *>(ta + loff[c]) = a[c];
+            *reinterpret_cast<uint4 *>(tb + loff[c]) = b[c];
         }
     }
 };
@@ -95,18 +85,33 @@ __device__ __forceinline__ void store_rows_t(bf16 *rowp, const f32x16 *acc, floa
         }
 }
 
+// 16-byte row operand of a swizzled tile: row r, columns [col, col + 8).
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const bf16 *tile, int r, int col) {
+    return *reinterpret_cast<const bf16x8 *>(tile + swz_off<D>(r, col));
+}
+
+// Transposed operand of a swizzled tile for a 16-row MFMA step starting at
+// row r16: lane gets column `col` (its lane % 32 within the 32-column block
+// starting at c32) at rows r16 + {4h+j, 8+4h+j}.  trow / tcol as in fwd.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const bf16 *tile, int r16, int c32, int trow,
+                                             int tcol) {
+    const int r = r16 + trow;
+    return cat8(lds_read_tr4(tile + swz_off<D>(r, c32 + tcol)),
+                lds_read_tr4(tile + swz_off<D>(r + 8, c32 + tcol)));
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- dK / dV
 template <int D, int NW, int QB>
-__global__ void __launch_bounds__(64 * NW)
+__global__ void __launch_bounds__(64 * NW, 2)
 bwd_dkdv_kernel(const AttnParams p) {
     constexpr int BKV = 32 * NW, BQ = 32 * QB, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) bf16 Qs[BQ][D + 8];
-    __shared__ __attribute__((aligned(16))) bf16 Qt[D][BQ + 8];
-    __shared__ __attribute__((aligned(16))) bf16 dOs[BQ][D + 8];
-    __shared__ __attribute__((aligned(16))) bf16 dOt[D][BQ + 8];
+    __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * D];
+    __shared__ __attribute__((aligned(16))) bf16 dOs[2][BQ * D];
 
     const int kt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -129,64 +134,83 @@ bwd_dkdv_kernel(const AttnParams p) {
     const int kl = lane & 31, hh = lane >> 5;
     const int key = k0 + w * 32 + kl;  // this lane's key row
     const bool k_valid = key < n;
+    const int trow = 4 * hh + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const bool has_mask = p.mask != nullptr;
+    const rsrc_t rmask = make_rsrc(has_mask ? p.mask + (int64_t)b * L * L : nullptr,
+                                   has_mask ? (int64_t)L * L : 0);
+
     // K^T and V^T operands of S = Q K^T and dP = dO V^T: lane holds row `key`.
+    const rsrc_t rk = make_rsrc(kb + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
+    const rsrc_t rv = make_rsrc(vb + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
     bf16x8 kreg[KS], vreg[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        kreg[ks] = as_bf16x8(k_valid ? load16(kb + (int64_t)key * p.sl + ks * 16 + hh * 8) : z);
-        vreg[ks] = as_bf16x8(k_valid ? load16(vb + (int64_t)key * p.sl + ks * 16 + hh * 8) : z);
+        const int off = (int)(((int64_t)(w * 32 + kl) * p.sl + ks * 16 + hh * 8) * 2);
+        kreg[ks] = as_bf16x8(buffer_load16(rk, off));
+        vreg[ks] = as_bf16x8(buffer_load16(rv, off));
     }
     const float beta = bias_value(p.bias_mode, n, L);
     const float c1 = -p.scale * kLog2e, c0 = -beta * kLog2e;
-    const int bj = k0 / p.block_k;
 
     f32x16 dvt[DB], dkt[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dvt[db] = dkt[db] = f32x16{};
 
-    const int nqt = (n + BQ - 1) / BQ;
-    auto active = [&](int qt) {
-        return p.block_mask == nullptr ||
-               p.block_mask[((int64_t)b * p.Tq + (qt * BQ) / p.block_q) * p.Tk + bj] != 0;
+    auto rows_rsrc = [&](const bf16 *base, int r0) {
+        return make_rsrc(base + (int64_t)r0 * p.sl, (int64_t)(n - r0) * p.sl * 2);
     };
-    int qt = 0;
-    while (qt < nqt && !active(qt)) ++qt;
-    TileStage<D, BQ, NT> stage;
-    if (qt < nqt) stage.load(qb, dob, p.sl, qt * BQ, n, tid);
+    TileSchedule<BQ> sched;
+    sched.init(p.block_mask ? p.block_mask + (int64_t)b * p.Tq * p.Tk + k0 / p.block_k : nullptr,
+               p.Tk, n, p.block_q);
+    int qt = sched.next();
+    PairStage<D, BQ, NT> stage;
+    stage.init(p.sl, tid);
+    int buf = 0;
+    stage.load(rows_rsrc(qb, qt >= 0 ? qt * BQ : 0), rows_rsrc(dob, qt >= 0 ? qt * BQ : 0));
+    stage.store(Qs[0], dOs[0]);
+    __syncthreads();
 
-    while (qt < nqt) {
+    while (qt >= 0) {
         const int q0 = qt * BQ;
-        __syncthreads();
-        stage.store(Qs, Qt, dOs, dOt, tid);
-        __syncthreads();
-        int nxt = qt + 1;
-        while (nxt < nqt && !active(nxt)) ++nxt;
-        if (nxt < nqt) stage.load(qb, dob, p.sl, nxt * BQ, n, tid);
-
-        const bool full = (q0 + BQ <= n) && (k0 + BKV <= n) && (p.mask == nullptr);
+        const int nxt = sched.next();
+        if (nxt >= 0) stage.load(rows_rsrc(qb, nxt * BQ), rows_rsrc(dob, nxt * BQ));
+        const bf16 *Qc = Qs[buf];
+        const bf16 *dOc = dOs[buf];
+        const bool full = (q0 + BQ <= n) && (k0 + BKV <= n) && !has_mask;
 #pragma unroll
         for (int qb2 = 0; qb2 < QB; ++qb2) {
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 aq =
-                    *reinterpret_cast<const bf16x8 *>(&Qs[qb2 * 32 + kl][ks * 16 + hh * 8]);
-                const bf16x8 ad =
-                    *reinterpret_cast<const bf16x8 *>(&dOs[qb2 * 32 + kl][ks * 16 + hh * 8]);
-                s = mfma32(aq, kreg[ks], s);
-                dp = mfma32(ad, vreg[ks], dp);
+                s = mfma32(row_operand<D>(Qc, qb2 * 32 + kl, ks * 16 + hh * 8), kreg[ks], s);
+                dp = mfma32(row_operand<D>(dOc, qb2 * 32 + kl, ks * 16 + hh * 8), vreg[ks], dp);
             }
             // s[4i + j] = S[query q0 + 32 qb2 + 8 i + 4 hh + j][key]
             float pv[16], dsv[16];
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qr = q0 + qb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                bool ok = full || (k_valid && qr < n &&
-                                   (p.mask == nullptr || p.mask[((int64_t)b * L + qr) * L + key]));
-                const float pr = ok ? sigmoid_from(s[r], c1, c0) : 0.0f;
-                pv[r] = pr;
-                dsv[r] = dp[r] * pr * (1.0f - pr);
+                for (int r = 0; r < 16; ++r) {
+                    const float pr = sigmoid_from(s[r], c1, c0);
+                    pv[r] = pr;
+                    dsv[r] = dp[r] * (pr - pr * pr);
+                }
+            } else {
+                uint8_t mk[16];
+                if (has_mask)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int qr = q0 + qb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                        mk[r] = buffer_load_u8(rmask, qr * L + key);
+                    }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qr = q0 + qb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                    const bool ok = k_valid && qr < n && (!has_mask || mk[r] != 0);
+                    const float pr = ok ? sigmoid_from(s[r], c1, c0) : 0.0f;
+                    pv[r] = pr;
+                    dsv[r] = dp[r] * (pr - pr * pr);
+                }
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -194,15 +218,15 @@ bwd_dkdv_kernel(const AttnParams p) {
                 const bf16x8 sb = pack8(&dsv[kk * 8]);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const bf16x8 ado = *reinterpret_cast<const bf16x8 *>(
-                        &dOt[db * 32 + kl][qb2 * 32 + kk * 16 + hh * 8]);
-                    const bf16x8 aqt = *reinterpret_cast<const bf16x8 *>(
-                        &Qt[db * 32 + kl][qb2 * 32 + kk * 16 + hh * 8]);
-                    dvt[db] = mfma32(ado, pb, dvt[db]);
-                    dkt[db] = mfma32(aqt, sb, dkt[db]);
+                    const int r16 = qb2 * 32 + kk * 16;
+                    dvt[db] = mfma32(tr_operand<D>(dOc, r16, db * 32, trow, tcol), pb, dvt[db]);
+                    dkt[db] = mfma32(tr_operand<D>(Qc, r16, db * 32, trow, tcol), sb, dkt[db]);
                 }
             }
         }
+        if (nxt >= 0) stage.store(Qs[buf ^ 1], dOs[buf ^ 1]);
+        __syncthreads();
+        buf ^= 1;
         qt = nxt;
     }
     if (key < L) {
@@ -213,13 +237,12 @@ bwd_dkdv_kernel(const AttnParams p) {
 
 // ---------------------------------------------------------------- dQ
 template <int D, int NW, int KB>
-__global__ void __launch_bounds__(64 * NW)
+__global__ void __launch_bounds__(64 * NW, 2)
 bwd_dq_kernel(const AttnParams p) {
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) bf16 Ks[BK][D + 8];
-    __shared__ __attribute__((aligned(16))) bf16 Kt[D][BK + 8];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[BK][D + 8];
+    __shared__ __attribute__((aligned(16))) bf16 Ks[2][BK * D];
+    __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * D];
 
     const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -239,16 +262,22 @@ bwd_dq_kernel(const AttnParams p) {
     const int ql = lane & 31, hh = lane >> 5;
     const int qr = q0 + w * 32 + ql;
     const bool q_valid = qr < n;
+    const int trow = 4 * hh + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const bool has_mask = p.mask != nullptr;
+    const rsrc_t rmask = make_rsrc(has_mask ? p.mask + (int64_t)b * L * L : nullptr,
+                                   has_mask ? (int64_t)L * L : 0);
+    const int mrow_off = qr * L;
+
+    const rsrc_t rq = make_rsrc(qb + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
+    const rsrc_t rdo = make_rsrc(dob + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
     bf16x8 qreg[KS], doreg[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        qreg[ks] = as_bf16x8(q_valid ? load16(qb + (int64_t)qr * p.sl + ks * 16 + hh * 8) : z);
-        doreg[ks] = as_bf16x8(q_valid ? load16(dob + (int64_t)qr * p.sl + ks * 16 + hh * 8) : z);
+        const int off = (int)(((int64_t)(w * 32 + ql) * p.sl + ks * 16 + hh * 8) * 2);
+        qreg[ks] = as_bf16x8(buffer_load16(rq, off));
+        doreg[ks] = as_bf16x8(buffer_load16(rdo, off));
     }
-    const uint8_t *mrow = (p.mask && q_valid) ? p.mask + ((int64_t)b * L + qr) * L : nullptr;
-    const uint8_t *bm_row =
-        p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + q0 / p.block_q) * p.Tk : nullptr;
     const float beta = bias_value(p.bias_mode, n, L);
     const float c1 = -p.scale * kLog2e, c0 = -beta * kLog2e;
 
@@ -256,55 +285,70 @@ bwd_dq_kernel(const AttnParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
 
-    const int nkt = (n + BK - 1) / BK;
-    auto active = [&](int t) { return bm_row == nullptr || bm_row[(t * BK) / p.block_k] != 0; };
-    int kt = 0;
-    while (kt < nkt && !active(kt)) ++kt;
-    TileStage<D, BK, NT> stage;
-    if (kt < nkt) stage.load(kb, vb, p.sl, kt * BK, n, tid);
+    auto rows_rsrc = [&](const bf16 *base, int r0) {
+        return make_rsrc(base + (int64_t)r0 * p.sl, (int64_t)(n - r0) * p.sl * 2);
+    };
+    TileSchedule<BK> sched;
+    sched.init(p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + q0 / p.block_q) * p.Tk : nullptr,
+               1, n, p.block_k);
+    int kt = sched.next();
+    PairStage<D, BK, NT> stage;
+    stage.init(p.sl, tid);
+    int buf = 0;
+    stage.load(rows_rsrc(kb, kt >= 0 ? kt * BK : 0), rows_rsrc(vb, kt >= 0 ? kt * BK : 0));
+    stage.store(Ks[0], Vs[0]);
+    __syncthreads();
 
-    while (kt < nkt) {
+    while (kt >= 0) {
         const int k0 = kt * BK;
-        __syncthreads();
-        stage.store(Ks, Kt, Vs, nullptr, tid);
-        __syncthreads();
-        int nxt = kt + 1;
-        while (nxt < nkt && !active(nxt)) ++nxt;
-        if (nxt < nkt) stage.load(kb, vb, p.sl, nxt * BK, n, tid);
-
-        const bool full = (k0 + BK <= n) && (q0 + BQ <= n) && (p.mask == nullptr);
+        const int nxt = sched.next();
+        if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
+        const bf16 *Kc = Ks[buf];
+        const bf16 *Vc = Vs[buf];
+        const bool full = (k0 + BK <= n) && (q0 + BQ <= n) && !has_mask;
 #pragma unroll
         for (int kb2 = 0; kb2 < KB; ++kb2) {
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 ak =
-                    *reinterpret_cast<const bf16x8 *>(&Ks[kb2 * 32 + ql][ks * 16 + hh * 8]);
-                const bf16x8 av =
-                    *reinterpret_cast<const bf16x8 *>(&Vs[kb2 * 32 + ql][ks * 16 + hh * 8]);
-                s = mfma32(ak, qreg[ks], s);
-                dp = mfma32(av, doreg[ks], dp);
+                s = mfma32(row_operand<D>(Kc, kb2 * 32 + ql, ks * 16 + hh * 8), qreg[ks], s);
+                dp = mfma32(row_operand<D>(Vc, kb2 * 32 + ql, ks * 16 + hh * 8), doreg[ks], dp);
             }
             // s[4i + j] = S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr]
             float dsv[16];
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                bool ok = full || (q_valid && key < n && (mrow == nullptr || mrow[key]));
-                const float pr = ok ? sigmoid_from(s[r], c1, c0) : 0.0f;
-                dsv[r] = dp[r] * pr * (1.0f - pr);
+                for (int r = 0; r < 16; ++r) {
+                    const float pr = sigmoid_from(s[r], c1, c0);
+                    dsv[r] = dp[r] * (pr - pr * pr);
+                }
+            } else {
+                uint8_t mk[16];
+                if (has_mask)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        mk[r] = buffer_load_u8(rmask, mrow_off + k0 + kb2 * 32 + (r >> 2) * 8 +
+                                                          hh * 4 + (r & 3));
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                    const bool ok = q_valid && key < n && (!has_mask || mk[r] != 0);
+                    const float pr = ok ? sigmoid_from(s[r], c1, c0) : 0.0f;
+                    dsv[r] = dp[r] * (pr - pr * pr);
+                }
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const bf16x8 sb = pack8(&dsv[kk * 8]);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const bf16x8 akt = *reinterpret_cast<const bf16x8 *>(
-                        &Kt[db * 32 + ql][kb2 * 32 + kk * 16 + hh * 8]);
-                    dqt[db] = mfma32(akt, sb, dqt[db]);
-                }
+                for (int db = 0; db < DB; ++db)
+                    dqt[db] = mfma32(tr_operand<D>(Kc, kb2 * 32 + kk * 16, db * 32, trow, tcol),
+                                     sb, dqt[db]);
             }
         }
+        if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
+        __syncthreads();
+        buf ^= 1;
         kt = nxt;
     }
     if (qr < L) store_rows_t<D>(dqb + (int64_t)qr * p.osl, dqt, p.scale, hh);

@@ -40,6 +40,105 @@ __device__ __forceinline__ int perm16(int x) {
     return (x & ~15) | (x & 3) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8-byte chunks addressed by
+// lanes 4 j + i / 4 (j = 0..3).  With every lane pointing at 4 consecutive
+// columns of a row-major tile, the group hands each lane one column taken
+// down four rows: the K-contiguous operand of an MFMA read from a tile whose
+// contiguous axis is the MFMA's M or N axis.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16 *p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    bf16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return r;
+}
+
+// Raw buffer descriptors: loads beyond num_records bytes return zeros, so a
+// descriptor limited to the valid rows of a sequence zero-fills padded rows
+// without branches and never reads them.  Word 3 selects 32-bit data format.
+constexpr int kBufferWord3 = 0x00020000;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t num_bytes) {
+    const int n = num_bytes <= 0 ? 0 : (num_bytes > 0x7fffffff ? 0x7fffffff : (int)num_bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, kBufferWord3);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(rsrc_t r, int byte_offset) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint8_t buffer_load_u8(rsrc_t r, int byte_offset) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, byte_offset, 0, 0);
+}
+
+// Iterates, in increasing order, the tiles of BT rows that one row (or one
+// column) of the block mask marks active, clipped to the n valid rows.  One
+// wave ballot reads 64 block-mask entries at a time; the result is uniform,
+// so the schedule lives in scalar registers.  A null block mask marks all
+// entries active (padding only).  Entry e is read at bm[e * stride].
+template <int BT>
+struct TileSchedule {
+    const uint8_t *bm;  // first entry, or null
+    int64_t stride;     // distance between consecutive entries
+    int nblk;           // block-mask entries covering [0, n)
+    int per_blk;        // kernel tiles per block-mask entry
+    int nkt;            // kernel tiles covering [0, n)
+    int wbase, entry, sub;
+    uint64_t act;
+
+    __device__ __forceinline__ void init(const uint8_t *first, int64_t step, int n, int block) {
+        bm = first;
+        stride = step;
+        nblk = (n + block - 1) / block;
+        per_blk = block / BT;
+        nkt = (n + BT - 1) / BT;
+        wbase = -64;
+        entry = -1;
+        sub = 0;
+        act = 0;
+    }
+
+    // Next active kernel tile index, or -1.
+    __device__ __forceinline__ int next() {
+        if (entry >= 0 && sub + 1 < per_blk && entry * per_blk + sub + 1 < nkt) {
+            ++sub;
+            return entry * per_blk + sub;
+        }
+        while (act == 0) {
+            wbase += 64;
+            if (wbase >= nblk) return -1;
+            const int e = wbase + (int)(threadIdx.x & 63);
+            const bool on = e < nblk && (bm == nullptr || bm[e * stride] != 0);
+            act = __ballot(on);
+        }
+        entry = wbase + __builtin_ctzll(act);
+        act &= act - 1;
+        sub = 0;
+        return entry * per_blk;
+    }
+};
+
+// Unpadded row-major [rows][D] bf16 tile in LDS with an XOR swizzle: the
+// 16-byte chunk c of row r sits at chunk position c ^ swz(r).  swz maps any 8
+// consecutive rows to 8 distinct chunk positions (16-byte reads of one
+// column chunk down 8 rows hit all 32 banks), and maps the 4 rows x 2
+// adjacent chunks touched by 16 lanes of a transposing read to 8 distinct
+// positions as well, so both access patterns are free of bank conflicts.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int col) {
+    return r * D + ((((col >> 3) ^ swz(r)) << 3) | (col & 7));
+}
+
 __device__ __forceinline__ uint4 load16(const bf16 *p) {
     return *reinterpret_cast<const uint4 *>(p);
 }

@@ -13,14 +13,17 @@
 // (batch entry, head); each wave owns 32 rows.  Key tiles of BK = 32*KB rows
 // are visited in increasing order; a tile whose block-mask entry is 0 is never
 // loaded.  Per tile:
-//   S^T = K Q^T           32x32x16 bf16 MFMA, K from LDS, Q held in registers
+//   S^T = K Q^T           32x32x16 bf16 MFMA; K rows from LDS, Q in registers
 //   P^T = f(S^T)          epilogue in registers (sigmoid, or online softmax)
-//   O^T += V^T P^T        P^T stays in registers as the B operand; V^T comes
-//                         from a transposed, key-permuted copy of V in LDS
+//   O^T += V^T P^T        P^T stays in registers as the B operand; V^T is read
+//                         from the row-major V tile with transposing LDS reads
 // Computing the transposed products puts one query per lane (lane % 32), so
 // softmax row statistics are lane-local plus one exchange with lane ^ 32.
-// The next tile's K/V are fetched into registers while the current tile
-// computes.  Fully padded query tiles only write zeros.
+// K and V tiles are double-buffered in LDS: the next tile's rows are fetched
+// into registers while the current tile computes, then written to the other
+// buffer, with one barrier per tile.  Tiles fully inside [0, n) x [0, n)
+// without an element mask take a branch-free epilogue.  Fully padded query
+// tiles only write zeros.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -28,60 +31,60 @@ namespace sigattn {
 
 namespace {
 
+// LDS row strides (elements).  K rows are read 16 bytes per lane down 32 rows:
+// a stride of 4 banks (mod 32) spreads 8 rows over all banks.  V rows are read
+// 8 bytes per lane, 4 rows x 32 bytes per 16 lanes: a stride of 8 banks.
+template <int D> struct Pad { static constexpr int K = D + 8, V = D + 16; };
+
 template <int D, int BK, int NT>
 struct KVStage {
-    // Each thread moves CH 16-byte chunks of K and of V per tile.
+    // Each thread moves CH 16-byte chunks of K and of V per tile.  Offsets are
+    // loop-invariant; the per-tile part lives in the buffer descriptors.
     static constexpr int kChunksPerRow = D / 8;
     static constexpr int CH = BK * kChunksPerRow / NT;
     static_assert(CH * NT == BK * kChunksPerRow, "tile must split evenly over threads");
     uint4 k[CH], v[CH];
+    int goff[CH], koff[CH], voff[CH];
 
-    __device__ __forceinline__ void load(const bf16 *kb, const bf16 *vb, int64_t sl, int k0,
-                                         int n, int tid) {
+    __device__ __forceinline__ void init(int64_t sl, int tid) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int idx = tid + c * NT;
             const int row = idx / kChunksPerRow, col = (idx % kChunksPerRow) * 8;
-            const int key = k0 + row;
-            if (key < n) {
-                k[c] = load16(kb + (int64_t)key * sl + col);
-                v[c] = load16(vb + (int64_t)key * sl + col);
-            } else {
-                k[c] = make_uint4(0, 0, 0, 0);
-                v[c] = make_uint4(0, 0, 0, 0);
-            }
+            goff[c] = (int)(((int64_t)row * sl + col) * 2);
+            koff[c] = row * Pad<D>::K + col;
+            voff[c] = row * Pad<D>::V + col;
         }
     }
 
-    // K row-major [BK][D + 8]; V transposed [D][BK + 8] with keys in perm16 order.
-    __device__ __forceinline__ void store(bf16 (*Ks)[D + 8], bf16 (*Vt)[BK + 8], int tid) const {
+    __device__ __forceinline__ void load(rsrc_t rk, rsrc_t rv) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int idx = tid + c * NT;
-            const int row = idx / kChunksPerRow, col = (idx % kChunksPerRow) * 8;
-            *reinterpret_cast<uint4 *>(&Ks[row][col]) = k[c];
-            const bf16x8 vv = as_bf16x8(v[c]);
-            const int pos = perm16(row);
+            k[c] = buffer_load16(rk, goff[c]);
+            v[c] = buffer_load16(rv, goff[c]);
+        }
+    }
+
+    __device__ __forceinline__ void store(bf16 *Ks, bf16 *Vs) const {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Vt[col + e][pos] = vv[e];
+        for (int c = 0; c < CH; ++c) {
+            *reinterpret_cast<uint4 *>(Ks + koff[c]) = k[c];
+            *reinterpret_cast<uint4 *>(Vs + voff[c]) = v[c];
         }
     }
 };
 
-__device__ __forceinline__ bool tile_active(const uint8_t *bm_row, int k0, int block_k) {
-    return bm_row == nullptr || bm_row[k0 / block_k] != 0;
-}
-
 }  // namespace
 
 template <int D, int VARIANT, int NW, int KB>
-__global__ void __launch_bounds__(64 * NW)
+__global__ void __launch_bounds__(64 * NW, 2)
 fwd_kernel(const AttnParams p) {
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
     constexpr int KS = D / 16;  // MFMA k-steps over the head dimension
     constexpr int DB = D / 32;  // 32-wide blocks of the head dimension
-    __shared__ __attribute__((aligned(16))) bf16 Ks[BK][D + 8];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[D][BK + 8];
+    constexpr int KP = Pad<D>::K, VP = Pad<D>::V;
+    __shared__ __attribute__((aligned(16))) bf16 Ks[2][BK * KP];
+    __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * VP];
 
     const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -107,19 +110,26 @@ fwd_kernel(const AttnParams p) {
     const bf16 *vb = reinterpret_cast<const bf16 *>(p.v) + b * p.sb + h * p.sh;
     const uint8_t *bm_row =
         p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + q0 / p.block_q) * p.Tk : nullptr;
-    const uint8_t *mrow = nullptr;
 
     const int ql = lane & 31, hh = lane >> 5;
     const int qr = q0 + w * 32 + ql;  // this lane's query row
     const bool q_valid = qr < n;
-    if (p.mask && q_valid) mrow = p.mask + ((int64_t)b * L + qr) * L;
+    const bool has_mask = p.mask != nullptr;
+    const rsrc_t rmask = make_rsrc(has_mask ? p.mask + (int64_t)b * L * L : nullptr,
+                                   has_mask ? (int64_t)L * L : 0);
+    const int mrow_off = qr * L;
+    // Per-lane offsets of the transposing V reads (see lds_read_tr4).
+    const int trow = 4 * hh + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     // Q^T operand: lane holds Q[qr][16 ks + 8 hh .. + 7].
+    // Rows >= n read as zeros through the descriptor.
+    const rsrc_t rq = make_rsrc(qb + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
     bf16x8 qreg[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qreg[ks] = q_valid ? as_bf16x8(load16(qb + (int64_t)qr * p.sl + ks * 16 + hh * 8))
-                           : as_bf16x8(make_uint4(0, 0, 0, 0));
+        qreg[ks] = as_bf16x8(
+            buffer_load16(rq, (int)(((int64_t)(w * 32 + ql) * p.sl + ks * 16 + hh * 8) * 2)));
 
     const float beta = bias_value(p.bias_mode, n, L);
     // SIGMOID: u = -(s) * log2 e; softmax: t = s * log2 e (log2-domain logits).
@@ -132,20 +142,28 @@ fwd_kernel(const AttnParams p) {
     float m_run = VARIANT == kSoftmax1 ? 0.0f : -INFINITY;  // log2 domain
     float l_run = (VARIANT == kSoftmax1 && hh == 0) ? 1.0f : 0.0f;  // split over lane halves
 
-    const int nkt = (n + BK - 1) / BK;
-    int kt = 0;
-    while (kt < nkt && !tile_active(bm_row, kt * BK, p.block_k)) ++kt;
+    // Descriptors of the K and V rows [k0, n): rows past n read as zeros.
+    auto rows_rsrc = [&](const bf16 *base, int k0) {
+        return make_rsrc(base + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
+    };
+    TileSchedule<BK> sched;
+    sched.init(bm_row, 1, n, p.block_k);
+    int kt = sched.next();
     KVStage<D, BK, NT> stage;
-    if (kt < nkt) stage.load(kb, vb, p.sl, kt * BK, n, tid);
+    stage.init(p.sl, tid);
+    int buf = 0;
+    // Staged unconditionally (tile 0 when nothing is active, harmless): every
+    // path into the loop has then waited for all earlier loads, Q included.
+    stage.load(rows_rsrc(kb, kt >= 0 ? kt * BK : 0), rows_rsrc(vb, kt >= 0 ? kt * BK : 0));
+    stage.store(Ks[0], Vs[0]);
+    __syncthreads();
 
-    while (kt < nkt) {
+    while (kt >= 0) {
         const int k0 = kt * BK;
-        __syncthreads();
-        stage.store(Ks, Vt, tid);
-        __syncthreads();
-        int nxt = kt + 1;
-        while (nxt < nkt && !tile_active(bm_row, nxt * BK, p.block_k)) ++nxt;
-        if (nxt < nkt) stage.load(kb, vb, p.sl, nxt * BK, n, tid);
+        const int nxt = sched.next();
+        if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
+        const bf16 *Kc = Ks[buf];
+        const bf16 *Vc = Vs[buf];
 
         // S^T for each 32-key block of the tile.
         f32x16 sacc[KB];
@@ -154,36 +172,61 @@ fwd_kernel(const AttnParams p) {
             sacc[kb2] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a =
-                    *reinterpret_cast<const bf16x8 *>(&Ks[kb2 * 32 + ql][ks * 16 + hh * 8]);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+                    Kc + (kb2 * 32 + ql) * KP + ks * 16 + hh * 8);
                 sacc[kb2] = mfma32(a, qreg[ks], sacc[kb2]);
             }
         }
 
-        // Validity: tile fully inside [0, n) x [0, n) and no element mask -> all valid.
-        const bool full = (k0 + BK <= n) && (q0 + BQ <= n) && (p.mask == nullptr);
+        // Epilogue.  sacc[kb2][4i + j] is S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr].
+        const bool full = (k0 + BK <= n) && (q0 + BQ <= n) && !has_mask;
         float pv[KB][16];
         if (VARIANT == kSigmoid) {
+            if (full) {
 #pragma unroll
-            for (int kb2 = 0; kb2 < KB; ++kb2)
+                for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                    bool ok = full || (q_valid && key < n && (mrow == nullptr || mrow[key]));
-                    pv[kb2][r] = ok ? sigmoid_from(sacc[kb2][r], c1, c0) : 0.0f;
+                    for (int r = 0; r < 16; ++r) pv[kb2][r] = sigmoid_from(sacc[kb2][r], c1, c0);
+            } else {
+#pragma unroll
+                for (int kb2 = 0; kb2 < KB; ++kb2) {
+                    uint8_t mk[16];
+                    if (has_mask)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            mk[r] = buffer_load_u8(rmask, mrow_off + k0 + kb2 * 32 + (r >> 2) * 8 +
+                                                              hh * 4 + (r & 3));
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                        const bool ok = q_valid && key < n && (!has_mask || mk[r] != 0);
+                        const float sg = sigmoid_from(sacc[kb2][r], c1, c0);
+                        pv[kb2][r] = ok ? sg : 0.0f;
+                    }
                 }
+            }
         } else {
             float tmax = -INFINITY;
 #pragma unroll
-            for (int kb2 = 0; kb2 < KB; ++kb2)
+            for (int kb2 = 0; kb2 < KB; ++kb2) {
+                uint8_t mk[16];
+                if (!full && has_mask)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        mk[r] = buffer_load_u8(rmask, mrow_off + k0 + kb2 * 32 + (r >> 2) * 8 +
+                                                          hh * 4 + (r & 3));
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                    bool ok = full || (q_valid && key < n && (mrow == nullptr || mrow[key]));
-                    const float t = ok ? fmaf(sacc[kb2][r], c1, c0) : -INFINITY;
+                    float t = fmaf(sacc[kb2][r], c1, c0);
+                    if (!full) {
+                        const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                        const bool ok = q_valid && key < n && (!has_mask || mk[r] != 0);
+                        t = ok ? t : -INFINITY;
+                    }
                     pv[kb2][r] = t;
                     tmax = fmaxf(tmax, t);
                 }
+            }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             const float m_new = fmaxf(m_run, tmax);
             const float m_use = m_new == -INFINITY ? 0.0f : m_new;
@@ -209,14 +252,19 @@ fwd_kernel(const AttnParams p) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const bf16x8 pb = pack8(&pv[kb2][kk * 8]);
+                const bf16 *vrow = Vc + (kb2 * 32 + kk * 16 + trow) * VP + tcol;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                        &Vt[db * 32 + ql][kb2 * 32 + kk * 16 + hh * 8]);
+                    const bf16x8 a =
+                        cat8(lds_read_tr4(vrow + db * 32), lds_read_tr4(vrow + 8 * VP + db * 32));
                     oacc[db] = mfma32(a, pb, oacc[db]);
                 }
             }
         }
+
+        if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
+        __syncthreads();
+        buf ^= 1;
         kt = nxt;
     }
 
