@@ -24,6 +24,8 @@
 // buffer, with one barrier per tile.  Tiles fully inside [0, n) x [0, n)
 // without an element mask take a branch-free epilogue.  Fully padded query
 // tiles only write zeros.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -86,7 +88,16 @@ fwd_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][BK * KP];
     __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * VP];
 
-    const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // Workgroups are dealt to the 8 XCDs round-robin by linear index, and each
+    // XCD has its own L2.  Map index i to XCD slot x = i % 8 and give XCD x the
+    // (batch entry, head) pairs P = x, x + 8, ...: all query tiles of one
+    // pair share an L2, and with H a multiple of 8 every XCD gets one head of
+    // every batch entry (equal work).
+    const int nqt = (p.L + BQ - 1) / BQ;
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    const int pair = x + 8 * (k / nqt);
+    if (pair >= p.B * p.H) return;
+    const int qt = k % nqt, h = pair % p.H, b = pair / p.H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
     const int n = clamp_len(p.seq_lens[b], L);
@@ -165,102 +176,98 @@ fwd_kernel(const AttnParams p) {
         const bf16 *Kc = Ks[buf];
         const bf16 *Vc = Vs[buf];
 
-        // S^T for each 32-key block of the tile.
-        f32x16 sacc[KB];
+        // One straight-line body per tile kind, so the scheduler can overlap
+        // the MFMAs of one key block with the epilogue of another.
+        // MODE 0: tile inside [0, n) x [0, n), no element mask; 1: tile on the
+        // padding boundary; 2: element mask.
+        auto tile = [&](auto mode_tag) {
+            constexpr int MODE = decltype(mode_tag)::value;
+            // S^T for each 32-key block: sacc[kb2][4i + j] is
+            // S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr].
+            f32x16 sacc[KB];
 #pragma unroll
-        for (int kb2 = 0; kb2 < KB; ++kb2) {
-            sacc[kb2] = f32x16{};
+            for (int kb2 = 0; kb2 < KB; ++kb2) {
+                sacc[kb2] = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                    Kc + (kb2 * 32 + ql) * KP + ks * 16 + hh * 8);
-                sacc[kb2] = mfma32(a, qreg[ks], sacc[kb2]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+                        Kc + (kb2 * 32 + ql) * KP + ks * 16 + hh * 8);
+                    sacc[kb2] = mfma32(a, qreg[ks], sacc[kb2]);
+                }
             }
-        }
-
-        // Epilogue.  sacc[kb2][4i + j] is S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr].
-        const bool full = (k0 + BK <= n) && (q0 + BQ <= n) && !has_mask;
-        float pv[KB][16];
-        if (VARIANT == kSigmoid) {
-            if (full) {
+            uint8_t mk[KB][16];
+            if constexpr (MODE == 2) {
 #pragma unroll
                 for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) pv[kb2][r] = sigmoid_from(sacc[kb2][r], c1, c0);
-            } else {
+                    for (int r = 0; r < 16; ++r)
+                        mk[kb2][r] = buffer_load_u8(rmask, mrow_off + k0 + kb2 * 32 +
+                                                               (r >> 2) * 8 + hh * 4 + (r & 3));
+            }
+            auto valid = [&](int kb2, int r) {
+                if constexpr (MODE == 0) return true;
+                const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                bool ok = q_valid && key < n;
+                if constexpr (MODE == 2) ok = ok && mk[kb2][r] != 0;
+                return ok;
+            };
+
+            float alpha = 1.0f, m_use = 0.0f;
+            if constexpr (VARIANT != kSigmoid) {
+                // Online softmax: tile maximum over this lane's keys and its
+                // partner lane's (lane ^ 32), then rescale the state.
+                float tmax = -INFINITY;
 #pragma unroll
-                for (int kb2 = 0; kb2 < KB; ++kb2) {
-                    uint8_t mk[16];
-                    if (has_mask)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            mk[r] = buffer_load_u8(rmask, mrow_off + k0 + kb2 * 32 + (r >> 2) * 8 +
-                                                              hh * 4 + (r & 3));
+                for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                        const bool ok = q_valid && key < n && (!has_mask || mk[r] != 0);
-                        const float sg = sigmoid_from(sacc[kb2][r], c1, c0);
-                        pv[kb2][r] = ok ? sg : 0.0f;
+                        const float t = fmaf(sacc[kb2][r], c1, c0);
+                        sacc[kb2][r] = valid(kb2, r) ? t : -INFINITY;
+                        tmax = fmaxf(tmax, sacc[kb2][r]);
                     }
-                }
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                const float m_new = fmaxf(m_run, tmax);
+                m_use = m_new == -INFINITY ? 0.0f : m_new;
+                alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
             }
-        } else {
-            float tmax = -INFINITY;
+
+            // Per 32-key block: weights, then O^T += V^T P^T (two 16-key steps).
 #pragma unroll
             for (int kb2 = 0; kb2 < KB; ++kb2) {
-                uint8_t mk[16];
-                if (!full && has_mask)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        mk[r] = buffer_load_u8(rmask, mrow_off + k0 + kb2 * 32 + (r >> 2) * 8 +
-                                                          hh * 4 + (r & 3));
+                float pv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float t = fmaf(sacc[kb2][r], c1, c0);
-                    if (!full) {
-                        const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                        const bool ok = q_valid && key < n && (!has_mask || mk[r] != 0);
-                        t = ok ? t : -INFINITY;
+                    if constexpr (VARIANT == kSigmoid) {
+                        const float sg = sigmoid_from(sacc[kb2][r], c1, c0);
+                        pv[r] = valid(kb2, r) ? sg : 0.0f;
+                    } else {
+                        pv[r] = __builtin_amdgcn_exp2f(sacc[kb2][r] - m_use);
+                        l_run += pv[r];
                     }
-                    pv[kb2][r] = t;
-                    tmax = fmaxf(tmax, t);
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8 pb = pack8(&pv[kk * 8]);
+                    const bf16 *vrow = Vc + (kb2 * 32 + kk * 16 + trow) * VP + tcol;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const bf16x8 a = cat8(lds_read_tr4(vrow + db * 32),
+                                              lds_read_tr4(vrow + 8 * VP + db * 32));
+                        oacc[db] = mfma32(a, pb, oacc[db]);
+                    }
                 }
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float m_new = fmaxf(m_run, tmax);
-            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            float psum = 0.0f;
-#pragma unroll
-            for (int kb2 = 0; kb2 < KB; ++kb2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(pv[kb2][r] - m_use);
-                    pv[kb2][r] = e;
-                    psum += e;
-                }
-            l_run = l_run * alpha + psum;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-            m_run = m_new;
-        }
-
-        // O^T += V^T P^T over the tile's 32-key blocks (two 16-key MFMA steps each).
-#pragma unroll
-        for (int kb2 = 0; kb2 < KB; ++kb2) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 pb = pack8(&pv[kb2][kk * 8]);
-                const bf16 *vrow = Vc + (kb2 * 32 + kk * 16 + trow) * VP + tcol;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const bf16x8 a =
-                        cat8(lds_read_tr4(vrow + db * 32), lds_read_tr4(vrow + 8 * VP + db * 32));
-                    oacc[db] = mfma32(a, pb, oacc[db]);
-                }
-            }
-        }
+        };
+        if ((k0 + BK <= n) && (q0 + BQ <= n) && !has_mask)
+            tile(std::integral_constant<int, 0>{});
+        else if (!has_mask)
+            tile(std::integral_constant<int, 1>{});
+        else
+            tile(std::integral_constant<int, 2>{});
 
         if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
         __syncthreads();
@@ -298,7 +305,8 @@ static hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
     const int nw = p.block_q >= 128 ? 4 : p.block_q / 32;
     const int kb = p.block_k >= 64 ? 2 : 1;
     const int bq = 32 * nw;
-    dim3 grid((p.L + bq - 1) / bq, p.H, p.B);
+    const int64_t pairs_per_xcd = ((int64_t)p.B * p.H + 7) / 8;
+    dim3 grid((unsigned)(8 * pairs_per_xcd * ((p.L + bq - 1) / bq)));
     dim3 block(64 * nw);
 #define SIGATTN_FWD_CASE(NW_, KB_)                                                        \
     if (nw == NW_ && kb == KB_) {                                                         \
