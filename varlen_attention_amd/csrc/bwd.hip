@@ -19,6 +19,8 @@
 // tile is fetched into registers through bounds-checked buffer loads while
 // the current one computes, with one barrier per tile.  The two kernels write
 // disjoint outputs.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -102,6 +104,24 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16 *tile, int r16, int c32,
                 lds_read_tr4(tile + swz_off<D>(r + 8, c32 + tcol)));
 }
 
+// Workgroups are dealt to the 8 XCDs round-robin by linear index; give XCD
+// x = i % 8 the (batch entry, head) pairs x, x + 8, ... so that all tiles of
+// one pair share that XCD's L2.  Returns false for indices past the last pair.
+__device__ __forceinline__ bool xcd_item(int ntiles, int B, int H, int &b, int &h, int &t) {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    const int pair = x + 8 * (k / ntiles);
+    if (pair >= B * H) return false;
+    t = k % ntiles;
+    h = pair % H;
+    b = pair / H;
+    return true;
+}
+
+__host__ __forceinline__ dim3 xcd_grid(int ntiles, int B, int H) {
+    const int64_t pairs_per_xcd = ((int64_t)B * H + 7) / 8;
+    return dim3((unsigned)(8 * pairs_per_xcd * ntiles));
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- dK / dV
@@ -113,7 +133,8 @@ bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * D];
     __shared__ __attribute__((aligned(16))) bf16 dOs[2][BQ * D];
 
-    const int kt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int b, h, kt;
+    if (!xcd_item((p.L + BKV - 1) / BKV, p.B, p.H, b, h, kt)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
     const int n = clamp_len(p.seq_lens[b], L);
@@ -177,53 +198,60 @@ bwd_dkdv_kernel(const AttnParams p) {
         if (nxt >= 0) stage.load(rows_rsrc(qb, nxt * BQ), rows_rsrc(dob, nxt * BQ));
         const bf16 *Qc = Qs[buf];
         const bf16 *dOc = dOs[buf];
-        const bool full = (q0 + BQ <= n) && (k0 + BKV <= n) && !has_mask;
+        // One straight-line body per tile kind (0: inside [0, n)^2 without an
+        // element mask; 1: padding boundary; 2: element mask).
+        auto tile = [&](auto mode_tag) {
+            constexpr int MODE = decltype(mode_tag)::value;
 #pragma unroll
-        for (int qb2 = 0; qb2 < QB; ++qb2) {
-            f32x16 s = f32x16{}, dp = f32x16{};
+            for (int qb2 = 0; qb2 < QB; ++qb2) {
+                f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s = mfma32(row_operand<D>(Qc, qb2 * 32 + kl, ks * 16 + hh * 8), kreg[ks], s);
-                dp = mfma32(row_operand<D>(dOc, qb2 * 32 + kl, ks * 16 + hh * 8), vreg[ks], dp);
-            }
-            // s[4i + j] = S[query q0 + 32 qb2 + 8 i + 4 hh + j][key]
-            float pv[16], dsv[16];
-            if (full) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pr = sigmoid_from(s[r], c1, c0);
-                    pv[r] = pr;
-                    dsv[r] = dp[r] * (pr - pr * pr);
+                for (int ks = 0; ks < KS; ++ks) {
+                    s = mfma32(row_operand<D>(Qc, qb2 * 32 + kl, ks * 16 + hh * 8), kreg[ks], s);
+                    dp = mfma32(row_operand<D>(dOc, qb2 * 32 + kl, ks * 16 + hh * 8), vreg[ks],
+                                dp);
                 }
-            } else {
+                // s[4i + j] = S[query q0 + 32 qb2 + 8 i + 4 hh + j][key]
                 uint8_t mk[16];
-                if (has_mask)
+                if constexpr (MODE == 2) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int qr = q0 + qb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
                         mk[r] = buffer_load_u8(rmask, qr * L + key);
                     }
+                }
+                float pv[16], dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int qr = q0 + qb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                    const bool ok = k_valid && qr < n && (!has_mask || mk[r] != 0);
-                    const float pr = ok ? sigmoid_from(s[r], c1, c0) : 0.0f;
+                    float pr = sigmoid_from(s[r], c1, c0);
+                    if constexpr (MODE != 0) {
+                        const int qr = q0 + qb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                        bool ok = k_valid && qr < n;
+                        if constexpr (MODE == 2) ok = ok && mk[r] != 0;
+                        pr = ok ? pr : 0.0f;
+                    }
                     pv[r] = pr;
                     dsv[r] = dp[r] * (pr - pr * pr);
                 }
-            }
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 pb = pack8(&pv[kk * 8]);
-                const bf16x8 sb = pack8(&dsv[kk * 8]);
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8 pb = pack8(&pv[kk * 8]);
+                    const bf16x8 sb = pack8(&dsv[kk * 8]);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int r16 = qb2 * 32 + kk * 16;
-                    dvt[db] = mfma32(tr_operand<D>(dOc, r16, db * 32, trow, tcol), pb, dvt[db]);
-                    dkt[db] = mfma32(tr_operand<D>(Qc, r16, db * 32, trow, tcol), sb, dkt[db]);
+                    for (int db = 0; db < DB; ++db) {
+                        const int r16 = qb2 * 32 + kk * 16;
+                        dvt[db] = mfma32(tr_operand<D>(dOc, r16, db * 32, trow, tcol), pb, dvt[db]);
+                        dkt[db] = mfma32(tr_operand<D>(Qc, r16, db * 32, trow, tcol), sb, dkt[db]);
+                    }
                 }
             }
-        }
+        };
+        if ((q0 + BQ <= n) && (k0 + BKV <= n) && !has_mask)
+            tile(std::integral_constant<int, 0>{});
+        else if (!has_mask)
+            tile(std::integral_constant<int, 1>{});
+        else
+            tile(std::integral_constant<int, 2>{});
         if (nxt >= 0) stage.store(Qs[buf ^ 1], dOs[buf ^ 1]);
         __syncthreads();
         buf ^= 1;
@@ -244,7 +272,8 @@ bwd_dq_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][BK * D];
     __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * D];
 
-    const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int b, h, qt;
+    if (!xcd_item((p.L + BQ - 1) / BQ, p.B, p.H, b, h, qt)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
     const int n = clamp_len(p.seq_lens[b], L);
@@ -305,47 +334,53 @@ bwd_dq_kernel(const AttnParams p) {
         if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
         const bf16 *Kc = Ks[buf];
         const bf16 *Vc = Vs[buf];
-        const bool full = (k0 + BK <= n) && (q0 + BQ <= n) && !has_mask;
+        auto tile = [&](auto mode_tag) {
+            constexpr int MODE = decltype(mode_tag)::value;
 #pragma unroll
-        for (int kb2 = 0; kb2 < KB; ++kb2) {
-            f32x16 s = f32x16{}, dp = f32x16{};
+            for (int kb2 = 0; kb2 < KB; ++kb2) {
+                f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s = mfma32(row_operand<D>(Kc, kb2 * 32 + ql, ks * 16 + hh * 8), qreg[ks], s);
-                dp = mfma32(row_operand<D>(Vc, kb2 * 32 + ql, ks * 16 + hh * 8), doreg[ks], dp);
-            }
-            // s[4i + j] = S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr]
-            float dsv[16];
-            if (full) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pr = sigmoid_from(s[r], c1, c0);
-                    dsv[r] = dp[r] * (pr - pr * pr);
+                for (int ks = 0; ks < KS; ++ks) {
+                    s = mfma32(row_operand<D>(Kc, kb2 * 32 + ql, ks * 16 + hh * 8), qreg[ks], s);
+                    dp = mfma32(row_operand<D>(Vc, kb2 * 32 + ql, ks * 16 + hh * 8), doreg[ks],
+                                dp);
                 }
-            } else {
+                // s[4i + j] = S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr]
                 uint8_t mk[16];
-                if (has_mask)
+                if constexpr (MODE == 2) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         mk[r] = buffer_load_u8(rmask, mrow_off + k0 + kb2 * 32 + (r >> 2) * 8 +
                                                           hh * 4 + (r & 3));
+                }
+                float dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                    const bool ok = q_valid && key < n && (!has_mask || mk[r] != 0);
-                    const float pr = ok ? sigmoid_from(s[r], c1, c0) : 0.0f;
+                    float pr = sigmoid_from(s[r], c1, c0);
+                    if constexpr (MODE != 0) {
+                        const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                        bool ok = q_valid && key < n;
+                        if constexpr (MODE == 2) ok = ok && mk[r] != 0;
+                        pr = ok ? pr : 0.0f;
+                    }
                     dsv[r] = dp[r] * (pr - pr * pr);
                 }
-            }
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 sb = pack8(&dsv[kk * 8]);
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8 sb = pack8(&dsv[kk * 8]);
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    dqt[db] = mfma32(tr_operand<D>(Kc, kb2 * 32 + kk * 16, db * 32, trow, tcol),
-                                     sb, dqt[db]);
+                    for (int db = 0; db < DB; ++db)
+                        dqt[db] = mfma32(tr_operand<D>(Kc, kb2 * 32 + kk * 16, db * 32, trow, tcol),
+                                         sb, dqt[db]);
+                }
             }
-        }
+        };
+        if ((k0 + BK <= n) && (q0 + BQ <= n) && !has_mask)
+            tile(std::integral_constant<int, 0>{});
+        else if (!has_mask)
+            tile(std::integral_constant<int, 1>{});
+        else
+            tile(std::integral_constant<int, 2>{});
         if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
         __syncthreads();
         buf ^= 1;
@@ -360,7 +395,7 @@ static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
     // must divide block_q.
     const int nw = p.block_k >= 128 ? 4 : p.block_k / 32;
     const int qb = p.block_q >= 64 ? 2 : 1;
-    dim3 grid((p.L + 32 * nw - 1) / (32 * nw), p.H, p.B);
+    const dim3 grid = xcd_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_DKDV_CASE(NW_, QB_)                                                     \
     if (nw == NW_ && qb == QB_) {                                                       \
@@ -383,7 +418,7 @@ static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     // must divide block_k.
     const int nw = p.block_q >= 128 ? 4 : p.block_q / 32;
     const int kb = p.block_k >= 64 ? 2 : 1;
-    dim3 grid((p.L + 32 * nw - 1) / (32 * nw), p.H, p.B);
+    const dim3 grid = xcd_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_DQ_CASE(NW_, KB_)                                                     \
     if (nw == NW_ && kb == KB_) {                                                     \
