@@ -70,6 +70,102 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
+def algorithmic_bytes(kernel: str, w) -> float:
+    """Minimum HBM bytes of one launch on workload w: every valid row of each
+    input read once, every row of each output written once (bf16)."""
+    valid = float(np.clip(w.seq_lens, 0, w.L).sum()) * w.H
+    every = float(w.B) * w.L * w.H
+    row = 2.0 * w.d
+    reads, writes = {"fwd": (3, 1), "bwd_dkdv": (4, 2), "bwd_dq": (4, 1)}[kernel]
+    return (reads * valid + writes * every) * row
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirname, suffix):
+    for root, _, files in os.walk(dirname):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirname}")
+
+
+KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
+                  "blockmask": "blockmask_"}
+
+
+def summarize_stats(dirname: str) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run."""
+    rows = _csv_rows(_find(dirname, "kernel_stats.csv"))
+    out = ["| kernel | calls | average (us) | min (us) | max (us) | share |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    return "\n".join(out)
+
+
+def _counter_per_dispatch(dirname: str, symbol: str, counter: str) -> float:
+    rows = _csv_rows(_find(dirname, "counter_collection.csv"))
+    vals = [float(r["Counter_Value"]) for r in rows
+            if symbol in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise ValueError(f"{counter} for {symbol} not found in {dirname}")
+    return float(np.mean(vals))
+
+
+def _copy_counter(dirname: str, counter: str) -> float:
+    rows = _csv_rows(_find(dirname, "counter_collection.csv"))
+    vals = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter]
+    return max(vals)
+
+
+def summarize_traffic(kernel: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                      copy_write_dir: str, copy_mib: int, workload, workload_name: str) -> str:
+    """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE counters
+    (KiB per dispatch), each scaled by what the same counter reads for a
+    plain device copy of copy_mib MiB."""
+    sym = KERNEL_SYMBOLS[kernel]
+    fetch = _counter_per_dispatch(fetch_dir, sym, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, sym, "WRITE_SIZE")
+    true_kib = copy_mib * 1024.0
+    fscale = true_kib / _copy_counter(copy_fetch_dir, "FETCH_SIZE")
+    wscale = true_kib / _copy_counter(copy_write_dir, "WRITE_SIZE")
+    hbm = (fetch * fscale + write * wscale) * 1024.0
+    algo = algorithmic_bytes(kernel, workload)
+    lines = [
+        f"# HBM traffic of {kernel} on {workload_name}",
+        f"kernel: {kernel}",
+        f"workload: {workload_name}",
+        f"source_sha256_16: {source_digest(kernel)}",
+        f"fetch_kib_per_launch_raw: {fetch:.1f}",
+        f"write_kib_per_launch_raw: {write:.1f}",
+        f"copy_reference_mib: {copy_mib}",
+        f"fetch_scale: {fscale:.4f}",
+        f"write_scale: {wscale:.4f}",
+        f"hbm_bytes_per_launch: {hbm:.0f}",
+        f"algorithmic_bytes_per_launch: {algo:.0f}",
+        f"traffic_over_algorithmic: {hbm / algo:.3f}",
+    ]
+    return "\n".join(lines)
+
+
+def copy_reference(mib: int) -> None:
+    """A plain device-to-device copy of `mib` MiB, for counter calibration."""
+    import torch
+    src = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {mib} MiB three times")
+
+
 def cpu_baseline(w, budget_s: float = 15.0):
     """The oracle (fp32 statement) timed on host cores over a sample of
     (batch entry, head) pairs: forward + backward, valid TFLOP/s."""
@@ -111,7 +207,27 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--summarize-stats", metavar="DIR",
+                    help="print a markdown table of a rocprofv3 --stats output directory")
+    ap.add_argument("--summarize-traffic", nargs=5,
+                    metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="print the HBM traffic summary of KERNEL from FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--copy-mib", type=int, default=256)
     args = ap.parse_args()
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats))
+        return 0
+    if args.summarize_traffic:
+        import synthetic as syn
+        w = syn.single_cell(args.seed, tensors=())
+        print(summarize_traffic(*args.summarize_traffic, args.copy_mib, w,
+                                "single_cell_b32h8d64_lognormal800"))
+        return 0
+    if args.copy_reference_mib:
+        copy_reference(args.copy_reference_mib)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by batch entry and head without any exchange).", file=sys.stderr)
