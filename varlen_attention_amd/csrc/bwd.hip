@@ -74,15 +74,18 @@ __device__ __forceinline__ void zero_rows(bf16 *base, int64_t sl, int r0, int ro
     }
 }
 
-// acc[db][4i + j] holds X^T[32 db + 8 i + 4 hh + j][row]; store scale * X[row][:].
+// acc[db][4i + j] holds X^T[32 db + 8 i + 4 hh + j][row]; store scale * X[row][:],
+// or exact zeros for a padded row.
 template <int D>
-__device__ __forceinline__ void store_rows_t(bf16 *rowp, const f32x16 *acc, float scale, int hh) {
+__device__ __forceinline__ void store_rows_t(bf16 *rowp, const f32x16 *acc, float scale, int hh,
+                                             bool row_valid) {
+    auto out = [&](float x) { return keep_or_zero(x * scale, row_valid); };
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bf16x4 v4 = pack4(acc[db][4 * i] * scale, acc[db][4 * i + 1] * scale,
-                                    acc[db][4 * i + 2] * scale, acc[db][4 * i + 3] * scale);
+            const bf16x4 v4 = pack4(out(acc[db][4 * i]), out(acc[db][4 * i + 1]),
+                                    out(acc[db][4 * i + 2]), out(acc[db][4 * i + 3]));
             *reinterpret_cast<bf16x4 *>(rowp + db * 32 + i * 8 + hh * 4) = v4;
         }
 }
@@ -125,7 +128,7 @@ __host__ __forceinline__ dim3 xcd_grid(int ntiles, int B, int H) {
 }  // namespace
 
 // ---------------------------------------------------------------- dK / dV
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, bool MASKED>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dkdv_kernel(const AttnParams p) {
     constexpr int BKV = 32 * NW, BQ = 32 * QB, NT = 64 * NW;
@@ -157,7 +160,7 @@ bwd_dkdv_kernel(const AttnParams p) {
     const bool k_valid = key < n;
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const bool has_mask = p.mask != nullptr;
+    const bool has_mask = MASKED;
     const rsrc_t rmask = make_rsrc(has_mask ? p.mask + (int64_t)b * L * L : nullptr,
                                    has_mask ? (int64_t)L * L : 0);
 
@@ -198,8 +201,10 @@ bwd_dkdv_kernel(const AttnParams p) {
         if (nxt >= 0) stage.load(rows_rsrc(qb, nxt * BQ), rows_rsrc(dob, nxt * BQ));
         const bf16 *Qc = Qs[buf];
         const bf16 *dOc = dOs[buf];
-        // One straight-line body per tile kind (0: inside [0, n)^2 without an
-        // element mask; 1: padding boundary; 2: element mask).
+        // One straight-line body per tile kind.  MODE 0 (no element mask)
+        // needs no per-element masking: padded query rows of Q and dO read as
+        // zeros, so dP = 0 and dS = 0 there and their dV terms multiply zero
+        // rows; padded key rows are zeroed at the store.  MODE 2: element mask.
         auto tile = [&](auto mode_tag) {
             constexpr int MODE = decltype(mode_tag)::value;
 #pragma unroll
@@ -212,23 +217,15 @@ bwd_dkdv_kernel(const AttnParams p) {
                                 dp);
                 }
                 // s[4i + j] = S[query q0 + 32 qb2 + 8 i + 4 hh + j][key]
-                uint8_t mk[16];
-                if constexpr (MODE == 2) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int qr = q0 + qb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                        mk[r] = buffer_load_u8(rmask, qr * L + key);
-                    }
-                }
                 float pv[16], dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float pr = sigmoid_from(s[r], c1, c0);
-                    if constexpr (MODE != 0) {
+                    if constexpr (MODE == 2) {
                         const int qr = q0 + qb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                        bool ok = k_valid && qr < n;
-                        if constexpr (MODE == 2) ok = ok && mk[r] != 0;
-                        pr = ok ? pr : 0.0f;
+                        const bool ok = k_valid && qr < n &&
+                                        buffer_load_u8(rmask, qr * L + key) != 0;
+                        pr = keep_or_zero(pr, ok);
                     }
                     pv[r] = pr;
                     dsv[r] = dp[r] * (pr - pr * pr);
@@ -246,25 +243,20 @@ bwd_dkdv_kernel(const AttnParams p) {
                 }
             }
         };
-        if ((q0 + BQ <= n) && (k0 + BKV <= n) && !has_mask)
-            tile(std::integral_constant<int, 0>{});
-        else if (!has_mask)
-            tile(std::integral_constant<int, 1>{});
-        else
-            tile(std::integral_constant<int, 2>{});
+        tile(std::integral_constant<int, MASKED ? 2 : 0>{});
         if (nxt >= 0) stage.store(Qs[buf ^ 1], dOs[buf ^ 1]);
         __syncthreads();
         buf ^= 1;
         qt = nxt;
     }
     if (key < L) {
-        store_rows_t<D>(dvb + (int64_t)key * p.osl, dvt, 1.0f, hh);
-        store_rows_t<D>(dkb + (int64_t)key * p.osl, dkt, p.scale, hh);
+        store_rows_t<D>(dvb + (int64_t)key * p.osl, dvt, 1.0f, hh, k_valid);
+        store_rows_t<D>(dkb + (int64_t)key * p.osl, dkt, p.scale, hh, k_valid);
     }
 }
 
 // ---------------------------------------------------------------- dQ
-template <int D, int NW, int KB>
+template <int D, int NW, int KB, bool MASKED>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dq_kernel(const AttnParams p) {
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
@@ -293,7 +285,7 @@ bwd_dq_kernel(const AttnParams p) {
     const bool q_valid = qr < n;
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const bool has_mask = p.mask != nullptr;
+    const bool has_mask = MASKED;
     const rsrc_t rmask = make_rsrc(has_mask ? p.mask + (int64_t)b * L * L : nullptr,
                                    has_mask ? (int64_t)L * L : 0);
     const int mrow_off = qr * L;
@@ -334,6 +326,9 @@ bwd_dq_kernel(const AttnParams p) {
         if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
         const bf16 *Kc = Ks[buf];
         const bf16 *Vc = Vs[buf];
+        // MODE 0 (no element mask): padded key rows of K and V read as zeros,
+        // so dP = 0 and dS = 0 there; padded query rows are zeroed at the
+        // store.  MODE 2: element mask.
         auto tile = [&](auto mode_tag) {
             constexpr int MODE = decltype(mode_tag)::value;
 #pragma unroll
@@ -346,22 +341,15 @@ bwd_dq_kernel(const AttnParams p) {
                                 dp);
                 }
                 // s[4i + j] = S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr]
-                uint8_t mk[16];
-                if constexpr (MODE == 2) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        mk[r] = buffer_load_u8(rmask, mrow_off + k0 + kb2 * 32 + (r >> 2) * 8 +
-                                                          hh * 4 + (r & 3));
-                }
                 float dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float pr = sigmoid_from(s[r], c1, c0);
-                    if constexpr (MODE != 0) {
+                    if constexpr (MODE == 2) {
                         const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                        bool ok = q_valid && key < n;
-                        if constexpr (MODE == 2) ok = ok && mk[r] != 0;
-                        pr = ok ? pr : 0.0f;
+                        const bool ok = q_valid && key < n &&
+                                        buffer_load_u8(rmask, mrow_off + key) != 0;
+                        pr = keep_or_zero(pr, ok);
                     }
                     dsv[r] = dp[r] * (pr - pr * pr);
                 }
@@ -375,18 +363,13 @@ bwd_dq_kernel(const AttnParams p) {
                 }
             }
         };
-        if ((k0 + BK <= n) && (q0 + BQ <= n) && !has_mask)
-            tile(std::integral_constant<int, 0>{});
-        else if (!has_mask)
-            tile(std::integral_constant<int, 1>{});
-        else
-            tile(std::integral_constant<int, 2>{});
+        tile(std::integral_constant<int, MASKED ? 2 : 0>{});
         if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
         __syncthreads();
         buf ^= 1;
         kt = nxt;
     }
-    if (qr < L) store_rows_t<D>(dqb + (int64_t)qr * p.osl, dqt, p.scale, hh);
+    if (qr < L) store_rows_t<D>(dqb + (int64_t)qr * p.osl, dqt, p.scale, hh, q_valid);
 }
 
 template <int D>
@@ -398,9 +381,14 @@ static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
     const dim3 grid = xcd_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_DKDV_CASE(NW_, QB_)                                                     \
-    if (nw == NW_ && qb == QB_) {                                                       \
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, QB_>), grid, block, 0, stream, p);  \
-        return hipGetLastError();                                                       \
+    if (nw == NW_ && qb == QB_) {                                                        \
+        if (p.mask != nullptr)                                                           \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, QB_, true>), grid, block, 0,     \
+                               stream, p);                                               \
+        else                                                                             \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, QB_, false>), grid, block, 0,    \
+                               stream, p);                                               \
+        return hipGetLastError();                                                        \
     }
     SIGATTN_DKDV_CASE(4, 2)
     SIGATTN_DKDV_CASE(4, 1)
@@ -421,9 +409,14 @@ static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     const dim3 grid = xcd_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_DQ_CASE(NW_, KB_)                                                     \
-    if (nw == NW_ && kb == KB_) {                                                     \
-        hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_>), grid, block, 0, stream, p);  \
-        return hipGetLastError();                                                     \
+    if (nw == NW_ && kb == KB_) {                                                        \
+        if (p.mask != nullptr)                                                           \
+            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, true>), grid, block, 0,       \
+                               stream, p);                                               \
+        else                                                                             \
+            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, false>), grid, block, 0,      \
+                               stream, p);                                               \
+        return hipGetLastError();                                                        \
     }
     SIGATTN_DQ_CASE(4, 2)
     SIGATTN_DQ_CASE(4, 1)

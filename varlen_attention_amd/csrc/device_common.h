@@ -169,6 +169,16 @@ __device__ __forceinline__ float sigmoid_from(float acc, float c1, float c0) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(acc, c1, c0)));
 }
 
+// Branch-free select: x where keep, else 0 (a bit mask, so the compiler does
+// not turn the choice into control flow around the work that produced x).
+__device__ __forceinline__ float keep_or_zero(float x, bool keep) {
+    return __uint_as_float(__float_as_uint(x) & (keep ? 0xffffffffu : 0u));
+}
+
+__device__ __forceinline__ float keep_or_neg_inf(float x, bool keep) {
+    return keep ? x : -INFINITY;
+}
+
 __device__ __forceinline__ float bias_value(int mode, int n, int L) {
     if (mode == kBiasLogSeqlen) return -logf((float)n);
     if (mode == kBiasLogPadlen) return -logf((float)L);

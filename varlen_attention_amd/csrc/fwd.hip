@@ -78,7 +78,7 @@ struct KVStage {
 
 }  // namespace
 
-template <int D, int VARIANT, int NW, int KB>
+template <int D, int VARIANT, int NW, int KB, bool MASKED>
 __global__ void __launch_bounds__(64 * NW, 2)
 fwd_kernel(const AttnParams p) {
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
@@ -125,7 +125,7 @@ fwd_kernel(const AttnParams p) {
     const int ql = lane & 31, hh = lane >> 5;
     const int qr = q0 + w * 32 + ql;  // this lane's query row
     const bool q_valid = qr < n;
-    const bool has_mask = p.mask != nullptr;
+    const bool has_mask = MASKED;
     const rsrc_t rmask = make_rsrc(has_mask ? p.mask + (int64_t)b * L * L : nullptr,
                                    has_mask ? (int64_t)L * L : 0);
     const int mrow_off = qr * L;
@@ -176,10 +176,14 @@ fwd_kernel(const AttnParams p) {
         const bf16 *Kc = Ks[buf];
         const bf16 *Vc = Vs[buf];
 
-        // One straight-line body per tile kind, so the scheduler can overlap
-        // the MFMAs of one key block with the epilogue of another.
-        // MODE 0: tile inside [0, n) x [0, n), no element mask; 1: tile on the
-        // padding boundary; 2: element mask.
+        // One straight-line tile body per kernel instantiation, so the
+        // scheduler can overlap the MFMAs of one key block with the epilogue
+        // of another, and the accumulators stay in place across iterations.
+        // MODE 0: no per-element masking.  Padded key rows of K and V read as
+        // zeros, so for sigmoid their weights multiply zero rows, and padded
+        // query rows are zeroed at the store: every padding-only sigmoid tile
+        // is MODE 0.  MODE 1: softmax without an element mask (padded keys
+        // must not enter the row max and sum).  MODE 2: element mask.
         auto tile = [&](auto mode_tag) {
             constexpr int MODE = decltype(mode_tag)::value;
             // S^T for each 32-key block: sacc[kb2][4i + j] is
@@ -195,24 +199,22 @@ fwd_kernel(const AttnParams p) {
                     sacc[kb2] = mfma32(a, qreg[ks], sacc[kb2]);
                 }
             }
-            uint8_t mk[KB][16];
-            if constexpr (MODE == 2) {
+            // Per-element validity (MODE 1, 2), computed without branches.
+            bool ok[KB][16];
+            if constexpr (MODE != 0) {
 #pragma unroll
                 for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        mk[kb2][r] = buffer_load_u8(rmask, mrow_off + k0 + kb2 * 32 +
-                                                               (r >> 2) * 8 + hh * 4 + (r & 3));
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                        ok[kb2][r] = q_valid && key < n;
+                        if constexpr (MODE == 2)
+                            ok[kb2][r] = ok[kb2][r] &&
+                                         buffer_load_u8(rmask, mrow_off + key) != 0;
+                    }
             }
-            auto valid = [&](int kb2, int r) {
-                if constexpr (MODE == 0) return true;
-                const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                bool ok = q_valid && key < n;
-                if constexpr (MODE == 2) ok = ok && mk[kb2][r] != 0;
-                return ok;
-            };
 
-            float alpha = 1.0f, m_use = 0.0f;
+            float m_use = 0.0f;
             if constexpr (VARIANT != kSigmoid) {
                 // Online softmax: tile maximum over this lane's keys and its
                 // partner lane's (lane ^ 32), then rescale the state.
@@ -221,14 +223,15 @@ fwd_kernel(const AttnParams p) {
                 for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float t = fmaf(sacc[kb2][r], c1, c0);
-                        sacc[kb2][r] = valid(kb2, r) ? t : -INFINITY;
-                        tmax = fmaxf(tmax, sacc[kb2][r]);
+                        float t = fmaf(sacc[kb2][r], c1, c0);
+                        if constexpr (MODE != 0) t = keep_or_neg_inf(t, ok[kb2][r]);
+                        sacc[kb2][r] = t;
+                        tmax = fmaxf(tmax, t);
                     }
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
                 const float m_new = fmaxf(m_run, tmax);
                 m_use = m_new == -INFINITY ? 0.0f : m_new;
-                alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
                 m_run = m_new;
                 l_run *= alpha;
 #pragma unroll
@@ -242,8 +245,8 @@ fwd_kernel(const AttnParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     if constexpr (VARIANT == kSigmoid) {
-                        const float sg = sigmoid_from(sacc[kb2][r], c1, c0);
-                        pv[r] = valid(kb2, r) ? sg : 0.0f;
+                        pv[r] = sigmoid_from(sacc[kb2][r], c1, c0);
+                        if constexpr (MODE == 2) pv[r] = keep_or_zero(pv[r], ok[kb2][r]);
                     } else {
                         pv[r] = __builtin_amdgcn_exp2f(sacc[kb2][r] - m_use);
                         l_run += pv[r];
@@ -262,12 +265,7 @@ fwd_kernel(const AttnParams p) {
                 }
             }
         };
-        if ((k0 + BK <= n) && (q0 + BQ <= n) && !has_mask)
-            tile(std::integral_constant<int, 0>{});
-        else if (!has_mask)
-            tile(std::integral_constant<int, 1>{});
-        else
-            tile(std::integral_constant<int, 2>{});
+        tile(std::integral_constant<int, MASKED ? 2 : (VARIANT == kSigmoid ? 0 : 1)>{});
 
         if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
         __syncthreads();
@@ -288,13 +286,15 @@ fwd_kernel(const AttnParams p) {
     }
     if (qr < L) {
         bf16 *orow = ob + (int64_t)qr * p.osl;
+        // Padded query rows are exactly +0 whatever their (finite) accumulators hold.
+        auto out = [&](float x) { return keep_or_zero(x * inv, q_valid); };
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x16 &a = oacc[db];
-                const bf16x4 v4 = pack4(a[4 * i] * inv, a[4 * i + 1] * inv, a[4 * i + 2] * inv,
-                                        a[4 * i + 3] * inv);
+                const bf16x4 v4 = pack4(out(a[4 * i]), out(a[4 * i + 1]), out(a[4 * i + 2]),
+                                        out(a[4 * i + 3]));
                 *reinterpret_cast<bf16x4 *>(orow + db * 32 + i * 8 + hh * 4) = v4;
             }
     }
@@ -308,10 +308,15 @@ static hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
     const int64_t pairs_per_xcd = ((int64_t)p.B * p.H + 7) / 8;
     dim3 grid((unsigned)(8 * pairs_per_xcd * ((p.L + bq - 1) / bq)));
     dim3 block(64 * nw);
-#define SIGATTN_FWD_CASE(NW_, KB_)                                                        \
-    if (nw == NW_ && kb == KB_) {                                                         \
-        hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_>), grid, block, 0, stream, p); \
-        return hipGetLastError();                                                         \
+#define SIGATTN_FWD_CASE(NW_, KB_)                                                         \
+    if (nw == NW_ && kb == KB_) {                                                          \
+        if (p.mask != nullptr)                                                             \
+            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, true>), grid, block, 0,   \
+                               stream, p);                                                 \
+        else                                                                               \
+            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, false>), grid, block, 0,  \
+                               stream, p);                                                 \
+        return hipGetLastError();                                                          \
     }
     SIGATTN_FWD_CASE(4, 2)
     SIGATTN_FWD_CASE(4, 1)
