@@ -107,24 +107,6 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16 *tile, int r16, int c32,
                 lds_read_tr4(tile + swz_off<D>(r + 8, c32 + tcol)));
 }
 
-// Workgroups are dealt to the 8 XCDs round-robin by linear index; give XCD
-// x = i % 8 the (batch entry, head) pairs x, x + 8, ... so that all tiles of
-// one pair share that XCD's L2.  Returns false for indices past the last pair.
-__device__ __forceinline__ bool xcd_item(int ntiles, int B, int H, int &b, int &h, int &t) {
-    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
-    const int pair = x + 8 * (k / ntiles);
-    if (pair >= B * H) return false;
-    t = k % ntiles;
-    h = pair % H;
-    b = pair / H;
-    return true;
-}
-
-__host__ __forceinline__ dim3 xcd_grid(int ntiles, int B, int H) {
-    const int64_t pairs_per_xcd = ((int64_t)B * H + 7) / 8;
-    return dim3((unsigned)(8 * pairs_per_xcd * ntiles));
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------- dK / dV
@@ -137,7 +119,7 @@ bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 dOs[2][BQ * D];
 
     int b, h, kt;
-    if (!xcd_item((p.L + BKV - 1) / BKV, p.B, p.H, b, h, kt)) return;
+    if (!lpt_xcd_item(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
     const int n = clamp_len(p.seq_lens[b], L);
@@ -265,7 +247,7 @@ bwd_dq_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * D];
 
     int b, h, qt;
-    if (!xcd_item((p.L + BQ - 1) / BQ, p.B, p.H, b, h, qt)) return;
+    if (!lpt_xcd_item(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
     const int n = clamp_len(p.seq_lens[b], L);
@@ -374,11 +356,11 @@ bwd_dq_kernel(const AttnParams p) {
 
 template <int D>
 static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
-    // 32*NW keys per workgroup must divide block_k; 32*QB queries per step
-    // must divide block_q.
+    // 32*NW keys per workgroup must divide block_k; queries are visited 32 at
+    // a time (QB = 1), which keeps the staging registers low.
     const int nw = p.block_k >= 128 ? 4 : p.block_k / 32;
-    const int qb = p.block_q >= 64 ? 2 : 1;
-    const dim3 grid = xcd_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
+    const int qb = 1;
+    const dim3 grid = lpt_xcd_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_DKDV_CASE(NW_, QB_)                                                     \
     if (nw == NW_ && qb == QB_) {                                                        \
@@ -390,11 +372,8 @@ static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
                                stream, p);                                               \
         return hipGetLastError();                                                        \
     }
-    SIGATTN_DKDV_CASE(4, 2)
     SIGATTN_DKDV_CASE(4, 1)
-    SIGATTN_DKDV_CASE(2, 2)
     SIGATTN_DKDV_CASE(2, 1)
-    SIGATTN_DKDV_CASE(1, 2)
     SIGATTN_DKDV_CASE(1, 1)
 #undef SIGATTN_DKDV_CASE
     return hipErrorInvalidValue;
@@ -406,7 +385,7 @@ static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     // must divide block_k.
     const int nw = p.block_q >= 128 ? 4 : p.block_q / 32;
     const int kb = p.block_k >= 64 ? 2 : 1;
-    const dim3 grid = xcd_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
+    const dim3 grid = lpt_xcd_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_DQ_CASE(NW_, KB_)                                                     \
     if (nw == NW_ && kb == KB_) {                                                        \

@@ -126,6 +126,47 @@ struct TileSchedule {
     }
 };
 
+// Batch entry holding length rank r (0 = longest; ties by index), so that the
+// longest sequences are dispatched first and the shortest fill the tail.
+// Computed by one wave: lane b ranks batch entry b against all others read
+// back with readlane, then a ballot finds the lane whose rank is r.  Batches
+// of more than 64 entries keep their natural order.
+__device__ __forceinline__ int batch_by_rank(const int32_t *seq_lens, int B, int L, int r) {
+    if (B > 64) return r;
+    const int lane = (int)(threadIdx.x & 63);
+    const int n = lane < B ? clamp_len(seq_lens[lane], L) : -1;
+    int rank = 0;
+    for (int c = 0; c < B; ++c) {
+        const int m = __builtin_amdgcn_readlane(n, c);
+        rank += (m > n) || (m == n && c < lane);
+    }
+    const uint64_t hit = __ballot(lane < B && rank == r);
+    return __builtin_ctzll(hit);
+}
+
+// Work item of a workgroup in a launch over (batch entry, head, tile) items.
+// Workgroups are dealt to the 8 XCDs round-robin by linear index and each XCD
+// has its own L2, so XCD x = i % 8 gets the pairs x, x + 8, ... of the
+// (length rank, head) order: all tiles of one (batch entry, head) share an
+// L2, every XCD gets one head of each batch entry when H is a multiple of 8,
+// and every XCD works through the longest sequences first.  Returns false
+// past the last pair.
+__device__ __forceinline__ bool lpt_xcd_item(const int32_t *seq_lens, int B, int H, int L,
+                                             int ntiles, int &b, int &h, int &t) {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    const int pair = x + 8 * (k / ntiles);
+    if (pair >= B * H) return false;
+    t = k % ntiles;
+    h = pair % H;
+    b = batch_by_rank(seq_lens, B, L, pair / H);
+    return true;
+}
+
+__host__ __forceinline__ dim3 lpt_xcd_grid(int ntiles, int B, int H) {
+    const int64_t pairs_per_xcd = ((int64_t)B * H + 7) / 8;
+    return dim3((unsigned)(8 * pairs_per_xcd * ntiles));
+}
+
 // Unpadded row-major [rows][D] bf16 tile in LDS with an XOR swizzle: the
 // 16-byte chunk c of row r sits at chunk position c ^ swz(r).  swz maps any 8
 // consecutive rows to 8 distinct chunk positions (16-byte reads of one

@@ -88,16 +88,8 @@ fwd_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][BK * KP];
     __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * VP];
 
-    // Workgroups are dealt to the 8 XCDs round-robin by linear index, and each
-    // XCD has its own L2.  Map index i to XCD slot x = i % 8 and give XCD x the
-    // (batch entry, head) pairs P = x, x + 8, ...: all query tiles of one
-    // pair share an L2, and with H a multiple of 8 every XCD gets one head of
-    // every batch entry (equal work).
-    const int nqt = (p.L + BQ - 1) / BQ;
-    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
-    const int pair = x + 8 * (k / nqt);
-    if (pair >= p.B * p.H) return;
-    const int qt = k % nqt, h = pair % p.H, b = pair / p.H;
+    int b, h, qt;
+    if (!lpt_xcd_item(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
     const int n = clamp_len(p.seq_lens[b], L);
@@ -305,8 +297,7 @@ static hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
     const int nw = p.block_q >= 128 ? 4 : p.block_q / 32;
     const int kb = p.block_k >= 64 ? 2 : 1;
     const int bq = 32 * nw;
-    const int64_t pairs_per_xcd = ((int64_t)p.B * p.H + 7) / 8;
-    dim3 grid((unsigned)(8 * pairs_per_xcd * ((p.L + bq - 1) / bq)));
+    const dim3 grid = lpt_xcd_grid((p.L + bq - 1) / bq, p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_FWD_CASE(NW_, KB_)                                                         \
     if (nw == NW_ && kb == KB_) {                                                          \
