@@ -312,6 +312,32 @@ def test_backward_small(va, d, L, bq, bk, bias, with_mask):
     assert_rows(gpu_f64(dv), wv, n, "dV")
 
 
+@pytest.mark.parametrize("B,H", [(70, 3), (64, 1), (9, 5)])
+def test_many_batch_entries_forward_backward(va, B, H):
+    """Dispatch order over many (batch entry, head) pairs: more than 64 batch
+    entries (natural order), exactly 64 (sorted in one wave), and pair counts
+    that do not divide over 8 XCDs; lengths include 0, 1 and L."""
+    L, d = 96, 64
+    rng = np.random.default_rng(B * 100 + H)
+    n = rng.integers(0, L + 1, size=B).astype(np.int32)
+    n[0], n[1], n[-1] = 0, L, 1
+    q, k, v, do = _inputs(4000 + B + H, B, H, L, d, n, names="qkvd")
+    say(f"many batch entries B={B} H={H}")
+    n_gpu = to_gpu(n, torch.int32)
+    bm = _bm(va, n_gpu, L, 32, 32)
+    args = [to_gpu_bf16(t) for t in (q, k, v)]
+    o = va.sigattn_fwd(*args, n_gpu, block_mask=bm, block_q=32, block_k=32)
+    dq, dk, dv = va.sigattn_bwd(*args, to_gpu_bf16(do), n_gpu, block_mask=bm, block_q=32,
+                                block_k=32)
+    torch.cuda.synchronize()
+    want_o, _ = oracle.fwd(q, k, v, n)
+    assert_rows(gpu_f64(o), want_o, n, "O many batch entries")
+    wq, wk, wv = oracle.bwd(q, k, v, do, n)
+    assert_rows(gpu_f64(dq), wq, n, "dQ many batch entries")
+    assert_rows(gpu_f64(dk), wk, n, "dK many batch entries")
+    assert_rows(gpu_f64(dv), wv, n, "dV many batch entries")
+
+
 def test_backward_poison_determinism_and_identities(va):
     B, H, L, d = 3, 2, 333, 64
     n = np.array([333, 180, 40], np.int32)

@@ -118,11 +118,10 @@ bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * D];
     __shared__ __attribute__((aligned(16))) bf16 dOs[2][BQ * D];
 
-    int b, h, kt;
-    if (!lpt_xcd_item(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt)) return;
+    int b, h, kt, n;
+    if (!tile_item<BKV>(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt, n)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
-    const int n = clamp_len(p.seq_lens[b], L);
     const int k0 = kt * BKV;
     bf16 *dkb = reinterpret_cast<bf16 *>(p.dk) + b * p.osb + h * p.osh;
     bf16 *dvb = reinterpret_cast<bf16 *>(p.dv) + b * p.osb + h * p.osh;
@@ -166,14 +165,17 @@ bwd_dkdv_kernel(const AttnParams p) {
     auto rows_rsrc = [&](const bf16 *base, int r0) {
         return make_rsrc(base + (int64_t)r0 * p.sl, (int64_t)(n - r0) * p.sl * 2);
     };
+    // Query tile 0 is fetched before the block mask is read (see the forward
+    // kernel); another first tile is fetched again.
+    PairStage<D, BQ, NT> stage;
+    stage.init(p.sl, tid);
+    stage.load(rows_rsrc(qb, 0), rows_rsrc(dob, 0));
     TileSchedule<BQ> sched;
     sched.init(p.block_mask ? p.block_mask + (int64_t)b * p.Tq * p.Tk + k0 / p.block_k : nullptr,
                p.Tk, n, p.block_q);
     int qt = sched.next();
-    PairStage<D, BQ, NT> stage;
-    stage.init(p.sl, tid);
+    if (qt > 0) stage.load(rows_rsrc(qb, qt * BQ), rows_rsrc(dob, qt * BQ));
     int buf = 0;
-    stage.load(rows_rsrc(qb, qt >= 0 ? qt * BQ : 0), rows_rsrc(dob, qt >= 0 ? qt * BQ : 0));
     stage.store(Qs[0], dOs[0]);
     __syncthreads();
 
@@ -246,11 +248,10 @@ bwd_dq_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][BK * D];
     __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * D];
 
-    int b, h, qt;
-    if (!lpt_xcd_item(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt)) return;
+    int b, h, qt, n;
+    if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
-    const int n = clamp_len(p.seq_lens[b], L);
     const int q0 = qt * BQ;
     bf16 *dqb = reinterpret_cast<bf16 *>(p.dq) + b * p.osb + h * p.osh;
     if (q0 >= n) {
@@ -291,14 +292,17 @@ bwd_dq_kernel(const AttnParams p) {
     auto rows_rsrc = [&](const bf16 *base, int r0) {
         return make_rsrc(base + (int64_t)r0 * p.sl, (int64_t)(n - r0) * p.sl * 2);
     };
+    // Key tile 0 is fetched before the block mask is read (see the forward
+    // kernel); another first tile is fetched again.
+    PairStage<D, BK, NT> stage;
+    stage.init(p.sl, tid);
+    stage.load(rows_rsrc(kb, 0), rows_rsrc(vb, 0));
     TileSchedule<BK> sched;
     sched.init(p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + q0 / p.block_q) * p.Tk : nullptr,
                1, n, p.block_k);
     int kt = sched.next();
-    PairStage<D, BK, NT> stage;
-    stage.init(p.sl, tid);
+    if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
     int buf = 0;
-    stage.load(rows_rsrc(kb, kt >= 0 ? kt * BK : 0), rows_rsrc(vb, kt >= 0 ? kt * BK : 0));
     stage.store(Ks[0], Vs[0]);
     __syncthreads();
 
@@ -360,7 +364,7 @@ static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
     // a time (QB = 1), which keeps the staging registers low.
     const int nw = p.block_k >= 128 ? 4 : p.block_k / 32;
     const int qb = 1;
-    const dim3 grid = lpt_xcd_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
+    const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_DKDV_CASE(NW_, QB_)                                                     \
     if (nw == NW_ && qb == QB_) {                                                        \
@@ -385,7 +389,7 @@ static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     // must divide block_k.
     const int nw = p.block_q >= 128 ? 4 : p.block_q / 32;
     const int kb = p.block_k >= 64 ? 2 : 1;
-    const dim3 grid = lpt_xcd_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
+    const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_DQ_CASE(NW_, KB_)                                                     \
     if (nw == NW_ && kb == KB_) {                                                        \

@@ -126,43 +126,87 @@ struct TileSchedule {
     }
 };
 
-// Batch entry holding length rank r (0 = longest; ties by index), so that the
-// longest sequences are dispatched first and the shortest fill the tail.
-// Computed by one wave: lane b ranks batch entry b against all others read
-// back with readlane, then a ballot finds the lane whose rank is r.  Batches
-// of more than 64 entries keep their natural order.
-__device__ __forceinline__ int batch_by_rank(const int32_t *seq_lens, int B, int L, int r) {
-    if (B > 64) return r;
+// Work item of a workgroup in a launch over (batch entry, head, tile) items,
+// ntiles tiles of ROWS rows per (batch entry, head).
+//
+// Placement: workgroups are dealt to the 8 XCDs round-robin by linear index
+// and each XCD has its own L2, so XCD x = i % 8 owns the pairs x, x + 8, ...
+// of the (length rank, head) order: all tiles of one (batch entry, head)
+// share an L2, and every XCD gets one head of each batch entry when H is a
+// multiple of 8.
+//
+// Order inside an XCD (its k-th workgroup, k = i / 8): first every tile that
+// holds valid rows, pair by pair from the longest sequence down (longest
+// processing time first), then the fully padded tiles, which only write
+// zeros and so fill the tail of the launch instead of holding slots while
+// long tiles are still waiting.
+//
+// Computed by every wave of the workgroup alike (the result is uniform):
+// lane b ranks batch entry b against all others (read back with readlane,
+// ties broken by index) and pushes its length to lane rank(b), so lane r
+// holds the r-th longest length; then wave prefix sums over the XCD's pairs
+// locate item k, 64 pairs at a time.  Batches of more than 64 entries keep
+// their natural order.  n is the clamped length of the chosen batch entry.
+// Returns false past the last item.
+template <int ROWS>
+__device__ __forceinline__ bool tile_item(const int32_t *seq_lens, int B, int H, int L,
+                                          int ntiles, int &b, int &h, int &t, int &n) {
     const int lane = (int)(threadIdx.x & 63);
-    const int n = lane < B ? clamp_len(seq_lens[lane], L) : -1;
-    int rank = 0;
-    for (int c = 0; c < B; ++c) {
-        const int m = __builtin_amdgcn_readlane(n, c);
-        rank += (m > n) || (m == n && c < lane);
+    const int x = blockIdx.x & 7;
+    int k = blockIdx.x >> 3;
+    const int pairs = B * H;
+    const int npx = pairs > x ? (pairs - x + 7) / 8 : 0;  // pairs owned by XCD x
+    int sorted_b = lane, sorted_n = 0;
+    if (B <= 64) {
+        const int nl = lane < B ? clamp_len(seq_lens[lane], L) : -1;
+        int rank = 0;
+        for (int c = 0; c < B; ++c) {
+            const int m = __builtin_amdgcn_readlane(nl, c);
+            rank += (m > nl) || (m == nl && c < lane);
+        }
+        // Lanes >= B all rank B (< 64) and only overwrite an unused lane.
+        sorted_b = __builtin_amdgcn_ds_permute(rank * 4, lane);
+        sorted_n = __builtin_amdgcn_ds_permute(rank * 4, nl);
     }
-    const uint64_t hit = __ballot(lane < B && rank == r);
-    return __builtin_ctzll(hit);
+    for (int pass = 0; pass < 2; ++pass) {  // 0: tiles with valid rows, 1: padded tiles
+        for (int j0 = 0; j0 < npx; j0 += 64) {
+            const int j = j0 + lane;
+            const bool valid = j < npx;
+            const int pair = x + 8 * (valid ? j : 0);
+            const int r = pair / H;
+            int bj, nj;
+            if (B <= 64) {
+                bj = __shfl(sorted_b, r);
+                nj = __shfl(sorted_n, r);
+            } else {
+                bj = r;
+                nj = clamp_len(seq_lens[r], L);
+            }
+            const int real_t = (nj + ROWS - 1) / ROWS;
+            const int cnt = valid ? (pass == 0 ? real_t : ntiles - real_t) : 0;
+            int incl = cnt;  // inclusive prefix sum over the wave
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int o = __shfl_up(incl, d);
+                if (lane >= d) incl += o;
+            }
+            const int total = __builtin_amdgcn_readlane(incl, 63);
+            if (k < total) {
+                const int jl = __builtin_ctzll(__ballot(incl > k));
+                const int before = __builtin_amdgcn_readlane(incl - cnt, jl);
+                h = __builtin_amdgcn_readlane(pair, jl) % H;
+                b = __builtin_amdgcn_readlane(bj, jl);
+                n = __builtin_amdgcn_readlane(nj, jl);
+                t = (pass == 0 ? 0 : __builtin_amdgcn_readlane(real_t, jl)) + (k - before);
+                return true;
+            }
+            k -= total;
+        }
+    }
+    return false;
 }
 
-// Work item of a workgroup in a launch over (batch entry, head, tile) items.
-// Workgroups are dealt to the 8 XCDs round-robin by linear index and each XCD
-// has its own L2, so XCD x = i % 8 gets the pairs x, x + 8, ... of the
-// (length rank, head) order: all tiles of one (batch entry, head) share an
-// L2, every XCD gets one head of each batch entry when H is a multiple of 8,
-// and every XCD works through the longest sequences first.  Returns false
-// past the last pair.
-__device__ __forceinline__ bool lpt_xcd_item(const int32_t *seq_lens, int B, int H, int L,
-                                             int ntiles, int &b, int &h, int &t) {
-    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
-    const int pair = x + 8 * (k / ntiles);
-    if (pair >= B * H) return false;
-    t = k % ntiles;
-    h = pair % H;
-    b = batch_by_rank(seq_lens, B, L, pair / H);
-    return true;
-}
-
-__host__ __forceinline__ dim3 lpt_xcd_grid(int ntiles, int B, int H) {
+__host__ __forceinline__ dim3 tile_grid(int ntiles, int B, int H) {
     const int64_t pairs_per_xcd = ((int64_t)B * H + 7) / 8;
     return dim3((unsigned)(8 * pairs_per_xcd * ntiles));
 }

@@ -88,11 +88,10 @@ fwd_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][BK * KP];
     __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * VP];
 
-    int b, h, qt;
-    if (!lpt_xcd_item(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt)) return;
+    int b, h, qt, n;
+    if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
-    const int n = clamp_len(p.seq_lens[b], L);
     const int q0 = qt * BQ;
     bf16 *ob = reinterpret_cast<bf16 *>(p.o) + b * p.osb + h * p.osh;
     float *lseb = p.lse ? p.lse + ((int64_t)b * p.H + h) * L : nullptr;
@@ -149,15 +148,20 @@ fwd_kernel(const AttnParams p) {
     auto rows_rsrc = [&](const bf16 *base, int k0) {
         return make_rsrc(base + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
     };
+    // The first active key tile is tile 0 unless the block mask says
+    // otherwise, so tile 0 is fetched before the block mask is read and the
+    // two memory round trips overlap; another first tile is fetched again.
+    // The first stage is written unconditionally (tile 0 when nothing is
+    // active, harmless): every path into the loop has then waited for all
+    // earlier loads, Q included.
+    KVStage<D, BK, NT> stage;
+    stage.init(p.sl, tid);
+    stage.load(rows_rsrc(kb, 0), rows_rsrc(vb, 0));
     TileSchedule<BK> sched;
     sched.init(bm_row, 1, n, p.block_k);
     int kt = sched.next();
-    KVStage<D, BK, NT> stage;
-    stage.init(p.sl, tid);
+    if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
     int buf = 0;
-    // Staged unconditionally (tile 0 when nothing is active, harmless): every
-    // path into the loop has then waited for all earlier loads, Q included.
-    stage.load(rows_rsrc(kb, kt >= 0 ? kt * BK : 0), rows_rsrc(vb, kt >= 0 ? kt * BK : 0));
     stage.store(Ks[0], Vs[0]);
     __syncthreads();
 
@@ -297,7 +301,7 @@ static hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
     const int nw = p.block_q >= 128 ? 4 : p.block_q / 32;
     const int kb = p.block_k >= 64 ? 2 : 1;
     const int bq = 32 * nw;
-    const dim3 grid = lpt_xcd_grid((p.L + bq - 1) / bq, p.B, p.H);
+    const dim3 grid = tile_grid((p.L + bq - 1) / bq, p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_FWD_CASE(NW_, KB_)                                                         \
     if (nw == NW_ && kb == KB_) {                                                          \
