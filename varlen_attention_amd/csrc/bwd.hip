@@ -155,8 +155,10 @@ bwd_dkdv_kernel(const AttnParams p) {
         kreg[ks] = as_bf16x8(buffer_load16(rk, off));
         vreg[ks] = as_bf16x8(buffer_load16(rv, off));
     }
-    const float beta = bias_value(p.bias_mode, n, L);
-    const float c1 = -p.scale * kLog2e, c0 = -beta * kLog2e;
+    // The operand held in registers for S is scaled by c1 before the loop, so
+    // the S accumulator is u = -scale * s * log2 e (see sigmoid_scaled).
+    const float c1 = -p.scale * kLog2e;
+    const float cexp = bias_factor(p.bias_mode, n, L);
 
     f32x16 dvt[DB], dkt[DB];
 #pragma unroll
@@ -177,6 +179,8 @@ bwd_dkdv_kernel(const AttnParams p) {
     if (qt > 0) stage.load(rows_rsrc(qb, qt * BQ), rows_rsrc(dob, qt * BQ));
     int buf = 0;
     stage.store(Qs[0], dOs[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kreg[ks] = scale8(kreg[ks], c1);
     __syncthreads();
 
     while (qt >= 0) {
@@ -204,7 +208,7 @@ bwd_dkdv_kernel(const AttnParams p) {
                 float pv[16], dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float pr = sigmoid_from(s[r], c1, c0);
+                    float pr = sigmoid_scaled(s[r], cexp);
                     if constexpr (MODE == 2) {
                         const int qr = q0 + qb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
                         const bool ok = k_valid && qr < n &&
@@ -282,8 +286,10 @@ bwd_dq_kernel(const AttnParams p) {
         qreg[ks] = as_bf16x8(buffer_load16(rq, off));
         doreg[ks] = as_bf16x8(buffer_load16(rdo, off));
     }
-    const float beta = bias_value(p.bias_mode, n, L);
-    const float c1 = -p.scale * kLog2e, c0 = -beta * kLog2e;
+    // The operand held in registers for S is scaled by c1 before the loop, so
+    // the S accumulator is u = -scale * s * log2 e (see sigmoid_scaled).
+    const float c1 = -p.scale * kLog2e;
+    const float cexp = bias_factor(p.bias_mode, n, L);
 
     f32x16 dqt[DB];
 #pragma unroll
@@ -304,6 +310,8 @@ bwd_dq_kernel(const AttnParams p) {
     if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
     int buf = 0;
     stage.store(Ks[0], Vs[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qreg[ks] = scale8(qreg[ks], c1);
     __syncthreads();
 
     while (kt >= 0) {
@@ -330,7 +338,7 @@ bwd_dq_kernel(const AttnParams p) {
                 float dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float pr = sigmoid_from(s[r], c1, c0);
+                    float pr = sigmoid_scaled(s[r], cexp);
                     if constexpr (MODE == 2) {
                         const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
                         const bool ok = q_valid && key < n &&

@@ -250,8 +250,22 @@ __device__ __forceinline__ bf16x4 pack4(float x0, float x1, float x2, float x3) 
 
 // sigma(s) with s = acc * scale + beta, evaluated as 1 / (1 + 2^u) where
 // u = acc * c1 + c0, c1 = -scale * log2(e), c0 = -beta * log2(e).
-__device__ __forceinline__ float sigmoid_from(float acc, float c1, float c0) {
-    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(acc, c1, c0)));
+// Sigmoid weight of one score.  The MFMA operand held in registers was
+// scaled by -scale * log2(e) beforehand (scale8), so the accumulator is
+// already u = -scale * (q . k) * log2(e), and with C = exp(-b):
+//   sigma(scale * (q . k) + b) = 1 / (1 + C * 2^u).
+// 2^u overflowing to +inf gives 0 and underflowing to 0 gives 1, the limits.
+__device__ __forceinline__ float sigmoid_scaled(float u, float cexp) {
+    return __builtin_amdgcn_rcpf(fmaf(__builtin_amdgcn_exp2f(u), cexp, 1.0f));
+}
+
+// Eight bf16 values times s, rounded back to bf16 (once per workgroup on the
+// operand held in registers: it folds the score scale into the dot product).
+__device__ __forceinline__ bf16x8 scale8(bf16x8 x, float s) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (float)x[e] * s;
+    return pack8(f);
 }
 
 // Branch-free select: x where keep, else 0 (a bit mask, so the compiler does
@@ -268,6 +282,13 @@ __device__ __forceinline__ float bias_value(int mode, int n, int L) {
     if (mode == kBiasLogSeqlen) return -logf((float)n);
     if (mode == kBiasLogPadlen) return -logf((float)L);
     return 0.0f;
+}
+
+// exp(-b) for the bias modes above: n, L or 1, exactly.
+__device__ __forceinline__ float bias_factor(int mode, int n, int L) {
+    if (mode == kBiasLogSeqlen) return (float)n;
+    if (mode == kBiasLogPadlen) return (float)L;
+    return 1.0f;
 }
 
 }  // namespace sigattn

@@ -133,10 +133,14 @@ fwd_kernel(const AttnParams p) {
         qreg[ks] = as_bf16x8(
             buffer_load16(rq, (int)(((int64_t)(w * 32 + ql) * p.sl + ks * 16 + hh * 8) * 2)));
 
-    const float beta = bias_value(p.bias_mode, n, L);
-    // SIGMOID: u = -(s) * log2 e; softmax: t = s * log2 e (log2-domain logits).
+    // SIGMOID: Q is scaled by c1 before the loop, so the S^T accumulator is
+    // u = -scale * s * log2 e and the weight is 1 / (1 + exp(-b) 2^u); the
+    // weight is rounded to bf16 for the PV product anyway.  Softmax keeps Q
+    // as it is and forms t = scale * s * log2 e + b * log2 e in fp32, since
+    // the log-sum-exp it returns would inherit the rounding of a scaled Q.
     const float c1 = VARIANT == kSigmoid ? -p.scale * kLog2e : p.scale * kLog2e;
-    const float c0 = VARIANT == kSigmoid ? -beta * kLog2e : beta * kLog2e;
+    const float c0 = bias_value(p.bias_mode, n, L) * kLog2e;
+    const float cexp = bias_factor(p.bias_mode, n, L);
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -163,6 +167,9 @@ fwd_kernel(const AttnParams p) {
     if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
     int buf = 0;
     stage.store(Ks[0], Vs[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        if constexpr (VARIANT == kSigmoid) qreg[ks] = scale8(qreg[ks], c1);
     __syncthreads();
 
     while (kt >= 0) {
@@ -241,7 +248,7 @@ fwd_kernel(const AttnParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     if constexpr (VARIANT == kSigmoid) {
-                        pv[r] = sigmoid_from(sacc[kb2][r], c1, c0);
+                        pv[r] = sigmoid_scaled(sacc[kb2][r], cexp);
                         if constexpr (MODE == 2) pv[r] = keep_or_zero(pv[r], ok[kb2][r]);
                     } else {
                         pv[r] = __builtin_amdgcn_exp2f(sacc[kb2][r] - m_use);
