@@ -79,6 +79,19 @@ __device__ __forceinline__ uint8_t buffer_load_u8(rsrc_t r, int byte_offset) {
     return __builtin_amdgcn_raw_buffer_load_b8(r, byte_offset, 0, 0);
 }
 
+// Buffer load that writes LDS instead of registers (gfx950, 16 bytes per
+// lane): lane l's 16 bytes at byte_offset land at lds + 16 * l, so one wave
+// instruction fills one contiguous KiB; lds must be the same in all lanes.
+// Out-of-range lanes write zeros, as a register load would return them.
+// Completion counts in vmcnt (wait_vm0 before a barrier that publishes it).
+__device__ __forceinline__ void lds_load16(rsrc_t r, void *lds, int byte_offset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds, 16, byte_offset, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0), leaving the other counters alone.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 // Iterates, in increasing order, the tiles of BT rows that one row (or one
 // column) of the block mask marks active, clipped to the n valid rows.  One
 // wave ballot reads 64 block-mask entries at a time; the result is uniform,
@@ -144,10 +157,25 @@ struct TileSchedule {
 // Computed by every wave of the workgroup alike (the result is uniform):
 // lane b ranks batch entry b against all others (read back with readlane,
 // ties broken by index) and pushes its length to lane rank(b), so lane r
-// holds the r-th longest length; then wave prefix sums over the XCD's pairs
-// locate item k, 64 pairs at a time.  Batches of more than 64 entries keep
+// holds the r-th longest length; then wave prefix sums (DPP) over the XCD's
+// pairs locate item k, 64 pairs at a time.  Batches of more than 64 entries keep
 // their natural order.  n is the clamped length of the chosen batch entry.
 // Returns false past the last item.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
+// round trips): row_shr 1, 2, 4, 8 scan each row of 16 lanes (lanes shifted
+// in from outside the row add 0), then row_bcast 15 adds row 0's total to row
+// 1 and row 2's to row 3, and row_bcast 31 adds the total of rows 0-1 to rows
+// 2 and 3.  Lanes a move does not write keep the 0 it starts from.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
 template <int ROWS>
 __device__ __forceinline__ bool tile_item(const int32_t *seq_lens, int B, int H, int L,
                                           int ntiles, int &b, int &h, int &t, int &n) {
@@ -184,12 +212,7 @@ __device__ __forceinline__ bool tile_item(const int32_t *seq_lens, int B, int H,
             }
             const int real_t = (nj + ROWS - 1) / ROWS;
             const int cnt = valid ? (pass == 0 ? real_t : ntiles - real_t) : 0;
-            int incl = cnt;  // inclusive prefix sum over the wave
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int o = __shfl_up(incl, d);
-                if (lane >= d) incl += o;
-            }
+            const int incl = wave_inclusive_scan(cnt);
             const int total = __builtin_amdgcn_readlane(incl, 63);
             if (k < total) {
                 const int jl = __builtin_ctzll(__ballot(incl > k));
