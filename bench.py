@@ -4,7 +4,7 @@ plus backward, on one MI355X.
 One step = the whole hot path over one synthetic single-cell-shaped batch
 (B32 H8 d64, log-normal lengths with median 800 clipped to [200, 2048], padded
 to the batch maximum, block 128, bias -ln n):
-  blockmask_build (from seq_lens) -> sigattn_fwd -> sigattn_bwd_dkdv -> sigattn_bwd_dq
+  blockmask_build (from seq_lens) -> sigattn_fwd -> sigattn_bwd (dK/dV and dQ, one launch)
 Inputs are resident in HBM before the timed region.  Valid FLOPs count only
 attended (query, key) pairs: 4 d per pair per head forward, 10 d backward.
 
@@ -31,8 +31,7 @@ PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "fwd": "varlen_attention_amd/csrc/fwd.hip",
-    "bwd_dkdv": "varlen_attention_amd/csrc/bwd.hip",
-    "bwd_dq": "varlen_attention_amd/csrc/bwd.hip",
+    "bwd": "varlen_attention_amd/csrc/bwd.hip",
     "blockmask": "varlen_attention_amd/csrc/blockmask.hip",
 }
 
@@ -76,7 +75,7 @@ def algorithmic_bytes(kernel: str, w) -> float:
     valid = float(np.clip(w.seq_lens, 0, w.L).sum()) * w.H
     every = float(w.B) * w.L * w.H
     row = 2.0 * w.d
-    reads, writes = {"fwd": (3, 1), "bwd_dkdv": (4, 2), "bwd_dq": (4, 1)}[kernel]
+    reads, writes = {"fwd": (3, 1), "bwd": (4, 3)}[kernel]
     return (reads * valid + writes * every) * row
 
 
@@ -94,8 +93,7 @@ def _find(dirname, suffix):
     raise FileNotFoundError(f"no *{suffix} under {dirname}")
 
 
-KERNEL_SYMBOLS = {"fwd": "fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
-                  "blockmask": "blockmask_"}
+KERNEL_SYMBOLS = {"fwd": "::fwd_kernel<", "bwd": "::bwd_kernel<", "blockmask": "blockmask_"}
 
 
 def summarize_stats(dirname: str) -> str:
@@ -309,7 +307,7 @@ def main() -> int:
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
-    names = ["blockmask", "fwd", "bwd_dkdv", "bwd_dq"]
+    names = ["blockmask", "fwd", "bwd"]
 
     timer = HipTimer(stream.cuda_stream)
 
@@ -322,17 +320,16 @@ def main() -> int:
         mark(1)
         va.sigattn_fwd(q, k, v, n, block_mask=bm, out=o, block_q=bq, block_k=bk)
         mark(2)
-        va.sigattn_bwd_dkdv(q, k, v, do, n, block_mask=bm, dk=dk, dv=dv, block_q=bq, block_k=bk)
+        va.sigattn_bwd(q, k, v, do, n, block_mask=bm, dq=dq, dk=dk, dv=dv, block_q=bq,
+                       block_k=bk)
         mark(3)
-        va.sigattn_bwd_dq(q, k, v, do, n, block_mask=bm, dq=dq, block_q=bq, block_k=bk)
-        mark(4)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    ev = [[timer.event() for _ in range(5)] for _ in range(args.steps)]
+    ev = [[timer.event() for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -351,8 +348,7 @@ def main() -> int:
     flops_bwd = 10.0 * d * H * pairs
     value = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
     # Per-kernel algorithmic FLOPs per launch: the GEMMs each kernel's output needs.
-    algo = {"fwd": 4.0 * d * H * pairs, "bwd_dkdv": 8.0 * d * H * pairs,
-            "bwd_dq": 6.0 * d * H * pairs}
+    algo = {"fwd": 4.0 * d * H * pairs, "bwd": 14.0 * d * H * pairs}
     dominant = max(algo, key=lambda k_: per_kernel[k_])
     achieved = algo[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
     traffic = read_traffic(dominant, workload)
@@ -381,7 +377,7 @@ def main() -> int:
         "config": {"workload": workload, "B": B, "H": H, "L": L, "d": d,
                    "sum_n": int(w.seq_lens.sum()), "valid_pairs_per_head": int(pairs),
                    "block": bq, "variant": "sigmoid", "bias": "-ln n", "seed": args.seed,
-                   "step": "blockmask_build + fwd + bwd_dkdv + bwd_dq",
+                   "step": "blockmask_build + fwd + bwd (dK/dV and dQ in one launch)",
                    "parallelism": "single GPU"},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "kernels": kernels,

@@ -134,8 +134,12 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
  *   seq_lens, block_mask, mask: as for sigattn_fwd
  *   dq, dk, dv      [device] bf16 [B, H, L, d] (output layout), fully written;
  *                   rows >= n are 0.
- * The two kernels write disjoint outputs and use no atomics, so results are
- * bit-for-bit reproducible.
+ * The dK/dV and dQ work items write disjoint outputs and use no atomics, so
+ * results are bit-for-bit reproducible and equal to those of the two calls
+ * below.  When the key tiles of dK/dV and the query tiles of dQ have the same
+ * height (block_q and block_k both >= 128, or equal), both kinds of work item
+ * go out in one launch, sharing one ramp-up and one tail; otherwise this is
+ * the two launches below.
  * Errors: as sigattn_fwd; UNSUPPORTED for a variant other than SIGMOID.
  */
 int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,

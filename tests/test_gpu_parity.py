@@ -338,6 +338,24 @@ def test_many_batch_entries_forward_backward(va, B, H):
     assert_rows(gpu_f64(dv), wv, n, "dV many batch entries")
 
 
+@pytest.mark.parametrize("bq,bk", [(128, 128), (64, 64), (128, 32)])
+def test_backward_parts_match_fused(va, bq, bk):
+    """sigattn_bwd (one launch for dK/dV and dQ when the tile heights agree,
+    two otherwise) equals sigattn_bwd_dkdv + sigattn_bwd_dq bit for bit."""
+    B, H, L, d = 5, 3, 290, 64
+    n = np.array([290, 0, 161, 33, 128], np.int32)
+    q, k, v, do = (to_gpu_bf16(t) for t in _inputs(91, B, H, L, d, n, names="qkvd"))
+    n_gpu = to_gpu(n, torch.int32)
+    bm = _bm(va, n_gpu, L, bq, bk)
+    say(f"bwd parts vs fused bq={bq} bk={bk}")
+    dq, dk, dv = va.sigattn_bwd(q, k, v, do, n_gpu, block_mask=bm, block_q=bq, block_k=bk)
+    dk2, dv2 = va.sigattn_bwd_dkdv(q, k, v, do, n_gpu, block_mask=bm, block_q=bq, block_k=bk)
+    dq2 = va.sigattn_bwd_dq(q, k, v, do, n_gpu, block_mask=bm, block_q=bq, block_k=bk)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_backward_poison_determinism_and_identities(va):
     B, H, L, d = 3, 2, 333, 64
     n = np.array([333, 180, 40], np.int32)

@@ -213,7 +213,10 @@ def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k
 def sigattn_bwd(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                 variant=SIGMOID, scale=None, block_q=128, block_k=128, dq=None, dk=None,
                 dv=None, stream=None):
-    """Gradients (dq, dk, dv) of sum(dout * o); bf16 [B, H, L, d] on the GPU."""
+    """Gradients (dq, dk, dv) of sum(dout * o); bf16 [B, H, L, d] on the GPU.
+
+    One launch for the dK/dV and dQ work when their tile heights agree (see
+    include/sigattn.h); results equal sigattn_bwd_dkdv + sigattn_bwd_dq."""
     dq, dk, dv = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dq, dk, dv), block_q,
                            block_k)
     shape = _shape(q, dq.stride(), scale, block_q, block_k)

@@ -177,12 +177,9 @@ int backward(const sigattn_shape *shape, const void *q, const void *k, const voi
     p.dk = dk;
     p.dv = dv;
     hipStream_t s = (hipStream_t)stream;
-    if (parts & kPartDkdv) {
-        st = launch_status(sigattn::launch_bwd_dkdv(p, s), name);
-        if (st != SIGATTN_OK) return st;
-    }
-    if (parts & kPartDq) return launch_status(sigattn::launch_bwd_dq(p, s), name);
-    return ok();
+    if (parts == (kPartDkdv | kPartDq)) return launch_status(sigattn::launch_bwd(p, s), name);
+    if (parts & kPartDkdv) return launch_status(sigattn::launch_bwd_dkdv(p, s), name);
+    return launch_status(sigattn::launch_bwd_dq(p, s), name);
 }
 
 }  // namespace

@@ -110,16 +110,22 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16 *tile, int r16, int c32,
 }  // namespace
 
 // ---------------------------------------------------------------- dK / dV
-template <int D, int NW, int QB, bool MASKED>
-__global__ void __launch_bounds__(64 * NW, 2)
-bwd_dkdv_kernel(const AttnParams p) {
+// LDS of one dK/dV tile (elements): Q and dO tiles of 32 rows, double-buffered.
+template <int D> constexpr int kDkdvLds = 2 * 2 * 32 * D;
+
+// dK and dV of key tile kt (32 NW keys) of (batch entry b, head h); smem
+// holds kDkdvLds<D> elements.
+template <int D, int NW, bool MASKED>
+__device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int kt, int n,
+                                          bf16 *smem) {
+    constexpr int QB = 1;
     constexpr int BKV = 32 * NW, BQ = 32 * QB, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * D];
-    __shared__ __attribute__((aligned(16))) bf16 dOs[2][BQ * D];
+    // Slot i of the Q and dO tiles (offsets from the LDS base, so the LDS
+    // address space stays visible to the compiler).
+    auto Qs = [&](int i) { return smem + i * (BQ * D); };
+    auto dOs = [&](int i) { return smem + (2 + i) * (BQ * D); };
 
-    int b, h, kt, n;
-    if (!tile_item<BKV>(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt, n)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
     const int k0 = kt * BKV;
@@ -178,7 +184,7 @@ bwd_dkdv_kernel(const AttnParams p) {
     int qt = sched.next();
     if (qt > 0) stage.load(rows_rsrc(qb, qt * BQ), rows_rsrc(dob, qt * BQ));
     int buf = 0;
-    stage.store(Qs[0], dOs[0]);
+    stage.store(Qs(0), dOs(0));
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kreg[ks] = scale8(kreg[ks], c1);
     __syncthreads();
@@ -187,8 +193,8 @@ bwd_dkdv_kernel(const AttnParams p) {
         const int q0 = qt * BQ;
         const int nxt = sched.next();
         if (nxt >= 0) stage.load(rows_rsrc(qb, nxt * BQ), rows_rsrc(dob, nxt * BQ));
-        const bf16 *Qc = Qs[buf];
-        const bf16 *dOc = dOs[buf];
+        const bf16 *Qc = Qs(buf);
+        const bf16 *dOc = dOs(buf);
         // One straight-line body per tile kind.  MODE 0 (no element mask)
         // needs no per-element masking: padded query rows of Q and dO read as
         // zeros, so dP = 0 and dS = 0 there and their dV terms multiply zero
@@ -232,7 +238,7 @@ bwd_dkdv_kernel(const AttnParams p) {
             }
         };
         tile(std::integral_constant<int, MASKED ? 2 : 0>{});
-        if (nxt >= 0) stage.store(Qs[buf ^ 1], dOs[buf ^ 1]);
+        if (nxt >= 0) stage.store(Qs(buf ^ 1), dOs(buf ^ 1));
         __syncthreads();
         buf ^= 1;
         qt = nxt;
@@ -244,16 +250,19 @@ bwd_dkdv_kernel(const AttnParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
+// LDS of one dQ tile (elements): K and V tiles of 32 KB rows, double-buffered.
+template <int D, int KB> constexpr int kDqLds = 2 * 2 * 32 * KB * D;
+
+// dQ of query tile qt (32 NW queries) of (batch entry b, head h), visiting
+// keys 32 KB at a time; smem holds kDqLds<D, KB> elements.
 template <int D, int NW, int KB, bool MASKED>
-__global__ void __launch_bounds__(64 * NW, 2)
-bwd_dq_kernel(const AttnParams p) {
+__device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int qt, int n,
+                                        bf16 *smem) {
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][BK * D];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * D];
+    auto Ks = [&](int i) { return smem + i * (BK * D); };
+    auto Vs = [&](int i) { return smem + (2 + i) * (BK * D); };
 
-    int b, h, qt, n;
-    if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
     const int q0 = qt * BQ;
@@ -309,7 +318,7 @@ bwd_dq_kernel(const AttnParams p) {
     int kt = sched.next();
     if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
     int buf = 0;
-    stage.store(Ks[0], Vs[0]);
+    stage.store(Ks(0), Vs(0));
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qreg[ks] = scale8(qreg[ks], c1);
     __syncthreads();
@@ -318,8 +327,8 @@ bwd_dq_kernel(const AttnParams p) {
         const int k0 = kt * BK;
         const int nxt = sched.next();
         if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
-        const bf16 *Kc = Ks[buf];
-        const bf16 *Vc = Vs[buf];
+        const bf16 *Kc = Ks(buf);
+        const bf16 *Vc = Vs(buf);
         // MODE 0 (no element mask): padded key rows of K and V read as zeros,
         // so dP = 0 and dS = 0 there; padded query rows are zeroed at the
         // store.  MODE 2: element mask.
@@ -358,7 +367,7 @@ bwd_dq_kernel(const AttnParams p) {
             }
         };
         tile(std::integral_constant<int, MASKED ? 2 : 0>{});
-        if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
+        if (nxt >= 0) stage.store(Ks(buf ^ 1), Vs(buf ^ 1));
         __syncthreads();
         buf ^= 1;
         kt = nxt;
@@ -366,40 +375,81 @@ bwd_dq_kernel(const AttnParams p) {
     if (qr < L) store_rows_t<D>(dqb + (int64_t)qr * p.osl, dqt, p.scale, hh, q_valid);
 }
 
+// ---------------------------------------------------------------- kernels
+template <int D, int NW, bool MASKED>
+__global__ void __launch_bounds__(64 * NW, 2)
+bwd_dkdv_kernel(const AttnParams p) {
+    __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
+    constexpr int BKV = 32 * NW;
+    int b, h, kt, n;
+    if (!tile_item<BKV>(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt, n)) return;
+    dkdv_tile<D, NW, MASKED>(p, b, h, kt, n, smem);
+}
+
+template <int D, int NW, int KB, bool MASKED>
+__global__ void __launch_bounds__(64 * NW, 2)
+bwd_dq_kernel(const AttnParams p) {
+    __shared__ __attribute__((aligned(16))) bf16 smem[kDqLds<D, KB>];
+    constexpr int BQ = 32 * NW;
+    int b, h, qt, n;
+    if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
+    dq_tile<D, NW, KB, MASKED>(p, b, h, qt, n, smem);
+}
+
+// dK/dV and dQ in one launch: both kinds of tile of a (batch entry, head)
+// pair are dealt out together, longest sequences first, so the two share one
+// ramp-up and one tail.  Needs the same 32 NW rows for the key tiles of
+// dK/dV and the query tiles of dQ.
+template <int D, int NW, int KB, bool MASKED>
+__global__ void __launch_bounds__(64 * NW, 2)
+bwd_kernel(const AttnParams p) {
+    constexpr int kLds = kDkdvLds<D> > kDqLds<D, KB> ? kDkdvLds<D> : kDqLds<D, KB>;
+    __shared__ __attribute__((aligned(16))) bf16 smem[kLds];
+    constexpr int R = 32 * NW;
+    const int nt = (p.L + R - 1) / R;
+    int b, h, kind, t, n;
+    if (!tile_item2<R, R>(p.seq_lens, p.B, p.H, p.L, nt, nt, b, h, kind, t, n)) return;
+    if (kind == 0)
+        dkdv_tile<D, NW, MASKED>(p, b, h, t, n, smem);
+    else
+        dq_tile<D, NW, KB, MASKED>(p, b, h, t, n, smem);
+}
+
+// Waves per workgroup: 32 NW keys per dK/dV workgroup must divide block_k,
+// 32 NW queries per dQ workgroup must divide block_q; dQ visits keys 32 KB at
+// a time with 32 KB dividing block_k.
+static int dkdv_waves(const AttnParams &p) { return p.block_k >= 128 ? 4 : p.block_k / 32; }
+static int dq_waves(const AttnParams &p) { return p.block_q >= 128 ? 4 : p.block_q / 32; }
+static int dq_key_blocks(const AttnParams &p) { return p.block_k >= 64 ? 2 : 1; }
+
 template <int D>
 static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
-    // 32*NW keys per workgroup must divide block_k; queries are visited 32 at
-    // a time (QB = 1), which keeps the staging registers low.
-    const int nw = p.block_k >= 128 ? 4 : p.block_k / 32;
-    const int qb = 1;
+    const int nw = dkdv_waves(p);
     const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
-#define SIGATTN_DKDV_CASE(NW_, QB_)                                                     \
-    if (nw == NW_ && qb == QB_) {                                                        \
+#define SIGATTN_DKDV_CASE(NW_)                                                          \
+    if (nw == NW_) {                                                                     \
         if (p.mask != nullptr)                                                           \
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, QB_, true>), grid, block, 0,     \
-                               stream, p);                                               \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, true>), grid, block, 0, stream,  \
+                               p);                                                       \
         else                                                                             \
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, QB_, false>), grid, block, 0,    \
-                               stream, p);                                               \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, false>), grid, block, 0, stream, \
+                               p);                                                       \
         return hipGetLastError();                                                        \
     }
-    SIGATTN_DKDV_CASE(4, 1)
-    SIGATTN_DKDV_CASE(2, 1)
-    SIGATTN_DKDV_CASE(1, 1)
+    SIGATTN_DKDV_CASE(4)
+    SIGATTN_DKDV_CASE(2)
+    SIGATTN_DKDV_CASE(1)
 #undef SIGATTN_DKDV_CASE
     return hipErrorInvalidValue;
 }
 
 template <int D>
 static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
-    // 32*NW queries per workgroup must divide block_q; 32*KB keys per step
-    // must divide block_k.
-    const int nw = p.block_q >= 128 ? 4 : p.block_q / 32;
-    const int kb = p.block_k >= 64 ? 2 : 1;
+    const int nw = dq_waves(p), kb = dq_key_blocks(p);
     const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
-#define SIGATTN_DQ_CASE(NW_, KB_)                                                     \
+#define SIGATTN_DQ_CASE(NW_, KB_)                                                        \
     if (nw == NW_ && kb == KB_) {                                                        \
         if (p.mask != nullptr)                                                           \
             hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, true>), grid, block, 0,       \
@@ -419,12 +469,45 @@ static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
+template <int D>
+static hipError_t launch_bwd_d(const AttnParams &p, hipStream_t stream) {
+    const int nw = dkdv_waves(p), kb = dq_key_blocks(p);
+    if (nw != dq_waves(p)) {  // different tile heights: two launches
+        hipError_t e = launch_dkdv_d<D>(p, stream);
+        return e != hipSuccess ? e : launch_dq_d<D>(p, stream);
+    }
+    const dim3 grid = tile_grid(2 * ((p.L + 32 * nw - 1) / (32 * nw)), p.B, p.H);
+    dim3 block(64 * nw);
+#define SIGATTN_BWD_CASE(NW_, KB_)                                                       \
+    if (nw == NW_ && kb == KB_) {                                                        \
+        if (p.mask != nullptr)                                                           \
+            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, true>), grid, block, 0, stream,  \
+                               p);                                                       \
+        else                                                                             \
+            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, false>), grid, block, 0, stream, \
+                               p);                                                       \
+        return hipGetLastError();                                                        \
+    }
+    SIGATTN_BWD_CASE(4, 2)
+    SIGATTN_BWD_CASE(4, 1)
+    SIGATTN_BWD_CASE(2, 2)
+    SIGATTN_BWD_CASE(2, 1)
+    SIGATTN_BWD_CASE(1, 2)
+    SIGATTN_BWD_CASE(1, 1)
+#undef SIGATTN_BWD_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_bwd_dkdv(const AttnParams &p, hipStream_t stream) {
     return p.d == 64 ? launch_dkdv_d<64>(p, stream) : launch_dkdv_d<128>(p, stream);
 }
 
 hipError_t launch_bwd_dq(const AttnParams &p, hipStream_t stream) {
     return p.d == 64 ? launch_dq_d<64>(p, stream) : launch_dq_d<128>(p, stream);
+}
+
+hipError_t launch_bwd(const AttnParams &p, hipStream_t stream) {
+    return p.d == 64 ? launch_bwd_d<64>(p, stream) : launch_bwd_d<128>(p, stream);
 }
 
 }  // namespace sigattn

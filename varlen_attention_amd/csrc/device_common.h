@@ -139,28 +139,6 @@ struct TileSchedule {
     }
 };
 
-// Work item of a workgroup in a launch over (batch entry, head, tile) items,
-// ntiles tiles of ROWS rows per (batch entry, head).
-//
-// Placement: workgroups are dealt to the 8 XCDs round-robin by linear index
-// and each XCD has its own L2, so XCD x = i % 8 owns the pairs x, x + 8, ...
-// of the (length rank, head) order: all tiles of one (batch entry, head)
-// share an L2, and every XCD gets one head of each batch entry when H is a
-// multiple of 8.
-//
-// Order inside an XCD (its k-th workgroup, k = i / 8): first every tile that
-// holds valid rows, pair by pair from the longest sequence down (longest
-// processing time first), then the fully padded tiles, which only write
-// zeros and so fill the tail of the launch instead of holding slots while
-// long tiles are still waiting.
-//
-// Computed by every wave of the workgroup alike (the result is uniform):
-// lane b ranks batch entry b against all others (read back with readlane,
-// ties broken by index) and pushes its length to lane rank(b), so lane r
-// holds the r-th longest length; then wave prefix sums (DPP) over the XCD's
-// pairs locate item k, 64 pairs at a time.  Batches of more than 64 entries keep
-// their natural order.  n is the clamped length of the chosen batch entry.
-// Returns false past the last item.
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
 // round trips): row_shr 1, 2, 4, 8 scan each row of 16 lanes (lanes shifted
 // in from outside the row add 0), then row_bcast 15 adds row 0's total to row
@@ -176,9 +154,32 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
-template <int ROWS>
-__device__ __forceinline__ bool tile_item(const int32_t *seq_lens, int B, int H, int L,
-                                          int ntiles, int &b, int &h, int &t, int &n) {
+// Work item of a workgroup in a launch over (batch entry, head, tile) items of
+// up to two kinds: NT0 tiles of ROWS0 rows and NT1 tiles of ROWS1 rows per
+// (batch entry, head) (NT1 = 0 for a launch of one kind).
+//
+// Placement: workgroups are dealt to the 8 XCDs round-robin by linear index
+// and each XCD has its own L2, so XCD x = i % 8 owns the pairs x, x + 8, ...
+// of the (length rank, head) order: all tiles of one (batch entry, head)
+// share an L2, and every XCD gets one head of each batch entry when H is a
+// multiple of 8.
+//
+// Order inside an XCD (its k-th workgroup, k = i / 8): first every tile that
+// holds valid rows, pair by pair from the longest sequence down (longest
+// processing time first; kind 0 before kind 1 within a pair), then the fully
+// padded tiles, which only write zeros and so fill the tail of the launch
+// instead of holding slots while long tiles are still waiting.
+//
+// Computed by every wave of the workgroup alike (the result is uniform):
+// lane b ranks batch entry b against all others (read back with readlane,
+// ties broken by index) and pushes its length to lane rank(b), so lane r
+// holds the r-th longest length; then wave prefix sums (DPP) over the XCD's
+// pairs locate item k, 64 pairs at a time.  Batches of more than 64 entries
+// keep their natural order.  n is the clamped length of the chosen batch
+// entry.  Returns false past the last item.
+template <int ROWS0, int ROWS1>
+__device__ __forceinline__ bool tile_item2(const int32_t *seq_lens, int B, int H, int L, int nt0,
+                                           int nt1, int &b, int &h, int &kind, int &t, int &n) {
     const int lane = (int)(threadIdx.x & 63);
     const int x = blockIdx.x & 7;
     int k = blockIdx.x >> 3;
@@ -210,23 +211,35 @@ __device__ __forceinline__ bool tile_item(const int32_t *seq_lens, int B, int H,
                 bj = r;
                 nj = clamp_len(seq_lens[r], L);
             }
-            const int real_t = (nj + ROWS - 1) / ROWS;
-            const int cnt = valid ? (pass == 0 ? real_t : ntiles - real_t) : 0;
+            const int real0 = (nj + ROWS0 - 1) / ROWS0;
+            const int real1 = nt1 > 0 ? (nj + ROWS1 - 1) / ROWS1 : 0;
+            const int first = pass == 0 ? real0 : nt0 - real0;  // items of kind 0 in this pass
+            const int cnt = valid ? first + (pass == 0 ? real1 : nt1 - real1) : 0;
             const int incl = wave_inclusive_scan(cnt);
             const int total = __builtin_amdgcn_readlane(incl, 63);
             if (k < total) {
                 const int jl = __builtin_ctzll(__ballot(incl > k));
-                const int before = __builtin_amdgcn_readlane(incl - cnt, jl);
+                const int idx = k - __builtin_amdgcn_readlane(incl - cnt, jl);
+                const int f = __builtin_amdgcn_readlane(first, jl);
                 h = __builtin_amdgcn_readlane(pair, jl) % H;
                 b = __builtin_amdgcn_readlane(bj, jl);
                 n = __builtin_amdgcn_readlane(nj, jl);
-                t = (pass == 0 ? 0 : __builtin_amdgcn_readlane(real_t, jl)) + (k - before);
+                kind = idx < f ? 0 : 1;
+                const int base = pass == 0 ? 0 : __builtin_amdgcn_readlane(kind == 0 ? real0 : real1, jl);
+                t = base + (kind == 0 ? idx : idx - f);
                 return true;
             }
             k -= total;
         }
     }
     return false;
+}
+
+template <int ROWS>
+__device__ __forceinline__ bool tile_item(const int32_t *seq_lens, int B, int H, int L,
+                                          int ntiles, int &b, int &h, int &t, int &n) {
+    int kind;
+    return tile_item2<ROWS, ROWS>(seq_lens, B, H, L, ntiles, 0, b, h, kind, t, n);
 }
 
 __host__ __forceinline__ dim3 tile_grid(int ntiles, int B, int H) {

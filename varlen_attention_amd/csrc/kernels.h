@@ -28,5 +28,7 @@ hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask, int B,
 hipError_t launch_fwd(const AttnParams &p, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnParams &p, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnParams &p, hipStream_t stream);
+// dK, dV and dQ in one launch (two launches when the tile heights differ).
+hipError_t launch_bwd(const AttnParams &p, hipStream_t stream);
 
 }  // namespace sigattn
