@@ -40,12 +40,23 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """Source text without // comments and blank lines: what the compiler sees."""
+    lines = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code.strip():
+            lines.append(code)
+    return "\n".join(lines)
+
+
 def source_digest(kernel: str) -> str:
+    """Digest of the code (not the comments) a kernel is built from."""
     paths = [KERNEL_SOURCES[kernel], "varlen_attention_amd/csrc/device_common.h"]
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -96,15 +107,34 @@ def _find(dirname, suffix):
 KERNEL_SYMBOLS = {"fwd": "::fwd_kernel<", "bwd": "::bwd_kernel<", "blockmask": "blockmask_"}
 
 
-def summarize_stats(dirname: str) -> str:
-    """Markdown table of a rocprofv3 --kernel-trace --stats run."""
+def summarize_stats(dirname: str, skip: int = 0) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run: the profiler's
+    own statistics over all calls, and per-dispatch durations from the kernel
+    trace without each kernel's first `skip` dispatches (the warmup steps,
+    which run before the clocks settle)."""
     rows = _csv_rows(_find(dirname, "kernel_stats.csv"))
-    out = ["| kernel | calls | average (us) | min (us) | max (us) | share |",
+    out = ["All dispatches (rocprofv3 --stats):", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share |",
            "|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.1f}% |")
+    trace = _csv_rows(_find(dirname, "kernel_trace.csv"))
+    by_kernel = {}
+    for r in trace:
+        by_kernel.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out += ["", f"Timed dispatches (kernel trace, first {skip} dispatches of each kernel "
+                "skipped):", "",
+            "| kernel | dispatches | average (us) | min (us) | max (us) |",
+            "|---|---|---|---|---|"]
+    for name, v in by_kernel.items():
+        v.sort()
+        d = np.array([x[1] for x in v[skip:]], dtype=np.float64) / 1e3
+        if d.size:
+            out.append(f"| `{name[:90]}` | {d.size} | {d.mean():.2f} | {d.min():.2f} | "
+                       f"{d.max():.2f} |")
     return "\n".join(out)
 
 
@@ -260,13 +290,15 @@ def main() -> int:
                     help="only run a plain device copy of this size (counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="print a markdown table of a rocprofv3 --stats output directory")
+    ap.add_argument("--skip-dispatches", type=int, default=0,
+                    help="with --summarize-stats: dispatches of each kernel to leave out")
     ap.add_argument("--summarize-traffic", nargs=5,
                     metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="print the HBM traffic summary of KERNEL from FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--copy-mib", type=int, default=256)
     args = ap.parse_args()
     if args.summarize_stats:
-        print(summarize_stats(args.summarize_stats))
+        print(summarize_stats(args.summarize_stats, args.skip_dispatches))
         return 0
     if args.summarize_traffic:
         import synthetic as syn

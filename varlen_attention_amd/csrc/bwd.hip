@@ -1,24 +1,25 @@
-// Backward kernels for sigmoid attention on gfx950: one kernel for dK/dV and
-// one for dQ, no atomics, scores and weights recomputed on the fly
+// Backward pass for sigmoid attention on gfx950: dK/dV work items and dQ work
+// items (each kind its own kernel, or both in one grid), no atomics, scores
+// and weights recomputed on the fly
 // ("Better Models, Faster Training: Sigmoid Attention for single-cell
 // Foundation Models", section 2.C).  The Jacobian of element-wise sigmoid
 // attention is diagonal (section 2.B), so with P = sigma(S) and
 // dP = dO V^T the score gradient is dS = dP * P * (1 - P), element by element.
 //
-// dK/dV kernel: a workgroup of NW waves owns 32*NW keys of one (batch entry,
+// dK/dV item: a workgroup of NW waves owns 32*NW keys of one (batch entry,
 // head); each wave holds its 32 K and V rows in registers and walks the query
 // tiles whose block-mask entry is 1 (one column of the block matrix):
 //   S  = Q K^T,  dP = dO V^T            (Q, dO rows from LDS)
 //   dV^T += dO^T P,  dK^T += Q^T dS     (P, dS stay in registers; Q^T and dO^T
 //                                        come from transposing LDS reads)
-// dQ kernel: a workgroup owns 32*NW queries; each wave holds its Q and dO rows
+// dQ item: a workgroup owns 32*NW queries; each wave holds its Q and dO rows
 // and walks the key tiles of one block-mask row:
 //   S^T = K Q^T,  dP^T = V dO^T         (K, V rows from LDS)
 //   dQ^T += K^T dS^T                    (K^T from transposing LDS reads)
 // Tiles are double-buffered in LDS (unpadded, XOR-swizzled rows): the next
 // tile is fetched into registers through bounds-checked buffer loads while
-// the current one computes, with one barrier per tile.  The two kernels write
-// disjoint outputs.
+// the current one computes, with one barrier per tile.  The two kinds of
+// item write disjoint outputs.
 #include <type_traits>
 
 #include "device_common.h"
