@@ -356,6 +356,42 @@ def test_backward_parts_match_fused(va, bq, bk):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("bq,bk", [(128, 128), (64, 32)])
+def test_every_output_row_written(va, bq, bk):
+    """Outputs start as NaN; afterwards valid rows match the oracle and every
+    padded row is exactly 0 (LSE -inf), whichever workgroup wrote it: lengths
+    0, L, one short sequence with many padded tiles, and odd lengths."""
+    B, H, L, d = 5, 2, 700, 64
+    n = np.array([0, 700, 9, 333, 129], np.int32)
+    q, k, v, do = _inputs(123, B, H, L, d, n, names="qkvd")
+    n_gpu = to_gpu(n, torch.int32)
+    bm = _bm(va, n_gpu, L, bq, bk)
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    nan = lambda: torch.full_like(g[0], float("nan"))
+    say(f"outputs fully written bq={bq} bk={bk}")
+    for variant in (SIGMOID, SOFTMAX1):
+        o = nan()
+        lse = torch.full((B, H, L), float("nan"), dtype=torch.float32, device=g[0].device)
+        va.sigattn_fwd(*g[:3], n_gpu, block_mask=bm, variant=variant, bias=0, out=o, lse=lse,
+                       block_q=bq, block_k=bk)
+        torch.cuda.synchronize()
+        want, want_lse = oracle.fwd(q, k, v, n, variant=variant, bias=0)
+        assert_rows(gpu_f64(o), want, n, f"O variant {variant}")
+        if variant != SIGMOID:
+            got = lse.cpu().numpy()
+            valid = row_valid(n, B, L)
+            for b in range(B):
+                assert np.all(np.isneginf(got[b][:, ~valid[b]]))
+                assert np.all(np.isfinite(got[b][:, valid[b]]))
+    dq, dk, dv = nan(), nan(), nan()
+    va.sigattn_bwd(*g, n_gpu, block_mask=bm, dq=dq, dk=dk, dv=dv, block_q=bq, block_k=bk)
+    torch.cuda.synchronize()
+    wq, wk, wv = oracle.bwd(q, k, v, do, n)
+    assert_rows(gpu_f64(dq), wq, n, "dQ")
+    assert_rows(gpu_f64(dk), wk, n, "dK")
+    assert_rows(gpu_f64(dv), wv, n, "dV")
+
+
 def test_backward_poison_determinism_and_identities(va):
     B, H, L, d = 3, 2, 333, 64
     n = np.array([333, 180, 40], np.int32)

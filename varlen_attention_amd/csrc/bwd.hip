@@ -16,9 +16,13 @@
 // and walks the key tiles of one block-mask row:
 //   S^T = K Q^T,  dP^T = V dO^T         (K, V rows from LDS)
 //   dQ^T += K^T dS^T                    (K^T from transposing LDS reads)
-// Tiles are double-buffered in LDS (unpadded, XOR-swizzled rows): the next
-// tile is fetched into registers through bounds-checked buffer loads while
-// the current one computes, with one barrier per tile.  The two kinds of
+// Tiles are double-buffered in LDS (unpadded, XOR-swizzled rows) with one
+// barrier per tile; the next tile is fetched through bounds-checked buffer
+// loads while the current one computes -- into registers for dK/dV, straight
+// into LDS for dQ (its K and V buffers are separate LDS objects and its loop
+// is unrolled by two, so the compiler sees the buffer being filled is not the
+// one being read; the freed staging registers let S and dP keep separate
+// accumulators).  The two kinds of
 // item write disjoint outputs.
 #include <type_traits>
 
@@ -62,6 +66,39 @@ struct PairStage {
         for (int c = 0; c < CH; ++c) {
             *reinterpret_cast<uint4 *>(ta + loff[c]) = a[c];
             *reinterpret_cast<uint4 *>(tb + loff[c]) = b[c];
+        }
+    }
+};
+
+// Fetches a [BT x D] tile of two tensors straight into swizzled LDS tiles
+// (buffer loads that write LDS, no staging registers).  One wave
+// instruction fills one contiguous KiB, lane l the 16 bytes at 16 l, so each
+// lane reads the global 16-byte chunk that the XOR swizzle (swz_off) places
+// at its slot.  Rows >= n read as zeros through the descriptor.
+template <int D, int BT, int NW>
+struct DmaPair {
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kBlocks = BT * kRowBytes / 1024;  // KiB blocks per tile
+    static constexpr int kPerWave = kBlocks / NW;
+    static_assert(kPerWave * NW == kBlocks, "tile must split evenly over the waves");
+    int goff[kPerWave];
+    int lds_off;  // byte offset of this wave's first block inside a tile
+
+    __device__ __forceinline__ void init(int64_t sl, int w, int lane) {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+            const int byte = (w * kPerWave + i) * 1024 + lane * 16;
+            const int row = byte / kRowBytes, pos = (byte % kRowBytes) / 16;
+            goff[i] = (int)(((int64_t)row * sl + (pos ^ swz(row)) * 8) * 2);
+        }
+        lds_off = w * kPerWave * 1024;
+    }
+
+    __device__ __forceinline__ void issue(rsrc_t ra, rsrc_t rb, bf16 *ta, bf16 *tb) const {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+            lds_load16(ra, reinterpret_cast<char *>(ta) + lds_off + i * 1024, goff[i]);
+            lds_load16(rb, reinterpret_cast<char *>(tb) + lds_off + i * 1024, goff[i]);
         }
     }
 };
@@ -132,10 +169,12 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     const int k0 = kt * BKV;
     bf16 *dkb = reinterpret_cast<bf16 *>(p.dk) + b * p.osb + h * p.osh;
     bf16 *dvb = reinterpret_cast<bf16 *>(p.dv) + b * p.osb + h * p.osh;
-    if (k0 >= n) {
-        const int rows = min(BKV, L - k0);
-        zero_rows<D>(dkb, p.osl, k0, rows, tid, NT);
-        zero_rows<D>(dvb, p.osl, k0, rows, tid, NT);
+    auto zero_tile = [&](int r0, int rows) {
+        zero_rows<D>(dkb, p.osl, r0, rows, tid, NT);
+        zero_rows<D>(dvb, p.osl, r0, rows, tid, NT);
+    };
+    if (k0 >= n) {  // a tile of an empty sequence: zeros, nothing else
+        zero_tile(k0, min(BKV, L - k0));
         return;
     }
     const bf16 *qb = reinterpret_cast<const bf16 *>(p.q) + b * p.sb + h * p.sh;
@@ -189,6 +228,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kreg[ks] = scale8(kreg[ks], c1);
     __syncthreads();
+    // This tile's share of the sequence's fully padded key tiles, written
+    // while the loop computes.
+    padded_share<BKV>(kt, n, L, zero_tile);
 
     while (qt >= 0) {
         const int q0 = qt * BQ;
@@ -251,25 +293,23 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
 }
 
 // ---------------------------------------------------------------- dQ
-// LDS of one dQ tile (elements): K and V tiles of 32 KB rows, double-buffered.
-template <int D, int KB> constexpr int kDqLds = 2 * 2 * 32 * KB * D;
-
 // dQ of query tile qt (32 NW queries) of (batch entry b, head h), visiting
-// keys 32 KB at a time; smem holds kDqLds<D, KB> elements.
+// keys 32 KB at a time.  K0, V0, K1, V1 are four separate LDS objects of
+// 32 KB rows x D each (two buffers of the K and V tiles).
 template <int D, int NW, int KB, bool MASKED>
 __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int qt, int n,
-                                        bf16 *smem) {
+                                        bf16 *K0, bf16 *V0, bf16 *K1, bf16 *V1) {
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
-    auto Ks = [&](int i) { return smem + i * (BK * D); };
-    auto Vs = [&](int i) { return smem + (2 + i) * (BK * D); };
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = p.L;
     const int q0 = qt * BQ;
     bf16 *dqb = reinterpret_cast<bf16 *>(p.dq) + b * p.osb + h * p.osh;
-    if (q0 >= n) {
-        zero_rows<D>(dqb, p.osl, q0, min(BQ, L - q0), tid, NT);
+    auto zero_tile = [&](int r0, int rows) { zero_rows<D>(dqb, p.osl, r0, rows, tid, NT); };
+    if (q0 >= n) {  // a tile of an empty sequence: zeros, nothing else
+        zero_tile(q0, min(BQ, L - q0));
         return;
     }
     const bf16 *qb = reinterpret_cast<const bf16 *>(p.q) + b * p.sb + h * p.sh;
@@ -309,27 +349,32 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
         return make_rsrc(base + (int64_t)r0 * p.sl, (int64_t)(n - r0) * p.sl * 2);
     };
     // Key tile 0 is fetched before the block mask is read (see the forward
-    // kernel); another first tile is fetched again.
-    PairStage<D, BK, NT> stage;
-    stage.init(p.sl, tid);
-    stage.load(rows_rsrc(kb, 0), rows_rsrc(vb, 0));
+    // kernel); another first tile is fetched again.  Tiles go straight into
+    // LDS; the two buffers are separate LDS objects and the loop below is
+    // unrolled by two, so the compiler sees that the buffer being filled is
+    // not the one being read.
+    DmaPair<D, BK, NW> dma;
+    dma.init(p.sl, w, lane);
+    auto fetch = [&](int t, bf16 *kd, bf16 *vd) {
+        dma.issue(rows_rsrc(kb, t * BK), rows_rsrc(vb, t * BK), kd, vd);
+    };
+    fetch(0, K0, V0);
     TileSchedule<BK> sched;
     sched.init(p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + q0 / p.block_q) * p.Tk : nullptr,
                1, n, p.block_k);
     int kt = sched.next();
-    if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
-    int buf = 0;
-    stage.store(Ks(0), Vs(0));
+    if (kt > 0) fetch(kt, K0, V0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qreg[ks] = scale8(qreg[ks], c1);
+    wait_vm0();
     __syncthreads();
+    // This tile's share of the sequence's fully padded query tiles.
+    padded_share<BQ>(qt, n, L, zero_tile);
 
-    while (kt >= 0) {
+    auto step = [&](const bf16 *Kc, const bf16 *Vc, bf16 *Kn, bf16 *Vn) {
         const int k0 = kt * BK;
         const int nxt = sched.next();
-        if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
-        const bf16 *Kc = Ks(buf);
-        const bf16 *Vc = Vs(buf);
+        if (nxt >= 0) fetch(nxt, Kn, Vn);
         // MODE 0 (no element mask): padded key rows of K and V read as zeros,
         // so dP = 0 and dS = 0 there; padded query rows are zeroed at the
         // store.  MODE 2: element mask.
@@ -368,10 +413,14 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
             }
         };
         tile(std::integral_constant<int, MASKED ? 2 : 0>{});
-        if (nxt >= 0) stage.store(Ks(buf ^ 1), Vs(buf ^ 1));
+        wait_vm0();
         __syncthreads();
-        buf ^= 1;
         kt = nxt;
+    };
+    while (kt >= 0) {
+        step(K0, V0, K1, V1);
+        if (kt < 0) break;
+        step(K1, V1, K0, V0);
     }
     if (qr < L) store_rows_t<D>(dqb + (int64_t)qr * p.osl, dqt, p.scale, hh, q_valid);
 }
@@ -390,11 +439,12 @@ bwd_dkdv_kernel(const AttnParams p) {
 template <int D, int NW, int KB, bool MASKED>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dq_kernel(const AttnParams p) {
-    __shared__ __attribute__((aligned(16))) bf16 smem[kDqLds<D, KB>];
+    constexpr int kTile = 32 * KB * D;
+    __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
     constexpr int BQ = 32 * NW;
     int b, h, qt, n;
     if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
-    dq_tile<D, NW, KB, MASKED>(p, b, h, qt, n, smem);
+    dq_tile<D, NW, KB, MASKED>(p, b, h, qt, n, K0, V0, K1, V1);
 }
 
 // dK/dV and dQ in one launch: both kinds of tile of a (batch entry, head)
@@ -404,8 +454,9 @@ bwd_dq_kernel(const AttnParams p) {
 template <int D, int NW, int KB, bool MASKED>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_kernel(const AttnParams p) {
-    constexpr int kLds = kDkdvLds<D> > kDqLds<D, KB> ? kDkdvLds<D> : kDqLds<D, KB>;
-    __shared__ __attribute__((aligned(16))) bf16 smem[kLds];
+    __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
+    constexpr int kTile = 32 * KB * D;
+    __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
     constexpr int R = 32 * NW;
     const int nt = (p.L + R - 1) / R;
     int b, h, kind, t, n;
@@ -413,7 +464,7 @@ bwd_kernel(const AttnParams p) {
     if (kind == 0)
         dkdv_tile<D, NW, MASKED>(p, b, h, t, n, smem);
     else
-        dq_tile<D, NW, KB, MASKED>(p, b, h, t, n, smem);
+        dq_tile<D, NW, KB, MASKED>(p, b, h, t, n, K0, V0, K1, V1);
 }
 
 // Waves per workgroup: 32 NW keys per dK/dV workgroup must divide block_k,
@@ -421,7 +472,9 @@ bwd_kernel(const AttnParams p) {
 // a time with 32 KB dividing block_k.
 static int dkdv_waves(const AttnParams &p) { return p.block_k >= 128 ? 4 : p.block_k / 32; }
 static int dq_waves(const AttnParams &p) { return p.block_q >= 128 ? 4 : p.block_q / 32; }
-static int dq_key_blocks(const AttnParams &p) { return p.block_k >= 64 ? 2 : 1; }
+// At d = 128 the dQ step visits 32 keys: with two 32-key blocks its S, dP and
+// operand registers no longer fit without spilling.
+static int dq_key_blocks(const AttnParams &p) { return p.block_k >= 64 && p.d == 64 ? 2 : 1; }
 
 template <int D>
 static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
@@ -451,6 +504,7 @@ static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_DQ_CASE(NW_, KB_)                                                        \
+    if constexpr (D == 64 || KB_ == 1)                                                   \
     if (nw == NW_ && kb == KB_) {                                                        \
         if (p.mask != nullptr)                                                           \
             hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, true>), grid, block, 0,       \
@@ -480,6 +534,7 @@ static hipError_t launch_bwd_d(const AttnParams &p, hipStream_t stream) {
     const dim3 grid = tile_grid(2 * ((p.L + 32 * nw - 1) / (32 * nw)), p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_BWD_CASE(NW_, KB_)                                                       \
+    if constexpr (D == 64 || KB_ == 1)                                                   \
     if (nw == NW_ && kb == KB_) {                                                        \
         if (p.mask != nullptr)                                                           \
             hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, true>), grid, block, 0, stream,  \

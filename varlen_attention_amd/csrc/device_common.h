@@ -164,11 +164,13 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 // share an L2, and every XCD gets one head of each batch entry when H is a
 // multiple of 8.
 //
-// Order inside an XCD (its k-th workgroup, k = i / 8): first every tile that
-// holds valid rows, pair by pair from the longest sequence down (longest
-// processing time first; kind 0 before kind 1 within a pair), then the fully
-// padded tiles, which only write zeros and so fill the tail of the launch
-// instead of holding slots while long tiles are still waiting.
+// Order inside an XCD (its k-th workgroup, k = i / 8): every tile that holds
+// valid rows, pair by pair from the longest sequence down (longest processing
+// time first; kind 0 before kind 1 within a pair), then the tiles of empty
+// sequences (n = 0), which only write zeros.  The other fully padded tiles
+// get no workgroup of their own: the tiles with valid rows of the same pair
+// and kind write their zeros (padded_share), so those writes overlap compute
+// and hold no slot.  Workgroups past the last item return false.
 //
 // Computed by every wave of the workgroup alike (the result is uniform):
 // lane b ranks batch entry b against all others (read back with readlane,
@@ -213,8 +215,10 @@ __device__ __forceinline__ bool tile_item2(const int32_t *seq_lens, int B, int H
             }
             const int real0 = (nj + ROWS0 - 1) / ROWS0;
             const int real1 = nt1 > 0 ? (nj + ROWS1 - 1) / ROWS1 : 0;
-            const int first = pass == 0 ? real0 : nt0 - real0;  // items of kind 0 in this pass
-            const int cnt = valid ? first + (pass == 0 ? real1 : nt1 - real1) : 0;
+            // Items of kind 0 in this pass; pass 1 holds only empty sequences.
+            const bool empty = nj == 0;
+            const int first = pass == 0 ? real0 : (empty ? nt0 : 0);
+            const int cnt = valid ? first + (pass == 0 ? real1 : (empty ? nt1 : 0)) : 0;
             const int incl = wave_inclusive_scan(cnt);
             const int total = __builtin_amdgcn_readlane(incl, 63);
             if (k < total) {
@@ -225,8 +229,7 @@ __device__ __forceinline__ bool tile_item2(const int32_t *seq_lens, int B, int H
                 b = __builtin_amdgcn_readlane(bj, jl);
                 n = __builtin_amdgcn_readlane(nj, jl);
                 kind = idx < f ? 0 : 1;
-                const int base = pass == 0 ? 0 : __builtin_amdgcn_readlane(kind == 0 ? real0 : real1, jl);
-                t = base + (kind == 0 ? idx : idx - f);
+                t = kind == 0 ? idx : idx - f;
                 return true;
             }
             k -= total;
@@ -240,6 +243,17 @@ __device__ __forceinline__ bool tile_item(const int32_t *seq_lens, int B, int H,
                                           int ntiles, int &b, int &h, int &t, int &n) {
     int kind;
     return tile_item2<ROWS, ROWS>(seq_lens, B, H, L, ntiles, 0, b, h, kind, t, n);
+}
+
+// The fully padded tiles (of ROWS rows) that tile t of a sequence with
+// real = ceil(n / ROWS) tiles holding valid rows writes zeros for: tiles
+// real + i with i = t, t + real, t + 2 real, ... below nt.  Calls
+// f(first_row, rows) for each.
+template <int ROWS, typename F>
+__device__ __forceinline__ void padded_share(int t, int n, int L, F &&f) {
+    const int real = (n + ROWS - 1) / ROWS, nt = (L + ROWS - 1) / ROWS;
+    if (real == 0) return;
+    for (int i = real + t; i < nt; i += real) f(i * ROWS, min(ROWS, L - i * ROWS));
 }
 
 __host__ __forceinline__ dim3 tile_grid(int ntiles, int B, int H) {

@@ -96,14 +96,17 @@ fwd_kernel(const AttnParams p) {
     bf16 *ob = reinterpret_cast<bf16 *>(p.o) + b * p.osb + h * p.osh;
     float *lseb = p.lse ? p.lse + ((int64_t)b * p.H + h) * L : nullptr;
 
-    if (q0 >= n) {  // fully padded query tile: zero rows, nothing else
-        const int rows = min(BQ, L - q0);
+    // Rows [r0, r0 + rows) of a fully padded query tile: zeros (LSE -inf).
+    auto zero_tile = [&](int r0, int rows) {
         for (int idx = tid; idx < rows * (D / 8); idx += NT) {
-            const int r = q0 + idx / (D / 8), c = (idx % (D / 8)) * 8;
+            const int r = r0 + idx / (D / 8), c = (idx % (D / 8)) * 8;
             *reinterpret_cast<uint4 *>(ob + (int64_t)r * p.osl + c) = make_uint4(0, 0, 0, 0);
         }
         if (VARIANT != kSigmoid && lseb)
-            for (int r = q0 + tid; r < q0 + rows; r += NT) lseb[r] = -INFINITY;
+            for (int r = r0 + tid; r < r0 + rows; r += NT) lseb[r] = -INFINITY;
+    };
+    if (q0 >= n) {  // a tile of an empty sequence: zeros, nothing else
+        zero_tile(q0, min(BQ, L - q0));
         return;
     }
 
@@ -171,6 +174,9 @@ fwd_kernel(const AttnParams p) {
     for (int ks = 0; ks < KS; ++ks)
         if constexpr (VARIANT == kSigmoid) qreg[ks] = scale8(qreg[ks], c1);
     __syncthreads();
+    // This tile's share of the sequence's fully padded query tiles, written
+    // while the loop computes (the stores complete during the first tile).
+    padded_share<BQ>(qt, n, L, zero_tile);
 
     while (kt >= 0) {
         const int k0 = kt * BK;
