@@ -125,27 +125,38 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
                 int32_t bias_mode, int32_t variant, void *o, float *lse, void *stream);
 
 /*
- * sigattn_bwd - gradients dQ, dK, dV of sum(dO * O) for the SIGMOID variant
+ * sigattn_bwd - gradients dQ, dK, dV of sum(dO * O)
  * (single-cell page section 2.C: two kernels, one for dQ and one for dK/dV,
  * no atomics, scores and weights recomputed on the fly; section 2.B: the
  * Jacobian of sigmoid attention is diagonal, dS = dP * sigma * (1 - sigma)).
+ * For SOFTMAX and SOFTMAX1 the weights are recomputed from the forward's
+ * log-sum-exp, P = exp(s - lse), and dS = P * (dP - D) with
+ * D = rowsum(dO * O) (the softmax Jacobian; softmax_1 note, "Properties of
+ * softmax_1": the derivative of softmax_1 has the same form).
  *
  *   q, k, v, dout   [device] bf16 [B, H, L, d] (input layout)
+ *   o               [device] bf16 [B, H, L, d] (output layout): the forward
+ *                   output of the same call; required for SOFTMAX and
+ *                   SOFTMAX1, ignored (may be NULL) for SIGMOID
+ *   lse             [device] fp32 [B, H, L] contiguous: the forward's
+ *                   log-sum-exp; same rule as o
  *   seq_lens, block_mask, mask: as for sigattn_fwd
  *   dq, dk, dv      [device] bf16 [B, H, L, d] (output layout), fully written;
  *                   rows >= n are 0.
+ * bias_mode and variant must be those the forward ran with.
  * The dK/dV and dQ work items write disjoint outputs and use no atomics, so
  * results are bit-for-bit reproducible and equal to those of the two calls
  * below.  When the key tiles of dK/dV and the query tiles of dQ have the same
  * height (block_q and block_k both >= 128, or equal), both kinds of work item
  * go out in one launch, sharing one ramp-up and one tail; otherwise this is
  * the two launches below.
- * Errors: as sigattn_fwd; UNSUPPORTED for a variant other than SIGMOID.
+ * Errors: as sigattn_fwd; INVALID_ARG for a softmax variant without o or
+ * lse, ALIGNMENT for o not 16-byte or lse not 4-byte aligned.
  */
 int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
-                const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
-                const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dq, void *dk,
-                void *dv, void *stream);
+                const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
+                const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode,
+                int32_t variant, void *dq, void *dk, void *dv, void *stream);
 
 /*
  * sigattn_bwd_dkdv / sigattn_bwd_dq - the two halves of sigattn_bwd, each one
@@ -156,13 +167,13 @@ int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const 
  * gradients, and to time the two kernels apart.
  */
 int sigattn_bwd_dkdv(const sigattn_shape *shape, const void *q, const void *k, const void *v,
-                     const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
-                     const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dk,
-                     void *dv, void *stream);
+                     const void *dout, const void *o, const float *lse,
+                     const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
+                     int32_t bias_mode, int32_t variant, void *dk, void *dv, void *stream);
 int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, const void *v,
-                   const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
-                   const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dq,
-                   void *stream);
+                   const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
+                   const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode,
+                   int32_t variant, void *dq, void *stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *sigattn_last_error(void);

@@ -75,14 +75,24 @@ def test_forward_argument_errors(lib):
 def test_backward_argument_errors(lib):
     import varlen_attention_amd as va
     sh = _shape(va)
-    args = [FAKE] * 4
-    assert lib.sigattn_bwd(ctypes.byref(sh), *args, FAKE, None, None, 1, 1, FAKE, FAKE, FAKE,
-                           None) == va.ERR_UNSUPPORTED  # softmax backward not built
-    assert lib.sigattn_bwd(ctypes.byref(sh), *args, FAKE, None, None, 1, 0, FAKE, None, FAKE,
-                           None) == va.ERR_INVALID_ARG
-    sh128 = _shape(va, d=128, L=0)
-    assert lib.sigattn_bwd(ctypes.byref(sh128), *args, FAKE, None, None, 1, 0, FAKE, FAKE, FAKE,
-                           None) == va.ERR_INVALID_ARG
+    args = [FAKE] * 4  # q, k, v, dout
+
+    def bwd(shape=sh, o=None, lse=None, var=0, dk=FAKE, bm=None, mask=None):
+        return lib.sigattn_bwd(ctypes.byref(shape), *args, o, lse, FAKE, bm, mask, 1, var, FAKE,
+                               dk, FAKE, None)
+
+    # The softmax variants need the forward's o and lse; SIGMOID ignores them.
+    assert bwd(var=1) == va.ERR_INVALID_ARG
+    assert bwd(var=2, o=FAKE) == va.ERR_INVALID_ARG
+    assert bwd(var=1, o=ctypes.c_void_p(0x10008), lse=FAKE) == va.ERR_ALIGNMENT
+    assert bwd(var=2, o=FAKE, lse=ctypes.c_void_p(0x10002)) == va.ERR_ALIGNMENT
+    assert bwd(dk=None) == va.ERR_INVALID_ARG
+    assert bwd(mask=FAKE) == va.ERR_INVALID_ARG  # an element mask needs its block mask
+    assert bwd(shape=_shape(va, d=128, L=0)) == va.ERR_INVALID_ARG
+    assert lib.sigattn_bwd_dq(ctypes.byref(sh), *args, None, None, FAKE, None, None, 1, 1, FAKE,
+                              None) == va.ERR_INVALID_ARG
+    assert lib.sigattn_bwd_dkdv(ctypes.byref(sh), *args, None, None, FAKE, None, None, 1, 0, FAKE,
+                                None, None) == va.ERR_INVALID_ARG
 
 
 def test_blockmask_argument_errors(lib):

@@ -338,6 +338,56 @@ def test_many_batch_entries_forward_backward(va, B, H):
     assert_rows(gpu_f64(dv), wv, n, "dV many batch entries")
 
 
+SOFT_BWD_CASES = [
+    # d, L, block_q, block_k, variant, bias, with_mask
+    (64, 300, 128, 128, SOFTMAX, 0, False),
+    (64, 300, 128, 128, SOFTMAX1, 0, False),
+    (64, 230, 64, 32, SOFTMAX1, 1, True),
+    (64, 150, 32, 64, SOFTMAX, 2, True),
+    (128, 201, 128, 128, SOFTMAX1, 0, False),
+    (128, 190, 64, 128, SOFTMAX, 1, True),
+]
+
+
+@pytest.mark.parametrize("d,L,bq,bk,variant,bias,with_mask", SOFT_BWD_CASES)
+def test_backward_softmax_variants(va, d, L, bq, bk, variant, bias, with_mask):
+    """Softmax-family backward from the forward's O and LSE against the
+    oracle's gradients (dS = P (dP - D), D = rowsum(dO O)); lengths L, short,
+    1 and 0, and with an element mask rows that see no key at all."""
+    B, H = 4, 2
+    n = np.array([L, L - 53, 1, 0], np.int32)
+    q, k, v, do = _inputs(3000 + d + L + variant, B, H, L, d, n, names="qkvd")
+    mask = None
+    if with_mask:
+        rng = np.random.default_rng(5)
+        mask = (rng.random((B, L, L)) < 0.35).astype(np.uint8)
+        mask[0, 7, :] = 0  # a valid query row with no valid key
+        mask[1, :, : L // 3] = 0  # whole tiles empty
+    say(f"softmax-family bwd d={d} L={L} bq={bq} bk={bk} variant={variant} bias={bias} "
+        f"mask={with_mask}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = None if mask is None else to_gpu(mask, torch.uint8)
+    bm = _bm(va, n_gpu, L, bq, bk, m_gpu)
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    o, lse = va.sigattn_fwd(*g[:3], n_gpu, block_mask=bm, mask=m_gpu, bias=bias,
+                            variant=variant, block_q=bq, block_k=bk, return_lse=True)
+    dq, dk, dv = va.sigattn_bwd(*g, n_gpu, block_mask=bm, mask=m_gpu, bias=bias, variant=variant,
+                                block_q=bq, block_k=bk, o=o, lse=lse)
+    torch.cuda.synchronize()
+    wq, wk, wv = oracle.bwd(q, k, v, do, n, mask=mask, bias=bias, variant=variant)
+    assert_rows(gpu_f64(dq), wq, n, "dQ")
+    assert_rows(gpu_f64(dk), wk, n, "dK")
+    assert_rows(gpu_f64(dv), wv, n, "dV")
+    # The two halves give the same bits as the one-launch call.
+    dk2, dv2 = va.sigattn_bwd_dkdv(*g, n_gpu, block_mask=bm, mask=m_gpu, bias=bias,
+                                   variant=variant, block_q=bq, block_k=bk, o=o, lse=lse)
+    dq2 = va.sigattn_bwd_dq(*g, n_gpu, block_mask=bm, mask=m_gpu, bias=bias, variant=variant,
+                            block_q=bq, block_k=bk, o=o, lse=lse)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 @pytest.mark.parametrize("bq,bk", [(128, 128), (64, 64), (128, 32)])
 def test_backward_parts_match_fused(va, bq, bk):
     """sigattn_bwd (one launch for dK/dV and dQ when the tile heights agree,

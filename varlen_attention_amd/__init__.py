@@ -62,11 +62,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.blockmask_build.restype = ctypes.c_int
     lib.sigattn_fwd.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, I, I, P, P, P]
     lib.sigattn_fwd.restype = ctypes.c_int
-    lib.sigattn_bwd.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, I, I, P, P, P, P]
+    lib.sigattn_bwd.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, P, P, I, I, P, P, P,
+                                P]
     lib.sigattn_bwd.restype = ctypes.c_int
-    lib.sigattn_bwd_dkdv.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.sigattn_bwd_dkdv.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, P, P, I, I, P, P,
+                                     P]
     lib.sigattn_bwd_dkdv.restype = ctypes.c_int
-    lib.sigattn_bwd_dq.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, I, I, P, P]
+    lib.sigattn_bwd_dq.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, P, P, I, I, P, P]
     lib.sigattn_bwd_dq.restype = ctypes.c_int
     lib.sigattn_last_error.argtypes = []
     lib.sigattn_last_error.restype = ctypes.c_char_p
@@ -187,7 +189,8 @@ def sigattn_fwd(q, k, v, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQ
     return (out, lse) if return_lse else out
 
 
-def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k):
+def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k, variant, o,
+              lse):
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, nm, torch.bfloat16)
     _layout([q, k, v, dout], ["q", "k", "v", "dout"])
@@ -198,6 +201,17 @@ def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k
         _need(g, "gradient output", torch.bfloat16)
     _layout(outs, ["gradient output"] * len(outs))
     B, H, L, d = q.shape
+    if variant != SIGMOID:
+        if o is None or lse is None:
+            raise ValueError("the softmax-variant backward needs the forward's o and lse")
+    if o is not None:
+        _need(o, "o", torch.bfloat16)
+        if tuple(o.shape) != tuple(q.shape) or o.stride() != outs[0].stride():
+            raise ValueError("o must have q's shape and the gradient outputs' strides")
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous fp32 [B, H, L] tensor")
     if mask is not None:
         _need(mask, "mask", torch.uint8)
         if tuple(mask.shape) != (B, L, L) or not mask.is_contiguous():
@@ -212,39 +226,46 @@ def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k
 
 def sigattn_bwd(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                 variant=SIGMOID, scale=None, block_q=128, block_k=128, dq=None, dk=None,
-                dv=None, stream=None):
+                dv=None, o=None, lse=None, stream=None):
     """Gradients (dq, dk, dv) of sum(dout * o); bf16 [B, H, L, d] on the GPU.
 
+    The softmax variants need the forward's output ``o`` and ``lse`` (from
+    ``sigattn_fwd(..., return_lse=True)`` with the same variant and bias).
     One launch for the dK/dV and dQ work when their tile heights agree (see
     include/sigattn.h); results equal sigattn_bwd_dkdv + sigattn_bwd_dq."""
     dq, dk, dv = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dq, dk, dv), block_q,
-                           block_k)
+                           block_k, variant, o, lse)
     shape = _shape(q, dq.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_bwd(
-        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(seq_lens.contiguous()),
-        _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dq), _ptr(dk), _ptr(dv),
-        _stream(stream)))
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), _ptr(lse),
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dq),
+        _ptr(dk), _ptr(dv), _stream(stream)))
     return dq, dk, dv
 
 
 def sigattn_bwd_dkdv(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                      variant=SIGMOID, scale=None, block_q=128, block_k=128, dk=None, dv=None,
-                     stream=None):
+                     o=None, lse=None, stream=None):
     """The dK/dV half of the backward pass (one kernel): returns (dk, dv)."""
-    dk, dv = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dk, dv), block_q, block_k)
+    dk, dv = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dk, dv), block_q, block_k,
+                       variant, o, lse)
     shape = _shape(q, dk.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_bwd_dkdv(
-        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(seq_lens.contiguous()),
-        _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dk), _ptr(dv), _stream(stream)))
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), _ptr(lse),
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dk),
+        _ptr(dv), _stream(stream)))
     return dk, dv
 
 
 def sigattn_bwd_dq(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
-                   variant=SIGMOID, scale=None, block_q=128, block_k=128, dq=None, stream=None):
+                   variant=SIGMOID, scale=None, block_q=128, block_k=128, dq=None, o=None,
+                   lse=None, stream=None):
     """The dQ half of the backward pass (one kernel): returns dq."""
-    (dq,) = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dq,), block_q, block_k)
+    (dq,) = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dq,), block_q, block_k,
+                      variant, o, lse)
     shape = _shape(q, dq.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_bwd_dq(
-        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(seq_lens.contiguous()),
-        _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dq), _stream(stream)))
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), _ptr(lse),
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dq),
+        _stream(stream)))
     return dq

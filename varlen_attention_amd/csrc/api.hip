@@ -152,9 +152,9 @@ namespace {
 enum BwdParts { kPartDkdv = 1, kPartDq = 2 };
 
 int backward(const sigattn_shape *shape, const void *q, const void *k, const void *v,
-             const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
-             const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dq, void *dk,
-             void *dv, void *stream, int parts, const char *name) {
+             const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
+             const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode, int32_t variant,
+             void *dq, void *dk, void *dv, void *stream, int parts, const char *name) {
     sigattn::AttnParams p = {};
     const void *inputs[4] = {q, k, v, dout};
     void *outputs[3];
@@ -167,8 +167,16 @@ int backward(const sigattn_shape *shape, const void *q, const void *k, const voi
     int st = check_attention(shape, inputs, 4, outputs, n_out, seq_lens, block_mask, mask,
                              bias_mode, variant, &p);
     if (st != SIGATTN_OK) return st;
-    if (variant != SIGATTN_SIGMOID)
-        return fail(SIGATTN_ERR_UNSUPPORTED, "backward is built for the SIGMOID variant only");
+    if (variant != SIGATTN_SIGMOID) {
+        if (o == nullptr || lse == nullptr)
+            return fail(SIGATTN_ERR_INVALID_ARG,
+                        "the softmax-variant backward needs the forward's o and lse");
+        if (!aligned16(o)) return fail(SIGATTN_ERR_ALIGNMENT, "o is not 16-byte aligned");
+        if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+            return fail(SIGATTN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
+        p.o = const_cast<void *>(o);
+        p.lse = const_cast<float *>(lse);
+    }
     p.q = q;
     p.k = k;
     p.v = v;
@@ -187,27 +195,27 @@ int backward(const sigattn_shape *shape, const void *q, const void *k, const voi
 extern "C" {
 
 int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
-                const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
-                const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dq, void *dk,
-                void *dv, void *stream) {
-    return backward(shape, q, k, v, dout, seq_lens, block_mask, mask, bias_mode, variant, dq, dk,
-                    dv, stream, kPartDkdv | kPartDq, "sigattn_bwd");
+                const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
+                const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode,
+                int32_t variant, void *dq, void *dk, void *dv, void *stream) {
+    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, bias_mode, variant,
+                    dq, dk, dv, stream, kPartDkdv | kPartDq, "sigattn_bwd");
 }
 
 int sigattn_bwd_dkdv(const sigattn_shape *shape, const void *q, const void *k, const void *v,
-                     const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
-                     const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dk,
-                     void *dv, void *stream) {
-    return backward(shape, q, k, v, dout, seq_lens, block_mask, mask, bias_mode, variant,
+                     const void *dout, const void *o, const float *lse,
+                     const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
+                     int32_t bias_mode, int32_t variant, void *dk, void *dv, void *stream) {
+    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, bias_mode, variant,
                     nullptr, dk, dv, stream, kPartDkdv, "sigattn_bwd_dkdv");
 }
 
 int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, const void *v,
-                   const void *dout, const int32_t *seq_lens, const uint8_t *block_mask,
-                   const uint8_t *mask, int32_t bias_mode, int32_t variant, void *dq,
-                   void *stream) {
-    return backward(shape, q, k, v, dout, seq_lens, block_mask, mask, bias_mode, variant, dq,
-                    nullptr, nullptr, stream, kPartDq, "sigattn_bwd_dq");
+                   const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
+                   const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode,
+                   int32_t variant, void *dq, void *stream) {
+    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, bias_mode, variant,
+                    dq, nullptr, nullptr, stream, kPartDq, "sigattn_bwd_dq");
 }
 
 const char *sigattn_last_error(void) { return g_last_error; }

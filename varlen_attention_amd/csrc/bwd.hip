@@ -103,6 +103,62 @@ struct DmaPair {
     }
 };
 
+// Dot product of two rows of eight bf16 values, accumulated in fp32.
+__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
+    const uint32_t x[4] = {a.x, a.y, a.z, a.w}, y[4] = {b.x, b.y, b.z, b.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc = fmaf(__uint_as_float(x[i] << 16), __uint_as_float(y[i] << 16), acc);
+        acc = fmaf(__uint_as_float(x[i] & 0xffff0000u), __uint_as_float(y[i] & 0xffff0000u), acc);
+    }
+    return acc;
+}
+
+// Softmax-family backward, dK/dV side: per query row of a staged tile, the
+// weight offset off = b log2 e - lse log2 e (-inf for a row without weights:
+// padded, or no valid key) and D = rowsum(dO * O).  D comes from the dO
+// chunks a PairStage holds and an O tile fetched alongside with the same
+// chunk-to-thread map; the lanes that hold one row are consecutive, so a
+// short xor reduction finishes each row.
+template <int D, int BT, int NT>
+struct RowStats {
+    static constexpr int kChunksPerRow = D / 8;
+    static constexpr int CH = BT * kChunksPerRow / NT;
+    uint4 o[CH];
+    int goff[CH];
+    float lse;
+
+    __device__ __forceinline__ void init(int64_t osl, int tid) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int idx = tid + c * NT;
+            goff[c] = (int)(((int64_t)(idx / kChunksPerRow) * osl + (idx % kChunksPerRow) * 8) * 2);
+        }
+    }
+
+    // O rows [r0, n) through ro; lse_rows points at the LSE of row r0.
+    __device__ __forceinline__ void load(rsrc_t ro, const float *lse_rows, int valid_rows,
+                                         int tid) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) o[c] = buffer_load16(ro, goff[c]);
+        lse = (tid < BT && tid < valid_rows) ? lse_rows[tid] : -INFINITY;
+    }
+
+    __device__ __forceinline__ void store(const uint4 *dout_chunks, float c0, float *d_lds,
+                                          float *off_lds, int tid) const {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            float part = dot8(dout_chunks[c], o[c]);
+#pragma unroll
+            for (int m = 1; m < kChunksPerRow; m <<= 1) part += __shfl_xor(part, m);
+            const int idx = tid + c * NT;
+            if (idx % kChunksPerRow == 0) d_lds[idx / kChunksPerRow] = part;
+        }
+        if (tid < BT) off_lds[tid] = lse == -INFINITY ? -INFINITY : c0 - lse * kLog2e;
+    }
+};
+
 template <int D>
 __device__ __forceinline__ void zero_rows(bf16 *base, int64_t sl, int r0, int rows, int tid,
                                           int nt) {
@@ -148,21 +204,24 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16 *tile, int r16, int c32,
 }  // namespace
 
 // ---------------------------------------------------------------- dK / dV
-// LDS of one dK/dV tile (elements): Q and dO tiles of 32 rows, double-buffered.
-template <int D> constexpr int kDkdvLds = 2 * 2 * 32 * D;
+// LDS of one dK/dV tile (elements): Q and dO tiles of 32 rows, double-buffered,
+// then two buffers of 2 x 32 floats of row statistics (softmax variants).
+template <int D> constexpr int kDkdvLds = 2 * 2 * 32 * D + 2 * 2 * 32 * 2;
 
 // dK and dV of key tile kt (32 NW keys) of (batch entry b, head h); smem
 // holds kDkdvLds<D> elements.
-template <int D, int NW, bool MASKED>
+template <int D, int NW, int VARIANT, bool MASKED>
 __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int kt, int n,
                                           bf16 *smem) {
-    constexpr int QB = 1;
-    constexpr int BKV = 32 * NW, BQ = 32 * QB, NT = 64 * NW;
+    constexpr int BKV = 32 * NW, BQ = 32, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
-    // Slot i of the Q and dO tiles (offsets from the LDS base, so the LDS
-    // address space stays visible to the compiler).
+    constexpr bool kSoft = VARIANT != kSigmoid;
+    // Slot i of the Q and dO tiles and of the row statistics (offsets from
+    // the LDS base, so the LDS address space stays visible to the compiler).
     auto Qs = [&](int i) { return smem + i * (BQ * D); };
     auto dOs = [&](int i) { return smem + (2 + i) * (BQ * D); };
+    auto Dl = [&](int i) { return reinterpret_cast<float *>(smem + 4 * BQ * D) + i * 2 * BQ; };
+    auto Offl = [&](int i) { return Dl(i) + BQ; };
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
@@ -181,15 +240,17 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     const bf16 *kb = reinterpret_cast<const bf16 *>(p.k) + b * p.sb + h * p.sh;
     const bf16 *vb = reinterpret_cast<const bf16 *>(p.v) + b * p.sb + h * p.sh;
     const bf16 *dob = reinterpret_cast<const bf16 *>(p.dout) + b * p.sb + h * p.sh;
+    const bf16 *obase = kSoft ? reinterpret_cast<const bf16 *>(p.o) + b * p.osb + h * p.osh
+                              : nullptr;
+    const float *lseb = kSoft ? p.lse + ((int64_t)b * p.H + h) * L : nullptr;
 
     const int kl = lane & 31, hh = lane >> 5;
     const int key = k0 + w * 32 + kl;  // this lane's key row
     const bool k_valid = key < n;
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const bool has_mask = MASKED;
-    const rsrc_t rmask = make_rsrc(has_mask ? p.mask + (int64_t)b * L * L : nullptr,
-                                   has_mask ? (int64_t)L * L : 0);
+    const rsrc_t rmask = make_rsrc(MASKED ? p.mask + (int64_t)b * L * L : nullptr,
+                                   MASKED ? (int64_t)L * L : 0);
 
     // K^T and V^T operands of S = Q K^T and dP = dO V^T: lane holds row `key`.
     const rsrc_t rk = make_rsrc(kb + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
@@ -201,10 +262,12 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         kreg[ks] = as_bf16x8(buffer_load16(rk, off));
         vreg[ks] = as_bf16x8(buffer_load16(rv, off));
     }
-    // The operand held in registers for S is scaled by c1 before the loop, so
-    // the S accumulator is u = -scale * s * log2 e (see sigmoid_scaled).
-    const float c1 = -p.scale * kLog2e;
+    // SIGMOID: K is scaled by c1 before the loop, so the S accumulator is
+    // u = -scale * s * log2 e (see sigmoid_scaled).  Softmax: the weight is
+    // exp2(s * c1 + off) with c1 = scale * log2 e and off from RowStats.
+    const float c1 = kSoft ? p.scale * kLog2e : -p.scale * kLog2e;
     const float cexp = bias_factor(p.bias_mode, n, L);
+    const float c0 = bias_value(p.bias_mode, n, L) * kLog2e;
 
     f32x16 dvt[DB], dkt[DB];
 #pragma unroll
@@ -213,20 +276,34 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     auto rows_rsrc = [&](const bf16 *base, int r0) {
         return make_rsrc(base + (int64_t)r0 * p.sl, (int64_t)(n - r0) * p.sl * 2);
     };
-    // Query tile 0 is fetched before the block mask is read (see the forward
-    // kernel); another first tile is fetched again.
+    auto out_rows_rsrc = [&](const bf16 *base, int r0) {
+        return make_rsrc(base + (int64_t)r0 * p.osl, (int64_t)(n - r0) * p.osl * 2);
+    };
     PairStage<D, BQ, NT> stage;
     stage.init(p.sl, tid);
-    stage.load(rows_rsrc(qb, 0), rows_rsrc(dob, 0));
+    RowStats<D, BQ, NT> stats;
+    if constexpr (kSoft) stats.init(p.osl, tid);
+    auto load_tile = [&](int t) {
+        stage.load(rows_rsrc(qb, t * BQ), rows_rsrc(dob, t * BQ));
+        if constexpr (kSoft) stats.load(out_rows_rsrc(obase, t * BQ), lseb + t * BQ, n - t * BQ, tid);
+    };
+    auto store_tile = [&](int i) {
+        stage.store(Qs(i), dOs(i));
+        if constexpr (kSoft) stats.store(stage.b, c0, Dl(i), Offl(i), tid);
+    };
+    // Query tile 0 is fetched before the block mask is read (see the forward
+    // kernel); another first tile is fetched again.
+    load_tile(0);
     TileSchedule<BQ> sched;
     sched.init(p.block_mask ? p.block_mask + (int64_t)b * p.Tq * p.Tk + k0 / p.block_k : nullptr,
                p.Tk, n, p.block_q);
     int qt = sched.next();
-    if (qt > 0) stage.load(rows_rsrc(qb, qt * BQ), rows_rsrc(dob, qt * BQ));
+    if (qt > 0) load_tile(qt);
     int buf = 0;
-    stage.store(Qs(0), dOs(0));
+    store_tile(0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kreg[ks] = scale8(kreg[ks], c1);
+    for (int ks = 0; ks < KS; ++ks)
+        if constexpr (!kSoft) kreg[ks] = scale8(kreg[ks], c1);
     __syncthreads();
     // This tile's share of the sequence's fully padded key tiles, written
     // while the loop computes.
@@ -235,53 +312,66 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     while (qt >= 0) {
         const int q0 = qt * BQ;
         const int nxt = sched.next();
-        if (nxt >= 0) stage.load(rows_rsrc(qb, nxt * BQ), rows_rsrc(dob, nxt * BQ));
+        if (nxt >= 0) load_tile(nxt);
         const bf16 *Qc = Qs(buf);
         const bf16 *dOc = dOs(buf);
+        const float *Dc = Dl(buf);
+        const float *Offc = Offl(buf);
         // One straight-line body per tile kind.  MODE 0 (no element mask)
         // needs no per-element masking: padded query rows of Q and dO read as
-        // zeros, so dP = 0 and dS = 0 there and their dV terms multiply zero
-        // rows; padded key rows are zeroed at the store.  MODE 2: element mask.
+        // zeros, so dP = 0 and dS = 0 there (softmax: their off is -inf, so
+        // P = 0) and their dV terms multiply zero rows; padded key rows are
+        // zeroed at the store.  MODE 2: element mask.
         auto tile = [&](auto mode_tag) {
             constexpr int MODE = decltype(mode_tag)::value;
+            f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int qb2 = 0; qb2 < QB; ++qb2) {
-                f32x16 s = f32x16{}, dp = f32x16{};
+            for (int ks = 0; ks < KS; ++ks) {
+                s = mfma32(row_operand<D>(Qc, kl, ks * 16 + hh * 8), kreg[ks], s);
+                dp = mfma32(row_operand<D>(dOc, kl, ks * 16 + hh * 8), vreg[ks], dp);
+            }
+            // s[4i + j] = S[query q0 + 8 i + 4 hh + j][key]
+            f32x4 offq[4], dq4[4];
+            if constexpr (kSoft) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    s = mfma32(row_operand<D>(Qc, qb2 * 32 + kl, ks * 16 + hh * 8), kreg[ks], s);
-                    dp = mfma32(row_operand<D>(dOc, qb2 * 32 + kl, ks * 16 + hh * 8), vreg[ks],
-                                dp);
+                for (int i = 0; i < 4; ++i) {
+                    offq[i] = *reinterpret_cast<const f32x4 *>(Offc + 8 * i + 4 * hh);
+                    dq4[i] = *reinterpret_cast<const f32x4 *>(Dc + 8 * i + 4 * hh);
                 }
-                // s[4i + j] = S[query q0 + 32 qb2 + 8 i + 4 hh + j][key]
-                float pv[16], dsv[16];
+            }
+            float pv[16], dsv[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pr = sigmoid_scaled(s[r], cexp);
-                    if constexpr (MODE == 2) {
-                        const int qr = q0 + qb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                        const bool ok = k_valid && qr < n &&
-                                        buffer_load_u8(rmask, qr * L + key) != 0;
-                        pr = keep_or_zero(pr, ok);
-                    }
-                    pv[r] = pr;
+            for (int r = 0; r < 16; ++r) {
+                float pr;
+                if constexpr (kSoft)
+                    pr = __builtin_amdgcn_exp2f(fmaf(s[r], c1, offq[r >> 2][r & 3]));
+                else
+                    pr = sigmoid_scaled(s[r], cexp);
+                if constexpr (MODE == 2) {
+                    const int qr = q0 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                    const bool ok = k_valid && qr < n &&
+                                    buffer_load_u8(rmask, qr * L + key) != 0;
+                    pr = keep_or_zero(pr, ok);
+                }
+                pv[r] = pr;
+                if constexpr (kSoft)
+                    dsv[r] = pr * (dp[r] - dq4[r >> 2][r & 3]);
+                else
                     dsv[r] = dp[r] * (pr - pr * pr);
-                }
+            }
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 pb = pack8(&pv[kk * 8]);
-                    const bf16x8 sb = pack8(&dsv[kk * 8]);
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 pb = pack8(&pv[kk * 8]);
+                const bf16x8 sb = pack8(&dsv[kk * 8]);
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const int r16 = qb2 * 32 + kk * 16;
-                        dvt[db] = mfma32(tr_operand<D>(dOc, r16, db * 32, trow, tcol), pb, dvt[db]);
-                        dkt[db] = mfma32(tr_operand<D>(Qc, r16, db * 32, trow, tcol), sb, dkt[db]);
-                    }
+                for (int db = 0; db < DB; ++db) {
+                    dvt[db] = mfma32(tr_operand<D>(dOc, kk * 16, db * 32, trow, tcol), pb, dvt[db]);
+                    dkt[db] = mfma32(tr_operand<D>(Qc, kk * 16, db * 32, trow, tcol), sb, dkt[db]);
                 }
             }
         };
         tile(std::integral_constant<int, MASKED ? 2 : 0>{});
-        if (nxt >= 0) stage.store(Qs(buf ^ 1), dOs(buf ^ 1));
+        if (nxt >= 0) store_tile(buf ^ 1);
         __syncthreads();
         buf ^= 1;
         qt = nxt;
@@ -296,11 +386,12 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
 // dQ of query tile qt (32 NW queries) of (batch entry b, head h), visiting
 // keys 32 KB at a time.  K0, V0, K1, V1 are four separate LDS objects of
 // 32 KB rows x D each (two buffers of the K and V tiles).
-template <int D, int NW, int KB, bool MASKED>
+template <int D, int NW, int KB, int VARIANT, bool MASKED>
 __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int qt, int n,
                                         bf16 *K0, bf16 *V0, bf16 *K1, bf16 *V1) {
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
+    constexpr bool kSoft = VARIANT != kSigmoid;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -336,10 +427,29 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
         qreg[ks] = as_bf16x8(buffer_load16(rq, off));
         doreg[ks] = as_bf16x8(buffer_load16(rdo, off));
     }
-    // The operand held in registers for S is scaled by c1 before the loop, so
-    // the S accumulator is u = -scale * s * log2 e (see sigmoid_scaled).
-    const float c1 = -p.scale * kLog2e;
+    // SIGMOID: Q is scaled by c1 before the loop, so the S accumulator is
+    // u = -scale * s * log2 e (see sigmoid_scaled).  Softmax: the weight is
+    // exp2(s * c1 + off) with c1 = scale * log2 e, off = b log2 e - lse log2 e
+    // (-inf for a padded row or one without weights), and dS = P (dP - D)
+    // with D = rowsum(dO * O) of this lane's query.
+    const float c1 = kSoft ? p.scale * kLog2e : -p.scale * kLog2e;
     const float cexp = bias_factor(p.bias_mode, n, L);
+    float off = 0.0f, drow = 0.0f;
+    if constexpr (kSoft) {
+        const bf16 *ob = reinterpret_cast<const bf16 *>(p.o) + b * p.osb + h * p.osh;
+        const rsrc_t ro = make_rsrc(ob + (int64_t)q0 * p.osl, (int64_t)(n - q0) * p.osl * 2);
+        float part = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint4 o8 = buffer_load16(
+                ro, (int)(((int64_t)(w * 32 + ql) * p.osl + ks * 16 + hh * 8) * 2));
+            part += dot8(__builtin_bit_cast(uint4, doreg[ks]), o8);
+        }
+        drow = part + __shfl_xor(part, 32);
+        const float lse = q_valid ? p.lse[((int64_t)b * p.H + h) * L + qr] : -INFINITY;
+        off = lse == -INFINITY ? -INFINITY
+                               : bias_value(p.bias_mode, n, L) * kLog2e - lse * kLog2e;
+    }
 
     f32x16 dqt[DB];
 #pragma unroll
@@ -365,7 +475,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     int kt = sched.next();
     if (kt > 0) fetch(kt, K0, V0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[ks] = scale8(qreg[ks], c1);
+    for (int ks = 0; ks < KS; ++ks)
+        if constexpr (!kSoft) qreg[ks] = scale8(qreg[ks], c1);
     wait_vm0();
     __syncthreads();
     // This tile's share of the sequence's fully padded query tiles.
@@ -393,14 +504,21 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                 float dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float pr = sigmoid_scaled(s[r], cexp);
+                    float pr;
+                    if constexpr (kSoft)
+                        pr = __builtin_amdgcn_exp2f(fmaf(s[r], c1, off));
+                    else
+                        pr = sigmoid_scaled(s[r], cexp);
                     if constexpr (MODE == 2) {
                         const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
                         const bool ok = q_valid && key < n &&
                                         buffer_load_u8(rmask, mrow_off + key) != 0;
                         pr = keep_or_zero(pr, ok);
                     }
-                    dsv[r] = dp[r] * (pr - pr * pr);
+                    if constexpr (kSoft)
+                        dsv[r] = pr * (dp[r] - drow);
+                    else
+                        dsv[r] = dp[r] * (pr - pr * pr);
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
@@ -426,17 +544,17 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
 }
 
 // ---------------------------------------------------------------- kernels
-template <int D, int NW, bool MASKED>
+template <int D, int NW, int VARIANT, bool MASKED>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
     constexpr int BKV = 32 * NW;
     int b, h, kt, n;
     if (!tile_item<BKV>(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt, n)) return;
-    dkdv_tile<D, NW, MASKED>(p, b, h, kt, n, smem);
+    dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, kt, n, smem);
 }
 
-template <int D, int NW, int KB, bool MASKED>
+template <int D, int NW, int KB, int VARIANT, bool MASKED>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dq_kernel(const AttnParams p) {
     constexpr int kTile = 32 * KB * D;
@@ -444,14 +562,14 @@ bwd_dq_kernel(const AttnParams p) {
     constexpr int BQ = 32 * NW;
     int b, h, qt, n;
     if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
-    dq_tile<D, NW, KB, MASKED>(p, b, h, qt, n, K0, V0, K1, V1);
+    dq_tile<D, NW, KB, VARIANT, MASKED>(p, b, h, qt, n, K0, V0, K1, V1);
 }
 
 // dK/dV and dQ in one launch: both kinds of tile of a (batch entry, head)
 // pair are dealt out together, longest sequences first, so the two share one
 // ramp-up and one tail.  Needs the same 32 NW rows for the key tiles of
 // dK/dV and the query tiles of dQ.
-template <int D, int NW, int KB, bool MASKED>
+template <int D, int NW, int KB, int VARIANT, bool MASKED>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
@@ -462,9 +580,9 @@ bwd_kernel(const AttnParams p) {
     int b, h, kind, t, n;
     if (!tile_item2<R, R>(p.seq_lens, p.B, p.H, p.L, nt, nt, b, h, kind, t, n)) return;
     if (kind == 0)
-        dkdv_tile<D, NW, MASKED>(p, b, h, t, n, smem);
+        dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, t, n, smem);
     else
-        dq_tile<D, NW, KB, MASKED>(p, b, h, t, n, K0, V0, K1, V1);
+        dq_tile<D, NW, KB, VARIANT, MASKED>(p, b, h, t, n, K0, V0, K1, V1);
 }
 
 // Waves per workgroup: 32 NW keys per dK/dV workgroup must divide block_k,
@@ -476,7 +594,7 @@ static int dq_waves(const AttnParams &p) { return p.block_q >= 128 ? 4 : p.block
 // operand registers no longer fit without spilling.
 static int dq_key_blocks(const AttnParams &p) { return p.block_k >= 64 && p.d == 64 ? 2 : 1; }
 
-template <int D>
+template <int D, int VARIANT>
 static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
     const int nw = dkdv_waves(p);
     const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
@@ -484,11 +602,11 @@ static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
 #define SIGATTN_DKDV_CASE(NW_)                                                          \
     if (nw == NW_) {                                                                     \
         if (p.mask != nullptr)                                                           \
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, true>), grid, block, 0, stream,  \
-                               p);                                                       \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, VARIANT, true>), grid, block, 0, \
+                               stream, p);                                               \
         else                                                                             \
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, false>), grid, block, 0, stream, \
-                               p);                                                       \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, VARIANT, false>), grid, block,   \
+                               0, stream, p);                                            \
         return hipGetLastError();                                                        \
     }
     SIGATTN_DKDV_CASE(4)
@@ -498,7 +616,7 @@ static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-template <int D>
+template <int D, int VARIANT>
 static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     const int nw = dq_waves(p), kb = dq_key_blocks(p);
     const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
@@ -507,11 +625,11 @@ static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     if constexpr (D == 64 || KB_ == 1)                                                   \
     if (nw == NW_ && kb == KB_) {                                                        \
         if (p.mask != nullptr)                                                           \
-            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, true>), grid, block, 0,       \
-                               stream, p);                                               \
+            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, VARIANT, true>), grid, block, \
+                               0, stream, p);                                            \
         else                                                                             \
-            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, false>), grid, block, 0,      \
-                               stream, p);                                               \
+            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, VARIANT, false>), grid,       \
+                               block, 0, stream, p);                                     \
         return hipGetLastError();                                                        \
     }
     SIGATTN_DQ_CASE(4, 2)
@@ -524,12 +642,12 @@ static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-template <int D>
+template <int D, int VARIANT>
 static hipError_t launch_bwd_d(const AttnParams &p, hipStream_t stream) {
     const int nw = dkdv_waves(p), kb = dq_key_blocks(p);
     if (nw != dq_waves(p)) {  // different tile heights: two launches
-        hipError_t e = launch_dkdv_d<D>(p, stream);
-        return e != hipSuccess ? e : launch_dq_d<D>(p, stream);
+        hipError_t e = launch_dkdv_d<D, VARIANT>(p, stream);
+        return e != hipSuccess ? e : launch_dq_d<D, VARIANT>(p, stream);
     }
     const dim3 grid = tile_grid(2 * ((p.L + 32 * nw - 1) / (32 * nw)), p.B, p.H);
     dim3 block(64 * nw);
@@ -537,11 +655,11 @@ static hipError_t launch_bwd_d(const AttnParams &p, hipStream_t stream) {
     if constexpr (D == 64 || KB_ == 1)                                                   \
     if (nw == NW_ && kb == KB_) {                                                        \
         if (p.mask != nullptr)                                                           \
-            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, true>), grid, block, 0, stream,  \
-                               p);                                                       \
+            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, VARIANT, true>), grid, block, 0, \
+                               stream, p);                                               \
         else                                                                             \
-            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, false>), grid, block, 0, stream, \
-                               p);                                                       \
+            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, VARIANT, false>), grid, block,   \
+                               0, stream, p);                                            \
         return hipGetLastError();                                                        \
     }
     SIGATTN_BWD_CASE(4, 2)
@@ -554,16 +672,39 @@ static hipError_t launch_bwd_d(const AttnParams &p, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
+// Dispatch on head dimension and variant.
+template <template <int, int> class F>
+static hipError_t by_shape(const AttnParams &p, hipStream_t stream) {
+    if (p.d == 64) {
+        if (p.variant == kSigmoid) return F<64, kSigmoid>::run(p, stream);
+        if (p.variant == kSoftmax) return F<64, kSoftmax>::run(p, stream);
+        return F<64, kSoftmax1>::run(p, stream);
+    }
+    if (p.variant == kSigmoid) return F<128, kSigmoid>::run(p, stream);
+    if (p.variant == kSoftmax) return F<128, kSoftmax>::run(p, stream);
+    return F<128, kSoftmax1>::run(p, stream);
+}
+
+template <int D, int V> struct DkdvLaunch {
+    static hipError_t run(const AttnParams &p, hipStream_t s) { return launch_dkdv_d<D, V>(p, s); }
+};
+template <int D, int V> struct DqLaunch {
+    static hipError_t run(const AttnParams &p, hipStream_t s) { return launch_dq_d<D, V>(p, s); }
+};
+template <int D, int V> struct BwdLaunch {
+    static hipError_t run(const AttnParams &p, hipStream_t s) { return launch_bwd_d<D, V>(p, s); }
+};
+
 hipError_t launch_bwd_dkdv(const AttnParams &p, hipStream_t stream) {
-    return p.d == 64 ? launch_dkdv_d<64>(p, stream) : launch_dkdv_d<128>(p, stream);
+    return by_shape<DkdvLaunch>(p, stream);
 }
 
 hipError_t launch_bwd_dq(const AttnParams &p, hipStream_t stream) {
-    return p.d == 64 ? launch_dq_d<64>(p, stream) : launch_dq_d<128>(p, stream);
+    return by_shape<DqLaunch>(p, stream);
 }
 
 hipError_t launch_bwd(const AttnParams &p, hipStream_t stream) {
-    return p.d == 64 ? launch_bwd_d<64>(p, stream) : launch_bwd_d<128>(p, stream);
+    return by_shape<BwdLaunch>(p, stream);
 }
 
 }  // namespace sigattn
