@@ -279,6 +279,208 @@ class HipTimer:
         self._events = []
 
 
+# --------------------------------------------------------------------------
+# Measurement suite (--suite): warm and cold kernel times, valid-work and
+# tile-work TFLOP/s and algorithmic HBM GB/s for the benchmark shapes, the
+# softmax variants at the single-cell shapes, a padding sweep and the
+# long packed-document case.  Markdown on stdout; the default JSON line above
+# is unaffected.
+# --------------------------------------------------------------------------
+
+SUITE_WARMUP = 20
+SUITE_REPS = 50
+SUITE_SETTLE_S = 0.3
+FLUSH_BYTES = 1 << 30  # larger than the last-level cache, so each cold rep starts empty
+
+
+def suite_bytes(kernel: str, w, variant: int, masked: bool) -> float:
+    """Algorithmic HBM bytes of one launch: valid rows of the inputs read once,
+    every row of the outputs written once; the softmax variants add O and the
+    log-sum-exp rows; the block-mask builder reads the element mask once."""
+    valid = float(np.clip(w.seq_lens, 0, w.L).sum()) * w.H
+    every = float(w.B) * w.L * w.H
+    row = 2.0 * w.d
+    if kernel == "blockmask":
+        tiles = float(w.B) * (-(-w.L // w.block_q)) * (-(-w.L // w.block_k))
+        return (float(w.B) * w.L * w.L if masked else 4.0 * w.B) + tiles
+    soft = variant != 0
+    if kernel == "fwd":
+        return (3 * valid + every) * row + (every * 4.0 if soft else 0.0)
+    reads = 5 if soft else 4
+    return (reads * valid + 3 * every) * row + (valid * 4.0 if soft else 0.0)
+
+
+class SuiteTimer:
+    """Per-launch durations from fence-free HIP events on one stream."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.timer = HipTimer(stream.cuda_stream)
+
+    def steps(self, fns, reps=SUITE_REPS, settle_s=SUITE_SETTLE_S):
+        """Repeats the sequence fns (one step) and returns per-launch times in
+        us, shape [reps, len(fns)].  Untimed steps run first until the clocks
+        have settled: at least SUITE_WARMUP steps and settle_s seconds."""
+        import torch
+        t0, done = time.perf_counter(), 0
+        while done < SUITE_WARMUP or time.perf_counter() - t0 < settle_s:
+            for fn in fns:
+                fn()
+            done += 1
+            if done % 10 == 0:
+                torch.cuda.synchronize()
+        ev = [self.timer.event() for _ in range(reps * len(fns) + 1)]
+        torch.cuda.synchronize()
+        self.timer.record(ev[0])
+        for i in range(reps):
+            for j, fn in enumerate(fns):
+                fn()
+                self.timer.record(ev[i * len(fns) + j + 1])
+        torch.cuda.synchronize()
+        t = [self.timer.elapsed_ms(ev[i], ev[i + 1]) for i in range(reps * len(fns))]
+        return np.array(t).reshape(reps, len(fns)) * 1e3
+
+    def cold(self, fn, flush, reps=SUITE_REPS):
+        """Per-launch times in us of fn run right after a fill of `flush`."""
+        import torch
+        fn()
+        ev = [self.timer.event() for _ in range(2 * reps)]
+        torch.cuda.synchronize()
+        for i in range(reps):
+            flush.fill_(float(i))
+            self.timer.record(ev[2 * i])
+            fn()
+            self.timer.record(ev[2 * i + 1])
+        torch.cuda.synchronize()
+        return np.array([self.timer.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(reps)]) * 1e3
+
+    def close(self):
+        self.timer.close()
+
+
+def run_suite(args) -> int:
+    import torch
+
+    import synthetic as syn
+    import varlen_attention_amd as va
+
+    assert torch.cuda.is_available(), "the suite needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    timer = SuiteTimer(stream)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    rows = []
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name}: {props.multi_processor_count} compute units")
+
+    def gpu(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def case(label, w, variant=syn.SIGMOID, bias=syn.BIAS_LOG_SEQLEN, block=128, kernels=("fwd", "bwd"),
+             cold=True):
+        """Times blockmask_build, fwd and bwd of workload w; one table row each."""
+        log(f"case {label}: B={w.B} H={w.H} L={w.L} d={w.d} block={block} variant={variant}")
+        q, k, v = gpu(w.q), gpu(w.k), gpu(w.v)
+        do = gpu(w.do) if w.do is not None else None
+        n = torch.from_numpy(w.seq_lens).to(dev)
+        mask = torch.from_numpy(w.mask).to(dev) if w.mask is not None else None
+        w.block_q = w.block_k = block
+        bm = va.blockmask_build(n, w.L, block, block, mask=mask)
+        tiles = int(bm.sum().item()) * w.H
+        pairs = w.valid_pairs * w.H
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev) if variant else None
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        fns = {
+            "blockmask": lambda: va.blockmask_build(n, w.L, block, block, mask=mask, out=bm),
+            "fwd": lambda: va.sigattn_fwd(q, k, v, n, block_mask=bm, mask=mask, bias=bias,
+                                          variant=variant, block_q=block, block_k=block, out=o,
+                                          lse=lse),
+            "bwd": lambda: va.sigattn_bwd(q, k, v, do, n, block_mask=bm, mask=mask, bias=bias,
+                                          variant=variant, block_q=block, block_k=block, dq=dq,
+                                          dk=dk, dv=dv, o=o if variant else None, lse=lse),
+        }
+        fns["fwd"]()
+        torch.cuda.synchronize()
+        per_pair = {"fwd": 4.0 * w.d, "bwd": 10.0 * w.d}
+        names = ("blockmask",) + tuple(kernels)
+        warm = timer.steps([fns[kern] for kern in names])
+        tot = warm.sum(axis=1)
+        for j, kern in enumerate(names):
+            cold_t = timer.cold(fns[kern], flush) if cold else None
+            med = float(np.median(warm[:, j]))
+            r = {"case": label, "kernel": kern, "warm_med_us": med,
+                 "warm_min_us": float(warm[:, j].min()),
+                 "cold_med_us": float(np.median(cold_t)) if cold else None,
+                 "gbs": suite_bytes(kern, w, variant, mask is not None) / (med * 1e-6) / 1e9}
+            if kern in per_pair:
+                r["valid_tf"] = per_pair[kern] * pairs / (med * 1e-6) / 1e12
+                r["tile_tf"] = per_pair[kern] * tiles * block * block / (med * 1e-6) / 1e12
+            rows.append(r)
+            log(f"  {kern}: warm median {med:.2f} us, min {warm[:, j].min():.2f} us"
+                + (f", cold median {np.median(cold_t):.2f} us" if cold else ""))
+        flops = sum(per_pair[kern] for kern in kernels) * pairs
+        rows.append({"case": label, "kernel": "step", "warm_med_us": float(np.median(tot)),
+                     "warm_min_us": float(tot.min()), "cold_med_us": None,
+                     "valid_tf": flops / (np.median(tot) * 1e-6) / 1e12,
+                     "tile_tf": flops / pairs * tiles * block * block / (np.median(tot) * 1e-6) / 1e12,
+                     "gbs": None})
+        del q, k, v, do, o, dq, dk, dv, mask, bm
+        torch.cuda.empty_cache()
+        return rows[-1]
+
+    # Single cell, sigmoid with bias -ln n, block 128 and 64.
+    w = syn.single_cell(args.seed, tensors=("q", "k", "v", "do"))
+    case("single cell, sigmoid, block 128", w)
+    case("single cell, sigmoid, block 64", w, block=64)
+    # The softmax variants at the same shapes (no bias).
+    case("single cell, softmax", w, variant=syn.SOFTMAX, bias=syn.BIAS_NONE)
+    case("single cell, softmax_1", w, variant=syn.SOFTMAX1, bias=syn.BIAS_NONE)
+    # Backward workload: lengths clipped to [200, 4096] (the same draw).
+    wb = syn.single_cell_backward(args.seed)
+    case("single cell bwd (clip 4096)", wb, kernels=("bwd",))
+    # Padding sweep: the same lengths padded to 1x, 2x and 4x the longest.
+    maxn = int(w.seq_lens.max())
+    for f in (1, 2, 4):
+        ws = syn.make_workload(f"pad{f}", seed=args.seed, B=w.B, H=w.H, d=w.d, lengths="lognormal",
+                               lo=200, hi=2048, seq_lens=w.seq_lens, L=f * maxn,
+                               tensors=("q", "k", "v", "do"))
+        case(f"padding sweep, L = {f} x max n", ws, cold=False)
+    # Equal valid tokens with no padding and with 25% padding.
+    flat = np.full(32, 768, dtype=np.int32)
+    ramp = np.rint(np.linspace(512, 1024, 32)).astype(np.int32)
+    for label, lens in (("0% padding (n = 768 for all 32)", flat),
+                        ("25% padding (n = 512..1024, L = 1024)", ramp)):
+        wp = syn.make_workload("pad_pair", seed=args.seed, B=32, H=8, d=64, lengths="uniform",
+                               lo=0, hi=0, seq_lens=lens, tensors=("q", "k", "v", "do"))
+        case(label, wp, cold=False)
+    del w, wb
+    # Long packed documents: causal mask within documents, d = 128.
+    wl = syn.long_packed_docs(args.seed, tensors=("q", "k", "v", "do"))
+    case("long packed documents, causal mask", wl)
+    timer.close()
+
+    print(f"Measurement suite on {props.name} ({props.multi_processor_count} CUs), seed {args.seed}.")
+    print(f"Warm: steps (block mask, forward, backward) repeated until the clocks settle "
+          f"(at least {SUITE_WARMUP} steps and {SUITE_SETTLE_S} s), then {SUITE_REPS} timed steps; "
+          f"cold: a {FLUSH_BYTES >> 20} MiB fill before each of {SUITE_REPS} timed launches of "
+          "one kernel.  Times are HIP-event durations per launch; rates use the warm median; "
+          "'step' is the sum of the step's kernels.")
+    print("Valid TF counts attended (query, key) pairs (4d per pair forward, 10d backward); tile TF "
+          "counts every pair of the tiles the block mask keeps; GB/s is algorithmic bytes "
+          "(valid input rows read once, every output row written once).")
+    print()
+    print("| case | kernel | warm median (us) | warm min (us) | cold median (us) | valid TFLOP/s | "
+          "tile TFLOP/s | algorithmic GB/s |")
+    print("|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        f = lambda key, fmt: (fmt.format(r[key]) if r.get(key) is not None else "-")
+        print(f"| {r['case']} | {r['kernel']} | {r['warm_med_us']:.2f} | {r['warm_min_us']:.2f} | "
+              f"{f('cold_med_us', '{:.2f}')} | {f('valid_tf', '{:.1f}')} | {f('tile_tf', '{:.1f}')} | "
+              f"{f('gbs', '{:.0f}')} |")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,6 +498,8 @@ def main() -> int:
                     metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="print the HBM traffic summary of KERNEL from FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--suite", action="store_true",
+                    help="run the measurement suite (markdown on stdout) instead of the step")
     args = ap.parse_args()
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats, args.skip_dispatches))
@@ -309,6 +513,8 @@ def main() -> int:
     if args.copy_reference_mib:
         copy_reference(args.copy_reference_mib)
         return 0
+    if args.suite:
+        return run_suite(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by batch entry and head without any exchange).", file=sys.stderr)

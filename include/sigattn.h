@@ -65,6 +65,11 @@ typedef enum {
     SIGATTN_ERR_LAUNCH = -4       /* HIP reported an error while enqueuing */
 } sigattn_status;
 
+/* Largest padded length accepted together with an element mask: the kernels
+ * address a batch entry's L x L mask (plus one tile of rows) with 32-bit
+ * offsets. */
+#define SIGATTN_MAX_MASKED_L 46080
+
 /*
  * Problem shape.  Q, K, V and dO share one layout, O, dQ, dK and dV another;
  * both are [B, H, L, d] with the head dimension contiguous (stride 1) and the
@@ -110,7 +115,9 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, int32_t B, int
  *   block_mask  [device] uint8 [B, Tq, Tk] from blockmask_build with the same
  *               block sizes, or NULL: tiles are then chosen from seq_lens
  *               alone.  Required when mask != NULL.
- *   mask        [device] uint8 [B, L, L] or NULL (element mask, all heads)
+ *   mask        [device] uint8 [B, L, L] or NULL (element mask, all heads;
+ *               non-zero = may attend; rows need no alignment); with a mask,
+ *               L <= SIGATTN_MAX_MASKED_L (else UNSUPPORTED)
  *   o           [device] bf16 [B, H, L, d] (output layout), fully written
  *   lse         [device] float [B, H, L] contiguous, or NULL.  Softmax
  *               variants write the natural log of each row's denominator

@@ -70,6 +70,8 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, va, _shape(va, stride_l=68)) == va.ERR_ALIGNMENT
     assert _fwd(lib, va, _shape(va, stride_l=32)) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va), lse=ctypes.c_void_p(0x10002)) == va.ERR_ALIGNMENT
+    # An element mask bounds L (32-bit offsets into each L x L mask).
+    assert _fwd(lib, va, _shape(va, L=46081), mask=FAKE, bm=FAKE) == va.ERR_UNSUPPORTED
 
 
 def test_backward_argument_errors(lib):
@@ -88,6 +90,7 @@ def test_backward_argument_errors(lib):
     assert bwd(var=2, o=FAKE, lse=ctypes.c_void_p(0x10002)) == va.ERR_ALIGNMENT
     assert bwd(dk=None) == va.ERR_INVALID_ARG
     assert bwd(mask=FAKE) == va.ERR_INVALID_ARG  # an element mask needs its block mask
+    assert bwd(shape=_shape(va, L=50000), mask=FAKE, bm=FAKE) == va.ERR_UNSUPPORTED
     assert bwd(shape=_shape(va, d=128, L=0)) == va.ERR_INVALID_ARG
     assert lib.sigattn_bwd_dq(ctypes.byref(sh), *args, None, None, FAKE, None, None, 1, 1, FAKE,
                               None) == va.ERR_INVALID_ARG

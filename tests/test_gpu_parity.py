@@ -204,6 +204,40 @@ def test_unit_values_row_sums(va):
         assert np.all(o1[b, :, : n[b]] > 0) and np.all(o1[b, :, : n[b]] <= 1)
 
 
+@pytest.mark.parametrize("d,L,bq,bk", [(64, 257, 128, 128), (128, 257, 128, 64),
+                                       (64, 211, 32, 32), (128, 300, 64, 128)])
+def test_mask_end_of_batch_entry(va, d, L, bq, bk):
+    """Mask entries in the last rows and keys of each batch entry, where a
+    tile's mask window runs past the end of the L x L mask: the last row sees
+    only its last key, so losing that entry would zero the row (bias 0 keeps
+    the weight near 1/2).  Forward and backward against the oracle."""
+    B, H = 2, 2
+    n = np.array([L, L - 1], np.int32)
+    q, k, v, do = _inputs(4000 + d + L, B, H, L, d, n, names="qkvd")
+    rng = np.random.default_rng(11)
+    mask = (rng.random((B, L, L)) < 0.2).astype(np.uint8)
+    for b in range(B):
+        nb = int(n[b])
+        mask[b, nb - 1, :] = 0
+        mask[b, nb - 1, nb - 1] = 1
+        mask[b, :, nb - 1] = 1  # every query sees the last key
+    say(f"mask end d={d} L={L} bq={bq} bk={bk}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = to_gpu(mask, torch.uint8)
+    bm = _bm(va, n_gpu, L, bq, bk, m_gpu)
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    o = va.sigattn_fwd(*g[:3], n_gpu, block_mask=bm, mask=m_gpu, bias=0, block_q=bq, block_k=bk)
+    dq, dk, dv = va.sigattn_bwd(*g, n_gpu, block_mask=bm, mask=m_gpu, bias=0, block_q=bq,
+                                block_k=bk)
+    torch.cuda.synchronize()
+    want, _ = oracle.fwd(q, k, v, n, mask=mask, bias=0)
+    assert_rows(gpu_f64(o), want, n, "O")
+    wq, wk, wv = oracle.bwd(q, k, v, do, n, mask=mask, bias=0)
+    assert_rows(gpu_f64(dq), wq, n, "dQ")
+    assert_rows(gpu_f64(dk), wk, n, "dK")
+    assert_rows(gpu_f64(dv), wv, n, "dV")
+
+
 # --------------------------------------------------------------- forward, full size
 def _sample_rows(rng, n, L, count=6):
     rows = {0, max(n - 1, 0), min(n, L - 1)}
@@ -476,14 +510,13 @@ def test_backward_poison_determinism_and_identities(va):
             assert abs(e1 - e2) <= 2e-2 * scale + 1e-6
 
 
-def test_backward_single_cell_full_size(va, single_cell_inputs):
-    w = single_cell_inputs
-    say(f"bwd full {w.name} L={w.L}")
+def _check_sampled_bwd(va, w):
     n = w.seq_lens
     n_gpu = to_gpu(n, torch.int32)
-    bm = _bm(va, n_gpu, w.L, 128, 128)
+    m_gpu = None if w.mask is None else to_gpu(w.mask, torch.uint8)
+    bm = _bm(va, n_gpu, w.L, 128, 128, m_gpu)
     dq, dk, dv = va.sigattn_bwd(*(to_gpu_bf16(t) for t in (w.q, w.k, w.v, w.do)), n_gpu,
-                                block_mask=bm)
+                                block_mask=bm, mask=m_gpu)
     torch.cuda.synchronize()
     dq, dk, dv = (gpu_f64(t) for t in (dq, dk, dv))
     valid = row_valid(n, w.B, w.L)
@@ -499,7 +532,7 @@ def test_backward_single_cell_full_size(va, single_cell_inputs):
         q_rows = _sample_rows(rng, nb, w.L, 4)
         k0 = int(rng.integers(0, max(nb - 8, 1)))
         k_rows = list(range(k0, min(k0 + 8, nb)))
-        rq, rk, rv = oracle.bwd_rows(w.q, w.k, w.v, w.do, n, b, h, q_rows, k_rows)
+        rq, rk, rv = oracle.bwd_rows(w.q, w.k, w.v, w.do, n, b, h, q_rows, k_rows, mask=w.mask)
         got["dq"].append(dq[b, h, q_rows])
         want["dq"].append(rq)
         got["dk"].append(dk[b, h, k_rows])
@@ -508,3 +541,16 @@ def test_backward_single_cell_full_size(va, single_cell_inputs):
         want["dv"].append(rv)
     for key in got:
         assert_close(np.concatenate(got[key]), np.concatenate(want[key]), f"{key} sampled")
+
+
+def test_backward_single_cell_full_size(va, single_cell_inputs):
+    w = single_cell_inputs
+    say(f"bwd full {w.name} L={w.L}")
+    _check_sampled_bwd(va, w)
+
+
+def test_backward_long_documents_full_size(va):
+    """The causal packed-document mask at B8 H16 d128 (L = 7122): sampled rows."""
+    w = syn.long_packed_docs(0, tensors=("q", "k", "v", "do"))
+    say(f"bwd full {w.name} L={w.L}")
+    _check_sampled_bwd(va, w)

@@ -62,6 +62,9 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
         if (outputs[i] == nullptr) return fail(SIGATTN_ERR_INVALID_ARG, "output %d is NULL", i);
     if (mask != nullptr && block_mask == nullptr)
         return fail(SIGATTN_ERR_INVALID_ARG, "an element mask needs its block mask");
+    if (mask != nullptr && s->L > SIGATTN_MAX_MASKED_L)
+        return fail(SIGATTN_ERR_UNSUPPORTED, "with an element mask L must be at most %d (got %d)",
+                    SIGATTN_MAX_MASKED_L, s->L);
     for (int i = 0; i < n_inputs; ++i)
         if (!aligned16(inputs[i]))
             return fail(SIGATTN_ERR_ALIGNMENT, "input %d is not 16-byte aligned", i);

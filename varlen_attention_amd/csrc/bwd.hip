@@ -208,11 +208,14 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16 *tile, int r16, int c32,
 // then two buffers of 2 x 32 floats of row statistics (softmax variants).
 template <int D> constexpr int kDkdvLds = 2 * 2 * 32 * D + 2 * 2 * 32 * 2;
 
+// Element-mask bits of two tiles (MaskStage words), for either kind of work.
+constexpr int kMaskWords = 2 * 256;
+
 // dK and dV of key tile kt (32 NW keys) of (batch entry b, head h); smem
-// holds kDkdvLds<D> elements.
+// holds kDkdvLds<D> elements, mbits kMaskWords words (element mask only).
 template <int D, int NW, int VARIANT, bool MASKED>
 __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int kt, int n,
-                                          bf16 *smem) {
+                                          bf16 *smem, uint32_t *mbits) {
     constexpr int BKV = 32 * NW, BQ = 32, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
     constexpr bool kSoft = VARIANT != kSigmoid;
@@ -251,6 +254,10 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const rsrc_t rmask = make_rsrc(MASKED ? p.mask + (int64_t)b * L * L : nullptr,
                                    MASKED ? (int64_t)L * L : 0);
+    // Mask words: key kl of this wave's 32 is one bit of the word of each query row.
+    const int mbit = mask_bit(kl);
+    using Mask = MaskStage<BQ, BKV, NT>;
+    auto Ml = [&](int i) { return mbits + i * Mask::kWords; };
 
     // K^T and V^T operands of S = Q K^T and dP = dO V^T: lane holds row `key`.
     const rsrc_t rk = make_rsrc(kb + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
@@ -283,13 +290,17 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     stage.init(p.sl, tid);
     RowStats<D, BQ, NT> stats;
     if constexpr (kSoft) stats.init(p.osl, tid);
+    Mask mstage;
+    if constexpr (MASKED) mstage.init(tid);
     auto load_tile = [&](int t) {
         stage.load(rows_rsrc(qb, t * BQ), rows_rsrc(dob, t * BQ));
         if constexpr (kSoft) stats.load(out_rows_rsrc(obase, t * BQ), lseb + t * BQ, n - t * BQ, tid);
+        if constexpr (MASKED) mstage.load(rmask, L, n, t * BQ, k0, tid);
     };
-    auto store_tile = [&](int i) {
+    auto store_tile = [&](int i, int t) {
         stage.store(Qs(i), dOs(i));
         if constexpr (kSoft) stats.store(stage.b, c0, Dl(i), Offl(i), tid);
+        if constexpr (MASKED) mstage.store(Ml(i), t * BQ, k0, n, tid);
     };
     // Query tile 0 is fetched before the block mask is read (see the forward
     // kernel); another first tile is fetched again.
@@ -300,7 +311,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     int qt = sched.next();
     if (qt > 0) load_tile(qt);
     int buf = 0;
-    store_tile(0);
+    store_tile(0, qt < 0 ? 0 : qt);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         if constexpr (!kSoft) kreg[ks] = scale8(kreg[ks], c1);
@@ -317,6 +328,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         const bf16 *dOc = dOs(buf);
         const float *Dc = Dl(buf);
         const float *Offc = Offl(buf);
+        const uint32_t *Mc = Ml(buf);
         // One straight-line body per tile kind.  MODE 0 (no element mask)
         // needs no per-element masking: padded query rows of Q and dO read as
         // zeros, so dP = 0 and dS = 0 there (softmax: their off is -inf, so
@@ -339,6 +351,13 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                     dq4[i] = *reinterpret_cast<const f32x4 *>(Dc + 8 * i + 4 * hh);
                 }
             }
+            // MODE 2: mask words of query rows 8 i + 4 hh + j (validity folded in).
+            uint4 mq[4];
+            if constexpr (MODE == 2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    mq[i] = *reinterpret_cast<const uint4 *>(Mc + w * 32 + 8 * i + 4 * hh);
+            }
             float pv[16], dsv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -348,10 +367,10 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                 else
                     pr = sigmoid_scaled(s[r], cexp);
                 if constexpr (MODE == 2) {
-                    const int qr = q0 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                    const bool ok = k_valid && qr < n &&
-                                    buffer_load_u8(rmask, qr * L + key) != 0;
-                    pr = keep_or_zero(pr, ok);
+                    const uint4 &m4 = mq[r >> 2];
+                    const uint32_t word = (r & 3) == 0 ? m4.x : (r & 3) == 1 ? m4.y
+                                        : (r & 3) == 2 ? m4.z : m4.w;
+                    pr = __uint_as_float(__float_as_uint(pr) & mask_select(word, mbit));
                 }
                 pv[r] = pr;
                 if constexpr (kSoft)
@@ -371,7 +390,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
             }
         };
         tile(std::integral_constant<int, MASKED ? 2 : 0>{});
-        if (nxt >= 0) store_tile(buf ^ 1);
+        if (nxt >= 0) store_tile(buf ^ 1, nxt);
         __syncthreads();
         buf ^= 1;
         qt = nxt;
@@ -388,7 +407,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
 // 32 KB rows x D each (two buffers of the K and V tiles).
 template <int D, int NW, int KB, int VARIANT, bool MASKED>
 __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int qt, int n,
-                                        bf16 *K0, bf16 *V0, bf16 *K1, bf16 *V1) {
+                                        bf16 *K0, bf16 *V0, bf16 *K1, bf16 *V1,
+                                        uint32_t *mbits) {
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
     constexpr bool kSoft = VARIANT != kSigmoid;
@@ -413,10 +433,10 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     const bool q_valid = qr < n;
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const bool has_mask = MASKED;
-    const rsrc_t rmask = make_rsrc(has_mask ? p.mask + (int64_t)b * L * L : nullptr,
-                                   has_mask ? (int64_t)L * L : 0);
-    const int mrow_off = qr * L;
+    const rsrc_t rmask = make_rsrc(MASKED ? p.mask + (int64_t)b * L * L : nullptr,
+                                   MASKED ? (int64_t)L * L : 0);
+    using Mask = MaskStage<BQ, BK, NT>;
+    uint32_t *M0 = mbits, *M1 = mbits + Mask::kWords;
 
     const rsrc_t rq = make_rsrc(qb + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
     const rsrc_t rdo = make_rsrc(dob + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
@@ -469,11 +489,18 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
         dma.issue(rows_rsrc(kb, t * BK), rows_rsrc(vb, t * BK), kd, vd);
     };
     fetch(0, K0, V0);
+    Mask mstage;
+    if constexpr (MASKED) mstage.init(tid);
     TileSchedule<BK> sched;
     sched.init(p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + q0 / p.block_q) * p.Tk : nullptr,
                1, n, p.block_k);
     int kt = sched.next();
     if (kt > 0) fetch(kt, K0, V0);
+    if constexpr (MASKED)
+        if (kt >= 0) {
+            mstage.load(rmask, L, n, q0, kt * BK, tid);
+            mstage.store(M0, q0, kt * BK, n, tid);
+        }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         if constexpr (!kSoft) qreg[ks] = scale8(qreg[ks], c1);
@@ -482,10 +509,12 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     // This tile's share of the sequence's fully padded query tiles.
     padded_share<BQ>(qt, n, L, zero_tile);
 
-    auto step = [&](const bf16 *Kc, const bf16 *Vc, bf16 *Kn, bf16 *Vn) {
-        const int k0 = kt * BK;
+    auto step = [&](const bf16 *Kc, const bf16 *Vc, const uint32_t *Mc, bf16 *Kn, bf16 *Vn,
+                    uint32_t *Mn) {
         const int nxt = sched.next();
         if (nxt >= 0) fetch(nxt, Kn, Vn);
+        if constexpr (MASKED)
+            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK, tid);
         // MODE 0 (no element mask): padded key rows of K and V read as zeros,
         // so dP = 0 and dS = 0 there; padded query rows are zeroed at the
         // store.  MODE 2: element mask.
@@ -500,7 +529,10 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                     dp = mfma32(row_operand<D>(Vc, kb2 * 32 + ql, ks * 16 + hh * 8), doreg[ks],
                                 dp);
                 }
-                // s[4i + j] = S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr]
+                // s[4i + j] = S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr]; in
+                // MODE 2 that key is bit 8 j + 2 i + hh of the row's mask word.
+                uint32_t mw = 0;
+                if constexpr (MODE == 2) mw = Mc[kb2 * BQ + w * 32 + ql] >> hh;
                 float dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -509,12 +541,9 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                         pr = __builtin_amdgcn_exp2f(fmaf(s[r], c1, off));
                     else
                         pr = sigmoid_scaled(s[r], cexp);
-                    if constexpr (MODE == 2) {
-                        const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                        const bool ok = q_valid && key < n &&
-                                        buffer_load_u8(rmask, mrow_off + key) != 0;
-                        pr = keep_or_zero(pr, ok);
-                    }
+                    if constexpr (MODE == 2)
+                        pr = __uint_as_float(__float_as_uint(pr) &
+                                             mask_select(mw, 8 * (r & 3) + 2 * (r >> 2)));
                     if constexpr (kSoft)
                         dsv[r] = pr * (dp[r] - drow);
                     else
@@ -531,14 +560,16 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
             }
         };
         tile(std::integral_constant<int, MASKED ? 2 : 0>{});
+        if constexpr (MASKED)
+            if (nxt >= 0) mstage.store(Mn, q0, nxt * BK, n, tid);
         wait_vm0();
         __syncthreads();
         kt = nxt;
     };
     while (kt >= 0) {
-        step(K0, V0, K1, V1);
+        step(K0, V0, M0, K1, V1, M1);
         if (kt < 0) break;
-        step(K1, V1, K0, V0);
+        step(K1, V1, M1, K0, V0, M0);
     }
     if (qr < L) store_rows_t<D>(dqb + (int64_t)qr * p.osl, dqt, p.scale, hh, q_valid);
 }
@@ -548,10 +579,11 @@ template <int D, int NW, int VARIANT, bool MASKED>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
+    __shared__ __attribute__((aligned(16))) uint32_t mbits[MASKED ? kMaskWords : 1];
     constexpr int BKV = 32 * NW;
     int b, h, kt, n;
     if (!tile_item<BKV>(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt, n)) return;
-    dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, kt, n, smem);
+    dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, kt, n, smem, mbits);
 }
 
 template <int D, int NW, int KB, int VARIANT, bool MASKED>
@@ -559,10 +591,11 @@ __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dq_kernel(const AttnParams p) {
     constexpr int kTile = 32 * KB * D;
     __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
+    __shared__ __attribute__((aligned(16))) uint32_t mbits[MASKED ? kMaskWords : 1];
     constexpr int BQ = 32 * NW;
     int b, h, qt, n;
     if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
-    dq_tile<D, NW, KB, VARIANT, MASKED>(p, b, h, qt, n, K0, V0, K1, V1);
+    dq_tile<D, NW, KB, VARIANT, MASKED>(p, b, h, qt, n, K0, V0, K1, V1, mbits);
 }
 
 // dK/dV and dQ in one launch: both kinds of tile of a (batch entry, head)
@@ -575,14 +608,15 @@ bwd_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
     constexpr int kTile = 32 * KB * D;
     __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
+    __shared__ __attribute__((aligned(16))) uint32_t mbits[MASKED ? kMaskWords : 1];
     constexpr int R = 32 * NW;
     const int nt = (p.L + R - 1) / R;
     int b, h, kind, t, n;
     if (!tile_item2<R, R>(p.seq_lens, p.B, p.H, p.L, nt, nt, b, h, kind, t, n)) return;
     if (kind == 0)
-        dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, t, n, smem);
+        dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, t, n, smem, mbits);
     else
-        dq_tile<D, NW, KB, VARIANT, MASKED>(p, b, h, t, n, K0, V0, K1, V1);
+        dq_tile<D, NW, KB, VARIANT, MASKED>(p, b, h, t, n, K0, V0, K1, V1, mbits);
 }
 
 // Waves per workgroup: 32 NW keys per dK/dV workgroup must divide block_k,

@@ -328,6 +328,11 @@ __device__ __forceinline__ float keep_or_neg_inf(float x, bool keep) {
     return keep ? x : -INFINITY;
 }
 
+// x where `keep` is all ones, -inf where it is zero (one bitfield insert).
+__device__ __forceinline__ float keep_bits_or_neg_inf(float x, uint32_t keep) {
+    return __uint_as_float((__float_as_uint(x) & keep) | (0xff800000u & ~keep));
+}
+
 __device__ __forceinline__ float bias_value(int mode, int n, int L) {
     if (mode == kBiasLogSeqlen) return -logf((float)n);
     if (mode == kBiasLogPadlen) return -logf((float)L);
@@ -340,5 +345,87 @@ __device__ __forceinline__ float bias_factor(int mode, int n, int L) {
     if (mode == kBiasLogPadlen) return (float)L;
     return 1.0f;
 }
+
+// ---------------------------------------------------------------------------
+// Element mask of one tile as bits.  Inside a tile that the binary block mask
+// keeps, the element mask still decides every (query, key) entry (Binary Block
+// Masking, "How it works").  Gathering those bytes lane by lane in the MFMA
+// layout costs one cache line per lane per byte; instead a workgroup reads the
+// tile's mask rows with coalesced 16-byte loads, one 32-key word per thread,
+// and leaves a bit per entry in LDS.
+//
+// Word (wi, r) of a tile with mask rows [r0, r0 + ROWS) and keys
+// [k0, k0 + KEYS) holds keys k0 + 32 wi + t of row r0 + r at bit
+// 8 (t % 4) + t / 4: the order in which a per-dword non-zero test of the 32
+// mask bytes delivers them.  Rows and keys at or past n are 0.  LDS layout:
+// words[wi * ROWS + r].  Mask rows are L bytes long and not aligned; the
+// 16-byte loads do not need to be.
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
+    return (((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;  // bit 7 of each byte
+}
+
+// Bit of key t (0..31) within a word.
+__device__ __forceinline__ constexpr int mask_bit(int t) { return 8 * (t & 3) + (t >> 2); }
+
+// All-ones (keep) or zero (drop) from bit `pos` of word.
+__device__ __forceinline__ uint32_t mask_select(uint32_t word, int pos) {
+    return (uint32_t)__builtin_amdgcn_sbfe((int)word, pos, 1);
+}
+
+template <int ROWS, int KEYS, int NT>
+struct MaskStage {
+    static constexpr int kWordsPerRow = KEYS / 32;
+    static constexpr int kWords = ROWS * kWordsPerRow;
+    static_assert(kWords <= NT, "at most one word per thread");
+    uint4 lo, hi;
+    int r, wi;
+
+    __device__ __forceinline__ bool active(int tid) const { return kWords == NT || tid < kWords; }
+
+    __device__ __forceinline__ void init(int tid) {
+        r = tid / kWordsPerRow;
+        wi = tid % kWordsPerRow;
+    }
+
+    // rmask covers exactly the batch entry's L x L mask; L * L fits in int.
+    // Words of rows or keys at or past n are not read (store clears them).
+    __device__ __forceinline__ void load(rsrc_t rmask, int L, int n, int r0, int k0, int tid) {
+        lo = hi = make_uint4(0u, 0u, 0u, 0u);
+        const int row = r0 + r, key = k0 + 32 * wi;
+        if (!active(tid) || row >= n || key >= n) return;
+        const int off = row * L + key;
+        if (off + 32 <= L * L) {
+            lo = buffer_load16(rmask, off);
+            hi = buffer_load16(rmask, off + 16);
+        } else {
+            // The last row's window runs past the end of the mask, where the
+            // range check would drop a 16-byte load whole: byte by byte, the
+            // bytes past the end reading 0.
+            uint32_t x[8] = {};
+#pragma unroll
+            for (int t = 0; t < 32; ++t)
+                x[t >> 2] |= (uint32_t)buffer_load_u8(rmask, off + t) << (8 * (t & 3));
+            lo = make_uint4(x[0], x[1], x[2], x[3]);
+            hi = make_uint4(x[4], x[5], x[6], x[7]);
+        }
+    }
+
+    __device__ __forceinline__ void store(uint32_t *words, int r0, int k0, int n, int tid) const {
+        if (!active(tid)) return;
+        uint32_t x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        if (k0 + KEYS > n) {  // keys at or past n: clear their bytes
+            const int m = n - k0 - 32 * wi;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int keep = min(max(m - 4 * j, 0), 4);
+                x[j] &= keep >= 4 ? 0xffffffffu : (1u << (8 * keep)) - 1u;
+            }
+        }
+        uint32_t bits = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bits |= nonzero_bytes(x[j]) >> (7 - j);
+        words[wi * ROWS + r] = r0 + r < n ? bits : 0u;
+    }
+};
 
 }  // namespace sigattn

@@ -87,6 +87,7 @@ fwd_kernel(const AttnParams p) {
     constexpr int KP = Pad<D>::K, VP = Pad<D>::V;
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][BK * KP];
     __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * VP];
+    __shared__ uint32_t Ms[2][MASKED ? BQ * BK / 32 : 1];  // element-mask bits per tile
 
     int b, h, qt, n;
     if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
@@ -119,10 +120,8 @@ fwd_kernel(const AttnParams p) {
     const int ql = lane & 31, hh = lane >> 5;
     const int qr = q0 + w * 32 + ql;  // this lane's query row
     const bool q_valid = qr < n;
-    const bool has_mask = MASKED;
-    const rsrc_t rmask = make_rsrc(has_mask ? p.mask + (int64_t)b * L * L : nullptr,
-                                   has_mask ? (int64_t)L * L : 0);
-    const int mrow_off = qr * L;
+    const rsrc_t rmask = make_rsrc(MASKED ? p.mask + (int64_t)b * L * L : nullptr,
+                                   MASKED ? (int64_t)L * L : 0);
     // Per-lane offsets of the transposing V reads (see lds_read_tr4).
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -164,12 +163,18 @@ fwd_kernel(const AttnParams p) {
     KVStage<D, BK, NT> stage;
     stage.init(p.sl, tid);
     stage.load(rows_rsrc(kb, 0), rows_rsrc(vb, 0));
+    MaskStage<BQ, BK, NT> mstage;
+    if constexpr (MASKED) mstage.init(tid);
     TileSchedule<BK> sched;
     sched.init(bm_row, 1, n, p.block_k);
     int kt = sched.next();
     if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
+    if constexpr (MASKED)
+        if (kt >= 0) mstage.load(rmask, L, n, q0, kt * BK, tid);
     int buf = 0;
     stage.store(Ks[0], Vs[0]);
+    if constexpr (MASKED)
+        if (kt >= 0) mstage.store(Ms[0], q0, kt * BK, n, tid);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         if constexpr (VARIANT == kSigmoid) qreg[ks] = scale8(qreg[ks], c1);
@@ -182,6 +187,8 @@ fwd_kernel(const AttnParams p) {
         const int k0 = kt * BK;
         const int nxt = sched.next();
         if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
+        if constexpr (MASKED)
+            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK, tid);
         const bf16 *Kc = Ks[buf];
         const bf16 *Vc = Vs[buf];
 
@@ -208,20 +215,27 @@ fwd_kernel(const AttnParams p) {
                     sacc[kb2] = mfma32(a, qreg[ks], sacc[kb2]);
                 }
             }
-            // Per-element validity (MODE 1, 2), computed without branches.
+            // Per-element validity.  MODE 1: compared, without branches.
+            // MODE 2: the tile's mask bits (validity folded in); key
+            // 8 i + 4 hh + j of a 32-key block is bit 8 j + 2 i + hh.
             bool ok[KB][16];
-            if constexpr (MODE != 0) {
+            uint32_t mw[KB];
+            if constexpr (MODE == 1) {
 #pragma unroll
                 for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
                         ok[kb2][r] = q_valid && key < n;
-                        if constexpr (MODE == 2)
-                            ok[kb2][r] = ok[kb2][r] &&
-                                         buffer_load_u8(rmask, mrow_off + key) != 0;
                     }
             }
+            if constexpr (MODE == 2) {
+#pragma unroll
+                for (int kb2 = 0; kb2 < KB; ++kb2) mw[kb2] = Ms[buf][kb2 * BQ + w * 32 + ql] >> hh;
+            }
+            auto keep = [&](int kb2, int r) {
+                return mask_select(mw[kb2], 8 * (r & 3) + 2 * (r >> 2));
+            };
 
             float m_use = 0.0f;
             if constexpr (VARIANT != kSigmoid) {
@@ -233,7 +247,8 @@ fwd_kernel(const AttnParams p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float t = fmaf(sacc[kb2][r], c1, c0);
-                        if constexpr (MODE != 0) t = keep_or_neg_inf(t, ok[kb2][r]);
+                        if constexpr (MODE == 1) t = keep_or_neg_inf(t, ok[kb2][r]);
+                        if constexpr (MODE == 2) t = keep_bits_or_neg_inf(t, keep(kb2, r));
                         sacc[kb2][r] = t;
                         tmax = fmaxf(tmax, t);
                     }
@@ -255,7 +270,8 @@ fwd_kernel(const AttnParams p) {
                 for (int r = 0; r < 16; ++r) {
                     if constexpr (VARIANT == kSigmoid) {
                         pv[r] = sigmoid_scaled(sacc[kb2][r], cexp);
-                        if constexpr (MODE == 2) pv[r] = keep_or_zero(pv[r], ok[kb2][r]);
+                        if constexpr (MODE == 2)
+                            pv[r] = __uint_as_float(__float_as_uint(pv[r]) & keep(kb2, r));
                     } else {
                         pv[r] = __builtin_amdgcn_exp2f(sacc[kb2][r] - m_use);
                         l_run += pv[r];
@@ -277,6 +293,8 @@ fwd_kernel(const AttnParams p) {
         tile(std::integral_constant<int, MASKED ? 2 : (VARIANT == kSigmoid ? 0 : 1)>{});
 
         if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
+        if constexpr (MASKED)
+            if (nxt >= 0) mstage.store(Ms[buf ^ 1], q0, nxt * BK, n, tid);
         __syncthreads();
         buf ^= 1;
         kt = nxt;
