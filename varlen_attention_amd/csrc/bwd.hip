@@ -211,11 +211,17 @@ template <int D> constexpr int kDkdvLds = 2 * 2 * 32 * D + 2 * 2 * 32 * 2;
 // Element-mask bits of two tiles (MaskStage words), for either kind of work.
 constexpr int kMaskWords = 2 * 256;
 
+// At d = 128 the V rows of a wave's keys wait in LDS (32 x D elements per
+// wave) rather than in registers: the dK and dV accumulators and the K rows
+// leave too few registers for the tile loop otherwise.
+template <int D> constexpr bool kVInLds = D == 128;
+
 // dK and dV of key tile kt (32 NW keys) of (batch entry b, head h); smem
-// holds kDkdvLds<D> elements, mbits kMaskWords words (element mask only).
+// holds kDkdvLds<D> elements, mbits kMaskWords words (element mask only),
+// vt this wave's 32 x D elements when kVInLds<D>.
 template <int D, int NW, int VARIANT, bool MASKED>
 __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int kt, int n,
-                                          bf16 *smem, uint32_t *mbits) {
+                                          bf16 *smem, uint32_t *mbits, bf16 *vt) {
     constexpr int BKV = 32 * NW, BQ = 32, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
     constexpr bool kSoft = VARIANT != kSigmoid;
@@ -256,19 +262,33 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                                    MASKED ? (int64_t)L * L : 0);
     // Mask words: key kl of this wave's 32 is one bit of the word of each query row.
     const int mbit = mask_bit(kl);
-    using Mask = MaskStage<BQ, BKV, NT>;
+    using Mask = MaskStage<BQ, BKV, NT, false>;
+    int mcls = kMixed;  // this wave's 32 x 32 entries of the current tile
     auto Ml = [&](int i) { return mbits + i * Mask::kWords; };
 
     // K^T and V^T operands of S = Q K^T and dP = dO V^T: lane holds row `key`.
     const rsrc_t rk = make_rsrc(kb + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
     const rsrc_t rv = make_rsrc(vb + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
-    bf16x8 kreg[KS], vreg[KS];
+    constexpr bool kVLds = kVInLds<D>;
+    bf16x8 kreg[KS], vreg[kVLds ? 1 : KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const int off = (int)(((int64_t)(w * 32 + kl) * p.sl + ks * 16 + hh * 8) * 2);
         kreg[ks] = as_bf16x8(buffer_load16(rk, off));
-        vreg[ks] = as_bf16x8(buffer_load16(rv, off));
+        const uint4 v8 = buffer_load16(rv, off);
+        // Each lane reads back only the 16 bytes it wrote (swizzled like the
+        // Q tile, so the reads spread over the banks).
+        if constexpr (kVLds)
+            *reinterpret_cast<uint4 *>(vt + swz_off<D>(kl, ks * 16 + hh * 8)) = v8;
+        else
+            vreg[ks] = as_bf16x8(v8);
     }
+    auto v_operand = [&](int ks) {
+        if constexpr (kVLds)
+            return row_operand<D>(vt, kl, ks * 16 + hh * 8);
+        else
+            return vreg[ks];
+    };
     // SIGMOID: K is scaled by c1 before the loop, so the S accumulator is
     // u = -scale * s * log2 e (see sigmoid_scaled).  Softmax: the weight is
     // exp2(s * c1 + off) with c1 = scale * log2 e and off from RowStats.
@@ -295,12 +315,12 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     auto load_tile = [&](int t) {
         stage.load(rows_rsrc(qb, t * BQ), rows_rsrc(dob, t * BQ));
         if constexpr (kSoft) stats.load(out_rows_rsrc(obase, t * BQ), lseb + t * BQ, n - t * BQ, tid);
-        if constexpr (MASKED) mstage.load(rmask, L, n, t * BQ, k0, tid);
+        if constexpr (MASKED) mstage.load(rmask, L, n, t * BQ, k0);
     };
     auto store_tile = [&](int i, int t) {
         stage.store(Qs(i), dOs(i));
         if constexpr (kSoft) stats.store(stage.b, c0, Dl(i), Offl(i), tid);
-        if constexpr (MASKED) mstage.store(Ml(i), t * BQ, k0, n, tid);
+        if constexpr (MASKED) mcls = mstage.store(Ml(i), t * BQ, k0, n);
     };
     // Query tile 0 is fetched before the block mask is read (see the forward
     // kernel); another first tile is fetched again.
@@ -340,7 +360,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 s = mfma32(row_operand<D>(Qc, kl, ks * 16 + hh * 8), kreg[ks], s);
-                dp = mfma32(row_operand<D>(dOc, kl, ks * 16 + hh * 8), vreg[ks], dp);
+                dp = mfma32(row_operand<D>(dOc, kl, ks * 16 + hh * 8), v_operand(ks), dp);
             }
             // s[4i + j] = S[query q0 + 8 i + 4 hh + j][key]
             f32x4 offq[4], dq4[4];
@@ -389,7 +409,13 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                 }
             }
         };
-        tile(std::integral_constant<int, MASKED ? 2 : 0>{});
+        if constexpr (MASKED) {
+            // This wave's 32 x 32 entries, as found when it staged them: none
+            // kept means no work.
+            if (mcls != kSkip) tile(std::integral_constant<int, 2>{});
+        } else {
+            tile(std::integral_constant<int, 0>{});
+        }
         if (nxt >= 0) store_tile(buf ^ 1, nxt);
         __syncthreads();
         buf ^= 1;
@@ -435,7 +461,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const rsrc_t rmask = make_rsrc(MASKED ? p.mask + (int64_t)b * L * L : nullptr,
                                    MASKED ? (int64_t)L * L : 0);
-    using Mask = MaskStage<BQ, BK, NT>;
+    using Mask = MaskStage<BQ, BK, NT, true>;
+    int mcls = kMixed;  // this wave's share of the current tile
     uint32_t *M0 = mbits, *M1 = mbits + Mask::kWords;
 
     const rsrc_t rq = make_rsrc(qb + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
@@ -498,8 +525,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     if (kt > 0) fetch(kt, K0, V0);
     if constexpr (MASKED)
         if (kt >= 0) {
-            mstage.load(rmask, L, n, q0, kt * BK, tid);
-            mstage.store(M0, q0, kt * BK, n, tid);
+            mstage.load(rmask, L, n, q0, kt * BK);
+            mcls = mstage.store(M0, q0, kt * BK, n);
         }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -514,7 +541,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
         const int nxt = sched.next();
         if (nxt >= 0) fetch(nxt, Kn, Vn);
         if constexpr (MASKED)
-            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK, tid);
+            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK);
         // MODE 0 (no element mask): padded key rows of K and V read as zeros,
         // so dP = 0 and dS = 0 there; padded query rows are zeroed at the
         // store.  MODE 2: element mask.
@@ -531,8 +558,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                 }
                 // s[4i + j] = S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr]; in
                 // MODE 2 that key is bit 8 j + 2 i + hh of the row's mask word.
-                uint32_t mw = 0;
-                if constexpr (MODE == 2) mw = Mc[kb2 * BQ + w * 32 + ql] >> hh;
+                uint32_t mwk = 0u;
+                if constexpr (MODE == 2) mwk = Mc[kb2 * BQ + w * 32 + ql] >> hh;
                 float dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -543,7 +570,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                         pr = sigmoid_scaled(s[r], cexp);
                     if constexpr (MODE == 2)
                         pr = __uint_as_float(__float_as_uint(pr) &
-                                             mask_select(mw, 8 * (r & 3) + 2 * (r >> 2)));
+                                             mask_select(mwk, 8 * (r & 3) + 2 * (r >> 2)));
                     if constexpr (kSoft)
                         dsv[r] = pr * (dp[r] - drow);
                     else
@@ -559,9 +586,15 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                 }
             }
         };
-        tile(std::integral_constant<int, MASKED ? 2 : 0>{});
+        if constexpr (MASKED) {
+            // The wave's entries of this tile, as found when it staged them:
+            // none kept means no work.
+            if (mcls != kSkip) tile(std::integral_constant<int, 2>{});
+        } else {
+            tile(std::integral_constant<int, 0>{});
+        }
         if constexpr (MASKED)
-            if (nxt >= 0) mstage.store(Mn, q0, nxt * BK, n, tid);
+            if (nxt >= 0) mcls = mstage.store(Mn, q0, nxt * BK, n);
         wait_vm0();
         __syncthreads();
         kt = nxt;
@@ -580,10 +613,12 @@ __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
     __shared__ __attribute__((aligned(16))) uint32_t mbits[MASKED ? kMaskWords : 1];
+    __shared__ __attribute__((aligned(16))) bf16 vts[kVInLds<D> ? NW * 32 * D : 1];
     constexpr int BKV = 32 * NW;
     int b, h, kt, n;
     if (!tile_item<BKV>(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt, n)) return;
-    dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, kt, n, smem, mbits);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, kt, n, smem, mbits, vts + w * 32 * D);
 }
 
 template <int D, int NW, int KB, int VARIANT, bool MASKED>
@@ -613,8 +648,14 @@ bwd_kernel(const AttnParams p) {
     const int nt = (p.L + R - 1) / R;
     int b, h, kind, t, n;
     if (!tile_item2<R, R>(p.seq_lens, p.B, p.H, p.L, nt, nt, b, h, kind, t, n)) return;
-    if (kind == 0)
-        dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, t, n, smem, mbits);
+    if (kind == 0) {
+        // A workgroup does one kind of work: the dQ key buffers, each 32 KB
+        // rows x D, hold the dK/dV waves' V rows (32 rows each when KB = 1).
+        static_assert(!kVInLds<D> || (KB == 1 && NW <= 4), "V rows need one dQ buffer per wave");
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        bf16 *vt = w == 0 ? K0 : w == 1 ? V0 : w == 2 ? K1 : V1;
+        dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, t, n, smem, mbits, vt);
+    }
     else
         dq_tile<D, NW, KB, VARIANT, MASKED>(p, b, h, t, n, K0, V0, K1, V1, mbits);
 }

@@ -372,27 +372,45 @@ __device__ __forceinline__ uint32_t mask_select(uint32_t word, int pos) {
     return (uint32_t)__builtin_amdgcn_sbfe((int)word, pos, 1);
 }
 
-template <int ROWS, int KEYS, int NT>
+// What a wave's share of a masked tile needs, from the OR and the AND of the
+// mask words its lanes hold: kSkip (no entry kept: no work at all), kDense
+// (every entry kept) or kMixed.
+enum { kSkip = 0, kDense = 1, kMixed = 2 };
+__device__ __forceinline__ int mask_class(uint32_t any_bits, uint32_t all_bits) {
+    if (__ballot(any_bits != 0u) == 0) return kSkip;
+    if (__ballot(all_bits != 0xffffffffu) == 0) return kDense;
+    return kMixed;
+}
+
+template <int ROWS, int KEYS, int NT, bool WAVE_ROWS>
 struct MaskStage {
+    // Wave w stages the words it reads itself: with WAVE_ROWS, every word of
+    // rows 32 w .. 32 w + 31 (the waves split the query rows); otherwise word
+    // w of all 32 rows (the waves split the keys).  So the wave learns what
+    // its next tile needs (mask_class) while it stages it.
     static constexpr int kWordsPerRow = KEYS / 32;
     static constexpr int kWords = ROWS * kWordsPerRow;
-    static_assert(kWords <= NT, "at most one word per thread");
+    static constexpr int kWordsPerWave = WAVE_ROWS ? kWordsPerRow : 1;
+    static_assert(kWordsPerWave <= 2, "at most one word per lane");
+    static_assert(WAVE_ROWS ? ROWS == NT / 2 : (ROWS == 32 && kWordsPerRow == NT / 64),
+                  "one wave per 32 rows, or per 32 keys");
     uint4 lo, hi;
     int r, wi;
-
-    __device__ __forceinline__ bool active(int tid) const { return kWords == NT || tid < kWords; }
+    bool act;
 
     __device__ __forceinline__ void init(int tid) {
-        r = tid / kWordsPerRow;
-        wi = tid % kWordsPerRow;
+        const int lane = tid & 63, w = tid >> 6;
+        r = (WAVE_ROWS ? 32 * w : 0) + (lane & 31);
+        wi = (WAVE_ROWS ? 0 : w) + (lane >> 5);
+        act = (lane >> 5) < kWordsPerWave;
     }
 
     // rmask covers exactly the batch entry's L x L mask; L * L fits in int.
     // Words of rows or keys at or past n are not read (store clears them).
-    __device__ __forceinline__ void load(rsrc_t rmask, int L, int n, int r0, int k0, int tid) {
+    __device__ __forceinline__ void load(rsrc_t rmask, int L, int n, int r0, int k0) {
         lo = hi = make_uint4(0u, 0u, 0u, 0u);
         const int row = r0 + r, key = k0 + 32 * wi;
-        if (!active(tid) || row >= n || key >= n) return;
+        if (!act || row >= n || key >= n) return;
         const int off = row * L + key;
         if (off + 32 <= L * L) {
             lo = buffer_load16(rmask, off);
@@ -410,8 +428,9 @@ struct MaskStage {
         }
     }
 
-    __device__ __forceinline__ void store(uint32_t *words, int r0, int k0, int n, int tid) const {
-        if (!active(tid)) return;
+    // Writes the bits and returns this wave's class for the tile (all lanes
+    // of the wave call it).
+    __device__ __forceinline__ int store(uint32_t *words, int r0, int k0, int n) const {
         uint32_t x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         if (k0 + KEYS > n) {  // keys at or past n: clear their bytes
             const int m = n - k0 - 32 * wi;
@@ -424,7 +443,9 @@ struct MaskStage {
         uint32_t bits = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) bits |= nonzero_bytes(x[j]) >> (7 - j);
-        words[wi * ROWS + r] = r0 + r < n ? bits : 0u;
+        if (r0 + r >= n) bits = 0u;
+        if (act) words[wi * ROWS + r] = bits;
+        return mask_class(bits, act ? bits : 0xffffffffu);
     }
 };
 

@@ -163,18 +163,19 @@ fwd_kernel(const AttnParams p) {
     KVStage<D, BK, NT> stage;
     stage.init(p.sl, tid);
     stage.load(rows_rsrc(kb, 0), rows_rsrc(vb, 0));
-    MaskStage<BQ, BK, NT> mstage;
+    MaskStage<BQ, BK, NT, true> mstage;
+    int mcls = kMixed;  // this wave's share of the current tile (element mask)
     if constexpr (MASKED) mstage.init(tid);
     TileSchedule<BK> sched;
     sched.init(bm_row, 1, n, p.block_k);
     int kt = sched.next();
     if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
     if constexpr (MASKED)
-        if (kt >= 0) mstage.load(rmask, L, n, q0, kt * BK, tid);
+        if (kt >= 0) mstage.load(rmask, L, n, q0, kt * BK);
     int buf = 0;
     stage.store(Ks[0], Vs[0]);
     if constexpr (MASKED)
-        if (kt >= 0) mstage.store(Ms[0], q0, kt * BK, n, tid);
+        if (kt >= 0) mcls = mstage.store(Ms[0], q0, kt * BK, n);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         if constexpr (VARIANT == kSigmoid) qreg[ks] = scale8(qreg[ks], c1);
@@ -188,7 +189,7 @@ fwd_kernel(const AttnParams p) {
         const int nxt = sched.next();
         if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
         if constexpr (MASKED)
-            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK, tid);
+            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK);
         const bf16 *Kc = Ks[buf];
         const bf16 *Vc = Vs[buf];
 
@@ -219,7 +220,6 @@ fwd_kernel(const AttnParams p) {
             // MODE 2: the tile's mask bits (validity folded in); key
             // 8 i + 4 hh + j of a 32-key block is bit 8 j + 2 i + hh.
             bool ok[KB][16];
-            uint32_t mw[KB];
             if constexpr (MODE == 1) {
 #pragma unroll
                 for (int kb2 = 0; kb2 < KB; ++kb2)
@@ -229,6 +229,7 @@ fwd_kernel(const AttnParams p) {
                         ok[kb2][r] = q_valid && key < n;
                     }
             }
+            uint32_t mw[KB];  // this lane's row of the tile's mask words
             if constexpr (MODE == 2) {
 #pragma unroll
                 for (int kb2 = 0; kb2 < KB; ++kb2) mw[kb2] = Ms[buf][kb2 * BQ + w * 32 + ql] >> hh;
@@ -290,11 +291,19 @@ fwd_kernel(const AttnParams p) {
                 }
             }
         };
-        tile(std::integral_constant<int, MASKED ? 2 : (VARIANT == kSigmoid ? 0 : 1)>{});
+        if constexpr (MASKED) {
+            // The wave's rows of this tile, as found when it staged them:
+            // nothing kept means no work.  (A second, unmasked copy of the
+            // body for tiles whose entries are all kept measured slower: it
+            // costs registers and the masked body's extra work is small.)
+            if (mcls != kSkip) tile(std::integral_constant<int, 2>{});
+        } else {
+            tile(std::integral_constant<int, VARIANT == kSigmoid ? 0 : 1>{});
+        }
 
         if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
         if constexpr (MASKED)
-            if (nxt >= 0) mstage.store(Ms[buf ^ 1], q0, nxt * BK, n, tid);
+            if (nxt >= 0) mcls = mstage.store(Ms[buf ^ 1], q0, nxt * BK, n);
         __syncthreads();
         buf ^= 1;
         kt = nxt;
