@@ -94,10 +94,15 @@ typedef struct {
  *   mask        [device] uint8 [B, L, L] row-major, non-zero = may attend;
  *               NULL for padding-only batches.  Must be 16-byte aligned.
  *   block_mask  [device] uint8 [B, Tq, Tk] output, Tq = ceil(L / block_q),
- *               Tk = ceil(L / block_k); every entry is written with 0 or 1.
- * Entry (b, i, j) is 1 iff some r in [i*block_q, min((i+1)*block_q, L)) and c
- * in [j*block_k, min((j+1)*block_k, L)) is valid (definition above without
- * the block-mask term).  With mask == NULL this is i*block_q < n && j*block_k < n.
+ *               Tk = ceil(L / block_k); every entry is written with 0, 1 or 3.
+ * Bit 0 of entry (b, i, j) is the binary block matrix: 1 iff some r in
+ * [i*block_q, min((i+1)*block_q, L)) and c in [j*block_k, min((j+1)*block_k, L))
+ * is valid (definition above without the block-mask term).  Bit 1 marks a full
+ * tile (the same page: runs of non-zero blocks need fewer checks): the whole
+ * block_q x block_k tile lies inside [0, n) x [0, n) and every element of it
+ * is valid; the attention kernels then read no element mask for it.  With
+ * mask == NULL bit 0 is i*block_q < n && j*block_k < n and bit 1 is
+ * (i+1)*block_q <= n && (j+1)*block_k <= n.
  * Errors: INVALID_ARG (null seq_lens/block_mask, B or L <= 0), UNSUPPORTED
  * (block size not 32/64/128), ALIGNMENT (mask not 16-byte aligned), LAUNCH.
  */
@@ -114,7 +119,9 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, int32_t B, int
  *   seq_lens    [device] int32 [B]
  *   block_mask  [device] uint8 [B, Tq, Tk] from blockmask_build with the same
  *               block sizes, or NULL: tiles are then chosen from seq_lens
- *               alone.  Required when mask != NULL.
+ *               alone.  Required when mask != NULL.  Tiles with a zero entry
+ *               are skipped; bit 1 set promises a full tile (see
+ *               blockmask_build), so a caller's own 0/1 matrix is also valid.
  *   mask        [device] uint8 [B, L, L] or NULL (element mask, all heads;
  *               non-zero = may attend; rows need no alignment); with a mask,
  *               L <= SIGATTN_MAX_MASKED_L (else UNSUPPORTED)

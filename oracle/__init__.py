@@ -96,7 +96,9 @@ def default_scale(d: int) -> float:
 
 
 def blockmask(seq_lens, mask, L: int, block_q: int, block_k: int) -> np.ndarray:
-    """Binary block matrix [B, Tq, Tk] (uint8, 0/1); see oracle_blockmask."""
+    """Block matrix [B, Tq, Tk] (uint8): bit 0 the binary block mask (tile holds
+    a valid element), bit 1 a full tile (inside [0, n)^2, every element valid);
+    see oracle_blockmask."""
     lib = _load()
     n = np.ascontiguousarray(seq_lens, dtype=np.int32)
     B = n.shape[0]

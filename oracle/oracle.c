@@ -85,9 +85,13 @@ static real sigmoid(real x) { return (real)1 / ((real)1 + exp(-x)); }
 #ifdef ORACLE_WITH_BLOCKMASK
 /*
  * Binary block mask ("Binary Block Masking", "Presentation" and "How it
- * works"): entry (b, i, j) is 1 when the tile rows [i*bq, min((i+1)*bq, L))
- * x columns [j*bk, min((j+1)*bk, L)) hold at least one valid element.
- * One matrix per batch entry, shared by every head.
+ * works"): bit 0 of entry (b, i, j) is 1 when the tile rows
+ * [i*bq, min((i+1)*bq, L)) x columns [j*bk, min((j+1)*bk, L)) hold at least
+ * one valid element.  One matrix per batch entry, shared by every head.
+ * Bit 1 marks a full tile (the same page's point that runs of non-zero blocks
+ * need fewer checks, read as: a tile with every element valid needs no
+ * per-element mask): the whole bq x bk tile lies inside [0, n) x [0, n) and
+ * every element of it is valid.  Entries are therefore 0, 1 or 3.
  * seq_lens [B]; mask [B, L, L] or NULL; out [B, Tq, Tk].
  */
 void oracle_blockmask(const int32_t *seq_lens, const uint8_t *mask, int B, int L, int bq, int bk,
@@ -99,10 +103,15 @@ void oracle_blockmask(const int32_t *seq_lens, const uint8_t *mask, int B, int L
         for (int i = 0; i < Tq; ++i)
             for (int j = 0; j < Tk; ++j) {
                 int any = 0;
-                for (int r = i * bq; r < (i + 1) * bq && r < L && !any; ++r)
-                    for (int c = j * bk; c < (j + 1) * bk && c < L; ++c)
-                        if (valid(r, c, n, mb, L)) { any = 1; break; }
-                out[((size_t)b * Tq + i) * Tk + j] = (uint8_t)any;
+                int all = (i + 1) * bq <= n && (j + 1) * bk <= n;
+                for (int r = i * bq; r < (i + 1) * bq && r < L; ++r)
+                    for (int c = j * bk; c < (j + 1) * bk && c < L; ++c) {
+                        if (valid(r, c, n, mb, L))
+                            any = 1;
+                        else
+                            all = 0;
+                    }
+                out[((size_t)b * Tq + i) * Tk + j] = (uint8_t)(any | (all << 1));
             }
     }
 }

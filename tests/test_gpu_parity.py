@@ -67,7 +67,8 @@ def test_blockmask_long_documents_full_size(va):
               to_gpu(w.mask, torch.uint8)).cpu().numpy()
     want = oracle.blockmask(w.seq_lens, w.mask, w.L, 128, 128)
     np.testing.assert_array_equal(got, want)
-    assert int(want.sum()) == 885
+    assert int((want & 1).sum()) == 885  # kept tiles (seed-0 draw)
+    assert int((want >> 1).sum()) == 318  # of which full
 
 
 # --------------------------------------------------------------- forward, small
@@ -236,6 +237,44 @@ def test_mask_end_of_batch_entry(va, d, L, bq, bk):
     assert_rows(gpu_f64(dq), wq, n, "dQ")
     assert_rows(gpu_f64(dk), wk, n, "dK")
     assert_rows(gpu_f64(dv), wv, n, "dV")
+
+
+@pytest.mark.parametrize("d,L,bq,bk,variant", [(64, 300, 64, 64, SIGMOID), (128, 330, 128, 128, SIGMOID),
+                                                 (64, 257, 128, 64, SOFTMAX), (128, 200, 64, 128, SOFTMAX1)])
+def test_causal_mask_full_tiles(va, d, L, bq, bk, variant):
+    """A causal mask has full tiles (bit 1 of the block mask) below the
+    diagonal: forward and backward against the oracle, and bit-identical to
+    the same call with the full bits cleared (every tile then reads its mask)."""
+    B, H = 3, 2
+    n = np.array([L, L - 29, bq + 3], np.int32)
+    q, k, v, do = _inputs(5000 + d + L + variant, B, H, L, d, n, names="qkvd")
+    idx = np.arange(L)
+    mask = np.broadcast_to((idx[None, :] <= idx[:, None]).astype(np.uint8), (B, L, L)).copy()
+    say(f"causal full tiles d={d} L={L} bq={bq} bk={bk} variant={variant}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = to_gpu(mask, torch.uint8)
+    bm = _bm(va, n_gpu, L, bq, bk, m_gpu)
+    np.testing.assert_array_equal(bm.cpu().numpy(), oracle.blockmask(n, mask, L, bq, bk))
+    assert (bm == 3).any()
+    bm01 = bm & 1
+    bias = 1 if variant == SIGMOID else 0
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    outs = []
+    for blk in (bm, bm01):
+        o, lse = va.sigattn_fwd(*g[:3], n_gpu, block_mask=blk, mask=m_gpu, bias=bias,
+                                variant=variant, block_q=bq, block_k=bk, return_lse=True)
+        grads = va.sigattn_bwd(*g, n_gpu, block_mask=blk, mask=m_gpu, bias=bias, variant=variant,
+                               block_q=bq, block_k=bk, o=o if variant else None,
+                               lse=lse if variant else None)
+        outs.append((o,) + tuple(grads))
+    torch.cuda.synchronize()
+    for a, b_ in zip(*outs):
+        assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
+    want, _ = oracle.fwd(q, k, v, n, mask=mask, bias=bias, variant=variant)
+    assert_rows(gpu_f64(outs[0][0]), want, n, "O")
+    wq, wk, wv = oracle.bwd(q, k, v, do, n, mask=mask, bias=bias, variant=variant)
+    for name, got_t, ref in zip(("dQ", "dK", "dV"), outs[0][1:], (wq, wk, wv)):
+        assert_rows(gpu_f64(got_t), ref, n, name)
 
 
 # --------------------------------------------------------------- forward, full size

@@ -1,13 +1,16 @@
 // Binary block mask builder (Binary Block Masking, "Presentation" and "How it
-// works"): entry (b, i, j) is 1 when query tile i x key tile j of batch entry b
-// holds at least one valid element.  One matrix per batch entry, shared by
-// every head and layer.
+// works"): bit 0 of entry (b, i, j) is 1 when query tile i x key tile j of
+// batch entry b holds at least one valid element; bit 1 marks a full tile (the
+// whole tile inside [0, n) x [0, n) with every element valid), where the
+// attention kernels need no element mask.  One matrix per batch entry, shared
+// by every head and layer.
 //
-// Padding-only batches use the closed form (i*bq < n) && (j*bk < n), one thread
-// per entry.  With an element mask the builder is one HBM scan of the valid
-// rectangle [0, n) x [0, n) of each mask: a workgroup owns a band of bq rows
-// and a group of key tiles, so it writes its outputs alone (no atomics to
-// global memory), and each wave walks one row at a time with 16-byte loads.
+// Padding-only batches use the closed form (i*bq < n) && (j*bk < n), and
+// ((i+1)*bq <= n) && ((j+1)*bk <= n) for full tiles, one thread per entry.
+// With an element mask the builder is one HBM scan of the valid rectangle
+// [0, n) x [0, n) of each mask: a workgroup owns a band of bq rows and a group
+// of key tiles, so it writes its outputs alone (no atomics to global memory),
+// and each wave walks one row at a time with 16-byte loads.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -23,7 +26,9 @@ blockmask_padding_kernel(const int32_t *__restrict__ seq_lens, int B, int L, int
     int i = (int)((idx / Tk) % Tq);
     int b = (int)(idx / ((int64_t)Tq * Tk));
     int n = clamp_len(seq_lens[b], L);
-    out[idx] = (uint8_t)((i * bq < n) && (j * bk < n));
+    const bool any = (i * bq < n) && (j * bk < n);
+    const bool full = ((i + 1) * bq <= n) && ((j + 1) * bk <= n);
+    out[idx] = (uint8_t)(any | (full << 1));
 }
 
 // Grid: (Tq * groups, B); 256 threads.  tiles_per_group * bk <= 1024 columns,
@@ -32,7 +37,7 @@ __global__ void __launch_bounds__(256)
 blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict__ mask,
                       int L, int bq, int bk_shift, int Tq, int Tk, int tiles_per_group,
                       int groups, uint8_t *__restrict__ out) {
-    __shared__ uint32_t flags;
+    __shared__ uint32_t flags, zeros;  // per key tile: a valid element seen / an invalid one
     const int b = blockIdx.y;
     const int i = blockIdx.x / groups;
     const int g = blockIdx.x % groups;
@@ -41,12 +46,12 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
     const int n = clamp_len(seq_lens[b], L);
     const int r_lo = i * bq, r_hi = min(min(r_lo + bq, L), n);
     const int c_lo = j0 << bk_shift, c_hi = min(j1 << bk_shift, n);
-    if (threadIdx.x == 0) flags = 0u;
+    if (threadIdx.x == 0) flags = zeros = 0u;
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint64_t total = (uint64_t)gridDim.y * (uint64_t)L * (uint64_t)L;
-    uint32_t bits = 0;
+    uint32_t bits = 0, zbits = 0;
     if (r_lo < r_hi && c_lo < c_hi) {
         for (int r = r_lo + wave; r < r_hi; r += 4) {
             const uint64_t row = ((uint64_t)b * L + r) * (uint64_t)L;
@@ -55,7 +60,14 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
                 uint8_t bytes[16];
                 if (a + 16 <= total) {
                     uint4 u = *reinterpret_cast<const uint4 *>(mask + a);
-                    if ((u.x | u.y | u.z | u.w) == 0u) continue;
+                    if ((u.x | u.y | u.z | u.w) == 0u) {
+                        // All sixteen invalid: the (at most two) tiles of the
+                        // in-range bytes are not full.
+                        const int c0 = (int)((a > lo ? a : lo) - row);
+                        const int c1 = (int)((a + 16 < hi ? a + 16 : hi) - row) - 1;
+                        zbits |= (1u << ((c0 >> bk_shift) - j0)) | (1u << ((c1 >> bk_shift) - j0));
+                        continue;
+                    }
                     *reinterpret_cast<uint4 *>(bytes) = u;
                 } else {
                     for (int t = 0; t < 16; ++t) bytes[t] = (a + t < total) ? mask[a + t] : 0;
@@ -63,18 +75,29 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
                     const uint64_t p = a + t;
-                    if (bytes[t] != 0 && p >= lo && p < hi) {
+                    if (p >= lo && p < hi) {
                         const int c = (int)(p - row);
-                        bits |= 1u << ((c >> bk_shift) - j0);
+                        const uint32_t f = 1u << ((c >> bk_shift) - j0);
+                        if (bytes[t] != 0)
+                            bits |= f;
+                        else
+                            zbits |= f;
                     }
                 }
             }
         }
     }
     if (bits) atomicOr(&flags, bits);
+    if (zbits) atomicOr(&zeros, zbits);
     __syncthreads();
     const int t = threadIdx.x;
-    if (t < j1 - j0) out[((int64_t)b * Tq + i) * Tk + j0 + t] = (uint8_t)((flags >> t) & 1u);
+    if (t < j1 - j0) {
+        // Full: the whole bq x bk tile inside [0, n)^2 and no invalid element.
+        const bool inside = (i + 1) * bq <= n && ((j0 + t + 1) << bk_shift) <= n;
+        const uint32_t any = (flags >> t) & 1u;
+        const uint32_t full = inside && !((zeros >> t) & 1u) ? 1u : 0u;
+        out[((int64_t)b * Tq + i) * Tk + j0 + t] = (uint8_t)(any | (full << 1));
+    }
 }
 
 hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask, int B, int L,

@@ -312,26 +312,28 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     if constexpr (kSoft) stats.init(p.osl, tid);
     Mask mstage;
     if constexpr (MASKED) mstage.init(tid);
-    auto load_tile = [&](int t) {
+    // full: the tile lies in a full block-mask entry (no element-mask reads).
+    auto load_tile = [&](int t, bool full) {
         stage.load(rows_rsrc(qb, t * BQ), rows_rsrc(dob, t * BQ));
         if constexpr (kSoft) stats.load(out_rows_rsrc(obase, t * BQ), lseb + t * BQ, n - t * BQ, tid);
-        if constexpr (MASKED) mstage.load(rmask, L, n, t * BQ, k0);
+        if constexpr (MASKED) mstage.load(rmask, L, n, t * BQ, k0, full);
     };
-    auto store_tile = [&](int i, int t) {
+    auto store_tile = [&](int i, int t, bool full) {
         stage.store(Qs(i), dOs(i));
         if constexpr (kSoft) stats.store(stage.b, c0, Dl(i), Offl(i), tid);
-        if constexpr (MASKED) mcls = mstage.store(Ml(i), t * BQ, k0, n);
+        if constexpr (MASKED) mcls = mstage.store(Ml(i), t * BQ, k0, n, full);
     };
     // Query tile 0 is fetched before the block mask is read (see the forward
     // kernel); another first tile is fetched again.
-    load_tile(0);
+    load_tile(0, false);
     TileSchedule<BQ> sched;
     sched.init(p.block_mask ? p.block_mask + (int64_t)b * p.Tq * p.Tk + k0 / p.block_k : nullptr,
                p.Tk, n, p.block_q);
     int qt = sched.next();
-    if (qt > 0) load_tile(qt);
+    const bool qt_full = sched.full;
+    if (qt > 0) load_tile(qt, qt_full);
     int buf = 0;
-    store_tile(0, qt < 0 ? 0 : qt);
+    store_tile(0, qt < 0 ? 0 : qt, qt_full);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         if constexpr (!kSoft) kreg[ks] = scale8(kreg[ks], c1);
@@ -343,7 +345,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     while (qt >= 0) {
         const int q0 = qt * BQ;
         const int nxt = sched.next();
-        if (nxt >= 0) load_tile(nxt);
+        const bool nxt_full = sched.full;
+        if (nxt >= 0) load_tile(nxt, nxt_full);
         const bf16 *Qc = Qs(buf);
         const bf16 *dOc = dOs(buf);
         const float *Dc = Dl(buf);
@@ -416,7 +419,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         } else {
             tile(std::integral_constant<int, 0>{});
         }
-        if (nxt >= 0) store_tile(buf ^ 1, nxt);
+        if (nxt >= 0) store_tile(buf ^ 1, nxt, nxt_full);
         __syncthreads();
         buf ^= 1;
         qt = nxt;
@@ -525,8 +528,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     if (kt > 0) fetch(kt, K0, V0);
     if constexpr (MASKED)
         if (kt >= 0) {
-            mstage.load(rmask, L, n, q0, kt * BK);
-            mcls = mstage.store(M0, q0, kt * BK, n);
+            mstage.load(rmask, L, n, q0, kt * BK, sched.full);
+            mcls = mstage.store(M0, q0, kt * BK, n, sched.full);
         }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -539,9 +542,10 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     auto step = [&](const bf16 *Kc, const bf16 *Vc, const uint32_t *Mc, bf16 *Kn, bf16 *Vn,
                     uint32_t *Mn) {
         const int nxt = sched.next();
+        const bool nxt_full = sched.full;
         if (nxt >= 0) fetch(nxt, Kn, Vn);
         if constexpr (MASKED)
-            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK);
+            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK, nxt_full);
         // MODE 0 (no element mask): padded key rows of K and V read as zeros,
         // so dP = 0 and dS = 0 there; padded query rows are zeroed at the
         // store.  MODE 2: element mask.
@@ -594,7 +598,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
             tile(std::integral_constant<int, 0>{});
         }
         if constexpr (MASKED)
-            if (nxt >= 0) mcls = mstage.store(Mn, q0, nxt * BK, n);
+            if (nxt >= 0) mcls = mstage.store(Mn, q0, nxt * BK, n, nxt_full);
         wait_vm0();
         __syncthreads();
         kt = nxt;

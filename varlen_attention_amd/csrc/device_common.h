@@ -105,7 +105,8 @@ struct TileSchedule {
     int per_blk;        // kernel tiles per block-mask entry
     int nkt;            // kernel tiles covering [0, n)
     int wbase, entry, sub;
-    uint64_t act;
+    uint64_t act, fullm;  // kept / full entries of the 64 at wbase
+    bool full;            // the tile next() returned lies in a full entry
 
     __device__ __forceinline__ void init(const uint8_t *first, int64_t step, int n, int block) {
         bm = first;
@@ -116,7 +117,8 @@ struct TileSchedule {
         wbase = -64;
         entry = -1;
         sub = 0;
-        act = 0;
+        act = fullm = 0;
+        full = false;
     }
 
     // Next active kernel tile index, or -1.
@@ -129,10 +131,13 @@ struct TileSchedule {
             wbase += 64;
             if (wbase >= nblk) return -1;
             const int e = wbase + (int)(threadIdx.x & 63);
-            const bool on = e < nblk && (bm == nullptr || bm[e * stride] != 0);
-            act = __ballot(on);
+            const int v = e < nblk ? (bm == nullptr ? 1 : (int)bm[e * stride]) : 0;
+            act = __ballot(v != 0);
+            fullm = __ballot((v & 2) != 0);
         }
-        entry = wbase + __builtin_ctzll(act);
+        const int bit = __builtin_ctzll(act);
+        entry = wbase + bit;
+        full = (fullm >> bit) & 1u;
         act &= act - 1;
         sub = 0;
         return entry * per_blk;
@@ -406,11 +411,12 @@ struct MaskStage {
     }
 
     // rmask covers exactly the batch entry's L x L mask; L * L fits in int.
-    // Words of rows or keys at or past n are not read (store clears them).
-    __device__ __forceinline__ void load(rsrc_t rmask, int L, int n, int r0, int k0) {
+    // Words of rows or keys at or past n are not read (store clears them),
+    // nor any word of a full tile (every entry valid: store writes ones).
+    __device__ __forceinline__ void load(rsrc_t rmask, int L, int n, int r0, int k0, bool full) {
         lo = hi = make_uint4(0u, 0u, 0u, 0u);
         const int row = r0 + r, key = k0 + 32 * wi;
-        if (!act || row >= n || key >= n) return;
+        if (full || !act || row >= n || key >= n) return;
         const int off = row * L + key;
         if (off + 32 <= L * L) {
             lo = buffer_load16(rmask, off);
@@ -430,7 +436,11 @@ struct MaskStage {
 
     // Writes the bits and returns this wave's class for the tile (all lanes
     // of the wave call it).
-    __device__ __forceinline__ int store(uint32_t *words, int r0, int k0, int n) const {
+    __device__ __forceinline__ int store(uint32_t *words, int r0, int k0, int n, bool full) const {
+        if (full) {
+            if (act) words[wi * ROWS + r] = 0xffffffffu;
+            return kDense;
+        }
         uint32_t x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         if (k0 + KEYS > n) {  // keys at or past n: clear their bytes
             const int m = n - k0 - 32 * wi;

@@ -169,13 +169,14 @@ fwd_kernel(const AttnParams p) {
     TileSchedule<BK> sched;
     sched.init(bm_row, 1, n, p.block_k);
     int kt = sched.next();
+    const bool kt_full = sched.full;
     if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
     if constexpr (MASKED)
-        if (kt >= 0) mstage.load(rmask, L, n, q0, kt * BK);
+        if (kt >= 0) mstage.load(rmask, L, n, q0, kt * BK, kt_full);
     int buf = 0;
     stage.store(Ks[0], Vs[0]);
     if constexpr (MASKED)
-        if (kt >= 0) mcls = mstage.store(Ms[0], q0, kt * BK, n);
+        if (kt >= 0) mcls = mstage.store(Ms[0], q0, kt * BK, n, kt_full);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         if constexpr (VARIANT == kSigmoid) qreg[ks] = scale8(qreg[ks], c1);
@@ -187,9 +188,10 @@ fwd_kernel(const AttnParams p) {
     while (kt >= 0) {
         const int k0 = kt * BK;
         const int nxt = sched.next();
+        const bool nxt_full = sched.full;
         if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
         if constexpr (MASKED)
-            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK);
+            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK, nxt_full);
         const bf16 *Kc = Ks[buf];
         const bf16 *Vc = Vs[buf];
 
@@ -303,7 +305,7 @@ fwd_kernel(const AttnParams p) {
 
         if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
         if constexpr (MASKED)
-            if (nxt >= 0) mcls = mstage.store(Ms[buf ^ 1], q0, nxt * BK, n);
+            if (nxt >= 0) mcls = mstage.store(Ms[buf ^ 1], q0, nxt * BK, n, nxt_full);
         __syncthreads();
         buf ^= 1;
         kt = nxt;
