@@ -4,7 +4,9 @@
  *
  * Operation (per batch entry b, head h; n = clamp(seq_lens[b], 0, L)):
  *   valid(r, c) = r < n and c < n and (mask == NULL or mask[b, r, c] != 0)
- *                 and (block_mask == NULL or its entry for the tile of (r, c) is 1)
+ *                 and (key_range == NULL or lo <= c <= hi, with
+ *                      (lo, hi) = key_range[b, r, 0..1])
+ *                 and (block_mask == NULL or its entry for the tile of (r, c) is non-zero)
  *   s[r, c]     = scale * <q_r, k_c> + beta
  *   beta        = 0 (NONE), -ln n (LOG_SEQLEN), -ln L (LOG_PADLEN)
  *   SIGMOID     o_r = sum_c sigma(s[r, c]) v_c
@@ -35,6 +37,17 @@
  *   the last failure on the calling thread.
  * - seq_lens lives in device memory, so its values are not checked on the
  *   host; kernels clamp each length into [0, L].
+ * - An element mask comes in one of two forms, never both in one call:
+ *     mask       [device] uint8 [B, L, L], non-zero = may attend (any pattern);
+ *     key_range  [device] int32 [B, L, 2], 8-byte aligned: query row r of
+ *                batch entry b attends the keys lo <= c <= hi (inclusive,
+ *                empty when lo > hi).  This covers the masks whose rows are
+ *                intervals (causal, packed documents, causal packed
+ *                documents, sliding windows) in 8 bytes per row; the kernels
+ *                evaluate it per tile and never read an L x L mask (Binary
+ *                Block Masking, "Applications and real-world tests", counts
+ *                packed-sequence masks among its targets).
+ *   Either form needs a block mask from blockmask_build with the same form.
  */
 #ifndef SIGATTN_H
 #define SIGATTN_H
@@ -93,6 +106,8 @@ typedef struct {
  *   seq_lens    [device] int32 [B]
  *   mask        [device] uint8 [B, L, L] row-major, non-zero = may attend;
  *               NULL for padding-only batches.  Must be 16-byte aligned.
+ *   key_range   [device] int32 [B, L, 2] (see above) or NULL; at most one of
+ *               mask and key_range.
  *   block_mask  [device] uint8 [B, Tq, Tk] output, Tq = ceil(L / block_q),
  *               Tk = ceil(L / block_k); every entry is written with 0, 1 or 3.
  * Bit 0 of entry (b, i, j) is the binary block matrix: 1 iff some r in
@@ -103,11 +118,15 @@ typedef struct {
  * is valid; the attention kernels then read no element mask for it.  With
  * mask == NULL bit 0 is i*block_q < n && j*block_k < n and bit 1 is
  * (i+1)*block_q <= n && (j+1)*block_k <= n.
- * Errors: INVALID_ARG (null seq_lens/block_mask, B or L <= 0), UNSUPPORTED
- * (block size not 32/64/128), ALIGNMENT (mask not 16-byte aligned), LAUNCH.
+ * With key_range the builder reads only the ranges (O(block_q) work per
+ * entry, no L x L scan).
+ * Errors: INVALID_ARG (null seq_lens/block_mask, B or L <= 0, both mask and
+ * key_range), UNSUPPORTED (block size not 32/64/128), ALIGNMENT (mask not
+ * 16-byte or key_range not 8-byte aligned), LAUNCH.
  */
-int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, int32_t B, int32_t L,
-                    int32_t block_q, int32_t block_k, uint8_t *block_mask, void *stream);
+int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t *key_range,
+                    int32_t B, int32_t L, int32_t block_q, int32_t block_k, uint8_t *block_mask,
+                    void *stream);
 
 /*
  * sigattn_fwd - forward pass (single-cell page section 2.C: one fused kernel,
@@ -119,12 +138,14 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, int32_t B, int
  *   seq_lens    [device] int32 [B]
  *   block_mask  [device] uint8 [B, Tq, Tk] from blockmask_build with the same
  *               block sizes, or NULL: tiles are then chosen from seq_lens
- *               alone.  Required when mask != NULL.  Tiles with a zero entry
+ *               alone.  Required with mask or key_range.  Tiles with a zero entry
  *               are skipped; bit 1 set promises a full tile (see
  *               blockmask_build), so a caller's own 0/1 matrix is also valid.
  *   mask        [device] uint8 [B, L, L] or NULL (element mask, all heads;
  *               non-zero = may attend; rows need no alignment); with a mask,
  *               L <= SIGATTN_MAX_MASKED_L (else UNSUPPORTED)
+ *   key_range   [device] int32 [B, L, 2] or NULL (key ranges, all heads; see
+ *               above); at most one of mask and key_range
  *   o           [device] bf16 [B, H, L, d] (output layout), fully written
  *   lse         [device] float [B, H, L] contiguous, or NULL.  Softmax
  *               variants write the natural log of each row's denominator
@@ -132,11 +153,13 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, int32_t B, int
  *               key); SIGMOID does not write it.
  * Accumulation is fp32; the weights are rounded to bf16 before the product
  * with V and the output is rounded to bf16 (round to nearest even).
- * Errors: INVALID_ARG, UNSUPPORTED (d not 64/128, block size), ALIGNMENT, LAUNCH.
+ * Errors: INVALID_ARG (also: both mask and key_range, or either without a
+ * block mask), UNSUPPORTED (d not 64/128, block size), ALIGNMENT, LAUNCH.
  */
 int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                 const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
-                int32_t bias_mode, int32_t variant, void *o, float *lse, void *stream);
+                const int32_t *key_range, int32_t bias_mode, int32_t variant, void *o,
+                float *lse, void *stream);
 
 /*
  * sigattn_bwd - gradients dQ, dK, dV of sum(dO * O)
@@ -154,7 +177,7 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
  *                   SOFTMAX1, ignored (may be NULL) for SIGMOID
  *   lse             [device] fp32 [B, H, L] contiguous: the forward's
  *                   log-sum-exp; same rule as o
- *   seq_lens, block_mask, mask: as for sigattn_fwd
+ *   seq_lens, block_mask, mask, key_range: as for sigattn_fwd
  *   dq, dk, dv      [device] bf16 [B, H, L, d] (output layout), fully written;
  *                   rows >= n are 0.
  * bias_mode and variant must be those the forward ran with.
@@ -169,8 +192,8 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
  */
 int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                 const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
-                const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode,
-                int32_t variant, void *dq, void *dk, void *dv, void *stream);
+                const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
+                int32_t bias_mode, int32_t variant, void *dq, void *dk, void *dv, void *stream);
 
 /*
  * sigattn_bwd_dkdv / sigattn_bwd_dq - the two halves of sigattn_bwd, each one
@@ -183,11 +206,12 @@ int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const 
 int sigattn_bwd_dkdv(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                      const void *dout, const void *o, const float *lse,
                      const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
-                     int32_t bias_mode, int32_t variant, void *dk, void *dv, void *stream);
+                     const int32_t *key_range, int32_t bias_mode, int32_t variant, void *dk,
+                     void *dv, void *stream);
 int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                    const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
-                   const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode,
-                   int32_t variant, void *dq, void *stream);
+                   const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
+                   int32_t bias_mode, int32_t variant, void *dq, void *stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *sigattn_last_error(void);

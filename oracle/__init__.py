@@ -95,10 +95,28 @@ def default_scale(d: int) -> float:
     return 1.0 / float(np.sqrt(d))
 
 
-def blockmask(seq_lens, mask, L: int, block_q: int, block_k: int) -> np.ndarray:
+def key_range_mask(key_range, L: int) -> np.ndarray:
+    """The element mask that key ranges stand for: uint8 [B, L, L] with
+    mask[b, r, c] = 1 iff key_range[b, r, 0] <= c <= key_range[b, r, 1]
+    (the definition in include/sigattn.h, written out)."""
+    kr = np.asarray(key_range, dtype=np.int64)
+    c = np.arange(L)[None, None, :]
+    return ((kr[:, :, 0:1] <= c) & (c <= kr[:, :, 1:2])).astype(np.uint8)
+
+
+def _element_mask(mask, key_range, L):
+    """One dense element mask from the two forms (both: both conditions)."""
+    if key_range is None:
+        return mask
+    km = key_range_mask(key_range, L)
+    return km if mask is None else (km & (np.asarray(mask) != 0)).astype(np.uint8)
+
+
+def blockmask(seq_lens, mask, L: int, block_q: int, block_k: int, key_range=None) -> np.ndarray:
     """Block matrix [B, Tq, Tk] (uint8): bit 0 the binary block mask (tile holds
     a valid element), bit 1 a full tile (inside [0, n)^2, every element valid);
-    see oracle_blockmask."""
+    see oracle_blockmask.  ``key_range`` [B, L, 2] stands for key_range_mask."""
+    mask = _element_mask(mask, key_range, L)
     lib = _load()
     n = np.ascontiguousarray(seq_lens, dtype=np.int32)
     B = n.shape[0]
@@ -115,12 +133,13 @@ def _heads(q):
 
 
 def fwd(q, k, v, seq_lens, mask=None, bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None,
-        precision="f64", threads=None, heads=None):
+        precision="f64", threads=None, heads=None, key_range=None):
     """Forward by the plain definition (oracle_fwd_rows) for every row.
 
     Returns (o [B, H, L, d], lse [B, H, L]).  ``heads``: optional list of
     (b, h) pairs to compute; the others are left at zero / -inf.
     """
+    mask = _element_mask(mask, key_range, q.shape[2])
     lib = _load()
     B, H, L, d = _heads(q)
     dt = _dtype(precision)
@@ -147,7 +166,7 @@ def fwd(q, k, v, seq_lens, mask=None, bias=BIAS_LOG_SEQLEN, variant=SIGMOID, sca
 
 
 def fwd_rows(q, k, v, seq_lens, b: int, h: int, rows, mask=None, bias=BIAS_LOG_SEQLEN,
-             variant=SIGMOID, scale=None, precision="f64"):
+             variant=SIGMOID, scale=None, precision="f64", key_range=None):
     """Selected output rows of one head: (o [len(rows), d], lse [len(rows)])."""
     lib = _load()
     B, H, L, d = _heads(q)
@@ -155,7 +174,10 @@ def fwd_rows(q, k, v, seq_lens, b: int, h: int, rows, mask=None, bias=BIAS_LOG_S
     fn = getattr(lib, "oracle_fwd_rows_" + precision)
     scale = default_scale(d) if scale is None else scale
     qs, ks, vs = (np.ascontiguousarray(t[b, h]) for t in (q, k, v))
+    # Only batch entry b's mask is needed (its key ranges written out).
     mb = None if mask is None else np.ascontiguousarray(mask[b])
+    if key_range is not None:
+        mb = _element_mask(None if mb is None else mb[None], key_range[b:b + 1], L)[0]
     rows = list(rows)
     o = np.zeros((len(rows), d), dtype=dt)
     lse = np.zeros(len(rows), dtype=dt)
@@ -171,11 +193,12 @@ def fwd_rows(q, k, v, seq_lens, b: int, h: int, rows, mask=None, bias=BIAS_LOG_S
 
 def fwd_tiled(q, k, v, seq_lens, block_mask=None, block_q=64, block_k=64, mask=None,
               bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None, precision="f64",
-              threads=None):
+              threads=None, key_range=None):
     """Forward by the tiled online algorithm (oracle_fwd_tiled).
 
     ``block_mask`` [B, Tq, Tk] selects the tiles visited; None visits all.
     """
+    mask = _element_mask(mask, key_range, q.shape[2])
     lib = _load()
     B, H, L, d = _heads(q)
     dt = _dtype(precision)
@@ -202,8 +225,9 @@ def fwd_tiled(q, k, v, seq_lens, block_mask=None, block_q=64, block_k=64, mask=N
 
 
 def bwd(q, k, v, do, seq_lens, mask=None, bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None,
-        precision="f64", threads=None, heads=None):
+        precision="f64", threads=None, heads=None, key_range=None):
     """dQ, dK, dV [B, H, L, d] by the plain definition (oracle_bwd_*_rows)."""
+    mask = _element_mask(mask, key_range, q.shape[2])
     lib = _load()
     B, H, L, d = _heads(q)
     dt = _dtype(precision)
@@ -235,7 +259,7 @@ def bwd(q, k, v, do, seq_lens, mask=None, bias=BIAS_LOG_SEQLEN, variant=SIGMOID,
 
 
 def bwd_rows(q, k, v, do, seq_lens, b: int, h: int, q_rows, k_rows, mask=None,
-             bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None, precision="f64"):
+             bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None, precision="f64", key_range=None):
     """Selected rows of one head: (dq [len(q_rows), d], dk, dv [len(k_rows), d])."""
     lib = _load()
     B, H, L, d = _heads(q)
@@ -244,7 +268,10 @@ def bwd_rows(q, k, v, do, seq_lens, b: int, h: int, q_rows, k_rows, mask=None,
     fkv = getattr(lib, "oracle_bwd_dkv_rows_" + precision)
     scale = default_scale(d) if scale is None else scale
     qs, ks, vs, ds = (np.ascontiguousarray(t[b, h]) for t in (q, k, v, do))
+    # Only batch entry b's mask is needed (its key ranges written out).
     mb = None if mask is None else np.ascontiguousarray(mask[b])
+    if key_range is not None:
+        mb = _element_mask(None if mb is None else mb[None], key_range[b:b + 1], L)[0]
     n = int(seq_lens[b])
     q_rows, k_rows = list(q_rows), list(k_rows)
     dq = np.zeros((len(q_rows), d), dtype=dt)

@@ -93,6 +93,23 @@ def packed_causal_mask(seq_lens: np.ndarray, docs: list, L: int) -> np.ndarray:
     return mask
 
 
+def packed_causal_ranges(seq_lens: np.ndarray, docs: list, L: int) -> np.ndarray:
+    """int32 [B, L, 2]: the key range [start of r's document, r] of each query
+    row r < n, and the empty range (0, -1) for padded rows.  The same pattern
+    as packed_causal_mask, one interval per row."""
+    B = len(seq_lens)
+    kr = np.zeros((B, L, 2), dtype=np.int32)
+    kr[:, :, 1] = -1
+    for b in range(B):
+        pos = 0
+        for length in docs[b]:
+            rows = np.arange(pos, pos + length)
+            kr[b, rows, 0] = pos
+            kr[b, rows, 1] = rows
+            pos += length
+    return kr
+
+
 def random_tensor(rng: np.random.Generator, shape) -> np.ndarray:
     return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
 
@@ -110,6 +127,7 @@ class Workload:
     variant: int = SIGMOID
     bias: int = BIAS_LOG_SEQLEN
     mask: Optional[np.ndarray] = None
+    key_range: Optional[np.ndarray] = None
     docs: Optional[list] = None
     q: Optional[np.ndarray] = None
     k: Optional[np.ndarray] = None
@@ -160,6 +178,7 @@ def make_workload(name: str, *, seed: int = 0, B: int, H: int, d: int,
     if docs:
         w.docs = [packed_documents(rng, int(min(max(x, 0), padded))) for x in n]
         w.mask = packed_causal_mask(n, w.docs, padded)
+        w.key_range = packed_causal_ranges(n, w.docs, padded)
     _tensors(rng, w, tensors)
     return w
 

@@ -48,9 +48,9 @@ FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below
 
 
 def _fwd(lib, va, shape, q=FAKE, k=FAKE, v=FAKE, seq=FAKE, bm=None, mask=None, bias=1, var=0,
-         o=FAKE, lse=None):
+         o=FAKE, lse=None, kr=None):
     return lib.sigattn_fwd(ctypes.byref(shape) if shape is not None else None, q, k, v, seq, bm,
-                           mask, bias, var, o, lse, None)
+                           mask, kr, bias, var, o, lse, None)
 
 
 def test_forward_argument_errors(lib):
@@ -72,6 +72,10 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, va, _shape(va), lse=ctypes.c_void_p(0x10002)) == va.ERR_ALIGNMENT
     # An element mask bounds L (32-bit offsets into each L x L mask).
     assert _fwd(lib, va, _shape(va, L=46081), mask=FAKE, bm=FAKE) == va.ERR_UNSUPPORTED
+    # Key ranges: not with a dense mask, only with a block mask, 8-byte aligned.
+    assert _fwd(lib, va, _shape(va), mask=FAKE, kr=FAKE, bm=FAKE) == va.ERR_INVALID_ARG
+    assert _fwd(lib, va, _shape(va), kr=FAKE) == va.ERR_INVALID_ARG
+    assert _fwd(lib, va, _shape(va), kr=ctypes.c_void_p(0x10004), bm=FAKE) == va.ERR_ALIGNMENT
 
 
 def test_backward_argument_errors(lib):
@@ -79,9 +83,9 @@ def test_backward_argument_errors(lib):
     sh = _shape(va)
     args = [FAKE] * 4  # q, k, v, dout
 
-    def bwd(shape=sh, o=None, lse=None, var=0, dk=FAKE, bm=None, mask=None):
-        return lib.sigattn_bwd(ctypes.byref(shape), *args, o, lse, FAKE, bm, mask, 1, var, FAKE,
-                               dk, FAKE, None)
+    def bwd(shape=sh, o=None, lse=None, var=0, dk=FAKE, bm=None, mask=None, kr=None):
+        return lib.sigattn_bwd(ctypes.byref(shape), *args, o, lse, FAKE, bm, mask, kr, 1, var,
+                               FAKE, dk, FAKE, None)
 
     # The softmax variants need the forward's o and lse; SIGMOID ignores them.
     assert bwd(var=1) == va.ERR_INVALID_ARG
@@ -92,20 +96,26 @@ def test_backward_argument_errors(lib):
     assert bwd(mask=FAKE) == va.ERR_INVALID_ARG  # an element mask needs its block mask
     assert bwd(shape=_shape(va, L=50000), mask=FAKE, bm=FAKE) == va.ERR_UNSUPPORTED
     assert bwd(shape=_shape(va, d=128, L=0)) == va.ERR_INVALID_ARG
-    assert lib.sigattn_bwd_dq(ctypes.byref(sh), *args, None, None, FAKE, None, None, 1, 1, FAKE,
-                              None) == va.ERR_INVALID_ARG
-    assert lib.sigattn_bwd_dkdv(ctypes.byref(sh), *args, None, None, FAKE, None, None, 1, 0, FAKE,
-                                None, None) == va.ERR_INVALID_ARG
+    assert bwd(mask=FAKE, kr=FAKE, bm=FAKE) == va.ERR_INVALID_ARG
+    assert bwd(kr=FAKE) == va.ERR_INVALID_ARG
+    assert bwd(kr=ctypes.c_void_p(0x10004), bm=FAKE) == va.ERR_ALIGNMENT
+    assert lib.sigattn_bwd_dq(ctypes.byref(sh), *args, None, None, FAKE, None, None, None, 1, 1,
+                              FAKE, None) == va.ERR_INVALID_ARG
+    assert lib.sigattn_bwd_dkdv(ctypes.byref(sh), *args, None, None, FAKE, None, None, None, 1, 0,
+                                FAKE, None, None) == va.ERR_INVALID_ARG
 
 
 def test_blockmask_argument_errors(lib):
     import varlen_attention_amd as va
-    assert lib.blockmask_build(None, None, 2, 100, 32, 32, FAKE, None) == va.ERR_INVALID_ARG
-    assert lib.blockmask_build(FAKE, None, 2, 100, 32, 32, None, None) == va.ERR_INVALID_ARG
-    assert lib.blockmask_build(FAKE, None, 0, 100, 32, 32, FAKE, None) == va.ERR_INVALID_ARG
-    assert lib.blockmask_build(FAKE, None, 2, 100, 16, 32, FAKE, None) == va.ERR_UNSUPPORTED
-    assert lib.blockmask_build(FAKE, ctypes.c_void_p(0x10001), 2, 100, 32, 32, FAKE,
-                               None) == va.ERR_ALIGNMENT
+    bmb = lib.blockmask_build
+    assert bmb(None, None, None, 2, 100, 32, 32, FAKE, None) == va.ERR_INVALID_ARG
+    assert bmb(FAKE, None, None, 2, 100, 32, 32, None, None) == va.ERR_INVALID_ARG
+    assert bmb(FAKE, None, None, 0, 100, 32, 32, FAKE, None) == va.ERR_INVALID_ARG
+    assert bmb(FAKE, None, None, 2, 100, 16, 32, FAKE, None) == va.ERR_UNSUPPORTED
+    assert bmb(FAKE, ctypes.c_void_p(0x10001), None, 2, 100, 32, 32, FAKE, None) == va.ERR_ALIGNMENT
+    assert bmb(FAKE, FAKE, FAKE, 2, 100, 32, 32, FAKE, None) == va.ERR_INVALID_ARG
+    assert bmb(FAKE, None, ctypes.c_void_p(0x10004), 2, 100, 32, 32, FAKE,
+               None) == va.ERR_ALIGNMENT
 
 
 def test_binding_rejects_cpu_tensors():

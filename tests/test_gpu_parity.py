@@ -29,8 +29,8 @@ def _inputs(seed, B, H, L, d, seq_lens, names=("q", "k", "v")):
     return [syn.random_tensor(rng, (B, H, L, d)) for _ in names]
 
 
-def _bm(va, n_gpu, L, bq, bk, mask_gpu=None):
-    out = va.blockmask_build(n_gpu, L, bq, bk, mask=mask_gpu)
+def _bm(va, n_gpu, L, bq, bk, mask_gpu=None, key_range=None):
+    out = va.blockmask_build(n_gpu, L, bq, bk, mask=mask_gpu, key_range=key_range)
     torch.cuda.synchronize()
     return out
 
@@ -274,6 +274,75 @@ def test_causal_mask_full_tiles(va, d, L, bq, bk, variant):
     assert_rows(gpu_f64(outs[0][0]), want, n, "O")
     wq, wk, wv = oracle.bwd(q, k, v, do, n, mask=mask, bias=bias, variant=variant)
     for name, got_t, ref in zip(("dQ", "dK", "dV"), outs[0][1:], (wq, wk, wv)):
+        assert_rows(gpu_f64(got_t), ref, n, name)
+
+
+def _window_ranges(rng, B, L):
+    """Sliding windows of random width per row, some reaching past the row,
+    some empty (lo > hi), some clipped at 0 or L - 1."""
+    r = np.arange(L)
+    lo = r[None, :] - rng.integers(0, 80, size=(B, L))
+    hi = r[None, :] + rng.integers(-4, 6, size=(B, L))
+    kr = np.stack([lo, hi], axis=2).astype(np.int32)
+    if L > 3:
+        kr[0, 3] = (9, 2)      # empty
+    kr[0, L - 1] = (-7, L + 9)  # whole row, clipped both ways
+    return kr
+
+
+@pytest.mark.parametrize("L,bq,bk", [(300, 64, 64), (257, 128, 32), (129, 32, 128), (1, 128, 64)])
+def test_blockmask_from_key_ranges_bitexact(va, L, bq, bk):
+    rng = np.random.default_rng(L + bk)
+    n = np.array([L, max(L - 50, 0), 1, 0], np.int32)
+    kr = _window_ranges(rng, 4, L)
+    got = _bm(va, to_gpu(n, torch.int32), L, bq, bk, key_range=to_gpu(kr, torch.int32))
+    np.testing.assert_array_equal(got.cpu().numpy(),
+                                  oracle.blockmask(n, None, L, bq, bk, key_range=kr))
+
+
+KEY_RANGE_CASES = [
+    # d, L, block_q, block_k, variant, bias
+    (64, 300, 128, 128, SIGMOID, 1),
+    (64, 211, 32, 64, SIGMOID, 0),
+    (128, 257, 128, 64, SIGMOID, 2),
+    (64, 230, 64, 32, SOFTMAX, 0),
+    (128, 190, 64, 128, SOFTMAX1, 1),
+]
+
+
+@pytest.mark.parametrize("d,L,bq,bk,variant,bias", KEY_RANGE_CASES)
+def test_key_range_mask(va, d, L, bq, bk, variant, bias):
+    """Key ranges against the oracle (forward and backward), and bit-identical
+    to the dense-mask path given the mask the ranges stand for."""
+    B, H = 4, 2
+    n = np.array([L, L - 37, 1, 0], np.int32)
+    q, k, v, do = _inputs(6000 + d + L + variant, B, H, L, d, n, names="qkvd")
+    kr = _window_ranges(np.random.default_rng(L * 3 + d), B, L)
+    dense = oracle.key_range_mask(kr, L)
+    say(f"key ranges d={d} L={L} bq={bq} bk={bk} variant={variant} bias={bias}")
+    n_gpu = to_gpu(n, torch.int32)
+    kr_gpu = to_gpu(kr, torch.int32)
+    m_gpu = to_gpu(dense, torch.uint8)
+    bm_r = _bm(va, n_gpu, L, bq, bk, key_range=kr_gpu)
+    bm_d = _bm(va, n_gpu, L, bq, bk, m_gpu)
+    assert torch.equal(bm_r, bm_d)
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    res = []
+    for form in ({"key_range": kr_gpu}, {"mask": m_gpu}):
+        blk = bm_r if "key_range" in form else bm_d
+        o, lse = va.sigattn_fwd(*g[:3], n_gpu, block_mask=blk, bias=bias, variant=variant,
+                                block_q=bq, block_k=bk, return_lse=True, **form)
+        grads = va.sigattn_bwd(*g, n_gpu, block_mask=blk, bias=bias, variant=variant,
+                               block_q=bq, block_k=bk, o=o if variant else None,
+                               lse=lse if variant else None, **form)
+        res.append((o,) + tuple(grads))
+    torch.cuda.synchronize()
+    for a, b_ in zip(*res):
+        assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
+    want, _ = oracle.fwd(q, k, v, n, bias=bias, variant=variant, key_range=kr)
+    assert_rows(gpu_f64(res[0][0]), want, n, "O")
+    wq, wk, wv = oracle.bwd(q, k, v, do, n, bias=bias, variant=variant, key_range=kr)
+    for name, got_t, ref in zip(("dQ", "dK", "dV"), res[0][1:], (wq, wk, wv)):
         assert_rows(gpu_f64(got_t), ref, n, name)
 
 
@@ -586,6 +655,28 @@ def test_backward_single_cell_full_size(va, single_cell_inputs):
     w = single_cell_inputs
     say(f"bwd full {w.name} L={w.L}")
     _check_sampled_bwd(va, w)
+
+
+def test_long_documents_key_ranges_full_size(va):
+    """The causal packed-document mask as key ranges (8 bytes per row instead
+    of an L x L mask) at B8 H16 d128: the same block mask and bit-identical
+    forward and backward results as the dense mask."""
+    w = syn.long_packed_docs(0, tensors=("q", "k", "v", "do"))
+    say(f"key ranges full {w.name} L={w.L}")
+    n_gpu = to_gpu(w.seq_lens, torch.int32)
+    kr_gpu = to_gpu(w.key_range, torch.int32)
+    m_gpu = to_gpu(w.mask, torch.uint8)
+    bm_r = _bm(va, n_gpu, w.L, 128, 128, key_range=kr_gpu)
+    bm_d = _bm(va, n_gpu, w.L, 128, 128, m_gpu)
+    assert torch.equal(bm_r, bm_d)
+    g = [to_gpu_bf16(t) for t in (w.q, w.k, w.v, w.do)]
+    res = []
+    for form, blk in (({"key_range": kr_gpu}, bm_r), ({"mask": m_gpu}, bm_d)):
+        o = va.sigattn_fwd(*g[:3], n_gpu, block_mask=blk, **form)
+        res.append((o,) + tuple(va.sigattn_bwd(*g, n_gpu, block_mask=blk, **form)))
+    torch.cuda.synchronize()
+    for a, b_ in zip(*res):
+        assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
 
 
 def test_backward_long_documents_full_size(va):

@@ -58,17 +58,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I = ctypes.c_int32
-    lib.blockmask_build.argtypes = [P, P, I, I, I, I, P, P]
+    S = ctypes.POINTER(Shape)
+    lib.blockmask_build.argtypes = [P, P, P, I, I, I, I, P, P]
     lib.blockmask_build.restype = ctypes.c_int
-    lib.sigattn_fwd.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, I, I, P, P, P]
+    lib.sigattn_fwd.argtypes = [S, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sigattn_fwd.restype = ctypes.c_int
-    lib.sigattn_bwd.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, P, P, I, I, P, P, P,
-                                P]
+    lib.sigattn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P, P]
     lib.sigattn_bwd.restype = ctypes.c_int
-    lib.sigattn_bwd_dkdv.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, P, P, I, I, P, P,
-                                     P]
+    lib.sigattn_bwd_dkdv.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sigattn_bwd_dkdv.restype = ctypes.c_int
-    lib.sigattn_bwd_dq.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, P, P, P, P, I, I, P, P]
+    lib.sigattn_bwd_dq.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, P, P]
     lib.sigattn_bwd_dq.restype = ctypes.c_int
     lib.sigattn_last_error.argtypes = []
     lib.sigattn_last_error.restype = ctypes.c_char_p
@@ -128,30 +127,41 @@ def num_tiles(L: int, block: int) -> int:
     return -(-L // block)
 
 
+def _key_range(key_range, B, L):
+    if key_range is not None:
+        _need(key_range, "key_range", torch.int32)
+        if tuple(key_range.shape) != (B, L, 2) or not key_range.is_contiguous():
+            raise ValueError("key_range must be a contiguous int32 [B, L, 2] tensor")
+
+
 def blockmask_build(seq_lens: torch.Tensor, L: int, block_q: int = 128, block_k: int = 128,
                     mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                    stream=None) -> torch.Tensor:
-    """Binary block matrix uint8 [B, ceil(L/block_q), ceil(L/block_k)] on the GPU."""
+                    stream=None, key_range: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block matrix uint8 [B, ceil(L/block_q), ceil(L/block_k)] on the GPU: bit 0
+    the binary block mask, bit 1 full tiles.  The element mask is ``mask``
+    (uint8 [B, L, L]) or ``key_range`` (int32 [B, L, 2]: row r keeps keys
+    lo..hi), not both."""
     _need(seq_lens, "seq_lens", torch.int32)
     B = seq_lens.shape[0]
     if mask is not None:
         _need(mask, "mask", torch.uint8)
         if tuple(mask.shape) != (B, L, L) or not mask.is_contiguous():
             raise ValueError("mask must be a contiguous uint8 [B, L, L] tensor")
+    _key_range(key_range, B, L)
     shape = (B, num_tiles(L, block_q), num_tiles(L, block_k))
     if out is None:
         out = torch.empty(shape, dtype=torch.uint8, device=seq_lens.device)
     elif tuple(out.shape) != shape or out.dtype != torch.uint8 or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous uint8 tensor of shape {shape}")
     lib = load_library()
-    _check(lib.blockmask_build(_ptr(seq_lens.contiguous()), _ptr(mask), B, L, block_q, block_k,
-                               _ptr(out), _stream(stream)))
+    _check(lib.blockmask_build(_ptr(seq_lens.contiguous()), _ptr(mask), _ptr(key_range), B, L,
+                               block_q, block_k, _ptr(out), _stream(stream)))
     return out
 
 
 def sigattn_fwd(q, k, v, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                 variant=SIGMOID, scale=None, block_q=128, block_k=128, out=None, lse=None,
-                return_lse=False, stream=None):
+                return_lse=False, stream=None, key_range=None):
     """Forward pass.  q, k, v: bf16 [B, H, L, d] on the GPU (equal strides).
 
     Returns o (bf16, same shape) or (o, lse) with ``return_lse=True``.
@@ -181,16 +191,17 @@ def sigattn_fwd(q, k, v, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQ
         want = (B, num_tiles(L, block_q), num_tiles(L, block_k))
         if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
             raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
+    _key_range(key_range, B, L)
     shape = _shape(q, out.stride(), scale, block_q, block_k)
     lib = load_library()
     _check(lib.sigattn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
-                           _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), bias,
-                           variant, _ptr(out), _ptr(lse), _stream(stream)))
+                           _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask),
+                           _ptr(key_range), bias, variant, _ptr(out), _ptr(lse), _stream(stream)))
     return (out, lse) if return_lse else out
 
 
 def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k, variant, o,
-              lse):
+              lse, key_range):
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, nm, torch.bfloat16)
     _layout([q, k, v, dout], ["q", "k", "v", "dout"])
@@ -221,12 +232,13 @@ def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k
         want = (B, num_tiles(L, block_q), num_tiles(L, block_k))
         if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
             raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
+    _key_range(key_range, B, L)
     return outs
 
 
 def sigattn_bwd(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                 variant=SIGMOID, scale=None, block_q=128, block_k=128, dq=None, dk=None,
-                dv=None, o=None, lse=None, stream=None):
+                dv=None, o=None, lse=None, stream=None, key_range=None):
     """Gradients (dq, dk, dv) of sum(dout * o); bf16 [B, H, L, d] on the GPU.
 
     The softmax variants need the forward's output ``o`` and ``lse`` (from
@@ -234,38 +246,38 @@ def sigattn_bwd(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_L
     One launch for the dK/dV and dQ work when their tile heights agree (see
     include/sigattn.h); results equal sigattn_bwd_dkdv + sigattn_bwd_dq."""
     dq, dk, dv = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dq, dk, dv), block_q,
-                           block_k, variant, o, lse)
+                           block_k, variant, o, lse, key_range)
     shape = _shape(q, dq.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_bwd(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), _ptr(lse),
-        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dq),
-        _ptr(dk), _ptr(dv), _stream(stream)))
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), _ptr(key_range), bias, variant,
+        _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
     return dq, dk, dv
 
 
 def sigattn_bwd_dkdv(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                      variant=SIGMOID, scale=None, block_q=128, block_k=128, dk=None, dv=None,
-                     o=None, lse=None, stream=None):
+                     o=None, lse=None, stream=None, key_range=None):
     """The dK/dV half of the backward pass (one kernel): returns (dk, dv)."""
     dk, dv = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dk, dv), block_q, block_k,
-                       variant, o, lse)
+                       variant, o, lse, key_range)
     shape = _shape(q, dk.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_bwd_dkdv(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), _ptr(lse),
-        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dk),
-        _ptr(dv), _stream(stream)))
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), _ptr(key_range), bias, variant,
+        _ptr(dk), _ptr(dv), _stream(stream)))
     return dk, dv
 
 
 def sigattn_bwd_dq(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                    variant=SIGMOID, scale=None, block_q=128, block_k=128, dq=None, o=None,
-                   lse=None, stream=None):
+                   lse=None, stream=None, key_range=None):
     """The dQ half of the backward pass (one kernel): returns dq."""
     (dq,) = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dq,), block_q, block_k,
-                      variant, o, lse)
+                      variant, o, lse, key_range)
     shape = _shape(q, dq.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_bwd_dq(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), _ptr(lse),
-        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), bias, variant, _ptr(dq),
-        _stream(stream)))
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), _ptr(key_range), bias, variant,
+        _ptr(dq), _stream(stream)))
     return dq

@@ -38,8 +38,8 @@ int launch_status(hipError_t e, const char *what) {
 // Shared checks of sigattn_fwd / sigattn_bwd; fills the common parameter block.
 int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inputs,
                     void *const *outputs, int n_outputs, const int32_t *seq_lens,
-                    const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode,
-                    int32_t variant, sigattn::AttnParams *p) {
+                    const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
+                    int32_t bias_mode, int32_t variant, sigattn::AttnParams *p) {
     if (s == nullptr) return fail(SIGATTN_ERR_INVALID_ARG, "shape is NULL");
     if (s->B <= 0 || s->H <= 0 || s->L <= 0)
         return fail(SIGATTN_ERR_INVALID_ARG, "B, H and L must be positive (got %d, %d, %d)",
@@ -60,8 +60,12 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
         if (inputs[i] == nullptr) return fail(SIGATTN_ERR_INVALID_ARG, "input %d is NULL", i);
     for (int i = 0; i < n_outputs; ++i)
         if (outputs[i] == nullptr) return fail(SIGATTN_ERR_INVALID_ARG, "output %d is NULL", i);
-    if (mask != nullptr && block_mask == nullptr)
+    if (mask != nullptr && key_range != nullptr)
+        return fail(SIGATTN_ERR_INVALID_ARG, "give an element mask or key ranges, not both");
+    if ((mask != nullptr || key_range != nullptr) && block_mask == nullptr)
         return fail(SIGATTN_ERR_INVALID_ARG, "an element mask needs its block mask");
+    if (key_range != nullptr && (reinterpret_cast<uintptr_t>(key_range) & 7u) != 0)
+        return fail(SIGATTN_ERR_ALIGNMENT, "key_range is not 8-byte aligned");
     if (mask != nullptr && s->L > SIGATTN_MAX_MASKED_L)
         return fail(SIGATTN_ERR_UNSUPPORTED, "with an element mask L must be at most %d (got %d)",
                     SIGATTN_MAX_MASKED_L, s->L);
@@ -89,6 +93,7 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
     p->seq_lens = seq_lens;
     p->block_mask = block_mask;
     p->mask = mask;
+    p->key_range = key_range;
     p->sb = s->stride_b;
     p->sh = s->stride_h;
     p->sl = s->stride_l;
@@ -113,8 +118,9 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
 
 extern "C" {
 
-int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, int32_t B, int32_t L,
-                    int32_t block_q, int32_t block_k, uint8_t *block_mask, void *stream) {
+int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t *key_range,
+                    int32_t B, int32_t L, int32_t block_q, int32_t block_k, uint8_t *block_mask,
+                    void *stream) {
     if (seq_lens == nullptr || block_mask == nullptr)
         return fail(SIGATTN_ERR_INVALID_ARG, "seq_lens and block_mask must not be NULL");
     if (B <= 0 || L <= 0) return fail(SIGATTN_ERR_INVALID_ARG, "B and L must be positive");
@@ -122,21 +128,26 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, int32_t B, int
     if (!block_size_ok(block_q) || !block_size_ok(block_k))
         return fail(SIGATTN_ERR_UNSUPPORTED, "block sizes must be 32, 64 or 128 (got %d, %d)",
                     block_q, block_k);
+    if (mask != nullptr && key_range != nullptr)
+        return fail(SIGATTN_ERR_INVALID_ARG, "give an element mask or key ranges, not both");
     if (mask != nullptr && !aligned16(mask))
         return fail(SIGATTN_ERR_ALIGNMENT, "mask is not 16-byte aligned");
-    return launch_status(sigattn::launch_blockmask(seq_lens, mask, B, L, block_q, block_k,
-                                                   block_mask, (hipStream_t)stream),
+    if (key_range != nullptr && (reinterpret_cast<uintptr_t>(key_range) & 7u) != 0)
+        return fail(SIGATTN_ERR_ALIGNMENT, "key_range is not 8-byte aligned");
+    return launch_status(sigattn::launch_blockmask(seq_lens, mask, key_range, B, L, block_q,
+                                                   block_k, block_mask, (hipStream_t)stream),
                          "blockmask_build");
 }
 
 int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                 const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
-                int32_t bias_mode, int32_t variant, void *o, float *lse, void *stream) {
+                const int32_t *key_range, int32_t bias_mode, int32_t variant, void *o, float *lse,
+                void *stream) {
     sigattn::AttnParams p = {};
     const void *inputs[3] = {q, k, v};
     void *outputs[1] = {o};
     int st = check_attention(shape, inputs, 3, outputs, 1, seq_lens, block_mask, mask,
-                             bias_mode, variant, &p);
+                             key_range, bias_mode, variant, &p);
     if (st != SIGATTN_OK) return st;
     if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
         return fail(SIGATTN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
@@ -156,8 +167,9 @@ enum BwdParts { kPartDkdv = 1, kPartDq = 2 };
 
 int backward(const sigattn_shape *shape, const void *q, const void *k, const void *v,
              const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
-             const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode, int32_t variant,
-             void *dq, void *dk, void *dv, void *stream, int parts, const char *name) {
+             const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
+             int32_t bias_mode, int32_t variant, void *dq, void *dk, void *dv, void *stream,
+             int parts, const char *name) {
     sigattn::AttnParams p = {};
     const void *inputs[4] = {q, k, v, dout};
     void *outputs[3];
@@ -168,7 +180,7 @@ int backward(const sigattn_shape *shape, const void *q, const void *k, const voi
         outputs[n_out++] = dv;
     }
     int st = check_attention(shape, inputs, 4, outputs, n_out, seq_lens, block_mask, mask,
-                             bias_mode, variant, &p);
+                             key_range, bias_mode, variant, &p);
     if (st != SIGATTN_OK) return st;
     if (variant != SIGATTN_SIGMOID) {
         if (o == nullptr || lse == nullptr)
@@ -199,26 +211,27 @@ extern "C" {
 
 int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                 const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
-                const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode,
-                int32_t variant, void *dq, void *dk, void *dv, void *stream) {
-    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, bias_mode, variant,
-                    dq, dk, dv, stream, kPartDkdv | kPartDq, "sigattn_bwd");
+                const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
+                int32_t bias_mode, int32_t variant, void *dq, void *dk, void *dv, void *stream) {
+    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, key_range,
+                    bias_mode, variant, dq, dk, dv, stream, kPartDkdv | kPartDq, "sigattn_bwd");
 }
 
 int sigattn_bwd_dkdv(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                      const void *dout, const void *o, const float *lse,
                      const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
-                     int32_t bias_mode, int32_t variant, void *dk, void *dv, void *stream) {
-    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, bias_mode, variant,
-                    nullptr, dk, dv, stream, kPartDkdv, "sigattn_bwd_dkdv");
+                     const int32_t *key_range, int32_t bias_mode, int32_t variant, void *dk,
+                     void *dv, void *stream) {
+    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, key_range,
+                    bias_mode, variant, nullptr, dk, dv, stream, kPartDkdv, "sigattn_bwd_dkdv");
 }
 
 int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                    const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
-                   const uint8_t *block_mask, const uint8_t *mask, int32_t bias_mode,
-                   int32_t variant, void *dq, void *stream) {
-    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, bias_mode, variant,
-                    dq, nullptr, nullptr, stream, kPartDq, "sigattn_bwd_dq");
+                   const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
+                   int32_t bias_mode, int32_t variant, void *dq, void *stream) {
+    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, key_range,
+                    bias_mode, variant, dq, nullptr, nullptr, stream, kPartDq, "sigattn_bwd_dq");
 }
 
 const char *sigattn_last_error(void) { return g_last_error; }

@@ -100,10 +100,49 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
     }
 }
 
-hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask, int B, int L,
-                            int block_q, int block_k, uint8_t *out, hipStream_t stream) {
+// Key-range masks: query row r keeps keys [lo_r, hi_r] within [0, n).  One
+// workgroup per (query tile i, batch entry b) reads the tile's ranges into
+// LDS once; each thread then decides its key tiles from the bq ranges alone
+// (a tile is kept when some row's range meets it, full when it lies inside
+// [0, n)^2 and every row's range covers it).  O(bq) work per entry, no mask.
+__global__ void __launch_bounds__(256)
+blockmask_range_kernel(const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ key_range,
+                       int L, int bq, int bk, int Tq, int Tk, uint8_t *__restrict__ out) {
+    __shared__ int2 rr[128];
+    const int b = blockIdx.y, i = blockIdx.x;
+    const int n = clamp_len(seq_lens[b], L);
+    const int r0 = i * bq, rows = min(bq, L - r0);
+    for (int t = threadIdx.x; t < rows; t += blockDim.x) {
+        int2 v = make_int2(1, 0);  // empty: rows at or past n keep nothing
+        if (r0 + t < n) {
+            const int2 kr = reinterpret_cast<const int2 *>(key_range)[(int64_t)b * L + r0 + t];
+            v = make_int2(max(kr.x, 0), min(kr.y, n - 1));
+        }
+        rr[t] = v;
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < Tk; j += blockDim.x) {
+        const int c0 = j * bk, c1 = c0 + bk - 1;
+        bool any = false, full = (i + 1) * bq <= n && (j + 1) * bk <= n;
+        for (int t = 0; t < rows; ++t) {
+            const int2 v = rr[t];
+            any = any || (v.x <= v.y && v.x <= c1 && v.y >= c0);
+            full = full && v.x <= c0 && v.y >= c1;
+        }
+        out[((int64_t)b * Tq + i) * Tk + j] = (uint8_t)(any | (full << 1));
+    }
+}
+
+hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask,
+                            const int32_t *key_range, int B, int L, int block_q, int block_k,
+                            uint8_t *out, hipStream_t stream) {
     const int Tq = (L + block_q - 1) / block_q;
     const int Tk = (L + block_k - 1) / block_k;
+    if (key_range != nullptr) {
+        hipLaunchKernelGGL(blockmask_range_kernel, dim3((unsigned)Tq, (unsigned)B), dim3(256), 0,
+                           stream, seq_lens, key_range, L, block_q, block_k, Tq, Tk, out);
+        return hipGetLastError();
+    }
     if (mask == nullptr) {
         const int64_t total = (int64_t)B * Tq * Tk;
         const int threads = 256;

@@ -219,9 +219,10 @@ template <int D> constexpr bool kVInLds = D == 128;
 // dK and dV of key tile kt (32 NW keys) of (batch entry b, head h); smem
 // holds kDkdvLds<D> elements, mbits kMaskWords words (element mask only),
 // vt this wave's 32 x D elements when kVInLds<D>.
-template <int D, int NW, int VARIANT, bool MASKED>
+template <int D, int NW, int VARIANT, int MASK>
 __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int kt, int n,
                                           bf16 *smem, uint32_t *mbits, bf16 *vt) {
+    constexpr bool MASKED = MASK != kMaskNone;
     constexpr int BKV = 32 * NW, BQ = 32, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
     constexpr bool kSoft = VARIANT != kSigmoid;
@@ -258,11 +259,10 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     const bool k_valid = key < n;
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const rsrc_t rmask = make_rsrc(MASKED ? p.mask + (int64_t)b * L * L : nullptr,
-                                   MASKED ? (int64_t)L * L : 0);
+    const MaskSource msrc = mask_source<MASK>(p.mask, p.key_range, b, L);
     // Mask words: key kl of this wave's 32 is one bit of the word of each query row.
-    const int mbit = mask_bit(kl);
-    using Mask = MaskStage<BQ, BKV, NT, false>;
+    const int mbit = key_bit<MASK>(kl);
+    using Mask = MaskStager<MASK, BQ, BKV, NT, false>;
     int mcls = kMixed;  // this wave's 32 x 32 entries of the current tile
     auto Ml = [&](int i) { return mbits + i * Mask::kWords; };
 
@@ -316,7 +316,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     auto load_tile = [&](int t, bool full) {
         stage.load(rows_rsrc(qb, t * BQ), rows_rsrc(dob, t * BQ));
         if constexpr (kSoft) stats.load(out_rows_rsrc(obase, t * BQ), lseb + t * BQ, n - t * BQ, tid);
-        if constexpr (MASKED) mstage.load(rmask, L, n, t * BQ, k0, full);
+        if constexpr (MASKED) mstage.load(msrc, n, t * BQ, k0, full);
     };
     auto store_tile = [&](int i, int t, bool full) {
         stage.store(Qs(i), dOs(i));
@@ -434,10 +434,11 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
 // dQ of query tile qt (32 NW queries) of (batch entry b, head h), visiting
 // keys 32 KB at a time.  K0, V0, K1, V1 are four separate LDS objects of
 // 32 KB rows x D each (two buffers of the K and V tiles).
-template <int D, int NW, int KB, int VARIANT, bool MASKED>
+template <int D, int NW, int KB, int VARIANT, int MASK>
 __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int qt, int n,
                                         bf16 *K0, bf16 *V0, bf16 *K1, bf16 *V1,
                                         uint32_t *mbits) {
+    constexpr bool MASKED = MASK != kMaskNone;
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
     constexpr bool kSoft = VARIANT != kSigmoid;
@@ -462,9 +463,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     const bool q_valid = qr < n;
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const rsrc_t rmask = make_rsrc(MASKED ? p.mask + (int64_t)b * L * L : nullptr,
-                                   MASKED ? (int64_t)L * L : 0);
-    using Mask = MaskStage<BQ, BK, NT, true>;
+    const MaskSource msrc = mask_source<MASK>(p.mask, p.key_range, b, L);
+    using Mask = MaskStager<MASK, BQ, BK, NT, true>;
     int mcls = kMixed;  // this wave's share of the current tile
     uint32_t *M0 = mbits, *M1 = mbits + Mask::kWords;
 
@@ -528,7 +528,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     if (kt > 0) fetch(kt, K0, V0);
     if constexpr (MASKED)
         if (kt >= 0) {
-            mstage.load(rmask, L, n, q0, kt * BK, sched.full);
+            mstage.load(msrc, n, q0, kt * BK, sched.full);
             mcls = mstage.store(M0, q0, kt * BK, n, sched.full);
         }
 #pragma unroll
@@ -545,7 +545,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
         const bool nxt_full = sched.full;
         if (nxt >= 0) fetch(nxt, Kn, Vn);
         if constexpr (MASKED)
-            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK, nxt_full);
+            if (nxt >= 0) mstage.load(msrc, n, q0, nxt * BK, nxt_full);
         // MODE 0 (no element mask): padded key rows of K and V read as zeros,
         // so dP = 0 and dS = 0 there; padded query rows are zeroed at the
         // store.  MODE 2: element mask.
@@ -561,9 +561,12 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                                 dp);
                 }
                 // s[4i + j] = S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr]; in
-                // MODE 2 that key is bit 8 j + 2 i + hh of the row's mask word.
+                // MODE 2 that key is bit key_bit(8 i + 4 hh + j) of the row's
+                // mask word: 8 j + 2 i + hh (dense) or 8 i + 4 hh + j (ranges).
+                constexpr bool kDenseBits = MASK == kMaskDense;
                 uint32_t mwk = 0u;
-                if constexpr (MODE == 2) mwk = Mc[kb2 * BQ + w * 32 + ql] >> hh;
+                if constexpr (MODE == 2)
+                    mwk = Mc[kb2 * BQ + w * 32 + ql] >> (kDenseBits ? hh : 4 * hh);
                 float dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -574,7 +577,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                         pr = sigmoid_scaled(s[r], cexp);
                     if constexpr (MODE == 2)
                         pr = __uint_as_float(__float_as_uint(pr) &
-                                             mask_select(mwk, 8 * (r & 3) + 2 * (r >> 2)));
+                                             mask_select(mwk, kDenseBits ? 8 * (r & 3) + 2 * (r >> 2)
+                                                                         : 8 * (r >> 2) + (r & 3)));
                     if constexpr (kSoft)
                         dsv[r] = pr * (dp[r] - drow);
                     else
@@ -612,42 +616,42 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
 }
 
 // ---------------------------------------------------------------- kernels
-template <int D, int NW, int VARIANT, bool MASKED>
+template <int D, int NW, int VARIANT, int MASK>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
-    __shared__ __attribute__((aligned(16))) uint32_t mbits[MASKED ? kMaskWords : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
     __shared__ __attribute__((aligned(16))) bf16 vts[kVInLds<D> ? NW * 32 * D : 1];
     constexpr int BKV = 32 * NW;
     int b, h, kt, n;
     if (!tile_item<BKV>(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt, n)) return;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, kt, n, smem, mbits, vts + w * 32 * D);
+    dkdv_tile<D, NW, VARIANT, MASK>(p, b, h, kt, n, smem, mbits, vts + w * 32 * D);
 }
 
-template <int D, int NW, int KB, int VARIANT, bool MASKED>
+template <int D, int NW, int KB, int VARIANT, int MASK>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dq_kernel(const AttnParams p) {
     constexpr int kTile = 32 * KB * D;
     __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
-    __shared__ __attribute__((aligned(16))) uint32_t mbits[MASKED ? kMaskWords : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
     constexpr int BQ = 32 * NW;
     int b, h, qt, n;
     if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
-    dq_tile<D, NW, KB, VARIANT, MASKED>(p, b, h, qt, n, K0, V0, K1, V1, mbits);
+    dq_tile<D, NW, KB, VARIANT, MASK>(p, b, h, qt, n, K0, V0, K1, V1, mbits);
 }
 
 // dK/dV and dQ in one launch: both kinds of tile of a (batch entry, head)
 // pair are dealt out together, longest sequences first, so the two share one
 // ramp-up and one tail.  Needs the same 32 NW rows for the key tiles of
 // dK/dV and the query tiles of dQ.
-template <int D, int NW, int KB, int VARIANT, bool MASKED>
+template <int D, int NW, int KB, int VARIANT, int MASK>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
     constexpr int kTile = 32 * KB * D;
     __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
-    __shared__ __attribute__((aligned(16))) uint32_t mbits[MASKED ? kMaskWords : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
     constexpr int R = 32 * NW;
     const int nt = (p.L + R - 1) / R;
     int b, h, kind, t, n;
@@ -658,10 +662,10 @@ bwd_kernel(const AttnParams p) {
         static_assert(!kVInLds<D> || (KB == 1 && NW <= 4), "V rows need one dQ buffer per wave");
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         bf16 *vt = w == 0 ? K0 : w == 1 ? V0 : w == 2 ? K1 : V1;
-        dkdv_tile<D, NW, VARIANT, MASKED>(p, b, h, t, n, smem, mbits, vt);
+        dkdv_tile<D, NW, VARIANT, MASK>(p, b, h, t, n, smem, mbits, vt);
     }
     else
-        dq_tile<D, NW, KB, VARIANT, MASKED>(p, b, h, t, n, K0, V0, K1, V1, mbits);
+        dq_tile<D, NW, KB, VARIANT, MASK>(p, b, h, t, n, K0, V0, K1, V1, mbits);
 }
 
 // Waves per workgroup: 32 NW keys per dK/dV workgroup must divide block_k,
@@ -678,15 +682,18 @@ static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
     const int nw = dkdv_waves(p);
     const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
-#define SIGATTN_DKDV_CASE(NW_)                                                          \
-    if (nw == NW_) {                                                                     \
-        if (p.mask != nullptr)                                                           \
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, VARIANT, true>), grid, block, 0, \
-                               stream, p);                                               \
-        else                                                                             \
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, VARIANT, false>), grid, block,   \
-                               0, stream, p);                                            \
-        return hipGetLastError();                                                        \
+#define SIGATTN_DKDV_CASE(NW_)                                                                 \
+    if (nw == NW_) {                                                                           \
+        if (p.mask != nullptr)                                                                 \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, VARIANT, kMaskDense>), grid, block, 0, \
+                               stream, p);                                                     \
+        else if (p.key_range != nullptr)                                                       \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, VARIANT, kMaskRange>), grid, block, 0, \
+                               stream, p);                                                     \
+        else                                                                                   \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, VARIANT, kMaskNone>), grid, block, 0,  \
+                               stream, p);                                                     \
+        return hipGetLastError();                                                              \
     }
     SIGATTN_DKDV_CASE(4)
     SIGATTN_DKDV_CASE(2)
@@ -700,16 +707,19 @@ static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     const int nw = dq_waves(p), kb = dq_key_blocks(p);
     const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
     dim3 block(64 * nw);
-#define SIGATTN_DQ_CASE(NW_, KB_)                                                        \
-    if constexpr (D == 64 || KB_ == 1)                                                   \
-    if (nw == NW_ && kb == KB_) {                                                        \
-        if (p.mask != nullptr)                                                           \
-            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, VARIANT, true>), grid, block, \
-                               0, stream, p);                                            \
-        else                                                                             \
-            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, VARIANT, false>), grid,       \
-                               block, 0, stream, p);                                     \
-        return hipGetLastError();                                                        \
+#define SIGATTN_DQ_CASE(NW_, KB_)                                                                 \
+    if constexpr (D == 64 || KB_ == 1)                                                            \
+    if (nw == NW_ && kb == KB_) {                                                                 \
+        if (p.mask != nullptr)                                                                    \
+            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, VARIANT, kMaskDense>), grid, block, 0, \
+                               stream, p);                                                        \
+        else if (p.key_range != nullptr)                                                          \
+            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, VARIANT, kMaskRange>), grid, block, 0, \
+                               stream, p);                                                        \
+        else                                                                                      \
+            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, VARIANT, kMaskNone>), grid, block, 0,  \
+                               stream, p);                                                        \
+        return hipGetLastError();                                                                 \
     }
     SIGATTN_DQ_CASE(4, 2)
     SIGATTN_DQ_CASE(4, 1)
@@ -730,16 +740,19 @@ static hipError_t launch_bwd_d(const AttnParams &p, hipStream_t stream) {
     }
     const dim3 grid = tile_grid(2 * ((p.L + 32 * nw - 1) / (32 * nw)), p.B, p.H);
     dim3 block(64 * nw);
-#define SIGATTN_BWD_CASE(NW_, KB_)                                                       \
-    if constexpr (D == 64 || KB_ == 1)                                                   \
-    if (nw == NW_ && kb == KB_) {                                                        \
-        if (p.mask != nullptr)                                                           \
-            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, VARIANT, true>), grid, block, 0, \
-                               stream, p);                                               \
-        else                                                                             \
-            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, VARIANT, false>), grid, block,   \
-                               0, stream, p);                                            \
-        return hipGetLastError();                                                        \
+#define SIGATTN_BWD_CASE(NW_, KB_)                                                             \
+    if constexpr (D == 64 || KB_ == 1)                                                         \
+    if (nw == NW_ && kb == KB_) {                                                              \
+        if (p.mask != nullptr)                                                                 \
+            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, VARIANT, kMaskDense>), grid, block, 0, \
+                               stream, p);                                                     \
+        else if (p.key_range != nullptr)                                                       \
+            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, VARIANT, kMaskRange>), grid, block, 0, \
+                               stream, p);                                                     \
+        else                                                                                   \
+            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, VARIANT, kMaskNone>), grid, block, 0,  \
+                               stream, p);                                                     \
+        return hipGetLastError();                                                              \
     }
     SIGATTN_BWD_CASE(4, 2)
     SIGATTN_BWD_CASE(4, 1)

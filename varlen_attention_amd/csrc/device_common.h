@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sigattn {
 
 typedef __bf16 bf16;
@@ -377,6 +379,25 @@ __device__ __forceinline__ uint32_t mask_select(uint32_t word, int pos) {
     return (uint32_t)__builtin_amdgcn_sbfe((int)word, pos, 1);
 }
 
+// Element-mask kinds of the attention kernels: none, dense bytes [L, L] per
+// batch entry, or one key range [lo, hi] per query row (causal, packed
+// documents, sliding windows: the masks whose rows are intervals).
+enum { kMaskNone = 0, kMaskDense = 1, kMaskRange = 2 };
+
+// One batch entry's element mask, in the form the kernel was built for.
+struct MaskSource {
+    rsrc_t bytes;          // dense: exactly its L x L bytes
+    const int32_t *range;  // ranges: [L, 2] (lo, hi) per query row
+    int L;
+};
+
+// Where key t (0..31) of a mask word sits: dense words keep the order in
+// which the byte test delivers them, range words the natural order.
+template <int MASK>
+__device__ __forceinline__ constexpr int key_bit(int t) {
+    return MASK == kMaskDense ? mask_bit(t) : t;
+}
+
 // What a wave's share of a masked tile needs, from the OR and the AND of the
 // mask words its lanes hold: kSkip (no entry kept: no work at all), kDense
 // (every entry kept) or kMixed.
@@ -410,17 +431,17 @@ struct MaskStage {
         act = (lane >> 5) < kWordsPerWave;
     }
 
-    // rmask covers exactly the batch entry's L x L mask; L * L fits in int.
-    // Words of rows or keys at or past n are not read (store clears them),
-    // nor any word of a full tile (every entry valid: store writes ones).
-    __device__ __forceinline__ void load(rsrc_t rmask, int L, int n, int r0, int k0, bool full) {
+    // src.bytes covers exactly the batch entry's L x L mask; L * L fits in
+    // int.  Words of rows or keys at or past n are not read (store clears
+    // them), nor any word of a full tile (every entry valid: store writes ones).
+    __device__ __forceinline__ void load(const MaskSource &src, int n, int r0, int k0, bool full) {
         lo = hi = make_uint4(0u, 0u, 0u, 0u);
-        const int row = r0 + r, key = k0 + 32 * wi;
+        const int row = r0 + r, key = k0 + 32 * wi, L = src.L;
         if (full || !act || row >= n || key >= n) return;
         const int off = row * L + key;
         if (off + 32 <= L * L) {
-            lo = buffer_load16(rmask, off);
-            hi = buffer_load16(rmask, off + 16);
+            lo = buffer_load16(src.bytes, off);
+            hi = buffer_load16(src.bytes, off + 16);
         } else {
             // The last row's window runs past the end of the mask, where the
             // range check would drop a 16-byte load whole: byte by byte, the
@@ -428,7 +449,7 @@ struct MaskStage {
             uint32_t x[8] = {};
 #pragma unroll
             for (int t = 0; t < 32; ++t)
-                x[t >> 2] |= (uint32_t)buffer_load_u8(rmask, off + t) << (8 * (t & 3));
+                x[t >> 2] |= (uint32_t)buffer_load_u8(src.bytes, off + t) << (8 * (t & 3));
             lo = make_uint4(x[0], x[1], x[2], x[3]);
             hi = make_uint4(x[4], x[5], x[6], x[7]);
         }
@@ -458,5 +479,69 @@ struct MaskStage {
         return mask_class(bits, act ? bits : 0xffffffffu);
     }
 };
+
+// The same tile words from key ranges: the kept keys of a row are the run
+// [max(lo, 0), min(hi, n - 1)], so a word is one shifted run of ones (natural
+// key order) and the mask itself is never read.  Same thread mapping and
+// LDS layout as MaskStage.
+template <int ROWS, int KEYS, int NT, bool WAVE_ROWS>
+struct RangeStage {
+    static constexpr int kWordsPerRow = KEYS / 32;
+    static constexpr int kWords = ROWS * kWordsPerRow;
+    static constexpr int kWordsPerWave = WAVE_ROWS ? kWordsPerRow : 1;
+    static_assert(kWordsPerWave <= 2, "at most one word per lane");
+    static_assert(WAVE_ROWS ? ROWS == NT / 2 : (ROWS == 32 && kWordsPerRow == NT / 64),
+                  "one wave per 32 rows, or per 32 keys");
+    int lo, hi;  // this lane's row keeps keys [lo, hi] (empty when lo > hi)
+    int r, wi;
+    bool act;
+
+    __device__ __forceinline__ void init(int tid) {
+        const int lane = tid & 63, w = tid >> 6;
+        r = (WAVE_ROWS ? 32 * w : 0) + (lane & 31);
+        wi = (WAVE_ROWS ? 0 : w) + (lane >> 5);
+        act = (lane >> 5) < kWordsPerWave;
+    }
+
+    __device__ __forceinline__ void load(const MaskSource &src, int n, int r0, int k0, bool full) {
+        lo = 1;
+        hi = 0;
+        const int row = r0 + r;
+        if (full || !act || row >= n) return;
+        const int2 kr = *reinterpret_cast<const int2 *>(src.range + 2 * row);
+        lo = max(kr.x, 0);
+        hi = min(kr.y, n - 1);
+    }
+
+    __device__ __forceinline__ int store(uint32_t *words, int r0, int k0, int n, bool full) const {
+        if (full) {
+            if (act) words[wi * ROWS + r] = 0xffffffffu;
+            return kDense;
+        }
+        const int base = k0 + 32 * wi;
+        const int a = max(lo, base), e = min(hi, base + 31);
+        const uint32_t bits = a > e ? 0u : ((2u << (e - a)) - 1u) << (a - base);
+        if (act) words[wi * ROWS + r] = bits;
+        return mask_class(bits, act ? bits : 0xffffffffu);
+    }
+};
+
+// The stager of a mask kind (none stages nothing; MaskStage is a placeholder).
+template <int MASK, int ROWS, int KEYS, int NT, bool WAVE_ROWS>
+using MaskStager = typename std::conditional<MASK == kMaskRange,
+                                             RangeStage<ROWS, KEYS, NT, WAVE_ROWS>,
+                                             MaskStage<ROWS, KEYS, NT, WAVE_ROWS>>::type;
+
+// The batch entry's mask source of a kernel of kind MASK.
+template <int MASK>
+__device__ __forceinline__ MaskSource mask_source(const uint8_t *mask, const int32_t *key_range,
+                                                  int b, int L) {
+    MaskSource m;
+    m.bytes = make_rsrc(MASK == kMaskDense ? mask + (int64_t)b * L * L : nullptr,
+                        MASK == kMaskDense ? (int64_t)L * L : 0);
+    m.range = MASK == kMaskRange ? key_range + (int64_t)b * L * 2 : nullptr;
+    m.L = L;
+    return m;
+}
 
 }  // namespace sigattn

@@ -78,9 +78,10 @@ struct KVStage {
 
 }  // namespace
 
-template <int D, int VARIANT, int NW, int KB, bool MASKED>
+template <int D, int VARIANT, int NW, int KB, int MASK>
 __global__ void __launch_bounds__(64 * NW, 2)
 fwd_kernel(const AttnParams p) {
+    constexpr bool MASKED = MASK != kMaskNone;
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
     constexpr int KS = D / 16;  // MFMA k-steps over the head dimension
     constexpr int DB = D / 32;  // 32-wide blocks of the head dimension
@@ -120,8 +121,7 @@ fwd_kernel(const AttnParams p) {
     const int ql = lane & 31, hh = lane >> 5;
     const int qr = q0 + w * 32 + ql;  // this lane's query row
     const bool q_valid = qr < n;
-    const rsrc_t rmask = make_rsrc(MASKED ? p.mask + (int64_t)b * L * L : nullptr,
-                                   MASKED ? (int64_t)L * L : 0);
+    const MaskSource msrc = mask_source<MASK>(p.mask, p.key_range, b, L);
     // Per-lane offsets of the transposing V reads (see lds_read_tr4).
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -163,7 +163,7 @@ fwd_kernel(const AttnParams p) {
     KVStage<D, BK, NT> stage;
     stage.init(p.sl, tid);
     stage.load(rows_rsrc(kb, 0), rows_rsrc(vb, 0));
-    MaskStage<BQ, BK, NT, true> mstage;
+    MaskStager<MASK, BQ, BK, NT, true> mstage;
     int mcls = kMixed;  // this wave's share of the current tile (element mask)
     if constexpr (MASKED) mstage.init(tid);
     TileSchedule<BK> sched;
@@ -172,7 +172,7 @@ fwd_kernel(const AttnParams p) {
     const bool kt_full = sched.full;
     if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
     if constexpr (MASKED)
-        if (kt >= 0) mstage.load(rmask, L, n, q0, kt * BK, kt_full);
+        if (kt >= 0) mstage.load(msrc, n, q0, kt * BK, kt_full);
     int buf = 0;
     stage.store(Ks[0], Vs[0]);
     if constexpr (MASKED)
@@ -191,7 +191,7 @@ fwd_kernel(const AttnParams p) {
         const bool nxt_full = sched.full;
         if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
         if constexpr (MASKED)
-            if (nxt >= 0) mstage.load(rmask, L, n, q0, nxt * BK, nxt_full);
+            if (nxt >= 0) mstage.load(msrc, n, q0, nxt * BK, nxt_full);
         const bf16 *Kc = Ks[buf];
         const bf16 *Vc = Vs[buf];
 
@@ -220,7 +220,8 @@ fwd_kernel(const AttnParams p) {
             }
             // Per-element validity.  MODE 1: compared, without branches.
             // MODE 2: the tile's mask bits (validity folded in); key
-            // 8 i + 4 hh + j of a 32-key block is bit 8 j + 2 i + hh.
+            // 8 i + 4 hh + j of a 32-key block is bit key_bit(8 i + 4 hh + j):
+            // 8 j + 2 i + hh (dense) or 8 i + 4 hh + j (ranges).
             bool ok[KB][16];
             if constexpr (MODE == 1) {
 #pragma unroll
@@ -232,12 +233,15 @@ fwd_kernel(const AttnParams p) {
                     }
             }
             uint32_t mw[KB];  // this lane's row of the tile's mask words
+            constexpr bool kDenseBits = MASK == kMaskDense;
             if constexpr (MODE == 2) {
 #pragma unroll
-                for (int kb2 = 0; kb2 < KB; ++kb2) mw[kb2] = Ms[buf][kb2 * BQ + w * 32 + ql] >> hh;
+                for (int kb2 = 0; kb2 < KB; ++kb2)
+                    mw[kb2] = Ms[buf][kb2 * BQ + w * 32 + ql] >> (kDenseBits ? hh : 4 * hh);
             }
             auto keep = [&](int kb2, int r) {
-                return mask_select(mw[kb2], 8 * (r & 3) + 2 * (r >> 2));
+                return mask_select(mw[kb2], kDenseBits ? 8 * (r & 3) + 2 * (r >> 2)
+                                                       : 8 * (r >> 2) + (r & 3));
             };
 
             float m_use = 0.0f;
@@ -345,15 +349,18 @@ static hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
     const int bq = 32 * nw;
     const dim3 grid = tile_grid((p.L + bq - 1) / bq, p.B, p.H);
     dim3 block(64 * nw);
-#define SIGATTN_FWD_CASE(NW_, KB_)                                                         \
-    if (nw == NW_ && kb == KB_) {                                                          \
-        if (p.mask != nullptr)                                                             \
-            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, true>), grid, block, 0,   \
-                               stream, p);                                                 \
-        else                                                                               \
-            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, false>), grid, block, 0,  \
-                               stream, p);                                                 \
-        return hipGetLastError();                                                          \
+#define SIGATTN_FWD_CASE(NW_, KB_)                                                             \
+    if (nw == NW_ && kb == KB_) {                                                              \
+        if (p.mask != nullptr)                                                                 \
+            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, kMaskDense>), grid, block, 0, \
+                               stream, p);                                                     \
+        else if (p.key_range != nullptr)                                                       \
+            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, kMaskRange>), grid, block, 0, \
+                               stream, p);                                                     \
+        else                                                                                   \
+            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, kMaskNone>), grid, block, 0,  \
+                               stream, p);                                                     \
+        return hipGetLastError();                                                              \
     }
     SIGATTN_FWD_CASE(4, 2)
     SIGATTN_FWD_CASE(4, 1)

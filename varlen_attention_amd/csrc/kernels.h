@@ -15,6 +15,7 @@ struct AttnParams {
     const int32_t *seq_lens;        // [B]
     const uint8_t *block_mask;      // [B, Tq, Tk] or null
     const uint8_t *mask;            // [B, L, L] or null
+    const int32_t *key_range;       // [B, L, 2] or null (at most one of mask, key_range)
     int64_t sb, sh, sl;             // input strides (elements)
     int64_t osb, osh, osl;          // output strides (elements)
     int B, H, L, d;
@@ -23,8 +24,9 @@ struct AttnParams {
     int bias_mode, variant;
 };
 
-hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask, int B, int L,
-                            int block_q, int block_k, uint8_t *out, hipStream_t stream);
+hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask,
+                            const int32_t *key_range, int B, int L, int block_q, int block_k,
+                            uint8_t *out, hipStream_t stream);
 hipError_t launch_fwd(const AttnParams &p, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnParams &p, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnParams &p, hipStream_t stream);
