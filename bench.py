@@ -293,15 +293,18 @@ SUITE_SETTLE_S = 0.3
 FLUSH_BYTES = 1 << 30  # larger than the last-level cache, so each cold rep starts empty
 
 
-def suite_bytes(kernel: str, w, variant: int, masked: bool) -> float:
+def suite_bytes(kernel: str, w, variant: int, masked, ranges: bool = False) -> float:
     """Algorithmic HBM bytes of one launch: valid rows of the inputs read once,
     every row of the outputs written once; the softmax variants add O and the
-    log-sum-exp rows; the block-mask builder reads the element mask once."""
+    log-sum-exp rows; the block-mask builder reads the element mask once (or
+    the key ranges, 8 bytes per row)."""
     valid = float(np.clip(w.seq_lens, 0, w.L).sum()) * w.H
     every = float(w.B) * w.L * w.H
     row = 2.0 * w.d
     if kernel == "blockmask":
         tiles = float(w.B) * (-(-w.L // w.block_q)) * (-(-w.L // w.block_k))
+        if ranges:
+            return 8.0 * w.B * w.L + tiles
         return (float(w.B) * w.L * w.L if masked else 4.0 * w.B) + tiles
     soft = variant != 0
     if kernel == "fwd":
@@ -377,28 +380,31 @@ def run_suite(args) -> int:
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
     def case(label, w, variant=syn.SIGMOID, bias=syn.BIAS_LOG_SEQLEN, block=128, kernels=("fwd", "bwd"),
-             cold=True):
-        """Times blockmask_build, fwd and bwd of workload w; one table row each."""
+             cold=True, ranges=False):
+        """Times blockmask_build, fwd and bwd of workload w; one table row each.
+        ranges: the element mask as key ranges instead of the dense mask."""
         log(f"case {label}: B={w.B} H={w.H} L={w.L} d={w.d} block={block} variant={variant}")
         q, k, v = gpu(w.q), gpu(w.k), gpu(w.v)
         do = gpu(w.do) if w.do is not None else None
         n = torch.from_numpy(w.seq_lens).to(dev)
-        mask = torch.from_numpy(w.mask).to(dev) if w.mask is not None else None
+        mask = torch.from_numpy(w.mask).to(dev) if w.mask is not None and not ranges else None
+        kr = torch.from_numpy(w.key_range).to(dev) if ranges else None
+        form = {"key_range": kr} if ranges else {"mask": mask}
         w.block_q = w.block_k = block
-        bm = va.blockmask_build(n, w.L, block, block, mask=mask)
-        tiles = int(bm.sum().item()) * w.H
+        bm = va.blockmask_build(n, w.L, block, block, **form)
+        tiles = int((bm != 0).sum().item()) * w.H  # kept tiles (entries are 0, 1 or 3)
         pairs = w.valid_pairs * w.H
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev) if variant else None
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         fns = {
-            "blockmask": lambda: va.blockmask_build(n, w.L, block, block, mask=mask, out=bm),
-            "fwd": lambda: va.sigattn_fwd(q, k, v, n, block_mask=bm, mask=mask, bias=bias,
+            "blockmask": lambda: va.blockmask_build(n, w.L, block, block, out=bm, **form),
+            "fwd": lambda: va.sigattn_fwd(q, k, v, n, block_mask=bm, bias=bias,
                                           variant=variant, block_q=block, block_k=block, out=o,
-                                          lse=lse),
-            "bwd": lambda: va.sigattn_bwd(q, k, v, do, n, block_mask=bm, mask=mask, bias=bias,
+                                          lse=lse, **form),
+            "bwd": lambda: va.sigattn_bwd(q, k, v, do, n, block_mask=bm, bias=bias,
                                           variant=variant, block_q=block, block_k=block, dq=dq,
-                                          dk=dk, dv=dv, o=o if variant else None, lse=lse),
+                                          dk=dk, dv=dv, o=o if variant else None, lse=lse, **form),
         }
         fns["fwd"]()
         torch.cuda.synchronize()
@@ -412,7 +418,7 @@ def run_suite(args) -> int:
             r = {"case": label, "kernel": kern, "warm_med_us": med,
                  "warm_min_us": float(warm[:, j].min()),
                  "cold_med_us": float(np.median(cold_t)) if cold else None,
-                 "gbs": suite_bytes(kern, w, variant, mask is not None) / (med * 1e-6) / 1e9}
+                 "gbs": suite_bytes(kern, w, variant, mask is not None, ranges) / (med * 1e-6) / 1e9}
             if kern in per_pair:
                 r["valid_tf"] = per_pair[kern] * pairs / (med * 1e-6) / 1e12
                 r["tile_tf"] = per_pair[kern] * tiles * block * block / (med * 1e-6) / 1e12
@@ -425,7 +431,7 @@ def run_suite(args) -> int:
                      "valid_tf": flops / (np.median(tot) * 1e-6) / 1e12,
                      "tile_tf": flops / pairs * tiles * block * block / (np.median(tot) * 1e-6) / 1e12,
                      "gbs": None})
-        del q, k, v, do, o, dq, dk, dv, mask, bm
+        del q, k, v, do, o, dq, dk, dv, mask, kr, bm
         torch.cuda.empty_cache()
         return rows[-1]
 
@@ -458,6 +464,7 @@ def run_suite(args) -> int:
     # Long packed documents: causal mask within documents, d = 128.
     wl = syn.long_packed_docs(args.seed, tensors=("q", "k", "v", "do"))
     case("long packed documents, causal mask", wl)
+    case("long packed documents, causal key ranges", wl, ranges=True)
     timer.close()
 
     print(f"Measurement suite on {props.name} ({props.multi_processor_count} CUs), seed {args.seed}.")

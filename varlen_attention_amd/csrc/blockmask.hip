@@ -52,37 +52,69 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint64_t total = (uint64_t)gridDim.y * (uint64_t)L * (uint64_t)L;
     uint32_t bits = 0, zbits = 0;
-    if (r_lo < r_hi && c_lo < c_hi) {
-        for (int r = r_lo + wave; r < r_hi; r += 4) {
-            const uint64_t row = ((uint64_t)b * L + r) * (uint64_t)L;
-            const uint64_t lo = row + c_lo, hi = row + c_hi;
-            for (uint64_t a = (lo & ~(uint64_t)15) + 16u * lane; a < hi; a += 16u * 64) {
-                uint8_t bytes[16];
-                if (a + 16 <= total) {
-                    uint4 u = *reinterpret_cast<const uint4 *>(mask + a);
-                    if ((u.x | u.y | u.z | u.w) == 0u) {
-                        // All sixteen invalid: the (at most two) tiles of the
-                        // in-range bytes are not full.
-                        const int c0 = (int)((a > lo ? a : lo) - row);
-                        const int c1 = (int)((a + 16 < hi ? a + 16 : hi) - row) - 1;
-                        zbits |= (1u << ((c0 >> bk_shift) - j0)) | (1u << ((c1 >> bk_shift) - j0));
-                        continue;
-                    }
-                    *reinterpret_cast<uint4 *>(bytes) = u;
-                } else {
-                    for (int t = 0; t < 16; ++t) bytes[t] = (a + t < total) ? mask[a + t] : 0;
-                }
+    // One 16-byte chunk at byte address a of row `row` (columns [lo, hi) of
+    // the scan): non-zero bytes mark their tile kept, zero bytes not full.
+    auto chunk = [&](uint4 u, uint64_t a, uint64_t row, uint64_t lo, uint64_t hi) {
+        const uint32_t nz = u.x | u.y | u.z | u.w;
+        const uint64_t s0 = a > lo ? a : lo, s1 = a + 16 < hi ? a + 16 : hi;  // in-range part
+        const int t0 = (int)((s0 - row) >> bk_shift) - j0;
+        const int t1 = (int)((s1 - 1 - row) >> bk_shift) - j0;
+        if (nz == 0u) {  // every byte invalid
+            zbits |= (1u << t0) | (1u << t1);
+            return;
+        }
+        const uint32_t zero_byte = ((u.x - 0x01010101u) & ~u.x) | ((u.y - 0x01010101u) & ~u.y) |
+                                   ((u.z - 0x01010101u) & ~u.z) | ((u.w - 0x01010101u) & ~u.w);
+        if ((zero_byte & 0x80808080u) == 0u && t0 == t1) {  // every byte valid, one tile
+            bits |= 1u << t0;
+            return;
+        }
+        uint8_t bytes[16];
+        *reinterpret_cast<uint4 *>(bytes) = u;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    const uint64_t p = a + t;
-                    if (p >= lo && p < hi) {
-                        const int c = (int)(p - row);
-                        const uint32_t f = 1u << ((c >> bk_shift) - j0);
-                        if (bytes[t] != 0)
-                            bits |= f;
-                        else
-                            zbits |= f;
+        for (int t = 0; t < 16; ++t) {
+            const uint64_t p = a + t;
+            if (p >= lo && p < hi) {
+                const uint32_t f = 1u << ((int)((p - row) >> bk_shift) - j0);
+                if (bytes[t] != 0)
+                    bits |= f;
+                else
+                    zbits |= f;
+            }
+        }
+    };
+    if (r_lo < r_hi && c_lo < c_hi) {
+        // Four rows per wave in flight: their loads are issued before any is
+        // examined (eight measured slower).  Chunks that would run past the end of the mask are
+        // read byte by byte (bytes past the end read 0).
+        for (int rb = r_lo + wave; rb < r_hi; rb += 16) {
+            uint4 u[4];
+            uint64_t arow[4], alo[4], ahi[4], a0[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = rb + 4 * t;
+                arow[t] = ((uint64_t)b * L + (r < r_hi ? r : r_lo)) * (uint64_t)L;
+                alo[t] = arow[t] + c_lo;
+                ahi[t] = r < r_hi ? arow[t] + c_hi : 0;  // rows past r_hi: nothing
+                a0[t] = (alo[t] & ~(uint64_t)15) + 16u * lane;
+                u[t] = make_uint4(0u, 0u, 0u, 0u);
+                if (a0[t] < ahi[t] && a0[t] + 16 <= total)
+                    u[t] = *reinterpret_cast<const uint4 *>(mask + a0[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                for (uint64_t a = a0[t]; a < ahi[t]; a += 16u * 64) {
+                    uint4 v = u[t];
+                    if (a != a0[t] || a + 16 > total) {
+                        if (a + 16 <= total) {
+                            v = *reinterpret_cast<const uint4 *>(mask + a);
+                        } else {
+                            uint8_t bb[16];
+                            for (int e = 0; e < 16; ++e) bb[e] = (a + e < total) ? mask[a + e] : 0;
+                            v = *reinterpret_cast<const uint4 *>(bb);
+                        }
                     }
+                    chunk(v, a, arow[t], alo[t], ahi[t]);
                 }
             }
         }
