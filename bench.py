@@ -461,6 +461,39 @@ def run_suite(args) -> int:
                                lo=0, hi=0, seq_lens=lens, tensors=("q", "k", "v", "do"))
         case(label, wp, cold=False)
     del w, wb
+    # Differential attention at the single-cell shapes: both maps in one
+    # launch, against two softmax forward launches (4 d flops per pair and map).
+    wd = syn.single_cell(args.seed, tensors=("q", "k", "v"))
+    rng = np.random.default_rng(args.seed + 1)
+    q1, k1, v = gpu(wd.q), gpu(wd.k), gpu(wd.v)
+    q2, k2 = gpu(syn.random_tensor(rng, wd.q.shape)), gpu(syn.random_tensor(rng, wd.k.shape))
+    n = torch.from_numpy(wd.seq_lens).to(dev)
+    bm = va.blockmask_build(n, wd.L, 128, 128)
+    o, o2 = torch.empty_like(q1), torch.empty_like(q1)
+    label = "single cell, differential (lambda 0.8)"
+    log(f"case {label}")
+    fns = [lambda: va.sigattn_diff_fwd(q1, k1, q2, k2, v, n, 0.8, block_mask=bm, out=o),
+           lambda: va.sigattn_fwd(q1, k1, v, n, block_mask=bm, variant=syn.SOFTMAX, bias=0, out=o),
+           lambda: va.sigattn_fwd(q2, k2, v, n, block_mask=bm, variant=syn.SOFTMAX, bias=0,
+                                  out=o2)]
+    warm = timer.steps(fns)
+    cold = timer.cold(fns[0], flush)
+    tiles = int((bm != 0).sum().item()) * wd.H
+    pairs = wd.valid_pairs * wd.H
+    for j, kern in enumerate(("diff fwd", "softmax fwd (map 1)", "softmax fwd (map 2)")):
+        med = float(np.median(warm[:, j]))
+        maps = 2 if j == 0 else 1
+        algo = ((3 + 2 * (maps - 1)) * float(np.clip(wd.seq_lens, 0, wd.L).sum()) * wd.H
+                + float(wd.B) * wd.L * wd.H) * 2.0 * wd.d
+        rows.append({"case": label, "kernel": kern, "warm_med_us": med,
+                     "warm_min_us": float(warm[:, j].min()),
+                     "cold_med_us": float(np.median(cold)) if j == 0 else None,
+                     "valid_tf": 4.0 * wd.d * maps * pairs / (med * 1e-6) / 1e12,
+                     "tile_tf": 4.0 * wd.d * maps * tiles * 128 * 128 / (med * 1e-6) / 1e12,
+                     "gbs": algo / (med * 1e-6) / 1e9})
+        log(f"  {kern}: warm median {med:.2f} us")
+    del q1, k1, q2, k2, v, o, o2, bm
+    torch.cuda.empty_cache()
     # Long packed documents: causal mask within documents, d = 128.
     wl = syn.long_packed_docs(args.seed, tensors=("q", "k", "v", "do"))
     case("long packed documents, causal mask", wl)

@@ -213,6 +213,36 @@ int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, con
                    const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
                    int32_t bias_mode, int32_t variant, void *dq, void *stream);
 
+/*
+ * sigattn_diff_fwd - differential attention forward ("Differential
+ * Transformer" note, "How differential attention works"): two softmax maps
+ * over one value tensor, the second subtracted with the scalar lambda,
+ *   o_r = sum_c softmax_c(s1[r, c]) v_c - lambda * sum_c softmax_c(s2[r, c]) v_c,
+ *   s_i[r, c] = scale * <q_i r, k_i c> + beta,
+ * over the valid (r, c) of the definition above (the same masks for both
+ * maps).  Both maps run through one tile loop: each V tile is loaded once and
+ * feeds both.  lambda is the layer's scalar as a plain input (its
+ * reparametrisation and the per-head normalisation after the attention
+ * belong to the model, not here).
+ *
+ *   q1, k1, q2, k2, v  [device] bf16 [B, H, L, d] (input layout), as q, k, v
+ *                      of sigattn_fwd
+ *   seq_lens, block_mask, mask, key_range, bias_mode: as for sigattn_fwd
+ *                      (the bias cancels in each softmax; it shifts the LSEs)
+ *   lambda             [host] finite float
+ *   o                  [device] bf16 [B, H, L, d] (output layout), fully
+ *                      written; padded rows and rows without a valid key are 0
+ *   lse1, lse2         [device] fp32 [B, H, L] contiguous, or NULL: each map's
+ *                      log-sum-exp, as sigattn_fwd's SOFTMAX lse
+ * Errors: as sigattn_fwd; INVALID_ARG for a non-finite lambda, ALIGNMENT for
+ * lse1 or lse2 not 4-byte aligned.
+ */
+int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
+                     const void *k2, const void *v, const int32_t *seq_lens,
+                     const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
+                     int32_t bias_mode, float lambda, void *o, float *lse1, float *lse2,
+                     void *stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *sigattn_last_error(void);
 

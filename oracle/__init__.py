@@ -293,3 +293,26 @@ def bwd_rows(q, k, v, do, seq_lens, b: int, h: int, q_rows, k_rows, mask=None,
             dk[i] = gk[c - lo]
             dv[i] = gv[c - lo]
     return dq, dk, dv
+
+
+def diff_fwd(q1, k1, q2, k2, v, seq_lens, lam: float, mask=None, bias=BIAS_NONE, scale=None,
+             precision="f64", threads=None, heads=None, key_range=None):
+    """Differential attention ("Differential Transformer" note, "How
+    differential attention works"): (softmax(S1) - lam softmax(S2)) V, each map
+    the SOFTMAX of ``fwd`` over the same valid (r, c).  Returns
+    (o, lse1, lse2)."""
+    o1, lse1 = fwd(q1, k1, v, seq_lens, mask=mask, bias=bias, variant=SOFTMAX, scale=scale,
+                   precision=precision, threads=threads, heads=heads, key_range=key_range)
+    o2, lse2 = fwd(q2, k2, v, seq_lens, mask=mask, bias=bias, variant=SOFTMAX, scale=scale,
+                   precision=precision, threads=threads, heads=heads, key_range=key_range)
+    return o1 - lam * o2, lse1, lse2
+
+
+def diff_fwd_rows(q1, k1, q2, k2, v, seq_lens, lam: float, b: int, h: int, rows, mask=None,
+                  bias=BIAS_NONE, scale=None, precision="f64", key_range=None):
+    """Selected output rows of one head of diff_fwd: o [len(rows), d]."""
+    o1, _ = fwd_rows(q1, k1, v, seq_lens, b, h, rows, mask=mask, bias=bias, variant=SOFTMAX,
+                     scale=scale, precision=precision, key_range=key_range)
+    o2, _ = fwd_rows(q2, k2, v, seq_lens, b, h, rows, mask=mask, bias=bias, variant=SOFTMAX,
+                     scale=scale, precision=precision, key_range=key_range)
+    return o1 - lam * o2

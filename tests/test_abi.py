@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["blockmask_build", "sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq",
-         "sigattn_last_error"])
+         "sigattn_diff_fwd", "sigattn_last_error"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -103,6 +103,23 @@ def test_backward_argument_errors(lib):
                               FAKE, None) == va.ERR_INVALID_ARG
     assert lib.sigattn_bwd_dkdv(ctypes.byref(sh), *args, None, None, FAKE, None, None, None, 1, 0,
                                 FAKE, None, None) == va.ERR_INVALID_ARG
+
+
+def test_diff_forward_argument_errors(lib):
+    import varlen_attention_amd as va
+    sh = _shape(va)
+
+    def diff(shape=sh, q2=FAKE, lam=0.5, lse2=None, mask=None, kr=None, bm=None):
+        return lib.sigattn_diff_fwd(ctypes.byref(shape), FAKE, FAKE, q2, FAKE, FAKE, FAKE, bm,
+                                    mask, kr, 0, lam, FAKE, None, lse2, None)
+
+    assert diff(q2=None) == va.ERR_INVALID_ARG
+    assert diff(lam=float("nan")) == va.ERR_INVALID_ARG
+    assert diff(lam=float("inf")) == va.ERR_INVALID_ARG
+    assert diff(lse2=ctypes.c_void_p(0x10002)) == va.ERR_ALIGNMENT
+    assert diff(q2=ctypes.c_void_p(0x10008)) == va.ERR_ALIGNMENT
+    assert diff(shape=_shape(va, d=96)) == va.ERR_UNSUPPORTED
+    assert diff(mask=FAKE) == va.ERR_INVALID_ARG  # mask needs its block mask
 
 
 def test_blockmask_argument_errors(lib):

@@ -684,3 +684,85 @@ def test_backward_long_documents_full_size(va):
     w = syn.long_packed_docs(0, tensors=("q", "k", "v", "do"))
     say(f"bwd full {w.name} L={w.L}")
     _check_sampled_bwd(va, w)
+
+
+# --------------------------------------------------------------- differential attention
+DIFF_CASES = [
+    # d, L, block_q, block_k, mask form ("none", "dense", "range"), lambda
+    (64, 300, 128, 128, "none", 0.8),
+    (64, 211, 64, 32, "dense", 0.37),
+    (128, 257, 128, 64, "range", 0.6),
+    (128, 190, 32, 128, "dense", -0.25),
+    (64, 150, 32, 64, "range", 1.0),
+]
+
+
+@pytest.mark.parametrize("d,L,bq,bk,form,lam", DIFF_CASES)
+def test_diff_forward(va, d, L, bq, bk, form, lam):
+    """Differential attention against the oracle (O and both LSEs); with
+    lambda = 0 the output and LSEs match two softmax calls, bit for bit where
+    both visit keys in the same steps."""
+    B, H = 4, 2
+    n = np.array([L, L - 37, 1, 0], np.int32)
+    q1, k1, q2, k2, v = _inputs(7000 + d + L, B, H, L, d, n, names="abcde")
+    rng = np.random.default_rng(L + d)
+    mask = kr = None
+    if form == "dense":
+        mask = (rng.random((B, L, L)) < 0.4).astype(np.uint8)
+        mask[0, 5, :] = 0
+    elif form == "range":
+        kr = _window_ranges(rng, B, L)
+    say(f"diff fwd d={d} L={L} bq={bq} bk={bk} form={form} lam={lam}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = None if mask is None else to_gpu(mask, torch.uint8)
+    kr_gpu = None if kr is None else to_gpu(kr, torch.int32)
+    bm = _bm(va, n_gpu, L, bq, bk, m_gpu, key_range=kr_gpu)
+    g = [to_gpu_bf16(t) for t in (q1, k1, q2, k2, v)]
+    kw = dict(block_mask=bm, mask=m_gpu, key_range=kr_gpu, block_q=bq, block_k=bk)
+    o, l1, l2 = va.sigattn_diff_fwd(*g, n_gpu, lam, return_lse=True, **kw)
+    o0, z1, z2 = va.sigattn_diff_fwd(*g, n_gpu, 0.0, return_lse=True, **kw)
+    s1, t1 = va.sigattn_fwd(g[0], g[1], g[4], n_gpu, variant=SOFTMAX, bias=0, return_lse=True, **kw)
+    _, t2 = va.sigattn_fwd(g[2], g[3], g[4], n_gpu, variant=SOFTMAX, bias=0, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    # Same key-block width as the softmax forward (32 keys per step at d =
+    # 128 against 64 there when block_k >= 64): identical online-softmax
+    # steps, identical bits.
+    if d == 64 or bk == 32:
+        assert torch.equal(o0.view(torch.int16), s1.view(torch.int16))
+        assert torch.equal(z1, t1) and torch.equal(z2, t2)
+    else:
+        assert_rows(gpu_f64(o0), gpu_f64(s1), n, "O (lambda 0) vs softmax")
+    want, w1, w2 = oracle.diff_fwd(q1, k1, q2, k2, v, n, lam, mask=mask, key_range=kr)
+    assert_rows(gpu_f64(o), want, n, "O")
+    valid = row_valid(n, B, L)
+    for got_l, want_l in ((l1, w1), (l2, w2)):
+        gl = got_l.cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isneginf(gl), np.isneginf(want_l))
+        fin = np.isfinite(want_l)
+        assert np.all(np.abs(gl[fin] - want_l[fin]) <= 1e-3 * np.maximum(1, np.abs(want_l[fin])))
+        assert np.all(np.isneginf(gl[~np.broadcast_to(valid[:, None, :], gl.shape)]))
+
+
+def test_diff_forward_single_cell_full_size(va, single_cell_inputs):
+    """Single-cell shapes (B32 H8 d64, L 1584): sampled rows against the oracle."""
+    w = single_cell_inputs
+    rng = np.random.default_rng(21)
+    q2 = syn.random_tensor(rng, w.q.shape)
+    k2 = syn.random_tensor(rng, w.k.shape)
+    lam = 0.8
+    say(f"diff fwd full {w.name} L={w.L}")
+    n_gpu = to_gpu(w.seq_lens, torch.int32)
+    bm = _bm(va, n_gpu, w.L, 128, 128)
+    o = va.sigattn_diff_fwd(*(to_gpu_bf16(t) for t in (w.q, w.k, q2, k2, w.v)), n_gpu, lam,
+                            block_mask=bm)
+    torch.cuda.synchronize()
+    og = gpu_f64(o)
+    valid = row_valid(w.seq_lens, w.B, w.L)
+    assert np.all(og[np.broadcast_to(~valid[:, None, :], og.shape[:3])] == 0)
+    got, want = [], []
+    for _ in range(6):
+        b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
+        rows = _sample_rows(rng, int(w.seq_lens[b]), w.L, 4)
+        want.append(oracle.diff_fwd_rows(w.q, w.k, q2, k2, w.v, w.seq_lens, lam, b, h, rows))
+        got.append(og[b, h, rows])
+    assert_close(np.concatenate(got), np.concatenate(want), "O sampled diff")

@@ -1,0 +1,56 @@
+"""Pins for the oracle's differential attention ("Differential Transformer"
+note, "How differential attention works": two softmax maps over one V, the
+second subtracted with a scalar lambda)."""
+import numpy as np
+import pytest
+
+from _tiny import SOFTMAX, BIAS_NONE, dense_python, random_inputs, widen
+
+
+@pytest.mark.parametrize("with_mask", [False, True])
+def test_diff_matches_dense_two_maps(oracle_lib, with_mask):
+    """Against two dense score matrices materialised in pure Python."""
+    rng = np.random.default_rng(11)
+    B, H, L, d = 2, 2, 14, 8
+    q1, k1, q2, k2, v = random_inputs(rng, B, H, L, d, names="abcde")
+    n = np.array([14, 9], np.int32)
+    mask = (rng.random((B, L, L)) < 0.6).astype(np.uint8) if with_mask else None
+    lam = 0.37
+    o, lse1, lse2 = oracle_lib.diff_fwd(q1, k1, q2, k2, v, n, lam, mask=mask)
+    scale = 1.0 / np.sqrt(d)
+    for b in range(B):
+        for h in range(H):
+            mb = None if mask is None else mask[b]
+            w1 = dense_python(widen(q1[b, h]), widen(k1[b, h]), widen(v[b, h]), n[b], mb,
+                              BIAS_NONE, SOFTMAX, scale)[1]
+            w2 = dense_python(widen(q2[b, h]), widen(k2[b, h]), widen(v[b, h]), n[b], mb,
+                              BIAS_NONE, SOFTMAX, scale)[1]
+            want = (np.array(w1) - lam * np.array(w2)) @ widen(v[b, h])
+            np.testing.assert_allclose(o[b, h], want, rtol=1e-12, atol=1e-13)
+
+
+def test_identical_maps_scale_by_one_minus_lambda(oracle_lib):
+    """Q2 = Q1 and K2 = K1: the two maps cancel to (1 - lambda) times one
+    softmax attention; lambda = 1 gives exactly 0."""
+    rng = np.random.default_rng(12)
+    B, H, L, d = 2, 1, 40, 16
+    q, k, v = random_inputs(rng, B, H, L, d)
+    n = np.array([40, 23], np.int32)
+    one, _ = oracle_lib.fwd(q, k, v, n, bias=BIAS_NONE, variant=SOFTMAX)
+    for lam in (0.0, 0.8, 1.0, -0.5):
+        o, l1, l2 = oracle_lib.diff_fwd(q, k, q, k, v, n, lam)
+        np.testing.assert_allclose(o, (1 - lam) * one, rtol=1e-13, atol=1e-15)
+        np.testing.assert_array_equal(l1, l2)
+    o, _, _ = oracle_lib.diff_fwd(q, k, q, k, v, n, 1.0)
+    assert np.all(o == 0)
+
+
+def test_rows_match_full(oracle_lib):
+    rng = np.random.default_rng(13)
+    B, H, L, d = 2, 2, 30, 8
+    q1, k1, q2, k2, v = random_inputs(rng, B, H, L, d, names="abcde")
+    n = np.array([30, 17], np.int32)
+    o, _, _ = oracle_lib.diff_fwd(q1, k1, q2, k2, v, n, 0.6)
+    rows = [0, 5, 16, 29]
+    got = oracle_lib.diff_fwd_rows(q1, k1, q2, k2, v, n, 0.6, 1, 1, rows)
+    np.testing.assert_allclose(got, o[1, 1, rows], rtol=1e-13, atol=1e-15)

@@ -23,7 +23,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_LAUNCH = 0, -1, -2, -3,
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsigattn.so")
 EXPORTS = ("blockmask_build", "sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq",
-           "sigattn_last_error")
+           "sigattn_diff_fwd", "sigattn_last_error")
 
 
 class SigattnError(RuntimeError):
@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sigattn_bwd_dkdv.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sigattn_bwd_dkdv.restype = ctypes.c_int
     lib.sigattn_bwd_dq.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, P, P]
+    lib.sigattn_diff_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, I, ctypes.c_float, P, P, P, P]
+    lib.sigattn_diff_fwd.restype = ctypes.c_int
     lib.sigattn_bwd_dq.restype = ctypes.c_int
     lib.sigattn_last_error.argtypes = []
     lib.sigattn_last_error.restype = ctypes.c_char_p
@@ -281,3 +283,45 @@ def sigattn_bwd_dq(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIA
         _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), _ptr(key_range), bias, variant,
         _ptr(dq), _stream(stream)))
     return dq
+
+def sigattn_diff_fwd(q1, k1, q2, k2, v, seq_lens, lam: float, block_mask=None, mask=None,
+                     key_range=None, bias=BIAS_NONE, scale=None, block_q=128, block_k=128,
+                     out=None, lse1=None, lse2=None, return_lse=False, stream=None):
+    """Differential attention forward: (softmax(S1) - lam softmax(S2)) V, both
+    maps in one tile loop.  q1, k1, q2, k2, v: bf16 [B, H, L, d] on the GPU
+    with equal strides.  Returns o, or (o, lse1, lse2) with return_lse=True."""
+    for t, nm in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v")):
+        _need(t, nm, torch.bfloat16)
+    _layout([q1, k1, q2, k2, v], ["q1", "k1", "q2", "k2", "v"])
+    _need(seq_lens, "seq_lens", torch.int32)
+    if out is None:
+        out = torch.empty_like(q1, memory_format=torch.contiguous_format)
+    _need(out, "out", torch.bfloat16)
+    if tuple(out.shape) != tuple(q1.shape) or out.stride(3) != 1:
+        raise ValueError("out must match q1's shape with unit stride in d")
+    B, H, L, d = q1.shape
+    lses = []
+    for l_ in (lse1, lse2):
+        if return_lse and l_ is None:
+            l_ = torch.empty((B, H, L), dtype=torch.float32, device=q1.device)
+        if l_ is not None:
+            _need(l_, "lse", torch.float32)
+            if tuple(l_.shape) != (B, H, L) or not l_.is_contiguous():
+                raise ValueError("lse1/lse2 must be contiguous float32 [B, H, L] tensors")
+        lses.append(l_)
+    if mask is not None:
+        _need(mask, "mask", torch.uint8)
+        if tuple(mask.shape) != (B, L, L) or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous uint8 [B, L, L] tensor")
+    _key_range(key_range, B, L)
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8)
+        want = (B, num_tiles(L, block_q), num_tiles(L, block_k))
+        if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
+            raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
+    shape = _shape(q1, out.stride(), scale, block_q, block_k)
+    _check(load_library().sigattn_diff_fwd(
+        ctypes.byref(shape), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v),
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), _ptr(key_range), bias,
+        float(lam), _ptr(out), _ptr(lses[0]), _ptr(lses[1]), _stream(stream)))
+    return (out, lses[0], lses[1]) if return_lse else out

@@ -159,6 +159,34 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
     return launch_status(sigattn::launch_fwd(p, (hipStream_t)stream), "sigattn_fwd");
 }
 
+int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
+                     const void *k2, const void *v, const int32_t *seq_lens,
+                     const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
+                     int32_t bias_mode, float lambda, void *o, float *lse1, float *lse2,
+                     void *stream) {
+    sigattn::AttnParams p = {};
+    const void *inputs[5] = {q1, k1, q2, k2, v};
+    void *outputs[1] = {o};
+    int st = check_attention(shape, inputs, 5, outputs, 1, seq_lens, block_mask, mask,
+                             key_range, bias_mode, SIGATTN_SOFTMAX, &p);
+    if (st != SIGATTN_OK) return st;
+    if (!isfinite(lambda)) return fail(SIGATTN_ERR_INVALID_ARG, "lambda must be finite");
+    if ((reinterpret_cast<uintptr_t>(lse1) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(lse2) & 3u) != 0)
+        return fail(SIGATTN_ERR_ALIGNMENT, "lse1/lse2 is not 4-byte aligned");
+    p.q = q1;
+    p.k = k1;
+    p.q2 = q2;
+    p.k2 = k2;
+    p.v = v;
+    p.o = o;
+    p.lse = lse1;
+    p.lse2 = lse2;
+    p.lambda = lambda;
+    p.variant = sigattn::kDiff;
+    return launch_status(sigattn::launch_fwd(p, (hipStream_t)stream), "sigattn_diff_fwd");
+}
+
 }  // extern "C"
 
 namespace {

@@ -8,6 +8,8 @@
 
 #include <type_traits>
 
+#include "kernels.h"
+
 namespace sigattn {
 
 typedef __bf16 bf16;
@@ -21,7 +23,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-enum Variant { kSigmoid = 0, kSoftmax = 1, kSoftmax1 = 2 };
 enum Bias { kBiasNone = 0, kBiasLogSeqlen = 1, kBiasLogPadlen = 2 };
 
 // D[32x32] += A[32x16] * B[16x32], bf16 inputs, fp32 accumulation.

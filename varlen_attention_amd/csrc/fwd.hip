@@ -38,14 +38,15 @@ namespace {
 // 8 bytes per lane, 4 rows x 32 bytes per 16 lanes: a stride of 8 banks.
 template <int D> struct Pad { static constexpr int K = D + 8, V = D + 16; };
 
-template <int D, int BK, int NT>
+template <int D, int BK, int NT, int NK = 1>
 struct KVStage {
-    // Each thread moves CH 16-byte chunks of K and of V per tile.  Offsets are
-    // loop-invariant; the per-tile part lives in the buffer descriptors.
+    // Each thread moves CH 16-byte chunks of each of the NK key tiles and of
+    // V per tile.  Offsets are loop-invariant; the per-tile part lives in the
+    // buffer descriptors.
     static constexpr int kChunksPerRow = D / 8;
     static constexpr int CH = BK * kChunksPerRow / NT;
     static_assert(CH * NT == BK * kChunksPerRow, "tile must split evenly over threads");
-    uint4 k[CH], v[CH];
+    uint4 k[NK][CH], v[CH];
     int goff[CH], koff[CH], voff[CH];
 
     __device__ __forceinline__ void init(int64_t sl, int tid) {
@@ -59,18 +60,24 @@ struct KVStage {
         }
     }
 
-    __device__ __forceinline__ void load(rsrc_t rk, rsrc_t rv) {
+    // rk[i]: the i-th key tensor's rows; Ks + i * KTILE receives it.
+    __device__ __forceinline__ void load(const rsrc_t (&rk)[NK], rsrc_t rv) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            k[c] = buffer_load16(rk, goff[c]);
+#pragma unroll
+            for (int i = 0; i < NK; ++i) k[i][c] = buffer_load16(rk[i], goff[c]);
             v[c] = buffer_load16(rv, goff[c]);
         }
     }
 
+    static constexpr int KTILE = BK * Pad<D>::K;
+
     __device__ __forceinline__ void store(bf16 *Ks, bf16 *Vs) const {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            *reinterpret_cast<uint4 *>(Ks + koff[c]) = k[c];
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+                *reinterpret_cast<uint4 *>(Ks + i * KTILE + koff[c]) = k[i][c];
             *reinterpret_cast<uint4 *>(Vs + voff[c]) = v[c];
         }
     }
@@ -78,15 +85,24 @@ struct KVStage {
 
 }  // namespace
 
+// Two maps at d = 128 hold two Q operands and two output accumulators (192
+// registers before the loop's own): such waves get the whole register file.
+template <int D, int VARIANT>
+constexpr int kFwdWavesPerSimd = VARIANT == kDiff && D == 128 ? 1 : 2;
+
 template <int D, int VARIANT, int NW, int KB, int MASK>
-__global__ void __launch_bounds__(64 * NW, 2)
+__global__ void __launch_bounds__(64 * NW, (kFwdWavesPerSimd<D, VARIANT>))
 fwd_kernel(const AttnParams p) {
     constexpr bool MASKED = MASK != kMaskNone;
+    // Differential attention runs two softmax maps (their own Q, K, running
+    // max and sum, and output accumulator) over the same V tiles and mask.
+    constexpr int MAPS = VARIANT == kDiff ? 2 : 1;
+    constexpr bool kSoft = VARIANT != kSigmoid;
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
     constexpr int KS = D / 16;  // MFMA k-steps over the head dimension
     constexpr int DB = D / 32;  // 32-wide blocks of the head dimension
     constexpr int KP = Pad<D>::K, VP = Pad<D>::V;
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][BK * KP];
+    __shared__ __attribute__((aligned(16))) bf16 Ks[2][MAPS * BK * KP];
     __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * VP];
     __shared__ uint32_t Ms[2][MASKED ? BQ * BK / 32 : 1];  // element-mask bits per tile
 
@@ -96,7 +112,9 @@ fwd_kernel(const AttnParams p) {
     const int L = p.L;
     const int q0 = qt * BQ;
     bf16 *ob = reinterpret_cast<bf16 *>(p.o) + b * p.osb + h * p.osh;
-    float *lseb = p.lse ? p.lse + ((int64_t)b * p.H + h) * L : nullptr;
+    float *lseb[MAPS];
+    lseb[0] = p.lse ? p.lse + ((int64_t)b * p.H + h) * L : nullptr;
+    if constexpr (MAPS == 2) lseb[1] = p.lse2 ? p.lse2 + ((int64_t)b * p.H + h) * L : nullptr;
 
     // Rows [r0, r0 + rows) of a fully padded query tile: zeros (LSE -inf).
     auto zero_tile = [&](int r0, int rows) {
@@ -104,16 +122,23 @@ fwd_kernel(const AttnParams p) {
             const int r = r0 + idx / (D / 8), c = (idx % (D / 8)) * 8;
             *reinterpret_cast<uint4 *>(ob + (int64_t)r * p.osl + c) = make_uint4(0, 0, 0, 0);
         }
-        if (VARIANT != kSigmoid && lseb)
-            for (int r = r0 + tid; r < r0 + rows; r += NT) lseb[r] = -INFINITY;
+#pragma unroll
+        for (int mp = 0; mp < MAPS; ++mp)
+            if (kSoft && lseb[mp])
+                for (int r = r0 + tid; r < r0 + rows; r += NT) lseb[mp][r] = -INFINITY;
     };
     if (q0 >= n) {  // a tile of an empty sequence: zeros, nothing else
         zero_tile(q0, min(BQ, L - q0));
         return;
     }
 
-    const bf16 *qb = reinterpret_cast<const bf16 *>(p.q) + b * p.sb + h * p.sh;
-    const bf16 *kb = reinterpret_cast<const bf16 *>(p.k) + b * p.sb + h * p.sh;
+    const bf16 *qb[MAPS], *kb[MAPS];
+    qb[0] = reinterpret_cast<const bf16 *>(p.q) + b * p.sb + h * p.sh;
+    kb[0] = reinterpret_cast<const bf16 *>(p.k) + b * p.sb + h * p.sh;
+    if constexpr (MAPS == 2) {
+        qb[1] = reinterpret_cast<const bf16 *>(p.q2) + b * p.sb + h * p.sh;
+        kb[1] = reinterpret_cast<const bf16 *>(p.k2) + b * p.sb + h * p.sh;
+    }
     const bf16 *vb = reinterpret_cast<const bf16 *>(p.v) + b * p.sb + h * p.sh;
     const uint8_t *bm_row =
         p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + q0 / p.block_q) * p.Tk : nullptr;
@@ -128,12 +153,15 @@ fwd_kernel(const AttnParams p) {
 
     // Q^T operand: lane holds Q[qr][16 ks + 8 hh .. + 7].
     // Rows >= n read as zeros through the descriptor.
-    const rsrc_t rq = make_rsrc(qb + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
-    bf16x8 qreg[KS];
+    bf16x8 qreg[MAPS][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        qreg[ks] = as_bf16x8(
-            buffer_load16(rq, (int)(((int64_t)(w * 32 + ql) * p.sl + ks * 16 + hh * 8) * 2)));
+    for (int mp = 0; mp < MAPS; ++mp) {
+        const rsrc_t rq = make_rsrc(qb[mp] + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qreg[mp][ks] = as_bf16x8(
+                buffer_load16(rq, (int)(((int64_t)(w * 32 + ql) * p.sl + ks * 16 + hh * 8) * 2)));
+    }
 
     // SIGMOID: Q is scaled by c1 before the loop, so the S^T accumulator is
     // u = -scale * s * log2 e and the weight is 1 / (1 + exp(-b) 2^u); the
@@ -144,11 +172,15 @@ fwd_kernel(const AttnParams p) {
     const float c0 = bias_value(p.bias_mode, n, L) * kLog2e;
     const float cexp = bias_factor(p.bias_mode, n, L);
 
-    f32x16 oacc[DB];
+    f32x16 oacc[MAPS][DB];
+    float m_run[MAPS], l_run[MAPS];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-    float m_run = VARIANT == kSoftmax1 ? 0.0f : -INFINITY;  // log2 domain
-    float l_run = (VARIANT == kSoftmax1 && hh == 0) ? 1.0f : 0.0f;  // split over lane halves
+    for (int mp = 0; mp < MAPS; ++mp) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[mp][db] = f32x16{};
+        m_run[mp] = VARIANT == kSoftmax1 ? 0.0f : -INFINITY;  // log2 domain
+        l_run[mp] = (VARIANT == kSoftmax1 && hh == 0) ? 1.0f : 0.0f;  // split over lane halves
+    }
 
     // Descriptors of the K and V rows [k0, n): rows past n read as zeros.
     auto rows_rsrc = [&](const bf16 *base, int k0) {
@@ -160,9 +192,15 @@ fwd_kernel(const AttnParams p) {
     // The first stage is written unconditionally (tile 0 when nothing is
     // active, harmless): every path into the loop has then waited for all
     // earlier loads, Q included.
-    KVStage<D, BK, NT> stage;
+    KVStage<D, BK, NT, MAPS> stage;
+    auto load_tile = [&](int t) {
+        rsrc_t rk[MAPS];
+#pragma unroll
+        for (int mp = 0; mp < MAPS; ++mp) rk[mp] = rows_rsrc(kb[mp], t * BK);
+        stage.load(rk, rows_rsrc(vb, t * BK));
+    };
     stage.init(p.sl, tid);
-    stage.load(rows_rsrc(kb, 0), rows_rsrc(vb, 0));
+    load_tile(0);
     MaskStager<MASK, BQ, BK, NT, true> mstage;
     int mcls = kMixed;  // this wave's share of the current tile (element mask)
     if constexpr (MASKED) mstage.init(tid);
@@ -170,7 +208,7 @@ fwd_kernel(const AttnParams p) {
     sched.init(bm_row, 1, n, p.block_k);
     int kt = sched.next();
     const bool kt_full = sched.full;
-    if (kt > 0) stage.load(rows_rsrc(kb, kt * BK), rows_rsrc(vb, kt * BK));
+    if (kt > 0) load_tile(kt);
     if constexpr (MASKED)
         if (kt >= 0) mstage.load(msrc, n, q0, kt * BK, kt_full);
     int buf = 0;
@@ -179,7 +217,7 @@ fwd_kernel(const AttnParams p) {
         if (kt >= 0) mcls = mstage.store(Ms[0], q0, kt * BK, n, kt_full);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        if constexpr (VARIANT == kSigmoid) qreg[ks] = scale8(qreg[ks], c1);
+        if constexpr (VARIANT == kSigmoid) qreg[0][ks] = scale8(qreg[0][ks], c1);
     __syncthreads();
     // This tile's share of the sequence's fully padded query tiles, written
     // while the loop computes (the stores complete during the first tile).
@@ -189,7 +227,7 @@ fwd_kernel(const AttnParams p) {
         const int k0 = kt * BK;
         const int nxt = sched.next();
         const bool nxt_full = sched.full;
-        if (nxt >= 0) stage.load(rows_rsrc(kb, nxt * BK), rows_rsrc(vb, nxt * BK));
+        if (nxt >= 0) load_tile(nxt);
         if constexpr (MASKED)
             if (nxt >= 0) mstage.load(msrc, n, q0, nxt * BK, nxt_full);
         const bf16 *Kc = Ks[buf];
@@ -205,19 +243,21 @@ fwd_kernel(const AttnParams p) {
         // must not enter the row max and sum).  MODE 2: element mask.
         auto tile = [&](auto mode_tag) {
             constexpr int MODE = decltype(mode_tag)::value;
-            // S^T for each 32-key block: sacc[kb2][4i + j] is
+            // S^T for each map and 32-key block: sacc[mp][kb2][4i + j] is
             // S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr].
-            f32x16 sacc[KB];
+            f32x16 sacc[MAPS][KB];
 #pragma unroll
-            for (int kb2 = 0; kb2 < KB; ++kb2) {
-                sacc[kb2] = f32x16{};
+            for (int mp = 0; mp < MAPS; ++mp)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                        Kc + (kb2 * 32 + ql) * KP + ks * 16 + hh * 8);
-                    sacc[kb2] = mfma32(a, qreg[ks], sacc[kb2]);
+                for (int kb2 = 0; kb2 < KB; ++kb2) {
+                    sacc[mp][kb2] = f32x16{};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+                            Kc + mp * BK * KP + (kb2 * 32 + ql) * KP + ks * 16 + hh * 8);
+                        sacc[mp][kb2] = mfma32(a, qreg[mp][ks], sacc[mp][kb2]);
+                    }
                 }
-            }
             // Per-element validity.  MODE 1: compared, without branches.
             // MODE 2: the tile's mask bits (validity folded in); key
             // 8 i + 4 hh + j of a 32-key block is bit key_bit(8 i + 4 hh + j):
@@ -244,55 +284,65 @@ fwd_kernel(const AttnParams p) {
                                                        : 8 * (r >> 2) + (r & 3));
             };
 
-            float m_use = 0.0f;
-            if constexpr (VARIANT != kSigmoid) {
-                // Online softmax: tile maximum over this lane's keys and its
-                // partner lane's (lane ^ 32), then rescale the state.
-                float tmax = -INFINITY;
+            float m_use[MAPS];
+            if constexpr (kSoft) {
+                // Online softmax, per map: tile maximum over this lane's keys
+                // and its partner lane's (lane ^ 32), then rescale the state.
 #pragma unroll
-                for (int kb2 = 0; kb2 < KB; ++kb2)
+                for (int mp = 0; mp < MAPS; ++mp) {
+                    float tmax = -INFINITY;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float t = fmaf(sacc[kb2][r], c1, c0);
-                        if constexpr (MODE == 1) t = keep_or_neg_inf(t, ok[kb2][r]);
-                        if constexpr (MODE == 2) t = keep_bits_or_neg_inf(t, keep(kb2, r));
-                        sacc[kb2][r] = t;
-                        tmax = fmaxf(tmax, t);
-                    }
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-                const float m_new = fmaxf(m_run, tmax);
-                m_use = m_new == -INFINITY ? 0.0f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-                m_run = m_new;
-                l_run *= alpha;
+                    for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+                        for (int r = 0; r < 16; ++r) {
+                            float t = fmaf(sacc[mp][kb2][r], c1, c0);
+                            if constexpr (MODE == 1) t = keep_or_neg_inf(t, ok[kb2][r]);
+                            if constexpr (MODE == 2) t = keep_bits_or_neg_inf(t, keep(kb2, r));
+                            sacc[mp][kb2][r] = t;
+                            tmax = fmaxf(tmax, t);
+                        }
+                    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                    const float m_new = fmaxf(m_run[mp], tmax);
+                    m_use[mp] = m_new == -INFINITY ? 0.0f : m_new;
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[mp] - m_use[mp]);
+                    m_run[mp] = m_new;
+                    l_run[mp] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) oacc[mp][db] *= alpha;
+                }
             }
 
-            // Per 32-key block: weights, then O^T += V^T P^T (two 16-key steps).
+            // Per 32-key block: weights, then O^T += V^T P^T (two 16-key
+            // steps); each V fragment serves every map.
 #pragma unroll
             for (int kb2 = 0; kb2 < KB; ++kb2) {
-                float pv[16];
+                float pv[MAPS][16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if constexpr (VARIANT == kSigmoid) {
-                        pv[r] = sigmoid_scaled(sacc[kb2][r], cexp);
-                        if constexpr (MODE == 2)
-                            pv[r] = __uint_as_float(__float_as_uint(pv[r]) & keep(kb2, r));
-                    } else {
-                        pv[r] = __builtin_amdgcn_exp2f(sacc[kb2][r] - m_use);
-                        l_run += pv[r];
+                for (int mp = 0; mp < MAPS; ++mp)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        if constexpr (VARIANT == kSigmoid) {
+                            pv[mp][r] = sigmoid_scaled(sacc[mp][kb2][r], cexp);
+                            if constexpr (MODE == 2)
+                                pv[mp][r] = __uint_as_float(__float_as_uint(pv[mp][r]) & keep(kb2, r));
+                        } else {
+                            pv[mp][r] = __builtin_amdgcn_exp2f(sacc[mp][kb2][r] - m_use[mp]);
+                            l_run[mp] += pv[mp][r];
+                        }
                     }
-                }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 pb = pack8(&pv[kk * 8]);
+                    bf16x8 pb[MAPS];
+#pragma unroll
+                    for (int mp = 0; mp < MAPS; ++mp) pb[mp] = pack8(&pv[mp][kk * 8]);
                     const bf16 *vrow = Vc + (kb2 * 32 + kk * 16 + trow) * VP + tcol;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         const bf16x8 a = cat8(lds_read_tr4(vrow + db * 32),
                                               lds_read_tr4(vrow + 8 * VP + db * 32));
-                        oacc[db] = mfma32(a, pb, oacc[db]);
+#pragma unroll
+                        for (int mp = 0; mp < MAPS; ++mp)
+                            oacc[mp][db] = mfma32(a, pb[mp], oacc[mp][db]);
                     }
                 }
             }
@@ -315,28 +365,38 @@ fwd_kernel(const AttnParams p) {
         kt = nxt;
     }
 
-    // Finalise and store: oacc[db][4i + j] is O[qr][32 db + 8 i + 4 hh + j].
-    float inv = 1.0f;
-    if (VARIANT != kSigmoid) {
-        const float l_tot = l_run + __shfl_xor(l_run, 32);
-        inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        if (lseb && hh == 0 && qr < L) {
-            float lse = -INFINITY;
-            if (q_valid && l_tot > 0.0f) lse = (m_run + __builtin_log2f(l_tot)) * kLn2;
-            lseb[qr] = lse;
+    // Finalise and store: oacc[mp][db][4i + j] is map mp's O^T entry for
+    // O[qr][32 db + 8 i + 4 hh + j]; differential attention writes
+    // O1 - lambda O2.
+    float inv[MAPS];
+#pragma unroll
+    for (int mp = 0; mp < MAPS; ++mp) {
+        inv[mp] = 1.0f;
+        if (kSoft) {
+            const float l_tot = l_run[mp] + __shfl_xor(l_run[mp], 32);
+            inv[mp] = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            if (lseb[mp] && hh == 0 && qr < L) {
+                float lse = -INFINITY;
+                if (q_valid && l_tot > 0.0f) lse = (m_run[mp] + __builtin_log2f(l_tot)) * kLn2;
+                lseb[mp][qr] = lse;
+            }
         }
     }
+    if constexpr (MAPS == 2) inv[1] *= -p.lambda;
     if (qr < L) {
         bf16 *orow = ob + (int64_t)qr * p.osl;
         // Padded query rows are exactly +0 whatever their (finite) accumulators hold.
-        auto out = [&](float x) { return keep_or_zero(x * inv, q_valid); };
+        auto out = [&](int db, int e) {
+            float x = oacc[0][db][e] * inv[0];
+            if constexpr (MAPS == 2) x = fmaf(oacc[1][db][e], inv[1], x);
+            return keep_or_zero(x, q_valid);
+        };
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f32x16 &a = oacc[db];
-                const bf16x4 v4 = pack4(out(a[4 * i]), out(a[4 * i + 1]), out(a[4 * i + 2]),
-                                        out(a[4 * i + 3]));
+                const bf16x4 v4 = pack4(out(db, 4 * i), out(db, 4 * i + 1), out(db, 4 * i + 2),
+                                        out(db, 4 * i + 3));
                 *reinterpret_cast<bf16x4 *>(orow + db * 32 + i * 8 + hh * 4) = v4;
             }
     }
@@ -344,12 +404,16 @@ fwd_kernel(const AttnParams p) {
 
 template <int D, int VARIANT>
 static hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
+    // Two maps at d = 128 visit 32 keys at a time: two K tiles and V of 64
+    // keys, double-buffered, would leave LDS for one workgroup per CU.
+    constexpr bool kNarrow = VARIANT == kDiff && D == 128;
     const int nw = p.block_q >= 128 ? 4 : p.block_q / 32;
-    const int kb = p.block_k >= 64 ? 2 : 1;
+    const int kb = p.block_k >= 64 && !kNarrow ? 2 : 1;
     const int bq = 32 * nw;
     const dim3 grid = tile_grid((p.L + bq - 1) / bq, p.B, p.H);
     dim3 block(64 * nw);
 #define SIGATTN_FWD_CASE(NW_, KB_)                                                             \
+    if constexpr (!kNarrow || KB_ == 1)                                                        \
     if (nw == NW_ && kb == KB_) {                                                              \
         if (p.mask != nullptr)                                                                 \
             hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, kMaskDense>), grid, block, 0, \
@@ -376,10 +440,12 @@ hipError_t launch_fwd(const AttnParams &p, hipStream_t stream) {
     if (p.d == 64) {
         if (p.variant == kSigmoid) return launch_fwd_d<64, kSigmoid>(p, stream);
         if (p.variant == kSoftmax) return launch_fwd_d<64, kSoftmax>(p, stream);
+        if (p.variant == kDiff) return launch_fwd_d<64, kDiff>(p, stream);
         return launch_fwd_d<64, kSoftmax1>(p, stream);
     }
     if (p.variant == kSigmoid) return launch_fwd_d<128, kSigmoid>(p, stream);
     if (p.variant == kSoftmax) return launch_fwd_d<128, kSoftmax>(p, stream);
+    if (p.variant == kDiff) return launch_fwd_d<128, kDiff>(p, stream);
     return launch_fwd_d<128, kSoftmax1>(p, stream);
 }
 

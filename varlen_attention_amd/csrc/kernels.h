@@ -8,10 +8,18 @@
 
 namespace sigattn {
 
+// The ABI's variants, plus kDiff: differential attention, two softmax maps
+// over one V combined as O1 - lambda O2 (forward only; set by the
+// differential entry point).
+enum Variant { kSigmoid = 0, kSoftmax = 1, kSoftmax1 = 2, kDiff = 3 };
+
 struct AttnParams {
     const void *q, *k, *v, *dout;   // bf16 [B, H, L, d] (input layout); dout: backward only
     void *o, *dq, *dk, *dv;         // bf16 [B, H, L, d] (output layout)
     float *lse;                     // float [B, H, L] or null
+    const void *q2, *k2;            // differential attention: the second map's Q and K
+    float *lse2;                    // differential attention: the second map's LSE, or null
+    float lambda;                   // differential attention: O = O1 - lambda O2
     const int32_t *seq_lens;        // [B]
     const uint8_t *block_mask;      // [B, Tq, Tk] or null
     const uint8_t *mask;            // [B, L, L] or null
