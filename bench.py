@@ -463,36 +463,45 @@ def run_suite(args) -> int:
     del w, wb
     # Differential attention at the single-cell shapes: both maps in one
     # launch, against two softmax forward launches (4 d flops per pair and map).
-    wd = syn.single_cell(args.seed, tensors=("q", "k", "v"))
+    wd = syn.single_cell(args.seed, tensors=("q", "k", "v", "do"))
     rng = np.random.default_rng(args.seed + 1)
     q1, k1, v = gpu(wd.q), gpu(wd.k), gpu(wd.v)
     q2, k2 = gpu(syn.random_tensor(rng, wd.q.shape)), gpu(syn.random_tensor(rng, wd.k.shape))
     n = torch.from_numpy(wd.seq_lens).to(dev)
     bm = va.blockmask_build(n, wd.L, 128, 128)
+    dout = gpu(wd.do)
     o, o2 = torch.empty_like(q1), torch.empty_like(q1)
     label = "single cell, differential (lambda 0.8)"
     log(f"case {label}")
+    _, l1, l2, m1, m2 = va.sigattn_diff_fwd(q1, k1, q2, k2, v, n, 0.8, block_mask=bm,
+                                            return_maps=True)
+    grads = [torch.empty_like(q1) for _ in range(5)]
     fns = [lambda: va.sigattn_diff_fwd(q1, k1, q2, k2, v, n, 0.8, block_mask=bm, out=o),
            lambda: va.sigattn_fwd(q1, k1, v, n, block_mask=bm, variant=syn.SOFTMAX, bias=0, out=o),
            lambda: va.sigattn_fwd(q2, k2, v, n, block_mask=bm, variant=syn.SOFTMAX, bias=0,
-                                  out=o2)]
+                                  out=o2),
+           lambda: va.sigattn_diff_bwd(q1, k1, q2, k2, v, dout, m1, m2, l1, l2, n, 0.8,
+                                       block_mask=bm, grads=grads)]
     warm = timer.steps(fns)
     cold = timer.cold(fns[0], flush)
     tiles = int((bm != 0).sum().item()) * wd.H
     pairs = wd.valid_pairs * wd.H
-    for j, kern in enumerate(("diff fwd", "softmax fwd (map 1)", "softmax fwd (map 2)")):
+    valid_rows = float(np.clip(wd.seq_lens, 0, wd.L).sum()) * wd.H
+    all_rows = float(wd.B) * wd.L * wd.H
+    # (name, maps, flops per pair and map, rows read, rows written)
+    kinds = (("diff fwd", 2, 4, 5, 1), ("softmax fwd (map 1)", 1, 4, 3, 1),
+             ("softmax fwd (map 2)", 1, 4, 3, 1), ("diff bwd (two launches)", 2, 10, 10, 5))
+    for j, (kern, maps, fpp, rd, wr) in enumerate(kinds):
         med = float(np.median(warm[:, j]))
-        maps = 2 if j == 0 else 1
-        algo = ((3 + 2 * (maps - 1)) * float(np.clip(wd.seq_lens, 0, wd.L).sum()) * wd.H
-                + float(wd.B) * wd.L * wd.H) * 2.0 * wd.d
+        algo = (rd * valid_rows + wr * all_rows) * 2.0 * wd.d
         rows.append({"case": label, "kernel": kern, "warm_med_us": med,
                      "warm_min_us": float(warm[:, j].min()),
                      "cold_med_us": float(np.median(cold)) if j == 0 else None,
-                     "valid_tf": 4.0 * wd.d * maps * pairs / (med * 1e-6) / 1e12,
-                     "tile_tf": 4.0 * wd.d * maps * tiles * 128 * 128 / (med * 1e-6) / 1e12,
+                     "valid_tf": fpp * wd.d * maps * pairs / (med * 1e-6) / 1e12,
+                     "tile_tf": fpp * wd.d * maps * tiles * 128 * 128 / (med * 1e-6) / 1e12,
                      "gbs": algo / (med * 1e-6) / 1e9})
         log(f"  {kern}: warm median {med:.2f} us")
-    del q1, k1, q2, k2, v, o, o2, bm
+    del q1, k1, q2, k2, v, dout, o, o2, bm, grads, l1, l2, m1, m2
     torch.cuda.empty_cache()
     # Long packed documents: causal mask within documents, d = 128.
     wl = syn.long_packed_docs(args.seed, tensors=("q", "k", "v", "do"))

@@ -232,16 +232,43 @@ int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, con
  *   lambda             [host] finite float
  *   o                  [device] bf16 [B, H, L, d] (output layout), fully
  *                      written; padded rows and rows without a valid key are 0
+ *   o1, o2             [device] bf16 [B, H, L, d] (output layout) or NULL: each
+ *                      map's own output softmax(S_i) V, fully written when
+ *                      given (sigattn_diff_bwd needs them)
  *   lse1, lse2         [device] fp32 [B, H, L] contiguous, or NULL: each map's
  *                      log-sum-exp, as sigattn_fwd's SOFTMAX lse
  * Errors: as sigattn_fwd; INVALID_ARG for a non-finite lambda, ALIGNMENT for
- * lse1 or lse2 not 4-byte aligned.
+ * o1 or o2 not 16-byte, lse1 or lse2 not 4-byte aligned.
  */
 int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
                      const void *k2, const void *v, const int32_t *seq_lens,
                      const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
-                     int32_t bias_mode, float lambda, void *o, float *lse1, float *lse2,
-                     void *stream);
+                     int32_t bias_mode, float lambda, void *o, void *o1, void *o2, float *lse1,
+                     float *lse2, void *stream);
+
+/*
+ * sigattn_diff_bwd - gradients of sum(dO * O) for O = O1 - lambda O2 of
+ * sigattn_diff_fwd.  The output is linear in the two maps, so each map's
+ * gradients are those of a softmax attention with dO (map 1) or -lambda dO
+ * (map 2), and dV is the sum of both (sigattn_bwd's softmax backward: P from
+ * the map's LSE, dS = P * (dP - D), D = rowsum(dO * O_i) with the map's own
+ * output O_i).  Two backward launches on `stream`; the second adds its dV to
+ * the first's, so no atomics are used and results are reproducible.
+ *
+ *   q1, k1, q2, k2, v, dout  [device] bf16 [B, H, L, d] (input layout)
+ *   o1, o2, lse1, lse2       the forward's per-map outputs and LSEs (required)
+ *   seq_lens, block_mask, mask, key_range, bias_mode, lambda: as for the forward
+ *   dq1, dk1, dq2, dk2, dv   [device] bf16 [B, H, L, d] (output layout), fully
+ *                            written; rows >= n are 0
+ * Errors: as sigattn_bwd; INVALID_ARG for a NULL tensor or a non-finite
+ * lambda (all checked before anything is enqueued).
+ */
+int sigattn_diff_bwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
+                     const void *k2, const void *v, const void *dout, const void *o1,
+                     const void *o2, const float *lse1, const float *lse2,
+                     const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
+                     const int32_t *key_range, int32_t bias_mode, float lambda, void *dq1,
+                     void *dk1, void *dq2, void *dk2, void *dv, void *stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *sigattn_last_error(void);

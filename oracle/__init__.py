@@ -316,3 +316,15 @@ def diff_fwd_rows(q1, k1, q2, k2, v, seq_lens, lam: float, b: int, h: int, rows,
     o2, _ = fwd_rows(q2, k2, v, seq_lens, b, h, rows, mask=mask, bias=bias, variant=SOFTMAX,
                      scale=scale, precision=precision, key_range=key_range)
     return o1 - lam * o2
+
+
+def diff_bwd(q1, k1, q2, k2, v, do, seq_lens, lam: float, mask=None, bias=BIAS_NONE, scale=None,
+             precision="f64", threads=None, key_range=None):
+    """Gradients (dq1, dk1, dq2, dk2, dv) of sum(do * o), o = diff_fwd(...).
+    The output is o1 - lam o2, linear in the two maps: map 1's gradients are
+    the SOFTMAX backward with do, map 2's are -lam times it, dv adds both."""
+    g1 = bwd(q1, k1, v, do, seq_lens, mask=mask, bias=bias, variant=SOFTMAX, scale=scale,
+             precision=precision, threads=threads, key_range=key_range)
+    g2 = bwd(q2, k2, v, do, seq_lens, mask=mask, bias=bias, variant=SOFTMAX, scale=scale,
+             precision=precision, threads=threads, key_range=key_range)
+    return g1[0], g1[1], -lam * g2[0], -lam * g2[1], g1[2] - lam * g2[2]

@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["blockmask_build", "sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq",
-         "sigattn_diff_fwd", "sigattn_last_error"])
+         "sigattn_diff_bwd", "sigattn_diff_fwd", "sigattn_last_error"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -109,9 +109,9 @@ def test_diff_forward_argument_errors(lib):
     import varlen_attention_amd as va
     sh = _shape(va)
 
-    def diff(shape=sh, q2=FAKE, lam=0.5, lse2=None, mask=None, kr=None, bm=None):
+    def diff(shape=sh, q2=FAKE, lam=0.5, lse2=None, mask=None, kr=None, bm=None, o1=None):
         return lib.sigattn_diff_fwd(ctypes.byref(shape), FAKE, FAKE, q2, FAKE, FAKE, FAKE, bm,
-                                    mask, kr, 0, lam, FAKE, None, lse2, None)
+                                    mask, kr, 0, lam, FAKE, o1, None, None, lse2, None)
 
     assert diff(q2=None) == va.ERR_INVALID_ARG
     assert diff(lam=float("nan")) == va.ERR_INVALID_ARG
@@ -120,6 +120,25 @@ def test_diff_forward_argument_errors(lib):
     assert diff(q2=ctypes.c_void_p(0x10008)) == va.ERR_ALIGNMENT
     assert diff(shape=_shape(va, d=96)) == va.ERR_UNSUPPORTED
     assert diff(mask=FAKE) == va.ERR_INVALID_ARG  # mask needs its block mask
+    assert diff(o1=ctypes.c_void_p(0x10008)) == va.ERR_ALIGNMENT
+
+
+def test_diff_backward_argument_errors(lib):
+    import varlen_attention_amd as va
+    sh = _shape(va)
+
+    def dbwd(lam=0.5, o2=FAKE, lse2=FAKE, dq2=FAKE, o1=FAKE, dv=FAKE):
+        return lib.sigattn_diff_bwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, o1, o2,
+                                    FAKE, lse2, FAKE, None, None, None, 0, lam, FAKE, FAKE, dq2,
+                                    FAKE, dv, None)
+
+    assert dbwd(lam=float("nan")) == va.ERR_INVALID_ARG
+    assert dbwd(o2=None) == va.ERR_INVALID_ARG
+    assert dbwd(dq2=None) == va.ERR_INVALID_ARG
+    assert dbwd(dv=None) == va.ERR_INVALID_ARG
+    assert dbwd(lse2=ctypes.c_void_p(0x10002)) == va.ERR_ALIGNMENT
+    assert dbwd(o2=ctypes.c_void_p(0x10008)) == va.ERR_ALIGNMENT
+    assert dbwd(o1=None) == va.ERR_INVALID_ARG  # map 1 needs its output too
 
 
 def test_blockmask_argument_errors(lib):

@@ -766,3 +766,48 @@ def test_diff_forward_single_cell_full_size(va, single_cell_inputs):
         want.append(oracle.diff_fwd_rows(w.q, w.k, q2, k2, w.v, w.seq_lens, lam, b, h, rows))
         got.append(og[b, h, rows])
     assert_close(np.concatenate(got), np.concatenate(want), "O sampled diff")
+
+
+DIFF_BWD_CASES = [
+    # d, L, block_q, block_k, mask form, lambda
+    (64, 300, 128, 128, "none", 0.8),
+    (64, 230, 64, 32, "dense", 0.37),
+    (128, 201, 128, 128, "range", 0.6),
+    (128, 190, 64, 128, "dense", -0.3),
+]
+
+
+@pytest.mark.parametrize("d,L,bq,bk,form,lam", DIFF_BWD_CASES)
+def test_diff_backward(va, d, L, bq, bk, form, lam):
+    """Differential attention backward (from the forward's per-map outputs and
+    LSEs) against the oracle; map 1's gradients equal sigattn_bwd's softmax
+    backward bit for bit."""
+    B, H = 4, 2
+    n = np.array([L, L - 53, 1, 0], np.int32)
+    q1, k1, q2, k2, v, do = _inputs(8000 + d + L, B, H, L, d, n, names="abcdef")
+    rng = np.random.default_rng(L * 7 + d)
+    mask = kr = None
+    if form == "dense":
+        mask = (rng.random((B, L, L)) < 0.4).astype(np.uint8)
+        mask[0, 5, :] = 0
+    elif form == "range":
+        kr = _window_ranges(rng, B, L)
+    say(f"diff bwd d={d} L={L} bq={bq} bk={bk} form={form} lam={lam}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = None if mask is None else to_gpu(mask, torch.uint8)
+    kr_gpu = None if kr is None else to_gpu(kr, torch.int32)
+    bm = _bm(va, n_gpu, L, bq, bk, m_gpu, key_range=kr_gpu)
+    g = [to_gpu_bf16(t) for t in (q1, k1, q2, k2, v, do)]
+    kw = dict(block_mask=bm, mask=m_gpu, key_range=kr_gpu, block_q=bq, block_k=bk)
+    o, l1, l2, o1, o2 = va.sigattn_diff_fwd(*g[:5], n_gpu, lam, return_maps=True, **kw)
+    grads = va.sigattn_diff_bwd(*g, o1, o2, l1, l2, n_gpu, lam, **kw)
+    ref1 = va.sigattn_bwd(g[0], g[1], g[4], g[5], n_gpu, variant=SOFTMAX, bias=0, o=o1, lse=l1,
+                          **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(grads[0].view(torch.int16), ref1[0].view(torch.int16))
+    assert torch.equal(grads[1].view(torch.int16), ref1[1].view(torch.int16))
+    w1, _ = oracle.fwd(q1, k1, v, n, mask=mask, key_range=kr, bias=0, variant=SOFTMAX)
+    assert_rows(gpu_f64(o1), w1, n, "O1")
+    want = oracle.diff_bwd(q1, k1, q2, k2, v, do, n, lam, mask=mask, key_range=kr)
+    for name, got_t, ref in zip(("dQ1", "dK1", "dQ2", "dK2", "dV"), grads, want):
+        assert_rows(gpu_f64(got_t), ref, n, name)

@@ -54,3 +54,34 @@ def test_rows_match_full(oracle_lib):
     rows = [0, 5, 16, 29]
     got = oracle_lib.diff_fwd_rows(q1, k1, q2, k2, v, n, 0.6, 1, 1, rows)
     np.testing.assert_allclose(got, o[1, 1, rows], rtol=1e-13, atol=1e-15)
+
+
+def test_diff_backward_matches_torch_autograd(oracle_lib):
+    """Gradients of sum(dO * O) through two dense softmax maps, by torch float64
+    autograd, against the oracle's composition."""
+    import torch
+    rng = np.random.default_rng(14)
+    B, H, L, d = 2, 2, 12, 8
+    q1, k1, q2, k2, v, do = random_inputs(rng, B, H, L, d, names="abcdef")
+    n = np.array([12, 7], np.int32)
+    mask = (rng.random((B, L, L)) < 0.5).astype(np.uint8)
+    mask[:, np.arange(L), np.arange(L)] = 1  # every valid row sees a key
+    lam = 0.45
+    got = oracle_lib.diff_bwd(q1, k1, q2, k2, v, do, n, lam, mask=mask)
+    t = [torch.tensor(widen(x), requires_grad=True) for x in (q1, k1, q2, k2, v)]
+    tdo = torch.tensor(widen(do))
+    idx = torch.arange(L)
+    valid = (idx[None, :, None] < torch.tensor(n)[:, None, None]) & \
+            (idx[None, None, :] < torch.tensor(n)[:, None, None]) & torch.tensor(mask != 0)
+    row_ok = (idx[None, :] < torch.tensor(n)[:, None])[:, None, :, None]
+    scale = 1.0 / np.sqrt(d)
+
+    def probs(q, k):
+        s = (q @ k.transpose(-1, -2)) * scale
+        s = s.masked_fill(~valid[:, None], float("-inf"))
+        return torch.where(row_ok, torch.softmax(s.masked_fill(~row_ok, 0.0), dim=-1), 0.0)
+
+    o = (probs(t[0], t[1]) - lam * probs(t[2], t[3])) @ t[4]
+    (o * tdo * row_ok).sum().backward()
+    for name, g_, tt in zip(("dq1", "dk1", "dq2", "dk2", "dv"), got, t):
+        np.testing.assert_allclose(g_, tt.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)

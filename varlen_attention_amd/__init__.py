@@ -23,7 +23,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_LAUNCH = 0, -1, -2, -3,
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsigattn.so")
 EXPORTS = ("blockmask_build", "sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq",
-           "sigattn_diff_fwd", "sigattn_last_error")
+           "sigattn_diff_fwd", "sigattn_diff_bwd", "sigattn_last_error")
 
 
 class SigattnError(RuntimeError):
@@ -68,8 +68,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sigattn_bwd_dkdv.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sigattn_bwd_dkdv.restype = ctypes.c_int
     lib.sigattn_bwd_dq.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, P, P]
-    lib.sigattn_diff_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, I, ctypes.c_float, P, P, P, P]
+    F = ctypes.c_float
+    lib.sigattn_diff_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, I, F, P, P, P, P, P, P]
     lib.sigattn_diff_fwd.restype = ctypes.c_int
+    lib.sigattn_diff_bwd.argtypes = [S] + [P] * 14 + [I, F] + [P] * 6
+    lib.sigattn_diff_bwd.restype = ctypes.c_int
     lib.sigattn_bwd_dq.restype = ctypes.c_int
     lib.sigattn_last_error.argtypes = []
     lib.sigattn_last_error.restype = ctypes.c_char_p
@@ -286,10 +289,13 @@ def sigattn_bwd_dq(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIA
 
 def sigattn_diff_fwd(q1, k1, q2, k2, v, seq_lens, lam: float, block_mask=None, mask=None,
                      key_range=None, bias=BIAS_NONE, scale=None, block_q=128, block_k=128,
-                     out=None, lse1=None, lse2=None, return_lse=False, stream=None):
+                     out=None, lse1=None, lse2=None, return_lse=False, stream=None,
+                     o1=None, o2=None, return_maps=False):
     """Differential attention forward: (softmax(S1) - lam softmax(S2)) V, both
     maps in one tile loop.  q1, k1, q2, k2, v: bf16 [B, H, L, d] on the GPU
-    with equal strides.  Returns o, or (o, lse1, lse2) with return_lse=True."""
+    with equal strides.  Returns o, or (o, lse1, lse2) with return_lse=True;
+    with return_maps=True also each map's own output: (o, lse1, lse2, o1, o2)
+    (what sigattn_diff_bwd needs)."""
     for t, nm in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v")):
         _need(t, nm, torch.bfloat16)
     _layout([q1, k1, q2, k2, v], ["q1", "k1", "q2", "k2", "v"])
@@ -319,9 +325,65 @@ def sigattn_diff_fwd(q1, k1, q2, k2, v, seq_lens, lam: float, block_mask=None, m
         want = (B, num_tiles(L, block_q), num_tiles(L, block_k))
         if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
             raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
+    if return_maps:
+        return_lse = True
+        lses = [torch.empty((B, H, L), dtype=torch.float32, device=q1.device) if l_ is None
+                else l_ for l_ in lses]
+        o1 = torch.empty_like(out) if o1 is None else o1
+        o2 = torch.empty_like(out) if o2 is None else o2
+    for om in (o1, o2):
+        if om is not None:
+            _need(om, "o1/o2", torch.bfloat16)
+            if tuple(om.shape) != tuple(out.shape) or om.stride() != out.stride():
+                raise ValueError("o1 and o2 must have out's shape and strides")
     shape = _shape(q1, out.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_diff_fwd(
         ctypes.byref(shape), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v),
         _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), _ptr(key_range), bias,
-        float(lam), _ptr(out), _ptr(lses[0]), _ptr(lses[1]), _stream(stream)))
+        float(lam), _ptr(out), _ptr(o1), _ptr(o2), _ptr(lses[0]), _ptr(lses[1]),
+        _stream(stream)))
+    if return_maps:
+        return out, lses[0], lses[1], o1, o2
     return (out, lses[0], lses[1]) if return_lse else out
+
+
+def sigattn_diff_bwd(q1, k1, q2, k2, v, dout, o1, o2, lse1, lse2, seq_lens, lam: float,
+                     block_mask=None, mask=None, key_range=None, bias=BIAS_NONE, scale=None,
+                     block_q=128, block_k=128, grads=None, stream=None):
+    """Gradients (dq1, dk1, dq2, dk2, dv) of sum(dout * o) for the differential
+    forward; o1, o2, lse1, lse2 from sigattn_diff_fwd(..., return_maps=True)."""
+    for t, nm in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v"), (dout, "dout")):
+        _need(t, nm, torch.bfloat16)
+    _layout([q1, k1, q2, k2, v, dout], ["q1", "k1", "q2", "k2", "v", "dout"])
+    _need(seq_lens, "seq_lens", torch.int32)
+    outs = [torch.empty_like(q1, memory_format=torch.contiguous_format) for _ in range(5)] \
+        if grads is None else list(grads)
+    for g_ in outs:
+        _need(g_, "gradient output", torch.bfloat16)
+    _layout(outs, ["gradient output"] * 5)
+    B, H, L, d = q1.shape
+    for om in (o1, o2):
+        _need(om, "o1/o2", torch.bfloat16)
+        if tuple(om.shape) != tuple(q1.shape) or om.stride() != outs[0].stride():
+            raise ValueError("o1 and o2 must have q1's shape and the gradient outputs' strides")
+    for l_ in (lse1, lse2):
+        _need(l_, "lse", torch.float32)
+        if tuple(l_.shape) != (B, H, L) or not l_.is_contiguous():
+            raise ValueError("lse1/lse2 must be contiguous float32 [B, H, L] tensors")
+    if mask is not None:
+        _need(mask, "mask", torch.uint8)
+        if tuple(mask.shape) != (B, L, L) or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous uint8 [B, L, L] tensor")
+    _key_range(key_range, B, L)
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8)
+        want = (B, num_tiles(L, block_q), num_tiles(L, block_k))
+        if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
+            raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
+    shape = _shape(q1, outs[0].stride(), scale, block_q, block_k)
+    _check(load_library().sigattn_diff_bwd(
+        ctypes.byref(shape), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(dout),
+        _ptr(o1), _ptr(o2), _ptr(lse1), _ptr(lse2), _ptr(seq_lens.contiguous()),
+        _ptr(block_mask), _ptr(mask), _ptr(key_range), bias, float(lam), *(_ptr(g_) for g_ in outs),
+        _stream(stream)))
+    return tuple(outs)

@@ -109,6 +109,7 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
     p->Tq = (s->L + s->block_q - 1) / s->block_q;
     p->Tk = (s->L + s->block_k - 1) / s->block_k;
     p->scale = s->scale > 0.0f ? s->scale : 1.0f / sqrtf((float)s->d);
+    p->grad_scale = 1.0f;
     p->bias_mode = bias_mode;
     p->variant = variant;
     return ok();
@@ -162,8 +163,8 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
 int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
                      const void *k2, const void *v, const int32_t *seq_lens,
                      const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
-                     int32_t bias_mode, float lambda, void *o, float *lse1, float *lse2,
-                     void *stream) {
+                     int32_t bias_mode, float lambda, void *o, void *o1, void *o2, float *lse1,
+                     float *lse2, void *stream) {
     sigattn::AttnParams p = {};
     const void *inputs[5] = {q1, k1, q2, k2, v};
     void *outputs[1] = {o};
@@ -174,6 +175,8 @@ int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1,
     if ((reinterpret_cast<uintptr_t>(lse1) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(lse2) & 3u) != 0)
         return fail(SIGATTN_ERR_ALIGNMENT, "lse1/lse2 is not 4-byte aligned");
+    if (!aligned16(o1) || !aligned16(o2))
+        return fail(SIGATTN_ERR_ALIGNMENT, "o1/o2 is not 16-byte aligned");
     p.q = q1;
     p.k = k1;
     p.q2 = q2;
@@ -182,6 +185,8 @@ int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1,
     p.o = o;
     p.lse = lse1;
     p.lse2 = lse2;
+    p.o1 = o1;
+    p.o2 = o2;
     p.lambda = lambda;
     p.variant = sigattn::kDiff;
     return launch_status(sigattn::launch_fwd(p, (hipStream_t)stream), "sigattn_diff_fwd");
@@ -197,7 +202,7 @@ int backward(const sigattn_shape *shape, const void *q, const void *k, const voi
              const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
              const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
              int32_t bias_mode, int32_t variant, void *dq, void *dk, void *dv, void *stream,
-             int parts, const char *name) {
+             int parts, const char *name, float grad_scale = 1.0f, bool accumulate_dv = false) {
     sigattn::AttnParams p = {};
     const void *inputs[4] = {q, k, v, dout};
     void *outputs[3];
@@ -227,6 +232,8 @@ int backward(const sigattn_shape *shape, const void *q, const void *k, const voi
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
+    p.grad_scale = grad_scale;
+    p.accumulate_dv = accumulate_dv ? 1 : 0;
     hipStream_t s = (hipStream_t)stream;
     if (parts == (kPartDkdv | kPartDq)) return launch_status(sigattn::launch_bwd(p, s), name);
     if (parts & kPartDkdv) return launch_status(sigattn::launch_bwd_dkdv(p, s), name);
@@ -263,5 +270,33 @@ int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, con
 }
 
 const char *sigattn_last_error(void) { return g_last_error; }
+
+int sigattn_diff_bwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
+                     const void *k2, const void *v, const void *dout, const void *o1,
+                     const void *o2, const float *lse1, const float *lse2,
+                     const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
+                     const int32_t *key_range, int32_t bias_mode, float lambda, void *dq1,
+                     void *dk1, void *dq2, void *dk2, void *dv, void *stream) {
+    // Everything the second pass needs is checked before the first is enqueued.
+    if (!isfinite(lambda)) return fail(SIGATTN_ERR_INVALID_ARG, "lambda must be finite");
+    const void *second[7] = {q2, k2, o2, lse2, dq2, dk2, dv};
+    for (const void *ptr : second)
+        if (ptr == nullptr)
+            return fail(SIGATTN_ERR_INVALID_ARG, "the second map's tensors must not be NULL");
+    if (!aligned16(q2) || !aligned16(k2) || !aligned16(o2) || !aligned16(dq2) || !aligned16(dk2))
+        return fail(SIGATTN_ERR_ALIGNMENT, "a second-map tensor is not 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse2) & 3u) != 0)
+        return fail(SIGATTN_ERR_ALIGNMENT, "lse2 is not 4-byte aligned");
+    // Map 1: the softmax backward of (Q1, K1) with dO writes dq1, dk1 and dv.
+    int st = backward(shape, q1, k1, v, dout, o1, lse1, seq_lens, block_mask, mask, key_range,
+                      bias_mode, SIGATTN_SOFTMAX, dq1, dk1, dv, stream, kPartDkdv | kPartDq,
+                      "sigattn_diff_bwd", 1.0f, false);
+    if (st != SIGATTN_OK) return st;
+    // Map 2 enters the output as -lambda O2: its gradients are -lambda times
+    // the softmax backward of (Q2, K2) with dO, and its dV adds to map 1's.
+    return backward(shape, q2, k2, v, dout, o2, lse2, seq_lens, block_mask, mask, key_range,
+                    bias_mode, SIGATTN_SOFTMAX, dq2, dk2, dv, stream, kPartDkdv | kPartDq,
+                    "sigattn_diff_bwd", -lambda, true);
+}
 
 }  // extern "C"

@@ -172,15 +172,23 @@ __device__ __forceinline__ void zero_rows(bf16 *base, int64_t sl, int r0, int ro
 // or exact zeros for a padded row.
 template <int D>
 __device__ __forceinline__ void store_rows_t(bf16 *rowp, const f32x16 *acc, float scale, int hh,
-                                             bool row_valid) {
-    auto out = [&](float x) { return keep_or_zero(x * scale, row_valid); };
+                                             bool row_valid, bool accumulate = false) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bf16x4 v4 = pack4(out(acc[db][4 * i]), out(acc[db][4 * i + 1]),
-                                    out(acc[db][4 * i + 2]), out(acc[db][4 * i + 3]));
-            *reinterpret_cast<bf16x4 *>(rowp + db * 32 + i * 8 + hh * 4) = v4;
+            bf16x4 *dst = reinterpret_cast<bf16x4 *>(rowp + db * 32 + i * 8 + hh * 4);
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * i + e] * scale;
+            if (accumulate) {  // a second pass adds to what the first wrote
+                const bf16x4 old = *dst;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] += (float)old[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = keep_or_zero(x[e], row_valid);
+            *dst = pack4(x[0], x[1], x[2], x[3]);
         }
 }
 
@@ -425,8 +433,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         qt = nxt;
     }
     if (key < L) {
-        store_rows_t<D>(dvb + (int64_t)key * p.osl, dvt, 1.0f, hh, k_valid);
-        store_rows_t<D>(dkb + (int64_t)key * p.osl, dkt, p.scale, hh, k_valid);
+        store_rows_t<D>(dvb + (int64_t)key * p.osl, dvt, p.grad_scale, hh, k_valid,
+                        p.accumulate_dv != 0);
+        store_rows_t<D>(dkb + (int64_t)key * p.osl, dkt, p.scale * p.grad_scale, hh, k_valid);
     }
 }
 
@@ -612,7 +621,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
         if (kt < 0) break;
         step(K1, V1, M1, K0, V0, M0);
     }
-    if (qr < L) store_rows_t<D>(dqb + (int64_t)qr * p.osl, dqt, p.scale, hh, q_valid);
+    if (qr < L) store_rows_t<D>(dqb + (int64_t)qr * p.osl, dqt, p.scale * p.grad_scale, hh, q_valid);
 }
 
 // ---------------------------------------------------------------- kernels

@@ -24,6 +24,7 @@
 // buffer, with one barrier per tile.  Tiles fully inside [0, n) x [0, n)
 // without an element mask take a branch-free epilogue.  Fully padded query
 // tiles only write zeros.
+#include <initializer_list>
 #include <type_traits>
 
 #include "device_common.h"
@@ -121,6 +122,12 @@ fwd_kernel(const AttnParams p) {
         for (int idx = tid; idx < rows * (D / 8); idx += NT) {
             const int r = r0 + idx / (D / 8), c = (idx % (D / 8)) * 8;
             *reinterpret_cast<uint4 *>(ob + (int64_t)r * p.osl + c) = make_uint4(0, 0, 0, 0);
+            if constexpr (MAPS == 2)
+                for (void *om : {p.o1, p.o2})
+                    if (om != nullptr)
+                        *reinterpret_cast<uint4 *>(reinterpret_cast<bf16 *>(om) + b * p.osb +
+                                                   h * p.osh + (int64_t)r * p.osl + c) =
+                            make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int mp = 0; mp < MAPS; ++mp)
@@ -382,7 +389,26 @@ fwd_kernel(const AttnParams p) {
             }
         }
     }
-    if constexpr (MAPS == 2) inv[1] *= -p.lambda;
+    if constexpr (MAPS == 2) {
+        // Each map's own output, when asked for (the backward needs them).
+        if (qr < L) {
+#pragma unroll
+            for (int mp = 0; mp < MAPS; ++mp) {
+                bf16 *om = reinterpret_cast<bf16 *>(mp == 0 ? p.o1 : p.o2);
+                if (om == nullptr) continue;
+                bf16 *orow = om + b * p.osb + h * p.osh + (int64_t)qr * p.osl;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        auto f = [&](int e) { return keep_or_zero(oacc[mp][db][4 * i + e] * inv[mp], q_valid); };
+                        *reinterpret_cast<bf16x4 *>(orow + db * 32 + i * 8 + hh * 4) =
+                            pack4(f(0), f(1), f(2), f(3));
+                    }
+            }
+        }
+        inv[1] *= -p.lambda;
+    }
     if (qr < L) {
         bf16 *orow = ob + (int64_t)qr * p.osl;
         // Padded query rows are exactly +0 whatever their (finite) accumulators hold.

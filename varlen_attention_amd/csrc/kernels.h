@@ -20,6 +20,9 @@ struct AttnParams {
     const void *q2, *k2;            // differential attention: the second map's Q and K
     float *lse2;                    // differential attention: the second map's LSE, or null
     float lambda;                   // differential attention: O = O1 - lambda O2
+    void *o1, *o2;                  // differential forward: each map's own output, or null
+    float grad_scale;               // backward: every gradient times this (1 normally)
+    int accumulate_dv;              // backward: add to dv instead of overwriting it
     const int32_t *seq_lens;        // [B]
     const uint8_t *block_mask;      // [B, Tq, Tk] or null
     const uint8_t *mask;            // [B, L, L] or null
