@@ -65,30 +65,39 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
         }
         const uint32_t zero_byte = ((u.x - 0x01010101u) & ~u.x) | ((u.y - 0x01010101u) & ~u.y) |
                                    ((u.z - 0x01010101u) & ~u.z) | ((u.w - 0x01010101u) & ~u.w);
-        if ((zero_byte & 0x80808080u) == 0u && t0 == t1) {  // every byte valid, one tile
-            bits |= 1u << t0;
+        if ((zero_byte & 0x80808080u) == 0u) {  // every byte valid: its tile(s) kept
+            bits |= (1u << t0) | (1u << t1);
             return;
         }
-        uint8_t bytes[16];
-        *reinterpret_cast<uint4 *>(bytes) = u;
+        // Mixed chunk: one bit per byte (non-zero), bit-parallel.
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        uint32_t nz16 = 0;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const uint64_t p = a + t;
-            if (p >= lo && p < hi) {
-                const uint32_t f = 1u << ((int)((p - row) >> bk_shift) - j0);
-                if (bytes[t] != 0)
-                    bits |= f;
-                else
-                    zbits |= f;
-            }
+        for (int q = 0; q < 4; ++q) {
+            // Bit 7 of each non-zero byte, moved to four adjacent bits.
+            const uint32_t m = (((w[q] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[q]) & 0x80808080u;
+            nz16 |= (((m >> 7) * 0x00204081u) >> 21 & 0xfu) << (4 * q);
         }
+        const int s = (int)(s0 - a), e = (int)(s1 - a);  // in-range bytes [s, e)
+        const uint32_t range16 = ((1u << e) - 1u) & ~((1u << s) - 1u);
+        // Bytes before the start of tile t1 belong to tile t0.
+        const int64_t split = (int64_t)(((uint64_t)(t1 + j0) << bk_shift) + row) - (int64_t)a;
+        const uint32_t first = t1 == t0 ? 0xffffu : (1u << split) - 1u;
+        const uint32_t in0 = range16 & first, in1 = range16 & ~first;
+        if (nz16 & in0) bits |= 1u << t0;
+        if (nz16 & in1) bits |= 1u << t1;
+        if (~nz16 & in0) zbits |= 1u << t0;
+        if (~nz16 & in1) zbits |= 1u << t1;
     };
     if (r_lo < r_hi && c_lo < c_hi) {
-        // Four rows per wave in flight: their loads are issued before any is
-        // examined (eight measured slower).  Chunks that would run past the end of the mask are
-        // read byte by byte (bytes past the end read 0).
+        // Four rows per wave in flight: all their loads are issued before any
+        // is examined (eight rows measured slower).  A row's window of at
+        // most 1024 columns, aligned down to 16 bytes, spans at most 65
+        // chunks: lane l takes chunks l and l + 64, both loaded up front so
+        // no lane waits on a second round trip.  Chunks that would run past
+        // the end of the mask are read byte by byte (bytes past the end 0).
         for (int rb = r_lo + wave; rb < r_hi; rb += 16) {
-            uint4 u[4];
+            uint4 u[4][2];
             uint64_t arow[4], alo[4], ahi[4], a0[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -97,26 +106,28 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
                 alo[t] = arow[t] + c_lo;
                 ahi[t] = r < r_hi ? arow[t] + c_hi : 0;  // rows past r_hi: nothing
                 a0[t] = (alo[t] & ~(uint64_t)15) + 16u * lane;
-                u[t] = make_uint4(0u, 0u, 0u, 0u);
-                if (a0[t] < ahi[t] && a0[t] + 16 <= total)
-                    u[t] = *reinterpret_cast<const uint4 *>(mask + a0[t]);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const uint64_t a = a0[t] + 1024u * k;
+                    u[t][k] = make_uint4(0u, 0u, 0u, 0u);
+                    if (a < ahi[t] && a + 16 <= total)
+                        u[t][k] = *reinterpret_cast<const uint4 *>(mask + a);
+                }
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                for (uint64_t a = a0[t]; a < ahi[t]; a += 16u * 64) {
-                    uint4 v = u[t];
-                    if (a != a0[t] || a + 16 > total) {
-                        if (a + 16 <= total) {
-                            v = *reinterpret_cast<const uint4 *>(mask + a);
-                        } else {
-                            uint8_t bb[16];
-                            for (int e = 0; e < 16; ++e) bb[e] = (a + e < total) ? mask[a + e] : 0;
-                            v = *reinterpret_cast<const uint4 *>(bb);
-                        }
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const uint64_t a = a0[t] + 1024u * k;
+                    if (a >= ahi[t]) continue;
+                    uint4 v = u[t][k];
+                    if (a + 16 > total) {
+                        uint8_t bb[16];
+                        for (int e = 0; e < 16; ++e) bb[e] = (a + e < total) ? mask[a + e] : 0;
+                        v = *reinterpret_cast<const uint4 *>(bb);
                     }
                     chunk(v, a, arow[t], alo[t], ahi[t]);
                 }
-            }
         }
     }
     if (bits) atomicOr(&flags, bits);
