@@ -1,14 +1,16 @@
-// Backward pass for sigmoid attention on gfx950: dK/dV work items and dQ work
-// items (each kind its own kernel, or both in one grid), no atomics, scores
-// and weights recomputed on the fly
+// Backward pass on gfx950 (sigmoid, and the softmax variants from the
+// forward's LSE): dK/dV work items and dQ work items (each kind its own
+// kernel, or both in one grid), no atomics, scores and weights recomputed on
+// the fly
 // ("Better Models, Faster Training: Sigmoid Attention for single-cell
 // Foundation Models", section 2.C).  The Jacobian of element-wise sigmoid
 // attention is diagonal (section 2.B), so with P = sigma(S) and
 // dP = dO V^T the score gradient is dS = dP * P * (1 - P), element by element.
 //
 // dK/dV item: a workgroup of NW waves owns 32*NW keys of one (batch entry,
-// head); each wave holds its 32 K and V rows in registers and walks the query
-// tiles whose block-mask entry is 1 (one column of the block matrix):
+// head); each wave holds its 32 K rows in registers, and its V rows in
+// registers (d = 64) or LDS (d = 128), and walks the query tiles whose
+// block-mask entry is non-zero (one column of the block matrix):
 //   S  = Q K^T,  dP = dO V^T            (Q, dO rows from LDS)
 //   dV^T += dO^T P,  dK^T += Q^T dS     (P, dS stay in registers; Q^T and dO^T
 //                                        come from transposing LDS reads)
@@ -22,8 +24,8 @@
 // into LDS for dQ (its K and V buffers are separate LDS objects and its loop
 // is unrolled by two, so the compiler sees the buffer being filled is not the
 // one being read; the freed staging registers let S and dP keep separate
-// accumulators).  The two kinds of
-// item write disjoint outputs.
+// accumulators).  The two kinds of item write disjoint outputs.  Element
+// masks arrive per tile as LDS bits, as in the forward kernel.
 #include <type_traits>
 
 #include "device_common.h"

@@ -1,5 +1,7 @@
 // Forward kernel: fused, tiled attention over a padded variable-length batch
-// for gfx950 (sigmoid, online softmax and softmax_1 through one tile loop).
+// for gfx950 (sigmoid, online softmax and softmax_1 through one tile loop, and
+// differential attention: two softmax maps over one V, "Differential
+// Transformer" note, "How differential attention works").
 //
 // Method: "Better Models, Faster Training: Sigmoid Attention for single-cell
 // Foundation Models", section 2.A (sigma(QK^T/sqrt(d) + b) V, b = -log n) and
@@ -21,9 +23,11 @@
 // softmax row statistics are lane-local plus one exchange with lane ^ 32.
 // K and V tiles are double-buffered in LDS: the next tile's rows are fetched
 // into registers while the current tile computes, then written to the other
-// buffer, with one barrier per tile.  Tiles fully inside [0, n) x [0, n)
-// without an element mask take a branch-free epilogue.  Fully padded query
-// tiles only write zeros.
+// buffer, with one barrier per tile.  An element mask (dense bytes or key
+// ranges) is staged per tile as bits in LDS next to K and V (MaskStage /
+// RangeStage); full tiles (block-mask bit 1) need none, and a wave whose
+// share of a tile keeps nothing skips it.  Fully padded query tiles only
+// write zeros.
 #include <initializer_list>
 #include <type_traits>
 
