@@ -90,6 +90,9 @@ typedef enum {
  * the input strides".  Every base pointer and every stride must be a multiple
  * of 16 bytes (8 bf16 elements).
  */
+/* Sizes: B, H <= 65535 and 2 * B * H * ceil(L / 32) < 2^31 (one launch's
+ * work items); larger problems are UNSUPPORTED and are split by the caller
+ * (along B or H: the work is independent). */
 typedef struct {
     int32_t B, H, L, d;       /* batch, heads, padded length, head dim (64 or 128) */
     int64_t stride_b, stride_h, stride_l;       /* Q, K, V, dO */

@@ -60,6 +60,8 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, va, _shape(va, d=96)) == va.ERR_UNSUPPORTED
     assert _fwd(lib, va, _shape(va, B=0)) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va, block_q=48)) == va.ERR_UNSUPPORTED
+    # Too many work items for one launch (2 * B * H * ceil(L / 32) >= 2^31).
+    assert _fwd(lib, va, _shape(va, B=65535, H=1024, L=10000)) == va.ERR_UNSUPPORTED
     assert _fwd(lib, va, _shape(va), q=None) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va), seq=None) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va), o=None) == va.ERR_INVALID_ARG

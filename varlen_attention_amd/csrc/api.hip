@@ -46,6 +46,10 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
                     s->B, s->H, s->L);
     if (s->B > 65535 || s->H > 65535)
         return fail(SIGATTN_ERR_UNSUPPORTED, "B and H must be at most 65535");
+    // One launch holds up to two work items per (batch entry, head) and
+    // 32-row tile; their count must fit the 32-bit grid and indices.
+    if ((int64_t)s->B * s->H * ((s->L + 31) / 32) * 2 > INT32_MAX)
+        return fail(SIGATTN_ERR_UNSUPPORTED, "B * H * L too large for one launch");
     if (s->d != 64 && s->d != 128)
         return fail(SIGATTN_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", s->d);
     if (!block_size_ok(s->block_q) || !block_size_ok(s->block_k))
