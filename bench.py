@@ -379,6 +379,12 @@ def run_suite(args) -> int:
     def gpu(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
+    def workload(w, variant, mask_form, block, tiles):
+        return {"seed": args.seed, "B": w.B, "H": w.H, "L": w.L, "d": w.d,
+                "sum_n": int(w.seq_lens.sum()), "valid_pairs": int(w.valid_pairs) * w.H,
+                "kept_tiles": tiles, "block": block, "mask": mask_form,
+                "variant": ("sigmoid", "softmax", "softmax_1", "differential")[int(variant)]}
+
     def case(label, w, variant=syn.SIGMOID, bias=syn.BIAS_LOG_SEQLEN, block=128, kernels=("fwd", "bwd"),
              cold=True, ranges=False):
         """Times blockmask_build, fwd and bwd of workload w; one table row each.
@@ -422,11 +428,15 @@ def run_suite(args) -> int:
             if kern in per_pair:
                 r["valid_tf"] = per_pair[kern] * pairs / (med * 1e-6) / 1e12
                 r["tile_tf"] = per_pair[kern] * tiles * block * block / (med * 1e-6) / 1e12
+            r.update(workload(w, variant, "key ranges" if ranges else
+                              ("dense" if mask is not None else "none"), block, tiles))
             rows.append(r)
             log(f"  {kern}: warm median {med:.2f} us, min {warm[:, j].min():.2f} us"
                 + (f", cold median {np.median(cold_t):.2f} us" if cold else ""))
         flops = sum(per_pair[kern] for kern in kernels) * pairs
-        rows.append({"case": label, "kernel": "step", "warm_med_us": float(np.median(tot)),
+        rows.append({**workload(w, variant, "key ranges" if ranges else
+                                ("dense" if mask is not None else "none"), block, tiles),
+                     "case": label, "kernel": "step", "warm_med_us": float(np.median(tot)),
                      "warm_min_us": float(tot.min()), "cold_med_us": None,
                      "valid_tf": flops / (np.median(tot) * 1e-6) / 1e12,
                      "tile_tf": flops / pairs * tiles * block * block / (np.median(tot) * 1e-6) / 1e12,
@@ -494,7 +504,8 @@ def run_suite(args) -> int:
     for j, (kern, maps, fpp, rd, wr) in enumerate(kinds):
         med = float(np.median(warm[:, j]))
         algo = (rd * valid_rows + wr * all_rows) * 2.0 * wd.d
-        rows.append({"case": label, "kernel": kern, "warm_med_us": med,
+        rows.append({**workload(wd, 3 if j in (0, 3) else syn.SOFTMAX, "none", 128, tiles),
+                     "case": label, "kernel": kern, "warm_med_us": med,
                      "warm_min_us": float(warm[:, j].min()),
                      "cold_med_us": float(np.median(cold)) if j == 0 else None,
                      "valid_tf": fpp * wd.d * maps * pairs / (med * 1e-6) / 1e12,
@@ -519,6 +530,14 @@ def run_suite(args) -> int:
           "counts every pair of the tiles the block mask keeps; GB/s is algorithmic bytes "
           "(valid input rows read once, every output row written once).")
     print()
+    if args.suite_jsonl:
+        with open(args.suite_jsonl, "w") as f:
+            for r in rows:
+                f.write(json.dumps({**r, "peak_bf16_tflops": PEAK_BF16_TFLOPS,
+                                    "frac_peak_valid": (r["valid_tf"] / PEAK_BF16_TFLOPS
+                                                        if r.get("valid_tf") else None),
+                                    "frac_hbm": (r["gbs"] / PEAK_HBM_GBS if r.get("gbs") else None)})
+                        + "\n")
     print("| case | kernel | warm median (us) | warm min (us) | cold median (us) | valid TFLOP/s | "
           "tile TFLOP/s | algorithmic GB/s |")
     print("|---|---|---|---|---|---|---|---|")
@@ -549,6 +568,8 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--suite", action="store_true",
                     help="run the measurement suite (markdown on stdout) instead of the step")
+    ap.add_argument("--suite-jsonl", metavar="PATH",
+                    help="with --suite: also write one JSON line per measured row to PATH")
     args = ap.parse_args()
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats, args.skip_dispatches))
