@@ -229,7 +229,9 @@ template <int D> constexpr bool kVInLds = D == 128;
 // dK and dV of key tile kt (32 NW keys) of (batch entry b, head h); smem
 // holds kDkdvLds<D> elements, mbits kMaskWords words (element mask only),
 // vt this wave's 32 x D elements when kVInLds<D>.
-template <int D, int NW, int VARIANT, int MASK>
+// C: block-mask columns per workgroup (BKV / block_k); wave w follows column
+// w * C / NW and works only on the query tiles that column keeps.
+template <int D, int NW, int VARIANT, int MASK, int C>
 __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int kt, int n,
                                           bf16 *smem, uint32_t *mbits, bf16 *vt) {
     constexpr bool MASKED = MASK != kMaskNone;
@@ -322,28 +324,33 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     if constexpr (kSoft) stats.init(p.osl, tid);
     Mask mstage;
     if constexpr (MASKED) mstage.init(tid);
-    // full: the tile lies in a full block-mask entry (no element-mask reads).
-    auto load_tile = [&](int t, bool full) {
+    // want: what this wave needs of the tile's element mask (kWant*).
+    auto load_tile = [&](int t, int want) {
         stage.load(rows_rsrc(qb, t * BQ), rows_rsrc(dob, t * BQ));
         if constexpr (kSoft) stats.load(out_rows_rsrc(obase, t * BQ), lseb + t * BQ, n - t * BQ, tid);
-        if constexpr (MASKED) mstage.load(msrc, n, t * BQ, k0, full);
+        if constexpr (MASKED) mstage.load(msrc, n, t * BQ, k0, want);
     };
-    auto store_tile = [&](int i, int t, bool full) {
+    auto store_tile = [&](int i, int t, int want) {
         stage.store(Qs(i), dOs(i));
         if constexpr (kSoft) stats.store(stage.b, c0, Dl(i), Offl(i), tid);
-        if constexpr (MASKED) mcls = mstage.store(Ml(i), t * BQ, k0, n, full);
+        if constexpr (MASKED) mcls = mstage.store(Ml(i), t * BQ, k0, n, want);
     };
     // Query tile 0 is fetched before the block mask is read (see the forward
     // kernel); another first tile is fetched again.
-    load_tile(0, false);
-    TileSchedule<BQ> sched;
-    sched.init(p.block_mask ? p.block_mask + (int64_t)b * p.Tq * p.Tk + k0 / p.block_k : nullptr,
-               p.Tk, n, p.block_q);
+    load_tile(0, kWantMask);
+    const int line0 = k0 / p.block_k;  // first block-mask column of this tile
+    const int wl = w * C / NW;        // this wave's column (0 .. C - 1)
+    const int lines = p.block_mask ? min(C, p.Tk - line0)
+                                   : min(C, (n - k0 + p.block_k - 1) / p.block_k);
+    TileSchedule<BQ, C> sched;
+    sched.init(p.block_mask ? p.block_mask + (int64_t)b * p.Tq * p.Tk + line0 : nullptr, p.Tk, 1,
+               lines, n, p.block_q);
     int qt = sched.next();
-    const bool qt_full = sched.full;
-    if (qt > 0) load_tile(qt, qt_full);
+    const int qt_want = want_of(sched.on, sched.full, wl);
+    bool on = qt_want != kWantNone;  // this wave's column keeps the current tile
+    if (qt > 0) load_tile(qt, qt_want);
     int buf = 0;
-    store_tile(0, qt < 0 ? 0 : qt, qt_full);
+    store_tile(0, qt < 0 ? 0 : qt, qt_want);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         if constexpr (!kSoft) kreg[ks] = scale8(kreg[ks], c1);
@@ -353,10 +360,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     padded_share<BKV>(kt, n, L, zero_tile);
 
     while (qt >= 0) {
-        const int q0 = qt * BQ;
         const int nxt = sched.next();
-        const bool nxt_full = sched.full;
-        if (nxt >= 0) load_tile(nxt, nxt_full);
+        const int nxt_want = want_of(sched.on, sched.full, wl);
+        if (nxt >= 0) load_tile(nxt, nxt_want);
         const bf16 *Qc = Qs(buf);
         const bf16 *dOc = dOs(buf);
         const float *Dc = Dl(buf);
@@ -426,10 +432,11 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
             // This wave's 32 x 32 entries, as found when it staged them: none
             // kept means no work.
             if (mcls != kSkip) tile(std::integral_constant<int, 2>{});
-        } else {
+        } else if (C == 1 || on) {
             tile(std::integral_constant<int, 0>{});
         }
-        if (nxt >= 0) store_tile(buf ^ 1, nxt, nxt_full);
+        if (nxt >= 0) store_tile(buf ^ 1, nxt, nxt_want);
+        on = nxt_want != kWantNone;
         __syncthreads();
         buf ^= 1;
         qt = nxt;
@@ -445,7 +452,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
 // dQ of query tile qt (32 NW queries) of (batch entry b, head h), visiting
 // keys 32 KB at a time.  K0, V0, K1, V1 are four separate LDS objects of
 // 32 KB rows x D each (two buffers of the K and V tiles).
-template <int D, int NW, int KB, int VARIANT, int MASK>
+// R: block-mask rows per workgroup (BQ / block_q); wave w follows row
+// w * R / NW.
+template <int D, int NW, int KB, int VARIANT, int MASK, int R>
 __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int qt, int n,
                                         bf16 *K0, bf16 *V0, bf16 *K1, bf16 *V1,
                                         uint32_t *mbits) {
@@ -532,15 +541,21 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     fetch(0, K0, V0);
     Mask mstage;
     if constexpr (MASKED) mstage.init(tid);
-    TileSchedule<BK> sched;
-    sched.init(p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + q0 / p.block_q) * p.Tk : nullptr,
-               1, n, p.block_k);
+    const int line0 = q0 / p.block_q;  // first block-mask row of this tile
+    const int wl = w * R / NW;        // this wave's row (0 .. R - 1)
+    const int lines = p.block_mask ? min(R, p.Tq - line0)
+                                   : min(R, (n - q0 + p.block_q - 1) / p.block_q);
+    TileSchedule<BK, R> sched;
+    sched.init(p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + line0) * p.Tk : nullptr, 1,
+               p.Tk, lines, n, p.block_k);
     int kt = sched.next();
+    const int kt_want = want_of(sched.on, sched.full, wl);
+    bool on = kt_want != kWantNone;  // this wave's row keeps the current tile
     if (kt > 0) fetch(kt, K0, V0);
     if constexpr (MASKED)
         if (kt >= 0) {
-            mstage.load(msrc, n, q0, kt * BK, sched.full);
-            mcls = mstage.store(M0, q0, kt * BK, n, sched.full);
+            mstage.load(msrc, n, q0, kt * BK, kt_want);
+            mcls = mstage.store(M0, q0, kt * BK, n, kt_want);
         }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -553,10 +568,10 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     auto step = [&](const bf16 *Kc, const bf16 *Vc, const uint32_t *Mc, bf16 *Kn, bf16 *Vn,
                     uint32_t *Mn) {
         const int nxt = sched.next();
-        const bool nxt_full = sched.full;
+        const int nxt_want = want_of(sched.on, sched.full, wl);
         if (nxt >= 0) fetch(nxt, Kn, Vn);
         if constexpr (MASKED)
-            if (nxt >= 0) mstage.load(msrc, n, q0, nxt * BK, nxt_full);
+            if (nxt >= 0) mstage.load(msrc, n, q0, nxt * BK, nxt_want);
         // MODE 0 (no element mask): padded key rows of K and V read as zeros,
         // so dP = 0 and dS = 0 there; padded query rows are zeroed at the
         // store.  MODE 2: element mask.
@@ -609,11 +624,12 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
             // The wave's entries of this tile, as found when it staged them:
             // none kept means no work.
             if (mcls != kSkip) tile(std::integral_constant<int, 2>{});
-        } else {
+        } else if (R == 1 || on) {
             tile(std::integral_constant<int, 0>{});
         }
         if constexpr (MASKED)
-            if (nxt >= 0) mcls = mstage.store(Mn, q0, nxt * BK, n, nxt_full);
+            if (nxt >= 0) mcls = mstage.store(Mn, q0, nxt * BK, n, nxt_want);
+        on = nxt_want != kWantNone;
         wait_vm0();
         __syncthreads();
         kt = nxt;
@@ -627,7 +643,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
 }
 
 // ---------------------------------------------------------------- kernels
-template <int D, int NW, int VARIANT, int MASK>
+template <int D, int NW, int VARIANT, int MASK, int C>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
@@ -637,10 +653,10 @@ bwd_dkdv_kernel(const AttnParams p) {
     int b, h, kt, n;
     if (!tile_item<BKV>(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt, n)) return;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    dkdv_tile<D, NW, VARIANT, MASK>(p, b, h, kt, n, smem, mbits, vts + w * 32 * D);
+    dkdv_tile<D, NW, VARIANT, MASK, C>(p, b, h, kt, n, smem, mbits, vts + w * 32 * D);
 }
 
-template <int D, int NW, int KB, int VARIANT, int MASK>
+template <int D, int NW, int KB, int VARIANT, int MASK, int R>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_dq_kernel(const AttnParams p) {
     constexpr int kTile = 32 * KB * D;
@@ -649,128 +665,133 @@ bwd_dq_kernel(const AttnParams p) {
     constexpr int BQ = 32 * NW;
     int b, h, qt, n;
     if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
-    dq_tile<D, NW, KB, VARIANT, MASK>(p, b, h, qt, n, K0, V0, K1, V1, mbits);
+    dq_tile<D, NW, KB, VARIANT, MASK, R>(p, b, h, qt, n, K0, V0, K1, V1, mbits);
 }
 
 // dK/dV and dQ in one launch: both kinds of tile of a (batch entry, head)
 // pair are dealt out together, longest sequences first, so the two share one
 // ramp-up and one tail.  Needs the same 32 NW rows for the key tiles of
 // dK/dV and the query tiles of dQ.
-template <int D, int NW, int KB, int VARIANT, int MASK>
+// R: block-mask rows and columns per workgroup (block_q == block_k).
+template <int D, int NW, int KB, int VARIANT, int MASK, int R>
 __global__ void __launch_bounds__(64 * NW, 2)
 bwd_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
     constexpr int kTile = 32 * KB * D;
     __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
     __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
-    constexpr int R = 32 * NW;
-    const int nt = (p.L + R - 1) / R;
+    constexpr int ROWS = 32 * NW;
+    const int nt = (p.L + ROWS - 1) / ROWS;
     int b, h, kind, t, n;
-    if (!tile_item2<R, R>(p.seq_lens, p.B, p.H, p.L, nt, nt, b, h, kind, t, n)) return;
+    if (!tile_item2<ROWS, ROWS>(p.seq_lens, p.B, p.H, p.L, nt, nt, b, h, kind, t, n)) return;
     if (kind == 0) {
         // A workgroup does one kind of work: the dQ key buffers, each 32 KB
         // rows x D, hold the dK/dV waves' V rows (32 rows each when KB = 1).
         static_assert(!kVInLds<D> || (KB == 1 && NW <= 4), "V rows need one dQ buffer per wave");
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         bf16 *vt = w == 0 ? K0 : w == 1 ? V0 : w == 2 ? K1 : V1;
-        dkdv_tile<D, NW, VARIANT, MASK>(p, b, h, t, n, smem, mbits, vt);
+        dkdv_tile<D, NW, VARIANT, MASK, R>(p, b, h, t, n, smem, mbits, vt);
     }
     else
-        dq_tile<D, NW, KB, VARIANT, MASK>(p, b, h, t, n, K0, V0, K1, V1, mbits);
+        dq_tile<D, NW, KB, VARIANT, MASK, R>(p, b, h, t, n, K0, V0, K1, V1, mbits);
 }
 
-// Waves per workgroup: 32 NW keys per dK/dV workgroup must divide block_k,
-// 32 NW queries per dQ workgroup must divide block_q; dQ visits keys 32 KB at
-// a time with 32 KB dividing block_k.
-static int dkdv_waves(const AttnParams &p) { return p.block_k >= 128 ? 4 : p.block_k / 32; }
-static int dq_waves(const AttnParams &p) { return p.block_q >= 128 ? 4 : p.block_q / 32; }
+// Every workgroup runs four waves: 128 keys (dK/dV) or 128 queries (dQ), the
+// block-mask columns or rows those cover (1, 2 or 4) given as a template
+// argument.  dQ visits keys 32 KB at a time with 32 KB dividing block_k.
+constexpr int kBwdWaves = 4;
+static int dkdv_cols(const AttnParams &p) { return 32 * kBwdWaves / p.block_k; }
+static int dq_rows(const AttnParams &p) { return 32 * kBwdWaves / p.block_q; }
 // At d = 128 the dQ step visits 32 keys: with two 32-key blocks its S, dP and
 // operand registers no longer fit without spilling.
 static int dq_key_blocks(const AttnParams &p) { return p.block_k >= 64 && p.d == 64 ? 2 : 1; }
 
 template <int D, int VARIANT>
 static hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
-    const int nw = dkdv_waves(p);
-    const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
-    dim3 block(64 * nw);
-#define SIGATTN_DKDV_CASE(NW_)                                                                 \
-    if (nw == NW_) {                                                                           \
+    constexpr int NW = kBwdWaves;
+    const int cols = dkdv_cols(p);
+    const dim3 grid = tile_grid((p.L + 32 * NW - 1) / (32 * NW), p.B, p.H);
+    dim3 block(64 * NW);
+#define SIGATTN_DKDV_CASE(C_)                                                                  \
+    if (cols == C_) {                                                                          \
         if (p.mask != nullptr)                                                                 \
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, VARIANT, kMaskDense>), grid, block, 0, \
-                               stream, p);                                                     \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, VARIANT, kMaskDense, C_>), grid, block, \
+                               0, stream, p);                                                  \
         else if (p.key_range != nullptr)                                                       \
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, VARIANT, kMaskRange>), grid, block, 0, \
-                               stream, p);                                                     \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, VARIANT, kMaskRange, C_>), grid, block, \
+                               0, stream, p);                                                  \
         else                                                                                   \
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW_, VARIANT, kMaskNone>), grid, block, 0,  \
-                               stream, p);                                                     \
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, VARIANT, kMaskNone, C_>), grid, block,  \
+                               0, stream, p);                                                  \
         return hipGetLastError();                                                              \
     }
-    SIGATTN_DKDV_CASE(4)
-    SIGATTN_DKDV_CASE(2)
     SIGATTN_DKDV_CASE(1)
+    SIGATTN_DKDV_CASE(2)
+    SIGATTN_DKDV_CASE(4)
 #undef SIGATTN_DKDV_CASE
     return hipErrorInvalidValue;
 }
 
 template <int D, int VARIANT>
 static hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
-    const int nw = dq_waves(p), kb = dq_key_blocks(p);
-    const dim3 grid = tile_grid((p.L + 32 * nw - 1) / (32 * nw), p.B, p.H);
-    dim3 block(64 * nw);
-#define SIGATTN_DQ_CASE(NW_, KB_)                                                                 \
-    if constexpr (D == 64 || KB_ == 1)                                                            \
-    if (nw == NW_ && kb == KB_) {                                                                 \
-        if (p.mask != nullptr)                                                                    \
-            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, VARIANT, kMaskDense>), grid, block, 0, \
-                               stream, p);                                                        \
-        else if (p.key_range != nullptr)                                                          \
-            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, VARIANT, kMaskRange>), grid, block, 0, \
-                               stream, p);                                                        \
-        else                                                                                      \
-            hipLaunchKernelGGL((bwd_dq_kernel<D, NW_, KB_, VARIANT, kMaskNone>), grid, block, 0,  \
-                               stream, p);                                                        \
-        return hipGetLastError();                                                                 \
+    constexpr int NW = kBwdWaves;
+    const int rows = dq_rows(p), kb = dq_key_blocks(p);
+    const dim3 grid = tile_grid((p.L + 32 * NW - 1) / (32 * NW), p.B, p.H);
+    dim3 block(64 * NW);
+#define SIGATTN_DQ_CASE(R_, KB_)                                                                 \
+    if constexpr (D == 64 || KB_ == 1)                                                           \
+    if (rows == R_ && kb == KB_) {                                                               \
+        if (p.mask != nullptr)                                                                   \
+            hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KB_, VARIANT, kMaskDense, R_>), grid, block, \
+                               0, stream, p);                                                    \
+        else if (p.key_range != nullptr)                                                         \
+            hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KB_, VARIANT, kMaskRange, R_>), grid, block, \
+                               0, stream, p);                                                    \
+        else                                                                                     \
+            hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KB_, VARIANT, kMaskNone, R_>), grid, block,  \
+                               0, stream, p);                                                    \
+        return hipGetLastError();                                                                \
     }
-    SIGATTN_DQ_CASE(4, 2)
-    SIGATTN_DQ_CASE(4, 1)
-    SIGATTN_DQ_CASE(2, 2)
-    SIGATTN_DQ_CASE(2, 1)
     SIGATTN_DQ_CASE(1, 2)
     SIGATTN_DQ_CASE(1, 1)
+    SIGATTN_DQ_CASE(2, 2)
+    SIGATTN_DQ_CASE(2, 1)
+    SIGATTN_DQ_CASE(4, 2)
+    SIGATTN_DQ_CASE(4, 1)
 #undef SIGATTN_DQ_CASE
     return hipErrorInvalidValue;
 }
 
 template <int D, int VARIANT>
 static hipError_t launch_bwd_d(const AttnParams &p, hipStream_t stream) {
-    const int nw = dkdv_waves(p), kb = dq_key_blocks(p);
-    if (nw != dq_waves(p)) {  // different tile heights: two launches
+    constexpr int NW = kBwdWaves;
+    const int lines = dq_rows(p), kb = dq_key_blocks(p);
+    if (lines != dkdv_cols(p)) {  // block_q != block_k: two launches
         hipError_t e = launch_dkdv_d<D, VARIANT>(p, stream);
         return e != hipSuccess ? e : launch_dq_d<D, VARIANT>(p, stream);
     }
-    const dim3 grid = tile_grid(2 * ((p.L + 32 * nw - 1) / (32 * nw)), p.B, p.H);
-    dim3 block(64 * nw);
-#define SIGATTN_BWD_CASE(NW_, KB_)                                                             \
+    const dim3 grid = tile_grid(2 * ((p.L + 32 * NW - 1) / (32 * NW)), p.B, p.H);
+    dim3 block(64 * NW);
+#define SIGATTN_BWD_CASE(R_, KB_)                                                              \
     if constexpr (D == 64 || KB_ == 1)                                                         \
-    if (nw == NW_ && kb == KB_) {                                                              \
+    if (lines == R_ && kb == KB_) {                                                            \
         if (p.mask != nullptr)                                                                 \
-            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, VARIANT, kMaskDense>), grid, block, 0, \
-                               stream, p);                                                     \
+            hipLaunchKernelGGL((bwd_kernel<D, NW, KB_, VARIANT, kMaskDense, R_>), grid, block, \
+                               0, stream, p);                                                  \
         else if (p.key_range != nullptr)                                                       \
-            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, VARIANT, kMaskRange>), grid, block, 0, \
-                               stream, p);                                                     \
+            hipLaunchKernelGGL((bwd_kernel<D, NW, KB_, VARIANT, kMaskRange, R_>), grid, block, \
+                               0, stream, p);                                                  \
         else                                                                                   \
-            hipLaunchKernelGGL((bwd_kernel<D, NW_, KB_, VARIANT, kMaskNone>), grid, block, 0,  \
-                               stream, p);                                                     \
+            hipLaunchKernelGGL((bwd_kernel<D, NW, KB_, VARIANT, kMaskNone, R_>), grid, block,  \
+                               0, stream, p);                                                  \
         return hipGetLastError();                                                              \
     }
-    SIGATTN_BWD_CASE(4, 2)
-    SIGATTN_BWD_CASE(4, 1)
-    SIGATTN_BWD_CASE(2, 2)
-    SIGATTN_BWD_CASE(2, 1)
     SIGATTN_BWD_CASE(1, 2)
     SIGATTN_BWD_CASE(1, 1)
+    SIGATTN_BWD_CASE(2, 2)
+    SIGATTN_BWD_CASE(2, 1)
+    SIGATTN_BWD_CASE(4, 2)
+    SIGATTN_BWD_CASE(4, 1)
 #undef SIGATTN_BWD_CASE
     return hipErrorInvalidValue;
 }

@@ -100,31 +100,42 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70);
 // wave ballot reads 64 block-mask entries at a time; the result is uniform,
 // so the schedule lives in scalar registers.  A null block mask marks all
 // entries active (padding only).  Entry e is read at bm[e * stride].
-template <int BT>
+// The kernel tiles along R adjacent lines of the block matrix (block rows for
+// the query side, block columns for dK/dV) that one workgroup's waves share:
+// a tile is visited when any line keeps it, and bit r of `on` / `full` says
+// whether line r keeps it / whether that entry is full.  A wave works only on
+// the tiles its own line keeps, so every element still obeys its own entry.
+// Lines at or past `lines` are off.
+template <int BT, int R = 1>
 struct TileSchedule {
-    const uint8_t *bm;  // first entry, or null
-    int64_t stride;     // distance between consecutive entries
-    int nblk;           // block-mask entries covering [0, n)
-    int per_blk;        // kernel tiles per block-mask entry
-    int nkt;            // kernel tiles covering [0, n)
+    const uint8_t *bm;        // line 0's first entry, or null (from seq_lens)
+    int64_t stride, lstride;  // between consecutive entries; between lines
+    int nlines;               // lines that exist
+    int nblk;                 // block-mask entries covering [0, n)
+    int per_blk;              // kernel tiles per block-mask entry
+    int nkt;                  // kernel tiles covering [0, n)
     int wbase, entry, sub;
-    uint64_t act, fullm;  // kept / full entries of the 64 at wbase
-    bool full;            // the tile next() returned lies in a full entry
+    uint64_t act;             // entries (of the 64 at wbase) some line keeps
+    uint64_t onm[R], fullm[R];
+    uint32_t on, full;        // per line, for the tile next() returned
 
-    __device__ __forceinline__ void init(const uint8_t *first, int64_t step, int n, int block) {
+    __device__ __forceinline__ void init(const uint8_t *first, int64_t step, int64_t line_step,
+                                         int lines, int n, int block) {
         bm = first;
         stride = step;
+        lstride = line_step;
+        nlines = lines;
         nblk = (n + block - 1) / block;
         per_blk = block / BT;
         nkt = (n + BT - 1) / BT;
         wbase = -64;
         entry = -1;
         sub = 0;
-        act = fullm = 0;
-        full = false;
+        act = 0;
+        on = full = 0;
     }
 
-    // Next active kernel tile index, or -1.
+    // Next kernel tile some line keeps, or -1.
     __device__ __forceinline__ int next() {
         if (entry >= 0 && sub + 1 < per_blk && entry * per_blk + sub + 1 < nkt) {
             ++sub;
@@ -134,13 +145,23 @@ struct TileSchedule {
             wbase += 64;
             if (wbase >= nblk) return -1;
             const int e = wbase + (int)(threadIdx.x & 63);
-            const int v = e < nblk ? (bm == nullptr ? 1 : (int)bm[e * stride]) : 0;
-            act = __ballot(v != 0);
-            fullm = __ballot((v & 2) != 0);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int v = e < nblk && r < nlines
+                                  ? (bm == nullptr ? 1 : (int)bm[r * lstride + e * stride]) : 0;
+                onm[r] = __ballot(v != 0);
+                fullm[r] = __ballot((v & 2) != 0);
+                act |= onm[r];
+            }
         }
         const int bit = __builtin_ctzll(act);
         entry = wbase + bit;
-        full = (fullm >> bit) & 1u;
+        on = full = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            on |= (uint32_t)((onm[r] >> bit) & 1u) << r;
+            full |= (uint32_t)((fullm[r] >> bit) & 1u) << r;
+        }
         act &= act - 1;
         sub = 0;
         return entry * per_blk;
@@ -399,6 +420,13 @@ __device__ __forceinline__ constexpr int key_bit(int t) {
     return MASK == kMaskDense ? mask_bit(t) : t;
 }
 
+// What a wave stages for a tile: nothing (its block-mask line leaves the
+// tile out), all-ones words (its entry is full) or the mask itself.
+enum { kWantNone = 0, kWantFull = 1, kWantMask = 2 };
+__device__ __forceinline__ int want_of(uint32_t on, uint32_t full, int line) {
+    return !((on >> line) & 1u) ? kWantNone : ((full >> line) & 1u) ? kWantFull : kWantMask;
+}
+
 // What a wave's share of a masked tile needs, from the OR and the AND of the
 // mask words its lanes hold: kSkip (no entry kept: no work at all), kDense
 // (every entry kept) or kMixed.
@@ -435,10 +463,10 @@ struct MaskStage {
     // src.bytes covers exactly the batch entry's L x L mask; L * L fits in
     // int.  Words of rows or keys at or past n are not read (store clears
     // them), nor any word of a full tile (every entry valid: store writes ones).
-    __device__ __forceinline__ void load(const MaskSource &src, int n, int r0, int k0, bool full) {
+    __device__ __forceinline__ void load(const MaskSource &src, int n, int r0, int k0, int want) {
         lo = hi = make_uint4(0u, 0u, 0u, 0u);
         const int row = r0 + r, key = k0 + 32 * wi, L = src.L;
-        if (full || !act || row >= n || key >= n) return;
+        if (want != kWantMask || !act || row >= n || key >= n) return;
         const int off = row * L + key;
         if (off + 32 <= L * L) {
             lo = buffer_load16(src.bytes, off);
@@ -458,8 +486,9 @@ struct MaskStage {
 
     // Writes the bits and returns this wave's class for the tile (all lanes
     // of the wave call it).
-    __device__ __forceinline__ int store(uint32_t *words, int r0, int k0, int n, bool full) const {
-        if (full) {
+    __device__ __forceinline__ int store(uint32_t *words, int r0, int k0, int n, int want) const {
+        if (want == kWantNone) return kSkip;  // the wave leaves this tile out
+        if (want == kWantFull) {
             if (act) words[wi * ROWS + r] = 0xffffffffu;
             return kDense;
         }
@@ -504,18 +533,19 @@ struct RangeStage {
         act = (lane >> 5) < kWordsPerWave;
     }
 
-    __device__ __forceinline__ void load(const MaskSource &src, int n, int r0, int k0, bool full) {
+    __device__ __forceinline__ void load(const MaskSource &src, int n, int r0, int k0, int want) {
         lo = 1;
         hi = 0;
         const int row = r0 + r;
-        if (full || !act || row >= n) return;
+        if (want != kWantMask || !act || row >= n) return;
         const int2 kr = *reinterpret_cast<const int2 *>(src.range + 2 * row);
         lo = max(kr.x, 0);
         hi = min(kr.y, n - 1);
     }
 
-    __device__ __forceinline__ int store(uint32_t *words, int r0, int k0, int n, bool full) const {
-        if (full) {
+    __device__ __forceinline__ int store(uint32_t *words, int r0, int k0, int n, int want) const {
+        if (want == kWantNone) return kSkip;  // the wave leaves this tile out
+        if (want == kWantFull) {
             if (act) words[wi * ROWS + r] = 0xffffffffu;
             return kDense;
         }

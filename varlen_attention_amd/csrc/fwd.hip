@@ -95,7 +95,9 @@ struct KVStage {
 template <int D, int VARIANT>
 constexpr int kFwdWavesPerSimd = VARIANT == kDiff && D == 128 ? 1 : 2;
 
-template <int D, int VARIANT, int NW, int KB, int MASK>
+// R: block-mask rows per workgroup (BQ / block_q); wave w follows row
+// w * R / NW, so smaller block rows keep four waves per workgroup.
+template <int D, int VARIANT, int NW, int KB, int MASK, int R>
 __global__ void __launch_bounds__(64 * NW, (kFwdWavesPerSimd<D, VARIANT>))
 fwd_kernel(const AttnParams p) {
     constexpr bool MASKED = MASK != kMaskNone;
@@ -151,10 +153,15 @@ fwd_kernel(const AttnParams p) {
         kb[1] = reinterpret_cast<const bf16 *>(p.k2) + b * p.sb + h * p.sh;
     }
     const bf16 *vb = reinterpret_cast<const bf16 *>(p.v) + b * p.sb + h * p.sh;
+    const int line0 = q0 / p.block_q;  // first block-mask row of this tile
     const uint8_t *bm_row =
-        p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + q0 / p.block_q) * p.Tk : nullptr;
+        p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + line0) * p.Tk : nullptr;
+    // Block rows that exist (with a block mask) or start below n (without).
+    const int lines = p.block_mask ? min(R, p.Tq - line0)
+                                   : min(R, (n - q0 + p.block_q - 1) / p.block_q);
 
     const int ql = lane & 31, hh = lane >> 5;
+    const int wl = w * R / NW;        // this wave's block-mask row (0 .. R - 1)
     const int qr = q0 + w * 32 + ql;  // this lane's query row
     const bool q_valid = qr < n;
     const MaskSource msrc = mask_source<MASK>(p.mask, p.key_range, b, L);
@@ -215,17 +222,18 @@ fwd_kernel(const AttnParams p) {
     MaskStager<MASK, BQ, BK, NT, true> mstage;
     int mcls = kMixed;  // this wave's share of the current tile (element mask)
     if constexpr (MASKED) mstage.init(tid);
-    TileSchedule<BK> sched;
-    sched.init(bm_row, 1, n, p.block_k);
+    TileSchedule<BK, R> sched;
+    sched.init(bm_row, 1, p.Tk, lines, n, p.block_k);
     int kt = sched.next();
-    const bool kt_full = sched.full;
+    const int kt_want = want_of(sched.on, sched.full, wl);
+    bool on = kt_want != kWantNone;  // this wave's row keeps the current tile
     if (kt > 0) load_tile(kt);
     if constexpr (MASKED)
-        if (kt >= 0) mstage.load(msrc, n, q0, kt * BK, kt_full);
+        if (kt >= 0) mstage.load(msrc, n, q0, kt * BK, kt_want);
     int buf = 0;
     stage.store(Ks[0], Vs[0]);
     if constexpr (MASKED)
-        if (kt >= 0) mcls = mstage.store(Ms[0], q0, kt * BK, n, kt_full);
+        if (kt >= 0) mcls = mstage.store(Ms[0], q0, kt * BK, n, kt_want);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         if constexpr (VARIANT == kSigmoid) qreg[0][ks] = scale8(qreg[0][ks], c1);
@@ -237,10 +245,10 @@ fwd_kernel(const AttnParams p) {
     while (kt >= 0) {
         const int k0 = kt * BK;
         const int nxt = sched.next();
-        const bool nxt_full = sched.full;
+        const int nxt_want = want_of(sched.on, sched.full, wl);
         if (nxt >= 0) load_tile(nxt);
         if constexpr (MASKED)
-            if (nxt >= 0) mstage.load(msrc, n, q0, nxt * BK, nxt_full);
+            if (nxt >= 0) mstage.load(msrc, n, q0, nxt * BK, nxt_want);
         const bf16 *Kc = Ks[buf];
         const bf16 *Vc = Vs[buf];
 
@@ -364,13 +372,14 @@ fwd_kernel(const AttnParams p) {
             // body for tiles whose entries are all kept measured slower: it
             // costs registers and the masked body's extra work is small.)
             if (mcls != kSkip) tile(std::integral_constant<int, 2>{});
-        } else {
+        } else if (R == 1 || on) {
             tile(std::integral_constant<int, VARIANT == kSigmoid ? 0 : 1>{});
         }
 
         if (nxt >= 0) stage.store(Ks[buf ^ 1], Vs[buf ^ 1]);
         if constexpr (MASKED)
-            if (nxt >= 0) mcls = mstage.store(Ms[buf ^ 1], q0, nxt * BK, n, nxt_full);
+            if (nxt >= 0) mcls = mstage.store(Ms[buf ^ 1], q0, nxt * BK, n, nxt_want);
+        on = nxt_want != kWantNone;
         __syncthreads();
         buf ^= 1;
         kt = nxt;
@@ -437,31 +446,31 @@ static hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
     // Two maps at d = 128 visit 32 keys at a time: two K tiles and V of 64
     // keys, double-buffered, would leave LDS for one workgroup per CU.
     constexpr bool kNarrow = VARIANT == kDiff && D == 128;
-    const int nw = p.block_q >= 128 ? 4 : p.block_q / 32;
+    constexpr int NW = 4, BQ = 32 * NW;
+    const int rows = BQ / p.block_q;  // block-mask rows per workgroup: 1, 2 or 4
     const int kb = p.block_k >= 64 && !kNarrow ? 2 : 1;
-    const int bq = 32 * nw;
-    const dim3 grid = tile_grid((p.L + bq - 1) / bq, p.B, p.H);
-    dim3 block(64 * nw);
-#define SIGATTN_FWD_CASE(NW_, KB_)                                                             \
-    if constexpr (!kNarrow || KB_ == 1)                                                        \
-    if (nw == NW_ && kb == KB_) {                                                              \
-        if (p.mask != nullptr)                                                                 \
-            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, kMaskDense>), grid, block, 0, \
-                               stream, p);                                                     \
-        else if (p.key_range != nullptr)                                                       \
-            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, kMaskRange>), grid, block, 0, \
-                               stream, p);                                                     \
-        else                                                                                   \
-            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW_, KB_, kMaskNone>), grid, block, 0,  \
-                               stream, p);                                                     \
-        return hipGetLastError();                                                              \
+    const dim3 grid = tile_grid((p.L + BQ - 1) / BQ, p.B, p.H);
+    dim3 block(64 * NW);
+#define SIGATTN_FWD_CASE(R_, KB_)                                                                  \
+    if constexpr (!kNarrow || KB_ == 1)                                                            \
+    if (rows == R_ && kb == KB_) {                                                                 \
+        if (p.mask != nullptr)                                                                     \
+            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW, KB_, kMaskDense, R_>), grid, block, 0,  \
+                               stream, p);                                                         \
+        else if (p.key_range != nullptr)                                                           \
+            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW, KB_, kMaskRange, R_>), grid, block, 0,  \
+                               stream, p);                                                         \
+        else                                                                                       \
+            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW, KB_, kMaskNone, R_>), grid, block, 0,   \
+                               stream, p);                                                         \
+        return hipGetLastError();                                                                  \
     }
-    SIGATTN_FWD_CASE(4, 2)
-    SIGATTN_FWD_CASE(4, 1)
-    SIGATTN_FWD_CASE(2, 2)
-    SIGATTN_FWD_CASE(2, 1)
     SIGATTN_FWD_CASE(1, 2)
     SIGATTN_FWD_CASE(1, 1)
+    SIGATTN_FWD_CASE(2, 2)
+    SIGATTN_FWD_CASE(2, 1)
+    SIGATTN_FWD_CASE(4, 2)
+    SIGATTN_FWD_CASE(4, 1)
 #undef SIGATTN_FWD_CASE
     return hipErrorInvalidValue;
 }
