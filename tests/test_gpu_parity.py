@@ -277,6 +277,48 @@ def test_causal_mask_full_tiles(va, d, L, bq, bk, variant):
         assert_rows(gpu_f64(got_t), ref, n, name)
 
 
+@pytest.mark.parametrize("d,L,bq,bk,variant,with_mask", [
+    (64, 300, 32, 32, SIGMOID, False), (64, 280, 64, 128, SOFTMAX, False),
+    (128, 260, 32, 64, SIGMOID, True), (64, 230, 128, 32, SOFTMAX1, True),
+    (128, 300, 64, 64, SOFTMAX, False)])
+def test_caller_block_mask_per_line(va, d, L, bq, bk, variant, with_mask):
+    """A caller's own 0/1 block mask drops tiles whose elements are valid.  A
+    workgroup of 128 rows (keys in dK/dV) spans several block-mask lines when
+    a block is 32 or 64 wide, and each line must drop exactly its own tiles:
+    the oracle takes the block mask as an element mask (each element keeps
+    its entry's value), ANDed with the element mask when there is one."""
+    B, H = 3, 2
+    n = np.array([L, L - 37, bq + 5], np.int32)
+    q, k, v, do = _inputs(6000 + d + L + variant, B, H, L, d, n, names="qkvd")
+    rng = np.random.default_rng(d + L + bq + bk)
+    Tq, Tk = -(-L // bq), -(-L // bk)
+    blk = (rng.random((B, Tq, Tk)) < 0.55).astype(np.uint8)
+    blk[0, 0, :] = 1
+    blk[1, :, 0] = 0
+    elem = np.ascontiguousarray(blk.repeat(bq, axis=1).repeat(bk, axis=2)[:, :L, :L])
+    mask = None
+    if with_mask:
+        mask = (rng.random((B, L, L)) < 0.7).astype(np.uint8)
+        elem = elem & mask
+    say(f"caller block mask d={d} L={L} bq={bq} bk={bk} variant={variant} mask={with_mask}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = None if mask is None else to_gpu(mask, torch.uint8)
+    bias = 1 if variant == SIGMOID else 0
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    bm = to_gpu(blk, torch.uint8)
+    o, lse = va.sigattn_fwd(*g[:3], n_gpu, block_mask=bm, mask=m_gpu, bias=bias, variant=variant,
+                            block_q=bq, block_k=bk, return_lse=True)
+    grads = va.sigattn_bwd(*g, n_gpu, block_mask=bm, mask=m_gpu, bias=bias, variant=variant,
+                           block_q=bq, block_k=bk, o=o if variant else None,
+                           lse=lse if variant else None)
+    torch.cuda.synchronize()
+    want, _ = oracle.fwd(q, k, v, n, mask=elem, bias=bias, variant=variant)
+    assert_rows(gpu_f64(o), want, n, "O")
+    wq, wk, wv = oracle.bwd(q, k, v, do, n, mask=elem, bias=bias, variant=variant)
+    for name, got_t, ref in zip(("dQ", "dK", "dV"), grads, (wq, wk, wv)):
+        assert_rows(gpu_f64(got_t), ref, n, name)
+
+
 def _window_ranges(rng, B, L):
     """Sliding windows of random width per row, some reaching past the row,
     some empty (lo > hi), some clipped at 0 or L - 1."""
