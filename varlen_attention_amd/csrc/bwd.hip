@@ -342,11 +342,11 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     const int wl = w * C / NW;        // this wave's column (0 .. C - 1)
     const int lines = p.block_mask ? min(C, p.Tk - line0)
                                    : min(C, (n - k0 + p.block_k - 1) / p.block_k);
-    TileSchedule<BQ, C> sched;
-    sched.init(p.block_mask ? p.block_mask + (int64_t)b * p.Tq * p.Tk + line0 : nullptr, p.Tk, 1,
-               lines, n, p.block_q);
+    TileSchedule<BQ, C, false> sched;
+    sched.init(p.block_mask ? p.block_mask + (int64_t)b * p.Tq * p.Tk + line0 : nullptr, p.Tk,
+               lines, wl, n, p.block_q);
     int qt = sched.next();
-    const int qt_want = want_of(sched.on, sched.full, wl);
+    const int qt_want = sched.want();
     bool on = qt_want != kWantNone;  // this wave's column keeps the current tile
     if (qt > 0) load_tile(qt, qt_want);
     int buf = 0;
@@ -361,7 +361,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
 
     while (qt >= 0) {
         const int nxt = sched.next();
-        const int nxt_want = want_of(sched.on, sched.full, wl);
+        const int nxt_want = sched.want();
         if (nxt >= 0) load_tile(nxt, nxt_want);
         const bf16 *Qc = Qs(buf);
         const bf16 *dOc = dOs(buf);
@@ -545,11 +545,11 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     const int wl = w * R / NW;        // this wave's row (0 .. R - 1)
     const int lines = p.block_mask ? min(R, p.Tq - line0)
                                    : min(R, (n - q0 + p.block_q - 1) / p.block_q);
-    TileSchedule<BK, R> sched;
-    sched.init(p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + line0) * p.Tk : nullptr, 1,
-               p.Tk, lines, n, p.block_k);
+    TileSchedule<BK, R, true> sched;
+    sched.init(p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + line0) * p.Tk : nullptr, p.Tk,
+               lines, wl, n, p.block_k);
     int kt = sched.next();
-    const int kt_want = want_of(sched.on, sched.full, wl);
+    const int kt_want = sched.want();
     bool on = kt_want != kWantNone;  // this wave's row keeps the current tile
     if (kt > 0) fetch(kt, K0, V0);
     if constexpr (MASKED)
@@ -568,7 +568,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     auto step = [&](const bf16 *Kc, const bf16 *Vc, const uint32_t *Mc, bf16 *Kn, bf16 *Vn,
                     uint32_t *Mn) {
         const int nxt = sched.next();
-        const int nxt_want = want_of(sched.on, sched.full, wl);
+        const int nxt_want = sched.want();
         if (nxt >= 0) fetch(nxt, Kn, Vn);
         if constexpr (MASKED)
             if (nxt >= 0) mstage.load(msrc, n, q0, nxt * BK, nxt_want);
@@ -643,8 +643,14 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
 }
 
 // ---------------------------------------------------------------- kernels
+// Waves per SIMD the register allocation must allow.  The unmasked sigmoid
+// kernels at d = 64 need about 168 VGPRs: held to that, three waves share a
+// SIMD (LDS allows three workgroups per CU even in the one-launch kernel).
+template <int D, int VARIANT, int MASK>
+constexpr int kBwdWavesPerSimd = D == 64 && VARIANT == kSigmoid && MASK == kMaskNone ? 3 : 2;
+
 template <int D, int NW, int VARIANT, int MASK, int C>
-__global__ void __launch_bounds__(64 * NW, 2)
+__global__ void __launch_bounds__(64 * NW, (kBwdWavesPerSimd<D, VARIANT, MASK>))
 bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
     __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
@@ -657,7 +663,7 @@ bwd_dkdv_kernel(const AttnParams p) {
 }
 
 template <int D, int NW, int KB, int VARIANT, int MASK, int R>
-__global__ void __launch_bounds__(64 * NW, 2)
+__global__ void __launch_bounds__(64 * NW, (kBwdWavesPerSimd<D, VARIANT, MASK>))
 bwd_dq_kernel(const AttnParams p) {
     constexpr int kTile = 32 * KB * D;
     __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
@@ -674,7 +680,7 @@ bwd_dq_kernel(const AttnParams p) {
 // dK/dV and the query tiles of dQ.
 // R: block-mask rows and columns per workgroup (block_q == block_k).
 template <int D, int NW, int KB, int VARIANT, int MASK, int R>
-__global__ void __launch_bounds__(64 * NW, 2)
+__global__ void __launch_bounds__(64 * NW, (kBwdWavesPerSimd<D, VARIANT, MASK>))
 bwd_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
     constexpr int kTile = 32 * KB * D;

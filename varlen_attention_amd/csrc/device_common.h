@@ -95,44 +95,55 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, void *lds, int byte_offset)
 // s_waitcnt vmcnt(0), leaving the other counters alone.
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// What a wave stages for a tile: nothing (its block-mask line leaves the
+// tile out), all-ones words (its entry is full) or the mask itself.
+enum { kWantNone = 0, kWantFull = 1, kWantMask = 2 };
+
 // Iterates, in increasing order, the tiles of BT rows that one row (or one
 // column) of the block mask marks active, clipped to the n valid rows.  One
 // wave ballot reads 64 block-mask entries at a time; the result is uniform,
 // so the schedule lives in scalar registers.  A null block mask marks all
-// entries active (padding only).  Entry e is read at bm[e * stride].
+// entries active (padding only).  ROW: the schedule walks along block-mask
+// rows (entry e of line r at bm[r * tk + e]), else down columns (at
+// bm[e * tk + r]); tk is the length of a block-mask row.
 // The kernel tiles along R adjacent lines of the block matrix (block rows for
 // the query side, block columns for dK/dV) that one workgroup's waves share:
-// a tile is visited when any line keeps it, and bit r of `on` / `full` says
-// whether line r keeps it / whether that entry is full.  A wave works only on
-// the tiles its own line keeps, so every element still obeys its own entry.
-// Lines at or past `lines` are off.
-template <int BT, int R = 1>
+// a tile is visited when any line keeps it, and want() says what the calling
+// wave's own line (`line`) needs of it: kWantNone when that line drops it, so
+// every element still obeys its own entry.  Lines at or past `lines` are off.
+// Only the union and the wave's own line are kept, in six scalar registers.
+template <int BT, int R, bool ROW>
 struct TileSchedule {
     const uint8_t *bm;        // line 0's first entry, or null (from seq_lens)
-    int64_t stride, lstride;  // between consecutive entries; between lines
-    int nlines;               // lines that exist
+    int tk;                   // entries per block-mask row
+    int nlines, line;         // lines that exist; the wave's own line
     int nblk;                 // block-mask entries covering [0, n)
     int per_blk;              // kernel tiles per block-mask entry
     int nkt;                  // kernel tiles covering [0, n)
     int wbase, entry, sub;
     uint64_t act;             // entries (of the 64 at wbase) some line keeps
-    uint64_t onm[R], fullm[R];
-    uint32_t on, full;        // per line, for the tile next() returned
+    uint64_t mine, mine_full; // entries the wave's line keeps / marks full
+    bool on, full;            // the same two, for the tile next() returned
 
-    __device__ __forceinline__ void init(const uint8_t *first, int64_t step, int64_t line_step,
-                                         int lines, int n, int block) {
+    __device__ __forceinline__ void init(const uint8_t *first, int row_len, int lines, int own_line,
+                                         int n, int block) {
         bm = first;
-        stride = step;
-        lstride = line_step;
+        tk = row_len;
         nlines = lines;
+        line = own_line;
         nblk = (n + block - 1) / block;
         per_blk = block / BT;
         nkt = (n + BT - 1) / BT;
         wbase = -64;
         entry = -1;
         sub = 0;
-        act = 0;
-        on = full = 0;
+        act = mine = mine_full = 0;
+        on = full = false;
+    }
+
+    // Offset of entry e of line r from line 0's first entry.
+    __device__ __forceinline__ int64_t at(int r, int e) const {
+        return ROW ? (int64_t)r * tk + e : (int64_t)e * tk + r;
     }
 
     // Next kernel tile some line keeps, or -1.
@@ -145,26 +156,44 @@ struct TileSchedule {
             wbase += 64;
             if (wbase >= nblk) return -1;
             const int e = wbase + (int)(threadIdx.x & 63);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int v = e < nblk && r < nlines
-                                  ? (bm == nullptr ? 1 : (int)bm[r * lstride + e * stride]) : 0;
-                onm[r] = __ballot(v != 0);
-                fullm[r] = __ballot((v & 2) != 0);
-                act |= onm[r];
+            if constexpr (R == 1) {
+                // One line: every visited tile is the wave's own.
+                const int v = e < nblk ? (bm == nullptr ? 1 : (int)bm[at(0, e)]) : 0;
+                act = __ballot(v != 0);
+                mine_full = __ballot((v & 2) != 0);
+            } else {
+                // A rolled loop: unrolled, the lines' addresses stay live
+                // across the kernel's main loop.
+                mine = mine_full = 0;
+                const uint8_t *pe = bm == nullptr ? nullptr : bm + at(0, e);
+#pragma unroll 1
+                for (int r = 0; r < nlines; ++r) {
+                    const int v = e < nblk ? (pe == nullptr ? 1 : (int)*pe) : 0;
+                    const uint64_t kept = __ballot(v != 0);
+                    act |= kept;
+                    if (r == line) {
+                        mine = kept;
+                        mine_full = __ballot((v & 2) != 0);
+                    }
+                    if (pe != nullptr) pe += ROW ? tk : 1;
+                }
             }
         }
         const int bit = __builtin_ctzll(act);
         entry = wbase + bit;
-        on = full = 0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            on |= (uint32_t)((onm[r] >> bit) & 1u) << r;
-            full |= (uint32_t)((fullm[r] >> bit) & 1u) << r;
-        }
+        on = R == 1 || ((mine >> bit) & 1u);
+        full = (mine_full >> bit) & 1u;
         act &= act - 1;
         sub = 0;
         return entry * per_blk;
+    }
+
+    // What the wave's line needs of the current tile's element mask.
+    __device__ __forceinline__ int want() const {
+        if constexpr (R == 1)
+            return full ? kWantFull : kWantMask;
+        else
+            return !on ? kWantNone : full ? kWantFull : kWantMask;
     }
 };
 
@@ -418,13 +447,6 @@ struct MaskSource {
 template <int MASK>
 __device__ __forceinline__ constexpr int key_bit(int t) {
     return MASK == kMaskDense ? mask_bit(t) : t;
-}
-
-// What a wave stages for a tile: nothing (its block-mask line leaves the
-// tile out), all-ones words (its entry is full) or the mask itself.
-enum { kWantNone = 0, kWantFull = 1, kWantMask = 2 };
-__device__ __forceinline__ int want_of(uint32_t on, uint32_t full, int line) {
-    return !((on >> line) & 1u) ? kWantNone : ((full >> line) & 1u) ? kWantFull : kWantMask;
 }
 
 // What a wave's share of a masked tile needs, from the OR and the AND of the

@@ -222,10 +222,10 @@ fwd_kernel(const AttnParams p) {
     MaskStager<MASK, BQ, BK, NT, true> mstage;
     int mcls = kMixed;  // this wave's share of the current tile (element mask)
     if constexpr (MASKED) mstage.init(tid);
-    TileSchedule<BK, R> sched;
-    sched.init(bm_row, 1, p.Tk, lines, n, p.block_k);
+    TileSchedule<BK, R, true> sched;
+    sched.init(bm_row, p.Tk, lines, wl, n, p.block_k);
     int kt = sched.next();
-    const int kt_want = want_of(sched.on, sched.full, wl);
+    const int kt_want = sched.want();
     bool on = kt_want != kWantNone;  // this wave's row keeps the current tile
     if (kt > 0) load_tile(kt);
     if constexpr (MASKED)
@@ -245,7 +245,7 @@ fwd_kernel(const AttnParams p) {
     while (kt >= 0) {
         const int k0 = kt * BK;
         const int nxt = sched.next();
-        const int nxt_want = want_of(sched.on, sched.full, wl);
+        const int nxt_want = sched.want();
         if (nxt >= 0) load_tile(nxt);
         if constexpr (MASKED)
             if (nxt >= 0) mstage.load(msrc, n, q0, nxt * BK, nxt_want);
