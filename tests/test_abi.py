@@ -73,7 +73,7 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, va, _shape(va, stride_l=32)) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va), lse=ctypes.c_void_p(0x10002)) == va.ERR_ALIGNMENT
     # An element mask bounds L (32-bit offsets into each L x L mask).
-    assert _fwd(lib, va, _shape(va, L=46081), mask=FAKE, bm=FAKE) == va.ERR_UNSUPPORTED
+    assert _fwd(lib, va, _shape(va, L=va.MAX_MASKED_L + 1), mask=FAKE, bm=FAKE) == va.ERR_UNSUPPORTED
     # Key ranges: not with a dense mask, only with a block mask, 8-byte aligned.
     assert _fwd(lib, va, _shape(va), mask=FAKE, kr=FAKE, bm=FAKE) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va), kr=FAKE) == va.ERR_INVALID_ARG
@@ -163,3 +163,12 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         va.sigattn_fwd(q, q, q, torch.zeros(1, dtype=torch.int32))
+
+
+def test_max_masked_length_matches_header():
+    """The binding's MAX_MASKED_L is the header's SIGATTN_MAX_MASKED_L."""
+    import varlen_attention_amd as va
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "sigattn.h")).read()
+    m = re.search(r"#define\s+SIGATTN_MAX_MASKED_L\s+(\d+)", hdr)
+    assert m and int(m.group(1)) == va.MAX_MASKED_L
+

@@ -693,6 +693,98 @@ def _check_sampled_bwd(va, w):
         assert_close(np.concatenate(got[key]), np.concatenate(want[key]), f"{key} sampled")
 
 
+def _sampled_fwd_bwd(va, q, k, v, do, n, L, b_rows, gpu_kw, oracle_kw, what):
+    """Forward and backward through the C ABI, padded rows exactly zero, and
+    the oracle on sampled rows: b_rows holds (batch entry, head, query rows,
+    starts of 8-key windows for dK and dV)."""
+    n_gpu = to_gpu(n, torch.int32)
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    o = va.sigattn_fwd(*g[:3], n_gpu, **gpu_kw)
+    dq, dk, dv = va.sigattn_bwd(*g, n_gpu, **gpu_kw)
+    torch.cuda.synchronize()
+    B, H = q.shape[:2]
+    valid = np.broadcast_to(row_valid(n, B, L)[:, None, :], (B, H, L))
+    outs = {}
+    for name, t in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        outs[name] = t
+        assert bool((t.view(torch.int16)[torch.from_numpy(~valid).to(t.device)] == 0).all()), \
+            f"{what}: padded {name} rows not zero"
+    got = {key: [] for key in outs}
+    want = {key: [] for key in outs}
+    for b, h, rows, starts in b_rows:
+        ro, _ = oracle.fwd_rows(q, k, v, n, b, h, rows, **oracle_kw)
+        rq, _, _ = oracle.bwd_rows(q, k, v, do, n, b, h, rows, [], **oracle_kw)
+        for key, ref in (("O", ro), ("dQ", rq)):
+            got[key].append(gpu_f64(outs[key][b, h, rows]))
+            want[key].append(ref)
+        for c0 in starts:
+            cols = list(range(c0, min(c0 + 8, L)))
+            _, rk, rv = oracle.bwd_rows(q, k, v, do, n, b, h, [], cols, **oracle_kw)
+            for key, ref in (("dK", rk), ("dV", rv)):
+                got[key].append(gpu_f64(outs[key][b, h, cols]))
+                want[key].append(ref)
+    for key in got:
+        assert_close(np.concatenate(got[key]), np.concatenate(want[key]), f"{what} {key}")
+
+
+def _band_rows(rng, nb, L, extra=()):
+    rows = {0, 1, nb - 1, min(nb, L - 1)} | set(extra)
+    rows |= set(rng.integers(0, max(nb, 1), size=6).tolist())
+    return sorted(r for r in rows if 0 <= r < L)
+
+
+def test_max_masked_length(va):
+    """The longest padded length accepted with an element mask, with two
+    batch entries: the second entry's mask runs past 2^31 bytes from the
+    first's.  A causal band of 400 keys (with full tiles) keeps the work
+    small; the block mask is compared bit for bit, outputs and gradients on
+    sampled rows, including rows past the 2^31-byte mark and fully masked
+    rows."""
+    L, B, H, d, win = va.MAX_MASKED_L, 2, 1, 64, 400
+    n = np.array([L, L - 1001], np.int32)
+    rng = np.random.default_rng(46)
+    q, k, v, do = (syn.random_tensor(rng, (B, H, L, d)) for _ in range(4))
+    mask = np.zeros((B, L, L), np.uint8)
+    for r in range(L):
+        mask[:, r, max(0, r - win + 1):r + 1] = 1
+    mask[1, 30000:30100, :] = 0
+    say(f"max masked length L={L}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = to_gpu(mask, torch.uint8)
+    bm = _bm(va, n_gpu, L, 128, 128, m_gpu)
+    want_bm = oracle.blockmask(n, mask, L, 128, 128)
+    assert (want_bm == 3).any()
+    np.testing.assert_array_equal(bm.cpu().numpy(), want_bm)
+    b_rows = [(0, 0, _band_rows(rng, L, L), (0, 20000, L - 8)),
+              (1, 0, _band_rows(rng, int(n[1]), L, extra=(30000, 30099, 40000, L - 1002)),
+               (29996, 40000, int(n[1]) - 5))]
+    _sampled_fwd_bwd(va, q, k, v, do, n, L, b_rows, dict(block_mask=bm, mask=m_gpu),
+                     dict(mask=mask), "max masked length")
+
+
+def test_key_ranges_past_max_masked_length(va):
+    """Key ranges carry no L x L mask, so they go past the dense mask's
+    length limit: L = 65536 with sliding windows (some empty, some reaching
+    past the row), block mask bit for bit, sampled rows against the oracle
+    with the ranges written out as an element mask."""
+    L, B, H, d = 65536, 1, 2, 64
+    n = np.array([60001], np.int32)
+    rng = np.random.default_rng(65)
+    q, k, v, do = (syn.random_tensor(rng, (B, H, L, d)) for _ in range(4))
+    kr = _window_ranges(rng, B, L)
+    kr[0, 50000:50010] = (10, 5)  # empty rows
+    say(f"key ranges past max masked length L={L}")
+    n_gpu = to_gpu(n, torch.int32)
+    kr_gpu = to_gpu(kr, torch.int32)
+    bm = _bm(va, n_gpu, L, 128, 128, key_range=kr_gpu)
+    elem = oracle.key_range_mask(kr, L)  # what the ranges stand for, written out once
+    np.testing.assert_array_equal(bm.cpu().numpy(), oracle.blockmask(n, elem, L, 128, 128))
+    b_rows = [(0, h, _band_rows(rng, int(n[0]), L, extra=(50000, 50009, 59999)),
+               (0, 49996, int(n[0]) - 4)) for h in range(H)]
+    _sampled_fwd_bwd(va, q, k, v, do, n, L, b_rows, dict(block_mask=bm, key_range=kr_gpu),
+                     dict(mask=elem), "key ranges L=65536")
+
+
 def test_backward_single_cell_full_size(va, single_cell_inputs):
     w = single_cell_inputs
     say(f"bwd full {w.name} L={w.L}")

@@ -20,6 +20,8 @@ import torch
 SIGMOID, SOFTMAX, SOFTMAX1 = 0, 1, 2
 BIAS_NONE, BIAS_LOG_SEQLEN, BIAS_LOG_PADLEN = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_LAUNCH = 0, -1, -2, -3, -4
+# Longest padded length accepted together with an element mask (SIGATTN_MAX_MASKED_L).
+MAX_MASKED_L = 46080
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsigattn.so")
 EXPORTS = ("blockmask_build", "sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq",
