@@ -382,10 +382,6 @@ __device__ __forceinline__ float keep_or_zero(float x, bool keep) {
     return __uint_as_float(__float_as_uint(x) & (keep ? 0xffffffffu : 0u));
 }
 
-__device__ __forceinline__ float keep_or_neg_inf(float x, bool keep) {
-    return keep ? x : -INFINITY;
-}
-
 // x where `keep` is all ones, -inf where it is zero (one bitfield insert).
 __device__ __forceinline__ float keep_bits_or_neg_inf(float x, uint32_t keep) {
     return __uint_as_float((__float_as_uint(x) & keep) | (0xff800000u & ~keep));

@@ -90,6 +90,10 @@ struct KVStage {
 
 }  // namespace
 
+// Online softmax: how far (log2 units) a row maximum may pass the reference
+// maximum before the running state is rescaled.
+constexpr float kLazyRescale = 8.0f;
+
 // Two maps at d = 128 hold two Q operands and two output accumulators (192
 // registers before the loop's own): such waves get the whole register file.
 template <int D, int VARIANT>
@@ -277,19 +281,22 @@ fwd_kernel(const AttnParams p) {
                         sacc[mp][kb2] = mfma32(a, qreg[mp][ks], sacc[mp][kb2]);
                     }
                 }
-            // Per-element validity.  MODE 1: compared, without branches.
-            // MODE 2: the tile's mask bits (validity folded in); key
-            // 8 i + 4 hh + j of a 32-key block is bit key_bit(8 i + 4 hh + j):
-            // 8 j + 2 i + hh (dense) or 8 i + 4 hh + j (ranges).
-            bool ok[KB][16];
+            // Per-element validity.  MODE 1: key 8 i + 4 hh + j of a 32-key
+            // block is valid when 8 i + j < lim: bit 8 i + j of a word with
+            // the lim lowest bits set, taken out like a mask bit (bit ops
+            // instead of compares, whose condition registers cost wait
+            // states).  Padded query rows need no check: their output is
+            // zeroed at the store and their LSE set apart.  MODE 2: the
+            // tile's mask bits (validity folded in); key 8 i + 4 hh + j is
+            // bit key_bit(8 i + 4 hh + j): 8 j + 2 i + hh (dense) or
+            // 8 i + 4 hh + j (ranges).
+            uint32_t vw[KB];
             if constexpr (MODE == 1) {
 #pragma unroll
-                for (int kb2 = 0; kb2 < KB; ++kb2)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kb2 * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                        ok[kb2][r] = q_valid && key < n;
-                    }
+                for (int kb2 = 0; kb2 < KB; ++kb2) {
+                    const int lim = n - (k0 + kb2 * 32 + hh * 4);
+                    vw[kb2] = lim >= 32 ? ~0u : lim <= 0 ? 0u : (1u << lim) - 1u;
+                }
             }
             uint32_t mw[KB];  // this lane's row of the tile's mask words
             constexpr bool kDenseBits = MASK == kMaskDense;
@@ -303,31 +310,46 @@ fwd_kernel(const AttnParams p) {
                                                        : 8 * (r >> 2) + (r & 3));
             };
 
-            float m_use[MAPS];
+            // moff: per map, c0 - m, so that a weight is exp2(s c1 + moff).
+            float moff[MAPS];
             if constexpr (kSoft) {
-                // Online softmax, per map: tile maximum over this lane's keys
-                // and its partner lane's (lane ^ 32), then rescale the state.
+                // Online softmax, per map: tile maximum of the raw scores over
+                // this lane's keys and its partner lane's (lane ^ 32).  c1 > 0,
+                // and s c1 + c0 rounds monotonically in s, so the maximum of
+                // the logits t = s c1 + c0 is the logit of the maximum score.
+                // Then rescale the state.
 #pragma unroll
                 for (int mp = 0; mp < MAPS; ++mp) {
-                    float tmax = -INFINITY;
+                    float smax = -INFINITY;
 #pragma unroll
                     for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            float t = fmaf(sacc[mp][kb2][r], c1, c0);
-                            if constexpr (MODE == 1) t = keep_or_neg_inf(t, ok[kb2][r]);
-                            if constexpr (MODE == 2) t = keep_bits_or_neg_inf(t, keep(kb2, r));
-                            sacc[mp][kb2][r] = t;
-                            tmax = fmaxf(tmax, t);
+                            float sv = sacc[mp][kb2][r];
+                            if constexpr (MODE == 1)
+                                sv = keep_bits_or_neg_inf(sv, mask_select(vw[kb2], (r >> 2) * 8 + (r & 3)));
+                            if constexpr (MODE == 2) sv = keep_bits_or_neg_inf(sv, keep(kb2, r));
+                            sacc[mp][kb2][r] = sv;
+                            smax = fmaxf(smax, sv);
                         }
-                    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-                    const float m_new = fmaxf(m_run[mp], tmax);
-                    m_use[mp] = m_new == -INFINITY ? 0.0f : m_new;
-                    const float alpha = __builtin_amdgcn_exp2f(m_run[mp] - m_use[mp]);
-                    m_run[mp] = m_new;
-                    l_run[mp] *= alpha;
+                    smax = fmaxf(smax, __shfl_xor(smax, 32));
+                    const float tmax = fmaf(smax, c1, c0);
+                    // The reference m_run moves only when some row's maximum
+                    // passes it by more than kLazyRescale (weights stay below
+                    // 2^kLazyRescale, harmless in fp32 and bf16): most tiles
+                    // then skip rescaling the state.  The sums stay exact
+                    // relative to m_run, and so does the log-sum-exp.  Two
+                    // maps rescale every tile: their branches cost registers.
+                    if (MAPS == 2 || __ballot(tmax > m_run[mp] + kLazyRescale) != 0) {
+                        const float m_new = fmaxf(m_run[mp], tmax);
+                        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+                        const float alpha = __builtin_amdgcn_exp2f(m_run[mp] - m_use);
+                        m_run[mp] = m_new;
+                        l_run[mp] *= alpha;
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) oacc[mp][db] *= alpha;
+                        for (int db = 0; db < DB; ++db) oacc[mp][db] *= alpha;
+                    }
+                    moff[mp] = c0 - (m_run[mp] == -INFINITY ? 0.0f : m_run[mp]);
                 }
             }
 
@@ -345,7 +367,7 @@ fwd_kernel(const AttnParams p) {
                             if constexpr (MODE == 2)
                                 pv[mp][r] = __uint_as_float(__float_as_uint(pv[mp][r]) & keep(kb2, r));
                         } else {
-                            pv[mp][r] = __builtin_amdgcn_exp2f(sacc[mp][kb2][r] - m_use[mp]);
+                            pv[mp][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mp][kb2][r], c1, moff[mp]));
                             l_run[mp] += pv[mp][r];
                         }
                     }
