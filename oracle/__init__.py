@@ -105,11 +105,13 @@ def key_range_mask(key_range, L: int) -> np.ndarray:
 
 
 def _element_mask(mask, key_range, L):
-    """One dense element mask from the two forms (both: both conditions)."""
+    """The dense element mask of a call: ``mask`` itself, or the one the key
+    ranges stand for.  A call takes one form or the other (as the C ABI)."""
     if key_range is None:
         return mask
-    km = key_range_mask(key_range, L)
-    return km if mask is None else (km & (np.asarray(mask) != 0)).astype(np.uint8)
+    if mask is not None:
+        raise ValueError("mask and key_range are alternative forms of one element mask")
+    return key_range_mask(key_range, L)
 
 
 def blockmask(seq_lens, mask, L: int, block_q: int, block_k: int, key_range=None) -> np.ndarray:

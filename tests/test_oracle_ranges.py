@@ -55,3 +55,12 @@ def test_block_mask_from_ranges_equals_dense(oracle_lib, L, bq, bk):
     tiles = pad.reshape(B, Tq, bq, Tk, bk)
     want = tiles.any(axis=(2, 4)).astype(np.uint8) | (tiles.all(axis=(2, 4)).astype(np.uint8) << 1)
     np.testing.assert_array_equal(got, want)
+
+
+def test_one_element_mask_form_per_call():
+    """Like the C ABI, the oracle takes a dense mask or key ranges, not both."""
+    import oracle
+    n = np.array([5], np.int32)
+    with pytest.raises(ValueError):
+        oracle.blockmask(n, np.ones((1, 8, 8), np.uint8), 8, 4, 4,
+                         key_range=np.zeros((1, 8, 2), np.int32))
