@@ -151,9 +151,7 @@ struct RowStats {
                                           float *off_lds, int tid) const {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            float part = dot8(dout_chunks[c], o[c]);
-#pragma unroll
-            for (int m = 1; m < kChunksPerRow; m <<= 1) part += __shfl_xor(part, m);
+            const float part = group_sum<kChunksPerRow>(dot8(dout_chunks[c], o[c]));
             const int idx = tid + c * NT;
             if (idx % kChunksPerRow == 0) d_lds[idx / kChunksPerRow] = part;
         }

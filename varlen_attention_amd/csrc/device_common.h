@@ -212,6 +212,25 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
+// Sum over each aligned group of G lanes (G = 8 or 16), every lane of a group
+// receiving its group's sum, with DPP moves (no LDS round trips): swap
+// neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), then mirror
+// within 8 lanes (the other quad's sum) and, for 16, within the row.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(G == 8 || G == 16, "groups of 8 or 16 lanes");
+    auto mv = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             0, __builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                             0xf, 0xf, false));
+    };
+    x += mv(x, std::integral_constant<int, 0xb1>{});   // quad_perm 1,0,3,2
+    x += mv(x, std::integral_constant<int, 0x4e>{});   // quad_perm 2,3,0,1
+    x += mv(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    if constexpr (G == 16) x += mv(x, std::integral_constant<int, 0x140>{});  // row_mirror
+    return x;
+}
+
 // Work item of a workgroup in a launch over (batch entry, head, tile) items of
 // up to two kinds: NT0 tiles of ROWS0 rows and NT1 tiles of ROWS1 rows per
 // (batch entry, head) (NT1 = 0 for a launch of one kind).
