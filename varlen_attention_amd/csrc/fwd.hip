@@ -318,6 +318,20 @@ fwd_kernel(const AttnParams p) {
                 // and s c1 + c0 rounds monotonically in s, so the maximum of
                 // the logits t = s c1 + c0 is the logit of the maximum score.
                 // Then rescale the state.
+                // MODE 1 masks only the tile that holds key n - 1 (a uniform
+                // branch; the tiles before it have no padded key).
+                if constexpr (MODE == 1) {
+                    if (k0 + BK > n) {
+#pragma unroll
+                        for (int mp = 0; mp < MAPS; ++mp)
+#pragma unroll
+                            for (int kb2 = 0; kb2 < KB; ++kb2)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r)
+                                    sacc[mp][kb2][r] = keep_bits_or_neg_inf(
+                                        sacc[mp][kb2][r], mask_select(vw[kb2], (r >> 2) * 8 + (r & 3)));
+                    }
+                }
 #pragma unroll
                 for (int mp = 0; mp < MAPS; ++mp) {
                     float smax = -INFINITY;
@@ -326,8 +340,6 @@ fwd_kernel(const AttnParams p) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             float sv = sacc[mp][kb2][r];
-                            if constexpr (MODE == 1)
-                                sv = keep_bits_or_neg_inf(sv, mask_select(vw[kb2], (r >> 2) * 8 + (r & 3)));
                             if constexpr (MODE == 2) sv = keep_bits_or_neg_inf(sv, keep(kb2, r));
                             sacc[mp][kb2][r] = sv;
                             smax = fmaxf(smax, sv);
