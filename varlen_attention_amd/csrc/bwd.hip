@@ -388,12 +388,21 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                     dq4[i] = *reinterpret_cast<const f32x4 *>(Dc + 8 * i + 4 * hh);
                 }
             }
-            // MODE 2: mask words of query rows 8 i + 4 hh + j (validity folded in).
-            uint4 mq[4];
+            // MODE 2: mask words of query rows 8 i + 4 hh + j (validity folded
+            // in), read and applied only when this wave's share of the tile
+            // is not entirely kept (a uniform branch): masked scores turn into
+            // the values whose weights are exactly 0.
             if constexpr (MODE == 2) {
+                if (mcls != kDense) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    mq[i] = *reinterpret_cast<const uint4 *>(Mc + w * 32 + 8 * i + 4 * hh);
+                    for (int i = 0; i < 4; ++i) {
+                        const uint4 m4 = *reinterpret_cast<const uint4 *>(Mc + w * 32 + 8 * i + 4 * hh);
+                        s[4 * i + 0] = keep_score<kSoft>(s[4 * i + 0], mask_select(m4.x, mbit));
+                        s[4 * i + 1] = keep_score<kSoft>(s[4 * i + 1], mask_select(m4.y, mbit));
+                        s[4 * i + 2] = keep_score<kSoft>(s[4 * i + 2], mask_select(m4.z, mbit));
+                        s[4 * i + 3] = keep_score<kSoft>(s[4 * i + 3], mask_select(m4.w, mbit));
+                    }
+                }
             }
             float pv[16], dsv[16];
 #pragma unroll
@@ -403,12 +412,6 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                     pr = __builtin_amdgcn_exp2f(fmaf(s[r], c1, offq[r >> 2][r & 3]));
                 else
                     pr = sigmoid_scaled(s[r], cexp);
-                if constexpr (MODE == 2) {
-                    const uint4 &m4 = mq[r >> 2];
-                    const uint32_t word = (r & 3) == 0 ? m4.x : (r & 3) == 1 ? m4.y
-                                        : (r & 3) == 2 ? m4.z : m4.w;
-                    pr = __uint_as_float(__float_as_uint(pr) & mask_select(word, mbit));
-                }
                 pv[r] = pr;
                 if constexpr (kSoft)
                     dsv[r] = pr * (dp[r] - dq4[r >> 2][r & 3]);
@@ -588,9 +591,18 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                 // MODE 2 that key is bit key_bit(8 i + 4 hh + j) of the row's
                 // mask word: 8 j + 2 i + hh (dense) or 8 i + 4 hh + j (ranges).
                 constexpr bool kDenseBits = MASK == kMaskDense;
-                uint32_t mwk = 0u;
-                if constexpr (MODE == 2)
-                    mwk = Mc[kb2 * BQ + w * 32 + ql] >> (kDenseBits ? hh : 4 * hh);
+                // Applied only when this wave's share of the tile is not
+                // entirely kept (a uniform branch).
+                if constexpr (MODE == 2) {
+                    if (mcls != kDense) {
+                        const uint32_t mwk = Mc[kb2 * BQ + w * 32 + ql] >> (kDenseBits ? hh : 4 * hh);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            s[r] = keep_score<kSoft>(
+                                s[r], mask_select(mwk, kDenseBits ? 8 * (r & 3) + 2 * (r >> 2)
+                                                                  : 8 * (r >> 2) + (r & 3)));
+                    }
+                }
                 float dsv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -599,10 +611,6 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                         pr = __builtin_amdgcn_exp2f(fmaf(s[r], c1, off));
                     else
                         pr = sigmoid_scaled(s[r], cexp);
-                    if constexpr (MODE == 2)
-                        pr = __uint_as_float(__float_as_uint(pr) &
-                                             mask_select(mwk, kDenseBits ? 8 * (r & 3) + 2 * (r >> 2)
-                                                                         : 8 * (r >> 2) + (r & 3)));
                     if constexpr (kSoft)
                         dsv[r] = pr * (dp[r] - drow);
                     else

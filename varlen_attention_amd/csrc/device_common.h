@@ -406,6 +406,15 @@ __device__ __forceinline__ float keep_bits_or_neg_inf(float x, uint32_t keep) {
     return __uint_as_float((__float_as_uint(x) & keep) | (0xff800000u & ~keep));
 }
 
+// A score accumulator where `keep` is all ones, else the value whose weight is
+// exactly 0: -inf for a softmax logit (2^-inf = 0), +inf for a sigmoid
+// exponent u (1 / (1 + C 2^u) = 1 / inf = 0).
+template <bool SOFT>
+__device__ __forceinline__ float keep_score(float x, uint32_t keep) {
+    constexpr uint32_t kDrop = SOFT ? 0xff800000u : 0x7f800000u;
+    return __uint_as_float((__float_as_uint(x) & keep) | (kDrop & ~keep));
+}
+
 __device__ __forceinline__ float bias_value(int mode, int n, int L) {
     if (mode == kBiasLogSeqlen) return -logf((float)n);
     if (mode == kBiasLogPadlen) return -logf((float)L);

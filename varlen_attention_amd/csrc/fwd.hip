@@ -298,17 +298,27 @@ fwd_kernel(const AttnParams p) {
                     vw[kb2] = lim >= 32 ? ~0u : lim <= 0 ? 0u : (1u << lim) - 1u;
                 }
             }
-            uint32_t mw[KB];  // this lane's row of the tile's mask words
-            constexpr bool kDenseBits = MASK == kMaskDense;
+            // MODE 2: a wave whose share of the tile keeps every entry
+            // (kDense, found when it staged the words) needs no selects; the
+            // others drop the masked scores before the weights (a uniform
+            // branch, so the kept tiles pay nothing).
             if constexpr (MODE == 2) {
+                if (mcls != kDense) {
+                    constexpr bool kDenseBits = MASK == kMaskDense;
 #pragma unroll
-                for (int kb2 = 0; kb2 < KB; ++kb2)
-                    mw[kb2] = Ms[buf][kb2 * BQ + w * 32 + ql] >> (kDenseBits ? hh : 4 * hh);
+                    for (int kb2 = 0; kb2 < KB; ++kb2) {
+                        const uint32_t mw = Ms[buf][kb2 * BQ + w * 32 + ql] >> (kDenseBits ? hh : 4 * hh);
+#pragma unroll
+                        for (int mp = 0; mp < MAPS; ++mp)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                sacc[mp][kb2][r] = keep_score<kSoft>(
+                                    sacc[mp][kb2][r],
+                                    mask_select(mw, kDenseBits ? 8 * (r & 3) + 2 * (r >> 2)
+                                                               : 8 * (r >> 2) + (r & 3)));
+                    }
+                }
             }
-            auto keep = [&](int kb2, int r) {
-                return mask_select(mw[kb2], kDenseBits ? 8 * (r & 3) + 2 * (r >> 2)
-                                                       : 8 * (r >> 2) + (r & 3));
-            };
 
             // moff: per map, c0 - m, so that a weight is exp2(s c1 + moff).
             float moff[MAPS];
@@ -339,10 +349,7 @@ fwd_kernel(const AttnParams p) {
                     for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            float sv = sacc[mp][kb2][r];
-                            if constexpr (MODE == 2) sv = keep_bits_or_neg_inf(sv, keep(kb2, r));
-                            sacc[mp][kb2][r] = sv;
-                            smax = fmaxf(smax, sv);
+                            smax = fmaxf(smax, sacc[mp][kb2][r]);
                         }
                     smax = fmaxf(smax, __shfl_xor(smax, 32));
                     const float tmax = fmaf(smax, c1, c0);
@@ -376,8 +383,6 @@ fwd_kernel(const AttnParams p) {
                     for (int r = 0; r < 16; ++r) {
                         if constexpr (VARIANT == kSigmoid) {
                             pv[mp][r] = sigmoid_scaled(sacc[mp][kb2][r], cexp);
-                            if constexpr (MODE == 2)
-                                pv[mp][r] = __uint_as_float(__float_as_uint(pv[mp][r]) & keep(kb2, r));
                         } else {
                             pv[mp][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mp][kb2][r], c1, moff[mp]));
                             l_run[mp] += pv[mp][r];
