@@ -366,7 +366,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         const float *Dc = Dl(buf);
         const float *Offc = Offl(buf);
         const uint32_t *Mc = Ml(buf);
-        // One straight-line body per tile kind.  MODE 0 (no element mask)
+        // One body per tile kind (its only branch is the uniform one around
+        // the element-mask selects).  MODE 0 (no element mask)
         // needs no per-element masking: padded query rows of Q and dO read as
         // zeros, so dP = 0 and dS = 0 there (softmax: their off is -inf, so
         // P = 0) and their dV terms multiply zero rows; padded key rows are

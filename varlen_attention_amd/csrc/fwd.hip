@@ -256,10 +256,11 @@ fwd_kernel(const AttnParams p) {
         const bf16 *Kc = Ks[buf];
         const bf16 *Vc = Vs[buf];
 
-        // One straight-line tile body per kernel instantiation, so the
-        // scheduler can overlap the MFMAs of one key block with the epilogue
-        // of another, and the accumulators stay in place across iterations.
-        // MODE 0: no per-element masking.  Padded key rows of K and V read as
+        // One tile body per kernel instantiation (no second copy for special
+        // tiles), so the scheduler can overlap the MFMAs of one key block with
+        // the epilogue of another, and the accumulators stay in place across
+        // iterations; its only branches are uniform ones around work that
+        // most tiles skip.  MODE 0: no per-element masking.  Padded key rows of K and V read as
         // zeros, so for sigmoid their weights multiply zero rows, and padded
         // query rows are zeroed at the store: every padding-only sigmoid tile
         // is MODE 0.  MODE 1: softmax without an element mask (padded keys
@@ -286,10 +287,7 @@ fwd_kernel(const AttnParams p) {
             // the lim lowest bits set, taken out like a mask bit (bit ops
             // instead of compares, whose condition registers cost wait
             // states).  Padded query rows need no check: their output is
-            // zeroed at the store and their LSE set apart.  MODE 2: the
-            // tile's mask bits (validity folded in); key 8 i + 4 hh + j is
-            // bit key_bit(8 i + 4 hh + j): 8 j + 2 i + hh (dense) or
-            // 8 i + 4 hh + j (ranges).
+            // zeroed at the store and their LSE set apart.
             uint32_t vw[KB];
             if constexpr (MODE == 1) {
 #pragma unroll
@@ -298,9 +296,12 @@ fwd_kernel(const AttnParams p) {
                     vw[kb2] = lim >= 32 ? ~0u : lim <= 0 ? 0u : (1u << lim) - 1u;
                 }
             }
-            // MODE 2: a wave whose share of the tile keeps every entry
-            // (kDense, found when it staged the words) needs no selects; the
-            // others drop the masked scores before the weights (a uniform
+            // MODE 2: the tile's mask bits (validity folded in); key
+            // 8 i + 4 hh + j of a 32-key block is bit key_bit(8 i + 4 hh + j):
+            // 8 j + 2 i + hh (dense) or 8 i + 4 hh + j (ranges).  A wave whose
+            // share of the tile keeps every entry (kDense, found when it
+            // staged the words) needs no selects; the others turn masked
+            // scores into values of weight 0 before the weights (a uniform
             // branch, so the kept tiles pay nothing).
             if constexpr (MODE == 2) {
                 if (mcls != kDense) {
