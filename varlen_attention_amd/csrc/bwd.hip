@@ -381,14 +381,6 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                 dp = mfma32(row_operand<D>(dOc, kl, ks * 16 + hh * 8), v_operand(ks), dp);
             }
             // s[4i + j] = S[query q0 + 8 i + 4 hh + j][key]
-            f32x4 offq[4], dq4[4];
-            if constexpr (kSoft) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    offq[i] = *reinterpret_cast<const f32x4 *>(Offc + 8 * i + 4 * hh);
-                    dq4[i] = *reinterpret_cast<const f32x4 *>(Dc + 8 * i + 4 * hh);
-                }
-            }
             // MODE 2: mask words of query rows 8 i + 4 hh + j (validity folded
             // in), read and applied only when this wave's share of the tile
             // is not entirely kept (a uniform branch): masked scores turn into
@@ -407,17 +399,28 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
             }
             float pv[16], dsv[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float pr;
-                if constexpr (kSoft)
-                    pr = __builtin_amdgcn_exp2f(fmaf(s[r], c1, offq[r >> 2][r & 3]));
-                else
-                    pr = sigmoid_scaled(s[r], cexp);
-                pv[r] = pr;
-                if constexpr (kSoft)
-                    dsv[r] = pr * (dp[r] - dq4[r >> 2][r & 3]);
-                else
-                    dsv[r] = dp[r] * (pr - pr * pr);
+            for (int i = 0; i < 4; ++i) {
+                // Softmax row statistics of query rows 8 i + 4 hh + j, read
+                // four rows at a time (all sixteen at once cost registers).
+                f32x4 offq, dq4;
+                if constexpr (kSoft) {
+                    offq = *reinterpret_cast<const f32x4 *>(Offc + 8 * i + 4 * hh);
+                    dq4 = *reinterpret_cast<const f32x4 *>(Dc + 8 * i + 4 * hh);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * i + j;
+                    float pr;
+                    if constexpr (kSoft)
+                        pr = __builtin_amdgcn_exp2f(fmaf(s[r], c1, offq[j]));
+                    else
+                        pr = sigmoid_scaled(s[r], cexp);
+                    pv[r] = pr;
+                    if constexpr (kSoft)
+                        dsv[r] = pr * (dp[r] - dq4[j]);
+                    else
+                        dsv[r] = dp[r] * (pr - pr * pr);
+                }
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
