@@ -1023,3 +1023,60 @@ def test_diff_backward(va, d, L, bq, bk, form, lam):
     want = oracle.diff_bwd(q1, k1, q2, k2, v, do, n, lam, mask=mask, key_range=kr)
     for name, got_t, ref in zip(("dQ1", "dK1", "dQ2", "dK2", "dV"), grads, want):
         assert_rows(gpu_f64(got_t), ref, n, name)
+
+
+@pytest.mark.parametrize("variant", [SIGMOID, SOFTMAX])
+def test_hip_graph_capture_and_replay(va, variant):
+    """The whole step (block mask, forward, backward) captured in one HIP
+    graph through torch: the library allocates nothing and records no memset,
+    so replays (with eager work and synchronisations between them) give the
+    eager results bit for bit."""
+    B, H, L, d = 4, 2, 300, 64
+    n = np.array([300, 177, 31, 0], np.int32)
+    q, k, v, do = _inputs(4242 + variant, B, H, L, d, n, names="qkvd")
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    n_gpu = to_gpu(n, torch.int32)
+    bias = 1 if variant == SIGMOID else 0
+    say(f"graph capture variant={variant}")
+
+    def step(out):
+        bm = va.blockmask_build(n_gpu, L, 64, 64, out=out["bm"])
+        va.sigattn_fwd(*g[:3], n_gpu, block_mask=bm, bias=bias, variant=variant, block_q=64,
+                       block_k=64, out=out["o"], lse=out["lse"])
+        va.sigattn_bwd(*g, n_gpu, block_mask=bm, bias=bias, variant=variant, block_q=64,
+                       block_k=64, dq=out["dq"], dk=out["dk"], dv=out["dv"],
+                       o=out["o"] if variant else None, lse=out["lse"] if variant else None)
+
+    def buffers():
+        t = {key: torch.empty_like(g[0]) for key in ("o", "dq", "dk", "dv")}
+        t["lse"] = torch.empty((B, H, L), dtype=torch.float32, device=g[0].device)
+        t["bm"] = torch.empty((B, -(-L // 64), -(-L // 64)), dtype=torch.uint8,
+                              device=g[0].device)
+        return t
+
+    eager = buffers()
+    step(eager)
+    torch.cuda.synchronize()
+    cap = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture, as torch asks
+        step(cap)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(cap)
+    for rep in range(3):
+        for t in cap.values():
+            t.zero_()
+        junk = buffers()
+        step(junk)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for key in ("bm", "o", "dq", "dk", "dv"):
+            assert torch.equal(cap[key].view(torch.uint8), eager[key].view(torch.uint8)), \
+                f"replay {rep}: {key} differs from the eager run"
+        if variant:
+            assert torch.equal(cap["lse"], eager["lse"]), f"replay {rep}: lse differs"
