@@ -1080,3 +1080,33 @@ def test_hip_graph_capture_and_replay(va, variant):
                 f"replay {rep}: {key} differs from the eager run"
         if variant:
             assert torch.equal(cap["lse"], eager["lse"]), f"replay {rep}: lse differs"
+
+
+def test_two_streams_at_once(va):
+    """The library keeps no state between calls: two problems launched on two
+    streams, interleaved, give what each gives alone, bit for bit."""
+    B, H, d = 3, 2, 64
+    cases = []
+    for seed, L in ((1, 257), (2, 400)):
+        n = np.array([L, L // 3, 7], np.int32)
+        q, k, v, do = _inputs(4300 + seed, B, H, L, d, n, names="qkvd")
+        cases.append(([to_gpu_bf16(t) for t in (q, k, v, do)], to_gpu(n, torch.int32), L))
+    say("two streams")
+
+    def run(case, stream):
+        g, n_gpu, L = case
+        with torch.cuda.stream(stream):
+            bm = va.blockmask_build(n_gpu, L, 128, 128)
+            o = va.sigattn_fwd(*g[:3], n_gpu, block_mask=bm)
+            grads = va.sigattn_bwd(*g, n_gpu, block_mask=bm)
+        return (o,) + tuple(grads)
+
+    alone = [run(c, torch.cuda.current_stream()) for c in cases]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        together = [run(cases[0], s1), run(cases[1], s2)]
+        torch.cuda.synchronize()
+        for a, b_ in zip(alone, together):
+            for x, y in zip(a, b_):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16))
