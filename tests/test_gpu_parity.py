@@ -1110,3 +1110,31 @@ def test_two_streams_at_once(va):
         for a, b_ in zip(alone, together):
             for x, y in zip(a, b_):
                 assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_binding_rejects_malformed_tensors(va):
+    """The binding checks dtypes, shapes, strides and the softmax backward's
+    extra inputs before anything reaches the library; each case raises and
+    launches nothing."""
+    dev = torch.device("cuda:0")
+    B, H, L, d = 2, 2, 64, 64
+    q = torch.zeros(B, H, L, d, dtype=torch.bfloat16, device=dev)
+    n = torch.full((B,), L, dtype=torch.int32, device=dev)
+    say("binding argument checks")
+    with pytest.raises(TypeError):
+        va.sigattn_fwd(q.float(), q, q, n)                       # dtype
+    with pytest.raises(ValueError):
+        va.sigattn_fwd(q, q[:, :, :32], q, n)                    # shape
+    with pytest.raises(ValueError):
+        va.sigattn_fwd(q, q.transpose(2, 3).contiguous().transpose(2, 3), q, n)  # d stride
+    with pytest.raises(ValueError):
+        va.sigattn_fwd(q, q, q, n, mask=torch.zeros(B, L, L - 1, dtype=torch.uint8, device=dev),
+                       block_mask=va.blockmask_build(n, L))       # mask shape
+    with pytest.raises(ValueError):
+        va.sigattn_fwd(q, q, q, n, block_mask=torch.zeros(B, 3, 3, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError):
+        va.sigattn_bwd(q, q, q, q, n, variant=SOFTMAX)           # softmax needs o and lse
+    with pytest.raises(ValueError):
+        va.sigattn_fwd(q, q, q, n, lse=torch.zeros(B, H, L + 1, device=dev), variant=SOFTMAX)
+    with pytest.raises(ValueError):
+        va.blockmask_build(n, L, key_range=torch.zeros(B, L, 3, dtype=torch.int32, device=dev))
