@@ -83,6 +83,10 @@ typedef enum {
  * offsets. */
 #define SIGATTN_MAX_MASKED_L 46080
 
+/* Largest row stride (stride_l, o_stride_l) in elements: the kernels address
+ * the rows of one tile from its first row with 32-bit byte offsets. */
+#define SIGATTN_MAX_ROW_STRIDE 4194304
+
 /*
  * Problem shape.  Q, K, V and dO share one layout, O, dQ, dK and dV another;
  * both are [B, H, L, d] with the head dimension contiguous (stride 1) and the
@@ -91,8 +95,9 @@ typedef enum {
  * of 16 bytes (8 bf16 elements).
  */
 /* Sizes: B, H <= 65535 and 2 * B * H * ceil(L / 32) < 2^31 (one launch's
- * work items); larger problems are UNSUPPORTED and are split by the caller
- * (along B or H: the work is independent). */
+ * work items), row strides at most SIGATTN_MAX_ROW_STRIDE; larger problems
+ * are UNSUPPORTED and are split by the caller (along B or H: the work is
+ * independent). */
 typedef struct {
     int32_t B, H, L, d;       /* batch, heads, padded length, head dim (64 or 128) */
     int64_t stride_b, stride_h, stride_l;       /* Q, K, V, dO */

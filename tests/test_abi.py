@@ -74,6 +74,8 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, va, _shape(va), lse=ctypes.c_void_p(0x10002)) == va.ERR_ALIGNMENT
     # An element mask bounds L (32-bit offsets into each L x L mask).
     assert _fwd(lib, va, _shape(va, L=va.MAX_MASKED_L + 1), mask=FAKE, bm=FAKE) == va.ERR_UNSUPPORTED
+    # Row strides above the 32-bit tile addressing limit.
+    assert _fwd(lib, va, _shape(va, stride_l=4194304 + 8)) == va.ERR_UNSUPPORTED
     # Key ranges: not with a dense mask, only with a block mask, 8-byte aligned.
     assert _fwd(lib, va, _shape(va), mask=FAKE, kr=FAKE, bm=FAKE) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va), kr=FAKE) == va.ERR_INVALID_ARG

@@ -94,6 +94,9 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
     }
     if (s->stride_l < s->d || osl < s->d)
         return fail(SIGATTN_ERR_INVALID_ARG, "row stride smaller than the head dimension");
+    if (s->stride_l > SIGATTN_MAX_ROW_STRIDE || osl > SIGATTN_MAX_ROW_STRIDE)
+        return fail(SIGATTN_ERR_UNSUPPORTED, "row stride above %d elements",
+                    SIGATTN_MAX_ROW_STRIDE);
     p->seq_lens = seq_lens;
     p->block_mask = block_mask;
     p->mask = mask;
