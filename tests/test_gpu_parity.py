@@ -1138,3 +1138,29 @@ def test_binding_rejects_malformed_tensors(va):
         va.sigattn_fwd(q, q, q, n, lse=torch.zeros(B, H, L + 1, device=dev), variant=SOFTMAX)
     with pytest.raises(ValueError):
         va.blockmask_build(n, L, key_range=torch.zeros(B, L, 3, dtype=torch.int32, device=dev))
+
+
+@pytest.mark.parametrize("variant", [SIGMOID, SOFTMAX1])
+def test_lengths_outside_zero_to_L_are_clamped(va, variant):
+    """seq_lens is device memory and not checked on the host: a negative
+    length acts as 0 and one past L as L, in the block mask, the forward and
+    the backward alike."""
+    B, H, L, d = 4, 2, 150, 64
+    n = np.array([-5, L + 7, L, 3], np.int32)
+    q, k, v, do = _inputs(4400 + variant, B, H, L, d, np.clip(n, 0, L), names="qkvd")
+    say(f"clamped lengths variant={variant}")
+    n_gpu = to_gpu(n, torch.int32)
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    bm = _bm(va, n_gpu, L, 64, 64)
+    np.testing.assert_array_equal(bm.cpu().numpy(), oracle.blockmask(n, None, L, 64, 64))
+    bias = 1 if variant == SIGMOID else 0
+    kw = dict(block_mask=bm, bias=bias, variant=variant, block_q=64, block_k=64)
+    o, lse = va.sigattn_fwd(*g[:3], n_gpu, return_lse=True, **kw)
+    grads = va.sigattn_bwd(*g, n_gpu, o=o if variant else None, lse=lse if variant else None, **kw)
+    torch.cuda.synchronize()
+    nc = np.clip(n, 0, L).astype(np.int32)
+    want, _ = oracle.fwd(q, k, v, n, bias=bias, variant=variant)
+    assert_rows(gpu_f64(o), want, nc, "O")
+    for name, got_t, ref in zip(("dQ", "dK", "dV"), grads,
+                                oracle.bwd(q, k, v, do, n, bias=bias, variant=variant)):
+        assert_rows(gpu_f64(got_t), ref, nc, name)
