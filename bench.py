@@ -310,7 +310,8 @@ def suite_bytes(kernel: str, w, variant: int, masked, ranges: bool = False) -> f
     if kernel == "fwd":
         return (3 * valid + every) * row + (every * 4.0 if soft else 0.0)
     reads = 5 if soft else 4
-    return (reads * valid + 3 * every) * row + (valid * 4.0 if soft else 0.0)
+    writes = {"bwd": 3, "dkdv": 2, "dq": 1}[kernel]
+    return (reads * valid + writes * every) * row + (valid * 4.0 if soft else 0.0)
 
 
 class SuiteTimer:
@@ -411,10 +412,19 @@ def run_suite(args) -> int:
             "bwd": lambda: va.sigattn_bwd(q, k, v, do, n, block_mask=bm, bias=bias,
                                           variant=variant, block_q=block, block_k=block, dq=dq,
                                           dk=dk, dv=dv, o=o if variant else None, lse=lse, **form),
+            "dkdv": lambda: va.sigattn_bwd_dkdv(q, k, v, do, n, block_mask=bm, bias=bias,
+                                                variant=variant, block_q=block, block_k=block,
+                                                dk=dk, dv=dv, o=o if variant else None, lse=lse,
+                                                **form),
+            "dq": lambda: va.sigattn_bwd_dq(q, k, v, do, n, block_mask=bm, bias=bias,
+                                            variant=variant, block_q=block, block_k=block, dq=dq,
+                                            o=o if variant else None, lse=lse, **form),
         }
         fns["fwd"]()
         torch.cuda.synchronize()
-        per_pair = {"fwd": 4.0 * w.d, "bwd": 10.0 * w.d}
+        # The halves alone count the products they execute: S, dP, dV, dK
+        # (8d) and S, dP, dQ (6d).
+        per_pair = {"fwd": 4.0 * w.d, "bwd": 10.0 * w.d, "dkdv": 8.0 * w.d, "dq": 6.0 * w.d}
         names = ("blockmask",) + tuple(kernels)
         warm = timer.steps([fns[kern] for kern in names])
         tot = warm.sum(axis=1)
@@ -455,6 +465,7 @@ def run_suite(args) -> int:
     # Backward workload: lengths clipped to [200, 4096] (the same draw).
     wb = syn.single_cell_backward(args.seed)
     case("single cell bwd (clip 4096)", wb, kernels=("bwd",))
+    case("single cell bwd halves, two launches", wb, kernels=("dkdv", "dq"))
     # Padding sweep: the same lengths padded to 1x, 2x and 4x the longest.
     maxn = int(w.seq_lens.max())
     for f in (1, 2, 4):
@@ -526,7 +537,8 @@ def run_suite(args) -> int:
           f"cold: a {FLUSH_BYTES >> 20} MiB fill before each of {SUITE_REPS} timed launches of "
           "one kernel.  Times are HIP-event durations per launch; rates use the warm median; "
           "'step' is the sum of the step's kernels.")
-    print("Valid TF counts attended (query, key) pairs (4d per pair forward, 10d backward); tile TF "
+    print("Valid TF counts attended (query, key) pairs (4d per pair forward, 10d backward; the "
+          "backward halves alone 8d and 6d, the products they execute); tile TF "
           "counts every pair of the tiles the block mask keeps; GB/s is algorithmic bytes "
           "(valid input rows read once, every output row written once).")
     print()
