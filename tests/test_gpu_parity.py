@@ -249,6 +249,34 @@ def test_forward_strided_views(va):
     assert_rows(gpu_f64(o), want, n, "O (strided)")
 
 
+@pytest.mark.parametrize("variant", [SIGMOID, SOFTMAX])
+def test_backward_strided_views(va, variant):
+    """Q, K, V and dO as views of one packed [B, L, 4, H, d] tensor (row stride
+    4 H d); O, dQ, dK and dV written into views of a packed [B, L, 4, H, d]
+    output with their own strides."""
+    B, H, L, d = 2, 3, 230, 64
+    n = np.array([230, 101], np.int32)
+    rng = np.random.default_rng(22 + variant)
+    packed = syn.random_tensor(rng, (B, L, 4, H, d))
+    t = to_gpu_bf16(packed)
+    q, k, v, do = (t[:, :, i].permute(0, 2, 1, 3) for i in range(4))
+    out_store = torch.zeros(B, L, 4, H, d, dtype=torch.bfloat16, device="cuda")
+    o, dq, dk, dv = (out_store[:, :, i].permute(0, 2, 1, 3) for i in range(4))
+    n_gpu = to_gpu(n, torch.int32)
+    bias = 1 if variant == SIGMOID else 0
+    say(f"bwd strided views variant={variant}")
+    _, lse = va.sigattn_fwd(q, k, v, n_gpu, out=o, bias=bias, variant=variant, return_lse=True)
+    va.sigattn_bwd(q, k, v, do, n_gpu, bias=bias, variant=variant, dq=dq, dk=dk, dv=dv,
+                   o=o if variant else None, lse=lse if variant else None)
+    torch.cuda.synchronize()
+    qn, kn, vn, don = (np.ascontiguousarray(packed[:, :, i].transpose(0, 2, 1, 3)) for i in range(4))
+    want, _ = oracle.fwd(qn, kn, vn, n, bias=bias, variant=variant)
+    assert_rows(gpu_f64(o), want, n, "O (strided)")
+    wq, wk, wv = oracle.bwd(qn, kn, vn, don, n, bias=bias, variant=variant)
+    for name, got_t, ref in zip(("dQ", "dK", "dV"), (dq, dk, dv), (wq, wk, wv)):
+        assert_rows(gpu_f64(got_t), ref, n, f"{name} (strided)")
+
+
 def test_softmax1_equals_softmax_with_zero_key_on_gpu(va):
     """softmax_1 page: a prepended zero key with a zero value adds 1 to each denominator."""
     B, H, L, d = 2, 2, 190, 64
