@@ -174,3 +174,28 @@ def test_max_masked_length_matches_header():
     m = re.search(r"#define\s+SIGATTN_MAX_MASKED_L\s+(\d+)", hdr)
     assert m and int(m.group(1)) == va.MAX_MASKED_L
 
+
+
+def test_error_messages_are_per_thread(lib):
+    """sigattn_last_error is thread-local: two host threads failing for
+    different reasons at the same time each read back their own message."""
+    import threading
+
+    import varlen_attention_amd as va
+    bad = {"head dim": _shape(va, d=96), "must be positive": _shape(va, B=0)}
+    errors = []
+
+    def worker(expect, shape):
+        for _ in range(2000):
+            st = _fwd(lib, va, shape)
+            msg = lib.sigattn_last_error().decode()
+            if st == va.OK or expect not in msg:
+                errors.append((expect, st, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=item) for item in bad.items()]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
