@@ -1,0 +1,67 @@
+"""Host-side logic of bench.py (no GPU): the source digest that ties a
+counter summary to the kernel code, the algorithmic byte counts, and the
+traffic arithmetic from rocprofv3 counter tables."""
+import os
+
+import numpy as np
+
+import bench
+import synthetic as syn
+
+
+def test_digest_ignores_comments_and_blank_lines():
+    a = "int f(int x) {\n    return x + 1;  // one more\n}\n"
+    b = "// a new header comment\n\nint f(int x) {\n    return x + 1;\n}\n\n"
+    c = "int f(int x) {\n    return x + 2;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+
+
+def test_committed_traffic_matches_or_is_withheld():
+    """A counter summary counts only while its digest matches the current
+    kernel code; otherwise read_traffic gives None (never stale numbers)."""
+    for kernel in ("fwd", "bwd"):
+        t = bench.read_traffic(kernel, "single_cell_b32h8d64_lognormal800")
+        assert t is None or t > 0
+        path = os.path.join(bench.PROFILES, f"traffic_{kernel}_single_cell_b32h8d64_lognormal800.txt")
+        text = open(path).read()
+        matches = f"source_sha256_16: {bench.source_digest(kernel)}" in text
+        assert (t is not None) == matches
+
+
+def test_algorithmic_bytes_by_hand():
+    w = syn.make_workload("t", seed=1, B=3, H=2, d=64, lengths="uniform", lo=10, hi=50,
+                          tensors=())
+    valid = int(np.clip(w.seq_lens, 0, w.L).sum()) * w.H
+    every = w.B * w.L * w.H
+    row = 2 * w.d
+    assert bench.algorithmic_bytes("fwd", w) == (3 * valid + every) * row
+    assert bench.algorithmic_bytes("bwd", w) == (4 * valid + 3 * every) * row
+
+
+def _counter_table(dirname, rows):
+    os.makedirs(dirname, exist_ok=True)
+    with open(os.path.join(dirname, "p_counter_collection.csv"), "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (kernel, counter, value) in enumerate(rows):
+            f.write(f'{i},"{kernel}",{counter},{value}\n')
+
+
+def test_traffic_scaled_by_the_copy_reference(tmp_path):
+    """Counters read KiB per dispatch; each is scaled by the ratio between the
+    true size of a plain copy and what the same counter reads for it."""
+    sym = "void sigattn::fwd_kernel<64, 0, 4, 2, 0, 1>(sigattn::AttnParams)"
+    _counter_table(tmp_path / "fetch", [(sym, "FETCH_SIZE", 1000.0), (sym, "FETCH_SIZE", 1200.0),
+                                        ("other", "FETCH_SIZE", 9e9)])
+    _counter_table(tmp_path / "write", [(sym, "WRITE_SIZE", 500.0)])
+    _counter_table(tmp_path / "cf", [("copy", "FETCH_SIZE", 128 * 1024.0)])  # reads half
+    _counter_table(tmp_path / "cw", [("copy", "WRITE_SIZE", 256 * 1024.0)])  # exact
+    w = syn.make_workload("t", seed=1, B=2, H=1, d=64, lengths="uniform", lo=10, hi=20,
+                          tensors=())
+    text = bench.summarize_traffic("fwd", str(tmp_path / "fetch"), str(tmp_path / "write"),
+                                   str(tmp_path / "cf"), str(tmp_path / "cw"), 256, w, "t")
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line
+                  and not line.startswith("#"))
+    assert float(fields["fetch_scale"]) == 2.0 and float(fields["write_scale"]) == 1.0
+    assert int(fields["hbm_bytes_per_launch"]) == int((1100.0 * 2.0 + 500.0) * 1024)
+    assert fields["source_sha256_16"] == bench.source_digest("fwd")
