@@ -73,7 +73,8 @@ typedef enum {
 typedef enum {
     SIGATTN_OK = 0,
     SIGATTN_ERR_INVALID_ARG = -1, /* null required pointer, non-positive size, bad enum */
-    SIGATTN_ERR_UNSUPPORTED = -2, /* head dim or block size not built, strides not unit in d */
+    SIGATTN_ERR_UNSUPPORTED = -2, /* head dim or block size not built, sizes or strides
+                                     beyond the limits below */
     SIGATTN_ERR_ALIGNMENT = -3,   /* pointer or stride not 16-byte aligned */
     SIGATTN_ERR_LAUNCH = -4       /* HIP reported an error while enqueuing */
 } sigattn_status;
