@@ -192,10 +192,9 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
  * bias_mode and variant must be those the forward ran with.
  * The dK/dV and dQ work items write disjoint outputs and use no atomics, so
  * results are bit-for-bit reproducible and equal to those of the two calls
- * below.  When the key tiles of dK/dV and the query tiles of dQ have the same
- * height (block_q and block_k both >= 128, or equal), both kinds of work item
- * go out in one launch, sharing one ramp-up and one tail; otherwise this is
- * the two launches below.
+ * below.  When block_q == block_k, both kinds of work item go out in one
+ * launch, sharing one ramp-up and one tail; otherwise this is the two
+ * launches below.
  * Errors: as sigattn_fwd; INVALID_ARG for a softmax variant without o or
  * lse, ALIGNMENT for o not 16-byte or lse not 4-byte aligned.
  */
