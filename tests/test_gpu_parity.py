@@ -804,11 +804,19 @@ def _sampled_fwd_bwd(va, q, k, v, do, n, L, b_rows, gpu_kw, oracle_kw, what):
     starts of 8-key windows for dK and dV)."""
     n_gpu = to_gpu(n, torch.int32)
     g = [to_gpu_bf16(t) for t in (q, k, v, do)]
-    o = va.sigattn_fwd(*g[:3], n_gpu, **gpu_kw)
-    dq, dk, dv = va.sigattn_bwd(*g, n_gpu, **gpu_kw)
+    soft = gpu_kw.get("variant", SIGMOID) != SIGMOID
+    if soft:  # the softmax backward takes the forward's O and LSE
+        o, lse = va.sigattn_fwd(*g[:3], n_gpu, return_lse=True, **gpu_kw)
+        dq, dk, dv = va.sigattn_bwd(*g, n_gpu, o=o, lse=lse, **gpu_kw)
+    else:
+        o = va.sigattn_fwd(*g[:3], n_gpu, **gpu_kw)
+        dq, dk, dv = va.sigattn_bwd(*g, n_gpu, **gpu_kw)
     torch.cuda.synchronize()
     B, H = q.shape[:2]
     valid = np.broadcast_to(row_valid(n, B, L)[:, None, :], (B, H, L))
+    if soft:
+        got_lse = lse.cpu().numpy().astype(np.float64)
+        assert np.all(np.isneginf(got_lse[~valid])), f"{what}: padded LSE not -inf"
     outs = {}
     for name, t in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
         outs[name] = t
@@ -817,8 +825,12 @@ def _sampled_fwd_bwd(va, q, k, v, do, n, L, b_rows, gpu_kw, oracle_kw, what):
     got = {key: [] for key in outs}
     want = {key: [] for key in outs}
     for b, h, rows, starts in b_rows:
-        ro, _ = oracle.fwd_rows(q, k, v, n, b, h, rows, **oracle_kw)
+        ro, rl = oracle.fwd_rows(q, k, v, n, b, h, rows, **oracle_kw)
         rq, _, _ = oracle.bwd_rows(q, k, v, do, n, b, h, rows, [], **oracle_kw)
+        if soft:
+            live = [i for i, r in enumerate(rows) if r < int(n[b])]
+            np.testing.assert_allclose(got_lse[b, h, [rows[i] for i in live]], rl[live],
+                                       rtol=1e-3, atol=1e-3, err_msg=f"{what} LSE")
         for key, ref in (("O", ro), ("dQ", rq)):
             got[key].append(gpu_f64(outs[key][b, h, rows]))
             want[key].append(ref)
@@ -894,6 +906,35 @@ def test_backward_single_cell_full_size(va, single_cell_inputs):
     w = single_cell_inputs
     say(f"bwd full {w.name} L={w.L}")
     _check_sampled_bwd(va, w)
+
+
+@pytest.mark.parametrize("block,variant", [(64, SIGMOID), (128, SOFTMAX), (128, SOFTMAX1)])
+def test_single_cell_full_size_blocks_and_variants(va, single_cell_inputs, block, variant):
+    """The single-cell shapes (B32 H8 d64, L 1584) in the other launch
+    configurations the benchmark suite times: 64-blocks (two block-mask lines
+    per workgroup) with sigmoid and the -ln n bias, and the softmax-family
+    forward and backward (the backward from the forward's O and LSE, no bias).
+    Padded rows exactly zero; sampled rows of O, LSE, dQ, dK, dV against the
+    oracle."""
+    w = single_cell_inputs
+    bias = 1 if variant == SIGMOID else 0
+    say(f"single cell full size block={block} variant={variant}")
+    n_gpu = to_gpu(w.seq_lens, torch.int32)
+    bm = _bm(va, n_gpu, w.L, block, block)
+    np.testing.assert_array_equal(bm.cpu().numpy(),
+                                  oracle.blockmask(w.seq_lens, None, w.L, block, block))
+    rng = np.random.default_rng(20 + block + variant)
+    order = np.argsort(w.seq_lens)
+    b_rows = []
+    for b in (int(order[0]), int(order[-1]), int(rng.integers(w.B))):  # shortest, longest, any
+        nb = int(w.seq_lens[b])
+        h = int(rng.integers(w.H))
+        starts = (0, max(nb - 8, 0), int(rng.integers(0, max(nb - 8, 1))))
+        b_rows.append((b, h, _band_rows(rng, nb, w.L), starts))
+    _sampled_fwd_bwd(va, w.q, w.k, w.v, w.do, w.seq_lens, w.L, b_rows,
+                     dict(block_mask=bm, bias=bias, variant=variant, block_q=block, block_k=block),
+                     dict(bias=bias, variant=variant),
+                     f"single cell block {block} variant {variant}")
 
 
 def test_long_documents_key_ranges_full_size(va):
