@@ -330,3 +330,15 @@ def diff_bwd(q1, k1, q2, k2, v, do, seq_lens, lam: float, mask=None, bias=BIAS_N
     g2 = bwd(q2, k2, v, do, seq_lens, mask=mask, bias=bias, variant=SOFTMAX, scale=scale,
              precision=precision, threads=threads, key_range=key_range)
     return g1[0], g1[1], -lam * g2[0], -lam * g2[1], g1[2] - lam * g2[2]
+
+
+def diff_bwd_rows(q1, k1, q2, k2, v, do, seq_lens, lam: float, b: int, h: int, q_rows, k_rows,
+                  mask=None, bias=BIAS_NONE, scale=None, precision="f64", key_range=None):
+    """Selected rows of one head of diff_bwd: (dq1 [len(q_rows), d], dk1
+    [len(k_rows), d], dq2, dk2, dv), by the same linearity (each map's SOFTMAX
+    backward rows with do; map 2's scaled by -lam; dv the sum)."""
+    kw = dict(mask=mask, bias=bias, variant=SOFTMAX, scale=scale, precision=precision,
+              key_range=key_range)
+    dq1, dk1, dv1 = bwd_rows(q1, k1, v, do, seq_lens, b, h, q_rows, k_rows, **kw)
+    dq2, dk2, dv2 = bwd_rows(q2, k2, v, do, seq_lens, b, h, q_rows, k_rows, **kw)
+    return dq1, dk1, -lam * dq2, -lam * dk2, dv1 - lam * dv2

@@ -1049,6 +1049,45 @@ def test_diff_forward_single_cell_full_size(va, single_cell_inputs):
     assert_close(np.concatenate(got), np.concatenate(want), "O sampled diff")
 
 
+def test_diff_backward_single_cell_full_size(va, single_cell_inputs):
+    """Differential backward at the single-cell shapes (B32 H8 d64, L 1584,
+    block 128) from the forward's per-map outputs and LSEs: padded rows of all
+    five gradients exactly zero, sampled rows against the oracle."""
+    w = single_cell_inputs
+    rng = np.random.default_rng(23)
+    q2 = syn.random_tensor(rng, w.q.shape)
+    k2 = syn.random_tensor(rng, w.k.shape)
+    lam = 0.8
+    say(f"diff bwd full {w.name} L={w.L}")
+    n_gpu = to_gpu(w.seq_lens, torch.int32)
+    bm = _bm(va, n_gpu, w.L, 128, 128)
+    g = [to_gpu_bf16(t) for t in (w.q, w.k, q2, k2, w.v, w.do)]
+    o, l1, l2, o1, o2 = va.sigattn_diff_fwd(*g[:5], n_gpu, lam, return_maps=True, block_mask=bm)
+    grads = va.sigattn_diff_bwd(*g, o1, o2, l1, l2, n_gpu, lam, block_mask=bm)
+    torch.cuda.synchronize()
+    names = ("dQ1", "dK1", "dQ2", "dK2", "dV")
+    valid = np.broadcast_to(row_valid(w.seq_lens, w.B, w.L)[:, None, :], (w.B, w.H, w.L))
+    pad = torch.from_numpy(~valid).to(grads[0].device)
+    for name, t in zip(names, grads):
+        assert bool((t.view(torch.int16)[pad] == 0).all()), f"padded {name} rows not zero"
+    got = {key: [] for key in names}
+    want = {key: [] for key in names}
+    order = np.argsort(w.seq_lens)
+    for b in (int(order[0]), int(order[-1]), int(rng.integers(w.B))):  # shortest, longest, any
+        nb, h = int(w.seq_lens[b]), int(rng.integers(w.H))
+        q_rows = _band_rows(rng, nb, w.L)
+        k0 = int(rng.integers(0, max(nb - 8, 1)))
+        k_rows = sorted(set(range(k0, min(k0 + 8, nb))) | set(range(max(nb - 4, 0), nb)))
+        ref = oracle.diff_bwd_rows(w.q, w.k, q2, k2, w.v, w.do, w.seq_lens, lam, b, h, q_rows,
+                                   k_rows)
+        for name, t, r in zip(names, grads, ref):
+            rows = q_rows if name.startswith("dQ") else k_rows
+            got[name].append(gpu_f64(t[b, h, rows]))
+            want[name].append(r)
+    for key in names:
+        assert_close(np.concatenate(got[key]), np.concatenate(want[key]), f"diff {key} sampled")
+
+
 DIFF_BWD_CASES = [
     # d, L, block_q, block_k, mask form, lambda
     (64, 300, 128, 128, "none", 0.8),

@@ -56,6 +56,30 @@ def test_rows_match_full(oracle_lib):
     np.testing.assert_allclose(got, o[1, 1, rows], rtol=1e-13, atol=1e-15)
 
 
+@pytest.mark.parametrize("form", ["none", "mask", "range"])
+def test_backward_rows_match_full(oracle_lib, form):
+    """The sampled-row backward equals the rows of the whole-tensor backward
+    (itself pinned by autograd below), with each mask form."""
+    rng = np.random.default_rng(15)
+    B, H, L, d = 2, 2, 30, 8
+    q1, k1, q2, k2, v, do = random_inputs(rng, B, H, L, d, names="abcdef")
+    n = np.array([30, 19], np.int32)
+    mask = kr = None
+    if form == "mask":
+        mask = (rng.random((B, L, L)) < 0.5).astype(np.uint8)
+    elif form == "range":
+        lo = rng.integers(0, L, size=(B, L))
+        kr = np.stack([lo, lo + rng.integers(-2, 12, size=(B, L))], axis=-1).astype(np.int32)
+    lam = -0.7
+    full = oracle_lib.diff_bwd(q1, k1, q2, k2, v, do, n, lam, mask=mask, key_range=kr)
+    q_rows, k_rows = [0, 4, 18, 19, 29], [3, 4, 5, 17, 18, 19, 20]
+    got = oracle_lib.diff_bwd_rows(q1, k1, q2, k2, v, do, n, lam, 1, 0, q_rows, k_rows,
+                                   mask=mask, key_range=kr)
+    for name, g_, f_ in zip(("dq1", "dk1", "dq2", "dk2", "dv"), got, full):
+        rows = q_rows if name.startswith("dq") else k_rows
+        np.testing.assert_allclose(g_, f_[1, 0, rows], rtol=1e-12, atol=1e-14, err_msg=name)
+
+
 def test_diff_backward_matches_torch_autograd(oracle_lib):
     """Gradients of sum(dO * O) through two dense softmax maps, by torch float64
     autograd, against the oracle's composition."""
