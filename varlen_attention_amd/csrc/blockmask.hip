@@ -6,7 +6,7 @@
 // by every head and layer.
 //
 // Padding-only batches use the closed form (i*bq < n) && (j*bk < n), and
-// ((i+1)*bq <= n) && ((j+1)*bk <= n) for full tiles, one thread per entry.
+// ((i+1)*bq <= n) && ((j+1)*bk <= n) for full tiles, one wave per block row.
 // With an element mask the builder is one HBM scan of the valid rectangle
 // [0, n) x [0, n) of each mask: a workgroup owns a band of bq rows and a group
 // of key tiles, so it writes its outputs alone (no atomics to global memory),
@@ -16,19 +16,21 @@
 
 namespace sigattn {
 
-__global__ void __launch_bounds__(256)
-blockmask_padding_kernel(const int32_t *__restrict__ seq_lens, int B, int L, int bq, int bk,
-                         int Tq, int Tk, uint8_t *__restrict__ out) {
-    int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int64_t total = (int64_t)B * Tq * Tk;
-    if (idx >= total) return;
-    int j = (int)(idx % Tk);
-    int i = (int)((idx / Tk) % Tq);
-    int b = (int)(idx / ((int64_t)Tq * Tk));
-    int n = clamp_len(seq_lens[b], L);
-    const bool any = (i * bq < n) && (j * bk < n);
-    const bool full = ((i + 1) * bq <= n) && ((j + 1) * bk <= n);
-    out[idx] = (uint8_t)(any | (full << 1));
+// Grid: (Tq, B); one wave per block row i of batch entry b, its lanes
+// stepping over the row's Tk entries.  The full-tile tests are written as
+// i*bq <= n - bq (that is, (i+1)*bq <= n) so that no product passes L.
+__global__ void __launch_bounds__(64)
+blockmask_padding_kernel(const int32_t *__restrict__ seq_lens, int L, int bq, int bk, int Tq,
+                         int Tk, uint8_t *__restrict__ out) {
+    const int i = blockIdx.x, b = blockIdx.y;
+    const int n = clamp_len(seq_lens[b], L);
+    const bool row_any = i * bq < n, row_full = i * bq <= n - bq;
+    uint8_t *row = out + ((int64_t)b * Tq + i) * Tk;
+    for (int j = (int)threadIdx.x; j < Tk; j += 64) {
+        const bool any = row_any && j * bk < n;
+        const bool full = row_full && j * bk <= n - bk;
+        row[j] = (uint8_t)(any | (full << 1));
+    }
 }
 
 // Grid: (Tq * groups, B); 256 threads.  tiles_per_group * bk <= 1024 columns,
@@ -179,19 +181,16 @@ blockmask_range_kernel(const int32_t *__restrict__ seq_lens, const int32_t *__re
 hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask,
                             const int32_t *key_range, int B, int L, int block_q, int block_k,
                             uint8_t *out, hipStream_t stream) {
-    const int Tq = (L + block_q - 1) / block_q;
-    const int Tk = (L + block_k - 1) / block_k;
+    const int Tq = (int)(((int64_t)L + block_q - 1) / block_q);
+    const int Tk = (int)(((int64_t)L + block_k - 1) / block_k);
     if (key_range != nullptr) {
         hipLaunchKernelGGL(blockmask_range_kernel, dim3((unsigned)Tq, (unsigned)B), dim3(256), 0,
                            stream, seq_lens, key_range, L, block_q, block_k, Tq, Tk, out);
         return hipGetLastError();
     }
     if (mask == nullptr) {
-        const int64_t total = (int64_t)B * Tq * Tk;
-        const int threads = 256;
-        const int64_t blocks = (total + threads - 1) / threads;
-        hipLaunchKernelGGL(blockmask_padding_kernel, dim3((unsigned)blocks), dim3(threads), 0,
-                           stream, seq_lens, B, L, block_q, block_k, Tq, Tk, out);
+        hipLaunchKernelGGL(blockmask_padding_kernel, dim3((unsigned)Tq, (unsigned)B), dim3(64), 0,
+                           stream, seq_lens, L, block_q, block_k, Tq, Tk, out);
         return hipGetLastError();
     }
     int bk_shift = 0;
