@@ -67,10 +67,10 @@ def _load():
         f.argtypes = [I, I, I, P, P, P, P, P, I, I, I, I, R, P, P]
         f.restype = None
         f = getattr(lib, "oracle_bwd_dq_rows" + sfx)
-        f.argtypes = [I, I, I, P, P, P, P, P, I, I, R, I, I, P]
+        f.argtypes = [I, I, I, P, P, P, P, P, P, I, I, R, I, I, P]
         f.restype = None
         f = getattr(lib, "oracle_bwd_dkv_rows" + sfx)
-        f.argtypes = [I, I, I, P, P, P, P, P, I, I, R, I, I, P, P]
+        f.argtypes = [I, I, I, P, P, P, P, P, P, I, I, R, I, I, P, P]
         f.restype = None
     lib.oracle_blockmask.argtypes = [P, P, I, I, I, I, P]
     lib.oracle_blockmask.restype = None
@@ -87,7 +87,13 @@ def _dtype(precision):
 
 
 def _threads(threads):
-    return threads or os.cpu_count() or 1
+    """Worker threads: as asked, else every CPU the process sees, capped by
+    OMP_NUM_THREADS when it is set (a machine's share of cores per GPU)."""
+    if threads:
+        return threads
+    n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(cap)) if cap.isdigit() and int(cap) > 0 else n
 
 
 def default_scale(d: int) -> float:
@@ -227,8 +233,13 @@ def fwd_tiled(q, k, v, seq_lens, block_mask=None, block_q=64, block_k=64, mask=N
 
 
 def bwd(q, k, v, do, seq_lens, mask=None, bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None,
-        precision="f64", threads=None, heads=None, key_range=None):
-    """dQ, dK, dV [B, H, L, d] by the plain definition (oracle_bwd_*_rows)."""
+        precision="f64", threads=None, heads=None, key_range=None, o=None):
+    """dQ, dK, dV [B, H, L, d] by the plain definition (oracle_bwd_*_rows).
+
+    ``o``: the forward output the backward is handed (bf16 bits [B, H, L, d],
+    softmax family only), from which D = rowsum(dO * O) is formed, as the
+    library's backward forms it from the O it is given; None for the exact
+    output."""
     mask = _element_mask(mask, key_range, q.shape[2])
     lib = _load()
     B, H, L, d = _heads(q)
@@ -244,15 +255,16 @@ def bwd(q, k, v, do, seq_lens, mask=None, bias=BIAS_LOG_SEQLEN, variant=SIGMOID,
     def one(bh):
         b, h = bh
         qs, ks, vs, ds = (np.ascontiguousarray(t[b, h]) for t in (q, k, v, do))
+        os_ = None if o is None else np.ascontiguousarray(o[b, h])
         mb = None if mask is None else np.ascontiguousarray(mask[b])
         gq = np.zeros((L, d), dtype=dt)
         gk = np.zeros((L, d), dtype=dt)
         gv = np.zeros((L, d), dtype=dt)
         n = int(seq_lens[b])
-        fq(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(mb), bias, variant, scale,
-           0, L, _ptr(gq))
-        fkv(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(mb), bias, variant, scale,
-            0, L, _ptr(gk), _ptr(gv))
+        fq(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(os_), _ptr(mb), bias, variant,
+           scale, 0, L, _ptr(gq))
+        fkv(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(os_), _ptr(mb), bias, variant,
+            scale, 0, L, _ptr(gk), _ptr(gv))
         dq[b, h], dk[b, h], dv[b, h] = gq, gk, gv
 
     with ThreadPoolExecutor(_threads(threads)) as ex:
@@ -261,8 +273,10 @@ def bwd(q, k, v, do, seq_lens, mask=None, bias=BIAS_LOG_SEQLEN, variant=SIGMOID,
 
 
 def bwd_rows(q, k, v, do, seq_lens, b: int, h: int, q_rows, k_rows, mask=None,
-             bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None, precision="f64", key_range=None):
-    """Selected rows of one head: (dq [len(q_rows), d], dk, dv [len(k_rows), d])."""
+             bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None, precision="f64", key_range=None,
+             o=None):
+    """Selected rows of one head: (dq [len(q_rows), d], dk, dv [len(k_rows), d]);
+    ``o`` as for bwd."""
     lib = _load()
     B, H, L, d = _heads(q)
     dt = _dtype(precision)
@@ -270,6 +284,7 @@ def bwd_rows(q, k, v, do, seq_lens, b: int, h: int, q_rows, k_rows, mask=None,
     fkv = getattr(lib, "oracle_bwd_dkv_rows_" + precision)
     scale = default_scale(d) if scale is None else scale
     qs, ks, vs, ds = (np.ascontiguousarray(t[b, h]) for t in (q, k, v, do))
+    os_ = None if o is None else np.ascontiguousarray(o[b, h])
     # Only batch entry b's mask is needed (its key ranges written out).
     mb = None if mask is None else np.ascontiguousarray(mask[b])
     if key_range is not None:
@@ -279,8 +294,8 @@ def bwd_rows(q, k, v, do, seq_lens, b: int, h: int, q_rows, k_rows, mask=None,
     dq = np.zeros((len(q_rows), d), dtype=dt)
     for i, r in enumerate(q_rows):
         row = np.zeros((1, d), dtype=dt)
-        fq(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(mb), bias, variant, scale,
-           int(r), int(r) + 1, _ptr(row))
+        fq(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(os_), _ptr(mb), bias, variant,
+           scale, int(r), int(r) + 1, _ptr(row))
         dq[i] = row[0]
     dk = np.zeros((len(k_rows), d), dtype=dt)
     dv = np.zeros((len(k_rows), d), dtype=dt)
@@ -289,8 +304,8 @@ def bwd_rows(q, k, v, do, seq_lens, b: int, h: int, q_rows, k_rows, mask=None,
         lo, hi = min(k_rows), max(k_rows) + 1
         gk = np.zeros((hi - lo, d), dtype=dt)
         gv = np.zeros((hi - lo, d), dtype=dt)
-        fkv(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(mb), bias, variant, scale,
-            lo, hi, _ptr(gk), _ptr(gv))
+        fkv(L, d, n, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(ds), _ptr(os_), _ptr(mb), bias, variant,
+            scale, lo, hi, _ptr(gk), _ptr(gv))
         for i, c in enumerate(k_rows):
             dk[i] = gk[c - lo]
             dv[i] = gv[c - lo]
@@ -321,14 +336,15 @@ def diff_fwd_rows(q1, k1, q2, k2, v, seq_lens, lam: float, b: int, h: int, rows,
 
 
 def diff_bwd(q1, k1, q2, k2, v, do, seq_lens, lam: float, mask=None, bias=BIAS_NONE, scale=None,
-             precision="f64", threads=None, key_range=None):
+             precision="f64", threads=None, key_range=None, o1=None, o2=None):
     """Gradients (dq1, dk1, dq2, dk2, dv) of sum(do * o), o = diff_fwd(...).
     The output is o1 - lam o2, linear in the two maps: map 1's gradients are
-    the SOFTMAX backward with do, map 2's are -lam times it, dv adds both."""
+    the SOFTMAX backward with do, map 2's are -lam times it, dv adds both.
+    o1, o2: each map's output as the backward is handed it (see bwd)."""
     g1 = bwd(q1, k1, v, do, seq_lens, mask=mask, bias=bias, variant=SOFTMAX, scale=scale,
-             precision=precision, threads=threads, key_range=key_range)
+             precision=precision, threads=threads, key_range=key_range, o=o1)
     g2 = bwd(q2, k2, v, do, seq_lens, mask=mask, bias=bias, variant=SOFTMAX, scale=scale,
-             precision=precision, threads=threads, key_range=key_range)
+             precision=precision, threads=threads, key_range=key_range, o=o2)
     return g1[0], g1[1], -lam * g2[0], -lam * g2[1], g1[2] - lam * g2[2]
 
 
@@ -342,3 +358,72 @@ def diff_bwd_rows(q1, k1, q2, k2, v, do, seq_lens, lam: float, b: int, h: int, q
     dq1, dk1, dv1 = bwd_rows(q1, k1, v, do, seq_lens, b, h, q_rows, k_rows, **kw)
     dq2, dk2, dv2 = bwd_rows(q2, k2, v, do, seq_lens, b, h, q_rows, k_rows, **kw)
     return dq1, dk1, -lam * dq2, -lam * dk2, dv1 - lam * dv2
+
+
+def schedule(seq_lens, block_mask, H: int, L: int, block_q: int, block_k: int) -> dict:
+    """Work schedule of one batch, by its definition (Binary Block Masking,
+    "Presentation": the block structure is built once and shared by every
+    head; "How it works": only the kept blocks are visited), written out with
+    plain loops.
+
+    Work items cover 128-row tiles of every (batch entry, head).  The pairs
+    are ordered by length rank (longest first, ties by index; batches of more
+    than 1024 entries keep index order) and then head; pair p goes to XCD
+    p % 8.  XCD x lists, for its pairs in order, the tiles ceil(n/128) of
+    every non-empty sequence (all tiles of kind 0, then of kind 1 when there
+    are two kinds), then, for its pairs again, all ceil(L/128) tiles of every
+    empty sequence.  Its k-th item sits in slot 8 k + x; slots past the end
+    are None.  Items are (b, h, kind, tile, n) with n = clamp(seq_lens[b]).
+
+    Kept-entry lists: for batch entry b and 128-row query group g, the lines
+    are the block rows g R .. g R + R - 1 (R = 128 / block_q) below Tq, and the
+    entries e < min(Tk, ceil(n / block_k)) that some line keeps, increasing,
+    each with the bits of the lines that keep it and of those whose entry is
+    3 (full).  Key groups the same down the block columns (C = 128 / block_k,
+    entries e < min(Tq, ceil(n / block_q))).
+
+    Returns {"items1": [...], "items2": [...], "qlists": [[...] per g] per b,
+    "klists": likewise}."""
+    n = [int(min(max(int(x), 0), L)) for x in seq_lens]
+    B = len(n)
+    bm = np.asarray(block_mask)
+    G = -(-L // 128)
+    Tq, Tk = -(-L // block_q), -(-L // block_k)
+    order = sorted(range(B), key=lambda b: (-n[b], b)) if B <= 1024 else list(range(B))
+    pairs = [(order[r], h) for r in range(B) for h in range(H)]
+    per_xcd = -(-(B * H) // 8)
+    out = {}
+    for K, name in ((1, "items1"), (2, "items2")):
+        slots = [None] * (8 * per_xcd * G * K)
+        for x in range(8):
+            seq = []
+            for p in range(x, B * H, 8):
+                b, h = pairs[p]
+                if n[b] > 0:
+                    seq += [(b, h, kind, t, n[b]) for kind in range(K)
+                            for t in range(-(-n[b] // 128))]
+            for p in range(x, B * H, 8):
+                b, h = pairs[p]
+                if n[b] == 0:
+                    seq += [(b, h, kind, t, 0) for kind in range(K) for t in range(G)]
+            for k, item in enumerate(seq):
+                slots[8 * k + x] = item
+        out[name] = slots
+
+    def entries(b, lines, nblk, value):
+        kept = []
+        for e in range(nblk):
+            on = sum(1 << r for r, ln in enumerate(lines) if value(b, ln, e) != 0)
+            full = sum(1 << r for r, ln in enumerate(lines) if value(b, ln, e) & 2)
+            if on:
+                kept.append((e, on, full))
+        return kept
+
+    R, C = 128 // block_q, 128 // block_k
+    out["qlists"] = [[entries(b, [g * R + r for r in range(R) if g * R + r < Tq],
+                              min(Tk, -(-n[b] // block_k)), lambda b_, ln, e: int(bm[b_, ln, e]))
+                      for g in range(G)] for b in range(B)]
+    out["klists"] = [[entries(b, [g * C + c for c in range(C) if g * C + c < Tk],
+                              min(Tq, -(-n[b] // block_q)), lambda b_, ln, e: int(bm[b_, e, ln]))
+                      for g in range(G)] for b in range(B)]
+    return out

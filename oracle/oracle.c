@@ -312,13 +312,30 @@ static real row_D(int L, int d, int n, const uint16_t *q, const uint16_t *k, con
 }
 
 /*
+ * D of one softmax-family row: rowsum(dO_r * o_r).  With the exact output
+ * (o == NULL) it is sum_c p[r, c] dp[r, c] (row_D); when the backward is
+ * handed a stored output o (bf16 bits [L, d], as the library's backward takes
+ * the forward's bf16 O), D is formed from that o, which is what the backward
+ * computes with.
+ */
+static real row_D_given(int L, int d, int n, const uint16_t *q, const uint16_t *k,
+                        const uint16_t *v, const uint16_t *dout, const uint16_t *o,
+                        const uint8_t *mask, int variant, real scale, real beta, int r, real mr,
+                        real lr) {
+    if (o == NULL) return row_D(L, d, n, q, k, v, dout, mask, variant, scale, beta, r, mr, lr);
+    return dot_bf16(dout + (size_t)r * d, o + (size_t)r * d, d);
+}
+
+/*
  * Backward, query side: dQ rows [r0, r1) of one head.
  *   dQ_r = scale * sum_c dS[r, c] k_c;  0 for padded rows.
- * dout: [L, d] bf16 bits.  dq: [(r1 - r0), d].
+ * dout: [L, d] bf16 bits; o: the output the backward is given (bf16 bits
+ * [L, d]) or NULL for the exact one (softmax family only).  dq: [(r1 - r0), d].
  */
 void FN(oracle_bwd_dq_rows)(int L, int d, int seq_len, const uint16_t *q, const uint16_t *k,
-                            const uint16_t *v, const uint16_t *dout, const uint8_t *mask,
-                            int bias_mode, int variant, real scale, int r0, int r1, real *dq) {
+                            const uint16_t *v, const uint16_t *dout, const uint16_t *o,
+                            const uint8_t *mask, int bias_mode, int variant, real scale, int r0,
+                            int r1, real *dq) {
     int n = clamp_len(seq_len, L);
     real beta = n > 0 ? bias_value(bias_mode, n, L) : (real)0;
     for (int r = r0; r < r1; ++r) {
@@ -329,7 +346,7 @@ void FN(oracle_bwd_dq_rows)(int L, int d, int seq_len, const uint16_t *q, const 
         if (variant != V_SIGMOID) {
             row_stats(L, d, n, q, k, mask, variant, scale, beta, r, &mr, &lr);
             if (lr == 0) continue; /* softmax row with no valid key */
-            Dr = row_D(L, d, n, q, k, v, dout, mask, variant, scale, beta, r, mr, lr);
+            Dr = row_D_given(L, d, n, q, k, v, dout, o, mask, variant, scale, beta, r, mr, lr);
         }
         for (int c = 0; c < n; ++c) {
             if (!valid(r, c, n, mask, L)) continue;
@@ -347,9 +364,9 @@ void FN(oracle_bwd_dq_rows)(int L, int d, int seq_len, const uint16_t *q, const 
  * 0 for padded key rows.  The bias is a constant and gets no gradient.
  */
 void FN(oracle_bwd_dkv_rows)(int L, int d, int seq_len, const uint16_t *q, const uint16_t *k,
-                             const uint16_t *v, const uint16_t *dout, const uint8_t *mask,
-                             int bias_mode, int variant, real scale, int c0, int c1, real *dk,
-                             real *dv) {
+                             const uint16_t *v, const uint16_t *dout, const uint16_t *o,
+                             const uint8_t *mask, int bias_mode, int variant, real scale, int c0,
+                             int c1, real *dk, real *dv) {
     int n = clamp_len(seq_len, L);
     real beta = n > 0 ? bias_value(bias_mode, n, L) : (real)0;
     real *mr = (real *)calloc((size_t)(n > 0 ? n : 1), sizeof(real));
@@ -359,7 +376,8 @@ void FN(oracle_bwd_dkv_rows)(int L, int d, int seq_len, const uint16_t *q, const
         for (int r = 0; r < n; ++r) {
             row_stats(L, d, n, q, k, mask, variant, scale, beta, r, &mr[r], &lr[r]);
             if (lr[r] != 0)
-                Dr[r] = row_D(L, d, n, q, k, v, dout, mask, variant, scale, beta, r, mr[r], lr[r]);
+                Dr[r] = row_D_given(L, d, n, q, k, v, dout, o, mask, variant, scale, beta, r,
+                                    mr[r], lr[r]);
         }
     for (int c = c0; c < c1; ++c) {
         real *gk = dk + (size_t)(c - c0) * d;

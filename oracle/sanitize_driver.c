@@ -21,12 +21,13 @@ void oracle_fwd_tiled_f64(int L, int d, int seq_len, const uint16_t *q, const ui
                           int bk, int bias_mode, int variant, double scale, double *o,
                           double *lse);
 void oracle_bwd_dq_rows_f64(int L, int d, int seq_len, const uint16_t *q, const uint16_t *k,
-                            const uint16_t *v, const uint16_t *dout, const uint8_t *mask,
-                            int bias_mode, int variant, double scale, int r0, int r1, double *dq);
+                            const uint16_t *v, const uint16_t *dout, const uint16_t *o,
+                            const uint8_t *mask, int bias_mode, int variant, double scale, int r0,
+                            int r1, double *dq);
 void oracle_bwd_dkv_rows_f64(int L, int d, int seq_len, const uint16_t *q, const uint16_t *k,
-                             const uint16_t *v, const uint16_t *dout, const uint8_t *mask,
-                             int bias_mode, int variant, double scale, int c0, int c1, double *dk,
-                             double *dv);
+                             const uint16_t *v, const uint16_t *dout, const uint16_t *o,
+                             const uint8_t *mask, int bias_mode, int variant, double scale,
+                             int c0, int c1, double *dk, double *dv);
 void oracle_fwd_rows_f32(int L, int d, int seq_len, const uint16_t *q, const uint16_t *k,
                          const uint16_t *v, const uint8_t *mask, int bias_mode, int variant,
                          float scale, int r0, int r1, float *o, float *lse);
@@ -71,8 +72,13 @@ int main(void) {
                     oracle_fwd_rows_f64(L, d, n, q, k, v, mb, bias, variant, 0.35, 0, L, o, lse);
                     oracle_fwd_tiled_f64(L, d, n, q, k, v, mb, b < B ? bm + (size_t)b * Tq * Tk : NULL,
                                          bq, bk, bias, variant, 0.35, o, lse);
-                    oracle_bwd_dq_rows_f64(L, d, n, q, k, v, dout, mb, bias, variant, 0.35, 0, L, g1);
-                    oracle_bwd_dkv_rows_f64(L, d, n, q, k, v, dout, mb, bias, variant, 0.35, 0, L, g1, g2);
+                    for (int given = 0; given < 2; ++given) {  /* exact O, then a given O */
+                        const uint16_t *og = given ? v : NULL;
+                        oracle_bwd_dq_rows_f64(L, d, n, q, k, v, dout, og, mb, bias, variant, 0.35,
+                                               0, L, g1);
+                        oracle_bwd_dkv_rows_f64(L, d, n, q, k, v, dout, og, mb, bias, variant,
+                                                0.35, 0, L, g1, g2);
+                    }
                     oracle_fwd_rows_f32(L, d, n, q, k, v, mb, bias, variant, 0.35f, 3, 9, of, lf);
                     for (int i = 0; i < L * d; ++i) sum += isfinite(g1[i]) ? g1[i] : 0.0;
                 }

@@ -192,3 +192,46 @@ def test_rows_api_matches_full(oracle_lib):
         rq, rk, rv = oracle_lib.bwd_rows(q, k, v, do, n, 1, 0, rows, rows, variant=variant)
         assert np.array_equal(rq, dq[1, 0, rows])
         assert np.array_equal(rk, dk[1, 0, rows]) and np.array_equal(rv, dv[1, 0, rows])
+
+
+@pytest.mark.parametrize("variant", [SOFTMAX, SOFTMAX1])
+def test_given_output_shifts_only_D(oracle_lib, variant):
+    """The softmax-family backward handed a stored output o forms
+    D_r = <dO_r, o_r> from it.  Changing D by delta_r changes dS[r, c] by
+    -P[r, c] delta_r, so, against the exact output: dQ_r moves by
+    -scale delta_r sum_c P[r, c] k_c, dK_c by -scale sum_r P[r, c] delta_r q_r,
+    and dV not at all (P from the dense pure-Python reference)."""
+    from _tiny import dense_python, random_inputs, widen
+    rng = np.random.default_rng(17 + variant)
+    B, H, L, d = 2, 1, 7, 4
+    q, k, v, do = random_inputs(rng, B, H, L, d, names="qkvd")
+    n = np.array([7, 4], np.int32)
+    mask = (rng.random((B, L, L)) < 0.7).astype(np.uint8)
+    scale = 0.6
+    o_exact, _ = oracle_lib.fwd(q, k, v, n, mask=mask, bias=0, variant=variant, scale=scale)
+    o_given = bf16(o_exact + 0.05 * rng.standard_normal(o_exact.shape))  # any stored output
+    g_exact = oracle_lib.bwd(q, k, v, do, n, mask=mask, bias=0, variant=variant, scale=scale)
+    g_given = oracle_lib.bwd(q, k, v, do, n, mask=mask, bias=0, variant=variant, scale=scale,
+                             o=o_given)
+    np.testing.assert_array_equal(g_given[2], g_exact[2])  # dV
+    qf, kf, vf, dof, of = (widen(t) for t in (q, k, v, do, o_given))
+    for b in range(B):
+        _, P = dense_python(qf[b, 0], kf[b, 0], vf[b, 0], n[b], mask[b], 0, variant, scale)
+        delta = (dof[b, 0] * of[b, 0]).sum(1) - (dof[b, 0] * o_exact[b, 0]).sum(1)
+        delta[int(n[b]):] = 0.0
+        want_dq = g_exact[0][b, 0] - scale * delta[:, None] * (P @ kf[b, 0])
+        want_dk = g_exact[1][b, 0] - scale * (P * delta[:, None]).T @ qf[b, 0]
+        np.testing.assert_allclose(g_given[0][b, 0], want_dq, rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(g_given[1][b, 0], want_dk, rtol=1e-9, atol=1e-11)
+
+
+def test_given_exact_output_changes_nothing_in_sigmoid(oracle_lib):
+    """SIGMOID has no D: a given output is ignored."""
+    from _tiny import random_inputs
+    rng = np.random.default_rng(3)
+    q, k, v, do = random_inputs(rng, 1, 2, 9, 8, names="qkvd")
+    n = np.array([9], np.int32)
+    a = oracle_lib.bwd(q, k, v, do, n, variant=SIGMOID)
+    b_ = oracle_lib.bwd(q, k, v, do, n, variant=SIGMOID, o=v)
+    for x, y in zip(a, b_):
+        np.testing.assert_array_equal(x, y)

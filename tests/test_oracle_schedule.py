@@ -1,0 +1,100 @@
+"""Pins of oracle.schedule (the work schedule written out from its
+definition; Binary Block Masking, "Presentation" and "How it works"):
+a hand-worked example, the invariants every schedule must meet (each tile
+exactly once, its pair's XCD, longest sequence first, empty sequences last),
+and the kept-entry lists against a vectorised numpy reduction of the block
+mask (a different computation from the oracle's loops)."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def test_hand_worked_example():
+    # Two sequences (n = 100, 300), one head, L = 300: the longer is rank 0
+    # (pair 0 -> XCD 0: tiles 0, 1, 2 in slots 0, 8, 16), the shorter rank 1
+    # (pair 1 -> XCD 1: tile 0 in slot 1).  24 slots = 8 XCDs x 1 pair x 3 tiles.
+    bm = oracle.blockmask(np.array([100, 300], np.int32), None, 300, 128, 128)
+    s = oracle.schedule([100, 300], bm, 1, 300, 128, 128)
+    assert len(s["items1"]) == 24 and len(s["items2"]) == 48
+    assert {i: x for i, x in enumerate(s["items1"]) if x} == {
+        0: (1, 0, 0, 0, 300), 8: (1, 0, 0, 1, 300), 16: (1, 0, 0, 2, 300), 1: (0, 0, 0, 0, 100)}
+    # Two kinds: the pair's kind-0 tiles, then its kind-1 tiles.
+    assert [x for x in s["items2"][0::8] if x] == [(1, 0, k, t, 300) for k in (0, 1) for t in range(3)]
+    # Sequence 0 keeps only block (0, 0) (100 < 128); sequence 1 keeps all of
+    # its 3 x 3 blocks, full where the block lies inside [0, 256)^2.
+    assert s["qlists"][0] == [[(0, 1, 0)], [], []]
+    assert s["qlists"][1] == [[(0, 1, 1), (1, 1, 1), (2, 1, 0)]] * 2 + [[(0, 1, 0), (1, 1, 0), (2, 1, 0)]]
+    assert s["klists"] == s["qlists"]  # a symmetric block mask
+
+
+def test_lines_of_a_group_and_their_bits():
+    # block_q = 32: a 128-row group spans block rows 0..3; an entry kept by
+    # rows 1 and 3 only carries kept bits 0b1010.
+    L, n = 128, np.array([128], np.int32)
+    bm = np.zeros((1, 4, 2), np.uint8)  # block_q 32, block_k 64
+    bm[0, 1, 1] = 1
+    bm[0, 3, 1] = 3
+    bm[0, 0, 0] = 1
+    s = oracle.schedule(n, bm, 1, L, 32, 64)
+    assert s["qlists"][0] == [[(0, 0b0001, 0), (1, 0b1010, 0b1000)]]
+    # Key group 0 spans block columns 0 and 1 (C = 2), entries down the 4 rows.
+    assert s["klists"][0] == [[(0, 0b01, 0), (1, 0b10, 0), (3, 0b10, 0b10)]]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_schedule_invariants(seed):
+    rng = np.random.default_rng(seed)
+    B, H = int(rng.integers(1, 20)), int(rng.integers(1, 11))
+    L = int(rng.integers(1, 700))
+    n = rng.integers(-5, L + 5, size=B).astype(np.int32)
+    n[rng.integers(B)] = 0
+    bq, bk = (32, 64, 128)[seed % 3], (128, 32, 64)[seed % 3]
+    bm = oracle.blockmask(n, None, L, bq, bk)
+    s = oracle.schedule(n, bm, H, L, bq, bk)
+    nc = np.clip(n, 0, L)
+    G = -(-L // 128)
+    order = sorted(range(B), key=lambda b: (-nc[b], b))
+    pair_of = {(order[r], h): r * H + h for r in range(B) for h in range(H)}
+    for K, name in ((1, "items1"), (2, "items2")):
+        slots = s[name]
+        assert len(slots) == 8 * (-(-(B * H) // 8)) * G * K
+        seen = [x for x in slots if x is not None]
+        want = sorted((b, h, kind, t, int(nc[b])) for b in range(B) for h in range(H)
+                      for kind in range(K) for t in range(-(-nc[b] // 128) if nc[b] else G))
+        assert sorted(seen) == want  # every tile exactly once
+        for x in range(8):
+            mine = [it for it in slots[x::8]]
+            live = [it for it in mine if it is not None]
+            assert mine[:len(live)] == live  # no hole before the last item
+            for b, h, kind, t, nb in live:
+                assert pair_of[(b, h)] % 8 == x  # the pair's XCD
+            lens = [nb for b, h, kind, t, nb in live]
+            nonzero = [v for v in lens if v > 0]
+            assert nonzero == sorted(nonzero, reverse=True)  # longest first
+            assert lens == nonzero + [0] * (len(lens) - len(nonzero))  # empty sequences last
+
+
+@pytest.mark.parametrize("bq,bk", [(32, 128), (64, 64), (128, 32)])
+def test_lists_against_numpy_reduction(bq, bk):
+    rng = np.random.default_rng(bq + bk)
+    B, L = 3, 517
+    n = np.array([517, 300, 0], np.int32)
+    mask = (rng.random((B, L, L)) < 0.002).astype(np.uint8)
+    mask[1, 100:260, 40:300] = 1
+    bm = oracle.blockmask(n, mask, L, bq, bk)
+    s = oracle.schedule(n, bm, 2, L, bq, bk)
+    G, Tq, Tk = -(-L // 128), -(-L // bq), -(-L // bk)
+    R, C = 128 // bq, 128 // bk
+    for b in range(B):
+        for g in range(G):
+            rows = bm[b, g * R:min(g * R + R, Tq), :min(Tk, -(-int(n[b]) // bk))]  # [lines, e]
+            w = (1 << np.arange(rows.shape[0]))[:, None]
+            on, full = ((rows != 0) * w).sum(0), (((rows >> 1) & 1) * w).sum(0)
+            want = [(int(e), int(on[e]), int(full[e])) for e in np.nonzero(on)[0]]
+            assert s["qlists"][b][g] == want
+            cols = bm[b, :min(Tq, -(-int(n[b]) // bq)), g * C:min(g * C + C, Tk)].T  # [lines, e]
+            w = (1 << np.arange(cols.shape[0]))[:, None]
+            on, full = ((cols != 0) * w).sum(0), (((cols >> 1) & 1) * w).sum(0)
+            want = [(int(e), int(on[e]), int(full[e])) for e in np.nonzero(on)[0]]
+            assert s["klists"][b][g] == want
