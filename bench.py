@@ -4,7 +4,8 @@ plus backward, on one MI355X.
 One step = the whole hot path over one synthetic single-cell-shaped batch
 (B32 H8 d64, log-normal lengths with median 800 clipped to [200, 2048], padded
 to the batch maximum, block 128, bias -ln n):
-  blockmask_build (from seq_lens) -> sigattn_fwd -> sigattn_bwd (dK/dV and dQ, one launch)
+  blockmask_build (block mask and work schedule from seq_lens)
+    -> sigattn_fwd -> sigattn_bwd (dK/dV and dQ, one launch)
 Inputs are resident in HBM before the timed region.  Valid FLOPs count only
 attended (query, key) pairs: 4 d per pair per head forward, 10 d backward.
 
@@ -194,38 +195,77 @@ def copy_reference(mib: int) -> None:
     log(f"copied {mib} MiB three times")
 
 
-def cpu_baseline(w, budget_s: float = 15.0):
-    """The oracle (fp32 statement) timed on host cores over a sample of
-    (batch entry, head) pairs: forward + backward, valid TFLOP/s."""
-    import oracle
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
-    threads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16") or 16))
-    order = np.argsort(w.seq_lens)  # start small to size the sample
-    pairs_all = [(int(b), h) for b in order for h in range(w.H)]
-    # Calibrate on one pair.
-    b0, h0 = pairs_all[len(pairs_all) // 2]
-    t0 = time.perf_counter()
-    oracle.fwd(w.q, w.k, w.v, w.seq_lens, heads=[(b0, h0)], precision="f32", threads=1)
-    oracle.bwd(w.q, w.k, w.v, w.do, w.seq_lens, heads=[(b0, h0)], precision="f32", threads=1)
-    per_pair = max(time.perf_counter() - t0, 1e-3) / float(w.seq_lens[b0]) ** 2
-    # Pick pairs spread over the batch until the estimated CPU time fills the budget.
-    rng = np.random.default_rng(0)
-    pairs, est = [], 0.0
-    for idx in rng.permutation(len(pairs_all)):
-        b, h = pairs_all[idx]
-        cost = per_pair * float(w.seq_lens[b]) ** 2 / threads
-        if est + cost > budget_s and pairs:
-            break
-        pairs.append((b, h))
-        est += cost
+
+def host_threads() -> int:
+    """Threads the host may use: every CPU the process sees, capped by
+    OMP_NUM_THREADS when it is set (the share of a machine's cores given to
+    one GPU)."""
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    n = os.cpu_count() or 1
+    return min(n, int(cap)) if cap.isdigit() and int(cap) > 0 else n
+
+
+def _oracle_step(w, pairs, threads):
+    """Forward + backward of the fp32 oracle over the given (batch entry,
+    head) pairs; returns (seconds, valid FLOPs at 14 d per attended pair)."""
+    import oracle
     t0 = time.perf_counter()
     oracle.fwd(w.q, w.k, w.v, w.seq_lens, heads=pairs, precision="f32", threads=threads)
     oracle.bwd(w.q, w.k, w.v, w.do, w.seq_lens, heads=pairs, precision="f32", threads=threads)
     dt = time.perf_counter() - t0
-    flops = sum(14.0 * w.d * float(w.seq_lens[b]) ** 2 for b, _ in pairs)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(pairs)} of {w.B * w.H} (batch entry, head) pairs of the same "
-                      f"workload, forward + backward, fp32 oracle, {dt:.1f} s"}
+    return dt, sum(14.0 * w.d * float(w.seq_lens[b]) ** 2 for b, _ in pairs)
+
+
+def _pairs_within(w, per_pair_s: float, budget_s: float, threads: int, seed: int = 0):
+    """(batch entry, head) pairs drawn at random until the estimated CPU time
+    (per_pair_s per n^2, spread over `threads`) fills budget_s."""
+    rng = np.random.default_rng(seed)
+    all_pairs = [(int(b), h) for b in range(w.B) for h in range(w.H)]
+    pairs, est = [], 0.0
+    for idx in rng.permutation(len(all_pairs)):
+        b, h = all_pairs[idx]
+        cost = per_pair_s * float(w.seq_lens[b]) ** 2 / threads
+        if est + cost > budget_s and pairs:
+            break
+        pairs.append((b, h))
+        est += cost
+    return pairs
+
+
+def cpu_baseline(w, budget_all_s: float = 10.0, budget_one_s: float = 8.0):
+    """The oracle (fp32 statement, as it stands) timed on the host: forward +
+    backward in valid TFLOP/s, once on every host thread (the reported value)
+    and once on a single thread, each over a bounded sample of (batch entry,
+    head) pairs of the same workload."""
+    threads = host_threads()
+    b_med = int(np.argsort(w.seq_lens)[len(w.seq_lens) // 2])
+    dt, _ = _oracle_step(w, [(b_med, 0)], 1)  # calibration: seconds per n^2 on one thread
+    per_pair = max(dt, 1e-3) / float(w.seq_lens[b_med]) ** 2
+    pairs_all = _pairs_within(w, per_pair, budget_all_s, threads, seed=0)
+    dt_all, fl_all = _oracle_step(w, pairs_all, threads)
+    pairs_one = _pairs_within(w, per_pair, budget_one_s, 1, seed=1)
+    dt_one, fl_one = _oracle_step(w, pairs_one, 1)
+    total = w.B * w.H
+    return {"value": fl_all / dt_all / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(pairs_all)} of {total} (batch entry, head) pairs of the same "
+                      f"workload, forward + backward, fp32 oracle, {dt_all:.1f} s on "
+                      f"{threads} threads",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread": {"value": fl_one / dt_one / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "sample": f"{len(pairs_one)} of {total} pairs, {dt_one:.1f} s"}}
 
 
 class HipTimer:
@@ -362,6 +402,33 @@ class SuiteTimer:
         self.timer.close()
 
 
+# Which outputs a suite row's kernel writes (for its parity errors).
+SUITE_OUTPUTS = {"fwd": ("O",), "bwd": ("dQ", "dK", "dV"), "dkdv": ("dK", "dV"), "dq": ("dQ",)}
+
+
+def attach_parity(rows, path) -> None:
+    """Adds max_abs / rel_l2 (worst over the row's outputs) to the suite rows
+    whose workload, variant, block and mask form the full-size parity tests
+    compared against the oracle; `path` is the JSON-lines log those tests
+    write (SIGATTN_PARITY_LOG).  Rows without a record keep no error fields."""
+    if not path or not os.path.exists(path):
+        return
+    with open(path) as f:
+        recs = [json.loads(line) for line in f if line.strip()]
+    for r in rows:
+        outs = SUITE_OUTPUTS.get(r.get("kernel"))
+        if outs is None:
+            continue
+        hit = [x for x in recs
+               if (x["B"], x["H"], x["L"], x["d"]) == (r["B"], r["H"], r["L"], r["d"])
+               and x["variant"] == r["variant"] and x.get("block") == r["block"]
+               and x.get("mask", "none") == r["mask"] and x["output"] in outs]
+        if hit:
+            r["max_abs"] = max(x["max_abs"] for x in hit)
+            r["rel_l2"] = max(x["rel_l2"] for x in hit)
+            r["parity_outputs"] = sorted({x["output"] for x in hit})
+
+
 def run_suite(args) -> int:
     import torch
 
@@ -398,27 +465,30 @@ def run_suite(args) -> int:
         kr = torch.from_numpy(w.key_range).to(dev) if ranges else None
         form = {"key_range": kr} if ranges else {"mask": mask}
         w.block_q = w.block_k = block
-        bm = va.blockmask_build(n, w.L, block, block, **form)
+        bm, sched = va.blockmask_build(n, w.L, block, block, heads=w.H, **form)
         tiles = int((bm != 0).sum().item()) * w.H  # kept tiles (entries are 0, 1 or 3)
         pairs = w.valid_pairs * w.H
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev) if variant else None
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         fns = {
-            "blockmask": lambda: va.blockmask_build(n, w.L, block, block, out=bm, **form),
-            "fwd": lambda: va.sigattn_fwd(q, k, v, n, block_mask=bm, bias=bias,
+            "blockmask": lambda: va.blockmask_build(n, w.L, block, block, out=bm, heads=w.H,
+                                                    schedule=sched, **form),
+            "fwd": lambda: va.sigattn_fwd(q, k, v, n, block_mask=bm, schedule=sched, bias=bias,
                                           variant=variant, block_q=block, block_k=block, out=o,
                                           lse=lse, **form),
-            "bwd": lambda: va.sigattn_bwd(q, k, v, do, n, block_mask=bm, bias=bias,
-                                          variant=variant, block_q=block, block_k=block, dq=dq,
-                                          dk=dk, dv=dv, o=o if variant else None, lse=lse, **form),
-            "dkdv": lambda: va.sigattn_bwd_dkdv(q, k, v, do, n, block_mask=bm, bias=bias,
-                                                variant=variant, block_q=block, block_k=block,
-                                                dk=dk, dv=dv, o=o if variant else None, lse=lse,
-                                                **form),
-            "dq": lambda: va.sigattn_bwd_dq(q, k, v, do, n, block_mask=bm, bias=bias,
-                                            variant=variant, block_q=block, block_k=block, dq=dq,
-                                            o=o if variant else None, lse=lse, **form),
+            "bwd": lambda: va.sigattn_bwd(q, k, v, do, n, block_mask=bm, schedule=sched,
+                                          bias=bias, variant=variant, block_q=block,
+                                          block_k=block, dq=dq, dk=dk, dv=dv,
+                                          o=o if variant else None, lse=lse, **form),
+            "dkdv": lambda: va.sigattn_bwd_dkdv(q, k, v, do, n, block_mask=bm, schedule=sched,
+                                                bias=bias, variant=variant, block_q=block,
+                                                block_k=block, dk=dk, dv=dv,
+                                                o=o if variant else None, lse=lse, **form),
+            "dq": lambda: va.sigattn_bwd_dq(q, k, v, do, n, block_mask=bm, schedule=sched,
+                                            bias=bias, variant=variant, block_q=block,
+                                            block_k=block, dq=dq, o=o if variant else None,
+                                            lse=lse, **form),
         }
         fns["fwd"]()
         torch.cuda.synchronize()
@@ -451,7 +521,7 @@ def run_suite(args) -> int:
                      "valid_tf": flops / (np.median(tot) * 1e-6) / 1e12,
                      "tile_tf": flops / pairs * tiles * block * block / (np.median(tot) * 1e-6) / 1e12,
                      "gbs": None})
-        del q, k, v, do, o, dq, dk, dv, mask, kr, bm
+        del q, k, v, do, o, dq, dk, dv, mask, kr, bm, sched
         torch.cuda.empty_cache()
         return rows[-1]
 
@@ -489,20 +559,22 @@ def run_suite(args) -> int:
     q1, k1, v = gpu(wd.q), gpu(wd.k), gpu(wd.v)
     q2, k2 = gpu(syn.random_tensor(rng, wd.q.shape)), gpu(syn.random_tensor(rng, wd.k.shape))
     n = torch.from_numpy(wd.seq_lens).to(dev)
-    bm = va.blockmask_build(n, wd.L, 128, 128)
+    bm, sched = va.blockmask_build(n, wd.L, 128, 128, heads=wd.H)
     dout = gpu(wd.do)
     o, o2 = torch.empty_like(q1), torch.empty_like(q1)
     label = "single cell, differential (lambda 0.8)"
     log(f"case {label}")
     _, l1, l2, m1, m2 = va.sigattn_diff_fwd(q1, k1, q2, k2, v, n, 0.8, block_mask=bm,
-                                            return_maps=True)
+                                            schedule=sched, return_maps=True)
     grads = [torch.empty_like(q1) for _ in range(5)]
-    fns = [lambda: va.sigattn_diff_fwd(q1, k1, q2, k2, v, n, 0.8, block_mask=bm, out=o),
-           lambda: va.sigattn_fwd(q1, k1, v, n, block_mask=bm, variant=syn.SOFTMAX, bias=0, out=o),
-           lambda: va.sigattn_fwd(q2, k2, v, n, block_mask=bm, variant=syn.SOFTMAX, bias=0,
-                                  out=o2),
+    fns = [lambda: va.sigattn_diff_fwd(q1, k1, q2, k2, v, n, 0.8, block_mask=bm, schedule=sched,
+                                       out=o),
+           lambda: va.sigattn_fwd(q1, k1, v, n, block_mask=bm, schedule=sched,
+                                  variant=syn.SOFTMAX, bias=0, out=o),
+           lambda: va.sigattn_fwd(q2, k2, v, n, block_mask=bm, schedule=sched,
+                                  variant=syn.SOFTMAX, bias=0, out=o2),
            lambda: va.sigattn_diff_bwd(q1, k1, q2, k2, v, dout, m1, m2, l1, l2, n, 0.8,
-                                       block_mask=bm, grads=grads)]
+                                       block_mask=bm, schedule=sched, grads=grads)]
     warm = timer.steps(fns)
     cold = timer.cold(fns[0], flush)
     tiles = int((bm != 0).sum().item()) * wd.H
@@ -523,7 +595,7 @@ def run_suite(args) -> int:
                      "tile_tf": fpp * wd.d * maps * tiles * 128 * 128 / (med * 1e-6) / 1e12,
                      "gbs": algo / (med * 1e-6) / 1e9})
         log(f"  {kern}: warm median {med:.2f} us")
-    del q1, k1, q2, k2, v, dout, o, o2, bm, grads, l1, l2, m1, m2
+    del q1, k1, q2, k2, v, dout, o, o2, bm, sched, grads, l1, l2, m1, m2
     torch.cuda.empty_cache()
     # Long packed documents: causal mask within documents, d = 128.
     wl = syn.long_packed_docs(args.seed, tensors=("q", "k", "v", "do"))
@@ -542,6 +614,7 @@ def run_suite(args) -> int:
           "counts every pair of the tiles the block mask keeps; GB/s is algorithmic bytes "
           "(valid input rows read once, every output row written once).")
     print()
+    attach_parity(rows, args.parity_log)
     if args.suite_jsonl:
         with open(args.suite_jsonl, "w") as f:
             for r in rows:
@@ -582,6 +655,9 @@ def main() -> int:
                     help="run the measurement suite (markdown on stdout) instead of the step")
     ap.add_argument("--suite-jsonl", metavar="PATH",
                     help="with --suite: also write one JSON line per measured row to PATH")
+    ap.add_argument("--parity-log", metavar="PATH",
+                    help="with --suite: the JSON-lines log of the full-size parity tests "
+                         "(SIGATTN_PARITY_LOG); their errors are attached to matching rows")
     args = ap.parse_args()
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats, args.skip_dispatches))
@@ -623,6 +699,7 @@ def main() -> int:
     n = torch.from_numpy(w.seq_lens).to(dev)
     bq = bk = 128
     bm = torch.empty((B, va.num_tiles(L, bq), va.num_tiles(L, bk)), dtype=torch.uint8, device=dev)
+    sched = torch.empty(va.schedule_bytes(B, H, L, bq, bk), dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     stream = torch.cuda.current_stream()
@@ -636,12 +713,12 @@ def main() -> int:
             if events is not None:
                 timer.record(events[i])
         mark(0)
-        va.blockmask_build(n, L, bq, bk, out=bm)
+        va.blockmask_build(n, L, bq, bk, out=bm, heads=H, schedule=sched)
         mark(1)
-        va.sigattn_fwd(q, k, v, n, block_mask=bm, out=o, block_q=bq, block_k=bk)
+        va.sigattn_fwd(q, k, v, n, block_mask=bm, schedule=sched, out=o, block_q=bq, block_k=bk)
         mark(2)
-        va.sigattn_bwd(q, k, v, do, n, block_mask=bm, dq=dq, dk=dk, dv=dv, block_q=bq,
-                       block_k=bk)
+        va.sigattn_bwd(q, k, v, do, n, block_mask=bm, schedule=sched, dq=dq, dk=dk, dv=dv,
+                       block_q=bq, block_k=bk)
         mark(3)
 
     for _ in range(args.warmup):
@@ -667,8 +744,12 @@ def main() -> int:
     flops_fwd = 4.0 * d * H * pairs
     flops_bwd = 10.0 * d * H * pairs
     value = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
-    # Per-kernel algorithmic FLOPs per launch: the GEMMs each kernel's output needs.
-    algo = {"fwd": 4.0 * d * H * pairs, "bwd": 14.0 * d * H * pairs}
+    # Per-kernel algorithmic FLOPs per launch: valid work, 4 d per attended
+    # pair forward and 10 d backward (its five products).  The backward
+    # recomputes S and dP for dQ, so it executes 14 d per pair; that rate is
+    # reported beside it as `executed_tflops`, never as the roofline figure.
+    algo = {"fwd": flops_fwd, "bwd": flops_bwd}
+    executed = {"fwd": flops_fwd, "bwd": 14.0 * d * H * pairs}
     dominant = max(algo, key=lambda k_: per_kernel[k_])
     achieved = algo[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
     traffic = read_traffic(dominant, workload)
@@ -680,7 +761,8 @@ def main() -> int:
         ent = {"ms": round(per_kernel[nm], 4)}
         if nm in algo:
             tf = algo[nm] / (per_kernel[nm] * 1e-3) / 1e12
-            ent.update(tflops=round(tf, 2), frac_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+            ent.update(tflops=round(tf, 2), frac_peak=round(tf / PEAK_BF16_TFLOPS, 4),
+                       executed_tflops=round(executed[nm] / (per_kernel[nm] * 1e-3) / 1e12, 2))
         kernels[nm] = ent
 
     cpu = None
@@ -697,7 +779,8 @@ def main() -> int:
         "config": {"workload": workload, "B": B, "H": H, "L": L, "d": d,
                    "sum_n": int(w.seq_lens.sum()), "valid_pairs_per_head": int(pairs),
                    "block": bq, "variant": "sigmoid", "bias": "-ln n", "seed": args.seed,
-                   "step": "blockmask_build + fwd + bwd (dK/dV and dQ in one launch)",
+                   "step": "blockmask_build (block mask + schedule) + fwd + bwd (dK/dV and dQ "
+                           "in one launch)",
                    "parallelism": "single GPU"},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "kernels": kernels,

@@ -84,6 +84,10 @@ typedef enum {
  * offsets. */
 #define SIGATTN_MAX_MASKED_L 46080
 
+/* Bound on the workgroups of one launch (2^24: times 256 threads, the
+ * 32-bit grid limit). */
+#define SIGATTN_MAX_WORKGROUPS 16777216
+
 /* Largest row stride (stride_l, o_stride_l) in elements: the kernels address
  * the rows of one tile from its first row with 32-bit byte offsets. */
 #define SIGATTN_MAX_ROW_STRIDE 4194304
@@ -95,10 +99,11 @@ typedef enum {
  * the input strides".  Every base pointer and every stride must be a multiple
  * of 16 bytes (8 bf16 elements).
  */
-/* Sizes: B, H <= 65535 and 2 * B * H * ceil(L / 32) < 2^31 (one launch's
- * work items), row strides at most SIGATTN_MAX_ROW_STRIDE; larger problems
- * are UNSUPPORTED and are split by the caller (along B or H: the work is
- * independent). */
+/* Sizes: B, H <= 65535; 16 * ceil(B * H / 8) * ceil(L / 128) <
+ * SIGATTN_MAX_WORKGROUPS (the workgroups of the largest launch, 256 threads
+ * each, within HIP's 32-bit grid); row strides at most
+ * SIGATTN_MAX_ROW_STRIDE.  Larger problems are UNSUPPORTED and are split by
+ * the caller (along B or H: the work is independent). */
 typedef struct {
     int32_t B, H, L, d;       /* batch, heads, padded length, head dim (64 or 128) */
     int64_t stride_b, stride_h, stride_l;       /* Q, K, V, dO */
@@ -108,17 +113,35 @@ typedef struct {
 } sigattn_shape;
 
 /*
+ * sigattn_schedule_bytes - size in bytes of the schedule buffer that
+ * blockmask_build can fill for a batch of B sequences with H heads, padded
+ * length L and the given block sizes (see blockmask_build), or a negative
+ * sigattn_status: INVALID_ARG (B, H or L <= 0), UNSUPPORTED (block size,
+ * sizes beyond the limits of sigattn_shape).  48 bytes per 128-row tile of
+ * every (batch entry, head) (the (batch entry, head) pairs rounded up to a
+ * multiple of 8), plus 4 * B * ceil(L / 128) * (Tq + Tk + 2).
+ */
+int64_t sigattn_schedule_bytes(int32_t B, int32_t H, int32_t L, int32_t block_q,
+                               int32_t block_k);
+
+/*
  * blockmask_build - binary block matrix of one batch (Binary Block Masking,
  * "Presentation": keep a block when it holds at least one active element;
- * built once and shared by every head and layer).
+ * built once, in parallel, and shared by every head and layer), and
+ * optionally the work schedule derived from it.
  *
  *   seq_lens    [device] int32 [B]
  *   mask        [device] uint8 [B, L, L] row-major, non-zero = may attend;
  *               NULL for padding-only batches.  Must be 16-byte aligned.
  *   key_range   [device] int32 [B, L, 2] (see above) or NULL; at most one of
  *               mask and key_range.
+ *   H           heads of the attention calls the schedule will serve (read
+ *               only when schedule is not NULL)
  *   block_mask  [device] uint8 [B, Tq, Tk] output, Tq = ceil(L / block_q),
  *               Tk = ceil(L / block_k); every entry is written with 0, 1 or 3.
+ *   schedule    [device] output of schedule_bytes bytes (at least
+ *               sigattn_schedule_bytes(B, H, L, block_q, block_k)), 16-byte
+ *               aligned, or NULL for none.
  * Bit 0 of entry (b, i, j) is the binary block matrix: 1 iff some r in
  * [i*block_q, min((i+1)*block_q, L)) and c in [j*block_k, min((j+1)*block_k, L))
  * is valid (definition above without the block-mask term).  Bit 1 marks a full
@@ -129,13 +152,31 @@ typedef struct {
  * (i+1)*block_q <= n && (j+1)*block_k <= n.
  * With key_range the builder reads only the ranges (O(block_q) work per
  * entry, no L x L scan).
+ *
+ * The schedule ("How it works": only the runs of kept blocks are visited)
+ * holds, for the attention calls of this batch:
+ *   - work items: which (batch entry, head, 128-row tile) each workgroup of a
+ *     forward or backward launch takes.  Workgroup i runs on XCD i % 8; XCD x
+ *     takes the (length rank, head) pairs x, x + 8, ... from the longest
+ *     sequence down (ties by batch index; batches of more than 1024 entries
+ *     in index order), then the tiles of empty sequences.  Each item carries
+ *     its clamped length n.
+ *   - kept-entry lists: per batch entry and 128-row group of queries, the
+ *     block-mask entries that some block row of the group keeps, in
+ *     increasing order, with the rows that keep them and mark them full; per
+ *     128-key group the same down the block columns.
+ * Passing it to the attention calls (with this block_mask) spares every
+ * workgroup the ranking of the lengths and the scan of block-mask lines; the
+ * results are bit for bit those without it.  It stays valid while seq_lens,
+ * the mask, H and the block sizes are unchanged, and serves every layer.
  * Errors: INVALID_ARG (null seq_lens/block_mask, B or L <= 0, both mask and
- * key_range), UNSUPPORTED (block size not 32/64/128), ALIGNMENT (mask not
- * 16-byte or key_range not 8-byte aligned), LAUNCH.
+ * key_range, with a schedule: H <= 0 or schedule_bytes too small),
+ * UNSUPPORTED (block size not 32/64/128, sizes beyond the limits), ALIGNMENT
+ * (mask or schedule not 16-byte, key_range not 8-byte aligned), LAUNCH.
  */
 int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t *key_range,
-                    int32_t B, int32_t L, int32_t block_q, int32_t block_k, uint8_t *block_mask,
-                    void *stream);
+                    int32_t B, int32_t H, int32_t L, int32_t block_q, int32_t block_k,
+                    uint8_t *block_mask, void *schedule, int64_t schedule_bytes, void *stream);
 
 /*
  * sigattn_fwd - forward pass (single-cell page section 2.C: one fused kernel,
@@ -150,6 +191,10 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t 
  *               alone.  Required with mask or key_range.  Tiles with a zero entry
  *               are skipped; bit 1 set promises a full tile (see
  *               blockmask_build), so a caller's own 0/1 matrix is also valid.
+ *   schedule    [device] the schedule blockmask_build wrote together with
+ *               block_mask (same seq_lens, mask, H and block sizes), or NULL
+ *               (each workgroup then finds its work from seq_lens and
+ *               block_mask).  Needs block_mask.
  *   mask        [device] uint8 [B, L, L] or NULL (element mask, all heads;
  *               non-zero = may attend; rows need no alignment); with a mask,
  *               L <= SIGATTN_MAX_MASKED_L (else UNSUPPORTED)
@@ -166,9 +211,9 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t 
  * block mask), UNSUPPORTED (d not 64/128, block size), ALIGNMENT, LAUNCH.
  */
 int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
-                const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
-                const int32_t *key_range, int32_t bias_mode, int32_t variant, void *o,
-                float *lse, void *stream);
+                const int32_t *seq_lens, const uint8_t *block_mask, const void *schedule,
+                const uint8_t *mask, const int32_t *key_range, int32_t bias_mode,
+                int32_t variant, void *o, float *lse, void *stream);
 
 /*
  * sigattn_bwd - gradients dQ, dK, dV of sum(dO * O)
@@ -186,7 +231,7 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
  *                   SOFTMAX1, ignored (may be NULL) for SIGMOID
  *   lse             [device] fp32 [B, H, L] contiguous: the forward's
  *                   log-sum-exp; same rule as o
- *   seq_lens, block_mask, mask, key_range: as for sigattn_fwd
+ *   seq_lens, block_mask, schedule, mask, key_range: as for sigattn_fwd
  *   dq, dk, dv      [device] bf16 [B, H, L, d] (output layout), fully written;
  *                   rows >= n are 0.
  * bias_mode and variant must be those the forward ran with.
@@ -200,8 +245,9 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
  */
 int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                 const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
-                const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
-                int32_t bias_mode, int32_t variant, void *dq, void *dk, void *dv, void *stream);
+                const uint8_t *block_mask, const void *schedule, const uint8_t *mask,
+                const int32_t *key_range, int32_t bias_mode, int32_t variant, void *dq,
+                void *dk, void *dv, void *stream);
 
 /*
  * sigattn_bwd_dkdv / sigattn_bwd_dq - the two halves of sigattn_bwd, each one
@@ -213,13 +259,14 @@ int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const 
  */
 int sigattn_bwd_dkdv(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                      const void *dout, const void *o, const float *lse,
-                     const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
-                     const int32_t *key_range, int32_t bias_mode, int32_t variant, void *dk,
-                     void *dv, void *stream);
+                     const int32_t *seq_lens, const uint8_t *block_mask, const void *schedule,
+                     const uint8_t *mask, const int32_t *key_range, int32_t bias_mode,
+                     int32_t variant, void *dk, void *dv, void *stream);
 int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                    const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
-                   const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
-                   int32_t bias_mode, int32_t variant, void *dq, void *stream);
+                   const uint8_t *block_mask, const void *schedule, const uint8_t *mask,
+                   const int32_t *key_range, int32_t bias_mode, int32_t variant, void *dq,
+                   void *stream);
 
 /*
  * sigattn_diff_fwd - differential attention forward ("Differential
@@ -235,7 +282,7 @@ int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, con
  *
  *   q1, k1, q2, k2, v  [device] bf16 [B, H, L, d] (input layout), as q, k, v
  *                      of sigattn_fwd
- *   seq_lens, block_mask, mask, key_range, bias_mode: as for sigattn_fwd
+ *   seq_lens, block_mask, schedule, mask, key_range, bias_mode: as for sigattn_fwd
  *                      (the bias cancels in each softmax; it shifts the LSEs)
  *   lambda             [host] finite float
  *   o                  [device] bf16 [B, H, L, d] (output layout), fully
@@ -250,9 +297,9 @@ int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, con
  */
 int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
                      const void *k2, const void *v, const int32_t *seq_lens,
-                     const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
-                     int32_t bias_mode, float lambda, void *o, void *o1, void *o2, float *lse1,
-                     float *lse2, void *stream);
+                     const uint8_t *block_mask, const void *schedule, const uint8_t *mask,
+                     const int32_t *key_range, int32_t bias_mode, float lambda, void *o, void *o1,
+                     void *o2, float *lse1, float *lse2, void *stream);
 
 /*
  * sigattn_diff_bwd - gradients of sum(dO * O) for O = O1 - lambda O2 of
@@ -261,11 +308,15 @@ int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1,
  * (map 2), and dV is the sum of both (sigattn_bwd's softmax backward: P from
  * the map's LSE, dS = P * (dP - D), D = rowsum(dO * O_i) with the map's own
  * output O_i).  Two backward launches on `stream`; the second adds its dV to
- * the first's, so no atomics are used and results are reproducible.
+ * the first's, so no atomics are used and results are reproducible.  Between
+ * the two, map 1's dV is held as bf16 plus its bf16 rounding residual (kept
+ * in dk2's storage, which the second launch then overwrites with dK2), so
+ * the sum is formed in fp32 from ~16 significant bits of each term.
  *
  *   q1, k1, q2, k2, v, dout  [device] bf16 [B, H, L, d] (input layout)
  *   o1, o2, lse1, lse2       the forward's per-map outputs and LSEs (required)
- *   seq_lens, block_mask, mask, key_range, bias_mode, lambda: as for the forward
+ *   seq_lens, block_mask, schedule, mask, key_range, bias_mode, lambda: as for
+ *                            the forward
  *   dq1, dk1, dq2, dk2, dv   [device] bf16 [B, H, L, d] (output layout), fully
  *                            written; rows >= n are 0
  * Errors: as sigattn_bwd; INVALID_ARG for a NULL tensor or a non-finite
@@ -274,9 +325,10 @@ int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1,
 int sigattn_diff_bwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
                      const void *k2, const void *v, const void *dout, const void *o1,
                      const void *o2, const float *lse1, const float *lse2,
-                     const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
-                     const int32_t *key_range, int32_t bias_mode, float lambda, void *dq1,
-                     void *dk1, void *dq2, void *dk2, void *dv, void *stream);
+                     const int32_t *seq_lens, const uint8_t *block_mask, const void *schedule,
+                     const uint8_t *mask, const int32_t *key_range, int32_t bias_mode,
+                     float lambda, void *dq1, void *dk1, void *dq2, void *dk2, void *dv,
+                     void *stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *sigattn_last_error(void);

@@ -2,10 +2,15 @@
 compare GPU results with the oracle to the stated bounds (max abs error
 <= 1e-2 and relative L2 error <= 5e-3 on valid rows; padded rows exactly 0).
 
-The max-abs bound is stated for unit-scale outputs.  Where the oracle's
-values exceed 1 in magnitude (sigmoid without the -ln n bias sums many
-weights near 1/2), bf16 storage alone moves a value by up to 2^-9 of its
-size, so the bound is applied to the error divided by max(1, max |want|)."""
+The max-abs bound is stated for unit-scale outputs.  It is applied per output
+row r: |got[r, i] - want[r, i]| <= 1e-2 * max(1, max_j |want[r, j]|).  Every
+element of a row is a sum over the same weights, and rounding those weights
+to bf16 (2^-9 relative each) moves all of them by an amount that grows with
+the row's scale: sigmoid without the -ln n bias sums tens of weights near
+1/2, rows reach |x| ~ 10, and a CPU model of the kernel's roundings alone
+(bf16 weights, bf16 output) gives 3e-2 on an element of size 0.3 in such a
+row.  A row whose values stay within 1 gets exactly the absolute bound,
+whatever the other rows hold; for every benchmark workload |O| < 1."""
 import sys
 
 import numpy as np
@@ -39,16 +44,32 @@ def row_valid(seq_lens, B, L):
     return idx[None, :] < n[:, None]  # [B, L]
 
 
-def assert_close(got: np.ndarray, want: np.ndarray, what: str):
-    """got/want: arrays of valid rows; checks both error bounds."""
+def scaled_max_abs(got: np.ndarray, want: np.ndarray) -> float:
+    """max |got - want| / max(1, row scale): the row scale is max_j |want[r, j]|
+    over the row's elements (the last axis of a 2-D array of rows), or |want_i|
+    itself for a 1-D array.  At most MAX_ABS when every element meets its
+    bound."""
     if got.size == 0:
-        return
-    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    err = np.abs(got - want)
-    max_abs = float(err.max()) / max(1.0, float(np.abs(want).max()))
+        return 0.0
+    mag = np.abs(want)
+    if want.ndim >= 2:
+        mag = mag.max(axis=-1, keepdims=True)
+    return float((np.abs(got - want) / np.maximum(1.0, mag)).max())
+
+
+def rel_l2(got: np.ndarray, want: np.ndarray) -> float:
     denom = float(np.linalg.norm(want))
-    rel = float(np.linalg.norm(got - want) / denom) if denom > 0 else float(np.linalg.norm(got))
-    assert max_abs <= MAX_ABS, f"{what}: scaled max abs error {max_abs:.3e} > {MAX_ABS}"
+    return float(np.linalg.norm(got - want) / denom) if denom > 0 else float(np.linalg.norm(got))
+
+
+def assert_close(got: np.ndarray, want: np.ndarray, what: str):
+    """got/want: arrays of valid rows ([rows, d]); checks both error bounds
+    and returns (row-scaled max-abs figure, relative L2)."""
+    if got.size == 0:
+        return 0.0, 0.0
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    max_abs, rel = scaled_max_abs(got, want), rel_l2(got, want)
+    assert max_abs <= MAX_ABS, f"{what}: max abs error (row-scaled) {max_abs:.3e} > {MAX_ABS}"
     assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e} > {REL_L2}"
     return max_abs, rel
 
@@ -64,14 +85,28 @@ def assert_rows(got_full: np.ndarray, want_full: np.ndarray, seq_lens, what: str
     return res
 
 
-def assert_rows_abs(got_full: np.ndarray, want_full: np.ndarray, seq_lens, what: str):
-    """As assert_rows with the (scaled) max-abs bound only."""
-    B, H, L, _ = got_full.shape
-    vmask = np.broadcast_to(row_valid(seq_lens, B, L)[:, None, :], (B, H, L))
-    got, want = got_full[vmask], want_full[vmask]
-    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    if got.size:
-        max_abs = float(np.abs(got - want).max()) / max(1.0, float(np.abs(want).max()))
-        assert max_abs <= MAX_ABS, f"{what}: scaled max abs error {max_abs:.3e} > {MAX_ABS}"
-    assert np.all(got_full[~vmask] == 0), f"{what}: padded rows are not exactly zero"
-
+def decode_schedule(buf: np.ndarray, B: int, H: int, L: int, block_q: int, block_k: int) -> dict:
+    """The schedule buffer blockmask_build writes, in oracle.schedule's form.
+    Layout (include/sigattn.h): items1 then items2, 16 bytes per slot
+    {b, h, tile | kind << 30, n} (tile -1 past the last item), then per batch
+    entry and 128-row group the query lists (count, then e | kept << 24 |
+    full << 28 per entry; 1 + Tk words each) and the key lists (1 + Tq)."""
+    G = -(-L // 128)
+    Tq, Tk = -(-L // block_q), -(-L // block_k)
+    slots1 = 8 * (-(-(B * H) // 8)) * G
+    words = np.frombuffer(np.ascontiguousarray(buf).tobytes(), dtype=np.int32)
+    out = {}
+    pos = 0
+    for name, nslots in (("items1", slots1), ("items2", 2 * slots1)):
+        it = words[pos:pos + 4 * nslots].reshape(nslots, 4)
+        out[name] = [None if z < 0 else (int(b), int(h), int(z) >> 30, int(z) & 0x3fffffff, int(n))
+                     for b, h, z, n in it]
+        pos += 4 * nslots
+    for name, stride in (("qlists", 1 + Tk), ("klists", 1 + Tq)):
+        lists = words[pos:pos + B * G * stride].reshape(B, G, stride).view(np.uint32)
+        out[name] = [[[(int(w & 0xffffff), int((w >> 24) & 15), int(w >> 28))
+                       for w in lists[b, g, 1:1 + lists[b, g, 0]]] for g in range(G)]
+                     for b in range(B)]
+        pos += B * G * stride
+    assert 4 * pos <= buf.size
+    return out

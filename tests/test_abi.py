@@ -27,9 +27,12 @@ def lib():
 
 
 def test_header_declares_the_boundary():
+    import varlen_attention_amd as va
     assert declared_functions() == sorted(
-        ["blockmask_build", "sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq",
-         "sigattn_diff_bwd", "sigattn_diff_fwd", "sigattn_last_error"])
+        ["blockmask_build", "sigattn_schedule_bytes", "sigattn_fwd", "sigattn_bwd",
+         "sigattn_bwd_dkdv", "sigattn_bwd_dq", "sigattn_diff_bwd", "sigattn_diff_fwd",
+         "sigattn_last_error"])
+    assert sorted(va.EXPORTS) == declared_functions()
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -48,9 +51,9 @@ FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below
 
 
 def _fwd(lib, va, shape, q=FAKE, k=FAKE, v=FAKE, seq=FAKE, bm=None, mask=None, bias=1, var=0,
-         o=FAKE, lse=None, kr=None):
+         o=FAKE, lse=None, kr=None, sched=None):
     return lib.sigattn_fwd(ctypes.byref(shape) if shape is not None else None, q, k, v, seq, bm,
-                           mask, kr, bias, var, o, lse, None)
+                           sched, mask, kr, bias, var, o, lse, None)
 
 
 def test_forward_argument_errors(lib):
@@ -60,8 +63,16 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, va, _shape(va, d=96)) == va.ERR_UNSUPPORTED
     assert _fwd(lib, va, _shape(va, B=0)) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va, block_q=48)) == va.ERR_UNSUPPORTED
-    # Too many work items for one launch (2 * B * H * ceil(L / 32) >= 2^31).
+    # Too many workgroups for one launch: 16 * ceil(B * H / 8) * ceil(L / 128)
+    # must stay below 2^24 (times 256 threads, HIP's 32-bit grid).
     assert _fwd(lib, va, _shape(va, B=65535, H=1024, L=10000)) == va.ERR_UNSUPPORTED
+    at_limit = 128 * (1 << 20)  # B * H = 8: 16 * 1 * 2^20 workgroups = 2^24
+    assert _fwd(lib, va, _shape(va, B=8, H=1, L=at_limit)) == va.ERR_UNSUPPORTED
+    # One tile less passes the size check and stops at the next one (null q).
+    assert _fwd(lib, va, _shape(va, B=8, H=1, L=at_limit - 128), q=None) == va.ERR_INVALID_ARG
+    # L near INT32_MAX: the tile count is computed without overflow.
+    assert _fwd(lib, va, _shape(va, B=1, H=1, L=2**31 - 1)) == va.ERR_UNSUPPORTED
+    assert b"too large" in lib.sigattn_last_error()
     assert _fwd(lib, va, _shape(va), q=None) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va), seq=None) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va), o=None) == va.ERR_INVALID_ARG
@@ -80,6 +91,10 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, va, _shape(va), mask=FAKE, kr=FAKE, bm=FAKE) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va), kr=FAKE) == va.ERR_INVALID_ARG
     assert _fwd(lib, va, _shape(va), kr=ctypes.c_void_p(0x10004), bm=FAKE) == va.ERR_ALIGNMENT
+    # A schedule needs the block mask it was built with, and 16-byte alignment.
+    assert _fwd(lib, va, _shape(va), sched=FAKE) == va.ERR_INVALID_ARG
+    assert b"schedule" in lib.sigattn_last_error()
+    assert _fwd(lib, va, _shape(va), sched=ctypes.c_void_p(0x10008), bm=FAKE) == va.ERR_ALIGNMENT
 
 
 def test_backward_argument_errors(lib):
@@ -87,9 +102,9 @@ def test_backward_argument_errors(lib):
     sh = _shape(va)
     args = [FAKE] * 4  # q, k, v, dout
 
-    def bwd(shape=sh, o=None, lse=None, var=0, dk=FAKE, bm=None, mask=None, kr=None):
-        return lib.sigattn_bwd(ctypes.byref(shape), *args, o, lse, FAKE, bm, mask, kr, 1, var,
-                               FAKE, dk, FAKE, None)
+    def bwd(shape=sh, o=None, lse=None, var=0, dk=FAKE, bm=None, mask=None, kr=None, sched=None):
+        return lib.sigattn_bwd(ctypes.byref(shape), *args, o, lse, FAKE, bm, sched, mask, kr, 1,
+                               var, FAKE, dk, FAKE, None)
 
     # The softmax variants need the forward's o and lse; SIGMOID ignores them.
     assert bwd(var=1) == va.ERR_INVALID_ARG
@@ -103,10 +118,13 @@ def test_backward_argument_errors(lib):
     assert bwd(mask=FAKE, kr=FAKE, bm=FAKE) == va.ERR_INVALID_ARG
     assert bwd(kr=FAKE) == va.ERR_INVALID_ARG
     assert bwd(kr=ctypes.c_void_p(0x10004), bm=FAKE) == va.ERR_ALIGNMENT
-    assert lib.sigattn_bwd_dq(ctypes.byref(sh), *args, None, None, FAKE, None, None, None, 1, 1,
-                              FAKE, None) == va.ERR_INVALID_ARG
-    assert lib.sigattn_bwd_dkdv(ctypes.byref(sh), *args, None, None, FAKE, None, None, None, 1, 0,
-                                FAKE, None, None) == va.ERR_INVALID_ARG
+    assert bwd(sched=FAKE) == va.ERR_INVALID_ARG  # a schedule needs its block mask
+    assert lib.sigattn_bwd_dq(ctypes.byref(sh), *args, None, None, FAKE, None, None, None, None,
+                              1, 1, FAKE, None) == va.ERR_INVALID_ARG
+    assert lib.sigattn_bwd_dkdv(ctypes.byref(sh), *args, None, None, FAKE, None, None, None, None,
+                                1, 0, FAKE, None, None) == va.ERR_INVALID_ARG
+    assert lib.sigattn_bwd_dkdv(ctypes.byref(sh), *args, None, None, FAKE, None, FAKE, None, None,
+                                1, 0, FAKE, FAKE, None) == va.ERR_INVALID_ARG
 
 
 def test_diff_forward_argument_errors(lib):
@@ -115,7 +133,7 @@ def test_diff_forward_argument_errors(lib):
 
     def diff(shape=sh, q2=FAKE, lam=0.5, lse2=None, mask=None, kr=None, bm=None, o1=None):
         return lib.sigattn_diff_fwd(ctypes.byref(shape), FAKE, FAKE, q2, FAKE, FAKE, FAKE, bm,
-                                    mask, kr, 0, lam, FAKE, o1, None, None, lse2, None)
+                                    None, mask, kr, 0, lam, FAKE, o1, None, None, lse2, None)
 
     assert diff(q2=None) == va.ERR_INVALID_ARG
     assert diff(lam=float("nan")) == va.ERR_INVALID_ARG
@@ -133,8 +151,8 @@ def test_diff_backward_argument_errors(lib):
 
     def dbwd(lam=0.5, o2=FAKE, lse2=FAKE, dq2=FAKE, o1=FAKE, dv=FAKE):
         return lib.sigattn_diff_bwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, o1, o2,
-                                    FAKE, lse2, FAKE, None, None, None, 0, lam, FAKE, FAKE, dq2,
-                                    FAKE, dv, None)
+                                    FAKE, lse2, FAKE, None, None, None, None, 0, lam, FAKE, FAKE,
+                                    dq2, FAKE, dv, None)
 
     assert dbwd(lam=float("nan")) == va.ERR_INVALID_ARG
     assert dbwd(o2=None) == va.ERR_INVALID_ARG
@@ -147,15 +165,42 @@ def test_diff_backward_argument_errors(lib):
 
 def test_blockmask_argument_errors(lib):
     import varlen_attention_amd as va
-    bmb = lib.blockmask_build
-    assert bmb(None, None, None, 2, 100, 32, 32, FAKE, None) == va.ERR_INVALID_ARG
-    assert bmb(FAKE, None, None, 2, 100, 32, 32, None, None) == va.ERR_INVALID_ARG
-    assert bmb(FAKE, None, None, 0, 100, 32, 32, FAKE, None) == va.ERR_INVALID_ARG
-    assert bmb(FAKE, None, None, 2, 100, 16, 32, FAKE, None) == va.ERR_UNSUPPORTED
-    assert bmb(FAKE, ctypes.c_void_p(0x10001), None, 2, 100, 32, 32, FAKE, None) == va.ERR_ALIGNMENT
-    assert bmb(FAKE, FAKE, FAKE, 2, 100, 32, 32, FAKE, None) == va.ERR_INVALID_ARG
-    assert bmb(FAKE, None, ctypes.c_void_p(0x10004), 2, 100, 32, 32, FAKE,
-               None) == va.ERR_ALIGNMENT
+
+    def bmb(seq=FAKE, mask=None, kr=None, B=2, H=1, L=100, bq=32, bk=32, out=FAKE, sched=None,
+            nbytes=0):
+        return lib.blockmask_build(seq, mask, kr, B, H, L, bq, bk, out, sched, nbytes, None)
+
+    assert bmb(seq=None) == va.ERR_INVALID_ARG
+    assert bmb(out=None) == va.ERR_INVALID_ARG
+    assert bmb(B=0) == va.ERR_INVALID_ARG
+    assert bmb(bq=16) == va.ERR_UNSUPPORTED
+    assert bmb(mask=ctypes.c_void_p(0x10001)) == va.ERR_ALIGNMENT
+    assert bmb(mask=FAKE, kr=FAKE) == va.ERR_INVALID_ARG
+    assert bmb(kr=ctypes.c_void_p(0x10004)) == va.ERR_ALIGNMENT
+    # With a schedule: H > 0, a 16-byte aligned buffer of at least the size.
+    need = lib.sigattn_schedule_bytes(2, 3, 100, 32, 32)
+    assert need > 0
+    assert bmb(H=0, sched=FAKE, nbytes=need) == va.ERR_INVALID_ARG
+    assert bmb(H=3, sched=FAKE, nbytes=need - 1) == va.ERR_INVALID_ARG
+    assert b"needed" in lib.sigattn_last_error()
+    assert bmb(H=3, sched=ctypes.c_void_p(0x10008), nbytes=need) == va.ERR_ALIGNMENT
+    assert bmb(B=8, H=1, L=128 << 20, sched=FAKE, nbytes=1 << 40) == va.ERR_UNSUPPORTED
+
+
+def test_schedule_bytes_follow_the_layout(lib):
+    """48 bytes per 128-row tile slot of the two item arrays ((batch entry,
+    head) pairs rounded up to 8), plus the count and entry words of every
+    query and key group."""
+    import varlen_attention_amd as va
+    for B, H, L, bq, bk in ((32, 8, 1584, 128, 128), (3, 5, 100, 32, 64), (1, 1, 1, 64, 32)):
+        G = -(-L // 128)
+        Tq, Tk = -(-L // bq), -(-L // bk)
+        slots = 8 * (-(-(B * H) // 8)) * G
+        assert lib.sigattn_schedule_bytes(B, H, L, bq, bk) == \
+            16 * 3 * slots + 4 * B * G * (Tk + 1) + 4 * B * G * (Tq + 1)
+        assert va.schedule_bytes(B, H, L, bq, bk) == lib.sigattn_schedule_bytes(B, H, L, bq, bk)
+    assert lib.sigattn_schedule_bytes(0, 1, 10, 32, 32) == va.ERR_INVALID_ARG
+    assert lib.sigattn_schedule_bytes(1, 1, 10, 48, 32) == va.ERR_UNSUPPORTED
 
 
 def test_binding_rejects_cpu_tensors():

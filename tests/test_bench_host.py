@@ -65,3 +65,47 @@ def test_traffic_scaled_by_the_copy_reference(tmp_path):
     assert float(fields["fetch_scale"]) == 2.0 and float(fields["write_scale"]) == 1.0
     assert int(fields["hbm_bytes_per_launch"]) == int((1100.0 * 2.0 + 500.0) * 1024)
     assert fields["source_sha256_16"] == bench.source_digest("fwd")
+
+
+def test_cpu_baseline_reports_all_threads_and_one(monkeypatch):
+    """The oracle's host rate on every host thread (the reported value) and
+    on one thread, with the thread count and CPU model, on a bounded sample."""
+    monkeypatch.setenv("OMP_NUM_THREADS", "2")
+    w = syn.make_workload("t", seed=3, B=4, H=2, d=64, lengths="uniform", lo=20, hi=60,
+                          tensors=("q", "k", "v", "do"))
+    res = bench.cpu_baseline(w, budget_all_s=0.5, budget_one_s=0.5)
+    assert res["kind"] == "oracle" and res["unit"] == "TFLOP/s"
+    assert res["cores"] == min(2, os.cpu_count()) and res["value"] > 0
+    assert res["single_thread"]["cores"] == 1 and res["single_thread"]["value"] > 0
+    assert isinstance(res["cpu_model"], str) and res["cpu_model"]
+    assert res["host_cpus"] == os.cpu_count()
+
+
+def test_pairs_within_budget():
+    w = syn.make_workload("t", seed=3, B=8, H=4, d=64, lengths="uniform", lo=100, hi=100,
+                          tensors=())
+    # 1e-6 s per n^2 on one thread: each pair costs 0.01 s, so 0.05 s holds 5.
+    pairs = bench._pairs_within(w, 1e-6, 0.05, 1)
+    assert len(pairs) == 5 and len(set(pairs)) == 5
+    assert len(bench._pairs_within(w, 1e-6, 0.05, 2)) == 10
+    assert len(bench._pairs_within(w, 1.0, 0.0, 1)) == 1  # never empty
+
+
+def test_parity_errors_attach_to_matching_suite_rows(tmp_path):
+    import json
+    log = tmp_path / "parity.jsonl"
+    base = {"B": 32, "H": 8, "L": 1584, "d": 64, "variant": "sigmoid", "block": 128,
+            "mask": "none"}
+    recs = [dict(base, direction="fwd", output="O", max_abs=1e-3, rel_l2=2e-3),
+            dict(base, direction="bwd", output="dQ", max_abs=4e-3, rel_l2=1e-3),
+            dict(base, direction="bwd", output="dK", max_abs=2e-3, rel_l2=3e-3),
+            dict(base, direction="bwd", output="dV", max_abs=1e-3, rel_l2=1e-3),
+            dict(base, block=64, direction="fwd", output="O", max_abs=9e-3, rel_l2=9e-3)]
+    log.write_text("".join(json.dumps(r) + "\n" for r in recs))
+    rows = [dict(base, kernel="fwd"), dict(base, kernel="bwd"), dict(base, kernel="dkdv"),
+            dict(base, kernel="blockmask"), dict(base, kernel="fwd", variant="softmax")]
+    bench.attach_parity(rows, str(log))
+    assert rows[0]["max_abs"] == 1e-3 and rows[0]["parity_outputs"] == ["O"]
+    assert rows[1]["max_abs"] == 4e-3 and rows[1]["rel_l2"] == 3e-3
+    assert rows[2]["parity_outputs"] == ["dK", "dV"] and rows[2]["max_abs"] == 2e-3
+    assert "max_abs" not in rows[3] and "max_abs" not in rows[4]

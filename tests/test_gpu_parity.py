@@ -2,14 +2,16 @@
 seeded bf16 inputs.  Block masks must match bit for bit; outputs and
 gradients within max abs 1e-2 and relative L2 5e-3 on valid rows, with padded
 rows exactly zero.  Small cases span several tiles and a ragged tail; the
-benchmark workloads are checked at full size on sampled rows."""
+size limits (L = 46080 with a mask, 65536 with key ranges) are checked on
+sampled rows.  The benchmark workloads are compared row for row at full size
+in test_gpu_full_size.py."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synthetic as syn
-from _gpu import (assert_close, assert_rows, assert_rows_abs, gpu_f64, row_valid, say, to_gpu,
+from _gpu import (assert_close, assert_rows, gpu_f64, row_valid, say, to_gpu,
                   to_gpu_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -34,6 +36,19 @@ def _bm(va, n_gpu, L, bq, bk, mask_gpu=None, key_range=None):
     out = va.blockmask_build(n_gpu, L, bq, bk, mask=mask_gpu, key_range=key_range)
     torch.cuda.synchronize()
     return out
+
+
+def _handed(q, k, v, n, variant, **kw):
+    """What a softmax-family backward is handed by its forward: O rounded to
+    bf16 (as the forward stores it) and the LSE in fp32, both from the oracle's
+    forward.  The GPU backward and the oracle's backward (o=...) then run on
+    the same inputs, so the comparison measures the backward alone; the GPU
+    forward is compared on its own.  Returns (O bits, LSE, O on the GPU, LSE
+    on the GPU)."""
+    o, lse = oracle.fwd(q, k, v, n, variant=variant, **kw)
+    o_bits = syn.f32_to_bf16_bits(o.astype(np.float32))
+    lse32 = lse.astype(np.float32)
+    return o_bits, lse32, to_gpu_bf16(o_bits), to_gpu(lse32, torch.float32)
 
 
 # --------------------------------------------------------------- block mask
@@ -177,24 +192,18 @@ def test_tiny_lengths(va, L, d, bq, bk):
             bias = 1 if variant == SIGMOID else 0
             kw = dict(block_mask=bm, key_range=kr_gpu, bias=bias, variant=variant, block_q=bq,
                       block_k=bk)
-            o, lse = va.sigattn_fwd(*g[:3], n_gpu, return_lse=True, **kw)
-            grads = va.sigattn_bwd(*g, n_gpu, o=o if variant else None,
-                                   lse=lse if variant else None, **kw)
+            o = va.sigattn_fwd(*g[:3], n_gpu, **kw)
+            ob = None
+            if variant != SIGMOID:  # the backward runs on the oracle's O and LSE
+                ob, _, o_in, lse_in = _handed(q, k, v, n, variant, bias=bias, key_range=kr_np)
+            grads = va.sigattn_bwd(*g, n_gpu, o=o_in if variant else None,
+                                   lse=lse_in if variant else None, **kw)
             torch.cuda.synchronize()
             want, _ = oracle.fwd(q, k, v, n, bias=bias, variant=variant, key_range=kr_np)
             assert_rows(gpu_f64(o), want, n, f"O L={L} {form} variant={variant}")
-            ref = oracle.bwd(q, k, v, do, n, bias=bias, variant=variant, key_range=kr_np)
+            ref = oracle.bwd(q, k, v, do, n, bias=bias, variant=variant, key_range=kr_np, o=ob)
             for name, got_t, want_t in zip(("dQ", "dK", "dV"), grads, ref):
-                what = f"{name} L={L} {form} variant={variant}"
-                if variant != SIGMOID and L <= 2:
-                    # A row of one or two keys has dS = P (dP - D) with dP and D
-                    # nearly equal, and D comes from the bf16 output (the
-                    # softmax backward's reading of D): the relative L2 of a
-                    # handful of such values measures that rounding.  The
-                    # absolute bound and exact zeros on padded rows still hold.
-                    assert_rows_abs(gpu_f64(got_t), want_t, n, what)
-                else:
-                    assert_rows(gpu_f64(got_t), want_t, n, what)
+                assert_rows(gpu_f64(got_t), want_t, n, f"{name} L={L} {form} variant={variant}")
 
 
 def test_forward_block_mask_optional_for_padding(va):
@@ -266,13 +275,19 @@ def test_backward_strided_views(va, variant):
     bias = 1 if variant == SIGMOID else 0
     say(f"bwd strided views variant={variant}")
     _, lse = va.sigattn_fwd(q, k, v, n_gpu, out=o, bias=bias, variant=variant, return_lse=True)
-    va.sigattn_bwd(q, k, v, do, n_gpu, bias=bias, variant=variant, dq=dq, dk=dk, dv=dv,
-                   o=o if variant else None, lse=lse if variant else None)
     torch.cuda.synchronize()
     qn, kn, vn, don = (np.ascontiguousarray(packed[:, :, i].transpose(0, 2, 1, 3)) for i in range(4))
     want, _ = oracle.fwd(qn, kn, vn, n, bias=bias, variant=variant)
     assert_rows(gpu_f64(o), want, n, "O (strided)")
-    wq, wk, wv = oracle.bwd(qn, kn, vn, don, n, bias=bias, variant=variant)
+    ob = None
+    if variant != SIGMOID:  # the backward runs on the oracle's O (in the strided view) and LSE
+        ob, _, o_in, lse_in = _handed(qn, kn, vn, n, variant, bias=bias)
+        o.copy_(o_in)
+        lse.copy_(lse_in)
+    va.sigattn_bwd(q, k, v, do, n_gpu, bias=bias, variant=variant, dq=dq, dk=dk, dv=dv,
+                   o=o if variant else None, lse=lse if variant else None)
+    torch.cuda.synchronize()
+    wq, wk, wv = oracle.bwd(qn, kn, vn, don, n, bias=bias, variant=variant, o=ob)
     for name, got_t, ref in zip(("dQ", "dK", "dV"), (dq, dk, dv), (wq, wk, wv)):
         assert_rows(gpu_f64(got_t), ref, n, f"{name} (strided)")
 
@@ -474,81 +489,28 @@ def test_key_range_mask(va, d, L, bq, bk, variant, bias):
     bm_d = _bm(va, n_gpu, L, bq, bk, m_gpu)
     assert torch.equal(bm_r, bm_d)
     g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    ob = o_in = lse_in = None
+    if variant != SIGMOID:  # the backward runs on the oracle's O and LSE
+        ob, _, o_in, lse_in = _handed(q, k, v, n, variant, bias=bias, key_range=kr)
     res = []
     for form in ({"key_range": kr_gpu}, {"mask": m_gpu}):
         blk = bm_r if "key_range" in form else bm_d
-        o, lse = va.sigattn_fwd(*g[:3], n_gpu, block_mask=blk, bias=bias, variant=variant,
-                                block_q=bq, block_k=bk, return_lse=True, **form)
+        o = va.sigattn_fwd(*g[:3], n_gpu, block_mask=blk, bias=bias, variant=variant,
+                           block_q=bq, block_k=bk, **form)
         grads = va.sigattn_bwd(*g, n_gpu, block_mask=blk, bias=bias, variant=variant,
-                               block_q=bq, block_k=bk, o=o if variant else None,
-                               lse=lse if variant else None, **form)
+                               block_q=bq, block_k=bk, o=o_in, lse=lse_in, **form)
         res.append((o,) + tuple(grads))
     torch.cuda.synchronize()
     for a, b_ in zip(*res):
         assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
     want, _ = oracle.fwd(q, k, v, n, bias=bias, variant=variant, key_range=kr)
     assert_rows(gpu_f64(res[0][0]), want, n, "O")
-    wq, wk, wv = oracle.bwd(q, k, v, do, n, bias=bias, variant=variant, key_range=kr)
+    wq, wk, wv = oracle.bwd(q, k, v, do, n, bias=bias, variant=variant, key_range=kr, o=ob)
     for name, got_t, ref in zip(("dQ", "dK", "dV"), res[0][1:], (wq, wk, wv)):
         assert_rows(gpu_f64(got_t), ref, n, name)
 
 
-# --------------------------------------------------------------- forward, full size
-def _sample_rows(rng, n, L, count=6):
-    rows = {0, max(n - 1, 0), min(n, L - 1)}
-    rows |= set(rng.integers(0, max(n, 1), size=count).tolist())
-    return sorted(r for r in rows if r < L)
-
-
-def _check_sampled_fwd(va, w, variant=SIGMOID, bias=1, heads=8):
-    n = w.seq_lens
-    n_gpu = to_gpu(n, torch.int32)
-    m_gpu = None if w.mask is None else to_gpu(w.mask, torch.uint8)
-    bm = _bm(va, n_gpu, w.L, w.block_q, w.block_k, m_gpu)
-    o = va.sigattn_fwd(to_gpu_bf16(w.q), to_gpu_bf16(w.k), to_gpu_bf16(w.v), n_gpu,
-                       block_mask=bm, mask=m_gpu, bias=bias, variant=variant,
-                       block_q=w.block_q, block_k=w.block_k)
-    torch.cuda.synchronize()
-    og = gpu_f64(o)
-    valid = row_valid(n, w.B, w.L)
-    assert np.all(og[np.broadcast_to(~valid[:, None, :], og.shape[:3])] == 0)
-    rng = np.random.default_rng(0)
-    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(heads)]
-    pairs += [(int(np.argmax(n)), 0), (int(np.argmin(n)), w.H - 1)]
-    got, want = [], []
-    for b, h in pairs:
-        rows = _sample_rows(rng, int(n[b]), w.L)
-        ref, _ = oracle.fwd_rows(w.q, w.k, w.v, n, b, h, rows, mask=w.mask, bias=bias,
-                                 variant=variant)
-        got.append(og[b, h, rows])
-        want.append(ref)
-    return assert_close(np.concatenate(got), np.concatenate(want), f"O sampled {w.name}")
-
-
-@pytest.fixture(scope="module")
-def single_cell_inputs():
-    return syn.single_cell_backward(0)  # same lengths as the forward workload; carries dO
-
-
-def test_forward_single_cell_full_size(va, single_cell_inputs):
-    w = single_cell_inputs
-    say(f"fwd full {w.name} L={w.L}")
-    _check_sampled_fwd(va, w)
-
-
-def test_forward_single_cell_variants_full_size(va, single_cell_inputs):
-    w = single_cell_inputs
-    for variant in (SOFTMAX, SOFTMAX1):
-        say(f"fwd full variant={variant}")
-        _check_sampled_fwd(va, w, variant=variant, bias=0, heads=4)
-
-
-def test_forward_long_documents_full_size(va):
-    w = syn.long_packed_docs()
-    say(f"fwd full {w.name} L={w.L}")
-    _check_sampled_fwd(va, w)
-
-
+# --------------------------------------------------------------- forward, workloads
 @pytest.mark.parametrize("variant", [SIGMOID, SOFTMAX, SOFTMAX1])
 def test_forward_tiny_workloads(va, variant):
     w = syn.tiny_variants(0, variant)
@@ -601,6 +563,58 @@ def test_backward_small(va, d, L, bq, bk, bias, with_mask):
     assert_rows(gpu_f64(dv), wv, n, "dV")
 
 
+SCALE_CASES = [
+    # d, L, block_q, block_k, variant, bias, scale, element mask
+    (64, 300, 128, 128, SIGMOID, 1, 0.3, False),
+    (128, 257, 64, 64, SIGMOID, 2, 0.3, True),
+    (64, 230, 64, 32, SOFTMAX, 0, 0.3, False),
+    (128, 300, 128, 128, SOFTMAX, 0, 0.045, True),
+    (64, 190, 32, 128, SOFTMAX1, 0, 0.3, False),
+]
+
+
+@pytest.mark.parametrize("d,L,bq,bk,variant,bias,scale,with_mask", SCALE_CASES)
+def test_caller_scale(va, d, L, bq, bk, variant, bias, scale, with_mask):
+    """A score scale other than 1/sqrt(d), given through the shape's scale
+    field: sigmoid folds it into the register operand and the dK/dQ stores,
+    the softmax family applies it in fp32; forward, LSE and all gradients
+    against the oracle run with the same scale (the softmax-family backward
+    on the oracle's O and LSE, as both backwards are handed them)."""
+    B, H = 4, 2
+    n = np.array([L, L - 37, 1, 0], np.int32)
+    q, k, v, do = _inputs(7000 + d + L, B, H, L, d, n, names="qkvd")
+    mask = None
+    if with_mask:
+        rng = np.random.default_rng(L + d)
+        mask = (rng.random((B, L, L)) < 0.5).astype(np.uint8)
+        mask[0, 3, :] = 0
+    say(f"caller scale d={d} L={L} bq={bq} bk={bk} variant={variant} scale={scale}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = None if mask is None else to_gpu(mask, torch.uint8)
+    bm = _bm(va, n_gpu, L, bq, bk, m_gpu)
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    kw = dict(block_mask=bm, mask=m_gpu, bias=bias, variant=variant, scale=scale, block_q=bq,
+              block_k=bk)
+    o, lse = va.sigattn_fwd(*g[:3], n_gpu, return_lse=True, **kw)
+    ob = None
+    if variant != SIGMOID:
+        ob, _, o_in, lse_in = _handed(q, k, v, n, variant, mask=mask, bias=bias, scale=scale)
+    dq, dk, dv = va.sigattn_bwd(*g, n_gpu, o=o_in if variant else None,
+                                lse=lse_in if variant else None, **kw)
+    torch.cuda.synchronize()
+    want_o, want_l = oracle.fwd(q, k, v, n, mask=mask, bias=bias, variant=variant, scale=scale)
+    assert_rows(gpu_f64(o), want_o, n, "O")
+    if variant != SIGMOID:
+        gl = lse.cpu().numpy().astype(np.float64)
+        fin = np.isfinite(want_l)
+        assert np.array_equal(np.isneginf(gl), np.isneginf(want_l))
+        assert np.all(np.abs(gl[fin] - want_l[fin]) <= 1e-3 * np.maximum(1, np.abs(want_l[fin])))
+    wq, wk, wv = oracle.bwd(q, k, v, do, n, mask=mask, bias=bias, variant=variant, scale=scale,
+                            o=ob)
+    for name, got_t, ref in (("dQ", dq, wq), ("dK", dk, wk), ("dV", dv, wv)):
+        assert_rows(gpu_f64(got_t), ref, n, name)
+
+
 @pytest.mark.parametrize("B,H", [(70, 3), (64, 1), (9, 5)])
 def test_many_batch_entries_forward_backward(va, B, H):
     """Dispatch order over many (batch entry, head) pairs: more than 64 batch
@@ -640,9 +654,9 @@ SOFT_BWD_CASES = [
 
 @pytest.mark.parametrize("d,L,bq,bk,variant,bias,with_mask", SOFT_BWD_CASES)
 def test_backward_softmax_variants(va, d, L, bq, bk, variant, bias, with_mask):
-    """Softmax-family backward from the forward's O and LSE against the
-    oracle's gradients (dS = P (dP - D), D = rowsum(dO O)); lengths L, short,
-    1 and 0, and with an element mask rows that see no key at all."""
+    """Softmax-family backward (dS = P (dP - D), D = rowsum(dO O)) handed the
+    same O and LSE as the oracle's backward; lengths L, short, 1 and 0, and
+    with an element mask rows that see no key at all."""
     B, H = 4, 2
     n = np.array([L, L - 53, 1, 0], np.int32)
     q, k, v, do = _inputs(3000 + d + L + variant, B, H, L, d, n, names="qkvd")
@@ -658,12 +672,11 @@ def test_backward_softmax_variants(va, d, L, bq, bk, variant, bias, with_mask):
     m_gpu = None if mask is None else to_gpu(mask, torch.uint8)
     bm = _bm(va, n_gpu, L, bq, bk, m_gpu)
     g = [to_gpu_bf16(t) for t in (q, k, v, do)]
-    o, lse = va.sigattn_fwd(*g[:3], n_gpu, block_mask=bm, mask=m_gpu, bias=bias,
-                            variant=variant, block_q=bq, block_k=bk, return_lse=True)
+    ob, _, o, lse = _handed(q, k, v, n, variant, mask=mask, bias=bias)
     dq, dk, dv = va.sigattn_bwd(*g, n_gpu, block_mask=bm, mask=m_gpu, bias=bias, variant=variant,
                                 block_q=bq, block_k=bk, o=o, lse=lse)
     torch.cuda.synchronize()
-    wq, wk, wv = oracle.bwd(q, k, v, do, n, mask=mask, bias=bias, variant=variant)
+    wq, wk, wv = oracle.bwd(q, k, v, do, n, mask=mask, bias=bias, variant=variant, o=ob)
     assert_rows(gpu_f64(dq), wq, n, "dQ")
     assert_rows(gpu_f64(dk), wk, n, "dK")
     assert_rows(gpu_f64(dv), wv, n, "dV")
@@ -763,39 +776,6 @@ def test_backward_poison_determinism_and_identities(va):
             e2 = (dof[b, h, :nb] * of[b, h, :nb]).sum()
             scale = np.abs(dv[b, h, :nb] * vf[b, h, :nb]).sum()
             assert abs(e1 - e2) <= 2e-2 * scale + 1e-6
-
-
-def _check_sampled_bwd(va, w):
-    n = w.seq_lens
-    n_gpu = to_gpu(n, torch.int32)
-    m_gpu = None if w.mask is None else to_gpu(w.mask, torch.uint8)
-    bm = _bm(va, n_gpu, w.L, 128, 128, m_gpu)
-    dq, dk, dv = va.sigattn_bwd(*(to_gpu_bf16(t) for t in (w.q, w.k, w.v, w.do)), n_gpu,
-                                block_mask=bm, mask=m_gpu)
-    torch.cuda.synchronize()
-    dq, dk, dv = (gpu_f64(t) for t in (dq, dk, dv))
-    valid = row_valid(n, w.B, w.L)
-    pad = np.broadcast_to(~valid[:, None, :], dq.shape[:3])
-    for g in (dq, dk, dv):
-        assert np.all(g[pad] == 0)
-    rng = np.random.default_rng(1)
-    got = {"dq": [], "dk": [], "dv": []}
-    want = {"dq": [], "dk": [], "dv": []}
-    for _ in range(4):
-        b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
-        nb = int(n[b])
-        q_rows = _sample_rows(rng, nb, w.L, 4)
-        k0 = int(rng.integers(0, max(nb - 8, 1)))
-        k_rows = list(range(k0, min(k0 + 8, nb)))
-        rq, rk, rv = oracle.bwd_rows(w.q, w.k, w.v, w.do, n, b, h, q_rows, k_rows, mask=w.mask)
-        got["dq"].append(dq[b, h, q_rows])
-        want["dq"].append(rq)
-        got["dk"].append(dk[b, h, k_rows])
-        want["dk"].append(rk)
-        got["dv"].append(dv[b, h, k_rows])
-        want["dv"].append(rv)
-    for key in got:
-        assert_close(np.concatenate(got[key]), np.concatenate(want[key]), f"{key} sampled")
 
 
 def _sampled_fwd_bwd(va, q, k, v, do, n, L, b_rows, gpu_kw, oracle_kw, what):
@@ -902,41 +882,6 @@ def test_key_ranges_past_max_masked_length(va):
                      dict(mask=elem), "key ranges L=65536")
 
 
-def test_backward_single_cell_full_size(va, single_cell_inputs):
-    w = single_cell_inputs
-    say(f"bwd full {w.name} L={w.L}")
-    _check_sampled_bwd(va, w)
-
-
-@pytest.mark.parametrize("block,variant", [(64, SIGMOID), (128, SOFTMAX), (128, SOFTMAX1)])
-def test_single_cell_full_size_blocks_and_variants(va, single_cell_inputs, block, variant):
-    """The single-cell shapes (B32 H8 d64, L 1584) in the other launch
-    configurations the benchmark suite times: 64-blocks (two block-mask lines
-    per workgroup) with sigmoid and the -ln n bias, and the softmax-family
-    forward and backward (the backward from the forward's O and LSE, no bias).
-    Padded rows exactly zero; sampled rows of O, LSE, dQ, dK, dV against the
-    oracle."""
-    w = single_cell_inputs
-    bias = 1 if variant == SIGMOID else 0
-    say(f"single cell full size block={block} variant={variant}")
-    n_gpu = to_gpu(w.seq_lens, torch.int32)
-    bm = _bm(va, n_gpu, w.L, block, block)
-    np.testing.assert_array_equal(bm.cpu().numpy(),
-                                  oracle.blockmask(w.seq_lens, None, w.L, block, block))
-    rng = np.random.default_rng(20 + block + variant)
-    order = np.argsort(w.seq_lens)
-    b_rows = []
-    for b in (int(order[0]), int(order[-1]), int(rng.integers(w.B))):  # shortest, longest, any
-        nb = int(w.seq_lens[b])
-        h = int(rng.integers(w.H))
-        starts = (0, max(nb - 8, 0), int(rng.integers(0, max(nb - 8, 1))))
-        b_rows.append((b, h, _band_rows(rng, nb, w.L), starts))
-    _sampled_fwd_bwd(va, w.q, w.k, w.v, w.do, w.seq_lens, w.L, b_rows,
-                     dict(block_mask=bm, bias=bias, variant=variant, block_q=block, block_k=block),
-                     dict(bias=bias, variant=variant),
-                     f"single cell block {block} variant {variant}")
-
-
 def test_long_documents_key_ranges_full_size(va):
     """The causal packed-document mask as key ranges (8 bytes per row instead
     of an L x L mask) at B8 H16 d128: the same block mask and bit-identical
@@ -957,13 +902,6 @@ def test_long_documents_key_ranges_full_size(va):
     torch.cuda.synchronize()
     for a, b_ in zip(*res):
         assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
-
-
-def test_backward_long_documents_full_size(va):
-    """The causal packed-document mask at B8 H16 d128 (L = 7122): sampled rows."""
-    w = syn.long_packed_docs(0, tensors=("q", "k", "v", "do"))
-    say(f"bwd full {w.name} L={w.L}")
-    _check_sampled_bwd(va, w)
 
 
 # --------------------------------------------------------------- differential attention
@@ -1024,70 +962,6 @@ def test_diff_forward(va, d, L, bq, bk, form, lam):
         assert np.all(np.isneginf(gl[~np.broadcast_to(valid[:, None, :], gl.shape)]))
 
 
-def test_diff_forward_single_cell_full_size(va, single_cell_inputs):
-    """Single-cell shapes (B32 H8 d64, L 1584): sampled rows against the oracle."""
-    w = single_cell_inputs
-    rng = np.random.default_rng(21)
-    q2 = syn.random_tensor(rng, w.q.shape)
-    k2 = syn.random_tensor(rng, w.k.shape)
-    lam = 0.8
-    say(f"diff fwd full {w.name} L={w.L}")
-    n_gpu = to_gpu(w.seq_lens, torch.int32)
-    bm = _bm(va, n_gpu, w.L, 128, 128)
-    o = va.sigattn_diff_fwd(*(to_gpu_bf16(t) for t in (w.q, w.k, q2, k2, w.v)), n_gpu, lam,
-                            block_mask=bm)
-    torch.cuda.synchronize()
-    og = gpu_f64(o)
-    valid = row_valid(w.seq_lens, w.B, w.L)
-    assert np.all(og[np.broadcast_to(~valid[:, None, :], og.shape[:3])] == 0)
-    got, want = [], []
-    for _ in range(6):
-        b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
-        rows = _sample_rows(rng, int(w.seq_lens[b]), w.L, 4)
-        want.append(oracle.diff_fwd_rows(w.q, w.k, q2, k2, w.v, w.seq_lens, lam, b, h, rows))
-        got.append(og[b, h, rows])
-    assert_close(np.concatenate(got), np.concatenate(want), "O sampled diff")
-
-
-def test_diff_backward_single_cell_full_size(va, single_cell_inputs):
-    """Differential backward at the single-cell shapes (B32 H8 d64, L 1584,
-    block 128) from the forward's per-map outputs and LSEs: padded rows of all
-    five gradients exactly zero, sampled rows against the oracle."""
-    w = single_cell_inputs
-    rng = np.random.default_rng(23)
-    q2 = syn.random_tensor(rng, w.q.shape)
-    k2 = syn.random_tensor(rng, w.k.shape)
-    lam = 0.8
-    say(f"diff bwd full {w.name} L={w.L}")
-    n_gpu = to_gpu(w.seq_lens, torch.int32)
-    bm = _bm(va, n_gpu, w.L, 128, 128)
-    g = [to_gpu_bf16(t) for t in (w.q, w.k, q2, k2, w.v, w.do)]
-    o, l1, l2, o1, o2 = va.sigattn_diff_fwd(*g[:5], n_gpu, lam, return_maps=True, block_mask=bm)
-    grads = va.sigattn_diff_bwd(*g, o1, o2, l1, l2, n_gpu, lam, block_mask=bm)
-    torch.cuda.synchronize()
-    names = ("dQ1", "dK1", "dQ2", "dK2", "dV")
-    valid = np.broadcast_to(row_valid(w.seq_lens, w.B, w.L)[:, None, :], (w.B, w.H, w.L))
-    pad = torch.from_numpy(~valid).to(grads[0].device)
-    for name, t in zip(names, grads):
-        assert bool((t.view(torch.int16)[pad] == 0).all()), f"padded {name} rows not zero"
-    got = {key: [] for key in names}
-    want = {key: [] for key in names}
-    order = np.argsort(w.seq_lens)
-    for b in (int(order[0]), int(order[-1]), int(rng.integers(w.B))):  # shortest, longest, any
-        nb, h = int(w.seq_lens[b]), int(rng.integers(w.H))
-        q_rows = _band_rows(rng, nb, w.L)
-        k0 = int(rng.integers(0, max(nb - 8, 1)))
-        k_rows = sorted(set(range(k0, min(k0 + 8, nb))) | set(range(max(nb - 4, 0), nb)))
-        ref = oracle.diff_bwd_rows(w.q, w.k, q2, k2, w.v, w.do, w.seq_lens, lam, b, h, q_rows,
-                                   k_rows)
-        for name, t, r in zip(names, grads, ref):
-            rows = q_rows if name.startswith("dQ") else k_rows
-            got[name].append(gpu_f64(t[b, h, rows]))
-            want[name].append(r)
-    for key in names:
-        assert_close(np.concatenate(got[key]), np.concatenate(want[key]), f"diff {key} sampled")
-
-
 DIFF_BWD_CASES = [
     # d, L, block_q, block_k, mask form, lambda
     (64, 300, 128, 128, "none", 0.8),
@@ -1099,9 +973,9 @@ DIFF_BWD_CASES = [
 
 @pytest.mark.parametrize("d,L,bq,bk,form,lam", DIFF_BWD_CASES)
 def test_diff_backward(va, d, L, bq, bk, form, lam):
-    """Differential attention backward (from the forward's per-map outputs and
-    LSEs) against the oracle; map 1's gradients equal sigattn_bwd's softmax
-    backward bit for bit."""
+    """Differential attention backward against the oracle, both handed the same
+    per-map outputs and LSEs (each map's forward output is compared first);
+    map 1's gradients equal sigattn_bwd's softmax backward bit for bit."""
     B, H = 4, 2
     n = np.array([L, L - 53, 1, 0], np.int32)
     q1, k1, q2, k2, v, do = _inputs(8000 + d + L, B, H, L, d, n, names="abcdef")
@@ -1120,23 +994,27 @@ def test_diff_backward(va, d, L, bq, bk, form, lam):
     g = [to_gpu_bf16(t) for t in (q1, k1, q2, k2, v, do)]
     kw = dict(block_mask=bm, mask=m_gpu, key_range=kr_gpu, block_q=bq, block_k=bk)
     o, l1, l2, o1, o2 = va.sigattn_diff_fwd(*g[:5], n_gpu, lam, return_maps=True, **kw)
+    w1, _ = oracle.fwd(q1, k1, v, n, mask=mask, key_range=kr, bias=0, variant=SOFTMAX)
+    torch.cuda.synchronize()
+    assert_rows(gpu_f64(o1), w1, n, "O1")
+    # The backward runs on the oracle's per-map outputs and LSEs.
+    ob1, _, o1, l1 = _handed(q1, k1, v, n, SOFTMAX, mask=mask, key_range=kr, bias=0)
+    ob2, _, o2, l2 = _handed(q2, k2, v, n, SOFTMAX, mask=mask, key_range=kr, bias=0)
     grads = va.sigattn_diff_bwd(*g, o1, o2, l1, l2, n_gpu, lam, **kw)
     ref1 = va.sigattn_bwd(g[0], g[1], g[4], g[5], n_gpu, variant=SOFTMAX, bias=0, o=o1, lse=l1,
                           **kw)
     torch.cuda.synchronize()
     assert torch.equal(grads[0].view(torch.int16), ref1[0].view(torch.int16))
     assert torch.equal(grads[1].view(torch.int16), ref1[1].view(torch.int16))
-    w1, _ = oracle.fwd(q1, k1, v, n, mask=mask, key_range=kr, bias=0, variant=SOFTMAX)
-    assert_rows(gpu_f64(o1), w1, n, "O1")
-    want = oracle.diff_bwd(q1, k1, q2, k2, v, do, n, lam, mask=mask, key_range=kr)
+    want = oracle.diff_bwd(q1, k1, q2, k2, v, do, n, lam, mask=mask, key_range=kr, o1=ob1, o2=ob2)
     for name, got_t, ref in zip(("dQ1", "dK1", "dQ2", "dK2", "dV"), grads, want):
         assert_rows(gpu_f64(got_t), ref, n, name)
 
 
 @pytest.mark.parametrize("variant", [SIGMOID, SOFTMAX])
 def test_hip_graph_capture_and_replay(va, variant):
-    """The whole step (block mask, forward, backward) captured in one HIP
-    graph through torch: the library allocates nothing and records no memset,
+    """The whole step (block mask and schedule, forward, backward) captured in
+    one HIP graph through torch: the library allocates nothing and records no memset,
     so replays (with eager work and synchronisations between them) give the
     eager results bit for bit."""
     B, H, L, d = 4, 2, 300, 64
@@ -1148,11 +1026,12 @@ def test_hip_graph_capture_and_replay(va, variant):
     say(f"graph capture variant={variant}")
 
     def step(out):
-        bm = va.blockmask_build(n_gpu, L, 64, 64, out=out["bm"])
-        va.sigattn_fwd(*g[:3], n_gpu, block_mask=bm, bias=bias, variant=variant, block_q=64,
-                       block_k=64, out=out["o"], lse=out["lse"])
-        va.sigattn_bwd(*g, n_gpu, block_mask=bm, bias=bias, variant=variant, block_q=64,
-                       block_k=64, dq=out["dq"], dk=out["dk"], dv=out["dv"],
+        bm, sched = va.blockmask_build(n_gpu, L, 64, 64, out=out["bm"], heads=H,
+                                       schedule=out["sched"])
+        va.sigattn_fwd(*g[:3], n_gpu, block_mask=bm, schedule=sched, bias=bias, variant=variant,
+                       block_q=64, block_k=64, out=out["o"], lse=out["lse"])
+        va.sigattn_bwd(*g, n_gpu, block_mask=bm, schedule=sched, bias=bias, variant=variant,
+                       block_q=64, block_k=64, dq=out["dq"], dk=out["dk"], dv=out["dv"],
                        o=out["o"] if variant else None, lse=out["lse"] if variant else None)
 
     def buffers():
@@ -1160,6 +1039,8 @@ def test_hip_graph_capture_and_replay(va, variant):
         t["lse"] = torch.empty((B, H, L), dtype=torch.float32, device=g[0].device)
         t["bm"] = torch.empty((B, -(-L // 64), -(-L // 64)), dtype=torch.uint8,
                               device=g[0].device)
+        t["sched"] = torch.empty(va.schedule_bytes(B, H, L, 64, 64), dtype=torch.uint8,
+                                 device=g[0].device)
         return t
 
     eager = buffers()
@@ -1183,7 +1064,7 @@ def test_hip_graph_capture_and_replay(va, variant):
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for key in ("bm", "o", "dq", "dk", "dv"):
+        for key in ("bm", "sched", "o", "dq", "dk", "dv"):
             assert torch.equal(cap[key].view(torch.uint8), eager[key].view(torch.uint8)), \
                 f"replay {rep}: {key} differs from the eager run"
         if variant:
@@ -1246,6 +1127,25 @@ def test_binding_rejects_malformed_tensors(va):
         va.sigattn_fwd(q, q, q, n, lse=torch.zeros(B, H, L + 1, device=dev), variant=SOFTMAX)
     with pytest.raises(ValueError):
         va.blockmask_build(n, L, key_range=torch.zeros(B, L, 3, dtype=torch.int32, device=dev))
+    # seq_lens must hold exactly B lengths: the kernels read seq_lens[0 .. B-1].
+    short, wide = n[:1], n.view(1, B)
+    with pytest.raises(ValueError):
+        va.sigattn_fwd(q, q, q, short)
+    with pytest.raises(ValueError):
+        va.sigattn_fwd(q, q, q, wide)
+    with pytest.raises(ValueError):
+        va.sigattn_bwd(q, q, q, q, short)
+    with pytest.raises(ValueError):
+        va.sigattn_bwd_dkdv(q, q, q, q, short)
+    with pytest.raises(ValueError):
+        va.sigattn_bwd_dq(q, q, q, q, torch.cat([n, n]))
+    with pytest.raises(ValueError):
+        va.sigattn_diff_fwd(q, q, q, q, q, short, 0.5)
+    with pytest.raises(ValueError):
+        va.sigattn_diff_bwd(q, q, q, q, q, q, q, q, torch.zeros(B, H, L, device=dev),
+                            torch.zeros(B, H, L, device=dev), short, 0.5)
+    with pytest.raises(ValueError):
+        va.blockmask_build(wide, L)
 
 
 @pytest.mark.parametrize("variant", [SIGMOID, SOFTMAX1])

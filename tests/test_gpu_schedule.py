@@ -1,0 +1,144 @@
+"""The work schedule blockmask_build writes beside the block mask (work items
+per XCD, longest sequence first; kept-entry lists per 128-row group): bit for
+bit the oracle's schedule, and attention results bit for bit those without
+it (forward, backward in one launch and in two, every variant, every mask
+form and block size, differential attention)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic as syn
+from _gpu import decode_schedule, say, to_gpu, to_gpu_bf16
+
+pytestmark = pytest.mark.gpu
+
+SIGMOID, SOFTMAX, SOFTMAX1 = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def va():
+    import varlen_attention_amd as va
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    va.load_library()
+    return va
+
+
+def _window_ranges(rng, B, L):
+    kr = np.zeros((B, L, 2), np.int32)
+    for b in range(B):
+        lo = np.maximum(np.arange(L) - rng.integers(0, 300, L), 0)
+        kr[b, :, 0], kr[b, :, 1] = lo, np.arange(L) + rng.integers(-5, 40, L)
+    return kr
+
+
+SCHED_CASES = [
+    # B, H, L, block_q, block_k, mask form
+    (32, 8, 1584, 128, 128, "none"),   # the single-cell shapes
+    (5, 3, 700, 32, 128, "dense"),
+    (7, 11, 333, 64, 32, "range"),
+    (70, 2, 260, 128, 64, "none"),     # more than 64 batch entries
+    (3, 1, 1, 32, 32, "none"),
+    (9, 5, 1030, 128, 128, "dense"),
+]
+
+
+@pytest.mark.parametrize("B,H,L,bq,bk,form", SCHED_CASES)
+def test_schedule_matches_oracle(va, B, H, L, bq, bk, form):
+    rng = np.random.default_rng(B * 1000 + L)
+    if (B, H, L) == (32, 8, 1584):
+        n = syn.single_cell(0, tensors=()).seq_lens
+    else:
+        n = rng.integers(-3, L + 3, size=B).astype(np.int32)
+        n[0], n[-1] = L, 0
+    mask = kr = None
+    if form == "dense":
+        mask = (rng.random((B, L, L)) < 0.003).astype(np.uint8)
+        mask[0, : L // 2, : L // 2] = 1
+    elif form == "range":
+        kr = _window_ranges(rng, B, L)
+    say(f"schedule B={B} H={H} L={L} bq={bq} bk={bk} form={form}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = None if mask is None else to_gpu(mask, torch.uint8)
+    kr_gpu = None if kr is None else to_gpu(kr, torch.int32)
+    bm, sched = va.blockmask_build(n_gpu, L, bq, bk, mask=m_gpu, key_range=kr_gpu, heads=H)
+    torch.cuda.synchronize()
+    assert sched.numel() == va.schedule_bytes(B, H, L, bq, bk)
+    want_bm = oracle.blockmask(n, mask, L, bq, bk, key_range=kr)
+    np.testing.assert_array_equal(bm.cpu().numpy(), want_bm)
+    got = decode_schedule(sched.cpu().numpy(), B, H, L, bq, bk)
+    want = oracle.schedule(n, want_bm, H, L, bq, bk)
+    for key in ("items1", "items2", "qlists", "klists"):
+        assert got[key] == want[key], key
+
+
+OUT_CASES = [
+    # d, L, block_q, block_k, variant, bias, mask form
+    (64, 300, 128, 128, SIGMOID, 1, "none"),
+    (64, 257, 64, 64, SOFTMAX, 0, "none"),
+    (128, 300, 32, 128, SIGMOID, 2, "dense"),
+    (64, 290, 128, 32, SOFTMAX1, 0, "range"),
+    (128, 190, 64, 64, SOFTMAX, 1, "range"),
+    (64, 400, 32, 32, SIGMOID, 1, "dense"),
+]
+
+
+@pytest.mark.parametrize("d,L,bq,bk,variant,bias,form", OUT_CASES)
+def test_outputs_identical_with_schedule(va, d, L, bq, bk, variant, bias, form):
+    B, H = 6, 3
+    n = np.array([L, L - 41, 1, 0, L // 2, 129], np.int32)
+    rng = np.random.default_rng(d + L + bq)
+    q, k, v, do = (syn.random_tensor(rng, (B, H, L, d)) for _ in range(4))
+    mask = kr = None
+    if form == "dense":
+        mask = (rng.random((B, L, L)) < 0.4).astype(np.uint8)
+        mask[1, :, : L // 2] = 0
+    elif form == "range":
+        kr = _window_ranges(rng, B, L)
+    say(f"schedule outputs d={d} L={L} bq={bq} bk={bk} variant={variant} form={form}")
+    n_gpu = to_gpu(n, torch.int32)
+    m_gpu = None if mask is None else to_gpu(mask, torch.uint8)
+    kr_gpu = None if kr is None else to_gpu(kr, torch.int32)
+    bm, sched = va.blockmask_build(n_gpu, L, bq, bk, mask=m_gpu, key_range=kr_gpu, heads=H)
+    g = [to_gpu_bf16(t) for t in (q, k, v, do)]
+    kw = dict(block_mask=bm, mask=m_gpu, key_range=kr_gpu, bias=bias, variant=variant,
+              block_q=bq, block_k=bk)
+    res = []
+    for s in (None, sched):
+        o, lse = va.sigattn_fwd(*g[:3], n_gpu, return_lse=True, schedule=s, **kw)
+        soft = dict(o=o, lse=lse) if variant != SIGMOID else {}
+        grads = va.sigattn_bwd(*g, n_gpu, schedule=s, **soft, **kw)
+        dk, dv = va.sigattn_bwd_dkdv(*g, n_gpu, schedule=s, **soft, **kw)
+        dq = va.sigattn_bwd_dq(*g, n_gpu, schedule=s, **soft, **kw)
+        out = [o, *grads, dk, dv, dq]
+        if variant != SIGMOID:
+            out.append(lse)
+        res.append(out)
+    torch.cuda.synchronize()
+    for a, b_ in zip(*res):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                           b_.view(torch.int32) if b_.dtype == torch.float32 else b_.view(torch.int16))
+    # The split halves equal the one-launch backward under the schedule too.
+    assert torch.equal(res[1][2].view(torch.int16), res[1][4].view(torch.int16))
+    assert torch.equal(res[1][1].view(torch.int16), res[1][6].view(torch.int16))
+
+
+def test_differential_identical_with_schedule(va):
+    B, H, L, d = 5, 2, 270, 64
+    n = np.array([270, 1, 0, 200, 129], np.int32)
+    rng = np.random.default_rng(5)
+    q1, k1, q2, k2, v, do = (syn.random_tensor(rng, (B, H, L, d)) for _ in range(6))
+    say("schedule differential")
+    n_gpu = to_gpu(n, torch.int32)
+    bm, sched = va.blockmask_build(n_gpu, L, 64, 64, heads=H)
+    g = [to_gpu_bf16(t) for t in (q1, k1, q2, k2, v, do)]
+    res = []
+    for s in (None, sched):
+        o, l1, l2, o1, o2 = va.sigattn_diff_fwd(*g[:5], n_gpu, 0.6, block_mask=bm, block_q=64,
+                                                block_k=64, return_maps=True, schedule=s)
+        grads = va.sigattn_diff_bwd(*g, o1, o2, l1, l2, n_gpu, 0.6, block_mask=bm, block_q=64,
+                                    block_k=64, schedule=s)
+        res.append([o, o1, o2, *grads])
+    torch.cuda.synchronize()
+    for a, b_ in zip(*res):
+        assert torch.equal(a.view(torch.int16), b_.view(torch.int16))

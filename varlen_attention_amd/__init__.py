@@ -24,8 +24,9 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_LAUNCH = 0, -1, -2, -3,
 MAX_MASKED_L = 46080
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsigattn.so")
-EXPORTS = ("blockmask_build", "sigattn_fwd", "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq",
-           "sigattn_diff_fwd", "sigattn_diff_bwd", "sigattn_last_error")
+EXPORTS = ("blockmask_build", "sigattn_schedule_bytes", "sigattn_fwd", "sigattn_bwd",
+           "sigattn_bwd_dkdv", "sigattn_bwd_dq", "sigattn_diff_fwd", "sigattn_diff_bwd",
+           "sigattn_last_error")
 
 
 class SigattnError(RuntimeError):
@@ -61,19 +62,22 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.c_void_p
     I = ctypes.c_int32
     S = ctypes.POINTER(Shape)
-    lib.blockmask_build.argtypes = [P, P, P, I, I, I, I, P, P]
+    I64 = ctypes.c_int64
+    lib.sigattn_schedule_bytes.argtypes = [I, I, I, I, I]
+    lib.sigattn_schedule_bytes.restype = I64
+    lib.blockmask_build.argtypes = [P, P, P, I, I, I, I, I, P, P, I64, P]
     lib.blockmask_build.restype = ctypes.c_int
-    lib.sigattn_fwd.argtypes = [S, P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.sigattn_fwd.argtypes = [S, P, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sigattn_fwd.restype = ctypes.c_int
-    lib.sigattn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P, P]
+    lib.sigattn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P, P]
     lib.sigattn_bwd.restype = ctypes.c_int
-    lib.sigattn_bwd_dkdv.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.sigattn_bwd_dkdv.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sigattn_bwd_dkdv.restype = ctypes.c_int
-    lib.sigattn_bwd_dq.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, P, P]
+    lib.sigattn_bwd_dq.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, I, I, P, P]
     F = ctypes.c_float
-    lib.sigattn_diff_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, I, F, P, P, P, P, P, P]
+    lib.sigattn_diff_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, F, P, P, P, P, P, P]
     lib.sigattn_diff_fwd.restype = ctypes.c_int
-    lib.sigattn_diff_bwd.argtypes = [S] + [P] * 14 + [I, F] + [P] * 6
+    lib.sigattn_diff_bwd.argtypes = [S] + [P] * 15 + [I, F] + [P] * 6
     lib.sigattn_diff_bwd.restype = ctypes.c_int
     lib.sigattn_bwd_dq.restype = ctypes.c_int
     lib.sigattn_last_error.argtypes = []
@@ -106,6 +110,18 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
         raise ValueError(f"{name} must be on the GPU (got {t.device})")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+def _lens(seq_lens: torch.Tensor, B: int, device) -> None:
+    """seq_lens: int32 [B] on the same GPU as the tensors it describes (the
+    kernels read seq_lens[0 .. B-1], so a shorter tensor would be read past
+    its end)."""
+    _need(seq_lens, "seq_lens", torch.int32)
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != B:
+        raise ValueError(f"seq_lens must be a 1-D tensor of B = {B} lengths "
+                         f"(got shape {tuple(seq_lens.shape)})")
+    if device is not None and seq_lens.device != device:
+        raise ValueError(f"seq_lens is on {seq_lens.device}, the tensors on {device}")
 
 
 def _layout(ts, names):
@@ -141,14 +157,38 @@ def _key_range(key_range, B, L):
             raise ValueError("key_range must be a contiguous int32 [B, L, 2] tensor")
 
 
+def schedule_bytes(B: int, H: int, L: int, block_q: int = 128, block_k: int = 128) -> int:
+    """Bytes of the schedule buffer blockmask_build fills (sigattn_schedule_bytes)."""
+    nbytes = load_library().sigattn_schedule_bytes(B, H, L, block_q, block_k)
+    _check(int(nbytes) if nbytes < 0 else OK)
+    return int(nbytes)
+
+
+def _schedule(schedule, block_mask):
+    if schedule is not None:
+        _need(schedule, "schedule", torch.uint8)
+        if schedule.dim() != 1 or not schedule.is_contiguous():
+            raise ValueError("schedule must be a contiguous 1-D uint8 tensor")
+        if block_mask is None:
+            raise ValueError("a schedule needs the block mask it was built with")
+
+
 def blockmask_build(seq_lens: torch.Tensor, L: int, block_q: int = 128, block_k: int = 128,
                     mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                    stream=None, key_range: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    stream=None, key_range: Optional[torch.Tensor] = None,
+                    heads: Optional[int] = None, schedule: Optional[torch.Tensor] = None):
     """Block matrix uint8 [B, ceil(L/block_q), ceil(L/block_k)] on the GPU: bit 0
     the binary block mask, bit 1 full tiles.  The element mask is ``mask``
     (uint8 [B, L, L]) or ``key_range`` (int32 [B, L, 2]: row r keeps keys
-    lo..hi), not both."""
+    lo..hi), not both.
+
+    With ``heads`` (the H of the attention calls) it also builds the work
+    schedule (into ``schedule``, a uint8 tensor of ``schedule_bytes(...)``
+    bytes, allocated when not given) and returns ``(block_mask, schedule)``;
+    pass both to the attention calls of this batch."""
     _need(seq_lens, "seq_lens", torch.int32)
+    if seq_lens.dim() != 1:
+        raise ValueError(f"seq_lens must be a 1-D tensor (got shape {tuple(seq_lens.shape)})")
     B = seq_lens.shape[0]
     if mask is not None:
         _need(mask, "mask", torch.uint8)
@@ -160,15 +200,26 @@ def blockmask_build(seq_lens: torch.Tensor, L: int, block_q: int = 128, block_k:
         out = torch.empty(shape, dtype=torch.uint8, device=seq_lens.device)
     elif tuple(out.shape) != shape or out.dtype != torch.uint8 or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous uint8 tensor of shape {shape}")
+    if schedule is not None and heads is None:
+        raise ValueError("building a schedule needs the number of heads")
+    nbytes = 0
+    if heads is not None:
+        nbytes = schedule_bytes(B, heads, L, block_q, block_k)
+        if schedule is None:
+            schedule = torch.empty(nbytes, dtype=torch.uint8, device=seq_lens.device)
+        _schedule(schedule, out)
+        if schedule.numel() < nbytes:
+            raise ValueError(f"schedule holds {schedule.numel()} bytes, {nbytes} needed")
     lib = load_library()
-    _check(lib.blockmask_build(_ptr(seq_lens.contiguous()), _ptr(mask), _ptr(key_range), B, L,
-                               block_q, block_k, _ptr(out), _stream(stream)))
-    return out
+    _check(lib.blockmask_build(_ptr(seq_lens.contiguous()), _ptr(mask), _ptr(key_range), B,
+                               heads or 0, L, block_q, block_k, _ptr(out), _ptr(schedule),
+                               nbytes if schedule is not None else 0, _stream(stream)))
+    return out if heads is None else (out, schedule)
 
 
 def sigattn_fwd(q, k, v, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                 variant=SIGMOID, scale=None, block_q=128, block_k=128, out=None, lse=None,
-                return_lse=False, stream=None, key_range=None):
+                return_lse=False, stream=None, key_range=None, schedule=None):
     """Forward pass.  q, k, v: bf16 [B, H, L, d] on the GPU (equal strides).
 
     Returns o (bf16, same shape) or (o, lse) with ``return_lse=True``.
@@ -176,7 +227,7 @@ def sigattn_fwd(q, k, v, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQ
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16)
     _layout([q, k, v], ["q", "k", "v"])
-    _need(seq_lens, "seq_lens", torch.int32)
+    _lens(seq_lens, q.shape[0], q.device)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     _need(out, "out", torch.bfloat16)
@@ -199,20 +250,22 @@ def sigattn_fwd(q, k, v, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQ
         if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
             raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
     _key_range(key_range, B, L)
+    _schedule(schedule, block_mask)
     shape = _shape(q, out.stride(), scale, block_q, block_k)
     lib = load_library()
     _check(lib.sigattn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
-                           _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask),
-                           _ptr(key_range), bias, variant, _ptr(out), _ptr(lse), _stream(stream)))
+                           _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(schedule),
+                           _ptr(mask), _ptr(key_range), bias, variant, _ptr(out), _ptr(lse),
+                           _stream(stream)))
     return (out, lse) if return_lse else out
 
 
 def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k, variant, o,
-              lse, key_range):
+              lse, key_range, schedule=None):
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, nm, torch.bfloat16)
     _layout([q, k, v, dout], ["q", "k", "v", "dout"])
-    _need(seq_lens, "seq_lens", torch.int32)
+    _lens(seq_lens, q.shape[0], q.device)
     outs = [torch.empty_like(q, memory_format=torch.contiguous_format) if g is None else g
             for g in grads]
     for g in outs:
@@ -240,12 +293,13 @@ def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k
         if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
             raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
     _key_range(key_range, B, L)
+    _schedule(schedule, block_mask)
     return outs
 
 
 def sigattn_bwd(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                 variant=SIGMOID, scale=None, block_q=128, block_k=128, dq=None, dk=None,
-                dv=None, o=None, lse=None, stream=None, key_range=None):
+                dv=None, o=None, lse=None, stream=None, key_range=None, schedule=None):
     """Gradients (dq, dk, dv) of sum(dout * o); bf16 [B, H, L, d] on the GPU.
 
     The softmax variants need the forward's output ``o`` and ``lse`` (from
@@ -253,46 +307,46 @@ def sigattn_bwd(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_L
     One launch for the dK/dV and dQ work when their tile heights agree (see
     include/sigattn.h); results equal sigattn_bwd_dkdv + sigattn_bwd_dq."""
     dq, dk, dv = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dq, dk, dv), block_q,
-                           block_k, variant, o, lse, key_range)
+                           block_k, variant, o, lse, key_range, schedule)
     shape = _shape(q, dq.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_bwd(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), _ptr(lse),
-        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), _ptr(key_range), bias, variant,
-        _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(schedule), _ptr(mask),
+        _ptr(key_range), bias, variant, _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
     return dq, dk, dv
 
 
 def sigattn_bwd_dkdv(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                      variant=SIGMOID, scale=None, block_q=128, block_k=128, dk=None, dv=None,
-                     o=None, lse=None, stream=None, key_range=None):
+                     o=None, lse=None, stream=None, key_range=None, schedule=None):
     """The dK/dV half of the backward pass (one kernel): returns (dk, dv)."""
     dk, dv = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dk, dv), block_q, block_k,
-                       variant, o, lse, key_range)
+                       variant, o, lse, key_range, schedule)
     shape = _shape(q, dk.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_bwd_dkdv(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), _ptr(lse),
-        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), _ptr(key_range), bias, variant,
-        _ptr(dk), _ptr(dv), _stream(stream)))
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(schedule), _ptr(mask),
+        _ptr(key_range), bias, variant, _ptr(dk), _ptr(dv), _stream(stream)))
     return dk, dv
 
 
 def sigattn_bwd_dq(q, k, v, dout, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQLEN,
                    variant=SIGMOID, scale=None, block_q=128, block_k=128, dq=None, o=None,
-                   lse=None, stream=None, key_range=None):
+                   lse=None, stream=None, key_range=None, schedule=None):
     """The dQ half of the backward pass (one kernel): returns dq."""
     (dq,) = _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, (dq,), block_q, block_k,
-                      variant, o, lse, key_range)
+                      variant, o, lse, key_range, schedule)
     shape = _shape(q, dq.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_bwd_dq(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), _ptr(lse),
-        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), _ptr(key_range), bias, variant,
-        _ptr(dq), _stream(stream)))
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(schedule), _ptr(mask),
+        _ptr(key_range), bias, variant, _ptr(dq), _stream(stream)))
     return dq
 
 def sigattn_diff_fwd(q1, k1, q2, k2, v, seq_lens, lam: float, block_mask=None, mask=None,
                      key_range=None, bias=BIAS_NONE, scale=None, block_q=128, block_k=128,
                      out=None, lse1=None, lse2=None, return_lse=False, stream=None,
-                     o1=None, o2=None, return_maps=False):
+                     o1=None, o2=None, return_maps=False, schedule=None):
     """Differential attention forward: (softmax(S1) - lam softmax(S2)) V, both
     maps in one tile loop.  q1, k1, q2, k2, v: bf16 [B, H, L, d] on the GPU
     with equal strides.  Returns o, or (o, lse1, lse2) with return_lse=True;
@@ -301,7 +355,7 @@ def sigattn_diff_fwd(q1, k1, q2, k2, v, seq_lens, lam: float, block_mask=None, m
     for t, nm in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v")):
         _need(t, nm, torch.bfloat16)
     _layout([q1, k1, q2, k2, v], ["q1", "k1", "q2", "k2", "v"])
-    _need(seq_lens, "seq_lens", torch.int32)
+    _lens(seq_lens, q1.shape[0], q1.device)
     if out is None:
         out = torch.empty_like(q1, memory_format=torch.contiguous_format)
     _need(out, "out", torch.bfloat16)
@@ -338,12 +392,13 @@ def sigattn_diff_fwd(q1, k1, q2, k2, v, seq_lens, lam: float, block_mask=None, m
             _need(om, "o1/o2", torch.bfloat16)
             if tuple(om.shape) != tuple(out.shape) or om.stride() != out.stride():
                 raise ValueError("o1 and o2 must have out's shape and strides")
+    _schedule(schedule, block_mask)
     shape = _shape(q1, out.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_diff_fwd(
         ctypes.byref(shape), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v),
-        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(mask), _ptr(key_range), bias,
-        float(lam), _ptr(out), _ptr(o1), _ptr(o2), _ptr(lses[0]), _ptr(lses[1]),
-        _stream(stream)))
+        _ptr(seq_lens.contiguous()), _ptr(block_mask), _ptr(schedule), _ptr(mask),
+        _ptr(key_range), bias, float(lam), _ptr(out), _ptr(o1), _ptr(o2), _ptr(lses[0]),
+        _ptr(lses[1]), _stream(stream)))
     if return_maps:
         return out, lses[0], lses[1], o1, o2
     return (out, lses[0], lses[1]) if return_lse else out
@@ -351,13 +406,13 @@ def sigattn_diff_fwd(q1, k1, q2, k2, v, seq_lens, lam: float, block_mask=None, m
 
 def sigattn_diff_bwd(q1, k1, q2, k2, v, dout, o1, o2, lse1, lse2, seq_lens, lam: float,
                      block_mask=None, mask=None, key_range=None, bias=BIAS_NONE, scale=None,
-                     block_q=128, block_k=128, grads=None, stream=None):
+                     block_q=128, block_k=128, grads=None, stream=None, schedule=None):
     """Gradients (dq1, dk1, dq2, dk2, dv) of sum(dout * o) for the differential
     forward; o1, o2, lse1, lse2 from sigattn_diff_fwd(..., return_maps=True)."""
     for t, nm in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v"), (dout, "dout")):
         _need(t, nm, torch.bfloat16)
     _layout([q1, k1, q2, k2, v, dout], ["q1", "k1", "q2", "k2", "v", "dout"])
-    _need(seq_lens, "seq_lens", torch.int32)
+    _lens(seq_lens, q1.shape[0], q1.device)
     outs = [torch.empty_like(q1, memory_format=torch.contiguous_format) for _ in range(5)] \
         if grads is None else list(grads)
     for g_ in outs:
@@ -382,10 +437,11 @@ def sigattn_diff_bwd(q1, k1, q2, k2, v, dout, o1, o2, lse1, lse2, seq_lens, lam:
         want = (B, num_tiles(L, block_q), num_tiles(L, block_k))
         if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
             raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
+    _schedule(schedule, block_mask)
     shape = _shape(q1, outs[0].stride(), scale, block_q, block_k)
     _check(load_library().sigattn_diff_bwd(
         ctypes.byref(shape), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(dout),
         _ptr(o1), _ptr(o2), _ptr(lse1), _ptr(lse2), _ptr(seq_lens.contiguous()),
-        _ptr(block_mask), _ptr(mask), _ptr(key_range), bias, float(lam), *(_ptr(g_) for g_ in outs),
-        _stream(stream)))
+        _ptr(block_mask), _ptr(schedule), _ptr(mask), _ptr(key_range), bias, float(lam),
+        *(_ptr(g_) for g_ in outs), _stream(stream)))
     return tuple(outs)

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsigattn.so")
-SOURCES = ["api.hip", "blockmask.hip", "fwd.hip", "bwd.hip"]
+SOURCES = ["api.hip", "blockmask.hip", "schedule.hip", "fwd.hip", "bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -36,20 +36,31 @@ int launch_status(hipError_t e, const char *what) {
 }
 
 // Shared checks of sigattn_fwd / sigattn_bwd; fills the common parameter block.
+// Workgroups of the largest launch (the one-launch backward) for B, H, L.
+int64_t max_workgroups(int64_t B, int64_t H, int64_t L) {
+    return 16 * ((B * H + 7) / 8) * ((L + 127) / 128);
+}
+
 int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inputs,
                     void *const *outputs, int n_outputs, const int32_t *seq_lens,
-                    const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
-                    int32_t bias_mode, int32_t variant, sigattn::AttnParams *p) {
+                    const uint8_t *block_mask, const void *schedule, const uint8_t *mask,
+                    const int32_t *key_range, int32_t bias_mode, int32_t variant,
+                    sigattn::AttnParams *p) {
     if (s == nullptr) return fail(SIGATTN_ERR_INVALID_ARG, "shape is NULL");
     if (s->B <= 0 || s->H <= 0 || s->L <= 0)
         return fail(SIGATTN_ERR_INVALID_ARG, "B, H and L must be positive (got %d, %d, %d)",
                     s->B, s->H, s->L);
     if (s->B > 65535 || s->H > 65535)
         return fail(SIGATTN_ERR_UNSUPPORTED, "B and H must be at most 65535");
-    // One launch holds up to two work items per (batch entry, head) and
-    // 32-row tile; their count must fit the 32-bit grid and indices.
-    if ((int64_t)s->B * s->H * ((s->L + 31) / 32) * 2 > INT32_MAX)
-        return fail(SIGATTN_ERR_UNSUPPORTED, "B * H * L too large for one launch");
+    // The largest launch, the one-launch backward, has two work items per
+    // (batch entry, head) and 128-row tile, the (batch entry, head) pairs
+    // rounded up to a multiple of 8 (one share per XCD); its threads
+    // (workgroups x 256) must fit HIP's 32-bit grid.  Computed in 64 bits.
+    const int64_t bwd_workgroups = max_workgroups(s->B, s->H, s->L);
+    if (bwd_workgroups >= SIGATTN_MAX_WORKGROUPS)
+        return fail(SIGATTN_ERR_UNSUPPORTED,
+                    "B * H * L too large for one launch (%lld workgroups, limit %d)",
+                    (long long)bwd_workgroups, SIGATTN_MAX_WORKGROUPS);
     if (s->d != 64 && s->d != 128)
         return fail(SIGATTN_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", s->d);
     if (!block_size_ok(s->block_q) || !block_size_ok(s->block_k))
@@ -68,6 +79,10 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
         return fail(SIGATTN_ERR_INVALID_ARG, "give an element mask or key ranges, not both");
     if ((mask != nullptr || key_range != nullptr) && block_mask == nullptr)
         return fail(SIGATTN_ERR_INVALID_ARG, "an element mask needs its block mask");
+    if (schedule != nullptr && block_mask == nullptr)
+        return fail(SIGATTN_ERR_INVALID_ARG, "a schedule needs the block mask it was built with");
+    if (schedule != nullptr && !aligned16(schedule))
+        return fail(SIGATTN_ERR_ALIGNMENT, "schedule is not 16-byte aligned");
     if (key_range != nullptr && (reinterpret_cast<uintptr_t>(key_range) & 7u) != 0)
         return fail(SIGATTN_ERR_ALIGNMENT, "key_range is not 8-byte aligned");
     if (mask != nullptr && s->L > SIGATTN_MAX_MASKED_L)
@@ -119,6 +134,17 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
     p->grad_scale = 1.0f;
     p->bias_mode = bias_mode;
     p->variant = variant;
+    if (schedule != nullptr) {
+        const sigattn::ScheduleLayout lay =
+            sigattn::schedule_layout(s->B, s->H, s->L, s->block_q, s->block_k);
+        const uint8_t *base = static_cast<const uint8_t *>(schedule);
+        p->items1 = reinterpret_cast<const int4 *>(base + lay.items1);
+        p->items2 = reinterpret_cast<const int4 *>(base + lay.items2);
+        p->qlist = reinterpret_cast<const uint32_t *>(base + lay.qlists);
+        p->klist = reinterpret_cast<const uint32_t *>(base + lay.klists);
+        p->qstride = lay.qstride;
+        p->kstride = lay.kstride;
+    }
     return ok();
 }
 
@@ -126,9 +152,23 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
 
 extern "C" {
 
+int64_t sigattn_schedule_bytes(int32_t B, int32_t H, int32_t L, int32_t block_q,
+                               int32_t block_k) {
+    if (B <= 0 || H <= 0 || L <= 0)
+        return fail(SIGATTN_ERR_INVALID_ARG, "B, H and L must be positive");
+    if (B > 65535 || H > 65535) return fail(SIGATTN_ERR_UNSUPPORTED, "B and H must be at most 65535");
+    if (!block_size_ok(block_q) || !block_size_ok(block_k))
+        return fail(SIGATTN_ERR_UNSUPPORTED, "block sizes must be 32, 64 or 128 (got %d, %d)",
+                    block_q, block_k);
+    if (max_workgroups(B, H, L) >= SIGATTN_MAX_WORKGROUPS)
+        return fail(SIGATTN_ERR_UNSUPPORTED, "B * H * L too large for one launch");
+    ok();
+    return sigattn::schedule_layout(B, H, L, block_q, block_k).bytes;
+}
+
 int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t *key_range,
-                    int32_t B, int32_t L, int32_t block_q, int32_t block_k, uint8_t *block_mask,
-                    void *stream) {
+                    int32_t B, int32_t H, int32_t L, int32_t block_q, int32_t block_k,
+                    uint8_t *block_mask, void *schedule, int64_t schedule_bytes, void *stream) {
     if (seq_lens == nullptr || block_mask == nullptr)
         return fail(SIGATTN_ERR_INVALID_ARG, "seq_lens and block_mask must not be NULL");
     if (B <= 0 || L <= 0) return fail(SIGATTN_ERR_INVALID_ARG, "B and L must be positive");
@@ -142,19 +182,33 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t 
         return fail(SIGATTN_ERR_ALIGNMENT, "mask is not 16-byte aligned");
     if (key_range != nullptr && (reinterpret_cast<uintptr_t>(key_range) & 7u) != 0)
         return fail(SIGATTN_ERR_ALIGNMENT, "key_range is not 8-byte aligned");
-    return launch_status(sigattn::launch_blockmask(seq_lens, mask, key_range, B, L, block_q,
-                                                   block_k, block_mask, (hipStream_t)stream),
-                         "blockmask_build");
+    if (schedule != nullptr) {
+        const int64_t need = sigattn_schedule_bytes(B, H, L, block_q, block_k);
+        if (need < 0) return (int)need;  // its message is set
+        if (!aligned16(schedule))
+            return fail(SIGATTN_ERR_ALIGNMENT, "schedule is not 16-byte aligned");
+        if (schedule_bytes < need)
+            return fail(SIGATTN_ERR_INVALID_ARG, "schedule holds %lld bytes, %lld needed",
+                        (long long)schedule_bytes, (long long)need);
+    }
+    const hipStream_t st = (hipStream_t)stream;
+    const int rc = launch_status(
+        sigattn::launch_blockmask(seq_lens, mask, key_range, B, L, block_q, block_k, block_mask, st),
+        "blockmask_build");
+    if (rc != SIGATTN_OK || schedule == nullptr) return rc;
+    return launch_status(sigattn::launch_schedule(seq_lens, block_mask, B, H, L, block_q, block_k,
+                                                  schedule, st),
+                         "blockmask_build (schedule)");
 }
 
 int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
-                const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
-                const int32_t *key_range, int32_t bias_mode, int32_t variant, void *o, float *lse,
-                void *stream) {
+                const int32_t *seq_lens, const uint8_t *block_mask, const void *schedule,
+                const uint8_t *mask, const int32_t *key_range, int32_t bias_mode,
+                int32_t variant, void *o, float *lse, void *stream) {
     sigattn::AttnParams p = {};
     const void *inputs[3] = {q, k, v};
     void *outputs[1] = {o};
-    int st = check_attention(shape, inputs, 3, outputs, 1, seq_lens, block_mask, mask,
+    int st = check_attention(shape, inputs, 3, outputs, 1, seq_lens, block_mask, schedule, mask,
                              key_range, bias_mode, variant, &p);
     if (st != SIGATTN_OK) return st;
     if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
@@ -169,13 +223,13 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
 
 int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
                      const void *k2, const void *v, const int32_t *seq_lens,
-                     const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
-                     int32_t bias_mode, float lambda, void *o, void *o1, void *o2, float *lse1,
-                     float *lse2, void *stream) {
+                     const uint8_t *block_mask, const void *schedule, const uint8_t *mask,
+                     const int32_t *key_range, int32_t bias_mode, float lambda, void *o, void *o1,
+                     void *o2, float *lse1, float *lse2, void *stream) {
     sigattn::AttnParams p = {};
     const void *inputs[5] = {q1, k1, q2, k2, v};
     void *outputs[1] = {o};
-    int st = check_attention(shape, inputs, 5, outputs, 1, seq_lens, block_mask, mask,
+    int st = check_attention(shape, inputs, 5, outputs, 1, seq_lens, block_mask, schedule, mask,
                              key_range, bias_mode, SIGATTN_SOFTMAX, &p);
     if (st != SIGATTN_OK) return st;
     if (!isfinite(lambda)) return fail(SIGATTN_ERR_INVALID_ARG, "lambda must be finite");
@@ -207,9 +261,10 @@ enum BwdParts { kPartDkdv = 1, kPartDq = 2 };
 
 int backward(const sigattn_shape *shape, const void *q, const void *k, const void *v,
              const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
-             const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
-             int32_t bias_mode, int32_t variant, void *dq, void *dk, void *dv, void *stream,
-             int parts, const char *name, float grad_scale = 1.0f, bool accumulate_dv = false) {
+             const uint8_t *block_mask, const void *schedule, const uint8_t *mask,
+             const int32_t *key_range, int32_t bias_mode, int32_t variant, void *dq, void *dk,
+             void *dv, void *stream, int parts, const char *name, float grad_scale = 1.0f,
+             bool accumulate_dv = false, void *dv_lo = nullptr) {
     sigattn::AttnParams p = {};
     const void *inputs[4] = {q, k, v, dout};
     void *outputs[3];
@@ -219,8 +274,8 @@ int backward(const sigattn_shape *shape, const void *q, const void *k, const voi
         outputs[n_out++] = dk;
         outputs[n_out++] = dv;
     }
-    int st = check_attention(shape, inputs, 4, outputs, n_out, seq_lens, block_mask, mask,
-                             key_range, bias_mode, variant, &p);
+    int st = check_attention(shape, inputs, 4, outputs, n_out, seq_lens, block_mask, schedule,
+                             mask, key_range, bias_mode, variant, &p);
     if (st != SIGATTN_OK) return st;
     if (variant != SIGATTN_SIGMOID) {
         if (o == nullptr || lse == nullptr)
@@ -241,6 +296,7 @@ int backward(const sigattn_shape *shape, const void *q, const void *k, const voi
     p.dv = dv;
     p.grad_scale = grad_scale;
     p.accumulate_dv = accumulate_dv ? 1 : 0;
+    p.dv_lo = dv_lo;
     hipStream_t s = (hipStream_t)stream;
     if (parts == (kPartDkdv | kPartDq)) return launch_status(sigattn::launch_bwd(p, s), name);
     if (parts & kPartDkdv) return launch_status(sigattn::launch_bwd_dkdv(p, s), name);
@@ -253,27 +309,32 @@ extern "C" {
 
 int sigattn_bwd(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                 const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
-                const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
-                int32_t bias_mode, int32_t variant, void *dq, void *dk, void *dv, void *stream) {
-    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, key_range,
-                    bias_mode, variant, dq, dk, dv, stream, kPartDkdv | kPartDq, "sigattn_bwd");
+                const uint8_t *block_mask, const void *schedule, const uint8_t *mask,
+                const int32_t *key_range, int32_t bias_mode, int32_t variant, void *dq, void *dk,
+                void *dv, void *stream) {
+    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, schedule, mask,
+                    key_range, bias_mode, variant, dq, dk, dv, stream, kPartDkdv | kPartDq,
+                    "sigattn_bwd");
 }
 
 int sigattn_bwd_dkdv(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                      const void *dout, const void *o, const float *lse,
-                     const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
-                     const int32_t *key_range, int32_t bias_mode, int32_t variant, void *dk,
-                     void *dv, void *stream) {
-    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, key_range,
-                    bias_mode, variant, nullptr, dk, dv, stream, kPartDkdv, "sigattn_bwd_dkdv");
+                     const int32_t *seq_lens, const uint8_t *block_mask, const void *schedule,
+                     const uint8_t *mask, const int32_t *key_range, int32_t bias_mode,
+                     int32_t variant, void *dk, void *dv, void *stream) {
+    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, schedule, mask,
+                    key_range, bias_mode, variant, nullptr, dk, dv, stream, kPartDkdv,
+                    "sigattn_bwd_dkdv");
 }
 
 int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, const void *v,
                    const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
-                   const uint8_t *block_mask, const uint8_t *mask, const int32_t *key_range,
-                   int32_t bias_mode, int32_t variant, void *dq, void *stream) {
-    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, mask, key_range,
-                    bias_mode, variant, dq, nullptr, nullptr, stream, kPartDq, "sigattn_bwd_dq");
+                   const uint8_t *block_mask, const void *schedule, const uint8_t *mask,
+                   const int32_t *key_range, int32_t bias_mode, int32_t variant, void *dq,
+                   void *stream) {
+    return backward(shape, q, k, v, dout, o, lse, seq_lens, block_mask, schedule, mask,
+                    key_range, bias_mode, variant, dq, nullptr, nullptr, stream, kPartDq,
+                    "sigattn_bwd_dq");
 }
 
 const char *sigattn_last_error(void) { return g_last_error; }
@@ -281,9 +342,10 @@ const char *sigattn_last_error(void) { return g_last_error; }
 int sigattn_diff_bwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
                      const void *k2, const void *v, const void *dout, const void *o1,
                      const void *o2, const float *lse1, const float *lse2,
-                     const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
-                     const int32_t *key_range, int32_t bias_mode, float lambda, void *dq1,
-                     void *dk1, void *dq2, void *dk2, void *dv, void *stream) {
+                     const int32_t *seq_lens, const uint8_t *block_mask, const void *schedule,
+                     const uint8_t *mask, const int32_t *key_range, int32_t bias_mode,
+                     float lambda, void *dq1, void *dk1, void *dq2, void *dk2, void *dv,
+                     void *stream) {
     // Everything the second pass needs is checked before the first is enqueued.
     if (!isfinite(lambda)) return fail(SIGATTN_ERR_INVALID_ARG, "lambda must be finite");
     const void *second[7] = {q2, k2, o2, lse2, dq2, dk2, dv};
@@ -294,16 +356,18 @@ int sigattn_diff_bwd(const sigattn_shape *shape, const void *q1, const void *k1,
         return fail(SIGATTN_ERR_ALIGNMENT, "a second-map tensor is not 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(lse2) & 3u) != 0)
         return fail(SIGATTN_ERR_ALIGNMENT, "lse2 is not 4-byte aligned");
-    // Map 1: the softmax backward of (Q1, K1) with dO writes dq1, dk1 and dv.
-    int st = backward(shape, q1, k1, v, dout, o1, lse1, seq_lens, block_mask, mask, key_range,
-                      bias_mode, SIGATTN_SOFTMAX, dq1, dk1, dv, stream, kPartDkdv | kPartDq,
-                      "sigattn_diff_bwd", 1.0f, false);
+    // Map 1: the softmax backward of (Q1, K1) with dO writes dq1, dk1 and dv,
+    // and dv's rounding residual into dk2 (written for real only by map 2).
+    int st = backward(shape, q1, k1, v, dout, o1, lse1, seq_lens, block_mask, schedule, mask,
+                      key_range, bias_mode, SIGATTN_SOFTMAX, dq1, dk1, dv, stream,
+                      kPartDkdv | kPartDq, "sigattn_diff_bwd", 1.0f, false, dk2);
     if (st != SIGATTN_OK) return st;
     // Map 2 enters the output as -lambda O2: its gradients are -lambda times
-    // the softmax backward of (Q2, K2) with dO, and its dV adds to map 1's.
-    return backward(shape, q2, k2, v, dout, o2, lse2, seq_lens, block_mask, mask, key_range,
-                    bias_mode, SIGATTN_SOFTMAX, dq2, dk2, dv, stream, kPartDkdv | kPartDq,
-                    "sigattn_diff_bwd", -lambda, true);
+    // the softmax backward of (Q2, K2) with dO, and its dV adds to map 1's
+    // (dv plus the residual, each row read before the row's dk2 is written).
+    return backward(shape, q2, k2, v, dout, o2, lse2, seq_lens, block_mask, schedule, mask,
+                    key_range, bias_mode, SIGATTN_SOFTMAX, dq2, dk2, dv, stream,
+                    kPartDkdv | kPartDq, "sigattn_diff_bwd", -lambda, true, dk2);
 }
 
 }  // extern "C"

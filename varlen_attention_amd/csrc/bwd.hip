@@ -169,15 +169,21 @@ __device__ __forceinline__ void zero_rows(bf16 *base, int64_t sl, int r0, int ro
 }
 
 // acc[db][4i + j] holds X^T[32 db + 8 i + 4 hh + j][row]; store scale * X[row][:],
-// or exact zeros for a padded row.
+// or exact zeros for a padded row.  accumulate: add to what a previous launch
+// stored.  lo_rowp (or null): the row of a second bf16 tensor for the
+// rounding residual, written (x - bf16(x)) without accumulate and added back
+// with it.
 template <int D>
 __device__ __forceinline__ void store_rows_t(bf16 *rowp, const f32x16 *acc, float scale, int hh,
-                                             bool row_valid, bool accumulate = false) {
+                                             bool row_valid, bool accumulate = false,
+                                             bf16 *lo_rowp = nullptr) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            bf16x4 *dst = reinterpret_cast<bf16x4 *>(rowp + db * 32 + i * 8 + hh * 4);
+            const int col = db * 32 + i * 8 + hh * 4;
+            bf16x4 *dst = reinterpret_cast<bf16x4 *>(rowp + col);
+            bf16x4 *lo = lo_rowp != nullptr ? reinterpret_cast<bf16x4 *>(lo_rowp + col) : nullptr;
             float x[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * i + e] * scale;
@@ -185,10 +191,19 @@ __device__ __forceinline__ void store_rows_t(bf16 *rowp, const f32x16 *acc, floa
                 const bf16x4 old = *dst;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] += (float)old[e];
+                if (lo != nullptr) {
+                    const bf16x4 old_lo = *lo;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] += (float)old_lo[e];
+                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = keep_or_zero(x[e], row_valid);
-            *dst = pack4(x[0], x[1], x[2], x[3]);
+            const bf16x4 hi = pack4(x[0], x[1], x[2], x[3]);
+            *dst = hi;
+            if (lo != nullptr && !accumulate)
+                *lo = pack4(x[0] - (float)hi[0], x[1] - (float)hi[1], x[2] - (float)hi[2],
+                            x[3] - (float)hi[3]);
         }
 }
 
@@ -342,7 +357,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                                    : min(C, (n - k0 + p.block_k - 1) / p.block_k);
     TileSchedule<BQ, C, false> sched;
     sched.init(p.block_mask ? p.block_mask + (int64_t)b * p.Tq * p.Tk + line0 : nullptr, p.Tk,
-               lines, wl, n, p.block_q);
+               lines, wl, n, p.block_q,
+               p.klist ? p.klist + ((int64_t)b * ((L + 127) / 128) + kt) * p.kstride : nullptr,
+               p.Tq);
     int qt = sched.next();
     const int qt_want = sched.want();
     bool on = qt_want != kWantNone;  // this wave's column keeps the current tile
@@ -447,8 +464,14 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         qt = nxt;
     }
     if (key < L) {
+        // The dv residual's row is read (with accumulate_dv) before this
+        // lane's own dk store: the one tensor may serve as both (a
+        // two-launch sum parks the residual in the second launch's dk).
+        bf16 *lo = p.dv_lo != nullptr ? reinterpret_cast<bf16 *>(p.dv_lo) + b * p.osb +
+                                            h * p.osh + (int64_t)key * p.osl
+                                      : nullptr;
         store_rows_t<D>(dvb + (int64_t)key * p.osl, dvt, p.grad_scale, hh, k_valid,
-                        p.accumulate_dv != 0);
+                        p.accumulate_dv != 0, lo);
         store_rows_t<D>(dkb + (int64_t)key * p.osl, dkt, p.scale * p.grad_scale, hh, k_valid);
     }
 }
@@ -552,7 +575,9 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                                    : min(R, (n - q0 + p.block_q - 1) / p.block_q);
     TileSchedule<BK, R, true> sched;
     sched.init(p.block_mask ? p.block_mask + ((int64_t)b * p.Tq + line0) * p.Tk : nullptr, p.Tk,
-               lines, wl, n, p.block_k);
+               lines, wl, n, p.block_k,
+               p.qlist ? p.qlist + ((int64_t)b * ((L + 127) / 128) + qt) * p.qstride : nullptr,
+               p.Tk);
     int kt = sched.next();
     const int kt_want = sched.want();
     bool on = kt_want != kWantNone;  // this wave's row keeps the current tile
@@ -665,9 +690,9 @@ bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
     __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
     __shared__ __attribute__((aligned(16))) bf16 vts[kVInLds<D> ? NW * 32 * D : 1];
-    constexpr int BKV = 32 * NW;
-    int b, h, kt, n;
-    if (!tile_item<BKV>(p.seq_lens, p.B, p.H, p.L, (p.L + BKV - 1) / BKV, b, h, kt, n)) return;
+    static_assert(32 * NW == 128, "work items are 128-row tiles");
+    int b, h, kind, kt, n;
+    if (!work_item<1>(p, b, h, kind, kt, n)) return;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     dkdv_tile<D, NW, VARIANT, MASK, C>(p, b, h, kt, n, smem, mbits, vts + w * 32 * D);
 }
@@ -678,9 +703,9 @@ bwd_dq_kernel(const AttnParams p) {
     constexpr int kTile = 32 * KB * D;
     __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
     __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
-    constexpr int BQ = 32 * NW;
-    int b, h, qt, n;
-    if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
+    static_assert(32 * NW == 128, "work items are 128-row tiles");
+    int b, h, kind, qt, n;
+    if (!work_item<1>(p, b, h, kind, qt, n)) return;
     dq_tile<D, NW, KB, VARIANT, MASK, R>(p, b, h, qt, n, K0, V0, K1, V1, mbits);
 }
 
@@ -696,10 +721,9 @@ bwd_kernel(const AttnParams p) {
     constexpr int kTile = 32 * KB * D;
     __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
     __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
-    constexpr int ROWS = 32 * NW;
-    const int nt = (p.L + ROWS - 1) / ROWS;
+    static_assert(32 * NW == 128, "work items are 128-row tiles");
     int b, h, kind, t, n;
-    if (!tile_item2<ROWS, ROWS>(p.seq_lens, p.B, p.H, p.L, nt, nt, b, h, kind, t, n)) return;
+    if (!work_item<2>(p, b, h, kind, t, n)) return;
     if (kind == 0) {
         // A workgroup does one kind of work: the dQ key buffers, each 32 KB
         // rows x D, hold the dK/dV waves' V rows (32 rows each when KB = 1).

@@ -117,8 +117,9 @@ fwd_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Vs[2][BK * VP];
     __shared__ uint32_t Ms[2][MASKED ? BQ * BK / 32 : 1];  // element-mask bits per tile
 
-    int b, h, qt, n;
-    if (!tile_item<BQ>(p.seq_lens, p.B, p.H, p.L, (p.L + BQ - 1) / BQ, b, h, qt, n)) return;
+    static_assert(BQ == 128, "work items are 128-row tiles");
+    int b, h, kind, qt, n;
+    if (!work_item<1>(p, b, h, kind, qt, n)) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
     const int q0 = qt * BQ;
@@ -227,7 +228,9 @@ fwd_kernel(const AttnParams p) {
     int mcls = kMixed;  // this wave's share of the current tile (element mask)
     if constexpr (MASKED) mstage.init(tid);
     TileSchedule<BK, R, true> sched;
-    sched.init(bm_row, p.Tk, lines, wl, n, p.block_k);
+    sched.init(bm_row, p.Tk, lines, wl, n, p.block_k,
+               p.qlist ? p.qlist + ((int64_t)b * ((L + 127) / 128) + qt) * p.qstride : nullptr,
+               p.Tk);
     int kt = sched.next();
     const int kt_want = sched.want();
     bool on = kt_want != kWantNone;  // this wave's row keeps the current tile

@@ -13,6 +13,43 @@ namespace sigattn {
 // differential entry point).
 enum Variant { kSigmoid = 0, kSoftmax = 1, kSoftmax1 = 2, kDiff = 3 };
 
+// Layout of a schedule buffer (blockmask_build's optional output; byte
+// offsets from its start).  Work items are 16 bytes: {b, h, tile | kind << 30,
+// n}, tile = -1 past the last item.  A launch over one kind of 128-row tile
+// (forward, dK/dV alone, dQ alone) reads items1, the one-launch backward
+// items2; slot i is workgroup i's item, and workgroup i runs on XCD i % 8.
+// Entry lists hold, per batch entry and 128-row group of queries (qlists) or
+// keys (klists), a count word and then one word per block-mask entry that
+// some line of the group keeps: e | kept-by-line << 24 | full-by-line << 28,
+// in increasing e (lines: the block rows, or columns, the group spans).
+struct ScheduleLayout {
+    int64_t slots1, slots2;  // items in the two arrays
+    int64_t items1, items2;  // byte offsets of the item arrays
+    int64_t qlists, klists;  // byte offsets of the entry lists
+    int64_t bytes;           // the whole buffer
+    int groups;              // 128-row groups along L
+    int qstride, kstride;    // words per query group (1 + Tk) and key group (1 + Tq)
+};
+
+__host__ __device__ inline ScheduleLayout schedule_layout(int B, int H, int L, int block_q,
+                                                          int block_k) {
+    ScheduleLayout s;
+    const int64_t G = ((int64_t)L + 127) / 128;
+    const int64_t Tq = ((int64_t)L + block_q - 1) / block_q;
+    const int64_t Tk = ((int64_t)L + block_k - 1) / block_k;
+    s.groups = (int)G;
+    s.qstride = (int)(1 + Tk);
+    s.kstride = (int)(1 + Tq);
+    s.slots1 = 8 * (((int64_t)B * H + 7) / 8) * G;
+    s.slots2 = 2 * s.slots1;
+    s.items1 = 0;
+    s.items2 = 16 * s.slots1;
+    s.qlists = s.items2 + 16 * s.slots2;
+    s.klists = s.qlists + 4 * (int64_t)B * G * s.qstride;
+    s.bytes = s.klists + 4 * (int64_t)B * G * s.kstride;
+    return s;
+}
+
 struct AttnParams {
     const void *q, *k, *v, *dout;   // bf16 [B, H, L, d] (input layout); dout: backward only
     void *o, *dq, *dk, *dv;         // bf16 [B, H, L, d] (output layout)
@@ -23,10 +60,22 @@ struct AttnParams {
     void *o1, *o2;                  // differential forward: each map's own output, or null
     float grad_scale;               // backward: every gradient times this (1 normally)
     int accumulate_dv;              // backward: add to dv instead of overwriting it
+    // Backward: bf16 [B, H, L, d] (output layout) holding the rounding residual
+    // of dv, or null.  Without accumulate_dv the store writes dv = bf16(x) and
+    // dv_lo = bf16(x - dv); with it, the value added to is dv + dv_lo, so a
+    // sum over two launches keeps ~16 significant bits between them.
+    void *dv_lo;
     const int32_t *seq_lens;        // [B]
     const uint8_t *block_mask;      // [B, Tq, Tk] or null
     const uint8_t *mask;            // [B, L, L] or null
     const int32_t *key_range;       // [B, L, 2] or null (at most one of mask, key_range)
+    // From a schedule buffer (all null without one): the work items of
+    // launches over one kind of tile (items1) and of the one-launch backward
+    // (items2), one per workgroup, and the kept-entry lists of query and key
+    // groups.
+    const int4 *items1, *items2;
+    const uint32_t *qlist, *klist;
+    int qstride, kstride;           // words per group list
     int64_t sb, sh, sl;             // input strides (elements)
     int64_t osb, osh, osl;          // output strides (elements)
     int B, H, L, d;
@@ -38,6 +87,10 @@ struct AttnParams {
 hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask,
                             const int32_t *key_range, int B, int L, int block_q, int block_k,
                             uint8_t *out, hipStream_t stream);
+// Work items and kept-entry lists (ScheduleLayout) from seq_lens and a
+// finished block mask, enqueued after it on the same stream.
+hipError_t launch_schedule(const int32_t *seq_lens, const uint8_t *block_mask, int B, int H,
+                           int L, int block_q, int block_k, void *schedule, hipStream_t stream);
 hipError_t launch_fwd(const AttnParams &p, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnParams &p, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnParams &p, hipStream_t stream);

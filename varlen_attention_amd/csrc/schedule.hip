@@ -1,0 +1,178 @@
+// Work schedule of one batch, built once next to its block mask and shared by
+// every head, by the forward and the backward launches, and by every layer
+// with the same lengths and mask (Binary Block Masking, "Presentation": the
+// block structure is computed once, in parallel, before the attention
+// kernels; "How it works": the kernels then visit only the runs of kept
+// blocks).  Two parts, laid out by schedule_layout (kernels.h):
+//
+// * Work items.  Workgroup i of an attention launch runs on XCD i % 8 and
+//   reads its item from slot i, so XCD x works through the (length rank,
+//   head) pairs x, x + 8, ... (all tiles of a pair share that XCD's L2; with
+//   H a multiple of 8 every XCD gets one head of each batch entry), longest
+//   sequence first (longest processing time first), then the tiles of empty
+//   sequences, which only write zeros.  The fully padded tiles of a
+//   non-empty sequence get no item: that sequence's tiles with valid rows
+//   write their zeros.  Without a schedule every workgroup derives the same
+//   item from seq_lens itself (a rank of the lengths and prefix sums over the
+//   pairs: several microseconds per workgroup).
+// * Kept-entry lists.  Per batch entry and 128-row group of queries (the
+//   rows one forward or dQ workgroup owns) the block-mask entries that some
+//   block row of the group keeps, with which rows keep it and which mark it
+//   full; per 128-key group the same down the block columns (dK/dV).  The
+//   kernels read their tiles from the list instead of scanning block-mask
+//   lines for non-zero entries.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace sigattn {
+
+namespace {
+
+constexpr int kSchedThreads = 256;
+constexpr int kSortMax = 1024;  // larger batches keep their natural order
+
+// Exclusive prefix sum over the workgroup's 256 threads; *total receives the
+// sum.  Every thread must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *wave_tot, int *total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int incl = wave_inclusive_scan(v);
+    if (lane == 63) wave_tot[w] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < kSchedThreads / 64; ++i) {
+        const int t = wave_tot[i];
+        before += i < w ? t : 0;
+        all += t;
+    }
+    __syncthreads();  // wave_tot is reused by the next call
+    *total = all;
+    return before + incl - v;
+}
+
+}  // namespace
+
+// Grid: 16 item workgroups (XCD x = blockIdx.x % 8; blockIdx.x / 8 selects
+// the one-kind array items1 or the two-kind array items2), then one wave per
+// (direction, batch entry, group) for the entry lists.
+__global__ void __launch_bounds__(kSchedThreads)
+schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict__ bm, int B,
+                int H, int L, int bq, int bk, int Tq, int Tk, uint8_t *__restrict__ sched) {
+    const ScheduleLayout lay = schedule_layout(B, H, L, bq, bk);
+    const int G = lay.groups;
+    const int tid = threadIdx.x;
+    if (blockIdx.x < 16) {
+        __shared__ int s_len[kSortMax], s_ord[kSortMax], s_tot[kSchedThreads / 64];
+        const int x = blockIdx.x & 7, K = blockIdx.x < 8 ? 1 : 2;
+        int4 *items = reinterpret_cast<int4 *>(sched + (K == 1 ? lay.items1 : lay.items2));
+        // Batch entries by decreasing length, ties by index (rank by counting).
+        const bool sorted = B <= kSortMax;
+        if (sorted) {
+            for (int c = tid; c < B; c += kSchedThreads) s_len[c] = clamp_len(seq_lens[c], L);
+            __syncthreads();
+            for (int c = tid; c < B; c += kSchedThreads) {
+                const int nc = s_len[c];
+                int rank = 0;
+                for (int c2 = 0; c2 < B; ++c2) {
+                    const int m = s_len[c2];
+                    rank += (m > nc) || (m == nc && c2 < c);
+                }
+                s_ord[rank] = c;
+            }
+            __syncthreads();
+        }
+        const int pairs = B * H;
+        const int npx = pairs > x ? (pairs - x + 7) / 8 : 0;  // pairs of XCD x
+        const int64_t cap = ((int64_t)(pairs + 7) / 8) * G * K;  // slots of XCD x
+        int64_t k = 0;                                         // items written so far
+        for (int pass = 0; pass < 2; ++pass) {  // 0: tiles with valid rows, 1: empty sequences
+            for (int j0 = 0; j0 < npx; j0 += kSchedThreads) {
+                const int j = j0 + tid;
+                const bool valid = j < npx;
+                const int pair = x + 8 * (valid ? j : 0);
+                const int r = pair / H, h = pair - r * H;
+                const int b = sorted ? s_ord[r] : r;
+                const int n = sorted ? s_len[b] : clamp_len(seq_lens[b], L);
+                const int per = pass == 0 ? (n + 127) / 128 : (n == 0 ? G : 0);
+                const int cnt = valid ? K * per : 0;
+                int total;
+                const int off = block_exclusive_scan(cnt, s_tot, &total);
+                for (int i = 0; i < cnt; ++i) {
+                    const int kind = i >= per ? 1 : 0, t = i - kind * per;
+                    items[8 * (k + off + i) + x] = make_int4(b, h, t | (kind << 30), n);
+                }
+                k += total;
+            }
+        }
+        for (int64_t kk = k + tid; kk < cap; kk += kSchedThreads)
+            items[8 * kk + x] = make_int4(0, 0, -1, 0);
+        return;
+    }
+
+    // Entry lists: one wave per (direction, batch entry, group).
+    const int lane = tid & 63;
+    const int64_t idx = (int64_t)(blockIdx.x - 16) * (kSchedThreads / 64) + (tid >> 6);
+    const int64_t per_dir = (int64_t)B * G;
+    if (idx >= 2 * per_dir) return;
+    const int dir = (int)(idx / per_dir);
+    const int b = (int)((idx % per_dir) / G), g = (int)(idx % G);
+    const int n = clamp_len(seq_lens[b], L);
+    const uint8_t *bmb = bm + (int64_t)b * Tq * Tk;
+    uint32_t *list;
+    int lines, nblk, stride;
+    int64_t line_step, entry_step;
+    const uint8_t *first;
+    if (dir == 0) {  // query group: block rows g R .. g R + R - 1, entries along the row
+        const int R = 128 / bq, line0 = g * R;
+        lines = min(R, Tq - line0);
+        nblk = min(Tk, (n + bk - 1) / bk);
+        first = bmb + (int64_t)line0 * Tk;
+        line_step = Tk;
+        entry_step = 1;
+        stride = lay.qstride;
+        list = reinterpret_cast<uint32_t *>(sched + lay.qlists) + ((int64_t)b * G + g) * stride;
+    } else {  // key group: block columns g C .. g C + C - 1, entries down the column
+        const int C = 128 / bk, col0 = g * C;
+        lines = min(C, Tk - col0);
+        nblk = min(Tq, (n + bq - 1) / bq);
+        first = bmb + col0;
+        line_step = 1;
+        entry_step = Tk;
+        stride = lay.kstride;
+        list = reinterpret_cast<uint32_t *>(sched + lay.klists) + ((int64_t)b * G + g) * stride;
+    }
+    int cnt = 0;
+    for (int e0 = 0; e0 < nblk; e0 += 64) {
+        const int e = e0 + lane;
+        uint32_t kept = 0, full = 0;
+        if (e < nblk) {
+            for (int r = 0; r < lines; ++r) {
+                const uint32_t v = first[(int64_t)r * line_step + (int64_t)e * entry_step];
+                kept |= (v != 0 ? 1u : 0u) << r;
+                full |= ((v >> 1) & 1u) << r;
+            }
+        }
+        const uint64_t m = __ballot(kept != 0);
+        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (kept != 0) list[1 + cnt + before] = (uint32_t)e | (kept << 24) | (full << 28);
+        cnt += __popcll(m);
+    }
+    if (lane == 0) list[0] = (uint32_t)cnt;
+    for (int i = 1 + cnt + lane; i < stride; i += 64) list[i] = 0u;  // every word written
+}
+
+hipError_t launch_schedule(const int32_t *seq_lens, const uint8_t *block_mask, int B, int H,
+                           int L, int block_q, int block_k, void *schedule, hipStream_t stream) {
+    const ScheduleLayout lay = schedule_layout(B, H, L, block_q, block_k);
+    const int Tq = (int)(((int64_t)L + block_q - 1) / block_q);
+    const int Tk = (int)(((int64_t)L + block_k - 1) / block_k);
+    const int64_t waves = 2 * (int64_t)B * lay.groups;
+    const int64_t blocks = 16 + (waves + kSchedThreads / 64 - 1) / (kSchedThreads / 64);
+    hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)blocks), dim3(kSchedThreads), 0, stream,
+                       seq_lens, block_mask, B, H, L, block_q, block_k, Tq, Tk,
+                       reinterpret_cast<uint8_t *>(schedule));
+    return hipGetLastError();
+}
+
+}  // namespace sigattn
