@@ -34,6 +34,7 @@ KERNEL_SOURCES = {
     "fwd": "varlen_attention_amd/csrc/fwd.hip",
     "bwd": "varlen_attention_amd/csrc/bwd.hip",
     "blockmask": "varlen_attention_amd/csrc/blockmask.hip",
+    "schedule": "varlen_attention_amd/csrc/schedule.hip",
 }
 
 
@@ -53,7 +54,8 @@ def _code_only(text: str) -> str:
 
 def source_digest(kernel: str) -> str:
     """Digest of the code (not the comments) a kernel is built from."""
-    paths = [KERNEL_SOURCES[kernel], "varlen_attention_amd/csrc/device_common.h"]
+    paths = [KERNEL_SOURCES[kernel], "varlen_attention_amd/csrc/device_common.h",
+             "varlen_attention_amd/csrc/kernels.h"]
     h = hashlib.sha256()
     for p in paths:
         with open(os.path.join(ROOT, p), encoding="utf-8") as f:
@@ -105,7 +107,8 @@ def _find(dirname, suffix):
     raise FileNotFoundError(f"no *{suffix} under {dirname}")
 
 
-KERNEL_SYMBOLS = {"fwd": "::fwd_kernel<", "bwd": "::bwd_kernel<", "blockmask": "blockmask_"}
+KERNEL_SYMBOLS = {"fwd": "::fwd_kernel<", "bwd": "::bwd_kernel<", "blockmask": "blockmask_",
+                  "schedule": "schedule_kernel"}
 
 
 def summarize_stats(dirname: str, skip: int = 0) -> str:
@@ -182,6 +185,58 @@ def summarize_traffic(kernel: str, fetch_dir: str, write_dir: str, copy_fetch_di
         f"traffic_over_algorithmic: {hbm / algo:.3f}",
     ]
     return "\n".join(lines)
+
+
+def summarize_counters(kernel: str, dirs) -> str:
+    """Markdown table of rocprofv3 --pmc runs (one or more output directories)
+    for one kernel: each counter's average per dispatch, and the ratios the
+    kernel's bound is read from, with their formulas."""
+    sym = KERNEL_SYMBOLS[kernel]
+    vals = {}
+    for d in dirs:
+        for r in _csv_rows(_find(d, "counter_collection.csv")):
+            if sym in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    avg = {k: float(np.mean(v)) for k, v in vals.items()}
+    out = [f"Counters of `{kernel}` (source digest {source_digest(kernel)}), average per "
+           "dispatch:", "", "| counter | dispatches | average |", "|---|---|---|"]
+    for k in sorted(avg):
+        out.append(f"| {k} | {len(vals[k])} | {avg[k]:.6g} |")
+    # GRBM_GUI_ACTIVE counts GPU-busy cycles summed over the 8 XCDs, so one
+    # XCD's cycles are a eighth of it; the SQ cycle counters sum over all
+    # 1024 SIMDs (256 CUs x 4).
+    simds = 256 * 4
+    xcds = 8
+    derived = []
+
+    def have(*names):
+        return all(n in avg for n in names)
+    if have("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"):
+        derived.append(("MFMA busy, SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 "
+                        "SIMDs)",
+                        avg["SQ_VALU_MFMA_BUSY_CYCLES"] * xcds / (avg["GRBM_GUI_ACTIVE"] * simds)))
+    if have("SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE"):
+        derived.append(("VALU active, 4 x SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 "
+                        "SIMDs)",
+                        4 * avg["SQ_ACTIVE_INST_VALU"] * xcds / (avg["GRBM_GUI_ACTIVE"] * simds)))
+    if have("SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES"):
+        derived.append(("MFMA cycles with VALU issuing beside them, "
+                        "SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES",
+                        avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"]))
+    for num in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU_CVT",
+                "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_MUL_F32", "SQ_INSTS_VALU_ADD_F32",
+                "SQ_INSTS_VALU_INT32", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
+        if have(num, "SQ_INSTS_MFMA"):
+            derived.append((f"{num} per MFMA instruction", avg[num] / avg["SQ_INSTS_MFMA"]))
+    if have("SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS"):
+        derived.append(("LDS bank-conflict cycles per LDS instruction",
+                        avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_INSTS_LDS"]))
+    if have("GRBM_GUI_ACTIVE"):
+        derived.append(("one XCD's busy cycles, GRBM_GUI_ACTIVE / 8", avg["GRBM_GUI_ACTIVE"] / xcds))
+    if derived:
+        out += ["", "| derived | value |", "|---|---|"]
+        out += [f"| {name} | {value:.4g} |" for name, value in derived]
+    return "\n".join(out)
 
 
 def copy_reference(mib: int) -> None:
@@ -651,6 +706,8 @@ def main() -> int:
                     metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="print the HBM traffic summary of KERNEL from FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--summarize-counters", nargs="+", metavar=("KERNEL", "DIR"),
+                    help="print the counter summary of KERNEL from rocprofv3 --pmc output DIRs")
     ap.add_argument("--suite", action="store_true",
                     help="run the measurement suite (markdown on stdout) instead of the step")
     ap.add_argument("--suite-jsonl", metavar="PATH",
@@ -661,6 +718,9 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats, args.skip_dispatches))
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1:]))
         return 0
     if args.summarize_traffic:
         import synthetic as syn

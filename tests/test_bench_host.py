@@ -109,3 +109,16 @@ def test_parity_errors_attach_to_matching_suite_rows(tmp_path):
     assert rows[1]["max_abs"] == 4e-3 and rows[1]["rel_l2"] == 3e-3
     assert rows[2]["parity_outputs"] == ["dK", "dV"] and rows[2]["max_abs"] == 2e-3
     assert "max_abs" not in rows[3] and "max_abs" not in rows[4]
+
+
+def test_counter_summary_ratios(tmp_path):
+    sym = "void sigattn::bwd_kernel<64, 4, 2, 0, 0, 1>(sigattn::AttnParams)"
+    _counter_table(tmp_path / "a", [(sym, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 500.0),
+                                    (sym, "GRBM_GUI_ACTIVE", 8 * 1000.0),
+                                    (sym, "SQ_INSTS_MFMA", 10.0),
+                                    (sym, "SQ_INSTS_VALU_TRANS_F32", 25.0),
+                                    ("other", "SQ_INSTS_MFMA", 99.0)])
+    text = bench.summarize_counters("bwd", [str(tmp_path / "a")])
+    assert "| SQ_INSTS_MFMA | 1 | 10 |" in text
+    assert "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) | 0.5 |" in text
+    assert "SQ_INSTS_VALU_TRANS_F32 per MFMA instruction | 2.5 |" in text
