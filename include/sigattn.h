@@ -269,6 +269,31 @@ int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, con
                    void *stream);
 
 /*
+ * sigattn_fwd_noalloc - sigattn_fwd with its work schedule kept in memory the
+ * library holds, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * It builds the schedule (see blockmask_build) from seq_lens and block_mask
+ * into a static device array of SIGATTN_NOALLOC_SCRATCH_BYTES bytes (one per
+ * GPU, held until the process ends; its address is looked up once per device
+ * on the first call there), then runs the forward with it.  It calls no
+ * allocator.  Results equal sigattn_fwd's with a schedule from
+ * blockmask_build, bit for bit.
+ * Arguments as sigattn_fwd (no schedule argument); block_mask is required.
+ * Every call on one GPU uses that GPU's one array, whatever the stream:
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race and must be ordered by the caller; calls in one stream are ordered.
+ * Errors: as sigattn_fwd; INVALID_ARG for a NULL block_mask; UNSUPPORTED when
+ * the schedule (sigattn_schedule_bytes(B, H, L, block_q, block_k)) exceeds
+ * SIGATTN_NOALLOC_SCRATCH_BYTES; LAUNCH also when the array's address cannot
+ * be obtained.
+ */
+#define SIGATTN_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+int sigattn_fwd_noalloc(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+                        const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
+                        const int32_t *key_range, int32_t bias_mode, int32_t variant, void *o,
+                        float *lse, void *stream);
+
+/*
  * sigattn_diff_fwd - differential attention forward ("Differential
  * Transformer" note, "How differential attention works"): two softmax maps
  * over one value tensor, the second subtracted with the scalar lambda,

@@ -29,9 +29,9 @@ def lib():
 def test_header_declares_the_boundary():
     import varlen_attention_amd as va
     assert declared_functions() == sorted(
-        ["blockmask_build", "sigattn_schedule_bytes", "sigattn_fwd", "sigattn_bwd",
-         "sigattn_bwd_dkdv", "sigattn_bwd_dq", "sigattn_diff_bwd", "sigattn_diff_fwd",
-         "sigattn_last_error"])
+        ["blockmask_build", "sigattn_schedule_bytes", "sigattn_fwd", "sigattn_fwd_noalloc",
+         "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq", "sigattn_diff_bwd",
+         "sigattn_diff_fwd", "sigattn_last_error"])
     assert sorted(va.EXPORTS) == declared_functions()
 
 
@@ -95,6 +95,30 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, va, _shape(va), sched=FAKE) == va.ERR_INVALID_ARG
     assert b"schedule" in lib.sigattn_last_error()
     assert _fwd(lib, va, _shape(va), sched=ctypes.c_void_p(0x10008), bm=FAKE) == va.ERR_ALIGNMENT
+
+
+def test_noalloc_forward_argument_errors(lib):
+    """sigattn_fwd_noalloc: as sigattn_fwd, plus a required block mask and a
+    schedule no larger than the library's array; all checked before any HIP
+    call (none of these reaches the GPU)."""
+    import varlen_attention_amd as va
+
+    def fwd0(shape, bm=FAKE, q=FAKE, mask=None, kr=None):
+        return lib.sigattn_fwd_noalloc(ctypes.byref(shape), q, FAKE, FAKE, FAKE, bm, mask, kr, 1,
+                                       0, FAKE, None, None)
+
+    assert fwd0(_shape(va), bm=None) == va.ERR_INVALID_ARG
+    assert b"block mask" in lib.sigattn_last_error()
+    assert fwd0(_shape(va), q=None) == va.ERR_INVALID_ARG
+    assert fwd0(_shape(va, d=96)) == va.ERR_UNSUPPORTED
+    # B32 H64 L65536: a schedule of ~50 MB, beyond the 8 MiB the library holds.
+    big = _shape(va, B=32, H=64, L=65536, stride_b=64 * 65536 * 64, stride_h=65536 * 64)
+    assert lib.sigattn_schedule_bytes(32, 64, 65536, 128, 128) > va.NOALLOC_SCRATCH_BYTES
+    assert fwd0(big) == va.ERR_UNSUPPORTED
+    assert b"holds" in lib.sigattn_last_error()
+    hdr = open(HEADER).read()
+    m = re.search(r"#define\s+SIGATTN_NOALLOC_SCRATCH_BYTES\s+\((\d+) \* 1024 \* 1024\)", hdr)
+    assert m and int(m.group(1)) * 1024 * 1024 == va.NOALLOC_SCRATCH_BYTES
 
 
 def test_backward_argument_errors(lib):

@@ -24,9 +24,12 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_LAUNCH = 0, -1, -2, -3,
 MAX_MASKED_L = 46080
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsigattn.so")
-EXPORTS = ("blockmask_build", "sigattn_schedule_bytes", "sigattn_fwd", "sigattn_bwd",
-           "sigattn_bwd_dkdv", "sigattn_bwd_dq", "sigattn_diff_fwd", "sigattn_diff_bwd",
-           "sigattn_last_error")
+EXPORTS = ("blockmask_build", "sigattn_schedule_bytes", "sigattn_fwd", "sigattn_fwd_noalloc",
+           "sigattn_bwd", "sigattn_bwd_dkdv", "sigattn_bwd_dq", "sigattn_diff_fwd",
+           "sigattn_diff_bwd", "sigattn_last_error")
+# Bytes of the library's own schedule memory for sigattn_fwd_noalloc
+# (SIGATTN_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024
 
 
 class SigattnError(RuntimeError):
@@ -69,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.blockmask_build.restype = ctypes.c_int
     lib.sigattn_fwd.argtypes = [S, P, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sigattn_fwd.restype = ctypes.c_int
+    lib.sigattn_fwd_noalloc.argtypes = [S, P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.sigattn_fwd_noalloc.restype = ctypes.c_int
     lib.sigattn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P, P]
     lib.sigattn_bwd.restype = ctypes.c_int
     lib.sigattn_bwd_dkdv.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P]
@@ -258,6 +263,43 @@ def sigattn_fwd(q, k, v, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQ
                            _ptr(mask), _ptr(key_range), bias, variant, _ptr(out), _ptr(lse),
                            _stream(stream)))
     return (out, lse) if return_lse else out
+
+
+def sigattn_fwd_noalloc(q, k, v, seq_lens, block_mask, out, lse=None, mask=None,
+                        bias=BIAS_LOG_SEQLEN, variant=SIGMOID, scale=None, block_q=128,
+                        block_k=128, stream=None, key_range=None):
+    """sigattn_fwd with the work schedule kept in the library's own device
+    memory (sigattn_fwd_noalloc): allocates nothing, so the output ``out`` (and
+    ``lse``, when wanted) must be given.  block_mask is required."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, nm, torch.bfloat16)
+    _layout([q, k, v], ["q", "k", "v"])
+    _lens(seq_lens, q.shape[0], q.device)
+    if not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous")
+    if tuple(out.shape) != tuple(q.shape) or out.stride(3) != 1:
+        raise ValueError("out must match q's shape with unit stride in d")
+    B, H, L, d = q.shape
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, H, L) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [B, H, L] tensor")
+    if block_mask is None:
+        raise ValueError("sigattn_fwd_noalloc needs the block mask")
+    _need(block_mask, "block_mask", torch.uint8)
+    want = (B, num_tiles(L, block_q), num_tiles(L, block_k))
+    if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
+        raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
+    if mask is not None:
+        _need(mask, "mask", torch.uint8)
+        if tuple(mask.shape) != (B, L, L) or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous uint8 [B, L, L] tensor")
+    _key_range(key_range, B, L)
+    shape = _shape(q, out.stride(), scale, block_q, block_k)
+    _check(load_library().sigattn_fwd_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(block_mask),
+        _ptr(mask), _ptr(key_range), bias, variant, _ptr(out), _ptr(lse), _stream(stream)))
+    return out
 
 
 def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k, variant, o,

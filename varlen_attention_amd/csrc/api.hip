@@ -6,8 +6,16 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/sigattn.h"
 #include "kernels.h"
+
+// Device memory for sigattn_fwd_noalloc's work schedule: one copy per GPU
+// (a file-scope device array), held until the process ends.  Host code never
+// uses the array's name as an address: scratch_ptr() fetches each device's
+// own address once, with hipGetSymbolAddress, and keeps it.
+static __device__ __align__(256) uint8_t scratch[SIGATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -36,6 +44,30 @@ int launch_status(hipError_t e, const char *what) {
 }
 
 // Shared checks of sigattn_fwd / sigattn_bwd; fills the common parameter block.
+// Address of the current device's copy of `scratch` (nullptr and *err set
+// on failure), looked up on the device's first use and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+void *scratch_ptr(hipError_t *err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 // Workgroups of the largest launch (the one-launch backward) for B, H, L.
 int64_t max_workgroups(int64_t B, int64_t H, int64_t L) {
     return 16 * ((B * H + 7) / 8) * ((L + 127) / 128);
@@ -219,6 +251,49 @@ int sigattn_fwd(const sigattn_shape *shape, const void *q, const void *k, const 
     p.o = o;
     p.lse = lse;
     return launch_status(sigattn::launch_fwd(p, (hipStream_t)stream), "sigattn_fwd");
+}
+
+int sigattn_fwd_noalloc(const sigattn_shape *shape, const void *q, const void *k, const void *v,
+                        const int32_t *seq_lens, const uint8_t *block_mask, const uint8_t *mask,
+                        const int32_t *key_range, int32_t bias_mode, int32_t variant, void *o,
+                        float *lse, void *stream) {
+    if (block_mask == nullptr)
+        return fail(SIGATTN_ERR_INVALID_ARG, "sigattn_fwd_noalloc needs the block mask");
+    sigattn::AttnParams p = {};
+    const void *inputs[3] = {q, k, v};
+    void *outputs[1] = {o};
+    int st = check_attention(shape, inputs, 3, outputs, 1, seq_lens, block_mask, nullptr, mask,
+                             key_range, bias_mode, variant, &p);
+    if (st != SIGATTN_OK) return st;
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+        return fail(SIGATTN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
+    const sigattn::ScheduleLayout lay =
+        sigattn::schedule_layout(shape->B, shape->H, shape->L, shape->block_q, shape->block_k);
+    if (lay.bytes > SIGATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(SIGATTN_ERR_UNSUPPORTED,
+                    "sigattn_fwd_noalloc: the schedule needs %lld bytes, the library holds %d",
+                    (long long)lay.bytes, SIGATTN_NOALLOC_SCRATCH_BYTES);
+    hipError_t err;
+    uint8_t *sched = static_cast<uint8_t *>(scratch_ptr(&err));
+    if (sched == nullptr) return launch_status(err, "sigattn_fwd_noalloc (scratch address)");
+    const hipStream_t hs = (hipStream_t)stream;
+    st = launch_status(sigattn::launch_schedule(seq_lens, block_mask, shape->B, shape->H,
+                                                shape->L, shape->block_q, shape->block_k, sched,
+                                                hs),
+                       "sigattn_fwd_noalloc (schedule)");
+    if (st != SIGATTN_OK) return st;
+    p.items1 = reinterpret_cast<const int4 *>(sched + lay.items1);
+    p.items2 = reinterpret_cast<const int4 *>(sched + lay.items2);
+    p.qlist = reinterpret_cast<const uint32_t *>(sched + lay.qlists);
+    p.klist = reinterpret_cast<const uint32_t *>(sched + lay.klists);
+    p.qstride = lay.qstride;
+    p.kstride = lay.kstride;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    return launch_status(sigattn::launch_fwd(p, hs), "sigattn_fwd_noalloc");
 }
 
 int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1, const void *q2,
