@@ -13,7 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsigattn.so")
-SOURCES = ["api.hip", "blockmask.hip", "schedule.hip", "fwd.hip", "bwd.hip"]
+SOURCES = ["api.hip", "blockmask.hip", "schedule.hip", "fwd.hip", "fwd_sigmoid.hip",
+           "fwd_softmax.hip", "fwd_diff.hip", "bwd.hip", "bwd_sigmoid.hip", "bwd_softmax.hip",
+           "bwd_softmax1.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -40,7 +42,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
+    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])

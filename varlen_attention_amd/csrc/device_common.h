@@ -112,34 +112,22 @@ enum { kWantNone = 0, kWantFull = 1, kWantMask = 2 };
 // wave's own line (`line`) needs of it: kWantNone when that line drops it, so
 // every element still obeys its own entry.  Lines at or past `lines` are off.
 // Only the union and the wave's own line are kept, in six scalar registers.
-//
-// With a kept-entry list from a schedule buffer (list != null: a count word,
-// then e | kept-by-line << 24 | full-by-line << 28 per entry some line keeps,
-// in increasing e) the entries come from the list instead: 64 list words per
-// vector load, one read out per tile, and no empty entry is ever visited.
 template <int BT, int R, bool ROW>
 struct TileSchedule {
     const uint8_t *bm;        // line 0's first entry, or null (from seq_lens)
-    const uint32_t *list;     // kept-entry list (count word first), or null
     int tk;                   // entries per block-mask row
     int nlines, line;         // lines that exist; the wave's own line
     int nblk;                 // block-mask entries covering [0, n)
     int per_blk;              // kernel tiles per block-mask entry
     int nkt;                  // kernel tiles covering [0, n)
     int wbase, entry, sub;
-    int lcnt, lmax, lpos;     // list: entries, words after the count, next entry
-    uint32_t lwords;          // list: words wbase .. wbase + 63 (one per lane)
     uint64_t act;             // entries (of the 64 at wbase) some line keeps
     uint64_t mine, mine_full; // entries the wave's line keeps / marks full
     bool on, full;            // the same two, for the tile next() returned
 
-    // lst / lst_max: the group's kept-entry list and its capacity in entries
-    // (the words after the count), or null.
     __device__ __forceinline__ void init(const uint8_t *first, int row_len, int lines, int own_line,
-                                         int n, int block, const uint32_t *lst = nullptr,
-                                         int lst_max = 0) {
+                                         int n, int block) {
         bm = first;
-        list = lst;
         tk = row_len;
         nlines = lines;
         line = own_line;
@@ -151,15 +139,6 @@ struct TileSchedule {
         sub = 0;
         act = mine = mine_full = 0;
         on = full = false;
-        lcnt = lpos = 0;
-        lmax = lst_max;
-        lwords = 0;
-        if (list != nullptr) {
-            const int lane = (int)(threadIdx.x & 63);
-            lcnt = (int)list[0];
-            wbase = 0;
-            lwords = lane < lmax ? list[1 + lane] : 0u;
-        }
     }
 
     // Offset of entry e of line r from line 0's first entry.
@@ -172,21 +151,6 @@ struct TileSchedule {
         if (entry >= 0 && sub + 1 < per_blk && entry * per_blk + sub + 1 < nkt) {
             ++sub;
             return entry * per_blk + sub;
-        }
-        if (list != nullptr) {
-            if (lpos >= lcnt) return -1;
-            if (lpos - wbase >= 64) {  // the next 64 list words
-                wbase += 64;
-                const int lane = (int)(threadIdx.x & 63);
-                lwords = wbase + lane < lmax ? list[1 + wbase + lane] : 0u;
-            }
-            const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)lwords, lpos - wbase);
-            ++lpos;
-            entry = (int)(w & 0xffffffu);
-            on = R == 1 || ((w >> (24 + line)) & 1u);
-            full = (w >> (28 + line)) & 1u;
-            sub = 0;
-            return entry * per_blk;
         }
         while (act == 0) {
             wbase += 64;
@@ -232,6 +196,71 @@ struct TileSchedule {
             return !on ? kWantNone : full ? kWantFull : kWantMask;
     }
 };
+
+// The same walk over a kept-entry list from a schedule buffer (a count word,
+// then e | kept-by-line << 24 | full-by-line << 28 per entry some line
+// keeps, in increasing e): 64 list words per vector load, one read out per
+// tile, and no empty entry is ever visited.  Kernels built for a schedule use
+// this instead of TileSchedule, so neither carries the other's registers.
+template <int BT, int R>
+struct ListSchedule {
+    const uint32_t *list;     // the group's list, count word first
+    int cnt, cap;             // entries in the list; words after the count word
+    int base, pos;            // first entry held in `words`; next entry to return
+    int line;                 // the wave's own line
+    int per_blk, nkt;         // kernel tiles per block-mask entry; covering [0, n)
+    int entry, sub;
+    uint32_t words;           // entries base .. base + 63, one per lane
+    bool on, full;            // the wave's line keeps / marks full the current entry
+
+    __device__ __forceinline__ void init(const uint32_t *lst, int lst_cap, int own_line, int n,
+                                         int block) {
+        const int lane = (int)(threadIdx.x & 63);
+        list = lst;
+        cap = lst_cap;
+        cnt = (int)list[0];
+        base = pos = 0;
+        line = own_line;
+        per_blk = block / BT;
+        nkt = (n + BT - 1) / BT;
+        entry = -1;
+        sub = 0;
+        on = full = false;
+        words = lane < cap ? list[1 + lane] : 0u;
+    }
+
+    __device__ __forceinline__ int next() {
+        if (entry >= 0 && sub + 1 < per_blk && entry * per_blk + sub + 1 < nkt) {
+            ++sub;
+            return entry * per_blk + sub;
+        }
+        if (pos >= cnt) return -1;
+        if (pos - base >= 64) {  // the next 64 list words
+            base += 64;
+            const int lane = (int)(threadIdx.x & 63);
+            words = base + lane < cap ? list[1 + base + lane] : 0u;
+        }
+        const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)words, pos - base);
+        ++pos;
+        entry = (int)(w & 0xffffffu);
+        on = R == 1 || ((w >> (24 + line)) & 1u);
+        full = (w >> (28 + line)) & 1u;
+        sub = 0;
+        return entry * per_blk;
+    }
+
+    __device__ __forceinline__ int want() const {
+        if constexpr (R == 1)
+            return full ? kWantFull : kWantMask;
+        else
+            return !on ? kWantNone : full ? kWantFull : kWantMask;
+    }
+};
+
+// The schedule type of a kernel built with (LIST) or without a schedule.
+template <int BT, int R, bool ROW, bool LIST>
+using Schedule =
+    typename std::conditional<LIST, ListSchedule<BT, R>, TileSchedule<BT, R, ROW>>::type;
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
 // round trips): row_shr 1, 2, 4, 8 scan each row of 16 lanes (lanes shifted
@@ -358,15 +387,14 @@ __device__ __forceinline__ bool tile_item(const int32_t *seq_lens, int B, int H,
     return tile_item2<ROWS, ROWS>(seq_lens, B, H, L, ntiles, 0, b, h, kind, t, n);
 }
 
-// The workgroup's item: read from the schedule's item array when the launch
-// has one (one scalar load), else derived from seq_lens (tile_item2, same
-// placement and order).  Launches over 128-row tiles of one or two kinds.
-template <int KINDS>
+// The workgroup's item: read from the schedule's item array in kernels built
+// for a schedule (one scalar load), else derived from seq_lens (tile_item2,
+// same placement and order).  Launches over 128-row tiles of one or two kinds.
+template <int KINDS, bool LIST>
 __device__ __forceinline__ bool work_item(const AttnParams &p, int &b, int &h, int &kind, int &t,
                                           int &n) {
-    const int4 *items = KINDS == 2 ? p.items2 : p.items1;
-    if (items != nullptr) {
-        const int4 it = items[blockIdx.x];
+    if constexpr (LIST) {
+        const int4 it = (KINDS == 2 ? p.items2 : p.items1)[blockIdx.x];
         if (it.z < 0) return false;
         b = it.x;
         h = it.y;
@@ -374,11 +402,12 @@ __device__ __forceinline__ bool work_item(const AttnParams &p, int &b, int &h, i
         t = it.z & 0x3fffffff;
         n = it.w;
         return true;
+    } else {
+        const int nt = (p.L + 127) / 128;
+        kind = 0;
+        return tile_item2<128, 128>(p.seq_lens, p.B, p.H, p.L, nt, KINDS == 2 ? nt : 0, b, h,
+                                    kind, t, n);
     }
-    const int nt = (p.L + 127) / 128;
-    kind = 0;
-    return tile_item2<128, 128>(p.seq_lens, p.B, p.H, p.L, nt, KINDS == 2 ? nt : 0, b, h, kind, t,
-                                n);
 }
 
 // The fully padded tiles (of ROWS rows) that tile t of a sequence with
