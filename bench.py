@@ -30,11 +30,13 @@ METRIC = "valid-work TFLOP/s + % bf16 MFMA peak, padded varlen sigmoid attn fwd/
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
+# The sources each measured kernel is built from (the benchmark's sigmoid
+# instantiations), for the digest that ties a counter summary to the code.
 KERNEL_SOURCES = {
-    "fwd": "varlen_attention_amd/csrc/fwd.hip",
-    "bwd": "varlen_attention_amd/csrc/bwd.hip",
-    "blockmask": "varlen_attention_amd/csrc/blockmask.hip",
-    "schedule": "varlen_attention_amd/csrc/schedule.hip",
+    "fwd": ["varlen_attention_amd/csrc/fwd_kernel.h", "varlen_attention_amd/csrc/fwd_sigmoid.hip"],
+    "bwd": ["varlen_attention_amd/csrc/bwd_kernel.h", "varlen_attention_amd/csrc/bwd_sigmoid.hip"],
+    "blockmask": ["varlen_attention_amd/csrc/blockmask.hip"],
+    "schedule": ["varlen_attention_amd/csrc/schedule.hip"],
 }
 
 
@@ -54,8 +56,8 @@ def _code_only(text: str) -> str:
 
 def source_digest(kernel: str) -> str:
     """Digest of the code (not the comments) a kernel is built from."""
-    paths = [KERNEL_SOURCES[kernel], "varlen_attention_amd/csrc/device_common.h",
-             "varlen_attention_amd/csrc/kernels.h"]
+    paths = KERNEL_SOURCES[kernel] + ["varlen_attention_amd/csrc/device_common.h",
+                                      "varlen_attention_amd/csrc/kernels.h"]
     h = hashlib.sha256()
     for p in paths:
         with open(os.path.join(ROOT, p), encoding="utf-8") as f:

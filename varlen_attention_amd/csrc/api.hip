@@ -224,6 +224,10 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t 
                         (long long)schedule_bytes, (long long)need);
     }
     const hipStream_t st = (hipStream_t)stream;
+    if (schedule != nullptr && mask == nullptr && key_range == nullptr)  // one launch for both
+        return launch_status(sigattn::launch_schedule(seq_lens, nullptr, B, H, L, block_q,
+                                                      block_k, schedule, st, block_mask),
+                             "blockmask_build");
     const int rc = launch_status(
         sigattn::launch_blockmask(seq_lens, mask, key_range, B, L, block_q, block_k, block_mask, st),
         "blockmask_build");

@@ -88,9 +88,12 @@ hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask,
                             const int32_t *key_range, int B, int L, int block_q, int block_k,
                             uint8_t *out, hipStream_t stream);
 // Work items and kept-entry lists (ScheduleLayout) from seq_lens and a
-// finished block mask, enqueued after it on the same stream.
+// finished block mask, enqueued after it on the same stream; or, with
+// padding_mask_out, for a padding-only batch: the block mask written into
+// padding_mask_out and the schedule in the same launch (block_mask unused).
 hipError_t launch_schedule(const int32_t *seq_lens, const uint8_t *block_mask, int B, int H,
-                           int L, int block_q, int block_k, void *schedule, hipStream_t stream);
+                           int L, int block_q, int block_k, void *schedule, hipStream_t stream,
+                           uint8_t *padding_mask_out = nullptr);
 hipError_t launch_fwd(const AttnParams &p, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const AttnParams &p, hipStream_t stream);
 hipError_t launch_bwd_dq(const AttnParams &p, hipStream_t stream);

@@ -21,6 +21,8 @@
 //   full; per 128-key group the same down the block columns (dK/dV).  The
 //   kernels read their tiles from the list instead of scanning block-mask
 //   lines for non-zero entries.
+// For a padding-only batch the block mask is a closed form of the lengths,
+// so the same launch writes it too.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -52,12 +54,25 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *wave_tot, int *t
 
 }  // namespace
 
+// Block-mask entry (i, j) of a padding-only batch entry of length n: bit 0
+// when the tile holds a valid element, bit 1 when it lies inside [0, n)^2.
+// The full-tile tests are written as i*bq <= n - bq so no product passes L.
+__device__ __forceinline__ uint32_t padding_entry(int i, int j, int n, int bq, int bk) {
+    const bool any = i * bq < n && j * bk < n;
+    const bool full = i * bq <= n - bq && j * bk <= n - bk;
+    return (any ? 1u : 0u) | (full ? 2u : 0u);
+}
+
 // Grid: 16 item workgroups (XCD x = blockIdx.x % 8; blockIdx.x / 8 selects
 // the one-kind array items1 or the two-kind array items2), then one wave per
-// (direction, batch entry, group) for the entry lists.
+// (direction, batch entry, group) for the entry lists, then, for a
+// padding-only batch (bm_out given), one wave per block row writing the
+// block mask, whose entries the lists then take from the same closed form
+// instead of reading bm: the whole build is one launch.
 __global__ void __launch_bounds__(kSchedThreads)
 schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict__ bm, int B,
-                int H, int L, int bq, int bk, int Tq, int Tk, uint8_t *__restrict__ sched) {
+                int H, int L, int bq, int bk, int Tq, int Tk, uint8_t *__restrict__ sched,
+                uint8_t *__restrict__ bm_out) {
     const ScheduleLayout lay = schedule_layout(B, H, L, bq, bk);
     const int G = lay.groups;
     const int tid = threadIdx.x;
@@ -113,7 +128,16 @@ schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict_
     const int lane = tid & 63;
     const int64_t idx = (int64_t)(blockIdx.x - 16) * (kSchedThreads / 64) + (tid >> 6);
     const int64_t per_dir = (int64_t)B * G;
-    if (idx >= 2 * per_dir) return;
+    if (idx >= 2 * per_dir) {
+        // Padding-only block mask: one wave per block row (b, i).
+        const int64_t row = idx - 2 * per_dir;
+        if (bm_out == nullptr || row >= (int64_t)B * Tq) return;
+        const int b = (int)(row / Tq), i = (int)(row % Tq);
+        const int n = clamp_len(seq_lens[b], L);
+        uint8_t *out = bm_out + ((int64_t)b * Tq + i) * Tk;
+        for (int j = lane; j < Tk; j += 64) out[j] = (uint8_t)padding_entry(i, j, n, bq, bk);
+        return;
+    }
     const int dir = (int)(idx / per_dir);
     const int b = (int)((idx % per_dir) / G), g = (int)(idx % G);
     const int n = clamp_len(seq_lens[b], L);
@@ -147,7 +171,12 @@ schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict_
         uint32_t kept = 0, full = 0;
         if (e < nblk) {
             for (int r = 0; r < lines; ++r) {
-                const uint32_t v = first[(int64_t)r * line_step + (int64_t)e * entry_step];
+                uint32_t v;
+                if (bm_out != nullptr)  // padding only: the closed form
+                    v = dir == 0 ? padding_entry(g * (128 / bq) + r, e, n, bq, bk)
+                                 : padding_entry(e, g * (128 / bk) + r, n, bq, bk);
+                else
+                    v = first[(int64_t)r * line_step + (int64_t)e * entry_step];
                 kept |= (v != 0 ? 1u : 0u) << r;
                 full |= ((v >> 1) & 1u) << r;
             }
@@ -163,15 +192,17 @@ schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict_
 }
 
 hipError_t launch_schedule(const int32_t *seq_lens, const uint8_t *block_mask, int B, int H,
-                           int L, int block_q, int block_k, void *schedule, hipStream_t stream) {
+                           int L, int block_q, int block_k, void *schedule, hipStream_t stream,
+                           uint8_t *padding_mask_out) {
     const ScheduleLayout lay = schedule_layout(B, H, L, block_q, block_k);
     const int Tq = (int)(((int64_t)L + block_q - 1) / block_q);
     const int Tk = (int)(((int64_t)L + block_k - 1) / block_k);
-    const int64_t waves = 2 * (int64_t)B * lay.groups;
+    int64_t waves = 2 * (int64_t)B * lay.groups;
+    if (padding_mask_out != nullptr) waves += (int64_t)B * Tq;
     const int64_t blocks = 16 + (waves + kSchedThreads / 64 - 1) / (kSchedThreads / 64);
     hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)blocks), dim3(kSchedThreads), 0, stream,
                        seq_lens, block_mask, B, H, L, block_q, block_k, Tq, Tk,
-                       reinterpret_cast<uint8_t *>(schedule));
+                       reinterpret_cast<uint8_t *>(schedule), padding_mask_out);
     return hipGetLastError();
 }
 
