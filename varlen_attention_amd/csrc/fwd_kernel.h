@@ -498,7 +498,11 @@ hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
     constexpr bool kNarrow = VARIANT == kDiff && D == 128;
     constexpr int NW = 4, BQ = 32 * NW;
     const int rows = BQ / p.block_q;  // block-mask rows per workgroup: 1, 2 or 4
-    const int kb = p.block_k >= 64 && !kNarrow ? 2 : 1;
+    // One map at d = 128 also visits 32 keys at a time, except under a dense
+    // mask: 64-key steps hold about 210 VGPRs (two waves per SIMD), 32-key
+    // steps about 170 (three).  A dense mask's words are staged per step, and
+    // at half the step that staging costs more than the third wave gains.
+    const int kb = p.block_k >= 64 && !kNarrow && (D == 64 || p.mask != nullptr) ? 2 : 1;
     const dim3 grid = tile_grid((p.L + BQ - 1) / BQ, p.B, p.H);
     dim3 block(64 * NW);
 #define SIGATTN_FWD_LAUNCH(KB_, MASK_, R_)                                                         \
