@@ -10,7 +10,7 @@
 // With an element mask the builder is one HBM scan of the valid rectangle
 // [0, n) x [0, n) of each mask: a workgroup owns a band of bq rows and a group
 // of key tiles, so it writes its outputs alone (no atomics to global memory),
-// and each wave walks one row at a time with 16-byte loads.
+// and each wave keeps the 16-byte loads of eight rows in flight.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -33,9 +33,12 @@ blockmask_padding_kernel(const int32_t *__restrict__ seq_lens, int L, int bq, in
     }
 }
 
-// Grid: (Tq * groups, B); 256 threads.  tiles_per_group * bk <= 1024 columns,
-// and tiles_per_group <= 32 so one 32-bit word holds the group's flags.
-__global__ void __launch_bounds__(256)
+// Grid: (Tq * groups, B); kScanThreads threads.  tiles_per_group * bk <= 1024
+// columns, and tiles_per_group <= 32 so one 32-bit word holds the group's
+// flags.  Offsets inside a row are 32-bit and relative to the row's first
+// byte; each row keeps its own 64-bit pointer.
+constexpr int kScanThreads = 256;
+__global__ void __launch_bounds__(kScanThreads)
 blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict__ mask,
                       int L, int bq, int bk_shift, int Tq, int Tk, int tiles_per_group,
                       int groups, uint8_t *__restrict__ out) {
@@ -51,16 +54,16 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
     if (threadIdx.x == 0) flags = zeros = 0u;
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t total = (uint64_t)gridDim.y * (uint64_t)L * (uint64_t)L;
+    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: rows in SGPRs
     uint32_t bits = 0, zbits = 0;
-    // One 16-byte chunk at byte address a of row `row` (columns [lo, hi) of
-    // the scan): non-zero bytes mark their tile kept, zero bytes not full.
-    auto chunk = [&](uint4 u, uint64_t a, uint64_t row, uint64_t lo, uint64_t hi) {
+    // One 16-byte chunk at offset a of its row (columns [lo, hi) of the
+    // scan): non-zero bytes mark their tile kept, zero bytes not full.
+    auto chunk = [&](uint4 u, int a, int lo, int hi) {
         const uint32_t nz = u.x | u.y | u.z | u.w;
-        const uint64_t s0 = a > lo ? a : lo, s1 = a + 16 < hi ? a + 16 : hi;  // in-range part
-        const int t0 = (int)((s0 - row) >> bk_shift) - j0;
-        const int t1 = (int)((s1 - 1 - row) >> bk_shift) - j0;
+        const int s0 = a > lo ? a : lo, s1 = a + 16 < hi ? a + 16 : hi;  // in-range part
+        const int t0 = (s0 >> bk_shift) - j0;
+        const int t1 = ((s1 - 1) >> bk_shift) - j0;
         if (nz == 0u) {  // every byte invalid
             zbits |= (1u << t0) | (1u << t1);
             return;
@@ -80,10 +83,10 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
             const uint32_t m = (((w[q] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[q]) & 0x80808080u;
             nz16 |= (((m >> 7) * 0x00204081u) >> 21 & 0xfu) << (4 * q);
         }
-        const int s = (int)(s0 - a), e = (int)(s1 - a);  // in-range bytes [s, e)
+        const int s = s0 - a, e = s1 - a;  // in-range bytes [s, e)
         const uint32_t range16 = ((1u << e) - 1u) & ~((1u << s) - 1u);
         // Bytes before the start of tile t1 belong to tile t0.
-        const int64_t split = (int64_t)(((uint64_t)(t1 + j0) << bk_shift) + row) - (int64_t)a;
+        const int split = ((t1 + j0) << bk_shift) - a;
         const uint32_t first = t1 == t0 ? 0xffffu : (1u << split) - 1u;
         const uint32_t in0 = range16 & first, in1 = range16 & ~first;
         if (nz16 & in0) bits |= 1u << t0;
@@ -92,44 +95,55 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
         if (~nz16 & in1) zbits |= 1u << t1;
     };
     if (r_lo < r_hi && c_lo < c_hi) {
-        // Four rows per wave in flight: all their loads are issued before any
-        // is examined (eight rows measured slower).  A row's window of at
-        // most 1024 columns, aligned down to 16 bytes, spans at most 65
-        // chunks: lane l takes chunks l and l + 64, both loaded up front so
-        // no lane waits on a second round trip.  Chunks that would run past
-        // the end of the mask are read byte by byte (bytes past the end 0).
-        for (int rb = r_lo + wave; rb < r_hi; rb += 16) {
-            uint4 u[4][2];
-            uint64_t arow[4], alo[4], ahi[4], a0[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int r = rb + 4 * t;
-                arow[t] = ((uint64_t)b * L + (r < r_hi ? r : r_lo)) * (uint64_t)L;
-                alo[t] = arow[t] + c_lo;
-                ahi[t] = r < r_hi ? arow[t] + c_hi : 0;  // rows past r_hi: nothing
-                a0[t] = (alo[t] & ~(uint64_t)15) + 16u * lane;
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const uint64_t a = a0[t] + 1024u * k;
-                    u[t][k] = make_uint4(0u, 0u, 0u, 0u);
-                    if (a < ahi[t] && a + 16 <= total)
-                        u[t][k] = *reinterpret_cast<const uint4 *>(mask + a);
-                }
+        // kRows rows per wave in flight, all their loads issued before any is
+        // examined: wave w takes rows w kRows .. w kRows + kRows - 1 of each
+        // group of kRows nw rows of the band.  A row's window of at most 1024
+        // columns, aligned down to 16 bytes in memory (the mask is), spans at
+        // most 65 chunks: lane l takes chunk l of every row, and lane t the
+        // 65th chunk of row t.  A chunk may run past its row into the next
+        // one (the window masks those bytes out); only past the last row of
+        // the whole mask is it read byte by byte (bytes past the end 0).
+        constexpr int kRows = 8;
+        const uint8_t *last_row = mask + ((uint64_t)gridDim.y * L - 1) * (uint64_t)L;
+        auto row_ptr = [&](int r) { return mask + ((uint64_t)b * L + r) * (uint64_t)L; };
+        // First chunk of row p's window, relative to the row's first byte.
+        auto first = [&](const uint8_t *rp) {
+            return c_lo - (int)(reinterpret_cast<uintptr_t>(rp + c_lo) & 15u);
+        };
+        auto fetch = [&](const uint8_t *rp, int a, int hi) {
+            uint4 u = make_uint4(0u, 0u, 0u, 0u);
+            if (a < hi && (rp != last_row || a + 16 <= L)) u = *reinterpret_cast<const uint4 *>(rp + a);
+            return u;
+        };
+        auto examine = [&](uint4 v, const uint8_t *rp, int a, int hi) {
+            if (a >= hi) return;
+            if (rp == last_row && a + 16 > L) {
+                uint8_t bb[16];
+                for (int e = 0; e < 16; ++e) bb[e] = (a + e < L) ? rp[a + e] : 0;
+                v = *reinterpret_cast<const uint4 *>(bb);
             }
+            chunk(v, a, c_lo, hi);
+        };
+        for (int rb = r_lo + kRows * wave; rb < r_hi; rb += kRows * nw) {
+            uint4 u[kRows];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < kRows; ++t) {
+                const int r = rb + t;
+                const uint8_t *rp = row_ptr(r < r_hi ? r : r_lo);
+                u[t] = fetch(rp, first(rp) + 16 * lane, r < r_hi ? c_hi : -16);
+            }
+            // The 65th chunk of row rb + lane (rows past r_hi: nothing).
+            const int rx = rb + lane;
+            const uint8_t *rpx = row_ptr(rx < r_hi ? rx : r_lo);
+            const int ax = first(rpx) + 1024, hix = lane < kRows && rx < r_hi ? c_hi : -16;
+            const uint4 ux = fetch(rpx, ax, hix);
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const uint64_t a = a0[t] + 1024u * k;
-                    if (a >= ahi[t]) continue;
-                    uint4 v = u[t][k];
-                    if (a + 16 > total) {
-                        uint8_t bb[16];
-                        for (int e = 0; e < 16; ++e) bb[e] = (a + e < total) ? mask[a + e] : 0;
-                        v = *reinterpret_cast<const uint4 *>(bb);
-                    }
-                    chunk(v, a, arow[t], alo[t], ahi[t]);
-                }
+            for (int t = 0; t < kRows; ++t) {
+                const int r = rb + t;
+                const uint8_t *rp = row_ptr(r < r_hi ? r : r_lo);
+                examine(u[t], rp, first(rp) + 16 * lane, r < r_hi ? c_hi : -16);
+            }
+            examine(ux, rpx, ax, hix);
         }
     }
     if (bits) atomicOr(&flags, bits);
@@ -198,7 +212,7 @@ hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask,
     const int tiles_per_group = 1024 / block_k;  // 8, 16 or 32 tiles: 1 KiB of each row
     const int groups = (Tk + tiles_per_group - 1) / tiles_per_group;
     hipLaunchKernelGGL(blockmask_scan_kernel, dim3((unsigned)(Tq * groups), (unsigned)B),
-                       dim3(256), 0, stream, seq_lens, mask, L, block_q, bk_shift, Tq, Tk,
+                       dim3(kScanThreads), 0, stream, seq_lens, mask, L, block_q, bk_shift, Tq, Tk,
                        tiles_per_group, groups, out);
     return hipGetLastError();
 }
