@@ -463,8 +463,6 @@ __device__ __forceinline__ bf16x4 pack4(float x0, float x1, float x2, float x3) 
     return r;
 }
 
-// sigma(s) with s = acc * scale + beta, evaluated as 1 / (1 + 2^u) where
-// u = acc * c1 + c0, c1 = -scale * log2(e), c0 = -beta * log2(e).
 // Sigmoid weight of one score.  The MFMA operand held in registers was
 // scaled by -scale * log2(e) beforehand (scale8), so the accumulator is
 // already u = -scale * (q . k) * log2(e), and with C = exp(-b):
