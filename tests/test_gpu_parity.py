@@ -76,6 +76,25 @@ def test_blockmask_arbitrary_mask_bitexact(va, L, bq, bk, density):
     np.testing.assert_array_equal(got, oracle.blockmask(n, mask, L, bq, bk))
 
 
+@pytest.mark.parametrize("L,bk", [(77, 32), (1031, 32), (1031, 128)])
+def test_blockmask_mask_end_of_array(va, L, bk):
+    """The last row of the whole mask array, its window unaligned (L is not a
+    multiple of 16) and its only non-zero bytes in its last 16: the 16-byte
+    chunk that would run past the array's end is read byte by byte, and a
+    1 KiB window of an unaligned row takes a 65th chunk."""
+    B = 3
+    n = np.array([L, 5, L], np.int32)
+    mask = np.zeros((B, L, L), np.uint8)
+    mask[B - 1, L - 1, L - 3] = 1
+    mask[B - 1, L - 1, L - 1] = 1
+    mask[0, L - 1, min(1023, L - 1)] = 1  # the end of a 1 KiB window in an unaligned row
+    say(f"blockmask end of array L={L} bk={bk}")
+    got = _bm(va, to_gpu(n, torch.int32), L, 32, bk, to_gpu(mask, torch.uint8)).cpu().numpy()
+    want = oracle.blockmask(n, mask, L, 32, bk)
+    np.testing.assert_array_equal(got, want)
+    assert want[B - 1, -1, -1] & 1 and int((want[B - 1] & 1).sum()) == 1
+
+
 def test_blockmask_long_documents_full_size(va):
     w = syn.long_packed_docs(tensors=())
     say(f"blockmask {w.name} L={w.L}")
