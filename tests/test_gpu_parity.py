@@ -33,7 +33,11 @@ def _inputs(seed, B, H, L, d, seq_lens, names=("q", "k", "v")):
 
 
 def _bm(va, n_gpu, L, bq, bk, mask_gpu=None, key_range=None):
-    out = va.blockmask_build(n_gpu, L, bq, bk, mask=mask_gpu, key_range=key_range)
+    """The block matrix, built into a buffer filled with 0xAA first, so an
+    entry the builder leaves unwritten shows."""
+    shape = (n_gpu.shape[0], -(-L // bq), -(-L // bk))
+    out = torch.full(shape, 0xAA, dtype=torch.uint8, device=n_gpu.device)
+    va.blockmask_build(n_gpu, L, bq, bk, mask=mask_gpu, key_range=key_range, out=out)
     torch.cuda.synchronize()
     return out
 
@@ -72,6 +76,20 @@ def test_blockmask_arbitrary_mask_bitexact(va, L, bq, bk, density):
     mask = (rng.random((B, L, L)) < density).astype(np.uint8)
     mask[0, L - 1, L - 1] = 1  # corner of the clipped last tile
     say(f"blockmask mask L={L} bq={bq} bk={bk}")
+    got = _bm(va, to_gpu(n, torch.int32), L, bq, bk, to_gpu(mask, torch.uint8)).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.blockmask(n, mask, L, bq, bk))
+
+
+@pytest.mark.parametrize("B,L,bq,bk", [(70, 100, 32, 32), (131, 1100, 128, 64)])
+def test_blockmask_mask_many_entries(va, B, L, bq, bk):
+    """More than 64 batch entries (the scan finds each workgroup's band over
+    several 64-entry steps), lengths from 0 to L: every entry written, the
+    units that read and those that only write zeros."""
+    rng = np.random.default_rng(B + L)
+    n = rng.integers(0, L + 1, size=B).astype(np.int32)
+    n[:3] = [0, L, 1]
+    mask = (rng.random((B, L, L)) < 0.002).astype(np.uint8)
+    say(f"blockmask mask B={B} L={L} bq={bq} bk={bk}")
     got = _bm(va, to_gpu(n, torch.int32), L, bq, bk, to_gpu(mask, torch.uint8)).cpu().numpy()
     np.testing.assert_array_equal(got, oracle.blockmask(n, mask, L, bq, bk))
 
