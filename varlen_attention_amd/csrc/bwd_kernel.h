@@ -686,11 +686,12 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
 }
 
 // ---------------------------------------------------------------- kernels
-// Waves per SIMD the register allocation must allow.  The unmasked sigmoid
-// kernels at d = 64 need about 168 VGPRs: held to that, three waves share a
-// SIMD (LDS allows three workgroups per CU even in the one-launch kernel).
+// Waves per SIMD the register allocation must allow.  The unmasked kernels
+// at d = 64 need about 168 VGPRs (the softmax variants a few more, spilled):
+// held to that, three waves share a SIMD (LDS allows three workgroups per CU
+// even in the one-launch kernel).
 template <int D, int VARIANT, int MASK>
-constexpr int kBwdWavesPerSimd = D == 64 && VARIANT == kSigmoid && MASK == kMaskNone ? 3 : 2;
+constexpr int kBwdWavesPerSimd = D == 64 && MASK == kMaskNone ? 3 : 2;
 
 // LIST: built for a schedule (work items and kept-entry lists from it).
 template <int D, int NW, int VARIANT, int MASK, int C, bool LIST>
