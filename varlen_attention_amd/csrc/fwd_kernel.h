@@ -101,17 +101,21 @@ constexpr float kLazyRescale = 8.0f;
 // hold two Q operands and two output accumulators (192 registers before the
 // loop's own): such waves get the whole register file.  One unmasked map at
 // d = 64 is held to 128 registers, four waves: the softmax variants would
-// otherwise take about 138 and run three (measured: 3 % slower).
-template <int D, int VARIANT, int MASK>
+// otherwise take about 138 and run three (3 % slower).  One map at d = 128
+// with 32-key steps is held to 168, three waves: the softmax variants would
+// otherwise take up to 204 and run two (15 % slower with key ranges).
+template <int D, int VARIANT, int MASK, int KB>
 constexpr int kFwdWavesPerSimd =
-    VARIANT == kDiff && D == 128 ? 1
-                                 : (D == 64 && VARIANT != kDiff && MASK == kMaskNone ? 4 : 2);
+    VARIANT == kDiff && D == 128
+        ? 1
+        : (D == 64 && VARIANT != kDiff && MASK == kMaskNone ? 4
+                                                              : (D == 128 && KB == 1 ? 3 : 2));
 
 // R: block-mask rows per workgroup (BQ / block_q); wave w follows row
 // w * R / NW, so smaller block rows keep four waves per workgroup.
 // LIST: built for a schedule (work items and kept-entry lists from it).
 template <int D, int VARIANT, int NW, int KB, int MASK, int R, bool LIST>
-__global__ void __launch_bounds__(64 * NW, (kFwdWavesPerSimd<D, VARIANT, MASK>))
+__global__ void __launch_bounds__(64 * NW, (kFwdWavesPerSimd<D, VARIANT, MASK, KB>))
 fwd_kernel(const AttnParams p) {
     constexpr bool MASKED = MASK != kMaskNone;
     // Differential attention runs two softmax maps (their own Q, K, running
@@ -503,11 +507,10 @@ hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
     constexpr bool kNarrow = VARIANT == kDiff && D == 128;
     constexpr int NW = 4, BQ = 32 * NW;
     const int rows = BQ / p.block_q;  // block-mask rows per workgroup: 1, 2 or 4
-    // One map at d = 128 also visits 32 keys at a time, except under a dense
-    // mask: 64-key steps hold about 210 VGPRs (two waves per SIMD), 32-key
-    // steps about 170 (three).  A dense mask's words are staged per step, and
-    // at half the step that staging costs more than the third wave gains.
-    const int kb = p.block_k >= 64 && !kNarrow && (D == 64 || p.mask != nullptr) ? 2 : 1;
+    // One map at d = 128 also visits 32 keys at a time: 64-key steps hold
+    // about 210 VGPRs (two waves per SIMD), 32-key steps are held to 168
+    // (three).
+    const int kb = p.block_k >= 64 && !kNarrow && D == 64 ? 2 : 1;
     const dim3 grid = tile_grid((p.L + BQ - 1) / BQ, p.B, p.H);
     dim3 block(64 * NW);
 #define SIGATTN_FWD_LAUNCH(KB_, MASK_, R_)                                                         \
