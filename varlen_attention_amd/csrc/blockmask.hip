@@ -38,6 +38,16 @@ blockmask_padding_kernel(const int32_t *__restrict__ seq_lens, int L, int bq, in
 // flags.  Offsets inside a row are 32-bit and relative to the row's first
 // byte; each row keeps its own 64-bit pointer.
 constexpr int kScanThreads = 256;
+
+// A 16-byte load marked non-temporal: the scan reads each mask byte once, and
+// its lines then neither displace what the caches hold nor, arriving in
+// caches full of an earlier kernel's dirty lines, force their write-back
+// (with the mask evicted: 66.7 -> 44.1 us for the long-document mask).
+__device__ __forceinline__ uint4 load16_stream(const uint8_t *p) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 __global__ void __launch_bounds__(kScanThreads)
 blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict__ mask,
                       int L, int bq, int bk_shift, int Tq, int Tk, int tiles_per_group,
@@ -112,7 +122,7 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
         };
         auto fetch = [&](const uint8_t *rp, int a, int hi) {
             uint4 u = make_uint4(0u, 0u, 0u, 0u);
-            if (a < hi && (rp != last_row || a + 16 <= L)) u = *reinterpret_cast<const uint4 *>(rp + a);
+            if (a < hi && (rp != last_row || a + 16 <= L)) u = load16_stream(rp + a);
             return u;
         };
         auto examine = [&](uint4 v, const uint8_t *rp, int a, int hi) {
