@@ -119,10 +119,12 @@ typedef struct {
  * sigattn_status: INVALID_ARG (B, H or L <= 0), UNSUPPORTED (block size,
  * sizes beyond the limits of sigattn_shape).  48 bytes per 128-row tile of
  * every (batch entry, head) (the (batch entry, head) pairs rounded up to a
- * multiple of 8), plus 4 * B * ceil(L / 128) * (Tq + Tk + 2).
+ * multiple of 8), plus 4 * B * ceil(L / 128) * (Tq + Tk + 2); with
+ * dense_mask != 0 (a schedule for a batch with an element mask), rounded up
+ * to 16 bytes plus 4 * B * L * ceil(L / 32) for the mask packed to bits.
  */
 int64_t sigattn_schedule_bytes(int32_t B, int32_t H, int32_t L, int32_t block_q,
-                               int32_t block_k);
+                               int32_t block_k, int32_t dense_mask);
 
 /*
  * blockmask_build - binary block matrix of one batch (Binary Block Masking,
@@ -140,8 +142,8 @@ int64_t sigattn_schedule_bytes(int32_t B, int32_t H, int32_t L, int32_t block_q,
  *   block_mask  [device] uint8 [B, Tq, Tk] output, Tq = ceil(L / block_q),
  *               Tk = ceil(L / block_k); every entry is written with 0, 1 or 3.
  *   schedule    [device] output of schedule_bytes bytes (at least
- *               sigattn_schedule_bytes(B, H, L, block_q, block_k)), 16-byte
- *               aligned, or NULL for none.
+ *               sigattn_schedule_bytes(B, H, L, block_q, block_k,
+ *               mask != NULL)), 16-byte aligned, or NULL for none.
  * Bit 0 of entry (b, i, j) is the binary block matrix: 1 iff some r in
  * [i*block_q, min((i+1)*block_q, L)) and c in [j*block_k, min((j+1)*block_k, L))
  * is valid (definition above without the block-mask term).  Bit 1 marks a full
@@ -165,10 +167,16 @@ int64_t sigattn_schedule_bytes(int32_t B, int32_t H, int32_t L, int32_t block_q,
  *     block-mask entries that some block row of the group keeps, in
  *     increasing order, with the rows that keep them and mark them full; per
  *     128-key group the same down the block columns.
- * Passing it to the attention calls (with this block_mask) spares every
- * workgroup the ranking of the lengths and the scan of block-mask lines; the
- * results are bit for bit those without it.  It stays valid while seq_lens,
- * the mask, H and the block sizes are unchanged, and serves every layer.
+ *   - with a mask: the mask packed to one bit per entry (the scan that
+ *     builds the block mask reads every valid byte anyway), which the
+ *     attention kernels then read instead of the mask's bytes: 4 bytes per
+ *     32 entries, one conversion for all heads and layers.
+ * Passing it to the attention calls (with this block_mask, and the same mask)
+ * spares every workgroup the ranking of the lengths and the scan of
+ * block-mask lines; the results are bit for bit those without it.  It stays
+ * valid while seq_lens, the mask, H and the block sizes are unchanged, and
+ * serves every layer.  A schedule built without a mask must not be passed
+ * together with a mask (it holds no packed mask).
  * Errors: INVALID_ARG (null seq_lens/block_mask, B or L <= 0, both mask and
  * key_range, with a schedule: H <= 0 or schedule_bytes too small),
  * UNSUPPORTED (block size not 32/64/128, sizes beyond the limits), ALIGNMENT
@@ -283,7 +291,7 @@ int sigattn_bwd_dq(const sigattn_shape *shape, const void *q, const void *k, con
  * calls that overlap in time on one GPU (other streams, other host threads)
  * race and must be ordered by the caller; calls in one stream are ordered.
  * Errors: as sigattn_fwd; INVALID_ARG for a NULL block_mask; UNSUPPORTED when
- * the schedule (sigattn_schedule_bytes(B, H, L, block_q, block_k)) exceeds
+ * the schedule (sigattn_schedule_bytes(B, H, L, block_q, block_k, 0)) exceeds
  * SIGATTN_NOALLOC_SCRATCH_BYTES; LAUNCH also when the array's address cannot
  * be obtained.
  */

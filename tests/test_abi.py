@@ -113,7 +113,7 @@ def test_noalloc_forward_argument_errors(lib):
     assert fwd0(_shape(va, d=96)) == va.ERR_UNSUPPORTED
     # B32 H64 L65536: a schedule of ~50 MB, beyond the 8 MiB the library holds.
     big = _shape(va, B=32, H=64, L=65536, stride_b=64 * 65536 * 64, stride_h=65536 * 64)
-    assert lib.sigattn_schedule_bytes(32, 64, 65536, 128, 128) > va.NOALLOC_SCRATCH_BYTES
+    assert lib.sigattn_schedule_bytes(32, 64, 65536, 128, 128, 0) > va.NOALLOC_SCRATCH_BYTES
     assert fwd0(big) == va.ERR_UNSUPPORTED
     assert b"holds" in lib.sigattn_last_error()
     hdr = open(HEADER).read()
@@ -202,29 +202,39 @@ def test_blockmask_argument_errors(lib):
     assert bmb(mask=FAKE, kr=FAKE) == va.ERR_INVALID_ARG
     assert bmb(kr=ctypes.c_void_p(0x10004)) == va.ERR_ALIGNMENT
     # With a schedule: H > 0, a 16-byte aligned buffer of at least the size.
-    need = lib.sigattn_schedule_bytes(2, 3, 100, 32, 32)
+    need = lib.sigattn_schedule_bytes(2, 3, 100, 32, 32, 0)
     assert need > 0
     assert bmb(H=0, sched=FAKE, nbytes=need) == va.ERR_INVALID_ARG
     assert bmb(H=3, sched=FAKE, nbytes=need - 1) == va.ERR_INVALID_ARG
     assert b"needed" in lib.sigattn_last_error()
     assert bmb(H=3, sched=ctypes.c_void_p(0x10008), nbytes=need) == va.ERR_ALIGNMENT
+    # A batch with a mask needs the larger schedule (it carries the packed mask).
+    need_m = lib.sigattn_schedule_bytes(2, 3, 100, 32, 32, 1)
+    assert need_m > need
+    assert bmb(mask=FAKE, H=3, sched=FAKE, nbytes=need) == va.ERR_INVALID_ARG
+    assert b"needed" in lib.sigattn_last_error()
     assert bmb(B=8, H=1, L=128 << 20, sched=FAKE, nbytes=1 << 40) == va.ERR_UNSUPPORTED
 
 
 def test_schedule_bytes_follow_the_layout(lib):
     """48 bytes per 128-row tile slot of the two item arrays ((batch entry,
     head) pairs rounded up to 8), plus the count and entry words of every
-    query and key group."""
+    query and key group; for a batch with a mask, rounded up to 16 bytes plus
+    ceil(L / 32) words per row of the packed mask."""
     import varlen_attention_amd as va
     for B, H, L, bq, bk in ((32, 8, 1584, 128, 128), (3, 5, 100, 32, 64), (1, 1, 1, 64, 32)):
         G = -(-L // 128)
         Tq, Tk = -(-L // bq), -(-L // bk)
         slots = 8 * (-(-(B * H) // 8)) * G
-        assert lib.sigattn_schedule_bytes(B, H, L, bq, bk) == \
-            16 * 3 * slots + 4 * B * G * (Tk + 1) + 4 * B * G * (Tq + 1)
-        assert va.schedule_bytes(B, H, L, bq, bk) == lib.sigattn_schedule_bytes(B, H, L, bq, bk)
-    assert lib.sigattn_schedule_bytes(0, 1, 10, 32, 32) == va.ERR_INVALID_ARG
-    assert lib.sigattn_schedule_bytes(1, 1, 10, 48, 32) == va.ERR_UNSUPPORTED
+        base = 16 * 3 * slots + 4 * B * G * (Tk + 1) + 4 * B * G * (Tq + 1)
+        assert lib.sigattn_schedule_bytes(B, H, L, bq, bk, 0) == base
+        assert lib.sigattn_schedule_bytes(B, H, L, bq, bk, 1) == \
+            -(-base // 16) * 16 + 4 * B * L * -(-L // 32)
+        assert va.schedule_bytes(B, H, L, bq, bk) == base
+        assert va.schedule_bytes(B, H, L, bq, bk, dense_mask=True) == \
+            lib.sigattn_schedule_bytes(B, H, L, bq, bk, 1)
+    assert lib.sigattn_schedule_bytes(0, 1, 10, 32, 32, 0) == va.ERR_INVALID_ARG
+    assert lib.sigattn_schedule_bytes(1, 1, 10, 48, 32, 0) == va.ERR_UNSUPPORTED
 
 
 def test_binding_rejects_cpu_tensors():

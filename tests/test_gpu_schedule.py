@@ -32,6 +32,26 @@ def _window_ranges(rng, B, L):
     return kr
 
 
+def _check_packed_mask(buf, mask, n, B, H, L, bq, bk):
+    """The mask packed to bits at the end of the schedule (after the lists,
+    at a 16-byte boundary): bit t of word w of row r is entry (r, 32 w + t).
+    Compared with the mask for rows and keys below n (the rest is
+    unspecified)."""
+    G = -(-L // 128)
+    Tq, Tk = -(-L // bq), -(-L // bk)
+    slots1 = 8 * (-(-(B * H) // 8)) * G
+    off = -(-(16 * 3 * slots1 + 4 * B * G * (Tk + 1 + Tq + 1)) // 16) * 16
+    W = -(-L // 32)
+    words = np.frombuffer(buf[off:off + 4 * B * L * W].tobytes(), dtype=np.uint32)
+    words = words.reshape(B, L, W)
+    for b in range(B):
+        nb = int(np.clip(n[b], 0, L))
+        if nb == 0:
+            continue
+        got = np.unpackbits(words[b, :nb].view(np.uint8), axis=1, bitorder="little")[:, :nb]
+        np.testing.assert_array_equal(got, (mask[b, :nb, :nb] != 0).astype(np.uint8))
+
+
 SCHED_CASES = [
     # B, H, L, block_q, block_k, mask form
     (32, 8, 1584, 128, 128, "none"),   # the single-cell shapes
@@ -63,7 +83,9 @@ def test_schedule_matches_oracle(va, B, H, L, bq, bk, form):
     kr_gpu = None if kr is None else to_gpu(kr, torch.int32)
     bm, sched = va.blockmask_build(n_gpu, L, bq, bk, mask=m_gpu, key_range=kr_gpu, heads=H)
     torch.cuda.synchronize()
-    assert sched.numel() == va.schedule_bytes(B, H, L, bq, bk)
+    assert sched.numel() == va.schedule_bytes(B, H, L, bq, bk, dense_mask=mask is not None)
+    if mask is not None:
+        _check_packed_mask(sched.cpu().numpy(), mask, n, B, H, L, bq, bk)
     want_bm = oracle.blockmask(n, mask, L, bq, bk, key_range=kr)
     np.testing.assert_array_equal(bm.cpu().numpy(), want_bm)
     got = decode_schedule(sched.cpu().numpy(), B, H, L, bq, bk)
@@ -80,6 +102,8 @@ OUT_CASES = [
     (64, 290, 128, 32, SOFTMAX1, 0, "range"),
     (128, 190, 64, 64, SOFTMAX, 1, "range"),
     (64, 400, 32, 32, SIGMOID, 1, "dense"),
+    (64, 333, 64, 64, SOFTMAX, 0, "dense"),     # rows not 16-byte aligned
+    (128, 333, 128, 128, SOFTMAX1, 0, "dense"),
 ]
 
 
@@ -123,21 +147,26 @@ def test_outputs_identical_with_schedule(va, d, L, bq, bk, variant, bias, form):
     assert torch.equal(res[1][1].view(torch.int16), res[1][6].view(torch.int16))
 
 
-def test_differential_identical_with_schedule(va):
+@pytest.mark.parametrize("form", ["none", "dense"])
+def test_differential_identical_with_schedule(va, form):
     B, H, L, d = 5, 2, 270, 64
     n = np.array([270, 1, 0, 200, 129], np.int32)
     rng = np.random.default_rng(5)
     q1, k1, q2, k2, v, do = (syn.random_tensor(rng, (B, H, L, d)) for _ in range(6))
-    say("schedule differential")
+    m_gpu = None
+    if form == "dense":
+        m_gpu = to_gpu((rng.random((B, L, L)) < 0.5).astype(np.uint8), torch.uint8)
+    say(f"schedule differential form={form}")
     n_gpu = to_gpu(n, torch.int32)
-    bm, sched = va.blockmask_build(n_gpu, L, 64, 64, heads=H)
+    bm, sched = va.blockmask_build(n_gpu, L, 64, 64, mask=m_gpu, heads=H)
     g = [to_gpu_bf16(t) for t in (q1, k1, q2, k2, v, do)]
     res = []
     for s in (None, sched):
         o, l1, l2, o1, o2 = va.sigattn_diff_fwd(*g[:5], n_gpu, 0.6, block_mask=bm, block_q=64,
-                                                block_k=64, return_maps=True, schedule=s)
+                                                block_k=64, return_maps=True, schedule=s,
+                                                mask=m_gpu)
         grads = va.sigattn_diff_bwd(*g, o1, o2, l1, l2, n_gpu, 0.6, block_mask=bm, block_q=64,
-                                    block_k=64, schedule=s)
+                                    block_k=64, schedule=s, mask=m_gpu)
         res.append([o, o1, o2, *grads])
     torch.cuda.synchronize()
     for a, b_ in zip(*res):

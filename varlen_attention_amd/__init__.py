@@ -66,7 +66,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     I = ctypes.c_int32
     S = ctypes.POINTER(Shape)
     I64 = ctypes.c_int64
-    lib.sigattn_schedule_bytes.argtypes = [I, I, I, I, I]
+    lib.sigattn_schedule_bytes.argtypes = [I, I, I, I, I, I]
     lib.sigattn_schedule_bytes.restype = I64
     lib.blockmask_build.argtypes = [P, P, P, I, I, I, I, I, P, P, I64, P]
     lib.blockmask_build.restype = ctypes.c_int
@@ -162,20 +162,31 @@ def _key_range(key_range, B, L):
             raise ValueError("key_range must be a contiguous int32 [B, L, 2] tensor")
 
 
-def schedule_bytes(B: int, H: int, L: int, block_q: int = 128, block_k: int = 128) -> int:
-    """Bytes of the schedule buffer blockmask_build fills (sigattn_schedule_bytes)."""
-    nbytes = load_library().sigattn_schedule_bytes(B, H, L, block_q, block_k)
+def schedule_bytes(B: int, H: int, L: int, block_q: int = 128, block_k: int = 128,
+                   dense_mask: bool = False) -> int:
+    """Bytes of the schedule buffer blockmask_build fills (sigattn_schedule_bytes);
+    ``dense_mask``: for a batch with an element mask (the schedule then also
+    holds the mask packed to bits)."""
+    nbytes = load_library().sigattn_schedule_bytes(B, H, L, block_q, block_k, int(dense_mask))
     _check(int(nbytes) if nbytes < 0 else OK)
     return int(nbytes)
 
 
-def _schedule(schedule, block_mask):
+def _schedule(schedule, block_mask, mask=None, dims=None):
+    """Checks a schedule argument; with a mask (dims = B, H, L, block_q,
+    block_k) the schedule must hold the packed mask, which only a schedule
+    built with that mask does."""
     if schedule is not None:
         _need(schedule, "schedule", torch.uint8)
         if schedule.dim() != 1 or not schedule.is_contiguous():
             raise ValueError("schedule must be a contiguous 1-D uint8 tensor")
         if block_mask is None:
             raise ValueError("a schedule needs the block mask it was built with")
+        if mask is not None and dims is not None:
+            need = schedule_bytes(*dims, dense_mask=True)
+            if schedule.numel() < need:
+                raise ValueError(f"with a mask the schedule must be one built with it "
+                                 f"({need} bytes, got {schedule.numel()})")
 
 
 def blockmask_build(seq_lens: torch.Tensor, L: int, block_q: int = 128, block_k: int = 128,
@@ -209,7 +220,7 @@ def blockmask_build(seq_lens: torch.Tensor, L: int, block_q: int = 128, block_k:
         raise ValueError("building a schedule needs the number of heads")
     nbytes = 0
     if heads is not None:
-        nbytes = schedule_bytes(B, heads, L, block_q, block_k)
+        nbytes = schedule_bytes(B, heads, L, block_q, block_k, dense_mask=mask is not None)
         if schedule is None:
             schedule = torch.empty(nbytes, dtype=torch.uint8, device=seq_lens.device)
         _schedule(schedule, out)
@@ -255,7 +266,7 @@ def sigattn_fwd(q, k, v, seq_lens, block_mask=None, mask=None, bias=BIAS_LOG_SEQ
         if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
             raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
     _key_range(key_range, B, L)
-    _schedule(schedule, block_mask)
+    _schedule(schedule, block_mask, mask, (B, H, L, block_q, block_k))
     shape = _shape(q, out.stride(), scale, block_q, block_k)
     lib = load_library()
     _check(lib.sigattn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
@@ -335,7 +346,7 @@ def _bwd_args(q, k, v, dout, seq_lens, block_mask, mask, grads, block_q, block_k
         if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
             raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
     _key_range(key_range, B, L)
-    _schedule(schedule, block_mask)
+    _schedule(schedule, block_mask, mask, (B, H, L, block_q, block_k))
     return outs
 
 
@@ -434,7 +445,7 @@ def sigattn_diff_fwd(q1, k1, q2, k2, v, seq_lens, lam: float, block_mask=None, m
             _need(om, "o1/o2", torch.bfloat16)
             if tuple(om.shape) != tuple(out.shape) or om.stride() != out.stride():
                 raise ValueError("o1 and o2 must have out's shape and strides")
-    _schedule(schedule, block_mask)
+    _schedule(schedule, block_mask, mask, (B, H, L, block_q, block_k))
     shape = _shape(q1, out.stride(), scale, block_q, block_k)
     _check(load_library().sigattn_diff_fwd(
         ctypes.byref(shape), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v),
@@ -479,7 +490,7 @@ def sigattn_diff_bwd(q1, k1, q2, k2, v, dout, o1, o2, lse1, lse2, seq_lens, lam:
         want = (B, num_tiles(L, block_q), num_tiles(L, block_k))
         if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
             raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape {want}")
-    _schedule(schedule, block_mask)
+    _schedule(schedule, block_mask, mask, (B, H, L, block_q, block_k))
     shape = _shape(q1, outs[0].stride(), scale, block_q, block_k)
     _check(load_library().sigattn_diff_bwd(
         ctypes.byref(shape), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(dout),

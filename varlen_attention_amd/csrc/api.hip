@@ -168,8 +168,12 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
     p->variant = variant;
     if (schedule != nullptr) {
         const sigattn::ScheduleLayout lay =
-            sigattn::schedule_layout(s->B, s->H, s->L, s->block_q, s->block_k);
+            sigattn::schedule_layout(s->B, s->H, s->L, s->block_q, s->block_k, mask != nullptr);
         const uint8_t *base = static_cast<const uint8_t *>(schedule);
+        if (mask != nullptr) {  // built with this mask: it holds the mask's bits
+            p->mask_bits = reinterpret_cast<const uint32_t *>(base + lay.bits);
+            p->bits_w = lay.words_per_row;
+        }
         p->items1 = reinterpret_cast<const int4 *>(base + lay.items1);
         p->items2 = reinterpret_cast<const int4 *>(base + lay.items2);
         p->qlist = reinterpret_cast<const uint32_t *>(base + lay.qlists);
@@ -185,7 +189,7 @@ int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inp
 extern "C" {
 
 int64_t sigattn_schedule_bytes(int32_t B, int32_t H, int32_t L, int32_t block_q,
-                               int32_t block_k) {
+                               int32_t block_k, int32_t dense_mask) {
     if (B <= 0 || H <= 0 || L <= 0)
         return fail(SIGATTN_ERR_INVALID_ARG, "B, H and L must be positive");
     if (B > 65535 || H > 65535) return fail(SIGATTN_ERR_UNSUPPORTED, "B and H must be at most 65535");
@@ -195,7 +199,7 @@ int64_t sigattn_schedule_bytes(int32_t B, int32_t H, int32_t L, int32_t block_q,
     if (max_workgroups(B, H, L) >= SIGATTN_MAX_WORKGROUPS)
         return fail(SIGATTN_ERR_UNSUPPORTED, "B * H * L too large for one launch");
     ok();
-    return sigattn::schedule_layout(B, H, L, block_q, block_k).bytes;
+    return sigattn::schedule_layout(B, H, L, block_q, block_k, dense_mask != 0).bytes;
 }
 
 int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t *key_range,
@@ -215,7 +219,7 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t 
     if (key_range != nullptr && (reinterpret_cast<uintptr_t>(key_range) & 7u) != 0)
         return fail(SIGATTN_ERR_ALIGNMENT, "key_range is not 8-byte aligned");
     if (schedule != nullptr) {
-        const int64_t need = sigattn_schedule_bytes(B, H, L, block_q, block_k);
+        const int64_t need = sigattn_schedule_bytes(B, H, L, block_q, block_k, mask != nullptr);
         if (need < 0) return (int)need;  // its message is set
         if (!aligned16(schedule))
             return fail(SIGATTN_ERR_ALIGNMENT, "schedule is not 16-byte aligned");
@@ -228,9 +232,14 @@ int blockmask_build(const int32_t *seq_lens, const uint8_t *mask, const int32_t 
         return launch_status(sigattn::launch_schedule(seq_lens, nullptr, B, H, L, block_q,
                                                       block_k, schedule, st, block_mask),
                              "blockmask_build");
-    const int rc = launch_status(
-        sigattn::launch_blockmask(seq_lens, mask, key_range, B, L, block_q, block_k, block_mask, st),
-        "blockmask_build");
+    uint32_t *bits = nullptr;  // with a mask, the schedule also carries it packed to bits
+    if (schedule != nullptr && mask != nullptr)
+        bits = reinterpret_cast<uint32_t *>(
+            static_cast<uint8_t *>(schedule) +
+            sigattn::schedule_layout(B, H, L, block_q, block_k, true).bits);
+    const int rc = launch_status(sigattn::launch_blockmask(seq_lens, mask, key_range, B, L, block_q,
+                                                           block_k, block_mask, st, bits),
+                                 "blockmask_build");
     if (rc != SIGATTN_OK || schedule == nullptr) return rc;
     return launch_status(sigattn::launch_schedule(seq_lens, block_mask, B, H, L, block_q, block_k,
                                                   schedule, st),

@@ -10,7 +10,10 @@
 // With an element mask the builder is one HBM scan of the valid rectangle
 // [0, n) x [0, n) of each mask: a workgroup owns a band of bq rows and a group
 // of key tiles, so it writes its outputs alone (no atomics to global memory),
-// and each wave keeps the 16-byte loads of eight rows in flight.
+// and each wave keeps the 16-byte loads of eight rows in flight.  With a
+// schedule, the same scan also packs the mask to one bit per entry for the
+// attention kernels (32 keys per 4-byte load instead of 32 bytes), which
+// every head then reads.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -48,11 +51,22 @@ __device__ __forceinline__ uint4 load16_stream(const uint8_t *p) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+// Rows a wave scans at once.
+constexpr int kScanRows = 8;
+
+// bits_out (or null): the mask packed to bits, W words per row, bit t of
+// word w the entry for key 32 w + t; each workgroup writes the words of its
+// band's rows below n that start inside its columns [c_lo, c_hi).  A wave
+// gathers its rows' bits in LDS (one 32-word line per row: 1 KiB of columns)
+// and stores whole words.
 __global__ void __launch_bounds__(kScanThreads)
 blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict__ mask,
                       int L, int bq, int bk_shift, int Tq, int Tk, int tiles_per_group,
-                      int groups, uint8_t *__restrict__ out) {
+                      int groups, uint8_t *__restrict__ out, uint32_t *__restrict__ bits_out,
+                      int W) {
     __shared__ uint32_t flags, zeros;  // per key tile: a valid element seen / an invalid one
+    __shared__ uint32_t line_bits[kScanThreads / 64][kScanRows][32];
     const int b = blockIdx.y;
     const int i = blockIdx.x / groups;
     const int g = blockIdx.x % groups;
@@ -67,13 +81,29 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
     const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: rows in SGPRs
     uint32_t bits = 0, zbits = 0;
+    // The 16 entries of columns [a, a + 16) (bit i: column a + i; those
+    // outside the scan's columns zero) ORed into a row's LDS line.
+    auto put = [&](uint32_t *line, int a, uint32_t v16) {
+        if (line == nullptr || v16 == 0u) return;
+        int pos = a - c_lo;
+        if (pos < 0) {  // the window's first chunk starts before c_lo: no bits there
+            v16 >>= -pos;
+            pos = 0;
+        }
+        const int wd = pos >> 5, sh = pos & 31;
+        atomicOr(&line[wd], v16 << sh);
+        const uint32_t spill = sh > 16 ? v16 >> (32 - sh) : 0u;
+        if (spill != 0u) atomicOr(&line[wd + 1], spill);  // a column below c_hi: wd + 1 < 32
+    };
     // One 16-byte chunk at offset a of its row (columns [lo, hi) of the
     // scan): non-zero bytes mark their tile kept, zero bytes not full.
-    auto chunk = [&](uint4 u, int a, int lo, int hi) {
+    auto chunk = [&](uint4 u, int a, int lo, int hi, uint32_t *line) {
         const uint32_t nz = u.x | u.y | u.z | u.w;
         const int s0 = a > lo ? a : lo, s1 = a + 16 < hi ? a + 16 : hi;  // in-range part
         const int t0 = (s0 >> bk_shift) - j0;
         const int t1 = ((s1 - 1) >> bk_shift) - j0;
+        const int s = s0 - a, e = s1 - a;  // in-range bytes [s, e)
+        const uint32_t range16 = ((1u << e) - 1u) & ~((1u << s) - 1u);
         if (nz == 0u) {  // every byte invalid
             zbits |= (1u << t0) | (1u << t1);
             return;
@@ -82,6 +112,7 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
                                    ((u.z - 0x01010101u) & ~u.z) | ((u.w - 0x01010101u) & ~u.w);
         if ((zero_byte & 0x80808080u) == 0u) {  // every byte valid: its tile(s) kept
             bits |= (1u << t0) | (1u << t1);
+            put(line, a, range16);
             return;
         }
         // Mixed chunk: one bit per byte (non-zero), bit-parallel.
@@ -93,8 +124,7 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
             const uint32_t m = (((w[q] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[q]) & 0x80808080u;
             nz16 |= (((m >> 7) * 0x00204081u) >> 21 & 0xfu) << (4 * q);
         }
-        const int s = s0 - a, e = s1 - a;  // in-range bytes [s, e)
-        const uint32_t range16 = ((1u << e) - 1u) & ~((1u << s) - 1u);
+        put(line, a, nz16 & range16);
         // Bytes before the start of tile t1 belong to tile t0.
         const int split = ((t1 + j0) << bk_shift) - a;
         const uint32_t first = t1 == t0 ? 0xffffu : (1u << split) - 1u;
@@ -113,7 +143,14 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
         // 65th chunk of row t.  A chunk may run past its row into the next
         // one (the window masks those bytes out); only past the last row of
         // the whole mask is it read byte by byte (bytes past the end 0).
-        constexpr int kRows = 8;
+        constexpr int kRows = kScanRows;
+        uint32_t(*lines)[32] = line_bits[wave];  // this wave's rows' lines
+        if (bits_out != nullptr) {
+#pragma unroll
+            for (int k = 0; k < kRows * 32 / 64; ++k) lines[(k * 64 + lane) >> 5][lane & 31] = 0u;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
         const uint8_t *last_row = mask + ((uint64_t)gridDim.y * L - 1) * (uint64_t)L;
         auto row_ptr = [&](int r) { return mask + ((uint64_t)b * L + r) * (uint64_t)L; };
         // First chunk of row p's window, relative to the row's first byte.
@@ -125,14 +162,14 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
             if (a < hi && (rp != last_row || a + 16 <= L)) u = load16_stream(rp + a);
             return u;
         };
-        auto examine = [&](uint4 v, const uint8_t *rp, int a, int hi) {
+        auto examine = [&](uint4 v, const uint8_t *rp, int a, int hi, int slot) {
             if (a >= hi) return;
             if (rp == last_row && a + 16 > L) {
                 uint8_t bb[16];
                 for (int e = 0; e < 16; ++e) bb[e] = (a + e < L) ? rp[a + e] : 0;
                 v = *reinterpret_cast<const uint4 *>(bb);
             }
-            chunk(v, a, c_lo, hi);
+            chunk(v, a, c_lo, hi, bits_out != nullptr ? lines[slot] : nullptr);
         };
         for (int rb = r_lo + kRows * wave; rb < r_hi; rb += kRows * nw) {
             uint4 u[kRows];
@@ -151,9 +188,25 @@ blockmask_scan_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__res
             for (int t = 0; t < kRows; ++t) {
                 const int r = rb + t;
                 const uint8_t *rp = row_ptr(r < r_hi ? r : r_lo);
-                examine(u[t], rp, first(rp) + 16 * lane, r < r_hi ? c_hi : -16);
+                examine(u[t], rp, first(rp) + 16 * lane, r < r_hi ? c_hi : -16, t);
             }
-            examine(ux, rpx, ax, hix);
+            examine(ux, rpx, ax, hix, lane < kRows ? lane : 0);
+            if (bits_out != nullptr) {
+                // This wave's lines are complete (its LDS operations run in
+                // order): store the words that start below c_hi, then clear.
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int k = 0; k < kRows * 32 / 64; ++k) {
+                    const int idx = k * 64 + lane, t = idx >> 5, wd = idx & 31;
+                    const int r = rb + t;
+                    if (r < r_hi && c_lo + 32 * wd < c_hi)
+                        bits_out[((int64_t)b * L + r) * W + (c_lo >> 5) + wd] = lines[t][wd];
+                    lines[t][wd] = 0u;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+            }
         }
     }
     if (bits) atomicOr(&flags, bits);
@@ -204,7 +257,7 @@ blockmask_range_kernel(const int32_t *__restrict__ seq_lens, const int32_t *__re
 
 hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask,
                             const int32_t *key_range, int B, int L, int block_q, int block_k,
-                            uint8_t *out, hipStream_t stream) {
+                            uint8_t *out, hipStream_t stream, uint32_t *bits_out) {
     const int Tq = (int)(((int64_t)L + block_q - 1) / block_q);
     const int Tk = (int)(((int64_t)L + block_k - 1) / block_k);
     if (key_range != nullptr) {
@@ -223,7 +276,7 @@ hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask,
     const int groups = (Tk + tiles_per_group - 1) / tiles_per_group;
     hipLaunchKernelGGL(blockmask_scan_kernel, dim3((unsigned)(Tq * groups), (unsigned)B),
                        dim3(kScanThreads), 0, stream, seq_lens, mask, L, block_q, bk_shift, Tq, Tk,
-                       tiles_per_group, groups, out);
+                       tiles_per_group, groups, out, bits_out, (int)(((int64_t)L + 31) / 32));
     return hipGetLastError();
 }
 

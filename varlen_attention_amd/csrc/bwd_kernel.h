@@ -287,7 +287,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     const bool k_valid = key < n;
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const MaskSource msrc = mask_source<MASK>(p.mask, p.key_range, b, L);
+    const MaskSource msrc = mask_source<MASK>(p, b);
     // Mask words: key kl of this wave's 32 is one bit of the word of each query row.
     const int mbit = key_bit<MASK>(kl);
     using Mask = MaskStager<MASK, BQ, BKV, NT, false>;
@@ -516,7 +516,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     const bool q_valid = qr < n;
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const MaskSource msrc = mask_source<MASK>(p.mask, p.key_range, b, L);
+    const MaskSource msrc = mask_source<MASK>(p, b);
     using Mask = MaskStager<MASK, BQ, BK, NT, true>;
     int mcls = kMixed;  // this wave's share of the current tile
     uint32_t *M0 = mbits, *M1 = mbits + Mask::kWords;
@@ -775,7 +775,13 @@ hipError_t launch_dkdv_d(const AttnParams &p, hipStream_t stream) {
 #define SIGATTN_DKDV_CASE(C_)                                                                  \
     if (cols == C_) {                                                                          \
         if (p.mask != nullptr) {                                                               \
-            SIGATTN_LIST_LAUNCH(bwd_dkdv_kernel, D, NW, VARIANT, kMaskDense, C_)               \
+            if (p.mask_bits != nullptr) {                                                  \
+                hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, VARIANT, kMaskBits, C_, true>), grid, \
+                                   block, 0, stream, p);                                   \
+            } else {                                                                   \
+                hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, VARIANT, kMaskDense, C_, false>),    \
+                                   grid, block, 0, stream, p);                             \
+            }               \
         } else if (p.key_range != nullptr) {                                                   \
             SIGATTN_LIST_LAUNCH(bwd_dkdv_kernel, D, NW, VARIANT, kMaskRange, C_)               \
         } else {                                                                               \
@@ -800,7 +806,13 @@ hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     if constexpr (D == 64 || KB_ == 1)                                                           \
     if (rows == R_ && kb == KB_) {                                                               \
         if (p.mask != nullptr) {                                                                 \
-            SIGATTN_LIST_LAUNCH(bwd_dq_kernel, D, NW, KB_, VARIANT, kMaskDense, R_)              \
+            if (p.mask_bits != nullptr) {                                                  \
+                hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KB_, VARIANT, kMaskBits, R_, true>),   \
+                                   grid, block, 0, stream, p);                             \
+            } else {                                                                   \
+                hipLaunchKernelGGL((bwd_dq_kernel<D, NW, KB_, VARIANT, kMaskDense, R_, false>), \
+                                   grid, block, 0, stream, p);                             \
+            }              \
         } else if (p.key_range != nullptr) {                                                     \
             SIGATTN_LIST_LAUNCH(bwd_dq_kernel, D, NW, KB_, VARIANT, kMaskRange, R_)              \
         } else {                                                                                 \
@@ -832,7 +844,13 @@ hipError_t launch_bwd_d(const AttnParams &p, hipStream_t stream) {
     if constexpr (D == 64 || KB_ == 1)                                                         \
     if (lines == R_ && kb == KB_) {                                                            \
         if (p.mask != nullptr) {                                                               \
-            SIGATTN_LIST_LAUNCH(bwd_kernel, D, NW, KB_, VARIANT, kMaskDense, R_)               \
+            if (p.mask_bits != nullptr) {                                                  \
+                hipLaunchKernelGGL((bwd_kernel<D, NW, KB_, VARIANT, kMaskBits, R_, true>),      \
+                                   grid, block, 0, stream, p);                             \
+            } else {                                                                   \
+                hipLaunchKernelGGL((bwd_kernel<D, NW, KB_, VARIANT, kMaskDense, R_, false>),    \
+                                   grid, block, 0, stream, p);                             \
+            }               \
         } else if (p.key_range != nullptr) {                                                   \
             SIGATTN_LIST_LAUNCH(bwd_kernel, D, NW, KB_, VARIANT, kMaskRange, R_)               \
         } else {                                                                               \

@@ -541,15 +541,17 @@ __device__ __forceinline__ uint32_t mask_select(uint32_t word, int pos) {
 }
 
 // Element-mask kinds of the attention kernels: none, dense bytes [L, L] per
-// batch entry, or one key range [lo, hi] per query row (causal, packed
-// documents, sliding windows: the masks whose rows are intervals).
-enum { kMaskNone = 0, kMaskDense = 1, kMaskRange = 2 };
+// batch entry, one key range [lo, hi] per query row (causal, packed
+// documents, sliding windows: the masks whose rows are intervals), or the
+// dense mask packed to bits by the block-mask builder (in a schedule).
+enum { kMaskNone = 0, kMaskDense = 1, kMaskRange = 2, kMaskBits = 3 };
 
 // One batch entry's element mask, in the form the kernel was built for.
 struct MaskSource {
     rsrc_t bytes;          // dense: exactly its L x L bytes
     const int32_t *range;  // ranges: [L, 2] (lo, hi) per query row
-    int L;
+    const uint32_t *bits;  // packed: [L, W] words, bit t of word w = key 32 w + t
+    int L, W;
 };
 
 // Where key t (0..31) of a mask word sits: dense words keep the order in
@@ -689,21 +691,71 @@ struct RangeStage {
     }
 };
 
+// The same tile words from the packed mask: one dword load per word, already
+// in natural key order.  Words of rows or keys at or past n are not read, and
+// a word's bits for keys at or past n are cleared.  Same thread mapping and
+// LDS layout as MaskStage.
+template <int ROWS, int KEYS, int NT, bool WAVE_ROWS>
+struct BitsStage {
+    static constexpr int kWordsPerRow = KEYS / 32;
+    static constexpr int kWords = ROWS * kWordsPerRow;
+    static constexpr int kWordsPerWave = WAVE_ROWS ? kWordsPerRow : 1;
+    static_assert(kWordsPerWave <= 2, "at most one word per lane");
+    static_assert(WAVE_ROWS ? ROWS == NT / 2 : (ROWS == 32 && kWordsPerRow == NT / 64),
+                  "one wave per 32 rows, or per 32 keys");
+    uint32_t word;
+    int r, wi;
+    bool act;
+
+    __device__ __forceinline__ void init(int tid) {
+        const int lane = tid & 63, w = tid >> 6;
+        r = (WAVE_ROWS ? 32 * w : 0) + (lane & 31);
+        wi = (WAVE_ROWS ? 0 : w) + (lane >> 5);
+        act = (lane >> 5) < kWordsPerWave;
+    }
+
+    __device__ __forceinline__ void load(const MaskSource &src, int n, int r0, int k0, int want) {
+        word = 0u;
+        const int row = r0 + r, key = k0 + 32 * wi;
+        if (want != kWantMask || !act || row >= n || key >= n) return;
+        word = src.bits[(int64_t)row * src.W + (key >> 5)];
+    }
+
+    __device__ __forceinline__ int store(uint32_t *words, int r0, int k0, int n, int want) const {
+        if (want == kWantNone) return kSkip;  // the wave leaves this tile out
+        if (want == kWantFull) {
+            if (act) words[wi * ROWS + r] = 0xffffffffu;
+            return kDense;
+        }
+        uint32_t bits = word;
+        const int m = n - (k0 + 32 * wi);  // keys of this word below n
+        if (m < 32) bits &= m <= 0 ? 0u : (1u << m) - 1u;
+        if (r0 + r >= n) bits = 0u;
+        if (act) words[wi * ROWS + r] = bits;
+        return mask_class(bits, act ? bits : 0xffffffffu);
+    }
+};
+
 // The stager of a mask kind (none stages nothing; MaskStage is a placeholder).
 template <int MASK, int ROWS, int KEYS, int NT, bool WAVE_ROWS>
-using MaskStager = typename std::conditional<MASK == kMaskRange,
-                                             RangeStage<ROWS, KEYS, NT, WAVE_ROWS>,
-                                             MaskStage<ROWS, KEYS, NT, WAVE_ROWS>>::type;
+using MaskStager = typename std::conditional<
+    MASK == kMaskRange, RangeStage<ROWS, KEYS, NT, WAVE_ROWS>,
+    typename std::conditional<MASK == kMaskBits, BitsStage<ROWS, KEYS, NT, WAVE_ROWS>,
+                              MaskStage<ROWS, KEYS, NT, WAVE_ROWS>>::type>::type;
 
 // The batch entry's mask source of a kernel of kind MASK.
 template <int MASK>
-__device__ __forceinline__ MaskSource mask_source(const uint8_t *mask, const int32_t *key_range,
-                                                  int b, int L) {
+__device__ __forceinline__ MaskSource mask_source(const AttnParams &p, int b) {
+    const uint8_t *mask = p.mask;
+    const int32_t *key_range = p.key_range;
+    const int L = p.L;
     MaskSource m;
     m.bytes = make_rsrc(MASK == kMaskDense ? mask + (int64_t)b * L * L : nullptr,
                         MASK == kMaskDense ? (int64_t)L * L : 0);
     m.range = MASK == kMaskRange ? key_range + (int64_t)b * L * 2 : nullptr;
+    m.bits = MASK == kMaskBits ? p.mask_bits + (int64_t)b * L * p.bits_w : nullptr;
     m.L = L;
+    m.W = p.bits_w;
     return m;
 }
 

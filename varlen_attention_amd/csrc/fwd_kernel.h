@@ -182,7 +182,7 @@ fwd_kernel(const AttnParams p) {
     const int wl = w * R / NW;        // this wave's block-mask row (0 .. R - 1)
     const int qr = q0 + w * 32 + ql;  // this lane's query row
     const bool q_valid = qr < n;
-    const MaskSource msrc = mask_source<MASK>(p.mask, p.key_range, b, L);
+    const MaskSource msrc = mask_source<MASK>(p, b);
     // Per-lane offsets of the transposing V reads (see lds_read_tr4).
     const int trow = 4 * hh + ((lane & 15) >> 2);
     const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -523,7 +523,10 @@ hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
 #define SIGATTN_FWD_CASE(R_, KB_)                                                                  \
     if constexpr (!kNarrow || KB_ == 1)                                                            \
     if (rows == R_ && kb == KB_) {                                                                 \
-        if (p.mask != nullptr) {                                                                   \
+        if (p.mask_bits != nullptr) { /* a dense mask, packed in the schedule */                  \
+            hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW, KB_, kMaskBits, R_, true>), grid,      \
+                               block, 0, stream, p);                                               \
+        } else if (p.mask != nullptr) {                                                            \
             SIGATTN_FWD_LAUNCH(KB_, kMaskDense, R_)                                                \
         } else if (p.key_range != nullptr) {                                                       \
             SIGATTN_FWD_LAUNCH(KB_, kMaskRange, R_)                                                \

@@ -22,17 +22,22 @@ enum Variant { kSigmoid = 0, kSoftmax = 1, kSoftmax1 = 2, kDiff = 3 };
 // keys (klists), a count word and then one word per block-mask entry that
 // some line of the group keeps: e | kept-by-line << 24 | full-by-line << 28,
 // in increasing e (lines: the block rows, or columns, the group spans).
+// A schedule built with a dense element mask ends with that mask packed to
+// bits: per batch entry and query row, words_per_row words, bit t of word w
+// the entry for key 32 w + t (rows and keys below n; the rest unspecified).
 struct ScheduleLayout {
     int64_t slots1, slots2;  // items in the two arrays
     int64_t items1, items2;  // byte offsets of the item arrays
     int64_t qlists, klists;  // byte offsets of the entry lists
+    int64_t bits;            // byte offset of the packed mask (dense_mask layouts)
     int64_t bytes;           // the whole buffer
     int groups;              // 128-row groups along L
     int qstride, kstride;    // words per query group (1 + Tk) and key group (1 + Tq)
+    int words_per_row;       // packed mask: ceil(L / 32)
 };
 
 __host__ __device__ inline ScheduleLayout schedule_layout(int B, int H, int L, int block_q,
-                                                          int block_k) {
+                                                          int block_k, bool dense_mask = false) {
     ScheduleLayout s;
     const int64_t G = ((int64_t)L + 127) / 128;
     const int64_t Tq = ((int64_t)L + block_q - 1) / block_q;
@@ -46,7 +51,10 @@ __host__ __device__ inline ScheduleLayout schedule_layout(int B, int H, int L, i
     s.items2 = 16 * s.slots1;
     s.qlists = s.items2 + 16 * s.slots2;
     s.klists = s.qlists + 4 * (int64_t)B * G * s.qstride;
-    s.bytes = s.klists + 4 * (int64_t)B * G * s.kstride;
+    s.bits = (s.klists + 4 * (int64_t)B * G * s.kstride + 15) / 16 * 16;
+    s.words_per_row = (int)(((int64_t)L + 31) / 32);
+    s.bytes = dense_mask ? s.bits + 4 * (int64_t)B * L * s.words_per_row
+                         : s.klists + 4 * (int64_t)B * G * s.kstride;
     return s;
 }
 
@@ -69,6 +77,11 @@ struct AttnParams {
     const uint8_t *block_mask;      // [B, Tq, Tk] or null
     const uint8_t *mask;            // [B, L, L] or null
     const int32_t *key_range;       // [B, L, 2] or null (at most one of mask, key_range)
+    // With a mask and a schedule: the mask packed to bits in the schedule
+    // (ScheduleLayout), bits_w words per row; kernels built for a schedule
+    // read these instead of the mask's bytes.
+    const uint32_t *mask_bits;
+    int bits_w;
     // From a schedule buffer (all null without one): the work items of
     // launches over one kind of tile (items1) and of the one-launch backward
     // (items2), one per workgroup, and the kept-entry lists of query and key
@@ -84,9 +97,11 @@ struct AttnParams {
     int bias_mode, variant;
 };
 
+// bits_out (or null; with mask): the mask packed to bits, ScheduleLayout's
+// words_per_row words per row.
 hipError_t launch_blockmask(const int32_t *seq_lens, const uint8_t *mask,
                             const int32_t *key_range, int B, int L, int block_q, int block_k,
-                            uint8_t *out, hipStream_t stream);
+                            uint8_t *out, hipStream_t stream, uint32_t *bits_out = nullptr);
 // Work items and kept-entry lists (ScheduleLayout) from seq_lens and a
 // finished block mask, enqueued after it on the same stream; or, with
 // padding_mask_out, for a padding-only batch: the block mask written into
