@@ -688,13 +688,16 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
 // ---------------------------------------------------------------- kernels
 // Waves per SIMD the register allocation must allow.  The unmasked kernels
 // at d = 64 need about 168 VGPRs (the softmax variants a few more, spilled),
-// and so does sigmoid with key ranges: held to that, three waves share a SIMD
-// (LDS allows three workgroups per CU even in the one-launch kernel).  With
-// key ranges that is 13 % faster than two; the other masked kernels would
-// spill more (76 to 152 bytes per lane) and gain nothing.
+// and so does sigmoid with key ranges or a packed mask: held to that, three
+// waves share a SIMD (LDS allows three workgroups per CU even in the
+// one-launch kernel), 12 to 13 % faster than two.  The other masked kernels
+// would spill more (76 to 152 bytes per lane) and gain nothing.
 template <int D, int VARIANT, int MASK>
 constexpr int kBwdWavesPerSimd =
-    D == 64 && (MASK == kMaskNone || (VARIANT == kSigmoid && MASK == kMaskRange)) ? 3 : 2;
+    D == 64 && (MASK == kMaskNone ||
+                (VARIANT == kSigmoid && (MASK == kMaskRange || MASK == kMaskBits)))
+        ? 3
+        : 2;
 
 // LIST: built for a schedule (work items and kept-entry lists from it).
 template <int D, int NW, int VARIANT, int MASK, int C, bool LIST>
