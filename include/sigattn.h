@@ -340,11 +340,14 @@ int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1,
  * gradients are those of a softmax attention with dO (map 1) or -lambda dO
  * (map 2), and dV is the sum of both (sigattn_bwd's softmax backward: P from
  * the map's LSE, dS = P * (dP - D), D = rowsum(dO * O_i) with the map's own
- * output O_i).  Two backward launches on `stream`; the second adds its dV to
- * the first's, so no atomics are used and results are reproducible.  Between
- * the two, map 1's dV is held as bf16 plus its bf16 rounding residual (kept
- * in dk2's storage, which the second launch then overwrites with dK2), so
- * the sum is formed in fp32 from ~16 significant bits of each term.
+ * output O_i).  No atomics are used and results are reproducible.  At
+ * d = 64 both maps run in one launch: each work item computes both maps'
+ * scores, dP = dO V^T once for both, and dV from the weights P1 - lambda P2
+ * (rounded to bf16 once).  At d = 128 two launches on `stream`; the second
+ * adds its dV to the first's.  Between the two, map 1's dV is held as bf16
+ * plus its bf16 rounding residual (kept in dk2's storage, which the second
+ * launch then overwrites with dK2), so the sum is formed in fp32 from ~16
+ * significant bits of each term.
  *
  *   q1, k1, q2, k2, v, dout  [device] bf16 [B, H, L, d] (input layout)
  *   o1, o2, lse1, lse2       the forward's per-map outputs and LSEs (required)

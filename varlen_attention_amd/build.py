@@ -15,7 +15,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsigattn.so")
 SOURCES = ["api.hip", "blockmask.hip", "schedule.hip", "fwd.hip", "fwd_sigmoid.hip",
            "fwd_softmax.hip", "fwd_diff.hip", "bwd.hip", "bwd_sigmoid.hip", "bwd_softmax.hip",
-           "bwd_softmax1.hip"]
+           "bwd_softmax1.hip", "bwd_diff.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

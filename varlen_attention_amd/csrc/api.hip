@@ -347,22 +347,39 @@ namespace {
 
 enum BwdParts { kPartDkdv = 1, kPartDq = 2 };
 
+// Differential attention's second map, for the backward that computes both
+// maps in one launch (all pointers checked by the caller).
+struct SecondMap {
+    const void *q2, *k2, *o2;
+    const float *lse2;
+    void *dq2, *dk2;
+    float lambda;
+};
+
 int backward(const sigattn_shape *shape, const void *q, const void *k, const void *v,
              const void *dout, const void *o, const float *lse, const int32_t *seq_lens,
              const uint8_t *block_mask, const void *schedule, const uint8_t *mask,
              const int32_t *key_range, int32_t bias_mode, int32_t variant, void *dq, void *dk,
              void *dv, void *stream, int parts, const char *name, float grad_scale = 1.0f,
-             bool accumulate_dv = false, void *dv_lo = nullptr) {
+             bool accumulate_dv = false, void *dv_lo = nullptr,
+             const SecondMap *second = nullptr) {
     sigattn::AttnParams p = {};
-    const void *inputs[4] = {q, k, v, dout};
-    void *outputs[3];
+    const void *inputs[6] = {q, k, v, dout};
+    int n_in = 4;
+    void *outputs[5];
     int n_out = 0;
     if (parts & kPartDq) outputs[n_out++] = dq;
     if (parts & kPartDkdv) {
         outputs[n_out++] = dk;
         outputs[n_out++] = dv;
     }
-    int st = check_attention(shape, inputs, 4, outputs, n_out, seq_lens, block_mask, schedule,
+    if (second != nullptr) {
+        inputs[n_in++] = second->q2;
+        inputs[n_in++] = second->k2;
+        outputs[n_out++] = second->dq2;
+        outputs[n_out++] = second->dk2;
+    }
+    int st = check_attention(shape, inputs, n_in, outputs, n_out, seq_lens, block_mask, schedule,
                              mask, key_range, bias_mode, variant, &p);
     if (st != SIGATTN_OK) return st;
     if (variant != SIGATTN_SIGMOID) {
@@ -385,6 +402,16 @@ int backward(const sigattn_shape *shape, const void *q, const void *k, const voi
     p.grad_scale = grad_scale;
     p.accumulate_dv = accumulate_dv ? 1 : 0;
     p.dv_lo = dv_lo;
+    if (second != nullptr) {
+        p.q2 = second->q2;
+        p.k2 = second->k2;
+        p.o2 = const_cast<void *>(second->o2);
+        p.lse2 = const_cast<float *>(second->lse2);
+        p.dq2 = second->dq2;
+        p.dk2 = second->dk2;
+        p.lambda = second->lambda;
+        p.variant = sigattn::kDiff;
+    }
     hipStream_t s = (hipStream_t)stream;
     if (parts == (kPartDkdv | kPartDq)) return launch_status(sigattn::launch_bwd(p, s), name);
     if (parts & kPartDkdv) return launch_status(sigattn::launch_bwd_dkdv(p, s), name);
@@ -444,7 +471,15 @@ int sigattn_diff_bwd(const sigattn_shape *shape, const void *q1, const void *k1,
         return fail(SIGATTN_ERR_ALIGNMENT, "a second-map tensor is not 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(lse2) & 3u) != 0)
         return fail(SIGATTN_ERR_ALIGNMENT, "lse2 is not 4-byte aligned");
-    // Map 1: the softmax backward of (Q1, K1) with dO writes dq1, dk1 and dv,
+    if (shape != nullptr && shape->d == 64) {
+        // Both maps in one pass: each work item holds both maps' operands,
+        // dP = dO V^T serves both, and dV takes the weights P1 - lambda P2.
+        const SecondMap second = {q2, k2, o2, lse2, dq2, dk2, lambda};
+        return backward(shape, q1, k1, v, dout, o1, lse1, seq_lens, block_mask, schedule, mask,
+                        key_range, bias_mode, SIGATTN_SOFTMAX, dq1, dk1, dv, stream,
+                        kPartDkdv | kPartDq, "sigattn_diff_bwd", 1.0f, false, nullptr, &second);
+    }
+    // d = 128: two passes.  Map 1: the softmax backward of (Q1, K1) with dO writes dq1, dk1 and dv,
     // and dv's rounding residual into dk2 (written for real only by map 2).
     int st = backward(shape, q1, k1, v, dout, o1, lse1, seq_lens, block_mask, schedule, mask,
                       key_range, bias_mode, SIGATTN_SOFTMAX, dq1, dk1, dv, stream,

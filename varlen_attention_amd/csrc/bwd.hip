@@ -1,6 +1,6 @@
 // Backward dispatch: the variant selects the translation unit that holds the
-// kernel instantiations (bwd_sigmoid.hip, bwd_softmax.hip, bwd_softmax1.hip);
-// they compile in parallel.
+// kernel instantiations (bwd_sigmoid.hip, bwd_softmax.hip, bwd_softmax1.hip,
+// bwd_diff.hip); they compile in parallel.
 #include "kernels.h"
 
 namespace sigattn {
@@ -9,8 +9,11 @@ namespace sigattn {
 hipError_t launch_bwd_sigmoid(const AttnParams &p, hipStream_t stream, int part);
 hipError_t launch_bwd_softmax(const AttnParams &p, hipStream_t stream, int part);
 hipError_t launch_bwd_softmax1(const AttnParams &p, hipStream_t stream, int part);
+// Differential attention at d = 64, both parts (bwd_diff.hip).
+hipError_t launch_bwd_diff(const AttnParams &p, hipStream_t stream);
 
 static hipError_t by_variant(const AttnParams &p, hipStream_t stream, int part) {
+    if (p.variant == kDiff) return part == 2 ? launch_bwd_diff(p, stream) : hipErrorInvalidValue;
     if (p.variant == kSigmoid) return launch_bwd_sigmoid(p, stream, part);
     if (p.variant == kSoftmax) return launch_bwd_softmax(p, stream, part);
     return launch_bwd_softmax1(p, stream, part);

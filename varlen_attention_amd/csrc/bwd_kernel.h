@@ -75,6 +75,23 @@ struct PairStage {
     }
 };
 
+// A third tensor of the same tile shape, moved with a PairStage's offsets.
+template <int D, int BT, int NT>
+struct OneStage {
+    static constexpr int CH = PairStage<D, BT, NT>::CH;
+    uint4 a[CH];
+
+    __device__ __forceinline__ void load(rsrc_t ra, const int (&goff)[CH]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) a[c] = buffer_load16(ra, goff[c]);
+    }
+
+    __device__ __forceinline__ void store(bf16 *ta, const int (&loff)[CH]) const {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) *reinterpret_cast<uint4 *>(ta + loff[c]) = a[c];
+    }
+};
+
 // Fetches a [BT x D] tile of two tensors straight into swizzled LDS tiles
 // (buffer loads that write LDS, no staging registers).  One wave
 // instruction fills one contiguous KiB, lane l the 16 bytes at 16 l, so each
@@ -105,6 +122,13 @@ struct DmaPair {
             lds_load16(ra, reinterpret_cast<char *>(ta) + lds_off + i * 1024, goff[i]);
             lds_load16(rb, reinterpret_cast<char *>(tb) + lds_off + i * 1024, goff[i]);
         }
+    }
+
+    // A third tensor of the same tile shape.
+    __device__ __forceinline__ void issue_one(rsrc_t ra, bf16 *ta) const {
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i)
+            lds_load16(ra, reinterpret_cast<char *>(ta) + lds_off + i * 1024, goff[i]);
     }
 };
 
@@ -230,21 +254,31 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16 *tile, int r16, int c32,
 }  // namespace
 
 // ---------------------------------------------------------------- dK / dV
-// LDS of one dK/dV tile (elements): Q and dO tiles of 32 rows, double-buffered,
-// then two buffers of 2 x 32 floats of row statistics (softmax variants).
-template <int D> constexpr int kDkdvLds = 2 * 2 * 32 * D + 2 * 2 * 32 * 2;
+// Softmax maps per work item: two for differential attention (both maps'
+// gradients in one pass: dP = dO V^T serves both, and dV takes the combined
+// weights P1 - lambda P2), one otherwise.
+template <int VARIANT> constexpr int kMapsOf = VARIANT == kDiff ? 2 : 1;
+
+// LDS of one dK/dV tile (elements): Q (per map) and dO tiles of 32 rows,
+// double-buffered, then two buffers of MAPS x 2 x 32 floats of row statistics
+// (softmax variants).
+template <int D, int MAPS = 1>
+constexpr int kDkdvLds = (MAPS + 1) * 2 * 32 * D + 2 * MAPS * 2 * 32 * 2;
 
 // Element-mask bits of two tiles (MaskStage words), for either kind of work.
 constexpr int kMaskWords = 2 * 256;
 
-// At d = 128 the V rows of a wave's keys wait in LDS (32 x D elements per
-// wave) rather than in registers: the dK and dV accumulators and the K rows
-// leave too few registers for the tile loop otherwise.
-template <int D> constexpr bool kVInLds = D == 128;
+// At d = 128, and with two maps, the V rows of a wave's keys wait in LDS
+// (32 x D elements per wave) rather than in registers: the dK and dV
+// accumulators and the K rows leave too few registers for the tile loop
+// otherwise.
+template <int D, int VARIANT> constexpr bool kVInLds = D == 128 || VARIANT == kDiff;
 
 // dK and dV of key tile kt (32 NW keys) of (batch entry b, head h); smem
-// holds kDkdvLds<D> elements, mbits kMaskWords words (element mask only),
-// vt this wave's 32 x D elements when kVInLds<D>.
+// holds kDkdvLds<D, MAPS> elements, mbits kMaskWords words (element mask
+// only), vt this wave's 32 x D elements when kVInLds<D, VARIANT>.  Differential
+// attention (two maps): also dK2, with S2 = Q2 K2^T, dS2 = P2 (dP - D2) and
+// dK2 = -lambda scale dS2^T Q2, and dV from the weights P1 - lambda P2.
 // C: block-mask columns per workgroup (BKV / block_k); wave w follows column
 // w * C / NW and works only on the query tiles that column keeps.
 template <int D, int NW, int VARIANT, int MASK, int C, bool LIST>
@@ -254,21 +288,28 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     constexpr int BKV = 32 * NW, BQ = 32, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
     constexpr bool kSoft = VARIANT != kSigmoid;
-    // Slot i of the Q and dO tiles and of the row statistics (offsets from
-    // the LDS base, so the LDS address space stays visible to the compiler).
+    constexpr int MAPS = kMapsOf<VARIANT>;
+    // Slot i of the Q and dO tiles (and map 2's Q) and of map mp's row
+    // statistics (offsets from the LDS base, so the LDS address space stays
+    // visible to the compiler).
     auto Qs = [&](int i) { return smem + i * (BQ * D); };
     auto dOs = [&](int i) { return smem + (2 + i) * (BQ * D); };
-    auto Dl = [&](int i) { return reinterpret_cast<float *>(smem + 4 * BQ * D) + i * 2 * BQ; };
-    auto Offl = [&](int i) { return Dl(i) + BQ; };
+    auto Q2s = [&](int i) { return smem + (4 + i) * (BQ * D); };
+    auto Dl = [&](int i, int mp = 0) {
+        return reinterpret_cast<float *>(smem + 2 * (MAPS + 1) * BQ * D) + (i * MAPS + mp) * 2 * BQ;
+    };
+    auto Offl = [&](int i, int mp = 0) { return Dl(i, mp) + BQ; };
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int L = p.L;
     const int k0 = kt * BKV;
     bf16 *dkb = reinterpret_cast<bf16 *>(p.dk) + b * p.osb + h * p.osh;
     bf16 *dvb = reinterpret_cast<bf16 *>(p.dv) + b * p.osb + h * p.osh;
+    bf16 *dk2b = MAPS == 2 ? reinterpret_cast<bf16 *>(p.dk2) + b * p.osb + h * p.osh : nullptr;
     auto zero_tile = [&](int r0, int rows) {
         zero_rows<D>(dkb, p.osl, r0, rows, tid, NT);
         zero_rows<D>(dvb, p.osl, r0, rows, tid, NT);
+        if constexpr (MAPS == 2) zero_rows<D>(dk2b, p.osl, r0, rows, tid, NT);
     };
     if (k0 >= n) {  // a tile of an empty sequence: zeros, nothing else
         zero_tile(k0, min(BKV, L - k0));
@@ -281,6 +322,14 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     const bf16 *obase = kSoft ? reinterpret_cast<const bf16 *>(p.o) + b * p.osb + h * p.osh
                               : nullptr;
     const float *lseb = kSoft ? p.lse + ((int64_t)b * p.H + h) * L : nullptr;
+    const bf16 *qb2 = nullptr, *k2base = nullptr, *obase2 = nullptr;
+    const float *lseb2 = nullptr;
+    if constexpr (MAPS == 2) {
+        qb2 = reinterpret_cast<const bf16 *>(p.q2) + b * p.sb + h * p.sh;
+        k2base = reinterpret_cast<const bf16 *>(p.k2) + b * p.sb + h * p.sh;
+        obase2 = reinterpret_cast<const bf16 *>(p.o2) + b * p.osb + h * p.osh;
+        lseb2 = p.lse2 + ((int64_t)b * p.H + h) * L;
+    }
 
     const int kl = lane & 31, hh = lane >> 5;
     const int key = k0 + w * 32 + kl;  // this lane's key row
@@ -297,7 +346,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     // K^T and V^T operands of S = Q K^T and dP = dO V^T: lane holds row `key`.
     const rsrc_t rk = make_rsrc(kb + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
     const rsrc_t rv = make_rsrc(vb + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
-    constexpr bool kVLds = kVInLds<D>;
+    constexpr bool kVLds = kVInLds<D, VARIANT>;
     bf16x8 kreg[KS], vreg[kVLds ? 1 : KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -317,6 +366,14 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         else
             return vreg[ks];
     };
+    bf16x8 kreg2[MAPS == 2 ? KS : 1];
+    if constexpr (MAPS == 2) {
+        const rsrc_t rk2 = make_rsrc(k2base + (int64_t)k0 * p.sl, (int64_t)(n - k0) * p.sl * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kreg2[ks] = as_bf16x8(buffer_load16(
+                rk2, (int)(((int64_t)(w * 32 + kl) * p.sl + ks * 16 + hh * 8) * 2)));
+    }
     // SIGMOID: K is scaled by c1 before the loop, so the S accumulator is
     // u = -scale * s * log2 e (see sigmoid_scaled).  Softmax: the weight is
     // exp2(s * c1 + off) with c1 = scale * log2 e and off from RowStats.
@@ -324,9 +381,12 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     const float cexp = bias_factor(p.bias_mode, n, L);
     const float c0 = bias_value(p.bias_mode, n, L) * kLog2e;
 
-    f32x16 dvt[DB], dkt[DB];
+    f32x16 dvt[DB], dkt[DB], dkt2[MAPS == 2 ? DB : 1];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dvt[db] = dkt[db] = f32x16{};
+    if constexpr (MAPS == 2)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dkt2[db] = f32x16{};
 
     auto rows_rsrc = [&](const bf16 *base, int r0) {
         return make_rsrc(base + (int64_t)r0 * p.sl, (int64_t)(n - r0) * p.sl * 2);
@@ -336,19 +396,26 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
     };
     PairStage<D, BQ, NT> stage;
     stage.init(p.sl, tid);
-    RowStats<D, BQ, NT> stats;
+    OneStage<D, BQ, NT> stage2;  // map 2's Q
+    RowStats<D, BQ, NT> stats, stats2;
     if constexpr (kSoft) stats.init(p.osl, tid);
+    if constexpr (MAPS == 2) stats2.init(p.osl, tid);
     Mask mstage;
     if constexpr (MASKED) mstage.init(tid);
     // want: what this wave needs of the tile's element mask (kWant*).
     auto load_tile = [&](int t, int want) {
         stage.load(rows_rsrc(qb, t * BQ), rows_rsrc(dob, t * BQ));
+        if constexpr (MAPS == 2) stage2.load(rows_rsrc(qb2, t * BQ), stage.goff);
         if constexpr (kSoft) stats.load(out_rows_rsrc(obase, t * BQ), lseb + t * BQ, n - t * BQ, tid);
+        if constexpr (MAPS == 2)
+            stats2.load(out_rows_rsrc(obase2, t * BQ), lseb2 + t * BQ, n - t * BQ, tid);
         if constexpr (MASKED) mstage.load(msrc, n, t * BQ, k0, want);
     };
     auto store_tile = [&](int i, int t, int want) {
         stage.store(Qs(i), dOs(i));
+        if constexpr (MAPS == 2) stage2.store(Q2s(i), stage.loff);
         if constexpr (kSoft) stats.store(stage.b, c0, Dl(i), Offl(i), tid);
+        if constexpr (MAPS == 2) stats2.store(stage.b, c0, Dl(i, 1), Offl(i, 1), tid);
         if constexpr (MASKED) mcls = mstage.store(Ml(i), t * BQ, k0, n, want);
     };
     // Query tile 0 is fetched before the block mask is read (see the forward
@@ -384,6 +451,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         const bf16 *dOc = dOs(buf);
         const float *Dc = Dl(buf);
         const float *Offc = Offl(buf);
+        const bf16 *Q2c = Q2s(buf);
+        const float *D2c = Dl(buf, MAPS - 1);
+        const float *Off2c = Offl(buf, MAPS - 1);
         const uint32_t *Mc = Ml(buf);
         // One body per tile kind (its only branch is the uniform one around
         // the element-mask selects).  MODE 0 (no element mask)
@@ -393,11 +463,13 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         // zeroed at the store.  MODE 2: element mask.
         auto tile = [&](auto mode_tag) {
             constexpr int MODE = decltype(mode_tag)::value;
-            f32x16 s = f32x16{}, dp = f32x16{};
+            f32x16 s = f32x16{}, dp = f32x16{}, s2 = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 s = mfma32(row_operand<D>(Qc, kl, ks * 16 + hh * 8), kreg[ks], s);
                 dp = mfma32(row_operand<D>(dOc, kl, ks * 16 + hh * 8), v_operand(ks), dp);
+                if constexpr (MAPS == 2)
+                    s2 = mfma32(row_operand<D>(Q2c, kl, ks * 16 + hh * 8), kreg2[ks], s2);
             }
             // s[4i + j] = S[query q0 + 8 i + 4 hh + j][key]
             // MODE 2: mask words of query rows 8 i + 4 hh + j (validity folded
@@ -413,18 +485,28 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                         s[4 * i + 1] = keep_score<kSoft>(s[4 * i + 1], mask_select(m4.y, mbit));
                         s[4 * i + 2] = keep_score<kSoft>(s[4 * i + 2], mask_select(m4.z, mbit));
                         s[4 * i + 3] = keep_score<kSoft>(s[4 * i + 3], mask_select(m4.w, mbit));
+                        if constexpr (MAPS == 2) {
+                            s2[4 * i + 0] = keep_score<kSoft>(s2[4 * i + 0], mask_select(m4.x, mbit));
+                            s2[4 * i + 1] = keep_score<kSoft>(s2[4 * i + 1], mask_select(m4.y, mbit));
+                            s2[4 * i + 2] = keep_score<kSoft>(s2[4 * i + 2], mask_select(m4.z, mbit));
+                            s2[4 * i + 3] = keep_score<kSoft>(s2[4 * i + 3], mask_select(m4.w, mbit));
+                        }
                     }
                 }
             }
-            float pv[16], dsv[16];
+            float pv[16], dsv[16], dsv2[MAPS == 2 ? 16 : 1];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // Softmax row statistics of query rows 8 i + 4 hh + j, read
                 // four rows at a time (all sixteen at once cost registers).
-                f32x4 offq, dq4;
+                f32x4 offq, dq4, offq2, dq42;
                 if constexpr (kSoft) {
                     offq = *reinterpret_cast<const f32x4 *>(Offc + 8 * i + 4 * hh);
                     dq4 = *reinterpret_cast<const f32x4 *>(Dc + 8 * i + 4 * hh);
+                }
+                if constexpr (MAPS == 2) {
+                    offq2 = *reinterpret_cast<const f32x4 *>(Off2c + 8 * i + 4 * hh);
+                    dq42 = *reinterpret_cast<const f32x4 *>(D2c + 8 * i + 4 * hh);
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -439,6 +521,13 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                         dsv[r] = pr * (dp[r] - dq4[j]);
                     else
                         dsv[r] = dp[r] * (pr - pr * pr);
+                    if constexpr (MAPS == 2) {
+                        // Map 2's score gradient without its factor -lambda
+                        // (applied at the dK2 store); dV's weight P1 - lambda P2.
+                        const float pr2 = __builtin_amdgcn_exp2f(fmaf(s2[r], c1, offq2[j]));
+                        dsv2[r] = pr2 * (dp[r] - dq42[j]);
+                        pv[r] = fmaf(-p.lambda, pr2, pr);
+                    }
                 }
             }
 #pragma unroll
@@ -449,6 +538,13 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
                 for (int db = 0; db < DB; ++db) {
                     dvt[db] = mfma32(tr_operand<D>(dOc, kk * 16, db * 32, trow, tcol), pb, dvt[db]);
                     dkt[db] = mfma32(tr_operand<D>(Qc, kk * 16, db * 32, trow, tcol), sb, dkt[db]);
+                }
+                if constexpr (MAPS == 2) {
+                    const bf16x8 sb2 = pack8(&dsv2[kk * 8]);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        dkt2[db] = mfma32(tr_operand<D>(Q2c, kk * 16, db * 32, trow, tcol), sb2,
+                                          dkt2[db]);
                 }
             }
         };
@@ -475,6 +571,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         store_rows_t<D>(dvb + (int64_t)key * p.osl, dvt, p.grad_scale, hh, k_valid,
                         p.accumulate_dv != 0, lo);
         store_rows_t<D>(dkb + (int64_t)key * p.osl, dkt, p.scale * p.grad_scale, hh, k_valid);
+        if constexpr (MAPS == 2)
+            store_rows_t<D>(dk2b + (int64_t)key * p.osl, dkt2, -p.lambda * p.scale * p.grad_scale,
+                            hh, k_valid);
     }
     // This tile's share of the sequence's fully padded key tiles, issued last
     // (nothing waits for these stores).
@@ -484,24 +583,32 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
 // ---------------------------------------------------------------- dQ
 // dQ of query tile qt (32 NW queries) of (batch entry b, head h), visiting
 // keys 32 KB at a time.  K0, V0, K1, V1 are four separate LDS objects of
-// 32 KB rows x D each (two buffers of the K and V tiles).
+// 32 KB rows x D each (two buffers of the K and V tiles); with two maps
+// (differential attention) K20, K21 are the two buffers of map 2's K tile,
+// and dQ2 = -lambda scale dS2 K2 is computed beside dQ.
 // R: block-mask rows per workgroup (BQ / block_q); wave w follows row
 // w * R / NW.
 template <int D, int NW, int KB, int VARIANT, int MASK, int R, bool LIST>
 __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int qt, int n,
                                         bf16 *K0, bf16 *V0, bf16 *K1, bf16 *V1,
-                                        uint32_t *mbits) {
+                                        uint32_t *mbits, bf16 *K20 = nullptr,
+                                        bf16 *K21 = nullptr) {
     constexpr bool MASKED = MASK != kMaskNone;
     constexpr int BQ = 32 * NW, BK = 32 * KB, NT = 64 * NW;
     constexpr int KS = D / 16, DB = D / 32;
     constexpr bool kSoft = VARIANT != kSigmoid;
+    constexpr int MAPS = kMapsOf<VARIANT>;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = p.L;
     const int q0 = qt * BQ;
     bf16 *dqb = reinterpret_cast<bf16 *>(p.dq) + b * p.osb + h * p.osh;
-    auto zero_tile = [&](int r0, int rows) { zero_rows<D>(dqb, p.osl, r0, rows, tid, NT); };
+    bf16 *dq2b = MAPS == 2 ? reinterpret_cast<bf16 *>(p.dq2) + b * p.osb + h * p.osh : nullptr;
+    auto zero_tile = [&](int r0, int rows) {
+        zero_rows<D>(dqb, p.osl, r0, rows, tid, NT);
+        if constexpr (MAPS == 2) zero_rows<D>(dq2b, p.osl, r0, rows, tid, NT);
+    };
     if (q0 >= n) {  // a tile of an empty sequence: zeros, nothing else
         zero_tile(q0, min(BQ, L - q0));
         return;
@@ -523,12 +630,22 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
 
     const rsrc_t rq = make_rsrc(qb + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
     const rsrc_t rdo = make_rsrc(dob + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
-    bf16x8 qreg[KS], doreg[KS];
+    bf16x8 qreg[KS], doreg[KS], qreg2[MAPS == 2 ? KS : 1];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const int off = (int)(((int64_t)(w * 32 + ql) * p.sl + ks * 16 + hh * 8) * 2);
         qreg[ks] = as_bf16x8(buffer_load16(rq, off));
         doreg[ks] = as_bf16x8(buffer_load16(rdo, off));
+    }
+    const bf16 *k2base = nullptr;
+    if constexpr (MAPS == 2) {
+        const bf16 *qb2 = reinterpret_cast<const bf16 *>(p.q2) + b * p.sb + h * p.sh;
+        k2base = reinterpret_cast<const bf16 *>(p.k2) + b * p.sb + h * p.sh;
+        const rsrc_t rq2 = make_rsrc(qb2 + (int64_t)q0 * p.sl, (int64_t)(n - q0) * p.sl * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qreg2[ks] = as_bf16x8(buffer_load16(
+                rq2, (int)(((int64_t)(w * 32 + ql) * p.sl + ks * 16 + hh * 8) * 2)));
     }
     // SIGMOID: Q is scaled by c1 before the loop, so the S accumulator is
     // u = -scale * s * log2 e (see sigmoid_scaled).  Softmax: the weight is
@@ -553,10 +670,30 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
         off = lse == -INFINITY ? -INFINITY
                                : bias_value(p.bias_mode, n, L) * kLog2e - lse * kLog2e;
     }
+    // Map 2's row statistics, from its own output O2 and LSE.
+    float off2 = 0.0f, drow2 = 0.0f;
+    if constexpr (MAPS == 2) {
+        const bf16 *ob2 = reinterpret_cast<const bf16 *>(p.o2) + b * p.osb + h * p.osh;
+        const rsrc_t ro2 = make_rsrc(ob2 + (int64_t)q0 * p.osl, (int64_t)(n - q0) * p.osl * 2);
+        float part = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint4 o8 = buffer_load16(
+                ro2, (int)(((int64_t)(w * 32 + ql) * p.osl + ks * 16 + hh * 8) * 2));
+            part += dot8(__builtin_bit_cast(uint4, doreg[ks]), o8);
+        }
+        drow2 = part + __shfl_xor(part, 32);
+        const float lse2 = q_valid ? p.lse2[((int64_t)b * p.H + h) * L + qr] : -INFINITY;
+        off2 = lse2 == -INFINITY ? -INFINITY
+                                 : bias_value(p.bias_mode, n, L) * kLog2e - lse2 * kLog2e;
+    }
 
-    f32x16 dqt[DB];
+    f32x16 dqt[DB], dqt2[MAPS == 2 ? DB : 1];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
+    if constexpr (MAPS == 2)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dqt2[db] = f32x16{};
 
     auto rows_rsrc = [&](const bf16 *base, int r0) {
         return make_rsrc(base + (int64_t)r0 * p.sl, (int64_t)(n - r0) * p.sl * 2);
@@ -568,10 +705,11 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     // not the one being read.
     DmaPair<D, BK, NW> dma;
     dma.init(p.sl, w, lane);
-    auto fetch = [&](int t, bf16 *kd, bf16 *vd) {
+    auto fetch = [&](int t, bf16 *kd, bf16 *vd, bf16 *k2d) {
         dma.issue(rows_rsrc(kb, t * BK), rows_rsrc(vb, t * BK), kd, vd);
+        if constexpr (MAPS == 2) dma.issue_one(rows_rsrc(k2base, t * BK), k2d);
     };
-    fetch(0, K0, V0);
+    fetch(0, K0, V0, K20);
     Mask mstage;
     if constexpr (MASKED) mstage.init(tid);
     const int line0 = q0 / p.block_q;  // first block-mask row of this tile
@@ -588,7 +726,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     int kt = sched.next();
     const int kt_want = sched.want();
     bool on = kt_want != kWantNone;  // this wave's row keeps the current tile
-    if (kt > 0) fetch(kt, K0, V0);
+    if (kt > 0) fetch(kt, K0, V0, K20);
     if constexpr (MASKED)
         if (kt >= 0) {
             mstage.load(msrc, n, q0, kt * BK, kt_want);
@@ -601,10 +739,10 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
     __syncthreads();
 
     auto step = [&](const bf16 *Kc, const bf16 *Vc, const uint32_t *Mc, bf16 *Kn, bf16 *Vn,
-                    uint32_t *Mn) {
+                    uint32_t *Mn, const bf16 *K2c, bf16 *K2n) {
         const int nxt = sched.next();
         const int nxt_want = sched.want();
-        if (nxt >= 0) fetch(nxt, Kn, Vn);
+        if (nxt >= 0) fetch(nxt, Kn, Vn, K2n);
         if constexpr (MASKED)
             if (nxt >= 0) mstage.load(msrc, n, q0, nxt * BK, nxt_want);
         // MODE 0 (no element mask): padded key rows of K and V read as zeros,
@@ -614,12 +752,15 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
             constexpr int MODE = decltype(mode_tag)::value;
 #pragma unroll
             for (int kb2 = 0; kb2 < KB; ++kb2) {
-                f32x16 s = f32x16{}, dp = f32x16{};
+                f32x16 s = f32x16{}, dp = f32x16{}, s2 = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     s = mfma32(row_operand<D>(Kc, kb2 * 32 + ql, ks * 16 + hh * 8), qreg[ks], s);
                     dp = mfma32(row_operand<D>(Vc, kb2 * 32 + ql, ks * 16 + hh * 8), doreg[ks],
                                 dp);
+                    if constexpr (MAPS == 2)
+                        s2 = mfma32(row_operand<D>(K2c, kb2 * 32 + ql, ks * 16 + hh * 8),
+                                    qreg2[ks], s2);
                 }
                 // s[4i + j] = S^T[key k0 + 32 kb2 + 8 i + 4 hh + j][qr]; in
                 // MODE 2 that key is bit key_bit(8 i + 4 hh + j) of the row's
@@ -635,9 +776,15 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                             s[r] = keep_score<kSoft>(
                                 s[r], mask_select(mwk, kDenseBits ? 8 * (r & 3) + 2 * (r >> 2)
                                                                   : 8 * (r >> 2) + (r & 3)));
+                        if constexpr (MAPS == 2)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                s2[r] = keep_score<kSoft>(
+                                    s2[r], mask_select(mwk, kDenseBits ? 8 * (r & 3) + 2 * (r >> 2)
+                                                                       : 8 * (r >> 2) + (r & 3)));
                     }
                 }
-                float dsv[16];
+                float dsv[16], dsv2[MAPS == 2 ? 16 : 1];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float pr;
@@ -649,6 +796,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                         dsv[r] = pr * (dp[r] - drow);
                     else
                         dsv[r] = dp[r] * (pr - pr * pr);
+                    if constexpr (MAPS == 2)  // without its factor -lambda
+                        dsv2[r] = __builtin_amdgcn_exp2f(fmaf(s2[r], c1, off2)) * (dp[r] - drow2);
                 }
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
@@ -657,6 +806,14 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
                     for (int db = 0; db < DB; ++db)
                         dqt[db] = mfma32(tr_operand<D>(Kc, kb2 * 32 + kk * 16, db * 32, trow, tcol),
                                          sb, dqt[db]);
+                    if constexpr (MAPS == 2) {
+                        const bf16x8 sb2 = pack8(&dsv2[kk * 8]);
+#pragma unroll
+                        for (int db = 0; db < DB; ++db)
+                            dqt2[db] = mfma32(
+                                tr_operand<D>(K2c, kb2 * 32 + kk * 16, db * 32, trow, tcol), sb2,
+                                dqt2[db]);
+                    }
                 }
             }
         };
@@ -675,11 +832,16 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
         kt = nxt;
     };
     while (kt >= 0) {
-        step(K0, V0, M0, K1, V1, M1);
+        step(K0, V0, M0, K1, V1, M1, K20, K21);
         if (kt < 0) break;
-        step(K1, V1, M1, K0, V0, M0);
+        step(K1, V1, M1, K0, V0, M0, K21, K20);
     }
-    if (qr < L) store_rows_t<D>(dqb + (int64_t)qr * p.osl, dqt, p.scale * p.grad_scale, hh, q_valid);
+    if (qr < L) {
+        store_rows_t<D>(dqb + (int64_t)qr * p.osl, dqt, p.scale * p.grad_scale, hh, q_valid);
+        if constexpr (MAPS == 2)
+            store_rows_t<D>(dq2b + (int64_t)qr * p.osl, dqt2, -p.lambda * p.scale * p.grad_scale,
+                            hh, q_valid);
+    }
     // This tile's share of the sequence's fully padded query tiles, issued
     // last (nothing waits for these stores).
     padded_share<BQ>(qt, n, L, zero_tile);
@@ -692,9 +854,11 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
 // waves share a SIMD (LDS allows three workgroups per CU even in the
 // one-launch kernel), 12 to 13 % faster than two.  The other masked kernels
 // would spill more (76 to 152 bytes per lane) and gain nothing.
+// Two maps (differential attention) hold twice the operands and accumulators:
+// two waves.
 template <int D, int VARIANT, int MASK>
 constexpr int kBwdWavesPerSimd =
-    D == 64 && (MASK == kMaskNone ||
+    D == 64 && VARIANT != kDiff && (MASK == kMaskNone ||
                 (VARIANT == kSigmoid && (MASK == kMaskRange || MASK == kMaskBits)))
         ? 3
         : 2;
@@ -703,9 +867,9 @@ constexpr int kBwdWavesPerSimd =
 template <int D, int NW, int VARIANT, int MASK, int C, bool LIST>
 __global__ void __launch_bounds__(64 * NW, (kBwdWavesPerSimd<D, VARIANT, MASK>))
 bwd_dkdv_kernel(const AttnParams p) {
-    __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
+    __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D, kMapsOf<VARIANT>>];
     __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
-    __shared__ __attribute__((aligned(16))) bf16 vts[kVInLds<D> ? NW * 32 * D : 1];
+    __shared__ __attribute__((aligned(16))) bf16 vts[kVInLds<D, VARIANT> ? NW * 32 * D : 1];
     static_assert(32 * NW == 128, "work items are 128-row tiles");
     int b, h, kind, kt, n;
     if (!work_item<1, LIST>(p, b, h, kind, kt, n)) return;
@@ -717,12 +881,14 @@ template <int D, int NW, int KB, int VARIANT, int MASK, int R, bool LIST>
 __global__ void __launch_bounds__(64 * NW, (kBwdWavesPerSimd<D, VARIANT, MASK>))
 bwd_dq_kernel(const AttnParams p) {
     constexpr int kTile = 32 * KB * D;
+    constexpr int kTile2 = kMapsOf<VARIANT> == 2 ? kTile : 8;  // map 2's K buffers
     __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
+    __shared__ __attribute__((aligned(1024))) bf16 K20[kTile2], K21[kTile2];
     __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
     static_assert(32 * NW == 128, "work items are 128-row tiles");
     int b, h, kind, qt, n;
     if (!work_item<1, LIST>(p, b, h, kind, qt, n)) return;
-    dq_tile<D, NW, KB, VARIANT, MASK, R, LIST>(p, b, h, qt, n, K0, V0, K1, V1, mbits);
+    dq_tile<D, NW, KB, VARIANT, MASK, R, LIST>(p, b, h, qt, n, K0, V0, K1, V1, mbits, K20, K21);
 }
 
 // dK/dV and dQ in one launch: both kinds of tile of a (batch entry, head)
@@ -733,23 +899,26 @@ bwd_dq_kernel(const AttnParams p) {
 template <int D, int NW, int KB, int VARIANT, int MASK, int R, bool LIST>
 __global__ void __launch_bounds__(64 * NW, (kBwdWavesPerSimd<D, VARIANT, MASK>))
 bwd_kernel(const AttnParams p) {
-    __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D>];
+    __shared__ __attribute__((aligned(16))) bf16 smem[kDkdvLds<D, kMapsOf<VARIANT>>];
     constexpr int kTile = 32 * KB * D;
+    constexpr int kTile2 = kMapsOf<VARIANT> == 2 ? kTile : 8;  // map 2's K buffers
     __shared__ __attribute__((aligned(1024))) bf16 K0[kTile], V0[kTile], K1[kTile], V1[kTile];
+    __shared__ __attribute__((aligned(1024))) bf16 K20[kTile2], K21[kTile2];
     __shared__ __attribute__((aligned(16))) uint32_t mbits[MASK != kMaskNone ? kMaskWords : 1];
     static_assert(32 * NW == 128, "work items are 128-row tiles");
     int b, h, kind, t, n;
     if (!work_item<2, LIST>(p, b, h, kind, t, n)) return;
     if (kind == 0) {
         // A workgroup does one kind of work: the dQ key buffers, each 32 KB
-        // rows x D, hold the dK/dV waves' V rows (32 rows each when KB = 1).
-        static_assert(!kVInLds<D> || (KB == 1 && NW <= 4), "V rows need one dQ buffer per wave");
+        // rows x D, hold the dK/dV waves' V rows (32 rows each).
+        static_assert(!kVInLds<D, VARIANT> || NW <= 4, "V rows need one dQ buffer per wave");
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         bf16 *vt = w == 0 ? K0 : w == 1 ? V0 : w == 2 ? K1 : V1;
         dkdv_tile<D, NW, VARIANT, MASK, R, LIST>(p, b, h, t, n, smem, mbits, vt);
     }
     else
-        dq_tile<D, NW, KB, VARIANT, MASK, R, LIST>(p, b, h, t, n, K0, V0, K1, V1, mbits);
+        dq_tile<D, NW, KB, VARIANT, MASK, R, LIST>(p, b, h, t, n, K0, V0, K1, V1, mbits, K20,
+                                                   K21);
 }
 
 // Every workgroup runs four waves: 128 keys (dK/dV) or 128 queries (dQ), the
@@ -758,9 +927,11 @@ bwd_kernel(const AttnParams p) {
 constexpr int kBwdWaves = 4;
 static int dkdv_cols(const AttnParams &p) { return 32 * kBwdWaves / p.block_k; }
 static int dq_rows(const AttnParams &p) { return 32 * kBwdWaves / p.block_q; }
-// At d = 128 the dQ step visits 32 keys: with two 32-key blocks its S, dP and
-// operand registers no longer fit without spilling.
-static int dq_key_blocks(const AttnParams &p) { return p.block_k >= 64 && p.d == 64 ? 2 : 1; }
+// At d = 128, and with two maps, the dQ step visits 32 keys: with two 32-key
+// blocks its S, dP and operand registers no longer fit without spilling.
+static int dq_key_blocks(const AttnParams &p) {
+    return p.block_k >= 64 && p.d == 64 && p.variant != kDiff ? 2 : 1;
+}
 
 // Launches kernel template K<..., LIST> with LIST = (the call has a schedule).
 #define SIGATTN_LIST_LAUNCH(KERNEL, ...)                                                           \

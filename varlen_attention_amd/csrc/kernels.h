@@ -9,8 +9,8 @@
 namespace sigattn {
 
 // The ABI's variants, plus kDiff: differential attention, two softmax maps
-// over one V combined as O1 - lambda O2 (forward only; set by the
-// differential entry point).
+// over one V combined as O1 - lambda O2 (set by the differential entry
+// points).
 enum Variant { kSigmoid = 0, kSoftmax = 1, kSoftmax1 = 2, kDiff = 3 };
 
 // Layout of a schedule buffer (blockmask_build's optional output; byte
@@ -95,6 +95,10 @@ struct AttnParams {
     int block_q, block_k, Tq, Tk;   // block-mask geometry
     float scale;
     int bias_mode, variant;
+    // Differential backward in one launch: the second map's gradients (bf16
+    // [B, H, L, d], output layout).  Its inputs are q2, k2, o2 (the map's own
+    // forward output) and lse2; the first map's are q, k, o and lse.
+    void *dq2, *dk2;
 };
 
 // bits_out (or null; with mask): the mask packed to bits, ScheduleLayout's
