@@ -640,7 +640,7 @@ def run_suite(args) -> int:
     all_rows = float(wd.B) * wd.L * wd.H
     # (name, maps, flops per pair and map, rows read, rows written)
     kinds = (("diff fwd", 2, 4, 5, 1), ("softmax fwd (map 1)", 1, 4, 3, 1),
-             ("softmax fwd (map 2)", 1, 4, 3, 1), ("diff bwd (two launches)", 2, 10, 10, 5))
+             ("softmax fwd (map 2)", 1, 4, 3, 1), ("diff bwd", 2, 10, 10, 5))
     for j, (kern, maps, fpp, rd, wr) in enumerate(kinds):
         med = float(np.median(warm[:, j]))
         algo = (rd * valid_rows + wr * all_rows) * 2.0 * wd.d

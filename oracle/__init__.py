@@ -360,6 +360,10 @@ def diff_bwd_rows(q1, k1, q2, k2, v, do, seq_lens, lam: float, b: int, h: int, q
     return dq1, dk1, -lam * dq2, -lam * dk2, dv1 - lam * dv2
 
 
+# Fully padded 128-row tiles per zero item of a work schedule.
+ZERO_TILES = 4
+
+
 def schedule(seq_lens, block_mask, H: int, L: int, block_q: int, block_k: int) -> dict:
     """Work schedule of one batch, by its definition (Binary Block Masking,
     "Presentation": the block structure is built once and shared by every
@@ -369,11 +373,17 @@ def schedule(seq_lens, block_mask, H: int, L: int, block_q: int, block_k: int) -
     Work items cover 128-row tiles of every (batch entry, head).  The pairs
     are ordered by length rank (longest first, ties by index; batches of more
     than 1024 entries keep index order) and then head; pair p goes to XCD
-    p % 8.  XCD x lists, for its pairs in order, the tiles ceil(n/128) of
-    every non-empty sequence (all tiles of kind 0, then of kind 1 when there
-    are two kinds), then, for its pairs again, all ceil(L/128) tiles of every
-    empty sequence.  Its k-th item sits in slot 8 k + x; slots past the end
-    are None.  Items are (b, h, kind, tile, n) with n = clamp(seq_lens[b]).
+    p % 8.  XCD x lists, for its pairs in order, the ceil(n/128) tiles with
+    valid rows (all tiles of kind 0, then of kind 1 when there are two
+    kinds): the compute items; and, for its pairs again, zero items: the
+    fully padded tiles ceil(n/128) .. ceil(L/128) - 1 (every tile of an
+    empty sequence) in runs of ZERO_TILES, one item per run, named by its
+    first tile (kind 0 runs, then kind 1).  One kind: the zero items follow
+    the Nc compute items.  Two kinds: with h = floor(Nc / 2) and R = Nc - h,
+    zero item j of Nz follows compute item h + floor(j R / Nz) (all zero
+    items when Nc = 0).  Its k-th item sits in slot 8 k + x; slots past the
+    end are None.  Items are (b, h, kind, tile, n) with
+    n = clamp(seq_lens[b]).
 
     Kept-entry lists: for batch entry b and 128-row query group g, the lines
     are the block rows g R .. g R + R - 1 (R = 128 / block_q) below Tq, and the
@@ -396,16 +406,26 @@ def schedule(seq_lens, block_mask, H: int, L: int, block_q: int, block_k: int) -
     for K, name in ((1, "items1"), (2, "items2")):
         slots = [None] * (8 * per_xcd * G * K)
         for x in range(8):
-            seq = []
+            compute, zero = [], []
             for p in range(x, B * H, 8):
                 b, h = pairs[p]
                 if n[b] > 0:
-                    seq += [(b, h, kind, t, n[b]) for kind in range(K)
-                            for t in range(-(-n[b] // 128))]
+                    compute += [(b, h, kind, t, n[b]) for kind in range(K)
+                                for t in range(-(-n[b] // 128))]
             for p in range(x, B * H, 8):
                 b, h = pairs[p]
-                if n[b] == 0:
-                    seq += [(b, h, kind, t, 0) for kind in range(K) for t in range(G)]
+                real = -(-n[b] // 128)
+                zero += [(b, h, kind, t, n[b]) for kind in range(K)
+                         for t in range(real, G, ZERO_TILES)]
+            if K == 1 or not compute:
+                seq = compute + zero
+            else:
+                half = len(compute) // 2
+                rest = len(compute) - half
+                seq = []
+                for c, item in enumerate(compute):
+                    seq.append(item)
+                    seq += [z for j, z in enumerate(zero) if half + j * rest // len(zero) == c]
             for k, item in enumerate(seq):
                 slots[8 * k + x] = item
         out[name] = slots

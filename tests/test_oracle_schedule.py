@@ -1,7 +1,8 @@
 """Pins of oracle.schedule (the work schedule written out from its
 definition; Binary Block Masking, "Presentation" and "How it works"):
 a hand-worked example, the invariants every schedule must meet (each tile
-exactly once, its pair's XCD, longest sequence first, empty sequences last),
+exactly once, its pair's XCD, longest sequence first, zero items after the
+compute items of one kind, spread evenly over the second half of two kinds),
 and the kept-entry lists against a vectorised numpy reduction of the block
 mask (a different computation from the oracle's loops)."""
 import numpy as np
@@ -13,14 +14,34 @@ import oracle
 def test_hand_worked_example():
     # Two sequences (n = 100, 300), one head, L = 300: the longer is rank 0
     # (pair 0 -> XCD 0: tiles 0, 1, 2 in slots 0, 8, 16), the shorter rank 1
-    # (pair 1 -> XCD 1: tile 0 in slot 1).  24 slots = 8 XCDs x 1 pair x 3 tiles.
+    # (pair 1 -> XCD 1: tile 0 in slot 1, then one zero item for its fully
+    # padded tiles 1 and 2 in slot 9).  24 slots = 8 XCDs x 1 pair x 3 tiles.
     bm = oracle.blockmask(np.array([100, 300], np.int32), None, 300, 128, 128)
     s = oracle.schedule([100, 300], bm, 1, 300, 128, 128)
     assert len(s["items1"]) == 24 and len(s["items2"]) == 48
     assert {i: x for i, x in enumerate(s["items1"]) if x} == {
-        0: (1, 0, 0, 0, 300), 8: (1, 0, 0, 1, 300), 16: (1, 0, 0, 2, 300), 1: (0, 0, 0, 0, 100)}
-    # Two kinds: the pair's kind-0 tiles, then its kind-1 tiles.
+        0: (1, 0, 0, 0, 300), 8: (1, 0, 0, 1, 300), 16: (1, 0, 0, 2, 300), 1: (0, 0, 0, 0, 100),
+        9: (0, 0, 0, 1, 100)}
+    # Two kinds: the pair's kind-0 tiles, then its kind-1 tiles.  XCD 1 has
+    # two compute items and two zero items (kind 0, then kind 1): h = 1,
+    # R = 1, so both follow compute item 1 + floor(j * 1 / 2) = 1.
     assert [x for x in s["items2"][0::8] if x] == [(1, 0, k, t, 300) for k in (0, 1) for t in range(3)]
+    assert [x for x in s["items2"][1::8] if x] == [(0, 0, 0, 0, 100), (0, 0, 1, 0, 100),
+                                                    (0, 0, 0, 1, 100), (0, 0, 1, 1, 100)]
+    # n = 600 at L = 1200: tiles 0..4 hold valid rows, tiles 5..8 and 9 form
+    # two zero items.  One kind: compute items, then zero items.  Two kinds:
+    # ten compute items (h = 5, R = 5) and four zero items, after compute
+    # items 5 + floor(j * 5 / 4) = 5, 6, 7, 8.
+    s5 = oracle.schedule([600], oracle.blockmask(np.array([600], np.int32), None, 1200, 128, 128),
+                         1, 1200, 128, 128)
+    assert [x[3] for x in s5["items1"] if x] == [0, 1, 2, 3, 4, 5, 9]
+    assert [(x[2], x[3]) for x in s5["items2"] if x] == (
+        [(0, t) for t in range(5)] + [(1, 0), (0, 5), (1, 1), (0, 9), (1, 2), (1, 5), (1, 3),
+                                      (1, 9), (1, 4)])
+    # An empty sequence among 9 tiles (L = 1100): zero items at tiles 0, 4, 8.
+    s0 = oracle.schedule([0], oracle.blockmask(np.array([0], np.int32), None, 1100, 128, 128),
+                         1, 1100, 128, 128)
+    assert [x for x in s0["items1"] if x] == [(0, 0, 0, t, 0) for t in (0, 4, 8)]
     # Sequence 0 keeps only block (0, 0) (100 < 128); sequence 1 keeps all of
     # its 3 x 3 blocks, full where the block lies inside [0, 256)^2.
     assert s["qlists"][0] == [[(0, 1, 0)], [], []]
@@ -60,19 +81,42 @@ def test_schedule_invariants(seed):
         slots = s[name]
         assert len(slots) == 8 * (-(-(B * H) // 8)) * G * K
         seen = [x for x in slots if x is not None]
-        want = sorted((b, h, kind, t, int(nc[b])) for b in range(B) for h in range(H)
-                      for kind in range(K) for t in range(-(-nc[b] // 128) if nc[b] else G))
-        assert sorted(seen) == want  # every tile exactly once
+        # A compute item covers its tile; a zero item (its tile at or past
+        # ceil(n / 128)) covers ZERO_TILES tiles from there, below G.
+        covered = []
+        for b, h, kind, t, nb in seen:
+            real = -(-nb // 128)
+            if t < real:
+                covered.append((b, h, kind, t))
+            else:
+                assert (t - real) % oracle.ZERO_TILES == 0  # runs start at the first padded tile
+                covered += [(b, h, kind, u) for u in range(t, min(G, t + oracle.ZERO_TILES))]
+            assert nb == nc[b]
+        want = sorted((b, h, kind, t) for b in range(B) for h in range(H)
+                      for kind in range(K) for t in range(G))
+        assert sorted(covered) == want  # every tile exactly once
         for x in range(8):
             mine = [it for it in slots[x::8]]
             live = [it for it in mine if it is not None]
             assert mine[:len(live)] == live  # no hole before the last item
             for b, h, kind, t, nb in live:
                 assert pair_of[(b, h)] % 8 == x  # the pair's XCD
-            lens = [nb for b, h, kind, t, nb in live]
-            nonzero = [v for v in lens if v > 0]
-            assert nonzero == sorted(nonzero, reverse=True)  # longest first
-            assert lens == nonzero + [0] * (len(lens) - len(nonzero))  # empty sequences last
+            work = [t * 128 < nb for b, h, kind, t, nb in live]
+            lens = [nb for (b, h, kind, t, nb), w in zip(live, work) if w]
+            assert lens == sorted(lens, reverse=True)  # longest first
+            # Zero items after the compute items (one kind), or spread evenly
+            # over their second half (two kinds): none before compute item
+            # h = floor(Nc / 2), and after each later one at most
+            # ceil(Nz / (Nc - h)).
+            n_c, n_z = sum(work), len(work) - sum(work)
+            if n_c and n_z:
+                runs = "".join("c" if w else "z" for w in work).split("c")[1:]
+                if K == 1:
+                    assert work == [True] * n_c + [False] * n_z
+                else:
+                    half = n_c // 2
+                    assert all(len(r) == 0 for r in runs[:half])
+                    assert max(len(r) for r in runs[half:]) <= -(-n_z // (n_c - half))
 
 
 @pytest.mark.parametrize("bq,bk", [(32, 128), (64, 64), (128, 32)])

@@ -311,8 +311,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
         zero_rows<D>(dvb, p.osl, r0, rows, tid, NT);
         if constexpr (MAPS == 2) zero_rows<D>(dk2b, p.osl, r0, rows, tid, NT);
     };
-    if (k0 >= n) {  // a tile of an empty sequence: zeros, nothing else
-        zero_tile(k0, min(BKV, L - k0));
+    if (k0 >= n) {  // a zero item: zeros, nothing else
+        zero_tile(k0, zero_item_rows<BKV, LIST>(k0, L));
         return;
     }
     const bf16 *qb = reinterpret_cast<const bf16 *>(p.q) + b * p.sb + h * p.sh;
@@ -575,9 +575,9 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, int b, int h, int
             store_rows_t<D>(dk2b + (int64_t)key * p.osl, dkt2, -p.lambda * p.scale * p.grad_scale,
                             hh, k_valid);
     }
-    // This tile's share of the sequence's fully padded key tiles, issued last
-    // (nothing waits for these stores).
-    padded_share<BKV>(kt, n, L, zero_tile);
+    // Without a schedule: this tile's share of the sequence's fully padded
+    // key tiles, issued last (nothing waits for these stores).
+    if constexpr (!LIST) padded_share<BKV>(kt, n, L, zero_tile);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -609,8 +609,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
         zero_rows<D>(dqb, p.osl, r0, rows, tid, NT);
         if constexpr (MAPS == 2) zero_rows<D>(dq2b, p.osl, r0, rows, tid, NT);
     };
-    if (q0 >= n) {  // a tile of an empty sequence: zeros, nothing else
-        zero_tile(q0, min(BQ, L - q0));
+    if (q0 >= n) {  // a zero item: zeros, nothing else
+        zero_tile(q0, zero_item_rows<BQ, LIST>(q0, L));
         return;
     }
     const bf16 *qb = reinterpret_cast<const bf16 *>(p.q) + b * p.sb + h * p.sh;
@@ -842,9 +842,9 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, int b, int h, int q
             store_rows_t<D>(dq2b + (int64_t)qr * p.osl, dqt2, -p.lambda * p.scale * p.grad_scale,
                             hh, q_valid);
     }
-    // This tile's share of the sequence's fully padded query tiles, issued
-    // last (nothing waits for these stores).
-    padded_share<BQ>(qt, n, L, zero_tile);
+    // Without a schedule: this tile's share of the sequence's fully padded
+    // query tiles, issued last (nothing waits for these stores).
+    if constexpr (!LIST) padded_share<BQ>(qt, n, L, zero_tile);
 }
 
 // ---------------------------------------------------------------- kernels

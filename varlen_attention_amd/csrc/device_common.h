@@ -410,10 +410,19 @@ __device__ __forceinline__ bool work_item(const AttnParams &p, int &b, int &h, i
     }
 }
 
-// The fully padded tiles (of ROWS rows) that tile t of a sequence with
-// real = ceil(n / ROWS) tiles holding valid rows writes zeros for: tiles
-// real + i with i = t, t + real, t + 2 real, ... below nt.  Calls
-// f(first_row, rows) for each.
+// Rows a zero item (its tile starts at or past n) writes from row r0:
+// kZeroTiles tiles with a schedule (its zero items cover runs of that many),
+// one tile without (every tile of an empty sequence is its own item).
+template <int ROWS, bool LIST>
+__device__ __forceinline__ int zero_item_rows(int r0, int L) {
+    return min(LIST ? kZeroTiles * ROWS : ROWS, L - r0);
+}
+
+// Without a schedule, the fully padded tiles (of ROWS rows) that tile t of a
+// sequence with real = ceil(n / ROWS) tiles holding valid rows writes zeros
+// for: tiles real + i with i = t, t + real, t + 2 real, ... below nt.  Calls
+// f(first_row, rows) for each.  (A schedule gives these tiles zero items of
+// their own.)
 template <int ROWS, typename F>
 __device__ __forceinline__ void padded_share(int t, int n, int L, F &&f) {
     const int real = (n + ROWS - 1) / ROWS, nt = (L + ROWS - 1) / ROWS;

@@ -158,8 +158,8 @@ fwd_kernel(const AttnParams p) {
             if (kSoft && lseb[mp])
                 for (int r = r0 + tid; r < r0 + rows; r += NT) lseb[mp][r] = -INFINITY;
     };
-    if (q0 >= n) {  // a tile of an empty sequence: zeros, nothing else
-        zero_tile(q0, min(BQ, L - q0));
+    if (q0 >= n) {  // a zero item: zeros, nothing else
+        zero_tile(q0, zero_item_rows<BQ, LIST>(q0, L));
         return;
     }
 
@@ -373,9 +373,9 @@ fwd_kernel(const AttnParams p) {
                     // passes it by more than kLazyRescale (weights stay below
                     // 2^kLazyRescale, harmless in fp32 and bf16): most tiles
                     // then skip rescaling the state.  The sums stay exact
-                    // relative to m_run, and so does the log-sum-exp.  Two
-                    // maps rescale every tile: their branches cost registers.
-                    if (MAPS == 2 || __ballot(tmax > m_run[mp] + kLazyRescale) != 0) {
+                    // relative to m_run, and so does the log-sum-exp (each
+                    // map of differential attention decides for itself).
+                    if (__ballot(tmax > m_run[mp] + kLazyRescale) != 0) {
                         const float m_new = fmaxf(m_run[mp], tmax);
                         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
                         const float alpha = __builtin_amdgcn_exp2f(m_run[mp] - m_use);
@@ -494,10 +494,11 @@ fwd_kernel(const AttnParams p) {
                 *reinterpret_cast<bf16x4 *>(orow + db * 32 + i * 8 + hh * 4) = v4;
             }
     }
-    // This tile's share of the sequence's fully padded query tiles, issued
-    // last: nothing waits for these stores (before the loop, the first tile's
-    // wait for its loads also waited for them, since stores count in vmcnt).
-    padded_share<BQ>(qt, n, L, zero_tile);
+    // Without a schedule: this tile's share of the sequence's fully padded
+    // query tiles, issued last: nothing waits for these stores (before the
+    // loop, the first tile's wait for its loads also waited for them, since
+    // stores count in vmcnt).
+    if constexpr (!LIST) padded_share<BQ>(qt, n, L, zero_tile);
 }
 
 template <int D, int VARIANT>

@@ -18,6 +18,10 @@ enum Variant { kSigmoid = 0, kSoftmax = 1, kSoftmax1 = 2, kDiff = 3 };
 // n}, tile = -1 past the last item.  A launch over one kind of 128-row tile
 // (forward, dK/dV alone, dQ alone) reads items1, the one-launch backward
 // items2; slot i is workgroup i's item, and workgroup i runs on XCD i % 8.
+// An item whose tile starts at or past n is a zero item: it writes the zero
+// rows of tiles tile .. tile + kZeroTiles - 1 (below L) and nothing else;
+// an XCD's zero items follow its compute items (items1) or are spread over
+// the second half of them (items2).
 // Entry lists hold, per batch entry and 128-row group of queries (qlists) or
 // keys (klists), a count word and then one word per block-mask entry that
 // some line of the group keeps: e | kept-by-line << 24 | full-by-line << 28,
@@ -25,6 +29,9 @@ enum Variant { kSigmoid = 0, kSoftmax = 1, kSoftmax1 = 2, kDiff = 3 };
 // A schedule built with a dense element mask ends with that mask packed to
 // bits: per batch entry and query row, words_per_row words, bit t of word w
 // the entry for key 32 w + t (rows and keys below n; the rest unspecified).
+// Fully padded 128-row tiles per zero item of a schedule.
+constexpr int kZeroTiles = 4;
+
 struct ScheduleLayout {
     int64_t slots1, slots2;  // items in the two arrays
     int64_t items1, items2;  // byte offsets of the item arrays

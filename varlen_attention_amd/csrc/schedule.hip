@@ -9,12 +9,18 @@
 //   reads its item from slot i, so XCD x works through the (length rank,
 //   head) pairs x, x + 8, ... (all tiles of a pair share that XCD's L2; with
 //   H a multiple of 8 every XCD gets one head of each batch entry), longest
-//   sequence first (longest processing time first), then the tiles of empty
-//   sequences, which only write zeros.  The fully padded tiles of a
-//   non-empty sequence get no item: that sequence's tiles with valid rows
-//   write their zeros.  Without a schedule every workgroup derives the same
-//   item from seq_lens itself (a rank of the lengths and prefix sums over the
-//   pairs: several microseconds per workgroup).
+//   sequence first (longest processing time first), and zero items: for its
+//   pairs again, the fully padded tiles (all tiles of an empty sequence) in
+//   runs of kZeroTiles, which only write zeros, so that the longest items
+//   do not also carry their sequence's zero stores.  The forward's zero items
+//   come after its compute items, where they fill the slots the launch's
+//   tail leaves idle; the one-launch backward's, with three times the zeros
+//   to write, are spread evenly over the second half of its compute items
+//   (dealt last they form a burst of pure writes that lengthens the launch
+//   at large padding).  Without a schedule every workgroup
+//   derives its item from seq_lens itself (a rank of the lengths and prefix
+//   sums over the pairs: several microseconds per workgroup), and the tiles
+//   with valid rows write their sequence's padded tiles.
 // * Kept-entry lists.  Per batch entry and 128-row group of queries (the
 //   rows one forward or dQ workgroup owns) the block-mask entries that some
 //   block row of the group keeps, with which rows keep it and which mark it
@@ -50,6 +56,19 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *wave_tot, int *t
     __syncthreads();  // wave_tot is reused by the next call
     *total = all;
     return before + incl - v;
+}
+
+// floor(a / b) for 0 <= a < 2^48 and 0 < b < 2^31, exact: the fp64 quotient
+// of two exactly represented operands is within 2^-5 of a / b, so its
+// truncation is off by at most one and one integer test corrects it (a 64-bit
+// integer division would be a long software sequence per item).
+__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
+    int64_t q = (int64_t)((double)a / (double)b);
+    if (q * b > a)
+        --q;
+    else if ((q + 1) * b <= a)
+        ++q;
+    return q;
 }
 
 }  // namespace
@@ -99,8 +118,21 @@ schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict_
         const int pairs = B * H;
         const int npx = pairs > x ? (pairs - x + 7) / 8 : 0;  // pairs of XCD x
         const int64_t cap = ((int64_t)(pairs + 7) / 8) * G * K;  // slots of XCD x
-        int64_t k = 0;                                         // items written so far
-        for (int pass = 0; pass < 2; ++pass) {  // 0: tiles with valid rows, 1: empty sequences
+        // Pass 0 counts the XCD's compute items (tiles with valid rows) and
+        // zero items; passes 1 and 2 write them, each kind of list in pair
+        // order.  One kind: the zero items after the compute items.  Two
+        // kinds: interleaved over the second half, zero item j following
+        // compute item h + floor(j R / Nz) (h = floor(Nc / 2), R = Nc - h), so
+        // compute item c >= h sits at c + ceil((c - h) Nz / R) and zero item
+        // j at j + h + floor(j R / Nz) + 1.
+        // Per chunk of 256 pairs: each pair's first item and its (b, h, n), so
+        // that all threads write the chunk's items together (a thread finds
+        // its item's pair by binary search over the first items).
+        __shared__ int s_off[kSchedThreads], s_b[kSchedThreads], s_h[kSchedThreads],
+            s_n[kSchedThreads];
+        int64_t nc = 0, nz = 0;
+        for (int pass = 0; pass < 3; ++pass) {
+            int64_t k = 0;  // items of this list written so far
             for (int j0 = 0; j0 < npx; j0 += kSchedThreads) {
                 const int j = j0 + tid;
                 const bool valid = j < npx;
@@ -108,18 +140,55 @@ schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict_
                 const int r = pair / H, h = pair - r * H;
                 const int b = sorted ? s_ord[r] : r;
                 const int n = sorted ? s_len[b] : clamp_len(seq_lens[b], L);
-                const int per = pass == 0 ? (n + 127) / 128 : (n == 0 ? G : 0);
-                const int cnt = valid ? K * per : 0;
-                int total;
-                const int off = block_exclusive_scan(cnt, s_tot, &total);
-                for (int i = 0; i < cnt; ++i) {
-                    const int kind = i >= per ? 1 : 0, t = i - kind * per;
-                    items[8 * (k + off + i) + x] = make_int4(b, h, t | (kind << 30), n);
+                const int real = (n + 127) / 128;
+                const int zero = (G - real + kZeroTiles - 1) / kZeroTiles;
+                if (pass == 0) {
+                    int tc, tz;
+                    block_exclusive_scan(valid ? K * real : 0, s_tot, &tc);
+                    block_exclusive_scan(valid ? K * zero : 0, s_tot, &tz);
+                    nc += tc;
+                    nz += tz;
+                    continue;
                 }
+                const int cnt = valid ? K * (pass == 1 ? real : zero) : 0;
+                int total;
+                s_off[tid] = block_exclusive_scan(cnt, s_tot, &total);
+                s_b[tid] = b;
+                s_h[tid] = h;
+                s_n[tid] = n;
+                __syncthreads();
+                const int64_t hc = K == 1 ? nc : nc / 2, rest = nc - hc;
+                for (int e = tid; e < total; e += kSchedThreads) {
+                    // The last pair whose first item is at or before e (pairs
+                    // without items share their successor's first item).
+                    int lo = 0, hi = kSchedThreads - 1;
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        if (s_off[mid] <= e)
+                            lo = mid;
+                        else
+                            hi = mid - 1;
+                    }
+                    const int pb = s_b[lo], ph = s_h[lo], pn = s_n[lo];
+                    const int preal = (pn + 127) / 128;
+                    const int per = pass == 1 ? preal : (G - preal + kZeroTiles - 1) / kZeroTiles;
+                    const int i = e - s_off[lo];
+                    const int kind = i >= per ? 1 : 0, u = i - kind * per;
+                    const int t = pass == 1 ? u : preal + kZeroTiles * u;
+                    const int64_t idx = k + e;
+                    int64_t pos;
+                    if (pass == 1)
+                        pos = idx < hc || nz == 0 ? idx
+                                                  : idx + floor_div((idx - hc) * nz + rest - 1, rest);
+                    else
+                        pos = idx + (rest == 0 ? hc : hc + floor_div(idx * rest, nz) + 1);
+                    items[8 * pos + x] = make_int4(pb, ph, t | (kind << 30), pn);
+                }
+                __syncthreads();  // s_off and the pair arrays are rewritten by the next chunk
                 k += total;
             }
         }
-        for (int64_t kk = k + tid; kk < cap; kk += kSchedThreads)
+        for (int64_t kk = nc + nz + tid; kk < cap; kk += kSchedThreads)
             items[8 * kk + x] = make_int4(0, 0, -1, 0);
         return;
     }
