@@ -230,9 +230,6 @@ def summarize_counters(kernel: str, dirs) -> str:
                 "SQ_INSTS_VALU_INT32", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
         if have(num, "SQ_INSTS_MFMA"):
             derived.append((f"{num} per MFMA instruction", avg[num] / avg["SQ_INSTS_MFMA"]))
-    if have("SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS"):
-        derived.append(("LDS bank-conflict cycles per LDS instruction",
-                        avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_INSTS_LDS"]))
     if have("GRBM_GUI_ACTIVE"):
         derived.append(("one XCD's busy cycles, GRBM_GUI_ACTIVE / 8", avg["GRBM_GUI_ACTIVE"] / xcds))
     if derived:
