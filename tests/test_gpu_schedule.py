@@ -1,8 +1,9 @@
 """The work schedule blockmask_build writes beside the block mask (work items
-per XCD, longest sequence first; kept-entry lists per 128-row group): bit for
-bit the oracle's schedule, and attention results bit for bit those without
-it (forward, backward in one launch and in two, every variant, every mask
-form and block size, differential attention)."""
+per XCD, longest sequence first, and zero items for the fully padded tiles;
+kept-entry lists per 128-row group): bit for bit the oracle's schedule, and
+attention results bit for bit those without it (forward, backward in one
+launch and in two, every variant, every mask form and block size,
+differential attention), every padded row written."""
 import numpy as np
 import pytest
 import torch
@@ -171,3 +172,61 @@ def test_differential_identical_with_schedule(va, form):
     torch.cuda.synchronize()
     for a, b_ in zip(*res):
         assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
+
+
+@pytest.mark.parametrize("variant,bias", [(SIGMOID, 1), (SOFTMAX, 0), (3, 0)])
+def test_zero_items_write_every_padded_row(va, variant, bias):
+    """With a schedule the fully padded tiles are zero items of their own, in
+    runs of four 128-row tiles: L = 1100 (9 tiles) with n = 300 leaves tiles
+    3..8 (a run of four, then of two), an empty sequence tiles 0..8 (runs of
+    four, four and one).  Every output starts as NaN; with and without the
+    schedule (forward, one-launch backward, its two halves, and differential
+    attention, variant 3) the results are bit-identical, every padded row is
+    +0 and every padded log-sum-exp -inf."""
+    B, H, L, d = 3, 2, 1100, 64
+    n = np.array([L, 300, 0], np.int32)
+    rng = np.random.default_rng(77 + variant)
+    q, k, v, do, q2, k2 = (syn.random_tensor(rng, (B, H, L, d)) for _ in range(6))
+    say(f"zero items variant={variant} L={L} n={n.tolist()}")
+    n_gpu = to_gpu(n, torch.int32)
+    bm, sched = va.blockmask_build(n_gpu, L, 128, 128, heads=H)
+    g = [to_gpu_bf16(t) for t in (q, k, v, do, q2, k2)]
+
+    def nan_like(t, dtype=None):
+        return torch.full(t.shape if dtype is None else t.shape[:3], float("nan"),
+                          dtype=dtype or t.dtype, device=t.device)
+
+    res = []
+    for s in (None, sched):
+        if variant == 3:
+            o, o1, o2 = (nan_like(g[0]) for _ in range(3))
+            l1, l2 = nan_like(g[0], torch.float32), nan_like(g[0], torch.float32)
+            va.sigattn_diff_fwd(g[0], g[1], g[4], g[5], g[2], n_gpu, 0.7, block_mask=bm,
+                                schedule=s, out=o, o1=o1, o2=o2, lse1=l1, lse2=l2)
+            grads = [nan_like(g[0]) for _ in range(5)]
+            va.sigattn_diff_bwd(g[0], g[1], g[4], g[5], g[2], g[3], o1, o2, l1, l2, n_gpu, 0.7,
+                                block_mask=bm, schedule=s, grads=grads)
+            res.append([o, o1, o2, *grads, l1, l2])
+            continue
+        kw = dict(block_mask=bm, bias=bias, variant=variant, schedule=s)
+        o = nan_like(g[0])
+        lse = nan_like(g[0], torch.float32) if variant != SIGMOID else None
+        va.sigattn_fwd(*g[:3], n_gpu, out=o, lse=lse, **kw)
+        soft = dict(o=o, lse=lse) if variant != SIGMOID else {}
+        dq, dk, dv, dk2, dv2, dq2 = (nan_like(g[0]) for _ in range(6))
+        va.sigattn_bwd(*g[:4], n_gpu, dq=dq, dk=dk, dv=dv, **soft, **kw)
+        va.sigattn_bwd_dkdv(*g[:4], n_gpu, dk=dk2, dv=dv2, **soft, **kw)
+        va.sigattn_bwd_dq(*g[:4], n_gpu, dq=dq2, **soft, **kw)
+        res.append([o, dq, dk, dv, dk2, dv2, dq2] + ([lse] if variant != SIGMOID else []))
+    torch.cuda.synchronize()
+    padded = torch.arange(L, device=n_gpu.device)[None, :] >= n_gpu[:, None]  # [B, L]
+    for a, b_ in zip(*res):
+        bits = (lambda t: t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16))
+        assert torch.equal(bits(a), bits(b_))
+        rows = padded[:, None, :].expand(B, H, L)
+        if a.dtype == torch.float32:  # a log-sum-exp
+            assert torch.all(torch.isneginf(a[rows]))
+            assert not torch.isnan(a).any()
+        else:
+            assert torch.all(a.view(torch.int16)[rows] == 0), "a padded row is not +0"
+            assert not torch.isnan(a.float()).any()
