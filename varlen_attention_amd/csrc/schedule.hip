@@ -107,6 +107,7 @@ schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict_
             for (int c = tid; c < B; c += kSchedThreads) {
                 const int nc = s_len[c];
                 int rank = 0;
+#pragma unroll 8
                 for (int c2 = 0; c2 < B; ++c2) {
                     const int m = s_len[c2];
                     rank += (m > nc) || (m == nc && c2 < c);
@@ -126,10 +127,14 @@ schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict_
         // compute item c >= h sits at c + ceil((c - h) Nz / R) and zero item
         // j at j + h + floor(j R / Nz) + 1.
         // Per chunk of 256 pairs: each pair's first item and its (b, h, n), so
-        // that all threads write the chunk's items together (a thread finds
-        // its item's pair by binary search over the first items).
+        // that all threads write the chunk's items together.  A thread finds
+        // its item's pair in an owner map (one byte per item, when the chunk
+        // has at most kOwnerMax items) or by binary search over the first
+        // items.
+        constexpr int kOwnerMax = 4096;
         __shared__ int s_off[kSchedThreads], s_b[kSchedThreads], s_h[kSchedThreads],
             s_n[kSchedThreads];
+        __shared__ uint8_t s_owner[kOwnerMax];
         int64_t nc = 0, nz = 0;
         for (int pass = 0; pass < 3; ++pass) {
             int64_t k = 0;  // items of this list written so far
@@ -156,19 +161,26 @@ schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict_
                 s_b[tid] = b;
                 s_h[tid] = h;
                 s_n[tid] = n;
+                const bool owner_map = total <= kOwnerMax;
+                if (owner_map)
+                    for (int i = 0; i < cnt; ++i) s_owner[s_off[tid] + i] = (uint8_t)tid;
                 __syncthreads();
                 const int64_t hc = K == 1 ? nc : nc / 2, rest = nc - hc;
                 for (int e = tid; e < total; e += kSchedThreads) {
-                    // The last pair whose first item is at or before e (pairs
-                    // without items share their successor's first item).
+                    // Without the owner map: the last pair whose first item is
+                    // at or before e (pairs without items share their
+                    // successor's first item).
                     int lo = 0, hi = kSchedThreads - 1;
-                    while (lo < hi) {
-                        const int mid = (lo + hi + 1) >> 1;
-                        if (s_off[mid] <= e)
-                            lo = mid;
-                        else
-                            hi = mid - 1;
-                    }
+                    if (owner_map)
+                        lo = s_owner[e];
+                    else
+                        while (lo < hi) {
+                            const int mid = (lo + hi + 1) >> 1;
+                            if (s_off[mid] <= e)
+                                lo = mid;
+                            else
+                                hi = mid - 1;
+                        }
                     const int pb = s_b[lo], ph = s_h[lo], pn = s_n[lo];
                     const int preal = (pn + 127) / 128;
                     const int per = pass == 1 ? preal : (G - preal + kZeroTiles - 1) / kZeroTiles;
