@@ -378,12 +378,13 @@ def schedule(seq_lens, block_mask, H: int, L: int, block_q: int, block_k: int) -
     kinds): the compute items; and, for its pairs again, zero items: the
     fully padded tiles ceil(n/128) .. ceil(L/128) - 1 (every tile of an
     empty sequence) in runs of ZERO_TILES, one item per run, named by its
-    first tile (kind 0 runs, then kind 1).  One kind: the zero items follow
-    the Nc compute items.  Two kinds: with h = floor(Nc / 2) and R = Nc - h,
-    zero item j of Nz follows compute item h + floor(j R / Nz) (all zero
-    items when Nc = 0).  Its k-th item sits in slot 8 k + x; slots past the
-    end are None.  Items are (b, h, kind, tile, n) with
-    n = clamp(seq_lens[b]).
+    first tile (kind 0 runs, then kind 1).  With Nc compute and Nz zero
+    items, h = Nc when there is one kind and Nz <= Nc, h = 0 when there is
+    one kind and Nz > Nc, h = floor(Nc / 2) with two kinds; with R = Nc - h,
+    zero item j follows compute item h + floor(j R / Nz), and when R = 0 all
+    zero items follow the compute items.  Its k-th item sits in slot
+    8 k + x; slots past the end are None.  Items are (b, h, kind, tile, n)
+    with n = clamp(seq_lens[b]).
 
     Kept-entry lists: for batch entry b and 128-row query group g, the lines
     are the block rows g R .. g R + R - 1 (R = 128 / block_q) below Tq, and the
@@ -417,15 +418,18 @@ def schedule(seq_lens, block_mask, H: int, L: int, block_q: int, block_k: int) -
                 real = -(-n[b] // 128)
                 zero += [(b, h, kind, t, n[b]) for kind in range(K)
                          for t in range(real, G, ZERO_TILES)]
-            if K == 1 or not compute:
+            if K == 2:
+                first = len(compute) // 2
+            else:
+                first = len(compute) if len(zero) <= len(compute) else 0
+            rest = len(compute) - first
+            if rest == 0:
                 seq = compute + zero
             else:
-                half = len(compute) // 2
-                rest = len(compute) - half
                 seq = []
                 for c, item in enumerate(compute):
                     seq.append(item)
-                    seq += [z for j, z in enumerate(zero) if half + j * rest // len(zero) == c]
+                    seq += [z for j, z in enumerate(zero) if first + j * rest // len(zero) == c]
             for k, item in enumerate(seq):
                 slots[8 * k + x] = item
         out[name] = slots

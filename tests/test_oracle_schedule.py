@@ -1,8 +1,9 @@
 """Pins of oracle.schedule (the work schedule written out from its
 definition; Binary Block Masking, "Presentation" and "How it works"):
 a hand-worked example, the invariants every schedule must meet (each tile
-exactly once, its pair's XCD, longest sequence first, zero items after the
-compute items of one kind, spread evenly over the second half of two kinds),
+exactly once, its pair's XCD, longest sequence first; zero items after the
+compute items of one kind when not more numerous, else spread between them,
+and spread evenly over the second half of two kinds),
 and the kept-entry lists against a vectorised numpy reduction of the block
 mask (a different computation from the oracle's loops)."""
 import numpy as np
@@ -29,12 +30,19 @@ def test_hand_worked_example():
     assert [x for x in s["items2"][1::8] if x] == [(0, 0, 0, 0, 100), (0, 0, 1, 0, 100),
                                                     (0, 0, 0, 1, 100), (0, 0, 1, 1, 100)]
     # n = 600 at L = 1200: tiles 0..4 hold valid rows, tiles 5..8 and 9 form
-    # two zero items.  One kind: compute items, then zero items.  Two kinds:
-    # ten compute items (h = 5, R = 5) and four zero items, after compute
-    # items 5 + floor(j * 5 / 4) = 5, 6, 7, 8.
+    # two zero items.  One kind: five compute items, two zero items (not more
+    # numerous): compute items, then zero items.  Two kinds: ten compute
+    # items (h = 5, R = 5) and four zero items, after compute items
+    # 5 + floor(j * 5 / 4) = 5, 6, 7, 8.
     s5 = oracle.schedule([600], oracle.blockmask(np.array([600], np.int32), None, 1200, 128, 128),
                          1, 1200, 128, 128)
     assert [x[3] for x in s5["items1"] if x] == [0, 1, 2, 3, 4, 5, 9]
+    # n = 200 at L = 2000: compute tiles 0, 1 and zero items at tiles 2, 6,
+    # 10, 14 (more numerous): spread, zero item j after compute item
+    # floor(j * 2 / 4) = 0, 0, 1, 1.
+    s6 = oracle.schedule([200], oracle.blockmask(np.array([200], np.int32), None, 2000, 128, 128),
+                         1, 2000, 128, 128)
+    assert [x[3] for x in s6["items1"] if x] == [0, 2, 6, 1, 10, 14]
     assert [(x[2], x[3]) for x in s5["items2"] if x] == (
         [(0, t) for t in range(5)] + [(1, 0), (0, 5), (1, 1), (0, 9), (1, 2), (1, 5), (1, 3),
                                       (1, 9), (1, 4)])
@@ -111,8 +119,10 @@ def test_schedule_invariants(seed):
             n_c, n_z = sum(work), len(work) - sum(work)
             if n_c and n_z:
                 runs = "".join("c" if w else "z" for w in work).split("c")[1:]
-                if K == 1:
+                if K == 1 and n_z <= n_c:
                     assert work == [True] * n_c + [False] * n_z
+                elif K == 1:
+                    assert work[0] and max(len(r) for r in runs) <= -(-n_z // n_c)
                 else:
                     half = n_c // 2
                     assert all(len(r) == 0 for r in runs[:half])

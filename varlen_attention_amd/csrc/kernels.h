@@ -20,8 +20,9 @@ enum Variant { kSigmoid = 0, kSoftmax = 1, kSoftmax1 = 2, kDiff = 3 };
 // items2; slot i is workgroup i's item, and workgroup i runs on XCD i % 8.
 // An item whose tile starts at or past n is a zero item: it writes the zero
 // rows of tiles tile .. tile + kZeroTiles - 1 (below L) and nothing else;
-// an XCD's zero items follow its compute items (items1) or are spread over
-// the second half of them (items2).
+// an XCD's zero items follow its compute items (items1, when they are not
+// more numerous; else spread between them) or are spread over the second
+// half of them (items2).
 // Entry lists hold, per batch entry and 128-row group of queries (qlists) or
 // keys (klists), a count word and then one word per block-mask entry that
 // some line of the group keeps: e | kept-by-line << 24 | full-by-line << 28,

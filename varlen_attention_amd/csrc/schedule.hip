@@ -14,10 +14,11 @@
 //   runs of kZeroTiles, which only write zeros, so that the longest items
 //   do not also carry their sequence's zero stores.  The forward's zero items
 //   come after its compute items, where they fill the slots the launch's
-//   tail leaves idle; the one-launch backward's, with three times the zeros
-//   to write, are spread evenly over the second half of its compute items
-//   (dealt last they form a burst of pure writes that lengthens the launch
-//   at large padding).  Without a schedule every workgroup
+//   tail leaves idle, unless they outnumber them (large padding): then they
+//   are spread evenly between them, since dealt last they would form a burst
+//   of pure writes that lengthens the launch.  The one-launch backward's,
+//   with three times the zeros to write, are spread evenly over the second
+//   half of its compute items.  Without a schedule every workgroup
 //   derives its item from seq_lens itself (a rank of the lengths and prefix
 //   sums over the pairs: several microseconds per workgroup), and the tiles
 //   with valid rows write their sequence's padded tiles.
@@ -121,11 +122,11 @@ schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict_
         const int64_t cap = ((int64_t)(pairs + 7) / 8) * G * K;  // slots of XCD x
         // Pass 0 counts the XCD's compute items (tiles with valid rows) and
         // zero items; passes 1 and 2 write them, each kind of list in pair
-        // order.  One kind: the zero items after the compute items.  Two
-        // kinds: interleaved over the second half, zero item j following
-        // compute item h + floor(j R / Nz) (h = floor(Nc / 2), R = Nc - h), so
-        // compute item c >= h sits at c + ceil((c - h) Nz / R) and zero item
-        // j at j + h + floor(j R / Nz) + 1.
+        // order, zero item j following compute item h + floor(j R / Nz)
+        // (R = Nc - h), so compute item c >= h sits at c + ceil((c - h) Nz / R)
+        // and zero item j at j + h + floor(j R / Nz) + 1.  One kind: h = Nc
+        // (the zero items after the compute items) when Nz <= Nc, else h = 0
+        // (spread between all of them).  Two kinds: h = floor(Nc / 2).
         // Per chunk of 256 pairs: each pair's first item and its (b, h, n), so
         // that all threads write the chunk's items together.  A thread finds
         // its item's pair in an owner map (one byte per item, when the chunk
@@ -165,7 +166,7 @@ schedule_kernel(const int32_t *__restrict__ seq_lens, const uint8_t *__restrict_
                 if (owner_map)
                     for (int i = 0; i < cnt; ++i) s_owner[s_off[tid] + i] = (uint8_t)tid;
                 __syncthreads();
-                const int64_t hc = K == 1 ? nc : nc / 2, rest = nc - hc;
+                const int64_t hc = K == 2 ? nc / 2 : (nz <= nc ? nc : 0), rest = nc - hc;
                 for (int e = tid; e < total; e += kSchedThreads) {
                     // Without the owner map: the last pair whose first item is
                     // at or before e (pairs without items share their
