@@ -1000,9 +1000,12 @@ def test_diff_forward(va, d, L, bq, bk, form, lam):
 
 
 DIFF_BWD_CASES = [
-    # d, L, block_q, block_k, mask form, lambda
+    # d, L, block_q, block_k, mask form, lambda (d = 64: both maps in one pass,
+    # in one launch when block_q == block_k)
     (64, 300, 128, 128, "none", 0.8),
     (64, 230, 64, 32, "dense", 0.37),
+    (64, 257, 128, 128, "range", 0.5),
+    (64, 190, 64, 64, "dense", -0.4),
     (128, 201, 128, 128, "range", 0.6),
     (128, 190, 64, 128, "dense", -0.3),
 ]
