@@ -1051,6 +1051,33 @@ def test_diff_backward(va, d, L, bq, bk, form, lam):
         assert_rows(gpu_f64(got_t), ref, n, name)
 
 
+@pytest.mark.parametrize("d,bq", [(64, 128), (64, 64), (128, 128)])
+def test_diff_backward_caller_scale(va, d, bq):
+    """Differential attention with a score scale other than 1/sqrt(d) (0.3):
+    forward and all five gradients against the oracle with the same scale.
+    d = 64 runs both maps in one pass (the scale and -lambda enter at the
+    dK2 and dQ2 stores), d = 128 as two softmax backward launches."""
+    B, H, L, lam, scale = 3, 2, 260, 0.6, 0.3
+    n = np.array([L, 131, 0], np.int32)
+    q1, k1, q2, k2, v, do = _inputs(6100 + d + bq, B, H, L, d, n, names="abcdef")
+    say(f"diff bwd caller scale d={d} bq={bq} scale={scale}")
+    n_gpu = to_gpu(n, torch.int32)
+    bm = _bm(va, n_gpu, L, bq, bq)
+    g = [to_gpu_bf16(t) for t in (q1, k1, q2, k2, v, do)]
+    kw = dict(block_mask=bm, block_q=bq, block_k=bq, scale=scale)
+    o = va.sigattn_diff_fwd(*g[:5], n_gpu, lam, **kw)
+    want_o, _, _ = oracle.diff_fwd(q1, k1, q2, k2, v, n, lam, scale=scale)
+    torch.cuda.synchronize()
+    assert_rows(gpu_f64(o), want_o, n, "O")
+    ob1, _, o1, l1 = _handed(q1, k1, v, n, SOFTMAX, bias=0, scale=scale)
+    ob2, _, o2, l2 = _handed(q2, k2, v, n, SOFTMAX, bias=0, scale=scale)
+    grads = va.sigattn_diff_bwd(*g, o1, o2, l1, l2, n_gpu, lam, **kw)
+    torch.cuda.synchronize()
+    want = oracle.diff_bwd(q1, k1, q2, k2, v, do, n, lam, scale=scale, o1=ob1, o2=ob2)
+    for name, got_t, ref in zip(("dQ1", "dK1", "dQ2", "dK2", "dV"), grads, want):
+        assert_rows(gpu_f64(got_t), ref, n, name)
+
+
 @pytest.mark.parametrize("variant", [SIGMOID, SOFTMAX])
 def test_hip_graph_capture_and_replay(va, variant):
     """The whole step (block mask and schedule, forward, backward) captured in
