@@ -225,6 +225,14 @@ def summarize_counters(kernel: str, dirs) -> str:
         derived.append(("MFMA cycles with VALU issuing beside them, "
                         "SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES",
                         avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"]))
+    if have("SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"):
+        # Summed over every CU's LDS, as rocprofv3's LdsUtil takes it.
+        derived.append(("LDS active, SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs)",
+                        avg["SQ_LDS_IDX_ACTIVE"] * xcds / (avg["GRBM_GUI_ACTIVE"] * 256)))
+    if have("SQ_INSTS_LDS_LOAD_BANDWIDTH", "GRBM_GUI_ACTIVE"):
+        derived.append(("LDS bytes loaded per CU and cycle, 64 x SQ_INSTS_LDS_LOAD_BANDWIDTH / "
+                        "(GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs)",
+                        64 * avg["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * xcds / (avg["GRBM_GUI_ACTIVE"] * 256)))
     for num in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU_CVT",
                 "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_MUL_F32", "SQ_INSTS_VALU_ADD_F32",
                 "SQ_INSTS_VALU_INT32", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
