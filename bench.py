@@ -233,6 +233,15 @@ def summarize_counters(kernel: str, dirs) -> str:
         derived.append(("LDS bytes loaded per CU and cycle, 64 x SQ_INSTS_LDS_LOAD_BANDWIDTH / "
                         "(GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs)",
                         64 * avg["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * xcds / (avg["GRBM_GUI_ACTIVE"] * 256)))
+    # Wave states, all in quad-cycles summed over the waves: waiting for
+    # anything (a dependency, a barrier), ready but not picked for issue, and
+    # issuing any instruction.
+    for num, what in (("SQ_WAIT_ANY", "waiting for anything"),
+                      ("SQ_WAIT_INST_ANY", "waiting for instruction issue"),
+                      ("SQ_ACTIVE_INST_ANY", "issuing an instruction")):
+        if have(num, "SQ_WAVE_CYCLES"):
+            derived.append((f"wave-cycles {what}, {num} / SQ_WAVE_CYCLES",
+                            avg[num] / avg["SQ_WAVE_CYCLES"]))
     for num in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU_CVT",
                 "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_MUL_F32", "SQ_INSTS_VALU_ADD_F32",
                 "SQ_INSTS_VALU_INT32", "SQ_INSTS_SALU", "SQ_INSTS_LDS"):
