@@ -712,6 +712,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="single_cell",
+                    choices=("single_cell", "long_docs_ranges", "long_docs_mask"),
+                    help="the step's workload: the single-cell benchmark (default), or, for "
+                         "profiling, the long packed documents (B8 H16 d128, causal within "
+                         "documents) with the mask as key ranges or as the dense array")
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR",
@@ -761,8 +766,18 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    w = syn.single_cell(args.seed, tensors=("q", "k", "v", "do"))
-    workload = "single_cell_b32h8d64_lognormal800"
+    form = {}  # the element mask, for the long-document workloads
+    if args.workload == "single_cell":
+        w = syn.single_cell(args.seed, tensors=("q", "k", "v", "do"))
+        workload = "single_cell_b32h8d64_lognormal800"
+    else:
+        w = syn.long_packed_docs(args.seed, tensors=("q", "k", "v", "do"))
+        if args.workload == "long_docs_ranges":
+            workload = "long_docs_b8h16d128_causal_ranges"
+            form = {"key_range": torch.from_numpy(w.key_range).to(dev)}
+        else:
+            workload = "long_docs_b8h16d128_causal_mask"
+            form = {"mask": torch.from_numpy(w.mask).to(dev)}
     B, H, L, d = w.B, w.H, w.L, w.d
     pairs = w.valid_pairs  # summed over the batch, per head
     log(f"workload {workload}: B={B} H={H} L={L} d={d} sum_n={int(w.seq_lens.sum())} "
@@ -775,7 +790,8 @@ def main() -> int:
     n = torch.from_numpy(w.seq_lens).to(dev)
     bq = bk = 128
     bm = torch.empty((B, va.num_tiles(L, bq), va.num_tiles(L, bk)), dtype=torch.uint8, device=dev)
-    sched = torch.empty(va.schedule_bytes(B, H, L, bq, bk), dtype=torch.uint8, device=dev)
+    sched = torch.empty(va.schedule_bytes(B, H, L, bq, bk, dense_mask="mask" in form),
+                        dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     stream = torch.cuda.current_stream()
@@ -789,12 +805,13 @@ def main() -> int:
             if events is not None:
                 timer.record(events[i])
         mark(0)
-        va.blockmask_build(n, L, bq, bk, out=bm, heads=H, schedule=sched)
+        va.blockmask_build(n, L, bq, bk, out=bm, heads=H, schedule=sched, **form)
         mark(1)
-        va.sigattn_fwd(q, k, v, n, block_mask=bm, schedule=sched, out=o, block_q=bq, block_k=bk)
+        va.sigattn_fwd(q, k, v, n, block_mask=bm, schedule=sched, out=o, block_q=bq, block_k=bk,
+                       **form)
         mark(2)
         va.sigattn_bwd(q, k, v, do, n, block_mask=bm, schedule=sched, dq=dq, dk=dk, dv=dv,
-                       block_q=bq, block_k=bk)
+                       block_q=bq, block_k=bk, **form)
         mark(3)
 
     for _ in range(args.warmup):
@@ -842,7 +859,7 @@ def main() -> int:
         kernels[nm] = ent
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not form:
         log("timing the CPU oracle on a sample ...")
         cpu = cpu_baseline(w)
         log(f"cpu baseline: {cpu}")
@@ -855,6 +872,7 @@ def main() -> int:
         "config": {"workload": workload, "B": B, "H": H, "L": L, "d": d,
                    "sum_n": int(w.seq_lens.sum()), "valid_pairs_per_head": int(pairs),
                    "block": bq, "variant": "sigmoid", "bias": "-ln n", "seed": args.seed,
+                   "mask": next(iter(form), "padding only"),
                    "step": "blockmask_build (block mask + schedule) + fwd + bwd (dK/dV and dQ "
                            "in one launch)",
                    "parallelism": "single GPU"},
