@@ -308,8 +308,11 @@ int sigattn_fwd_noalloc(const sigattn_shape *shape, const void *q, const void *k
  *   o_r = sum_c softmax_c(s1[r, c]) v_c - lambda * sum_c softmax_c(s2[r, c]) v_c,
  *   s_i[r, c] = scale * <q_i r, k_i c> + beta,
  * over the valid (r, c) of the definition above (the same masks for both
- * maps).  Both maps run through one tile loop: each V tile is loaded once and
- * feeds both.  lambda is the layer's scalar as a plain input (its
+ * maps).  At d = 64 both maps run through one tile loop: each V tile is
+ * loaded once and feeds both.  At d = 128 (where two maps' operands do not
+ * fit one loop) two softmax passes run on `stream`: the first writes map 1's
+ * output to o1, or without one to o, the second combines it with map 2's as
+ * o = bf16(O1) - lambda O2, rounded once more.  lambda is the layer's scalar as a plain input (its
  * reparametrisation and the per-head normalisation after the attention
  * belong to the model, not here).
  *

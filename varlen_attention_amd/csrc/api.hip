@@ -326,17 +326,41 @@ int sigattn_diff_fwd(const sigattn_shape *shape, const void *q1, const void *k1,
         return fail(SIGATTN_ERR_ALIGNMENT, "lse1/lse2 is not 4-byte aligned");
     if (!aligned16(o1) || !aligned16(o2))
         return fail(SIGATTN_ERR_ALIGNMENT, "o1/o2 is not 16-byte aligned");
+    p.v = v;
+    p.lambda = lambda;
+    if (shape->d == 128) {
+        // Two maps' operands and accumulators do not fit one tile loop at
+        // d = 128: two softmax passes on the stream.  The first writes map 1's
+        // output into o1 (or, without one, into o itself) and its LSE; the
+        // second writes map 2's (o2, lse2) and o = O1 - lambda O2 from the
+        // first's stored output.
+        sigattn::AttnParams p1 = p;
+        p1.q = q1;
+        p1.k = k1;
+        p1.o = o1 != nullptr ? o1 : o;
+        p1.lse = lse1;
+        p1.variant = sigattn::kSoftmax;
+        const hipError_t e = sigattn::launch_fwd(p1, (hipStream_t)stream);
+        if (e != hipSuccess) return launch_status(e, "sigattn_diff_fwd");
+        sigattn::AttnParams p2 = p;
+        p2.q = q2;
+        p2.k = k2;
+        p2.o = o;
+        p2.o1 = p1.o;
+        p2.o2 = o2;
+        p2.lse = lse2;
+        p2.variant = sigattn::kDiffSecond;
+        return launch_status(sigattn::launch_fwd(p2, (hipStream_t)stream), "sigattn_diff_fwd");
+    }
     p.q = q1;
     p.k = k1;
     p.q2 = q2;
     p.k2 = k2;
-    p.v = v;
     p.o = o;
     p.lse = lse1;
     p.lse2 = lse2;
     p.o1 = o1;
     p.o2 = o2;
-    p.lambda = lambda;
     p.variant = sigattn::kDiff;
     return launch_status(sigattn::launch_fwd(p, (hipStream_t)stream), "sigattn_diff_fwd");
 }

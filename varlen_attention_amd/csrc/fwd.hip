@@ -11,7 +11,7 @@ hipError_t launch_fwd_diff(const AttnParams &p, hipStream_t stream);
 
 hipError_t launch_fwd(const AttnParams &p, hipStream_t stream) {
     if (p.variant == kSigmoid) return launch_fwd_sigmoid(p, stream);
-    if (p.variant == kDiff) return launch_fwd_diff(p, stream);
+    if (p.variant == kDiff || p.variant == kDiffSecond) return launch_fwd_diff(p, stream);
     return launch_fwd_softmax(p, stream);
 }
 

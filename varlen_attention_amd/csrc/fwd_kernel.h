@@ -97,19 +97,15 @@ struct KVStage {
 // maximum before the running state is rescaled.
 constexpr float kLazyRescale = 8.0f;
 
-// Waves per SIMD the register allocation must allow.  Two maps at d = 128
-// hold two Q operands and two output accumulators (192 registers before the
-// loop's own): such waves get the whole register file.  One unmasked map at
+// Waves per SIMD the register allocation must allow.  One unmasked map at
 // d = 64 is held to 128 registers, four waves: the softmax variants would
 // otherwise take about 138 and run three (3 % slower).  One map at d = 128
 // with 32-key steps is held to 168, three waves: the softmax variants would
-// otherwise take up to 204 and run two (15 % slower with key ranges).
+// otherwise take up to 204 and run two (15 % slower with key ranges).  Two
+// maps (differential attention, d = 64 only) run two waves.
 template <int D, int VARIANT, int MASK, int KB>
 constexpr int kFwdWavesPerSimd =
-    VARIANT == kDiff && D == 128
-        ? 1
-        : (D == 64 && VARIANT != kDiff && MASK == kMaskNone ? 4
-                                                              : (D == 128 && KB == 1 ? 3 : 2));
+    D == 64 && VARIANT != kDiff && MASK == kMaskNone ? 4 : (D == 128 && KB == 1 ? 3 : 2);
 
 // R: block-mask rows per workgroup (BQ / block_q); wave w follows row
 // w * R / NW, so smaller block rows keep four waves per workgroup.
@@ -152,6 +148,11 @@ fwd_kernel(const AttnParams p) {
                         *reinterpret_cast<uint4 *>(reinterpret_cast<bf16 *>(om) + b * p.osb +
                                                    h * p.osh + (int64_t)r * p.osl + c) =
                             make_uint4(0, 0, 0, 0);
+            if constexpr (VARIANT == kDiffSecond)
+                if (p.o2 != nullptr)
+                    *reinterpret_cast<uint4 *>(reinterpret_cast<bf16 *>(p.o2) + b * p.osb +
+                                               h * p.osh + (int64_t)r * p.osl + c) =
+                        make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int mp = 0; mp < MAPS; ++mp)
@@ -485,14 +486,40 @@ fwd_kernel(const AttnParams p) {
             if constexpr (MAPS == 2) x = fmaf(oacc[1][db][e], inv[1], x);
             return keep_or_zero(x, q_valid);
         };
+        if constexpr (VARIANT == kDiffSecond) {
+            // The second map of a two-pass differential forward: its own
+            // output to o2 (when asked for), and o = O1 - lambda O2 with O1
+            // the first pass's stored bf16 output (o1, which may be o itself:
+            // each lane reads its elements before it writes them).
+            const int64_t roff = b * p.osb + h * p.osh + (int64_t)qr * p.osl;
+            const bf16 *o1row = reinterpret_cast<const bf16 *>(p.o1) + roff;
+            bf16 *o2row = p.o2 != nullptr ? reinterpret_cast<bf16 *>(p.o2) + roff : nullptr;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bf16x4 v4 = pack4(out(db, 4 * i), out(db, 4 * i + 1), out(db, 4 * i + 2),
-                                        out(db, 4 * i + 3));
-                *reinterpret_cast<bf16x4 *>(orow + db * 32 + i * 8 + hh * 4) = v4;
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const int col = db * 32 + i * 8 + hh * 4;
+                    float x[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = out(db, 4 * i + e);
+                    if (o2row != nullptr)
+                        *reinterpret_cast<bf16x4 *>(o2row + col) = pack4(x[0], x[1], x[2], x[3]);
+                    const bf16x4 first = *reinterpret_cast<const bf16x4 *>(o1row + col);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        x[e] = keep_or_zero(fmaf(-p.lambda, x[e], (float)first[e]), q_valid);
+                    *reinterpret_cast<bf16x4 *>(orow + col) = pack4(x[0], x[1], x[2], x[3]);
+                }
+        } else {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bf16x4 v4 = pack4(out(db, 4 * i), out(db, 4 * i + 1),
+                                            out(db, 4 * i + 2), out(db, 4 * i + 3));
+                    *reinterpret_cast<bf16x4 *>(orow + db * 32 + i * 8 + hh * 4) = v4;
+                }
+        }
     }
     // Without a schedule: this tile's share of the sequence's fully padded
     // query tiles, issued last: nothing waits for these stores (before the
@@ -503,15 +530,13 @@ fwd_kernel(const AttnParams p) {
 
 template <int D, int VARIANT>
 hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
-    // Two maps at d = 128 visit 32 keys at a time: two K tiles and V of 64
-    // keys, double-buffered, would leave LDS for one workgroup per CU.
-    constexpr bool kNarrow = VARIANT == kDiff && D == 128;
+    static_assert(VARIANT != kDiff || D == 64, "two maps in one loop at d = 64 only");
     constexpr int NW = 4, BQ = 32 * NW;
     const int rows = BQ / p.block_q;  // block-mask rows per workgroup: 1, 2 or 4
-    // One map at d = 128 also visits 32 keys at a time: 64-key steps hold
+    // At d = 128 the forward visits 32 keys at a time: 64-key steps hold
     // about 210 VGPRs (two waves per SIMD), 32-key steps are held to 168
     // (three).
-    const int kb = p.block_k >= 64 && !kNarrow && D == 64 ? 2 : 1;
+    const int kb = p.block_k >= 64 && D == 64 ? 2 : 1;
     const dim3 grid = tile_grid((p.L + BQ - 1) / BQ, p.B, p.H);
     dim3 block(64 * NW);
 #define SIGATTN_FWD_LAUNCH(KB_, MASK_, R_)                                                         \
@@ -522,7 +547,7 @@ hipError_t launch_fwd_d(const AttnParams &p, hipStream_t stream) {
         hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW, KB_, MASK_, R_, false>), grid, block, 0,    \
                            stream, p);
 #define SIGATTN_FWD_CASE(R_, KB_)                                                                  \
-    if constexpr (!kNarrow || KB_ == 1)                                                            \
+    if constexpr (D == 64 || KB_ == 1)                                                             \
     if (rows == R_ && kb == KB_) {                                                                 \
         if (p.mask_bits != nullptr) { /* a dense mask, packed in the schedule */                  \
             hipLaunchKernelGGL((fwd_kernel<D, VARIANT, NW, KB_, kMaskBits, R_, true>), grid,      \

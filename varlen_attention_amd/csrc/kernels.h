@@ -10,8 +10,10 @@ namespace sigattn {
 
 // The ABI's variants, plus kDiff: differential attention, two softmax maps
 // over one V combined as O1 - lambda O2 (set by the differential entry
-// points).
-enum Variant { kSigmoid = 0, kSoftmax = 1, kSoftmax1 = 2, kDiff = 3 };
+// points), and kDiffSecond: its forward's second pass where the two maps do
+// not fit one tile loop (d = 128), a softmax map whose store combines its
+// output with the first map's stored output.
+enum Variant { kSigmoid = 0, kSoftmax = 1, kSoftmax1 = 2, kDiff = 3, kDiffSecond = 4 };
 
 // Layout of a schedule buffer (blockmask_build's optional output; byte
 // offsets from its start).  Work items are 16 bytes: {b, h, tile | kind << 30,
@@ -103,6 +105,8 @@ struct AttnParams {
     int block_q, block_k, Tq, Tk;   // block-mask geometry
     float scale;
     int bias_mode, variant;
+    // Differential forward in two passes (kDiffSecond): o1 holds the first
+    // map's output, read at the store; o2, or null, receives the second's.
     // Differential backward in one launch: the second map's gradients (bf16
     // [B, H, L, d], output layout).  Its inputs are q2, k2, o2 (the map's own
     // forward output) and lse2; the first map's are q, k, o and lse.
