@@ -928,7 +928,8 @@ constexpr int kBwdWaves = 4;
 static int dkdv_cols(const AttnParams &p) { return 32 * kBwdWaves / p.block_k; }
 static int dq_rows(const AttnParams &p) { return 32 * kBwdWaves / p.block_q; }
 // At d = 128, and with two maps, the dQ step visits 32 keys: with two 32-key
-// blocks its S, dP and operand registers no longer fit without spilling.
+// blocks its S, dP and operand registers no longer fit without spilling
+// (the 64-key forms are not built for them).
 static int dq_key_blocks(const AttnParams &p) {
     return p.block_k >= 64 && p.d == 64 && p.variant != kDiff ? 2 : 1;
 }
@@ -977,7 +978,7 @@ hipError_t launch_dq_d(const AttnParams &p, hipStream_t stream) {
     const dim3 grid = tile_grid((p.L + 32 * NW - 1) / (32 * NW), p.B, p.H);
     dim3 block(64 * NW);
 #define SIGATTN_DQ_CASE(R_, KB_)                                                                 \
-    if constexpr (D == 64 || KB_ == 1)                                                           \
+    if constexpr ((D == 64 && VARIANT != kDiff) || KB_ == 1)                                   \
     if (rows == R_ && kb == KB_) {                                                               \
         if (p.mask != nullptr) {                                                                 \
             if (p.mask_bits != nullptr) {                                                  \
@@ -1015,7 +1016,7 @@ hipError_t launch_bwd_d(const AttnParams &p, hipStream_t stream) {
     const dim3 grid = tile_grid(2 * ((p.L + 32 * NW - 1) / (32 * NW)), p.B, p.H);
     dim3 block(64 * NW);
 #define SIGATTN_BWD_CASE(R_, KB_)                                                              \
-    if constexpr (D == 64 || KB_ == 1)                                                         \
+    if constexpr ((D == 64 && VARIANT != kDiff) || KB_ == 1)                                 \
     if (lines == R_ && kb == KB_) {                                                            \
         if (p.mask != nullptr) {                                                               \
             if (p.mask_bits != nullptr) {                                                  \
