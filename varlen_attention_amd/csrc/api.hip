@@ -43,7 +43,6 @@ int launch_status(hipError_t e, const char *what) {
     return ok();
 }
 
-// Shared checks of sigattn_fwd / sigattn_bwd; fills the common parameter block.
 // Address of the current device's copy of `scratch` (nullptr and *err set
 // on failure), looked up on the device's first use and kept.
 constexpr int kMaxDevices = 64;
@@ -73,6 +72,7 @@ int64_t max_workgroups(int64_t B, int64_t H, int64_t L) {
     return 16 * ((B * H + 7) / 8) * ((L + 127) / 128);
 }
 
+// Shared checks of sigattn_fwd / sigattn_bwd; fills the common parameter block.
 int check_attention(const sigattn_shape *s, const void *const *inputs, int n_inputs,
                     void *const *outputs, int n_outputs, const int32_t *seq_lens,
                     const uint8_t *block_mask, const void *schedule, const uint8_t *mask,
