@@ -949,6 +949,7 @@ DIFF_CASES = [
     (128, 257, 128, 64, "range", 0.6),
     (128, 190, 32, 128, "dense", -0.25),
     (64, 150, 32, 64, "range", 1.0),
+    (128, 333, 128, 128, "none", 0.8),
 ]
 
 
@@ -1008,6 +1009,7 @@ DIFF_BWD_CASES = [
     (64, 190, 64, 64, "dense", -0.4),
     (128, 201, 128, 128, "range", 0.6),
     (128, 190, 64, 128, "dense", -0.3),
+    (128, 333, 128, 128, "none", 0.8),
 ]
 
 

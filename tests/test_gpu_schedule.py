@@ -174,20 +174,22 @@ def test_differential_identical_with_schedule(va, form):
         assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
 
 
-@pytest.mark.parametrize("variant,bias", [(SIGMOID, 1), (SOFTMAX, 0), (3, 0)])
-def test_zero_items_write_every_padded_row(va, variant, bias):
+@pytest.mark.parametrize("variant,bias,d", [(SIGMOID, 1, 64), (SOFTMAX, 0, 64), (3, 0, 64),
+                                            (SIGMOID, 1, 128), (3, 0, 128)])
+def test_zero_items_write_every_padded_row(va, variant, bias, d):
     """With a schedule the fully padded tiles are zero items of their own, in
     runs of four 128-row tiles: L = 1100 (9 tiles) with n = 300 leaves tiles
     3..8 (a run of four, then of two), an empty sequence tiles 0..8 (runs of
     four, four and one).  Every output starts as NaN; with and without the
     schedule (forward, one-launch backward, its two halves, and differential
-    attention, variant 3) the results are bit-identical, every padded row is
-    +0 and every padded log-sum-exp -inf."""
-    B, H, L, d = 3, 2, 1100, 64
+    attention, variant 3; at d = 128 its forward is two passes) the results
+    are bit-identical, every padded row is +0 and every padded log-sum-exp
+    -inf."""
+    B, H, L = 3, 2, 1100
     n = np.array([L, 300, 0], np.int32)
     rng = np.random.default_rng(77 + variant)
     q, k, v, do, q2, k2 = (syn.random_tensor(rng, (B, H, L, d)) for _ in range(6))
-    say(f"zero items variant={variant} L={L} n={n.tolist()}")
+    say(f"zero items variant={variant} d={d} L={L} n={n.tolist()}")
     n_gpu = to_gpu(n, torch.int32)
     bm, sched = va.blockmask_build(n_gpu, L, 128, 128, heads=H)
     g = [to_gpu_bf16(t) for t in (q, k, v, do, q2, k2)]
