@@ -573,6 +573,7 @@ BWD_CASES = [
     (64, 150, 32, 64, 0, False),
     (128, 300, 128, 128, 1, False),
     (128, 201, 64, 128, 1, True),
+    (128, 190, 32, 32, 2, True),
 ]
 
 
@@ -686,6 +687,7 @@ SOFT_BWD_CASES = [
     (64, 150, 32, 64, SOFTMAX, 2, True),
     (128, 201, 128, 128, SOFTMAX1, 0, False),
     (128, 190, 64, 128, SOFTMAX, 1, True),
+    (128, 230, 32, 64, SOFTMAX, 0, False),
 ]
 
 
