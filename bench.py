@@ -622,52 +622,61 @@ def run_suite(args) -> int:
         wp = syn.make_workload("pad_pair", seed=args.seed, B=32, H=8, d=64, lengths="uniform",
                                lo=0, hi=0, seq_lens=lens, tensors=("q", "k", "v", "do"))
         case(label, wp, cold=False)
+    sc_B, sc_H, sc_L, sc_lens = w.B, w.H, w.L, w.seq_lens.copy()
     del w, wb
-    # Differential attention at the single-cell shapes: both maps in one
-    # launch, against two softmax forward launches (4 d flops per pair and map).
-    wd = syn.single_cell(args.seed, tensors=("q", "k", "v", "do"))
-    rng = np.random.default_rng(args.seed + 1)
-    q1, k1, v = gpu(wd.q), gpu(wd.k), gpu(wd.v)
-    q2, k2 = gpu(syn.random_tensor(rng, wd.q.shape)), gpu(syn.random_tensor(rng, wd.k.shape))
-    n = torch.from_numpy(wd.seq_lens).to(dev)
-    bm, sched = va.blockmask_build(n, wd.L, 128, 128, heads=wd.H)
-    dout = gpu(wd.do)
-    o, o2 = torch.empty_like(q1), torch.empty_like(q1)
-    label = "single cell, differential (lambda 0.8)"
-    log(f"case {label}")
-    _, l1, l2, m1, m2 = va.sigattn_diff_fwd(q1, k1, q2, k2, v, n, 0.8, block_mask=bm,
-                                            schedule=sched, return_maps=True)
-    grads = [torch.empty_like(q1) for _ in range(5)]
-    fns = [lambda: va.sigattn_diff_fwd(q1, k1, q2, k2, v, n, 0.8, block_mask=bm, schedule=sched,
-                                       out=o),
-           lambda: va.sigattn_fwd(q1, k1, v, n, block_mask=bm, schedule=sched,
-                                  variant=syn.SOFTMAX, bias=0, out=o),
-           lambda: va.sigattn_fwd(q2, k2, v, n, block_mask=bm, schedule=sched,
-                                  variant=syn.SOFTMAX, bias=0, out=o2),
-           lambda: va.sigattn_diff_bwd(q1, k1, q2, k2, v, dout, m1, m2, l1, l2, n, 0.8,
-                                       block_mask=bm, schedule=sched, grads=grads)]
-    warm = timer.steps(fns)
-    cold = timer.cold(fns[0], flush)
-    tiles = int((bm != 0).sum().item()) * wd.H
-    pairs = wd.valid_pairs * wd.H
-    valid_rows = float(np.clip(wd.seq_lens, 0, wd.L).sum()) * wd.H
-    all_rows = float(wd.B) * wd.L * wd.H
-    # (name, maps, flops per pair and map, rows read, rows written)
-    kinds = (("diff fwd", 2, 4, 5, 1), ("softmax fwd (map 1)", 1, 4, 3, 1),
-             ("softmax fwd (map 2)", 1, 4, 3, 1), ("diff bwd", 2, 10, 10, 5))
-    for j, (kern, maps, fpp, rd, wr) in enumerate(kinds):
-        med = float(np.median(warm[:, j]))
-        algo = (rd * valid_rows + wr * all_rows) * 2.0 * wd.d
-        rows.append({**workload(wd, 3 if j in (0, 3) else syn.SOFTMAX, "none", 128, tiles),
-                     "case": label, "kernel": kern, "warm_med_us": med,
-                     "warm_min_us": float(warm[:, j].min()),
-                     "cold_med_us": float(np.median(cold)) if j == 0 else None,
-                     "valid_tf": fpp * wd.d * maps * pairs / (med * 1e-6) / 1e12,
-                     "tile_tf": fpp * wd.d * maps * tiles * 128 * 128 / (med * 1e-6) / 1e12,
-                     "gbs": algo / (med * 1e-6) / 1e9})
-        log(f"  {kern}: warm median {med:.2f} us")
-    del q1, k1, q2, k2, v, dout, o, o2, bm, sched, grads, l1, l2, m1, m2
-    torch.cuda.empty_cache()
+    # Differential attention at the single-cell lengths, d = 64 (both maps in
+    # one forward launch) and d = 128 (a softmax pass for map 1, then map 2
+    # combined at its store), against two softmax forward launches (4 d flops
+    # per pair and map).
+    for dd in (64, 128):
+        if dd == 64:
+            wd = syn.single_cell(args.seed, tensors=("q", "k", "v", "do"))
+        else:
+            wd = syn.make_workload(f"single_cell_d{dd}", seed=args.seed, B=sc_B, H=sc_H, d=dd,
+                                   lengths="lognormal", lo=0, hi=0, seq_lens=sc_lens, L=sc_L,
+                                   tensors=("q", "k", "v", "do"))
+        rng = np.random.default_rng(args.seed + 1)
+        q1, k1, v = gpu(wd.q), gpu(wd.k), gpu(wd.v)
+        q2, k2 = gpu(syn.random_tensor(rng, wd.q.shape)), gpu(syn.random_tensor(rng, wd.k.shape))
+        n = torch.from_numpy(wd.seq_lens).to(dev)
+        bm, sched = va.blockmask_build(n, wd.L, 128, 128, heads=wd.H)
+        dout = gpu(wd.do)
+        o, o2 = torch.empty_like(q1), torch.empty_like(q1)
+        label = f"single cell{'' if dd == 64 else f', d = {dd}'}, differential (lambda 0.8)"
+        log(f"case {label}")
+        _, l1, l2, m1, m2 = va.sigattn_diff_fwd(q1, k1, q2, k2, v, n, 0.8, block_mask=bm,
+                                                schedule=sched, return_maps=True)
+        grads = [torch.empty_like(q1) for _ in range(5)]
+        fns = [lambda: va.sigattn_diff_fwd(q1, k1, q2, k2, v, n, 0.8, block_mask=bm,
+                                           schedule=sched, out=o),
+               lambda: va.sigattn_fwd(q1, k1, v, n, block_mask=bm, schedule=sched,
+                                      variant=syn.SOFTMAX, bias=0, out=o),
+               lambda: va.sigattn_fwd(q2, k2, v, n, block_mask=bm, schedule=sched,
+                                      variant=syn.SOFTMAX, bias=0, out=o2),
+               lambda: va.sigattn_diff_bwd(q1, k1, q2, k2, v, dout, m1, m2, l1, l2, n, 0.8,
+                                           block_mask=bm, schedule=sched, grads=grads)]
+        warm = timer.steps(fns)
+        cold = timer.cold(fns[0], flush)
+        tiles = int((bm != 0).sum().item()) * wd.H
+        pairs = wd.valid_pairs * wd.H
+        valid_rows = float(np.clip(wd.seq_lens, 0, wd.L).sum()) * wd.H
+        all_rows = float(wd.B) * wd.L * wd.H
+        # (name, maps, flops per pair and map, rows read, rows written)
+        kinds = (("diff fwd", 2, 4, 5, 1), ("softmax fwd (map 1)", 1, 4, 3, 1),
+                 ("softmax fwd (map 2)", 1, 4, 3, 1), ("diff bwd", 2, 10, 10, 5))
+        for j, (kern, maps, fpp, rd, wr) in enumerate(kinds):
+            med = float(np.median(warm[:, j]))
+            algo = (rd * valid_rows + wr * all_rows) * 2.0 * wd.d
+            rows.append({**workload(wd, 3 if j in (0, 3) else syn.SOFTMAX, "none", 128, tiles),
+                         "case": label, "kernel": kern, "warm_med_us": med,
+                         "warm_min_us": float(warm[:, j].min()),
+                         "cold_med_us": float(np.median(cold)) if j == 0 else None,
+                         "valid_tf": fpp * wd.d * maps * pairs / (med * 1e-6) / 1e12,
+                         "tile_tf": fpp * wd.d * maps * tiles * 128 * 128 / (med * 1e-6) / 1e12,
+                         "gbs": algo / (med * 1e-6) / 1e9})
+            log(f"  {kern}: warm median {med:.2f} us")
+        del wd, q1, k1, q2, k2, v, dout, o, o2, bm, sched, grads, l1, l2, m1, m2, fns
+        torch.cuda.empty_cache()
     # Long packed documents: causal mask within documents, d = 128.
     wl = syn.long_packed_docs(args.seed, tensors=("q", "k", "v", "do"))
     case("long packed documents, causal mask", wl)
